@@ -1,0 +1,479 @@
+"""DashAttention forward pass, written out plainly in float64 NumPy.
+
+TEST INFRASTRUCTURE ONLY.  This module is the oracle that the HIP library is
+checked against.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it.  It imports nothing from
+the HIP package, and the HIP package imports nothing from here.
+
+Sources (the pages are cited by title and section, never by line):
+
+* [NL] "Technische Samenvatting: DashAttention", gist.science/nl/paper/2605.18753,
+  sections "Fase 0: Lokale Chunk Samenvatting", "Fase 1: Entmax Chunk
+  Routering" (equation  w_hat = alpha-entmax(gamma * z_bar)) and
+  "Fase 2: Prior-Geinduceerde Spaarzame Softmax".
+* [ZH] "技术摘要：DashAttention", gist.science/zh/paper/2605.18753, sections
+  阶段 0 / 阶段 1 / 阶段 2 (the same three phases, same equation).
+* [ES] aiexpert.news article "DashAttention alcanza 75% de dispersidad ...",
+  the interface paragraph (q, k, v, head_cls, chunk_size, enable_gqa,
+  optional active_blocks) and the method paragraph (exact zeros below an
+  adaptive per-query threshold).
+* alpha-entmax itself is not printed by the pages.  It is the textbook
+  Tsallis transformation of Peters, Niculae & Martins (2019), "Sparse
+  Sequence-to-Sequence Models"; alpha = 2 is sparsemax of Martins & Astudillo
+  (2016), "From Softmax to Sparsemax".
+
+Readings taken where the pages are silent (each one is listed in the design doc):
+
+* Phase-0 "local scaled dot-product attention" uses scale 1/sqrt(D) and the
+  chunk's keys as its values, so a summary lives in key space and q_bar = 0
+  gives the plain mean of the chunk's keys ([NL] Fase 0, "Initialisatie").
+* Only complete chunks get a summary; a query at position i may route to
+  chunks c < floor(i / B).  Its own chunk is the diagonal branch, attended
+  causally with prior weight 1 (bias 0) ([NL] Fase 2, "Diagonaal Afhandeling").
+* Routing logits are u = gamma * s * <q, k_bar>, s the attention scale.
+* The prior is g = w_bar ** sigma on routed chunks, with g = 0 wherever
+  w_bar = 0 (so the bias is sigma * log(w_bar), and -inf off the support,
+  also when sigma = 0) ([NL] Fase 2, "Dynamische Maskering" and the sigma
+  sentence of "Diagonaal Afhandeling").  This exact form is not fixed by the
+  pages: parity of g beyond its sigma = 0 and "g = 0 where w = 0" properties
+  is unpinned.
+* Under GQA the routing probabilities of the query heads sharing a KV head
+  are averaged ([NL] Fase 1, "GQA-afhandeling"); query head q uses KV head
+  floor(q / G).  A chunk is active iff some head gives it a non-zero
+  probability, i.e. iff u > tau_hat for that head.
+* alpha = 1 is plain softmax routing: every routable chunk is active.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+F64 = np.float64
+
+
+# ---------------------------------------------------------------------------
+# small helpers
+# ---------------------------------------------------------------------------
+
+def round_to_bf16(x):
+    """Round to the nearest bfloat16 value (8 significant bits), ties to even.
+
+    bfloat16 keeps the float32 exponent range and 8 significant bits.  With
+    x = m * 2**e and 0.5 <= |m| < 1, the nearest such value is
+    rint(m * 256) * 2**(e - 8); ``np.rint`` rounds halves to even.
+    """
+    x = np.asarray(x, dtype=F64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
+def softmax(a):
+    """Numerically stable softmax of a 1-D array."""
+    a = np.asarray(a, dtype=F64)
+    z = np.exp(a - a.max())
+    return z / z.sum()
+
+
+def _default_scale(D, scale):
+    return 1.0 / math.sqrt(D) if (scale is None or scale <= 0) else float(scale)
+
+
+# ---------------------------------------------------------------------------
+# Phase 0: chunk summaries  ([NL] / [ZH] Fase 0 / 阶段 0)
+# ---------------------------------------------------------------------------
+
+def summarize(k, qbar, B, to_bf16=False):
+    """Summaries of the complete size-B chunks of one sequence.
+
+    k     : [L, Hkv, D] keys of one sequence
+    qbar  : [Hkv, D] learned summary query, one per KV head
+    returns k_bar [L // B, Hkv, D].
+
+    A learned query q_bar attends to the keys of each chunk with local scaled
+    dot-product attention; the chunk's keys serve as the values.  With
+    q_bar = 0 the weights are uniform and the summary is the mean key.  When
+    the keys are stored in bfloat16 the summary is stored in bfloat16 too
+    (rounded to nearest even), since it is cached like a key.
+    """
+    k = np.asarray(k, dtype=F64)
+    qbar = np.asarray(qbar, dtype=F64)
+    L, Hkv, D = k.shape
+    C = L // B
+    s = 1.0 / math.sqrt(D)
+    kbar = np.zeros((C, Hkv, D), dtype=F64)
+    for c in range(C):
+        for h in range(Hkv):
+            keys = k[c * B:(c + 1) * B, h, :]           # [B, D]
+            scores = s * (keys @ qbar[h])                # [B]
+            weights = softmax(scores)
+            kbar[c, h] = weights @ keys
+    return round_to_bf16(kbar) if to_bf16 else kbar
+
+
+def summarize_varlen(k, qbar, cu_seqlens, B, to_bf16=False):
+    """Packed summaries: each sequence's chunk grid restarts at its start.
+
+    Returns k_bar [sum_s floor(L_s / B), Hkv, D], sequences in order.
+    """
+    parts = []
+    for s in range(len(cu_seqlens) - 1):
+        a, b = int(cu_seqlens[s]), int(cu_seqlens[s + 1])
+        parts.append(summarize(k[a:b], qbar, B, to_bf16))
+    return np.concatenate(parts, axis=0)
+
+
+# ---------------------------------------------------------------------------
+# Phase 1: alpha-entmax routing  ([NL] / [ZH] Fase 1 / 阶段 1)
+# ---------------------------------------------------------------------------
+
+def routing_logits(q_vec, kbar_h, gamma, scale):
+    """u_c = gamma * s * <q, k_bar_c> for the routable chunks c."""
+    q_vec = np.asarray(q_vec, dtype=F64)
+    kbar_h = np.asarray(kbar_h, dtype=F64)
+    return gamma * scale * (kbar_h @ q_vec)
+
+
+def entmax_threshold_bisect(u, alpha):
+    """alpha-entmax (alpha > 1) by bisection on the threshold.
+
+    With x = (alpha - 1) * u, the solution is p_c = [x_c - tau]_+ ** (1/(alpha-1))
+    with tau chosen so that sum(p) = 1 (Peters et al. 2019).  The mass
+    sum_c [x_c - t]_+ ** (1/(alpha-1)) falls as t grows; it is >= 1 at
+    t = max(x) - 1 (the top entry alone gives 1) and <= 1 at
+    t = max(x) - n ** (1 - alpha) (every term is at most 1/n).  Bisect
+    between the two until the bracket cannot shrink in float64.
+
+    Returns (p, tau) with tau in x units.
+    """
+    u = np.asarray(u, dtype=F64)
+    n = u.size
+    x = (alpha - 1.0) * u
+    expo = 1.0 / (alpha - 1.0)
+    xmax = x.max()
+    lo = xmax - 1.0
+    hi = xmax - float(n) ** (1.0 - alpha)
+
+    def mass(t):
+        return np.sum(np.clip(x - t, 0.0, None) ** expo)
+
+    for _ in range(4000):
+        mid = 0.5 * (lo + hi)
+        if not (lo < mid < hi):
+            break
+        if mass(mid) >= 1.0:
+            lo = mid
+        else:
+            hi = mid
+    tau = 0.5 * (lo + hi)
+    p = np.clip(x - tau, 0.0, None) ** expo
+    p = p / p.sum()
+    return p, tau
+
+
+def sparsemax_sort(u):
+    """Sparsemax (alpha = 2), Martins & Astudillo (2016), by sorting.
+
+    Sort descending to z; the support size is the largest k with
+    1 + k * z_k > z_1 + ... + z_k, and tau = (z_1 + ... + z_k - 1) / k.
+    Returns (p, tau).
+    """
+    x = np.asarray(u, dtype=F64)
+    z = np.sort(x)[::-1]
+    ks = np.arange(1, z.size + 1, dtype=F64)
+    csum = np.cumsum(z)
+    support = ks[1.0 + ks * z > csum]
+    kstar = int(support.max())
+    tau = (csum[kstar - 1] - 1.0) / kstar
+    return np.clip(x - tau, 0.0, None), tau
+
+
+def entmax15_sort(u):
+    """1.5-entmax by sorting (Peters et al. 2019), with x = u / 2.
+
+    For each prefix of the descending order z, with M_k the mean of z_1..z_k
+    and S_k = sum_{j<=k} (z_j - M_k)**2, the candidate threshold is
+    tau_k = M_k - sqrt(max(0, (1 - S_k) / k)); the support size is the
+    largest k with tau_k <= z_k.  Returns (p, tau) with tau in x units.
+    """
+    x = 0.5 * np.asarray(u, dtype=F64)
+    z = np.sort(x)[::-1]
+    n = z.size
+    ks = np.arange(1, n + 1, dtype=F64)
+    means = np.cumsum(z) / ks
+    # S_k = sum_{j<=k} z_j**2 - k * M_k**2, the same sum of squared deviations
+    ss = np.cumsum(z * z) - ks * means * means
+    taus = means - np.sqrt(np.clip((1.0 - ss) / ks, 0.0, None))
+    ok = np.nonzero(taus <= z)[0]
+    kstar = int(ok.max()) + 1
+    tau = taus[kstar - 1]
+    return np.clip(x - tau, 0.0, None) ** 2, tau
+
+
+def entmax(u, alpha):
+    """alpha-entmax of one logit row.
+
+    Returns (p, tau_hat), tau_hat being the threshold in logit (u) units:
+    a chunk is active iff u > tau_hat.  alpha = 1 is softmax (every entry
+    active, tau_hat = -inf).  An empty row gives (empty, +inf).  For
+    alpha = 1.5 and alpha = 2 the closed forms are computed as well and
+    must agree with the bisection threshold.
+    """
+    u = np.asarray(u, dtype=F64)
+    if u.size == 0:
+        return np.zeros(0, dtype=F64), math.inf
+    if alpha == 1.0:
+        return softmax(u), -math.inf
+    if alpha < 1.0:
+        raise ValueError("alpha must be >= 1")
+    p, tau = entmax_threshold_bisect(u, alpha)
+    closed = None
+    if alpha == 2.0:
+        closed = sparsemax_sort(u)[1]
+    elif alpha == 1.5:
+        closed = entmax15_sort(u)[1]
+    if closed is not None:
+        assert abs(closed - tau) <= 1e-9 * max(1.0, abs(tau)), (closed, tau)
+    return p, tau / (alpha - 1.0)
+
+
+def route_position(q_group, kbar_h, alpha, gamma, scale):
+    """Route one position for one KV group.
+
+    q_group : [G, D] the query heads of one KV head at this position
+    kbar_h  : [n, D] that KV head's summaries of the routable chunks
+    Returns dict(u [G, n], tau_hat [G], p [G, n], wbar [n], mask [n] bool).
+
+    Each query head gets its own entmax distribution; the group shares the
+    average of the G distributions, and a chunk is active when any head
+    gives it non-zero probability.
+    """
+    q_group = np.asarray(q_group, dtype=F64)
+    G = q_group.shape[0]
+    n = kbar_h.shape[0]
+    u = np.zeros((G, n), dtype=F64)
+    p = np.zeros((G, n), dtype=F64)
+    tau_hat = np.zeros(G, dtype=F64)
+    for g in range(G):
+        u[g] = routing_logits(q_group[g], kbar_h, gamma, scale)
+        p[g], tau_hat[g] = entmax(u[g], alpha)
+    wbar = p.mean(axis=0) if n else np.zeros(0, dtype=F64)
+    if alpha == 1.0:
+        mask = np.ones(n, dtype=bool)
+    else:
+        mask = np.any(u > tau_hat[:, None], axis=0) if n else np.zeros(0, bool)
+    return dict(u=u, tau_hat=tau_hat, p=p, wbar=wbar, mask=mask)
+
+
+def route_sequence(q, kbar, B, alpha, gamma, sigma, G, scale, rows=None,
+                   num_slots=None):
+    """Phase 1 for one sequence.
+
+    q    : [L, Hq, D];  kbar : [C, Hkv, D] summaries of the complete chunks
+    rows : positions to route (default: all)
+    Returns mask [Hkv, L, S] bool, log_prior [Hkv, L, S] (-inf off the
+    support) and tau_hat [Hq, L] (NaN for rows not routed), S = num_slots
+    (default ceil(L / B)).  Position i routes to chunks c < floor(i / B).
+    """
+    q = np.asarray(q, dtype=F64)
+    kbar = np.asarray(kbar, dtype=F64)
+    L, Hq, D = q.shape
+    Hkv = kbar.shape[1]
+    S = num_slots if num_slots is not None else -(-L // B)
+    rows = range(L) if rows is None else rows
+    mask = np.zeros((Hkv, L, S), dtype=bool)
+    logp = np.full((Hkv, L, S), -np.inf, dtype=F64)
+    tau_hat = np.full((Hq, L), np.nan, dtype=F64)
+    for i in rows:
+        n = i // B
+        for h in range(Hkv):
+            r = route_position(q[i, h * G:(h + 1) * G, :], kbar[:n, h, :],
+                               alpha, gamma, scale)
+            tau_hat[h * G:(h + 1) * G, i] = r["tau_hat"]
+            mask[h, i, :n] = r["mask"]
+            on = r["mask"]
+            with np.errstate(divide="ignore"):
+                logp[h, i, :n][on] = sigma * np.log(r["wbar"][on])
+    return mask, logp, tau_hat
+
+
+# ---------------------------------------------------------------------------
+# Phase 2: prior-induced sparse softmax  ([NL] / [ZH] Fase 2 / 阶段 2)
+# ---------------------------------------------------------------------------
+
+def _row_keys_and_bias(i, B, mask_row, logp_row):
+    """Key positions a query at position i sees, with their additive bias.
+
+    Routed chunks c < floor(i / B) that are active contribute all B keys
+    with bias log_prior[c]; the diagonal chunk contributes keys
+    floor(i / B) * B ... i with bias 0.
+    """
+    ci = i // B
+    idx, bias = [], []
+    for c in range(ci):
+        if mask_row[c]:
+            idx.extend(range(c * B, (c + 1) * B))
+            bias.extend([logp_row[c]] * B)
+    idx.extend(range(ci * B, i + 1))
+    bias.extend([0.0] * (i + 1 - ci * B))
+    return np.asarray(idx, dtype=np.int64), np.asarray(bias, dtype=F64)
+
+
+def attention_rows(q, k, v, mask, log_prior, B, scale, G, rows):
+    """Row-sparse form: for each requested position, attend over its keys.
+
+    Returns out [len(rows), Hq, D], lse [Hq, len(rows)] (natural log).
+    Logits are s * <q_i, k_j> + bias_j over the active routed keys and the
+    causal diagonal; the result is their softmax applied to v.
+    """
+    q = np.asarray(q, dtype=F64)
+    k = np.asarray(k, dtype=F64)
+    v = np.asarray(v, dtype=F64)
+    Hq, D = q.shape[1], q.shape[2]
+    out = np.zeros((len(rows), Hq, D), dtype=F64)
+    lse = np.zeros((Hq, len(rows)), dtype=F64)
+    for r, i in enumerate(rows):
+        for qh in range(Hq):
+            h = qh // G
+            idx, bias = _row_keys_and_bias(i, B, mask[h, i], log_prior[h, i])
+            logits = scale * (k[idx, h, :] @ q[i, qh]) + bias
+            mx = logits.max()
+            w = np.exp(logits - mx)
+            ssum = w.sum()
+            out[r, qh] = (w / ssum) @ v[idx, h, :]
+            lse[qh, r] = mx + math.log(ssum)
+    return out, lse
+
+
+def attention_dense(q, k, v, mask, log_prior, B, scale, G):
+    """Dense form: a full causal L x L score matrix plus a bias matrix.
+
+    bias[i, j] = log_prior[c(j)] for j in an active routed chunk of row i,
+    0 on the diagonal chunk (j <= i), -inf everywhere else.  Returns
+    out [L, Hq, D], lse [Hq, L].
+    """
+    q = np.asarray(q, dtype=F64)
+    k = np.asarray(k, dtype=F64)
+    v = np.asarray(v, dtype=F64)
+    L, Hq, D = q.shape
+    Hkv = k.shape[1]
+    out = np.zeros((L, Hq, D), dtype=F64)
+    lse = np.zeros((Hq, L), dtype=F64)
+    for h in range(Hkv):
+        bias = np.full((L, L), -np.inf, dtype=F64)
+        for i in range(L):
+            ci = i // B
+            for c in range(ci):
+                if mask[h, i, c]:
+                    bias[i, c * B:(c + 1) * B] = log_prior[h, i, c]
+            bias[i, ci * B:i + 1] = 0.0
+        for qh in range(h * G, (h + 1) * G):
+            scores = scale * (q[:, qh, :] @ k[:, h, :].T) + bias
+            mx = scores.max(axis=1, keepdims=True)
+            w = np.exp(scores - mx)
+            ssum = w.sum(axis=1, keepdims=True)
+            out[:, qh, :] = (w / ssum) @ v[:, h, :]
+            lse[qh] = mx[:, 0] + np.log(ssum[:, 0])
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# whole forward passes
+# ---------------------------------------------------------------------------
+
+def _group_size(Hq, Hkv, enable_gqa):
+    if enable_gqa:
+        if Hq % Hkv:
+            raise ValueError("Hq must be a multiple of Hkv")
+    elif Hq != Hkv:
+        raise ValueError("enable_gqa=False needs Hq == Hkv")
+    return Hq // Hkv
+
+
+def prefill(q, k, v, qbar, B, alpha, gamma, sigma, enable_gqa=True,
+            to_bf16=False, scale=None, rows=None, dense=False, num_slots=None):
+    """Phases 0-2 for one sequence (causal prefill).
+
+    q [L, Hq, D], k/v [L, Hkv, D], qbar [Hkv, D].  ``to_bf16`` rounds the
+    summaries to bfloat16 (inputs stored in bfloat16).  ``rows`` limits
+    routing and attention to the given positions (row-sparse form);
+    ``dense=True`` uses the dense score-matrix form for every row instead.
+    Returns dict(kbar, mask, log_prior, tau_hat, out, lse, rows).
+    """
+    q = np.asarray(q, dtype=F64)
+    L, Hq, D = q.shape
+    Hkv = k.shape[1]
+    G = _group_size(Hq, Hkv, enable_gqa)
+    s = _default_scale(D, scale)
+    kbar = summarize(k, qbar, B, to_bf16)
+    rows = list(range(L)) if rows is None else list(rows)
+    mask, logp, tau_hat = route_sequence(q, kbar, B, alpha, gamma, sigma, G, s,
+                                         rows=rows, num_slots=num_slots)
+    if dense:
+        out, lse = attention_dense(q, k, v, mask, logp, B, s, G)
+        out, lse = out[rows], lse[:, rows]
+    else:
+        out, lse = attention_rows(q, k, v, mask, logp, B, s, G, rows)
+    return dict(kbar=kbar, mask=mask, log_prior=logp, tau_hat=tau_hat,
+                out=out, lse=lse, rows=rows)
+
+
+def prefill_varlen(q, k, v, qbar, cu_seqlens, B, alphas, gamma, sigma,
+                   enable_gqa=True, to_bf16=False, scale=None,
+                   rows_per_seq=None, num_slots=None):
+    """Packed variable-length prefill: every sequence is independent.
+
+    alphas[s] is sequence s's entmax alpha.  ``rows_per_seq[s]`` lists
+    positions local to sequence s (default: all).  Returns a list of
+    per-sequence result dicts (see ``prefill``).
+    """
+    res = []
+    for s in range(len(cu_seqlens) - 1):
+        a, b = int(cu_seqlens[s]), int(cu_seqlens[s + 1])
+        rows = None if rows_per_seq is None else rows_per_seq[s]
+        res.append(prefill(q[a:b], k[a:b], v[a:b], qbar, B, float(alphas[s]),
+                           gamma, sigma, enable_gqa, to_bf16, scale, rows,
+                           num_slots=num_slots))
+    return res
+
+
+def decode(q_new, k_cache, v_cache, kbar_cache, L, B, alpha, gamma, sigma,
+           enable_gqa=True, scale=None):
+    """One decode step: the row i = L - 1 of a sequence of length L.
+
+    q_new [Hq, D]; k_cache / v_cache [>= L, Hkv, D] hold the L tokens
+    (the new token's key and value at position L - 1); kbar_cache
+    [>= floor((L-1)/B), Hkv, D] holds the cached summaries of the complete
+    chunks.  Returns dict(out [Hq, D], lse [Hq], mask [Hkv, n],
+    log_prior [Hkv, n], tau_hat [Hq]) with n = floor((L-1)/B).
+    """
+    q_new = np.asarray(q_new, dtype=F64)
+    Hq, D = q_new.shape
+    Hkv = k_cache.shape[1]
+    G = _group_size(Hq, Hkv, enable_gqa)
+    s = _default_scale(D, scale)
+    i = L - 1
+    n = i // B
+    kb = np.asarray(kbar_cache[:n], dtype=F64)
+    mask = np.zeros((Hkv, n), dtype=bool)
+    logp = np.full((Hkv, n), -np.inf, dtype=F64)
+    tau_hat = np.zeros(Hq, dtype=F64)
+    for h in range(Hkv):
+        r = route_position(q_new[h * G:(h + 1) * G], kb[:, h, :], alpha, gamma, s)
+        mask[h] = r["mask"]
+        tau_hat[h * G:(h + 1) * G] = r["tau_hat"]
+        with np.errstate(divide="ignore"):
+            logp[h][r["mask"]] = sigma * np.log(r["wbar"][r["mask"]])
+    # attend: reuse the row-sparse form on a one-row view of the sequence
+    k_seq = np.asarray(k_cache[:L], dtype=F64)
+    v_seq = np.asarray(v_cache[:L], dtype=F64)
+    qfull = np.zeros((L, Hq, D), dtype=F64)
+    qfull[i] = q_new
+    mfull = np.zeros((Hkv, L, n + 1), dtype=bool)
+    lfull = np.full((Hkv, L, n + 1), -np.inf, dtype=F64)
+    mfull[:, i, :n] = mask
+    lfull[:, i, :n] = logp
+    out, lse = attention_rows(qfull, k_seq, v_seq, mfull, lfull, B, s, G, [i])
+    return dict(out=out[0], lse=lse[:, 0], mask=mask, log_prior=logp,
+                tau_hat=tau_hat)

@@ -1,0 +1,456 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself.
+
+Each test names what fixes the expected value: a hand-derived closed form, a
+textbook definition solved by a generic optimiser, a brute-force enumeration,
+or an independent library routine (torch's scaled_dot_product_attention,
+scipy's softmax) on a special case.  A dropped term, a wrong sign, a wrong
+index or a transposed operand in the oracle fails at least one of them.
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.optimize
+import scipy.special
+import torch
+import torch.nn.functional as F
+
+import oracle as O
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GOLD = json.load(open(os.path.join(HERE, "golden", "entmax_closed_forms.json")))
+
+
+def sdpa64(q, k, v, mask=None, causal=False, gqa=False):
+    """torch SDPA in float64 on the CPU. q [L,Hq,D] -> [L,Hq,D]."""
+    tq = torch.from_numpy(np.ascontiguousarray(q.transpose(1, 0, 2)))[None]
+    tk = torch.from_numpy(np.ascontiguousarray(k.transpose(1, 0, 2)))[None]
+    tv = torch.from_numpy(np.ascontiguousarray(v.transpose(1, 0, 2)))[None]
+    m = None if mask is None else torch.from_numpy(mask)
+    o = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=m, is_causal=causal,
+                                       enable_gqa=gqa)
+    return o[0].numpy().transpose(1, 0, 2)
+
+
+# ---------------------------------------------------------------- bf16 rounding
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(20000) * s for s in (1e-3, 1, 1e3)])
+    x32 = x.astype(np.float32)
+    ref = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.round_to_bf16(x32.astype(np.float64)), ref)
+
+
+def test_bf16_rounding_ties_to_even():
+    # 1 + 2^-8 lies halfway between 1 and 1 + 2^-7: even mantissa is 1.0
+    assert O.round_to_bf16(1.0 + 2.0 ** -8) == 1.0
+    # 1 + 3*2^-8 lies halfway between 1 + 2^-7 (odd) and 1 + 2^-6 (even)
+    assert O.round_to_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6
+    assert O.round_to_bf16(-(1.0 + 3 * 2.0 ** -8)) == -(1.0 + 2.0 ** -6)
+
+
+# ---------------------------------------------------------------- phase 0
+
+def test_summary_zero_query_is_mean_pooling():
+    # q_bar initialised to zero gives uniform mean pooling (Fase 0, Initialisatie)
+    rng = np.random.default_rng(1)
+    k = rng.standard_normal((200, 2, 16))
+    kb = O.summarize(k, np.zeros((2, 16)), 64)
+    assert kb.shape == (3, 2, 16)
+    for c in range(3):
+        np.testing.assert_allclose(kb[c], k[c * 64:(c + 1) * 64].mean(axis=0), atol=1e-14)
+
+
+def test_summary_is_local_sdpa_of_qbar_over_chunk_keys():
+    # local scaled dot-product attention of q_bar over each chunk (torch SDPA)
+    rng = np.random.default_rng(2)
+    D, B = 32, 16
+    k = rng.standard_normal((3 * B + 5, 2, D))
+    qbar = rng.standard_normal((2, D))
+    kb = O.summarize(k, qbar, B)
+    for c in range(3):
+        for h in range(2):
+            keys = torch.from_numpy(k[c * B:(c + 1) * B, h])[None, None]
+            qq = torch.from_numpy(qbar[h])[None, None, None]
+            ref = F.scaled_dot_product_attention(qq, keys, keys)[0, 0, 0].numpy()
+            np.testing.assert_allclose(kb[c, h], ref, atol=1e-13)
+
+
+def test_summary_chunk_indexing_and_partial_tail():
+    # keys constant per chunk: summary c must be c's constant; tail has none
+    B, D = 8, 4
+    k = np.zeros((3 * B + 3, 1, D))
+    for t in range(k.shape[0]):
+        k[t, 0, :] = t // B + 1
+    kb = O.summarize(k, np.ones((1, D)), B)
+    assert kb.shape[0] == 3
+    for c in range(3):
+        np.testing.assert_allclose(kb[c, 0], c + 1, atol=1e-14)
+
+
+def test_summary_permutation_invariant_and_sharp_limit():
+    rng = np.random.default_rng(3)
+    B, D = 16, 64
+    k = rng.standard_normal((B, 1, D))
+    qbar = rng.standard_normal((1, D))
+    perm = rng.permutation(B)
+    np.testing.assert_allclose(O.summarize(k, qbar, B), O.summarize(k[perm], qbar, B), atol=1e-13)
+    # q_bar far along key 5 (its own score dominates): summary -> key 5
+    t = 5
+    big = 1e4 * k[t, 0] / np.linalg.norm(k[t, 0])
+    assert np.argmax(k[:, 0] @ big) == t
+    np.testing.assert_allclose(O.summarize(k, big[None], B)[0, 0], k[t, 0], atol=1e-9)
+
+
+def test_summary_bf16_storage_rounds_once():
+    rng = np.random.default_rng(4)
+    k = rng.standard_normal((128, 1, 32))
+    qbar = rng.standard_normal((1, 32)) * 0.1
+    exact = O.summarize(k, qbar, 64)
+    stored = O.summarize(k, qbar, 64, to_bf16=True)
+    assert np.array_equal(stored, O.round_to_bf16(exact))
+    # half an ulp of an 8-significant-bit value is at most 2^-8 relative
+    assert np.max(np.abs(stored - exact) / np.abs(exact)) <= 2.0 ** -8
+
+
+# ---------------------------------------------------------------- entmax
+
+@pytest.mark.parametrize("case", GOLD["cases"], ids=lambda c: c["name"])
+def test_entmax_hand_derived_closed_forms(case):
+    p, tau_hat = O.entmax(np.array(case["u"]), case["alpha"])
+    np.testing.assert_allclose(p, case["p"], atol=1e-12)
+    assert abs(tau_hat - case["tau_hat"]) < 1e-12
+
+
+def test_sort_closed_forms_agree_with_bisection():
+    rng = np.random.default_rng(5)
+    for n in (1, 2, 5, 37, 300):
+        for _ in range(5):
+            u = rng.standard_normal(n) * rng.uniform(0.1, 30)
+            p2, t2 = O.sparsemax_sort(u)
+            pb, tb = O.entmax_threshold_bisect(u, 2.0)
+            assert abs(t2 - tb) < 1e-12 * max(1, abs(tb))
+            np.testing.assert_allclose(p2, pb, atol=1e-12)
+            p15, t15 = O.entmax15_sort(u)
+            pb, tb = O.entmax_threshold_bisect(u, 1.5)
+            assert abs(t15 - tb) < 1e-12 * max(1, abs(tb))
+            np.testing.assert_allclose(p15, pb, atol=1e-12)
+
+
+def _tsallis_argmax(u, alpha):
+    """Solve max_{p in simplex} <p,u> + sum(p - p^alpha)/(alpha(alpha-1))
+    with a generic constrained optimiser (the textbook definition)."""
+    n = len(u)
+
+    def neg(p):
+        p = np.clip(p, 0, None)
+        return -(p @ u + np.sum(p - p ** alpha) / (alpha * (alpha - 1)))
+
+    res = scipy.optimize.minimize(
+        neg, np.full(n, 1.0 / n), method="SLSQP", bounds=[(0, 1)] * n,
+        constraints=[{"type": "eq", "fun": lambda p: p.sum() - 1}],
+        options=dict(ftol=1e-15, maxiter=1000))
+    return np.clip(res.x, 0, None)
+
+
+@pytest.mark.parametrize("alpha", [1.25, 1.5, 2.0, 1.75])
+def test_entmax_is_the_tsallis_regularised_argmax(alpha):
+    rng = np.random.default_rng(6)
+    for _ in range(6):
+        u = rng.standard_normal(6) * 2
+        p, _ = O.entmax(u, alpha)
+        ref = _tsallis_argmax(u, alpha)
+        np.testing.assert_allclose(p, ref, atol=2e-4)
+
+
+def _brute_force_support(u, alpha):
+    """Enumerate supports S; exactly one admits a threshold t < min_S x with
+    sum_S (x_c - t)^(1/(alpha-1)) = 1 and every x_c outside S <= t."""
+    x = (alpha - 1) * np.asarray(u, float)
+    e = 1 / (alpha - 1)
+    n = len(x)
+    found = []
+    for r in range(1, n + 1):
+        for S in itertools.combinations(range(n), r):
+            xs = x[list(S)]
+            lo_t = xs.min()
+            f = lambda t: np.sum((xs - t) ** e) - 1
+            if f(lo_t) > 0:       # need the root strictly below min_S x
+                continue
+            t = scipy.optimize.brentq(f, lo_t - 2.0, lo_t, xtol=1e-15)
+            if t >= lo_t:
+                continue
+            rest = [x[c] for c in range(n) if c not in S]
+            if all(xr <= t for xr in rest):
+                found.append((set(S), t))
+    return found
+
+
+@pytest.mark.parametrize("alpha", [1.25, 1.5, 2.0])
+def test_entmax_support_matches_brute_force(alpha):
+    rng = np.random.default_rng(7)
+    for n in (2, 4, 7):
+        for _ in range(8):
+            u = rng.standard_normal(n) * rng.uniform(0.5, 6)
+            found = _brute_force_support(u, alpha)
+            assert len(found) == 1
+            S, t = found[0]
+            p, tau_hat = O.entmax(u, alpha)
+            assert set(np.nonzero(p > 0)[0]) == S
+            assert abs(tau_hat * (alpha - 1) - t) < 1e-10
+
+
+def test_entmax_alpha_to_one_is_softmax():
+    u = np.array([1.0, 0.5, -1.0])
+    sm = scipy.special.softmax(u)
+    errs = [np.abs(O.entmax(u, a)[0] - sm).max() for a in (1.1, 1.01, 1.001)]
+    assert errs[2] < 5e-4
+    assert errs[0] > errs[1] > errs[2]
+    # error shrinks about linearly in alpha - 1
+    assert 5 < errs[0] / errs[1] < 20 and 5 < errs[1] / errs[2] < 20
+    p, tau_hat = O.entmax(u, 1.0)
+    np.testing.assert_allclose(p, sm, atol=1e-15)
+    assert tau_hat == -math.inf
+
+
+def test_entmax_invariants():
+    rng = np.random.default_rng(8)
+    for alpha in (1.25, 1.5, 2.0):
+        for n in (1, 3, 50, 400):
+            u = rng.standard_normal(n) * 4
+            p, tau_hat = O.entmax(u, alpha)
+            assert np.all(p >= 0) and abs(p.sum() - 1) < 1e-12
+            # KKT: (x_c - tau) = p_c^(alpha-1) on the support, x_c <= tau off it
+            x, tau = (alpha - 1) * u, (alpha - 1) * tau_hat
+            on = p > 0
+            np.testing.assert_allclose(x[on] - tau, p[on] ** (alpha - 1), atol=1e-10)
+            assert np.all(x[~on] <= tau + 1e-12)
+            # translation invariance
+            np.testing.assert_allclose(O.entmax(u + 3.7, alpha)[0], p, atol=1e-10)
+        # tiny logits: full support; huge logits: support of one
+        u = rng.standard_normal(20)
+        assert np.all(O.entmax(1e-6 * u, alpha)[0] > 0)
+        assert np.count_nonzero(O.entmax(1e6 * u, alpha)[0]) == 1
+    assert O.entmax(np.zeros(0), 1.5)[1] == math.inf
+
+
+# ---------------------------------------------------------------- phase 1
+
+def test_gqa_average_and_or_mask_golden():
+    g = GOLD["gqa_average"]
+    heads = np.array(g["heads"])
+    # u = gamma * s * <q, kbar>: with kbar_c = u_c e_0, q = e_0, gamma * s = 1
+    D = 4
+    kb = np.zeros((3, D))
+    qg = np.zeros((2, D))
+    qg[0, 0], qg[1, 1] = 1.0, 1.0
+    kb[:, 0] = heads[0]
+    kb[:, 1] = heads[1]
+    r = O.route_position(qg, kb, g["alpha"], gamma=2.0, scale=0.5)
+    np.testing.assert_allclose(r["u"], heads, atol=1e-15)
+    np.testing.assert_allclose(r["wbar"], g["wbar"], atol=1e-12)
+    assert list(r["mask"]) == g["mask"]
+
+
+def test_routing_mask_is_union_of_head_supports():
+    rng = np.random.default_rng(9)
+    qg = rng.standard_normal((4, 16))
+    kb = rng.standard_normal((40, 16))
+    r = O.route_position(qg, kb, 1.5, gamma=30.0, scale=0.25)
+    union = np.zeros(40, bool)
+    for g in range(4):
+        union |= O.entmax(r["u"][g], 1.5)[0] > 0
+    assert np.array_equal(r["mask"], union)
+    assert np.array_equal(r["mask"], r["wbar"] > 0)
+    assert 0 < r["mask"].sum() < 40
+
+
+def test_routable_range_and_head_mapping():
+    # Hkv = 2, G = 2: query heads 0,1 -> kv head 0; 2,3 -> kv head 1.
+    rng = np.random.default_rng(10)
+    B, L, D = 4, 20, 8
+    q = rng.standard_normal((L, 4, D))
+    kbar = rng.standard_normal((L // B, 2, D))
+    kbar[:, 1, :] = 0.0          # kv head 1: all logits zero -> uniform entmax
+    mask, logp, tau = O.route_sequence(q, kbar, B, 1.5, 8.0, 1.0, 2, 0.5)
+    for i in range(L):
+        n = i // B
+        assert not mask[:, i, n:].any()
+        if n == 0:
+            assert np.all(np.isinf(tau[:, i]) & (tau[:, i] > 0))
+            continue
+        assert mask[1, i, :n].all()
+        np.testing.assert_allclose(logp[1, i, :n], math.log(1.0 / n), atol=1e-12)
+        assert np.all(tau[2:, i] < 0)          # zero logits: threshold below 0
+    # kv head 0 is sparse somewhere (its logits are not flat)
+    assert not mask[0, L - 1, :(L - 1) // B].all() or (L - 1) // B == 1
+
+
+# ---------------------------------------------------------------- phase 2
+
+def _tiny(seed, L=40, Hq=4, Hkv=2, D=8):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((L, Hq, D)), rng.standard_normal((L, Hkv, D)),
+            rng.standard_normal((L, Hkv, D)), rng.standard_normal((Hkv, D)) * 0.3)
+
+
+def test_dense_form_equals_row_sparse_form():
+    q, k, v, qb = _tiny(11)
+    for alpha, sigma in ((1.5, 1.0), (2.0, 0.5), (1.25, 2.0), (1.0, 1.0)):
+        rs = O.prefill(q, k, v, qb, 8, alpha, 6.0, sigma)
+        dn = O.prefill(q, k, v, qb, 8, alpha, 6.0, sigma, dense=True)
+        np.testing.assert_allclose(rs["out"], dn["out"], atol=1e-12)
+        np.testing.assert_allclose(rs["lse"], dn["lse"], atol=1e-12)
+
+
+def test_all_active_sigma0_is_dense_causal_attention():
+    # alpha = 1 activates every chunk; sigma = 0 makes the prior uniform
+    q, k, v, qb = _tiny(12)
+    r = O.prefill(q, k, v, qb, 8, 1.0, 3.0, 0.0)
+    ref = sdpa64(q, k, v, causal=True, gqa=True)
+    np.testing.assert_allclose(r["out"], ref, atol=1e-12)
+
+
+def test_short_sequence_is_plain_causal_attention():
+    q, k, v, qb = _tiny(13, L=16)
+    r = O.prefill(q, k, v, qb, 16, 1.5, 50.0, 1.0)
+    np.testing.assert_allclose(r["out"], sdpa64(q, k, v, causal=True, gqa=True), atol=1e-12)
+
+
+def test_softmax_routing_prior_is_log_probability_bias():
+    # alpha = 1, sigma = 1, G = 1: bias of chunk c is log softmax_c(u); build
+    # the additive mask with torch ops and compare to torch SDPA
+    rng = np.random.default_rng(14)
+    L, B, D = 24, 4, 8
+    q = rng.standard_normal((L, 1, D))
+    k = rng.standard_normal((L, 1, D))
+    v = rng.standard_normal((L, 1, D))
+    qb = rng.standard_normal((1, D))
+    gamma, s = 5.0, 1 / math.sqrt(D)
+    r = O.prefill(q, k, v, qb, B, 1.0, gamma, 1.0)
+    kbar = torch.from_numpy(O.summarize(k, qb, B)[:, 0])      # [C, D]
+    tq = torch.from_numpy(q[:, 0])
+    mask = torch.full((L, L), -math.inf, dtype=torch.float64)
+    for i in range(L):
+        n = i // B
+        if n:
+            logw = torch.log_softmax(gamma * s * (kbar[:n] @ tq[i]), 0)
+            mask[i, :n * B] = torch.repeat_interleave(logw, B)
+        mask[i, n * B:i + 1] = 0.0
+    ref = sdpa64(q, k, v, mask=mask.numpy())
+    np.testing.assert_allclose(r["out"], ref, atol=1e-12)
+
+
+def test_single_selected_chunk_attends_that_chunk_and_diagonal():
+    # every head of the group routes to chunk 2 only: w_bar = 1, bias = 0
+    rng = np.random.default_rng(15)
+    L, B, D, G = 48, 8, 16, 2
+    q = rng.standard_normal((L, G, D))
+    k = rng.standard_normal((L, 1, D)) * 0.1
+    v = rng.standard_normal((L, 1, D))
+    d = np.zeros(D)
+    d[0] = 1.0
+    q[:, :, 0] = 5.0
+    k[2 * B:3 * B, 0, :] += 40.0 * d          # summary of chunk 2 ~ 40 e_0
+    r = O.prefill(q, k, v, np.zeros((1, D)), B, 1.5, 1.0, 1.0)
+    i = L - 1
+    assert list(np.nonzero(r["mask"][0, i])[0]) == [2]
+    idx = list(range(2 * B, 3 * B)) + list(range((i // B) * B, i + 1))
+    ref = sdpa64(q[i:i + 1], k[idx], v[idx], gqa=True)
+    np.testing.assert_allclose(r["out"][i], ref[0], atol=1e-12)
+
+
+def test_sigma0_is_block_sparse_attention_on_the_support():
+    q, k, v, qb = _tiny(16)
+    B = 8
+    r = O.prefill(q, k, v, qb, B, 1.5, 8.0, 0.0)
+    L = q.shape[0]
+    for h in range(2):
+        allowed = np.zeros((L, L), bool)
+        for i in range(L):
+            for c in range(i // B):
+                allowed[i, c * B:(c + 1) * B] = r["mask"][h, i, c]
+            allowed[i, (i // B) * B:i + 1] = True
+        m = np.where(allowed, 0.0, -np.inf)
+        ref = sdpa64(q[:, 2 * h:2 * h + 2], k[:, h:h + 1], v[:, h:h + 1], mask=m, gqa=True)
+        np.testing.assert_allclose(r["out"][:, 2 * h:2 * h + 2], ref, atol=1e-12)
+
+
+def test_prior_induced_softmax_is_the_kl_regularised_argmax():
+    # Fase 2: softmax maximises z.p - KL(p||u); DashAttention swaps u for g.
+    # Solve max z.p - KL(p||g) numerically with g = w_bar^sigma (diagonal 1)
+    # and check that the oracle's attention weights are that maximiser.
+    rng = np.random.default_rng(17)
+    L, B, D = 20, 4, 8
+    q = rng.standard_normal((L, 1, D))
+    k = rng.standard_normal((L, 1, D))
+    v = np.eye(L)[:, None, :]                  # v = one-hot: out = weights
+    qb = rng.standard_normal((1, D))
+    sigma, gamma = 0.7, 6.0
+    # pad q, k, q_bar with zero dims up to L so that v can be the L x L
+    # identity (out = attention weights); scores and summaries are unchanged
+    # because the attention scale is passed explicitly and the padding is 0
+    kk = np.concatenate([k, np.zeros((L, 1, L - D))], axis=2)
+    qq = np.concatenate([q, np.zeros((L, 1, L - D))], axis=2)
+    qbp = np.concatenate([qb, np.zeros((1, L - D))], 1)
+    s = 1 / math.sqrt(D)
+    r = O.prefill(qq, kk, v, qbp, B, 1.5, gamma, sigma, scale=s)
+    i = L - 1
+    route = O.route_position(qq[i], O.summarize(kk, qbp, B)[: i // B, 0], 1.5,
+                             gamma, s)
+    g = np.zeros(L)
+    for c in range(i // B):
+        g[c * B:(c + 1) * B] = route["wbar"][c] ** sigma
+    g[(i // B) * B:i + 1] = 1.0
+    z = (k[:, 0] @ q[i, 0]) / math.sqrt(D)
+    on = g > 0
+
+    def neg(p):
+        p = np.clip(p, 1e-300, None)
+        return -(p @ z[on] - np.sum(p * (np.log(p) - np.log(g[on]))))
+
+    n = int(on.sum())
+    res = scipy.optimize.minimize(neg, np.full(n, 1.0 / n), method="SLSQP",
+                                  bounds=[(0, 1)] * n,
+                                  constraints=[{"type": "eq", "fun": lambda p: p.sum() - 1}],
+                                  options=dict(ftol=1e-14, maxiter=2000))
+    w = r["out"][i, 0]
+    assert np.all(w[~on] == 0)
+    np.testing.assert_allclose(w[on], res.x, atol=2e-4)
+
+
+def test_decode_equals_last_prefill_row():
+    q, k, v, qb = _tiny(18, L=43)
+    B = 8
+    pre = O.prefill(q, k, v, qb, B, 1.5, 7.0, 1.0)
+    kbar = O.summarize(k, qb, B)
+    for L in (43, 40, 33, 9, 5):
+        dec = O.decode(q[L - 1], k, v, kbar, L, B, 1.5, 7.0, 1.0)
+        sub = O.prefill(q[:L], k[:L], v[:L], qb, B, 1.5, 7.0, 1.0, rows=[L - 1])
+        np.testing.assert_allclose(dec["out"], sub["out"][0], atol=1e-12)
+        np.testing.assert_allclose(dec["lse"], sub["lse"][:, 0], atol=1e-12)
+    np.testing.assert_allclose(O.decode(q[42], k, v, kbar, 43, B, 1.5, 7.0, 1.0)["out"],
+                               pre["out"][42], atol=1e-12)
+
+
+def test_varlen_is_independent_sequences():
+    rng = np.random.default_rng(19)
+    lens = [13, 30, 21]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = cu[-1]
+    q = rng.standard_normal((T, 2, 8))
+    k = rng.standard_normal((T, 1, 8))
+    v = rng.standard_normal((T, 1, 8))
+    qb = rng.standard_normal((1, 8))
+    res = O.prefill_varlen(q, k, v, qb, cu, 4, [1.25, 1.5, 2.0], 5.0, 1.0)
+    for s in range(3):
+        a, b = cu[s], cu[s + 1]
+        one = O.prefill(q[a:b], k[a:b], v[a:b], qb, 4, [1.25, 1.5, 2.0][s], 5.0, 1.0)
+        np.testing.assert_allclose(res[s]["out"], one["out"], atol=0)
+    kb = O.summarize_varlen(k, qb, cu, 4)
+    assert kb.shape[0] == sum(n // 4 for n in lens)
