@@ -19,7 +19,9 @@ from .dash_oracle import (  # noqa: F401
     sparsemax_sort,
     entmax15_sort,
     entmax,
+    entmax_rows,
     route_position,
+    routing_margin,
     route_sequence,
     attention_dense,
     attention_rows,

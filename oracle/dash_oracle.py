@@ -238,6 +238,64 @@ def entmax(u, alpha):
     return p, tau / (alpha - 1.0)
 
 
+def entmax_rows(U, n, alpha):
+    """alpha-entmax of many rows at once; row r uses its first n[r] entries.
+
+    The same bisection as ``entmax_threshold_bisect``, run for all rows in
+    lockstep (each row keeps its own bracket), followed by the same
+    closed-form cross-checks for alpha = 2 and alpha = 1.5.  Returns
+    (P [R, C] with zeros past n[r], tau_hat [R]): +inf for empty rows, -inf
+    for alpha = 1 (softmax).
+    """
+    U = np.asarray(U, dtype=F64)
+    R, C = U.shape
+    n = np.asarray(n, dtype=np.int64)
+    valid = np.arange(C)[None, :] < n[:, None]
+    P = np.zeros((R, C), dtype=F64)
+    tau_hat = np.full(R, math.inf, dtype=F64)
+    rows = np.nonzero(n > 0)[0]
+    if rows.size == 0:
+        return P, tau_hat
+    Ur = np.where(valid[rows], U[rows], -np.inf)
+    if alpha == 1.0:
+        mx = Ur.max(axis=1, keepdims=True)
+        z = np.where(valid[rows], np.exp(Ur - mx), 0.0)
+        P[rows] = z / z.sum(axis=1, keepdims=True)
+        tau_hat[rows] = -math.inf
+        return P, tau_hat
+    if alpha < 1.0:
+        raise ValueError("alpha must be >= 1")
+    x = (alpha - 1.0) * Ur
+    expo = 1.0 / (alpha - 1.0)
+    xmax = x.max(axis=1)
+    lo = xmax - 1.0
+    hi = xmax - n[rows].astype(F64) ** (1.0 - alpha)
+
+    def mass(t):
+        d = np.clip(x - t[:, None], 0.0, None)
+        return np.sum(d ** expo, axis=1)
+
+    for _ in range(4000):
+        mid = 0.5 * (lo + hi)
+        live = (lo < mid) & (mid < hi)
+        if not live.any():
+            break
+        up = mass(mid) >= 1.0
+        lo = np.where(live & up, mid, lo)
+        hi = np.where(live & ~up, mid, hi)
+    tau = 0.5 * (lo + hi)
+    Pr = np.clip(x - tau[:, None], 0.0, None) ** expo
+    Pr = Pr / Pr.sum(axis=1, keepdims=True)
+    if alpha in (2.0, 1.5):
+        for j, r in enumerate(rows):
+            u = U[r, :n[r]]
+            closed = sparsemax_sort(u)[1] if alpha == 2.0 else entmax15_sort(u)[1]
+            assert abs(closed - tau[j]) <= 1e-9 * max(1.0, abs(tau[j])), (closed, tau[j])
+    P[rows] = Pr
+    tau_hat[rows] = tau / (alpha - 1.0)
+    return P, tau_hat
+
+
 def route_position(q_group, kbar_h, alpha, gamma, scale):
     """Route one position for one KV group.
 
@@ -253,11 +311,9 @@ def route_position(q_group, kbar_h, alpha, gamma, scale):
     G = q_group.shape[0]
     n = kbar_h.shape[0]
     u = np.zeros((G, n), dtype=F64)
-    p = np.zeros((G, n), dtype=F64)
-    tau_hat = np.zeros(G, dtype=F64)
     for g in range(G):
         u[g] = routing_logits(q_group[g], kbar_h, gamma, scale)
-        p[g], tau_hat[g] = entmax(u[g], alpha)
+    p, tau_hat = entmax_rows(u, np.full(G, n), alpha)
     wbar = p.mean(axis=0) if n else np.zeros(0, dtype=F64)
     if alpha == 1.0:
         mask = np.ones(n, dtype=bool)
@@ -281,21 +337,64 @@ def route_sequence(q, kbar, B, alpha, gamma, sigma, G, scale, rows=None,
     L, Hq, D = q.shape
     Hkv = kbar.shape[1]
     S = num_slots if num_slots is not None else -(-L // B)
-    rows = range(L) if rows is None else rows
+    rows = np.arange(L) if rows is None else np.asarray(list(rows), dtype=np.int64)
     mask = np.zeros((Hkv, L, S), dtype=bool)
     logp = np.full((Hkv, L, S), -np.inf, dtype=F64)
     tau_hat = np.full((Hq, L), np.nan, dtype=F64)
-    for i in rows:
-        n = i // B
-        for h in range(Hkv):
-            r = route_position(q[i, h * G:(h + 1) * G, :], kbar[:n, h, :],
-                               alpha, gamma, scale)
-            tau_hat[h * G:(h + 1) * G, i] = r["tau_hat"]
-            mask[h, i, :n] = r["mask"]
-            on = r["mask"]
+    if rows.size == 0:
+        return mask, logp, tau_hat
+    C = int(rows.max()) // B          # routable chunks of the last row
+    ns = rows // B                    # routable chunks of each row
+    for h in range(Hkv):
+        # u[row, g, c] = gamma * s * <q[row, hG+g], kbar[c, h]>, c < n_row
+        u = np.zeros((rows.size, G, max(C, 1)), dtype=F64)
+        if C:
+            u[:, :, :C] = gamma * scale * np.einsum(
+                "rgd,cd->rgc", q[rows, h * G:(h + 1) * G, :], kbar[:C, h, :])
+        P, th = entmax_rows(u.reshape(rows.size * G, -1), np.repeat(ns, G), alpha)
+        P = P.reshape(rows.size, G, -1)
+        th = th.reshape(rows.size, G)
+        tau_hat[h * G:(h + 1) * G, rows] = th.T
+        wbar = P.mean(axis=1)                                  # [rows, C]
+        if alpha == 1.0:
+            on = np.arange(u.shape[2])[None, :] < ns[:, None]
+        else:
+            on = np.any(u > th[:, :, None], axis=1)
+            on &= np.arange(u.shape[2])[None, :] < ns[:, None]
+        for j, i in enumerate(rows):
+            nn = int(ns[j])
+            mask[h, i, :nn] = on[j, :nn]
+            sel = on[j, :nn]
             with np.errstate(divide="ignore"):
-                logp[h, i, :n][on] = sigma * np.log(r["wbar"][on])
+                logp[h, i, :nn][sel] = sigma * np.log(wbar[j, :nn][sel])
     return mask, logp, tau_hat
+
+
+def routing_margin(q, kbar, B, gamma, scale, G, tau_hat, rows, num_slots):
+    """Distance of each routing decision from its threshold.
+
+    For every KV head h, requested row i and routable chunk c < floor(i/B):
+    min over the G query heads of h of |u_{q,i,c} - tau_hat_{q,i}|, in logit
+    units (+inf elsewhere, and for softmax routing where nothing is
+    thresholded).  A decision closer than a numerical tolerance to its
+    threshold may legitimately come out either way in finite precision.
+    Returns [Hkv, len(rows), num_slots].
+    """
+    q = np.asarray(q, dtype=F64)
+    kbar = np.asarray(kbar, dtype=F64)
+    Hkv = kbar.shape[1]
+    out = np.full((Hkv, len(rows), num_slots), np.inf, dtype=F64)
+    for j, i in enumerate(rows):
+        n = i // B
+        if n == 0:
+            continue
+        for h in range(Hkv):
+            u = gamma * scale * (q[i, h * G:(h + 1) * G, :] @ kbar[:n, h, :].T)
+            th = tau_hat[h * G:(h + 1) * G, i]
+            if not np.all(np.isfinite(th)):
+                continue
+            out[h, j, :n] = np.min(np.abs(u - th[:, None]), axis=0)
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -310,14 +409,10 @@ def _row_keys_and_bias(i, B, mask_row, logp_row):
     floor(i / B) * B ... i with bias 0.
     """
     ci = i // B
-    idx, bias = [], []
-    for c in range(ci):
-        if mask_row[c]:
-            idx.extend(range(c * B, (c + 1) * B))
-            bias.extend([logp_row[c]] * B)
-    idx.extend(range(ci * B, i + 1))
-    bias.extend([0.0] * (i + 1 - ci * B))
-    return np.asarray(idx, dtype=np.int64), np.asarray(bias, dtype=F64)
+    act = [c for c in range(ci) if mask_row[c]]
+    idx = [np.arange(c * B, (c + 1) * B) for c in act] + [np.arange(ci * B, i + 1)]
+    bias = [np.full(B, logp_row[c]) for c in act] + [np.zeros(i + 1 - ci * B)]
+    return np.concatenate(idx).astype(np.int64), np.concatenate(bias).astype(F64)
 
 
 def attention_rows(q, k, v, mask, log_prior, B, scale, G, rows):
@@ -331,18 +426,19 @@ def attention_rows(q, k, v, mask, log_prior, B, scale, G, rows):
     k = np.asarray(k, dtype=F64)
     v = np.asarray(v, dtype=F64)
     Hq, D = q.shape[1], q.shape[2]
+    Hkv = k.shape[1]
     out = np.zeros((len(rows), Hq, D), dtype=F64)
     lse = np.zeros((Hq, len(rows)), dtype=F64)
     for r, i in enumerate(rows):
-        for qh in range(Hq):
-            h = qh // G
+        for h in range(Hkv):
             idx, bias = _row_keys_and_bias(i, B, mask[h, i], log_prior[h, i])
-            logits = scale * (k[idx, h, :] @ q[i, qh]) + bias
-            mx = logits.max()
+            qg = q[i, h * G:(h + 1) * G, :]                    # [G, D]
+            logits = scale * (qg @ k[idx, h, :].T) + bias[None, :]
+            mx = logits.max(axis=1, keepdims=True)
             w = np.exp(logits - mx)
-            ssum = w.sum()
-            out[r, qh] = (w / ssum) @ v[idx, h, :]
-            lse[qh, r] = mx + math.log(ssum)
+            ssum = w.sum(axis=1, keepdims=True)
+            out[r, h * G:(h + 1) * G] = (w / ssum) @ v[idx, h, :]
+            lse[h * G:(h + 1) * G, r] = mx[:, 0] + np.log(ssum[:, 0])
     return out, lse
 
 

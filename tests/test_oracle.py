@@ -205,6 +205,20 @@ def test_entmax_support_matches_brute_force(alpha):
             assert abs(tau_hat * (alpha - 1) - t) < 1e-10
 
 
+@pytest.mark.parametrize("alpha", [1.0, 1.25, 1.5, 2.0])
+def test_batched_rows_equal_single_row_entmax(alpha):
+    # the row-batched solver runs the same bisection per row in lockstep
+    rng = np.random.default_rng(20)
+    n = np.array([0, 1, 2, 7, 30, 30, 13])
+    U = rng.standard_normal((len(n), 30)) * 3
+    P, th = O.entmax_rows(U, n, alpha)
+    for r, nr in enumerate(n):
+        p, t = O.entmax(U[r, :nr], alpha)
+        np.testing.assert_allclose(P[r, :nr], p, atol=1e-14)
+        assert np.all(P[r, nr:] == 0)
+        assert t == th[r] or abs(t - th[r]) < 1e-14
+
+
 def test_entmax_alpha_to_one_is_softmax():
     u = np.array([1.0, 0.5, -1.0])
     sm = scipy.special.softmax(u)
