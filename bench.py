@@ -1,0 +1,295 @@
+#!/usr/bin/env python3
+"""Benchmark of the DashAttention forward hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  prefill of the 64K-token planted-needle sequence (32 query / 2 KV heads,
+  D = 128, B = 64, bf16, ~75% block sparsity): chunk summaries, alpha-entmax
+  routing, sparse attention -- the three launches dash_attn_prefill makes,
+  issued here as dash_summarize, dash_route and dash_attn_sparse so that each
+  kernel is timed with its own HIP events on the stream it runs on;
+  then one decode step for 16 sequences with 128K-token caches (cached
+  summaries, ~75% sparsity, split-K): dash_attn_decode.
+
+value  = prefill active TFLOP/s: 4 * D * sum over query heads and rows of
+         (B * active routed chunks + diagonal length), counted from the mask
+         the step produced, over the whole prefill (all three launches).
+decode = microseconds per decode step and per token, and active K/V GB/s.
+roofline: the sparse-attention kernel (the dominant one) against the bf16
+         MFMA peak; decode against HBM.
+cpu_baseline: the float64 NumPy oracle on a sample of the same prefill rows.
+Inputs are resident in HBM before the timed region starts.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("prefill TFLOP/s (active) + decode µs/token at 64K–128K, 75% sparsity; "
+          "% roofline")
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PMC_FILE = os.path.join(ROOT, "profiles", "prefill_attn_pmc.json")
+KERNEL_SOURCES = ["attn_prefill.hip", "attn_stage.h", "dash_device.h"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "sparse_hierarchical_attention_dash_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def popcounts(mask_i64):
+    """[..., W] int64 words -> [...] number of set bits."""
+    a = np.ascontiguousarray(mask_i64).view(np.uint8)
+    return np.unpackbits(a, axis=-1).reshape(mask_i64.shape[:-1] + (-1,)).sum(-1)
+
+
+def prefill_active_flops(pop, B, D, G):
+    """pop [Hkv, T] active routed chunks per (KV head, row) of one sequence."""
+    T = pop.shape[1]
+    diag = (np.arange(T) % B) + 1
+    per = B * pop.astype(np.int64) + diag[None, :]
+    return 4.0 * D * G * float(per.sum())
+
+
+def to_bf16_dev(a):
+    import torch
+    return torch.from_numpy(a).to(torch.bfloat16).cuda()
+
+
+def cpu_baseline(d, w, gamma, rows_n, seed=0):
+    """Time the oracle on a stratified sample of prefill rows; returns the
+    oracle's active TFLOP/s on that sample (summaries prorated per row)."""
+    import oracle as O
+    import torch
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    qx = torch.from_numpy(d["q"]).to(torch.bfloat16).to(torch.float64).numpy()
+    kx = torch.from_numpy(d["k"]).to(torch.bfloat16).to(torch.float64).numpy()
+    vx = torch.from_numpy(d["v"]).to(torch.bfloat16).to(torch.float64).numpy()
+    L = qx.shape[0]
+    rng = np.random.default_rng(seed)
+    edges = np.linspace(w.B, L, rows_n + 1).astype(int)
+    rows = sorted(int(rng.integers(a, max(a + 1, b))) for a, b in zip(edges[:-1], edges[1:]))
+    t0 = time.perf_counter()
+    kbar = O.summarize(kx, d["qbar"], w.B, to_bf16=True)
+    t_sum = time.perf_counter() - t0
+    G = w.Hq // w.Hkv
+    s = 1.0 / math.sqrt(w.D)
+    t0 = time.perf_counter()
+    mask, logp, _ = O.route_sequence(qx, kbar, w.B, w.alpha, gamma, w.sigma, G, s, rows=rows)
+    O.attention_rows(qx, kx, vx, mask, logp, w.B, s, G, rows)
+    t_rows = time.perf_counter() - t0
+    t = t_rows + t_sum * len(rows) / L
+    flops = 0.0
+    for i in rows:
+        for h in range(w.Hkv):
+            flops += 4.0 * w.D * G * (w.B * int(mask[h, i].sum()) + (i % w.B) + 1)
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": (f"{len(rows)} stratified rows of the {L}-token prefill (routing + "
+                       f"attention, float64 NumPy) plus their {len(rows)}/{L} share of the "
+                       f"chunk summaries; {t:.1f} s of CPU time"),
+            "seconds": t}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--prefill", default="prefill_64k_needles")
+    ap.add_argument("--decode", default="decode_128k")
+    ap.add_argument("--only", choices=["both", "prefill", "decode"], default="both")
+    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures a single GPU: this build has no multi-GPU path, so "
+              "--gpus must be 1 (sharding is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_hierarchical_attention_dash_amd import _lib as L
+    from sparse_hierarchical_attention_dash_amd import ops
+    from sparse_hierarchical_attention_dash_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    L.lib()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    do_pre = args.only in ("both", "prefill")
+    do_dec = args.only in ("both", "decode")
+
+    # ---------------------------------------------------------------- inputs
+    t0 = time.time()
+    if do_pre:
+        dp = W.make(args.prefill)
+        wp = dp["workload"]
+        q = to_bf16_dev(dp["q"])
+        k = to_bf16_dev(dp["k"])
+        v = to_bf16_dev(dp["v"])
+        qbar = torch.from_numpy(dp["qbar"]).cuda()
+        T = q.shape[0]
+        G = wp.Hq // wp.Hkv
+        shp = ops._seq_shape(q, wp.Hq, wp.Hkv, wp.B, None, None)
+        lay = L.layout(shp)
+        kbar = torch.empty((lay.summary_rows, wp.Hkv, wp.D), dtype=torch.bfloat16, device=dev)
+        mask = torch.empty((wp.Hkv, T, lay.mask_words), dtype=torch.int64, device=dev)
+        logp = torch.empty((wp.Hkv, T, lay.chunk_slots), dtype=torch.float32, device=dev)
+        out = torch.empty_like(q)
+        ws_route = torch.empty(256, dtype=torch.uint8, device=dev)
+        log(f"prefill inputs {wp.name}: T={T} Hq={wp.Hq} Hkv={wp.Hkv} D={wp.D} B={wp.B} "
+            f"({time.time() - t0:.1f}s)")
+    if do_dec:
+        dd = W.make(args.decode)
+        wd = dd["workload"]
+        qd = to_bf16_dev(dd["q"])
+        kc = to_bf16_dev(dd["k_cache"])
+        vc = to_bf16_dev(dd["v_cache"])
+        del dd["k_cache"], dd["v_cache"]
+        seqlens = torch.from_numpy(dd["seqlens"]).cuda()
+        cap = kc.shape[1]
+        # the summary cache is built once (summaries of complete chunks are fixed)
+        kbar_c = ops.summarize(kc.view(-1, wd.Hkv, wd.D), torch.from_numpy(dd["qbar"]).cuda(),
+                               wd.B, max_seqlen=cap).view(wd.batch, cap // wd.B, wd.Hkv, wd.D)
+        ws_dec = ops.decode_workspace(qd, kc, wd.B)
+        out_d = torch.empty_like(qd)
+        ab_d = torch.empty((wd.Hkv, wd.batch, (cap // wd.B + 63) // 64), dtype=torch.int64,
+                           device=dev)
+        log(f"decode inputs {wd.name}: batch={wd.batch} cache={cap} ({time.time() - t0:.1f}s)")
+    torch.cuda.synchronize()
+
+    def step(ev):
+        if do_pre:
+            ev[0].record(stream)
+            ops.summarize(k, qbar, wp.B, out=kbar, workspace=ws_route)
+            ev[1].record(stream)
+            ops.route(q, kbar, wp.Hkv, wp.B, alpha=wp.alpha, gamma=wp.gamma, sigma=wp.sigma,
+                      mask_out=mask, log_prior_out=logp, log_prior=True, workspace=ws_route)
+            ev[2].record(stream)
+            ops.attn_sparse(q, k, v, mask, logp, wp.B, out=out)
+            ev[3].record(stream)
+        if do_dec:
+            ev[4].record(stream)
+            ops.attn_decode(qd, kc, vc, seqlens, kbar_c, wd.B, alpha=wd.alpha, gamma=wd.gamma,
+                            sigma=wd.sigma, workspace=ws_dec, out=out_d)
+            ev[5].record(stream)
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for _ in range(args.warmup):
+        step(mk())
+    torch.cuda.synchronize()
+    evs = [mk() for _ in range(args.steps)]
+    wall0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for e in evs:
+        step(e)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(stop) / args.steps
+
+    res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": total_ms, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+    config = {"workload": " + ".join(x for x in (args.prefill if do_pre else None,
+                                                args.decode if do_dec else None) if x)}
+    if do_pre:
+        t_sum = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        t_route = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        t_attn = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+        t_pre = t_sum + t_route + t_attn
+        # parity of the staged launches with the fused entry point (untimed)
+        out2, _, ab2 = ops.attn_prefill(q, k, v, qbar, wp.B, alpha=wp.alpha, gamma=wp.gamma,
+                                        sigma=wp.sigma, return_active_blocks=True)
+        torch.cuda.synchronize()
+        assert torch.equal(ab2, mask) and torch.equal(out2, out), "staged != fused prefill"
+        pop = popcounts(mask.cpu().numpy())
+        flops = prefill_active_flops(pop, wp.B, wp.D, G)
+        routable = float(np.sum(np.arange(T) // wp.B)) * wp.Hkv
+        support = float(pop.sum()) / routable
+        tflops = flops / (t_pre * 1e-3) / 1e12
+        attn_tflops = flops / (t_attn * 1e-3) / 1e12
+        res.update(value=tflops, unit="TFLOP/s")
+        traffic = None
+        if os.path.exists(PMC_FILE):
+            pmc = json.load(open(PMC_FILE))
+            if pmc.get("kernel_hash") == kernel_hash() and pmc.get("workload") == wp.name:
+                traffic = pmc.get("hbm_bytes_per_launch")
+        res["roofline"] = {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
+                           "traffic": traffic, "kernel": "prefill_attn_bf16_kernel<128>",
+                           "algorithmic_flops_per_launch": flops,
+                           "avg_launch_ms": t_attn}
+        config["prefill"] = {"workload": wp.name, "tokens": T, "q_heads": wp.Hq,
+                             "kv_heads": wp.Hkv, "head_dim": wp.D, "chunk": wp.B,
+                             "alpha": wp.alpha, "gamma": wp.gamma, "sigma": wp.sigma,
+                             "needles": wp.needles}
+        res["prefill"] = {"ms": t_pre, "summarize_ms": t_sum, "route_ms": t_route,
+                          "attention_ms": t_attn, "active_flops": flops,
+                          "block_support": support, "block_sparsity": 1.0 - support,
+                          "dense_causal_flops": 4.0 * wp.D * wp.Hq * T * (T + 1) / 2,
+                          "attention_tflops": attn_tflops}
+    if do_dec:
+        t_dec = float(np.mean([e[4].elapsed_time(e[5]) for e in evs]))
+        ops.attn_decode(qd, kc, vc, seqlens, kbar_c, wd.B, alpha=wd.alpha, gamma=wd.gamma,
+                        sigma=wd.sigma, workspace=ws_dec, out=out_d)
+        # active blocks of the decode step (untimed run returning the mask)
+        _, _, abd = ops.attn_decode(qd, kc, vc, seqlens, kbar_c, wd.B, alpha=wd.alpha,
+                                    gamma=wd.gamma, sigma=wd.sigma, workspace=ws_dec,
+                                    return_active_blocks=True)
+        torch.cuda.synchronize()
+        popd = popcounts(abd.cpu().numpy())                  # [Hkv, batch]
+        sl = dd["seqlens"].astype(np.int64)
+        diag = ((sl - 1) % wd.B) + 1
+        kv_bytes = float(np.sum(wd.B * popd + diag[None, :])) * wd.D * 2 * 2
+        gbs = kv_bytes / (t_dec * 1e-3) / 1e9
+        routable = float(np.sum((sl - 1) // wd.B)) * wd.Hkv
+        res["decode"] = {"us_per_step": t_dec * 1e3, "us_per_token": t_dec * 1e3 / wd.batch,
+                         "active_kv_bytes": kv_bytes, "GB_per_s": gbs,
+                         "block_support": float(popd.sum()) / routable,
+                         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                                      "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                                      "traffic": None}}
+        config["decode"] = {"workload": wd.name, "batch": wd.batch, "cache_tokens": cap,
+                            "q_heads": wd.Hq, "kv_heads": wd.Hkv, "head_dim": wd.D,
+                            "chunk": wd.B, "alpha": wd.alpha, "gamma": wd.gamma}
+        if not do_pre:
+            res.update(value=t_dec * 1e3 / wd.batch, unit="us/token", higher_is_better=False)
+    res["config"] = config
+    res["wall_s"] = wall
+    if do_pre and not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        res["cpu_baseline"] = cpu_baseline(dp, wp, wp.gamma, args.cpu_rows)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

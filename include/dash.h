@@ -1,0 +1,226 @@
+/*
+ * dash.h -- C ABI of the DashAttention forward path on MI355X (gfx950).
+ *
+ * DashAttention has three phases; each entry point below runs one or more of
+ * them on the GPU.  The phases are defined in the technical summary
+ * "Technische Samenvatting: DashAttention" (gist.science/nl/paper/2605.18753):
+ *   phase 0  "Fase 0: Lokale Chunk Samenvatting"   learned-query chunk summaries
+ *   phase 1  "Fase 1: Entmax Chunk Routering"      alpha-entmax routing, GQA
+ *            averaging, equation  w_hat = alpha-entmax(gamma * z_bar)
+ *   phase 2  "Fase 2: Prior-Geinduceerde Spaarzame Softmax"  prior-induced
+ *            sparse softmax over the active chunks plus the diagonal branch
+ * and the interface (q, k, v, a per-head summary query "head_cls", chunk_size,
+ * enable_gqa, an optional active_blocks output) in the aiexpert.news article
+ * "DashAttention alcanza 75% de dispersidad ...", interface paragraph.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Memory.   Every tensor argument is a DEVICE pointer to contiguous row-major
+ *           memory owned by the caller.  The library never allocates or frees
+ *           memory; scratch space comes from a caller-provided workspace of at
+ *           least dash_workspace_size(op, shape) bytes (256-byte aligned).
+ *           q/k/v/out/summaries must be 16-byte aligned.
+ * Layout.   Token-major packed "THD": q [T, Hq, D], k and v [T, Hkv, D].
+ *           Sequence s occupies rows cu_seqlens[s] .. cu_seqlens[s+1]-1, or
+ *           rows s*max_seqlen .. (s+1)*max_seqlen-1 when cu_seqlens is NULL.
+ *           Chunk c of a sequence holds its tokens c*B .. c*B+B-1; only
+ *           complete chunks have a summary.  Summaries of all sequences are
+ *           packed in sequence order: k_bar [sum_s floor(L_s/B), Hkv, D].
+ * Heads.    With enable_gqa = 0, Hq must equal Hkv.  With enable_gqa = 1,
+ *           Hq must be a multiple of Hkv; query head q reads KV head
+ *           floor(q / (Hq/Hkv)) (the repeat-interleave convention).
+ * Routing.  A query at local position i routes to the chunks c < floor(i/B)
+ *           of its own sequence; its own chunk is the diagonal branch,
+ *           attended causally with bias 0.  The mask row of (KV head h,
+ *           token t) is W = ceil(C_slots/64) 64-bit words, chunk c in bit
+ *           (c % 64) of word c / 64 (least significant bit first), with
+ *           C_slots = ceil(max_seqlen / B).  Bits c >= floor(i/B) are zero.
+ * Streams.  Every call only enqueues work on `stream` (a hipStream_t; NULL is
+ *           the default stream) and never synchronises.
+ * Errors.   All host-visible arguments are checked before any HIP call; on
+ *           an error nothing is enqueued and nothing is written.  A failed
+ *           kernel launch returns DASH_ERR_HIP.  Device-side contents
+ *           (cu_seqlens, seqlens, alpha_per_seq) are preconditions and are
+ *           not checked.  The library holds no mutable global state, so calls
+ *           from several host threads are safe; calls that share output or
+ *           workspace buffers must be ordered by the caller.
+ * Supported: head_dim in {64, 128}; chunk_size in {64, 128}; dtype bf16 or
+ *           fp32 (q, k, v, summaries and out share it; accumulation is fp32);
+ *           C_slots <= 2048; alpha in [1, 2].  In bf16 the GQA group size
+ *           Hq/Hkv must be 1, 2, 4, 8 or a multiple of 16.  Anything else
+ *           returns DASH_ERR_UNSUPPORTED.
+ */
+#ifndef DASH_H_
+#define DASH_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DASH_ABI_VERSION 1
+
+typedef enum {
+  DASH_OK = 0,
+  DASH_ERR_INVALID_ARGUMENT = 1,
+  DASH_ERR_UNSUPPORTED = 2,
+  DASH_ERR_WORKSPACE_TOO_SMALL = 3,
+  DASH_ERR_HIP = 4
+} dash_status;
+
+typedef enum { DASH_F32 = 0, DASH_BF16 = 1 } dash_dtype;
+
+typedef enum {
+  DASH_OP_SUMMARIZE = 0,
+  DASH_OP_ROUTE = 1,
+  DASH_OP_PREFILL = 2,
+  DASH_OP_DECODE = 3,
+  DASH_OP_SPARSE = 4
+} dash_op;
+
+typedef struct {
+  int32_t num_seqs;            /* sequences (prefill) or batch entries (decode)   */
+  int32_t max_seqlen;          /* fixed length, or an upper bound on every length;
+                                  decode: cache capacity per sequence             */
+  int64_t total_tokens;        /* T, rows of q/k/v; must be num_seqs*max_seqlen
+                                  when cu_seqlens is NULL; ignored by decode      */
+  const int32_t* cu_seqlens;   /* device [num_seqs+1] prefix sums, or NULL        */
+  int32_t num_q_heads;         /* Hq  */
+  int32_t num_kv_heads;        /* Hkv */
+  int32_t head_dim;            /* D   */
+  int32_t chunk_size;          /* B   */
+  int32_t dtype;               /* dash_dtype of q, k, v, summaries and out        */
+} dash_shape;
+
+/* Derived sizes of a shape, for sizing caller buffers.  Returns DASH_OK or
+ * the status the shape itself would produce. */
+typedef struct {
+  int64_t summary_rows;        /* rows of k_bar the caller must provide: floor(T/B)
+                                  (prefill), num_seqs*max_seqlen/B (decode cache) */
+  int32_t chunk_slots;         /* C_slots = ceil(max_seqlen / B)                  */
+  int32_t mask_words;          /* W = ceil(C_slots / 64)                          */
+  int32_t group_size;          /* G = Hq / Hkv                                    */
+} dash_layout;
+
+dash_status dash_get_layout(const dash_shape* shape, int enable_gqa, dash_layout* out);
+
+/* Phase 0 ("Fase 0: Lokale Chunk Samenvatting").  For every KV head h and
+ * complete chunk c of every sequence, a learned query q_bar[h] attends to the
+ * chunk's keys with local scaled dot-product attention (scale 1/sqrt(D)), the
+ * keys serving as values:
+ *     k_bar[c,h] = sum_t softmax_t(<q_bar[h], k[cB+t,h]> / sqrt(D)) k[cB+t,h].
+ * q_bar = 0 gives the mean of the chunk's keys.  Accumulation is fp32; a bf16
+ * result is rounded to nearest even once.
+ *   k     [T, Hkv, D] dtype                  (input)
+ *   qbar  [Hkv, D] fp32                      (input)
+ *   kbar  [>= summary_rows, Hkv, D] dtype    (output; rows past the last
+ *                                             complete chunk are not written)
+ * For a decode cache pass the cache as a fixed-length batch
+ * (cu_seqlens = NULL, max_seqlen = capacity, total_tokens = batch*capacity);
+ * the result is then k_bar [batch, capacity/B, Hkv, D]. */
+dash_status dash_summarize(const dash_shape* shape, const void* k, const float* qbar,
+                           void* kbar, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* Phase 1 ("Fase 1: Entmax Chunk Routering").  For token t at local position
+ * i and query head q (KV head h):
+ *     u_c     = gamma * s * <q[t,q], k_bar[c,h]>            c < floor(i/B)
+ *     p       = alpha-entmax(u):  p_c = [(alpha-1) u_c - tau]_+^(1/(alpha-1)),
+ *               sum_c p_c = 1 (alpha = 1: softmax; every chunk active)
+ *     w_bar_c = mean over the G query heads of KV head h of p_c
+ *     bit_c   = OR over those heads of [u_c > tau_hat],  tau_hat = tau/(alpha-1)
+ *     log_prior_c = sigma * log(w_bar_c) where bit_c = 1
+ * s = softmax_scale, or 1/sqrt(D) when softmax_scale <= 0.
+ *   q              [T, Hq, D] dtype                (input)
+ *   kbar           [summary_rows, Hkv, D] dtype    (input)
+ *   alpha          used when alpha_per_seq is NULL; 1 <= alpha <= 2
+ *   alpha_per_seq  device fp32 [num_seqs] or NULL
+ *   active_blocks  [Hkv, T, W] uint64              (output, required)
+ *   log_prior      [Hkv, T, C_slots] fp32 or NULL  (output; slots c < floor(i/B)
+ *                                                   are written, -inf where the
+ *                                                   bit is 0)
+ *   tau            [Hq, T] fp32 or NULL            (output: tau_hat in u units;
+ *                                                   +inf when no chunk is
+ *                                                   routable, -inf for alpha=1) */
+dash_status dash_route(const dash_shape* shape, const void* q, const void* kbar,
+                       float alpha, const float* alpha_per_seq, float gamma,
+                       float sigma, float softmax_scale, int enable_gqa,
+                       uint64_t* active_blocks, float* log_prior, float* tau,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Phases 0-2, causal prefill ("Fase 2: Prior-Geinduceerde Spaarzame Softmax").
+ * Runs dash_summarize and dash_route into the workspace, then for every token
+ * t at position i and query head q:
+ *     o[t,q] = sum_j softmax_j(s <q[t,q], k[j,h]> + b_j) v[j,h]
+ * over the keys j of the active routed chunks (b_j = log_prior of j's chunk)
+ * and the causal diagonal chunk floor(i/B)*B <= j <= i (b_j = 0).
+ *   q, k, v        [T, Hq|Hkv, D] dtype            (input)
+ *   qbar           [Hkv, D] fp32                   (input)
+ *   out            [T, Hq, D] dtype                (output)
+ *   lse            [Hq, T] fp32 or NULL            (output, natural log of the
+ *                                                   softmax denominator)
+ *   active_blocks  [Hkv, T, W] uint64 or NULL      (output) */
+dash_status dash_attn_prefill(const dash_shape* shape, const void* q, const void* k,
+                              const void* v, const float* qbar, float alpha,
+                              const float* alpha_per_seq, float gamma, float sigma,
+                              float softmax_scale, int enable_gqa, void* out,
+                              float* lse, uint64_t* active_blocks, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Phase 2 alone ("Fase 2: Prior-Geinduceerde Spaarzame Softmax", the
+ * FlashAttention-style kernel that walks a bit-packed mask and adds the
+ * routing bias before the softmax): the attention step of dash_attn_prefill
+ * for a given routing.  dash_attn_prefill is exactly dash_summarize, then
+ * dash_route, then this call.
+ *   q, k, v        [T, Hq|Hkv, D] dtype            (input)
+ *   active_blocks  [Hkv, T, W] uint64              (input, as dash_route writes it;
+ *                                                   bits c >= floor(i/B) must be 0)
+ *   log_prior      [Hkv, T, C_slots] fp32          (input; read where a bit is set)
+ *   out            [T, Hq, D] dtype                (output)
+ *   lse            [Hq, T] fp32 or NULL            (output)
+ * Needs no workspace (dash_workspace_size(DASH_OP_SPARSE, ...) is 0). */
+dash_status dash_attn_sparse(const dash_shape* shape, const void* q, const void* k,
+                             const void* v, const uint64_t* active_blocks,
+                             const float* log_prior, float softmax_scale, int enable_gqa,
+                             void* out, float* lse, void* stream);
+
+/* One incremental decode step: each batch entry b has one new query whose
+ * key and value are already written at position seqlens[b]-1 of its cache.
+ * Routes that query against the cached summaries of its complete chunks
+ * (summaries are fixed and cached once a chunk is complete, "Fase 0",
+ * Efficientie bullet) and attends as dash_attn_prefill does for its last row.
+ * shape: num_seqs = batch, max_seqlen = cache capacity (a multiple of B),
+ * cu_seqlens = NULL.
+ *   q              [batch, Hq, D] dtype            (input)
+ *   k_cache,v_cache[batch, capacity, Hkv, D] dtype (input)
+ *   seqlens        device int32 [batch], 1 <= seqlens[b] <= capacity
+ *   kbar_cache     [batch, capacity/B, Hkv, D] dtype (input; rows c <
+ *                                                   floor((seqlens[b]-1)/B) read)
+ *   out            [batch, Hq, D] dtype            (output)
+ *   lse            [Hq, batch] fp32 or NULL        (output)
+ *   active_blocks  [Hkv, batch, W] uint64 or NULL  (output) */
+dash_status dash_attn_decode(const dash_shape* shape, const void* q,
+                             const void* k_cache, const void* v_cache,
+                             const int32_t* seqlens, const void* kbar_cache,
+                             float alpha, float gamma, float sigma,
+                             float softmax_scale, int enable_gqa, void* out,
+                             float* lse, uint64_t* active_blocks, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Workspace bytes that `op` needs for `shape` (0 when none); the same
+ * enable_gqa / optional-output choices do not change it. */
+size_t dash_workspace_size(int op, const dash_shape* shape);
+
+/* Static description of a status code; never NULL. */
+const char* dash_status_string(dash_status status);
+
+/* DASH_ABI_VERSION of the built library. */
+int dash_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DASH_H_ */

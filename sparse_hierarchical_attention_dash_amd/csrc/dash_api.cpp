@@ -1,0 +1,368 @@
+// C ABI of the DashAttention forward path (include/dash.h): argument checks,
+// workspace layout and kernel dispatch.  Every argument visible on the host is
+// checked before the first HIP call; nothing here allocates or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/dash.h"
+#include "dash_internal.h"
+
+namespace {
+
+using dash::Geom;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape checks shared by every entry point.  Fills `g` on success.
+dash_status check_shape(const dash_shape* s, int enable_gqa, bool decode, Geom& g) {
+  if (!s) return DASH_ERR_INVALID_ARGUMENT;
+  if (s->num_seqs < 0 || s->max_seqlen < 0 || s->num_q_heads <= 0 || s->num_kv_heads <= 0 ||
+      s->head_dim <= 0 || s->chunk_size <= 0)
+    return DASH_ERR_INVALID_ARGUMENT;
+  if (s->dtype != DASH_F32 && s->dtype != DASH_BF16) return DASH_ERR_UNSUPPORTED;
+  if (s->num_seqs > 65535 || s->num_kv_heads > 65535) return DASH_ERR_UNSUPPORTED;
+  if (s->head_dim != 64 && s->head_dim != 128) return DASH_ERR_UNSUPPORTED;
+  if (s->chunk_size != 64 && s->chunk_size != 128) return DASH_ERR_UNSUPPORTED;
+  if (enable_gqa) {
+    if (s->num_q_heads % s->num_kv_heads) return DASH_ERR_INVALID_ARGUMENT;
+  } else if (s->num_q_heads != s->num_kv_heads) {
+    return DASH_ERR_INVALID_ARGUMENT;
+  }
+  const int G = s->num_q_heads / s->num_kv_heads;
+  if (s->dtype == DASH_BF16) {
+    const bool small = (G == 1 || G == 2 || G == 4 || G == 8);
+    const bool big = (G >= 16 && G % 16 == 0 && ((G / 16) & (G / 16 - 1)) == 0 && G <= 256);
+    if (!small && !big) return DASH_ERR_UNSUPPORTED;
+    if (decode && G > 64) return DASH_ERR_UNSUPPORTED;
+  }
+  const int64_t C_slots = ((int64_t)s->max_seqlen + s->chunk_size - 1) / s->chunk_size;
+  if (C_slots > 2048) return DASH_ERR_UNSUPPORTED;
+  if (decode) {
+    if (s->cu_seqlens) return DASH_ERR_INVALID_ARGUMENT;
+    if (s->max_seqlen % s->chunk_size) return DASH_ERR_INVALID_ARGUMENT;
+  } else {
+    if (s->total_tokens < 0) return DASH_ERR_INVALID_ARGUMENT;
+    if (!s->cu_seqlens && s->total_tokens != (int64_t)s->num_seqs * s->max_seqlen)
+      return DASH_ERR_INVALID_ARGUMENT;
+    if (s->total_tokens > (int64_t)INT32_MAX) return DASH_ERR_UNSUPPORTED;
+  }
+  g.num_seqs = s->num_seqs;
+  g.max_seqlen = s->max_seqlen;
+  g.T = decode ? s->num_seqs : s->total_tokens;
+  g.cu_seqlens = s->cu_seqlens;
+  g.cu_chunks = nullptr;
+  g.Hq = s->num_q_heads;
+  g.Hkv = s->num_kv_heads;
+  g.G = G;
+  g.D = s->head_dim;
+  g.B = s->chunk_size;
+  g.C_slots = (int)C_slots;
+  g.W = (int)((C_slots + 63) / 64);
+  g.bf16 = (s->dtype == DASH_BF16);
+  return DASH_OK;
+}
+
+bool finite(float x) { return std::isfinite(x); }
+
+dash_status check_routing(float alpha, float gamma, float sigma, float scale) {
+  if (!finite(alpha) || !finite(gamma) || !finite(sigma) || std::isnan(scale))
+    return DASH_ERR_INVALID_ARGUMENT;
+  if (alpha < 1.f) return DASH_ERR_INVALID_ARGUMENT;
+  if (alpha > 2.f) return DASH_ERR_UNSUPPORTED;
+  if (gamma <= 0.f || sigma < 0.f) return DASH_ERR_INVALID_ARGUMENT;
+  return DASH_OK;
+}
+
+float eff_scale(const Geom& g, float scale) {
+  return scale > 0.f ? scale : 1.f / std::sqrt((float)g.D);
+}
+
+size_t elt(const Geom& g) { return g.bf16 ? 2 : 4; }
+
+// Workspace layouts (offsets in bytes; every piece 256-byte aligned).
+struct PrefillWs {
+  size_t cu_chunks, kbar, mask, logp, total;
+};
+PrefillWs prefill_ws(const Geom& g) {
+  PrefillWs w{};
+  size_t o = 0;
+  w.cu_chunks = o;
+  o += g.cu_seqlens ? align_up(sizeof(int32_t) * (g.num_seqs + 1)) : 0;
+  w.kbar = o;
+  o += align_up((size_t)(g.T / g.B) * g.Hkv * g.D * elt(g));
+  w.mask = o;
+  o += align_up((size_t)g.Hkv * g.T * g.W * 8);
+  w.logp = o;
+  o += align_up((size_t)g.Hkv * g.T * g.C_slots * 4);
+  w.total = o;
+  return w;
+}
+struct DecodeWs {
+  size_t mask, logp, acc, ml, total;
+  int nsplit;
+};
+DecodeWs decode_ws(const Geom& g) {
+  DecodeWs w{};
+  w.nsplit = dash::decode_num_splits(g);
+  size_t o = 0;
+  w.mask = o;
+  o += align_up((size_t)g.Hkv * g.num_seqs * g.W * 8);
+  w.logp = o;
+  o += align_up((size_t)g.Hkv * g.num_seqs * g.C_slots * 4);
+  w.acc = o;
+  o += align_up((size_t)g.num_seqs * g.Hkv * w.nsplit * g.G * g.D * 4);
+  w.ml = o;
+  o += align_up((size_t)g.num_seqs * g.Hkv * w.nsplit * g.G * 2 * 4);
+  w.total = o;
+  return w;
+}
+size_t meta_ws(const Geom& g) {
+  return g.cu_seqlens ? align_up(sizeof(int32_t) * (g.num_seqs + 1)) : 0;
+}
+
+dash_status check_ws(void* ws, size_t have, size_t need) {
+  if (have < need) return DASH_ERR_WORKSPACE_TOO_SMALL;
+  if (need && !ws) return DASH_ERR_INVALID_ARGUMENT;
+  if (need && (reinterpret_cast<uintptr_t>(ws) % kAlign)) return DASH_ERR_INVALID_ARGUMENT;
+  return DASH_OK;
+}
+
+char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+#define DASH_HIP(call)                              \
+  do {                                              \
+    if ((call) != hipSuccess) return DASH_ERR_HIP;  \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int dash_abi_version(void) { return DASH_ABI_VERSION; }
+
+const char* dash_status_string(dash_status s) {
+  switch (s) {
+    case DASH_OK: return "ok";
+    case DASH_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case DASH_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DASH_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case DASH_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+dash_status dash_get_layout(const dash_shape* shape, int enable_gqa, dash_layout* out) {
+  if (!out) return DASH_ERR_INVALID_ARGUMENT;
+  Geom g;
+  dash_status st = check_shape(shape, enable_gqa, false, g);
+  if (st != DASH_OK) return st;
+  out->summary_rows = g.T / g.B;
+  out->chunk_slots = g.C_slots;
+  out->mask_words = g.W;
+  out->group_size = g.G;
+  return DASH_OK;
+}
+
+size_t dash_workspace_size(int op, const dash_shape* shape) {
+  Geom g;
+  const bool decode = (op == DASH_OP_DECODE);
+  if (check_shape(shape, 1, decode, g) != DASH_OK) return 0;
+  switch (op) {
+    case DASH_OP_SUMMARIZE:
+    case DASH_OP_ROUTE: return meta_ws(g);
+    case DASH_OP_PREFILL: return prefill_ws(g).total;
+    case DASH_OP_DECODE: return decode_ws(g).total;
+    case DASH_OP_SPARSE: return 0;
+  }
+  return 0;
+}
+
+dash_status dash_summarize(const dash_shape* shape, const void* k, const float* qbar,
+                           void* kbar, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  Geom g;
+  dash_status st = check_shape(shape, 1, false, g);
+  if (st != DASH_OK) return st;
+  if (!k || !qbar || !kbar) return DASH_ERR_INVALID_ARGUMENT;
+  if (!aligned16(k) || !aligned16(qbar) || !aligned16(kbar)) return DASH_ERR_INVALID_ARGUMENT;
+  const size_t need = meta_ws(g);
+  if ((st = check_ws(workspace, workspace_bytes, need)) != DASH_OK) return st;
+  if (g.T == 0 || g.num_seqs == 0) return DASH_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (g.cu_seqlens) {
+    g.cu_chunks = reinterpret_cast<int32_t*>(workspace);
+    DASH_HIP(dash::launch_varlen_meta(g.cu_seqlens, g.num_seqs, g.B,
+                                      reinterpret_cast<int32_t*>(workspace), s));
+  }
+  DASH_HIP(dash::launch_summarize(g, k, qbar, kbar, s));
+  return DASH_OK;
+}
+
+dash_status dash_route(const dash_shape* shape, const void* q, const void* kbar, float alpha,
+                       const float* alpha_per_seq, float gamma, float sigma,
+                       float softmax_scale, int enable_gqa, uint64_t* active_blocks,
+                       float* log_prior, float* tau, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  Geom g;
+  dash_status st = check_shape(shape, enable_gqa, false, g);
+  if (st != DASH_OK) return st;
+  if ((st = check_routing(alpha, gamma, sigma, softmax_scale)) != DASH_OK) return st;
+  if (!q || !kbar || !active_blocks) return DASH_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(kbar)) return DASH_ERR_INVALID_ARGUMENT;
+  const size_t need = meta_ws(g);
+  if ((st = check_ws(workspace, workspace_bytes, need)) != DASH_OK) return st;
+  if (g.T == 0 || g.num_seqs == 0) return DASH_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (g.cu_seqlens) {
+    g.cu_chunks = reinterpret_cast<int32_t*>(workspace);
+    DASH_HIP(dash::launch_varlen_meta(g.cu_seqlens, g.num_seqs, g.B,
+                                      reinterpret_cast<int32_t*>(workspace), s));
+  }
+  dash::RouteParams p;
+  p.q = q;
+  p.kbar = kbar;
+  p.alpha = alpha;
+  p.alpha_per_seq = alpha_per_seq;
+  p.gamma_scale = gamma * eff_scale(g, softmax_scale);
+  p.sigma = sigma;
+  p.mask = active_blocks;
+  p.log_prior = log_prior;
+  p.tau = tau;
+  p.rows = g.T;
+  DASH_HIP(dash::launch_route(g, p, s));
+  return DASH_OK;
+}
+
+dash_status dash_attn_prefill(const dash_shape* shape, const void* q, const void* k,
+                              const void* v, const float* qbar, float alpha,
+                              const float* alpha_per_seq, float gamma, float sigma,
+                              float softmax_scale, int enable_gqa, void* out, float* lse,
+                              uint64_t* active_blocks, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  Geom g;
+  dash_status st = check_shape(shape, enable_gqa, false, g);
+  if (st != DASH_OK) return st;
+  if ((st = check_routing(alpha, gamma, sigma, softmax_scale)) != DASH_OK) return st;
+  if (!q || !k || !v || !qbar || !out) return DASH_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(qbar))
+    return DASH_ERR_INVALID_ARGUMENT;
+  const PrefillWs w = prefill_ws(g);
+  if ((st = check_ws(workspace, workspace_bytes, w.total)) != DASH_OK) return st;
+  if (g.T == 0 || g.num_seqs == 0) return DASH_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (g.cu_seqlens) {
+    g.cu_chunks = reinterpret_cast<int32_t*>(at(workspace, w.cu_chunks));
+    DASH_HIP(dash::launch_varlen_meta(g.cu_seqlens, g.num_seqs, g.B,
+                                      const_cast<int32_t*>(g.cu_chunks), s));
+  }
+  void* kbar = at(workspace, w.kbar);
+  uint64_t* mask = active_blocks ? active_blocks : reinterpret_cast<uint64_t*>(at(workspace, w.mask));
+  float* logp = reinterpret_cast<float*>(at(workspace, w.logp));
+  DASH_HIP(dash::launch_summarize(g, k, qbar, kbar, s));
+  dash::RouteParams rp;
+  rp.q = q;
+  rp.kbar = kbar;
+  rp.alpha = alpha;
+  rp.alpha_per_seq = alpha_per_seq;
+  rp.gamma_scale = gamma * eff_scale(g, softmax_scale);
+  rp.sigma = sigma;
+  rp.mask = mask;
+  rp.log_prior = logp;
+  rp.tau = nullptr;
+  rp.rows = g.T;
+  DASH_HIP(dash::launch_route(g, rp, s));
+  dash::PrefillParams pp;
+  pp.q = q;
+  pp.k = k;
+  pp.v = v;
+  pp.mask = mask;
+  pp.log_prior = logp;
+  pp.out = out;
+  pp.lse = lse;
+  pp.scale = eff_scale(g, softmax_scale);
+  DASH_HIP(dash::launch_prefill_attn(g, pp, s));
+  return DASH_OK;
+}
+
+dash_status dash_attn_sparse(const dash_shape* shape, const void* q, const void* k,
+                             const void* v, const uint64_t* active_blocks,
+                             const float* log_prior, float softmax_scale, int enable_gqa,
+                             void* out, float* lse, void* stream) {
+  Geom g;
+  dash_status st = check_shape(shape, enable_gqa, false, g);
+  if (st != DASH_OK) return st;
+  if (std::isnan(softmax_scale)) return DASH_ERR_INVALID_ARGUMENT;
+  if (!q || !k || !v || !active_blocks || !log_prior || !out) return DASH_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return DASH_ERR_INVALID_ARGUMENT;
+  if (g.T == 0 || g.num_seqs == 0) return DASH_OK;
+  dash::PrefillParams pp;
+  pp.q = q;
+  pp.k = k;
+  pp.v = v;
+  pp.mask = active_blocks;
+  pp.log_prior = log_prior;
+  pp.out = out;
+  pp.lse = lse;
+  pp.scale = eff_scale(g, softmax_scale);
+  DASH_HIP(dash::launch_prefill_attn(g, pp, static_cast<hipStream_t>(stream)));
+  return DASH_OK;
+}
+
+dash_status dash_attn_decode(const dash_shape* shape, const void* q, const void* k_cache,
+                             const void* v_cache, const int32_t* seqlens,
+                             const void* kbar_cache, float alpha, float gamma, float sigma,
+                             float softmax_scale, int enable_gqa, void* out, float* lse,
+                             uint64_t* active_blocks, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  Geom g;
+  dash_status st = check_shape(shape, enable_gqa, true, g);
+  if (st != DASH_OK) return st;
+  if ((st = check_routing(alpha, gamma, sigma, softmax_scale)) != DASH_OK) return st;
+  if (!q || !k_cache || !v_cache || !seqlens || !kbar_cache || !out)
+    return DASH_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(kbar_cache) ||
+      !aligned16(out))
+    return DASH_ERR_INVALID_ARGUMENT;
+  const DecodeWs w = decode_ws(g);
+  if ((st = check_ws(workspace, workspace_bytes, w.total)) != DASH_OK) return st;
+  if (g.num_seqs == 0) return DASH_OK;
+  if (g.max_seqlen == 0) return DASH_ERR_INVALID_ARGUMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint64_t* mask = active_blocks ? active_blocks : reinterpret_cast<uint64_t*>(at(workspace, w.mask));
+  float* logp = reinterpret_cast<float*>(at(workspace, w.logp));
+  dash::RouteParams rp;
+  rp.q = q;
+  rp.kbar = kbar_cache;
+  rp.alpha = alpha;
+  rp.gamma_scale = gamma * eff_scale(g, softmax_scale);
+  rp.sigma = sigma;
+  rp.mask = mask;
+  rp.log_prior = logp;
+  rp.seqlens = seqlens;
+  rp.rows = g.num_seqs;
+  DASH_HIP(dash::launch_route(g, rp, s));
+  dash::DecodeParams dp;
+  dp.q = q;
+  dp.k = k_cache;
+  dp.v = v_cache;
+  dp.seqlens = seqlens;
+  dp.mask = mask;
+  dp.log_prior = logp;
+  dp.out = out;
+  dp.lse = lse;
+  dp.scale = eff_scale(g, softmax_scale);
+  dp.part_acc = reinterpret_cast<float*>(at(workspace, w.acc));
+  dp.part_ml = reinterpret_cast<float*>(at(workspace, w.ml));
+  dp.nsplit = w.nsplit;
+  DASH_HIP(dash::launch_decode_attn(g, dp, s));
+  return DASH_OK;
+}
+
+}  // extern "C"

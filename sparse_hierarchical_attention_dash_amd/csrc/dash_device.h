@@ -1,0 +1,131 @@
+// Device helpers shared by the DashAttention HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dash {
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// ---------------------------------------------------------------- wave reductions
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// ---------------------------------------------------------------- sequences
+
+// Where a sequence lives in the packed token and summary arrays.
+struct SeqInfo {
+  int64_t start;      // first token row
+  int32_t len;        // tokens
+  int64_t chunk_off;  // first summary row
+};
+
+// cu_seqlens == nullptr: fixed-length batch of max_seqlen tokens each.
+// cu_chunks may be null for callers that do not use chunk_off.
+__device__ __forceinline__ SeqInfo seq_info(const int32_t* cu_seqlens,
+                                            const int32_t* cu_chunks, int s,
+                                            int max_seqlen, int B) {
+  SeqInfo r;
+  if (cu_seqlens) {
+    int a = cu_seqlens[s];
+    r.start = a;
+    r.len = cu_seqlens[s + 1] - a;
+    r.chunk_off = cu_chunks ? cu_chunks[s] : 0;
+  } else {
+    r.start = (int64_t)s * max_seqlen;
+    r.len = max_seqlen;
+    r.chunk_off = (int64_t)s * (max_seqlen / B);
+  }
+  return r;
+}
+
+// Largest s with cu_seqlens[s] <= t (t a valid packed token row).
+__device__ __forceinline__ int find_seq(const int32_t* cu_seqlens, int num_seqs,
+                                        int64_t t) {
+  int lo = 0, hi = num_seqs - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)cu_seqlens[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Bits of mask word w that name chunks c < n.
+__device__ __forceinline__ unsigned long long routable_bits(int w, int n) {
+  const int k = n - 64 * w;
+  if (k <= 0) return 0ull;
+  if (k >= 64) return ~0ull;
+  return (1ull << k) - 1ull;
+}
+
+// ---------------------------------------------------------------- memory
+
+__device__ __forceinline__ u32x4 ldg16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+__device__ __forceinline__ s16x4 as_s16x4(u32x2 v) {
+  return __builtin_bit_cast(s16x4, v);
+}
+
+// D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16).  Lane l supplies
+// A[l%16][8(l/16)..+7] and B[8(l/16)..+7][l%16]; it receives D[4(l/16)+j][l%16].
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// D(16x16, fp32) += A(16x16, bf16) * B(16x16, bf16).  Lane l supplies
+// A[l%16][4(l/16)..+3] and B[4(l/16)..+3][l%16].
+__device__ __forceinline__ f32x4 mfma16x16x16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+}  // namespace dash

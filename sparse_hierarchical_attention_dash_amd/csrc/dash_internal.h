@@ -1,0 +1,81 @@
+// Internal launch interface between the C ABI (dash_api.cpp) and the kernels.
+// Everything here has been validated on the host before it is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dash {
+
+// Geometry of one call, validated and derived on the host.
+struct Geom {
+  int num_seqs = 0;
+  int max_seqlen = 0;
+  int64_t T = 0;                        // packed token rows (prefill / route)
+  const int32_t* cu_seqlens = nullptr;  // device [num_seqs+1] or null
+  const int32_t* cu_chunks = nullptr;   // device [num_seqs+1] (workspace) or null
+  int Hq = 0, Hkv = 0, G = 0, D = 0, B = 0;
+  int C_slots = 0;                      // ceil(max_seqlen / B)
+  int W = 0;                            // ceil(C_slots / 64)
+  bool bf16 = true;
+};
+
+// a0: cu_chunks[s] = sum_{s' < s} floor(L_s' / B).
+hipError_t launch_varlen_meta(const int32_t* cu_seqlens, int num_seqs, int B,
+                              int32_t* cu_chunks, hipStream_t st);
+
+// K0: chunk summaries.
+hipError_t launch_summarize(const Geom& g, const void* k, const float* qbar,
+                            void* kbar, hipStream_t st);
+
+// K1: routing.  Prefill mode routes every packed token row; decode mode
+// (seqlens != null) routes batch entry b at position seqlens[b] - 1 against
+// summary rows b * (max_seqlen / B) ...
+struct RouteParams {
+  const void* q = nullptr;
+  const void* kbar = nullptr;
+  float alpha = 1.5f;
+  const float* alpha_per_seq = nullptr;
+  float gamma_scale = 1.f;              // gamma * s
+  float sigma = 1.f;
+  uint64_t* mask = nullptr;             // [Hkv, rows, W]
+  float* log_prior = nullptr;           // [Hkv, rows, C_slots] or null
+  float* tau = nullptr;                 // [Hq, rows] or null
+  const int32_t* seqlens = nullptr;     // decode mode when non-null
+  int64_t rows = 0;                     // T (prefill) or batch (decode)
+};
+hipError_t launch_route(const Geom& g, const RouteParams& p, hipStream_t st);
+
+// K2p: prefill attention over the active chunks and the diagonal.
+struct PrefillParams {
+  const void* q = nullptr;
+  const void* k = nullptr;
+  const void* v = nullptr;
+  const uint64_t* mask = nullptr;       // [Hkv, T, W]
+  const float* log_prior = nullptr;     // [Hkv, T, C_slots]
+  void* out = nullptr;
+  float* lse = nullptr;                 // [Hq, T] or null
+  float scale = 0.f;
+};
+hipError_t launch_prefill_attn(const Geom& g, const PrefillParams& p, hipStream_t st);
+
+// K2d + K4: split-K decode attention and the combine of the partials.
+struct DecodeParams {
+  const void* q = nullptr;              // [batch, Hq, D]
+  const void* k = nullptr;              // [batch, cap, Hkv, D]
+  const void* v = nullptr;
+  const int32_t* seqlens = nullptr;     // [batch]
+  const uint64_t* mask = nullptr;       // [Hkv, batch, W]
+  const float* log_prior = nullptr;     // [Hkv, batch, C_slots]
+  void* out = nullptr;                  // [batch, Hq, D]
+  float* lse = nullptr;                 // [Hq, batch] or null
+  float scale = 0.f;
+  float* part_acc = nullptr;            // [batch, Hkv, nsplit, G, D]
+  float* part_ml = nullptr;             // [batch, Hkv, nsplit, G, 2]
+  int nsplit = 1;
+};
+int decode_num_splits(const Geom& g);
+hipError_t launch_decode_attn(const Geom& g, const DecodeParams& p, hipStream_t st);
+
+}  // namespace dash

@@ -1,0 +1,209 @@
+"""Torch-facing wrappers of the C ABI: dash.summarize / route / attn_prefill /
+attn_decode.
+
+Torch supplies device memory (inputs, outputs, the workspace) and the current
+stream; every computation runs in libdash.so.  Shapes follow include/dash.h:
+token-major q [T, Hq, D], k/v [T, Hkv, D]; decode caches [batch, cap, Hkv, D].
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib as L
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return L.DASH_BF16
+    if t.dtype == torch.float32:
+        return L.DASH_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("dash ops take GPU tensors")
+            if not t.is_contiguous():
+                raise ValueError("dash ops take contiguous tensors")
+
+
+def _seq_shape(q_or_k, num_heads_q, num_heads_kv, chunk_size, cu_seqlens, max_seqlen):
+    T, _, D = q_or_k.shape
+    if cu_seqlens is None:
+        num_seqs = 1 if max_seqlen is None else T // max_seqlen
+        max_seqlen = T if max_seqlen is None else max_seqlen
+        cu_ptr = None
+    else:
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+        num_seqs = cu_seqlens.numel() - 1
+        if max_seqlen is None:
+            raise ValueError("max_seqlen is required with cu_seqlens")
+        cu_ptr = cu_seqlens.data_ptr()
+    return L.make_shape(num_seqs, max_seqlen, T, cu_ptr, num_heads_q, num_heads_kv, D,
+                        chunk_size, _dtype_code(q_or_k))
+
+
+def _workspace(op, shape, device):
+    n = L.workspace_size(op, shape)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+    return ws, n
+
+
+def layout(shape, enable_gqa=True):
+    return L.layout(shape, enable_gqa)
+
+
+def summarize(k, qbar, chunk_size, cu_seqlens=None, max_seqlen=None, out=None,
+              workspace=None):
+    """Phase-0 chunk summaries; returns k_bar [floor(T/B), Hkv, D] (k's dtype)."""
+    _need_cuda(k, qbar, cu_seqlens)
+    T, Hkv, D = k.shape
+    shape = _seq_shape(k, Hkv, Hkv, chunk_size, cu_seqlens, max_seqlen)
+    if out is None:
+        lay = L.layout(shape)
+        out = torch.empty((lay.summary_rows, Hkv, D), dtype=k.dtype, device=k.device)
+    if workspace is None:
+        ws, n = _workspace(L.DASH_OP_SUMMARIZE, shape, k.device)
+    else:
+        ws, n = workspace, L.workspace_size(L.DASH_OP_SUMMARIZE, shape)
+    L.check("dash_summarize", L.lib().dash_summarize(
+        ctypes.byref(shape), _ptr(k), _ptr(qbar.float().contiguous() if qbar.dtype != torch.float32 else qbar),
+        _ptr(out), _ptr(ws), n, _stream(k.device)))
+    return out
+
+
+def route(q, kbar, num_kv_heads, chunk_size, *, alpha=1.5, gamma=1.0, sigma=1.0,
+          softmax_scale=0.0, enable_gqa=True, alpha_per_seq=None, cu_seqlens=None,
+          max_seqlen=None, log_prior=False, tau=False, mask_out=None, log_prior_out=None,
+          workspace=None):
+    """Phase-1 routing.  Returns (active_blocks [Hkv,T,W] int64 view of the
+    uint64 words, log_prior [Hkv,T,C_slots] or None, tau [Hq,T] or None)."""
+    _need_cuda(q, kbar, alpha_per_seq, cu_seqlens, mask_out, log_prior_out)
+    T, Hq, D = q.shape
+    shape = _seq_shape(q, Hq, num_kv_heads, chunk_size, cu_seqlens, max_seqlen)
+    dev = q.device
+    if mask_out is None or (log_prior and log_prior_out is None):
+        lay = L.layout(shape, enable_gqa)
+    mask = mask_out if mask_out is not None else torch.empty(
+        (num_kv_heads, T, lay.mask_words), dtype=torch.int64, device=dev)
+    if log_prior_out is not None:
+        lp = log_prior_out
+    else:
+        lp = (torch.full((num_kv_heads, T, lay.chunk_slots), float("nan"), device=dev)
+              if log_prior else None)
+    ta = torch.empty((Hq, T), dtype=torch.float32, device=dev) if tau else None
+    if workspace is None:
+        ws, n = _workspace(L.DASH_OP_ROUTE, shape, dev)
+    else:
+        ws, n = workspace, L.workspace_size(L.DASH_OP_ROUTE, shape)
+    L.check("dash_route", L.lib().dash_route(
+        ctypes.byref(shape), _ptr(q), _ptr(kbar), float(alpha), _ptr(alpha_per_seq),
+        float(gamma), float(sigma), float(softmax_scale), int(enable_gqa), _ptr(mask),
+        _ptr(lp), _ptr(ta), _ptr(ws), n, _stream(dev)))
+    return mask, lp, ta
+
+
+def attn_prefill(q, k, v, qbar, chunk_size, *, alpha=1.5, gamma=1.0, sigma=1.0,
+                 softmax_scale=0.0, enable_gqa=True, alpha_per_seq=None, cu_seqlens=None,
+                 max_seqlen=None, return_lse=False, return_active_blocks=False,
+                 workspace=None):
+    """Phases 0-2, causal prefill.  Returns (out, lse or None, active_blocks or None)."""
+    _need_cuda(q, k, v, qbar, alpha_per_seq, cu_seqlens)
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    shape = _seq_shape(q, Hq, Hkv, chunk_size, cu_seqlens, max_seqlen)
+    lay = L.layout(shape, enable_gqa)
+    dev = q.device
+    out = torch.empty_like(q)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=dev) if return_lse else None
+    ab = (torch.empty((Hkv, T, lay.mask_words), dtype=torch.int64, device=dev)
+          if return_active_blocks else None)
+    n = L.workspace_size(L.DASH_OP_PREFILL, shape)
+    if workspace is None or workspace.numel() < n:
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    L.check("dash_attn_prefill", L.lib().dash_attn_prefill(
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(qbar), float(alpha),
+        _ptr(alpha_per_seq), float(gamma), float(sigma), float(softmax_scale),
+        int(enable_gqa), _ptr(out), _ptr(lse), _ptr(ab), _ptr(workspace), n,
+        _stream(dev)))
+    return out, lse, ab
+
+
+def attn_sparse(q, k, v, active_blocks, log_prior, chunk_size, *, softmax_scale=0.0,
+                enable_gqa=True, cu_seqlens=None, max_seqlen=None, return_lse=False,
+                out=None):
+    """Phase 2 alone for a given routing (active_blocks [Hkv,T,W] int64 words,
+    log_prior [Hkv,T,C_slots] fp32).  Returns (out, lse or None)."""
+    _need_cuda(q, k, v, active_blocks, log_prior, cu_seqlens)
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    shape = _seq_shape(q, Hq, Hkv, chunk_size, cu_seqlens, max_seqlen)
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=dev) if return_lse else None
+    L.check("dash_attn_sparse", L.lib().dash_attn_sparse(
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(active_blocks), _ptr(log_prior),
+        float(softmax_scale), int(enable_gqa), _ptr(out), _ptr(lse), _stream(dev)))
+    return out, lse
+
+
+def prefill_workspace(q, k, chunk_size, cu_seqlens=None, max_seqlen=None):
+    """Allocate the workspace attn_prefill needs, for reuse across calls."""
+    T, Hq, D = q.shape
+    shape = _seq_shape(q, Hq, k.shape[1], chunk_size, cu_seqlens, max_seqlen)
+    n = L.workspace_size(L.DASH_OP_PREFILL, shape)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+
+
+def decode_shape(q, k_cache, chunk_size):
+    batch, Hq, D = q.shape
+    _, cap, Hkv, _ = k_cache.shape
+    return L.make_shape(batch, cap, batch, None, Hq, Hkv, D, chunk_size, _dtype_code(q))
+
+
+def attn_decode(q, k_cache, v_cache, seqlens, kbar_cache, chunk_size, *, alpha=1.5,
+                gamma=1.0, sigma=1.0, softmax_scale=0.0, enable_gqa=True,
+                return_lse=False, return_active_blocks=False, workspace=None, out=None):
+    """One decode step.  q [batch, Hq, D]; caches [batch, cap, Hkv, D];
+    seqlens int32 [batch]; kbar_cache [batch, cap/B, Hkv, D]."""
+    _need_cuda(q, k_cache, v_cache, seqlens, kbar_cache)
+    batch, Hq, D = q.shape
+    Hkv = k_cache.shape[2]
+    shape = decode_shape(q, k_cache, chunk_size)
+    lay = L.layout(L.make_shape(batch, k_cache.shape[1], batch * k_cache.shape[1], None, Hq,
+                                Hkv, D, chunk_size, _dtype_code(q)), enable_gqa)
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty((Hq, batch), dtype=torch.float32, device=dev) if return_lse else None
+    ab = (torch.empty((Hkv, batch, lay.mask_words), dtype=torch.int64, device=dev)
+          if return_active_blocks else None)
+    n = L.workspace_size(L.DASH_OP_DECODE, shape)
+    if workspace is None or workspace.numel() < n:
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    L.check("dash_attn_decode", L.lib().dash_attn_decode(
+        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens),
+        _ptr(kbar_cache), float(alpha), float(gamma), float(sigma), float(softmax_scale),
+        int(enable_gqa), _ptr(out), _ptr(lse), _ptr(ab), _ptr(workspace), n,
+        _stream(dev)))
+    return out, lse, ab
+
+
+def decode_workspace(q, k_cache, chunk_size):
+    n = L.workspace_size(L.DASH_OP_DECODE, decode_shape(q, k_cache, chunk_size))
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)

@@ -190,3 +190,18 @@ def make(name, **overrides):
         d["seqlens"] = np.full(w.batch, w.seqlen, dtype=np.int32)
     d["workload"] = w
     return d
+
+
+def gen_routing(Hkv, L, B, density, seed, lo=-6.0):
+    """A synthetic routing for driving the attention stage on its own: each
+    routable chunk c < floor(i/B) of each (KV head, position) is active with
+    probability ``density``; active chunks get a bias drawn uniformly in
+    [lo, 0], inactive ones -inf.  Returns (mask bool [Hkv, L, S],
+    log_prior float32 [Hkv, L, S]) with S = ceil(L / B)."""
+    rng = np.random.default_rng(seed + 3000)
+    S = -(-L // B)
+    n = (np.arange(L) // B)[None, :, None]
+    mask = (rng.random((Hkv, L, S)) < density) & (np.arange(S)[None, None, :] < n)
+    lp = rng.uniform(lo, 0.0, (Hkv, L, S)).astype(np.float32)
+    lp[~mask] = -np.inf
+    return mask, lp

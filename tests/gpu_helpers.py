@@ -1,0 +1,116 @@
+"""Shared helpers of the GPU parity tests (imported by test modules only)."""
+
+import math
+
+import numpy as np
+import torch
+
+import oracle as O
+from sparse_hierarchical_attention_dash_amd import ops
+
+BAND = 1e-4          # mask bits may differ only this close to the threshold
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+LSE_TOL = {"bf16": 2e-3, "f32": 1e-4}
+
+
+def to_dev(a, dtype):
+    """float32 numpy -> (device tensor in dtype, float64 numpy of its exact values)."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    return t.cuda(), t.to(torch.float64).numpy()
+
+
+def unpack_bits(ab, slots):
+    """int64 [..., W] words (chunk c = bit c%64 of word c//64) -> bool [..., slots]."""
+    a = np.ascontiguousarray(ab.detach().cpu().numpy()).view(np.uint64)
+    b = np.unpackbits(a.view(np.uint8), bitorder="little")
+    return b.reshape(a.shape[:-1] + (a.shape[-1] * 64,))[..., :slots].astype(bool)
+
+
+def pack_bits(mask):
+    """bool [..., S] -> int64 [..., W] words, chunk c in bit c%64 of word c//64."""
+    S = mask.shape[-1]
+    Wd = -(-S // 64)
+    full = np.zeros(mask.shape[:-1] + (Wd * 64,), dtype=bool)
+    full[..., :S] = mask
+    by = np.packbits(full, axis=-1, bitorder="little")
+    return np.ascontiguousarray(by).view(np.uint64).view(np.int64)
+
+
+def flush(msg):
+    print(msg, flush=True)
+
+
+def compare_masks(gpu_bits, ora_mask, margin, excused=None, what=""):
+    """gpu_bits/ora_mask/margin: [Hkv, R, S].  Flips are allowed only inside the
+    threshold band (and on chunks whose summaries differ, when given)."""
+    mism = gpu_bits != ora_mask
+    allowed = margin < BAND
+    if excused is not None:
+        allowed = allowed | excused
+    bad = mism & ~allowed
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{what}: {int(bad.sum())} mask bits differ outside the band, "
+                             f"first at {idx.tolist()} (margins {margin[tuple(idx.T)]})")
+    return int(mism.sum())
+
+
+def summary_excuse(kbar_gpu, kbar_ora, Hkv, R, S):
+    """[Hkv, R, S] True on chunks whose GPU summary differs from the oracle's."""
+    diff = np.any(kbar_gpu != kbar_ora, axis=2)            # [C, Hkv]
+    ex = np.zeros((Hkv, R, S), dtype=bool)
+    C = diff.shape[0]
+    ex[:, :, :C] = diff.T[:, None, :]
+    return ex
+
+
+def check_summaries(kbar_gpu, kbar_ora, dtype):
+    if dtype == "f32":
+        np.testing.assert_allclose(kbar_gpu, kbar_ora, atol=2e-6, rtol=1e-5)
+        return 0
+    # bf16: identical except where fp32 accumulation lands on the other side
+    # of a rounding midpoint, which moves the result by one unit in the last
+    # place (2^-8 relative at most)
+    d = np.abs(kbar_gpu - kbar_ora)
+    ulp = np.abs(kbar_ora) * 2.0 ** -7 + 1e-30
+    assert np.all(d <= ulp), float(np.max(d / ulp))
+    frac = float(np.mean(d > 0))
+    assert frac < 1e-3, frac
+    return frac
+
+
+def prefill_case(d, B, alpha, gamma, sigma, dtype, gqa=True, rows=None, scale=0.0):
+    """Run one prefill sequence on the GPU and through the oracle; compare."""
+    q, qx = to_dev(d["q"], dtype)
+    k, kx = to_dev(d["k"], dtype)
+    v, vx = to_dev(d["v"], dtype)
+    qbar = torch.from_numpy(d["qbar"]).cuda()
+    L, Hq, D = d["q"].shape
+    Hkv = d["k"].shape[1]
+    G = Hq // Hkv
+    out, lse, ab = ops.attn_prefill(q, k, v, qbar, B, alpha=alpha, gamma=gamma, sigma=sigma,
+                                    softmax_scale=scale, enable_gqa=gqa, return_lse=True,
+                                    return_active_blocks=True)
+    kb = ops.summarize(k, qbar, B)
+    torch.cuda.synchronize()
+    S = -(-L // B)
+    rows = list(range(L)) if rows is None else sorted(set(int(r) for r in rows))
+    ref = O.prefill(qx, kx, vx, d["qbar"].astype(np.float64), B, alpha, gamma, sigma, gqa,
+                    to_bf16=(dtype == "bf16"), scale=(scale if scale > 0 else None), rows=rows,
+                    num_slots=S)
+    kb_gpu = kb.to(torch.float64).cpu().numpy()
+    check_summaries(kb_gpu, ref["kbar"], dtype)
+    s = scale if scale > 0 else 1.0 / math.sqrt(D)
+    margin = O.routing_margin(qx, ref["kbar"], B, gamma, s, G, ref["tau_hat"], rows, S)
+    bits = unpack_bits(ab, S)[:, rows, :]
+    ex = summary_excuse(kb_gpu, ref["kbar"], Hkv, len(rows), S)
+    flips = compare_masks(bits, ref["mask"][:, rows, :], margin, ex, "prefill")
+    o = out.to(torch.float64).cpu().numpy()[rows]
+    err = float(np.max(np.abs(o - ref["out"])))
+    assert err <= TOL[dtype], f"out max-abs {err}"
+    le = lse.cpu().numpy().astype(np.float64)[:, rows]
+    lerr = float(np.max(np.abs(le - ref["lse"])))
+    assert lerr <= LSE_TOL[dtype], f"lse max-abs {lerr}"
+    return dict(err=err, lse_err=lerr, flips=flips, bits=bits, ref=ref, out=out, ab=ab)

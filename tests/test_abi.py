@@ -1,0 +1,169 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/dash.h declares, and rejects every invalid argument with the right
+status before any HIP call (nothing is launched on these paths)."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from sparse_hierarchical_attention_dash_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dash.h")
+
+A = 0x10000          # a 256-byte aligned stand-in address, never dereferenced
+BF16, F32 = L.DASH_BF16, L.DASH_F32
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:dash_status|size_t|const char\*|int)\s+(dash_\w+)\(",
+                                 text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libdash.so is not built (run __graft_entry__.build())")
+    return L.lib()
+
+
+def shape(T=256, Hq=32, Hkv=2, D=128, B=64, dtype=BF16, num_seqs=1, max_seqlen=None, cu=None):
+    return L.make_shape(num_seqs, T if max_seqlen is None else max_seqlen, T, cu, Hq, Hkv, D,
+                        B, dtype)
+
+
+_DEFAULT = object()
+
+
+def prefill(lib, s, *, q=A, k=A, v=A, qbar=A, out=A, alpha=1.5, gamma=1.0, sigma=1.0,
+            scale=0.0, gqa=1, ws=_DEFAULT, ws_bytes=None):
+    need = L.workspace_size(L.DASH_OP_PREFILL, s)
+    ws = A if ws is _DEFAULT else ws
+    ws_bytes = need if ws_bytes is None else ws_bytes
+    return lib.dash_attn_prefill(ctypes.byref(s), q, k, v, qbar, alpha, None, gamma, sigma,
+                                 scale, gqa, out, None, None, ws, ws_bytes, None)
+
+
+def test_header_declares_the_four_operations():
+    names = declared_functions()
+    for f in ("dash_summarize", "dash_route", "dash_attn_prefill", "dash_attn_decode"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(L.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.dash_abi_version() == 1
+    for code, text in ((0, "ok"), (1, "invalid argument"), (2, "unsupported configuration"),
+                       (3, "workspace too small"), (4, "HIP launch error")):
+        assert L.status_string(code) == text
+    assert L.status_string(99) == "unknown status"
+
+
+def test_layout_and_workspace_sizes(lib):
+    s = shape(T=1000, B=64)
+    lay = L.layout(s)
+    assert (lay.summary_rows, lay.chunk_slots, lay.mask_words, lay.group_size) == (15, 16, 1, 16)
+    s = shape(T=131072, B=64)
+    lay = L.layout(s)
+    assert (lay.chunk_slots, lay.mask_words) == (2048, 32)
+    # prefill workspace holds summaries, a mask and the dense log-prior
+    T, Hkv, D, W, C = 1000, 2, 128, 1, 16
+    need = L.workspace_size(L.DASH_OP_PREFILL, shape(T=T))
+    parts = [(T // 64) * Hkv * D * 2, Hkv * T * W * 8, Hkv * T * C * 4]
+    assert need == sum((p + 255) // 256 * 256 for p in parts)
+    assert L.workspace_size(L.DASH_OP_SUMMARIZE, shape()) == 0
+    assert L.workspace_size(L.DASH_OP_ROUTE, shape(cu=A, num_seqs=3)) == 256
+    assert L.workspace_size(L.DASH_OP_DECODE, shape(T=4, num_seqs=4, max_seqlen=4096)) > 0
+    assert L.workspace_size(L.DASH_OP_PREFILL, shape(D=96)) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=96), L.DASH_ERR_UNSUPPORTED),
+    (dict(B=32), L.DASH_ERR_UNSUPPORTED),
+    (dict(dtype=7), L.DASH_ERR_UNSUPPORTED),
+    (dict(Hq=6, Hkv=2), L.DASH_ERR_UNSUPPORTED),          # bf16 group of 3
+    (dict(Hq=48, Hkv=1), L.DASH_ERR_UNSUPPORTED),         # bf16 group of 48
+    (dict(Hq=5, Hkv=2), L.DASH_ERR_INVALID_ARGUMENT),
+    (dict(T=200000, B=64), L.DASH_ERR_UNSUPPORTED),       # more than 2048 chunk slots
+])
+def test_prefill_rejects_bad_shapes(lib, kw, status):
+    assert prefill(lib, shape(**kw)) == status
+
+
+def test_prefill_rejects_bad_arguments(lib):
+    s = shape()
+    assert lib.dash_attn_prefill(None, A, A, A, A, 1.5, None, 1.0, 1.0, 0.0, 1, A, None, None,
+                                 A, 1 << 30, None) == L.DASH_ERR_INVALID_ARGUMENT
+    assert prefill(lib, s, q=None) == L.DASH_ERR_INVALID_ARGUMENT
+    assert prefill(lib, s, out=None) == L.DASH_ERR_INVALID_ARGUMENT
+    assert prefill(lib, s, qbar=None) == L.DASH_ERR_INVALID_ARGUMENT
+    assert prefill(lib, s, k=A + 2) == L.DASH_ERR_INVALID_ARGUMENT      # misaligned
+    assert prefill(lib, s, alpha=0.5) == L.DASH_ERR_INVALID_ARGUMENT
+    assert prefill(lib, s, alpha=3.0) == L.DASH_ERR_UNSUPPORTED
+    assert prefill(lib, s, alpha=math.nan) == L.DASH_ERR_INVALID_ARGUMENT
+    assert prefill(lib, s, gamma=0.0) == L.DASH_ERR_INVALID_ARGUMENT
+    assert prefill(lib, s, gamma=math.inf) == L.DASH_ERR_INVALID_ARGUMENT
+    assert prefill(lib, s, sigma=-1.0) == L.DASH_ERR_INVALID_ARGUMENT
+    assert prefill(lib, s, scale=math.nan) == L.DASH_ERR_INVALID_ARGUMENT
+    assert prefill(lib, s, gqa=0) == L.DASH_ERR_INVALID_ARGUMENT       # Hq != Hkv
+    need = L.workspace_size(L.DASH_OP_PREFILL, s)
+    assert prefill(lib, s, ws_bytes=need - 1) == L.DASH_ERR_WORKSPACE_TOO_SMALL
+    assert prefill(lib, s, ws=None) == L.DASH_ERR_INVALID_ARGUMENT
+    assert prefill(lib, s, ws=A + 16) == L.DASH_ERR_INVALID_ARGUMENT   # not 256-aligned
+    bad = shape(T=100, num_seqs=2, max_seqlen=64)                       # T != num_seqs*max
+    assert prefill(lib, bad) == L.DASH_ERR_INVALID_ARGUMENT
+
+
+def test_empty_input_is_a_no_op(lib):
+    # zero tokens: valid, nothing to do, no HIP call is made
+    assert prefill(lib, shape(T=0, num_seqs=0, max_seqlen=0)) == L.DASH_OK
+    s = shape(T=0, num_seqs=0, max_seqlen=0)
+    assert lib.dash_summarize(ctypes.byref(s), A, A, A, None, 0, None) == L.DASH_OK
+    assert lib.dash_route(ctypes.byref(s), A, A, 1.5, None, 1.0, 1.0, 0.0, 1, A, None, None,
+                          None, 0, None) == L.DASH_OK
+
+
+def test_route_and_summarize_checks(lib):
+    s = shape()
+    assert lib.dash_route(ctypes.byref(s), A, A, 1.5, None, 1.0, 1.0, 0.0, 1, None, None, None,
+                          None, 0, None) == L.DASH_ERR_INVALID_ARGUMENT   # mask is required
+    assert lib.dash_route(ctypes.byref(s), A, A, 2.5, None, 1.0, 1.0, 0.0, 1, A, None, None,
+                          None, 0, None) == L.DASH_ERR_UNSUPPORTED
+    assert lib.dash_summarize(ctypes.byref(s), None, A, A, None, 0, None) == \
+        L.DASH_ERR_INVALID_ARGUMENT
+    v = shape(cu=A, num_seqs=3)
+    assert lib.dash_summarize(ctypes.byref(v), A, A, A, None, 0, None) == \
+        L.DASH_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_decode_checks(lib):
+    s = L.make_shape(4, 4096, 4, None, 32, 2, 128, 64, BF16)
+    need = L.workspace_size(L.DASH_OP_DECODE, s)
+
+    def dec(sh, **kw):
+        a = dict(q=A, k=A, v=A, sl=A, kb=A, out=A, ws=A, n=need, alpha=1.5)
+        a.update(kw)
+        return lib.dash_attn_decode(ctypes.byref(sh), a["q"], a["k"], a["v"], a["sl"], a["kb"],
+                                    a["alpha"], 1.0, 1.0, 0.0, 1, a["out"], None, None, a["ws"],
+                                    a["n"], None)
+
+    assert dec(s, sl=None) == L.DASH_ERR_INVALID_ARGUMENT
+    assert dec(s, kb=None) == L.DASH_ERR_INVALID_ARGUMENT
+    assert dec(s, n=need - 1) == L.DASH_ERR_WORKSPACE_TOO_SMALL
+    assert dec(s, alpha=0.9) == L.DASH_ERR_INVALID_ARGUMENT
+    assert dec(L.make_shape(4, 4000, 4, None, 32, 2, 128, 64, BF16)) == \
+        L.DASH_ERR_INVALID_ARGUMENT                                   # capacity % B
+    assert dec(L.make_shape(4, 4096, 4, A, 32, 2, 128, 64, BF16)) == \
+        L.DASH_ERR_INVALID_ARGUMENT                                   # no cu_seqlens
+    assert dec(L.make_shape(4, 4096, 4, None, 128, 1, 128, 64, BF16)) == \
+        L.DASH_ERR_UNSUPPORTED                                        # group > 64
