@@ -124,6 +124,9 @@ def main():
     ap.add_argument("--only", choices=["both", "prefill", "decode"], default="both")
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-ref", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (the "
+                         "reference for scaling HBM byte counters) and exit")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -137,6 +140,15 @@ def main():
     from sparse_hierarchical_attention_dash_amd import workloads as W
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_ref:
+        n = args.copy_ref * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_ref_bytes": n * 4, "reps": 5}))
+        return
     L.lib()
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)

@@ -226,33 +226,34 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(Geom g, DecodeParams p
   }
 }
 
+// One workgroup per (query head, sequence, KV head), one thread per output
+// dimension: the split maxima/sums are read as broadcasts, the accumulators
+// coalesced.
 template <int D>
-__global__ __launch_bounds__(256) void decode_combine_kernel(Geom g, DecodeParams p) {
-  const int b = blockIdx.x, h = blockIdx.y;
-  const int batch = gridDim.x;
+__global__ __launch_bounds__(D) void decode_combine_kernel(Geom g, DecodeParams p) {
+  const int q = blockIdx.x, b = blockIdx.y, h = blockIdx.z;
+  const int batch = gridDim.y;
+  const int d = threadIdx.x;
   const int G = g.G;
   const int ns = p.nsplit;
   const int64_t pb = ((int64_t)b * g.Hkv + h) * ns;
-  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
-    const int q = idx / D, d = idx - q * D;
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, p.part_ml[((pb + s) * G + q) * 2]);
-    float acc = 0.f, ls = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float ms = p.part_ml[((pb + s) * G + q) * 2];
-      if (ms == -INFINITY) continue;
-      const float sc = exp2f(ms - M);
-      ls += p.part_ml[((pb + s) * G + q) * 2 + 1] * sc;
-      acc += p.part_acc[((pb + s) * G + q) * D + d] * sc;
-    }
-    const float v = acc / ls;
-    const int64_t orow = ((int64_t)b * g.Hq + h * G + q) * D;
-    if (g.bf16)
-      ((uint16_t*)p.out)[orow + d] = (uint16_t)f32_to_bf16(v);
-    else
-      ((float*)p.out)[orow + d] = v;
-    if (p.lse && d == 0) p.lse[(int64_t)(h * G + q) * batch + b] = (M + __log2f(ls)) * kLn2;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, p.part_ml[((pb + s) * G + q) * 2]);
+  float acc = 0.f, ls = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float ms = p.part_ml[((pb + s) * G + q) * 2];
+    if (ms == -INFINITY) continue;
+    const float sc = exp2f(ms - M);
+    ls += p.part_ml[((pb + s) * G + q) * 2 + 1] * sc;
+    acc += p.part_acc[((pb + s) * G + q) * D + d] * sc;
   }
+  const float v = acc / ls;
+  const int64_t orow = ((int64_t)b * g.Hq + h * G + q) * D;
+  if (g.bf16)
+    ((uint16_t*)p.out)[orow + d] = (uint16_t)f32_to_bf16(v);
+  else
+    ((float*)p.out)[orow + d] = v;
+  if (p.lse && d == 0) p.lse[(int64_t)(h * G + q) * batch + b] = (M + __log2f(ls)) * kLn2;
 }
 
 int decode_num_splits(const Geom& g) {
@@ -290,10 +291,12 @@ hipError_t launch_decode_attn(const Geom& g, const DecodeParams& p, hipStream_t 
   } while (0)
   if (g.D == 64) {
     DASH_DEC_NT(64);
-    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(g.num_seqs, g.Hkv), dim3(256), 0, st, g, p);
+    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(g.G, g.num_seqs, g.Hkv), dim3(64), 0, st,
+                       g, p);
   } else {
     DASH_DEC_NT(128);
-    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(g.num_seqs, g.Hkv), dim3(256), 0, st, g, p);
+    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(g.G, g.num_seqs, g.Hkv), dim3(128), 0,
+                       st, g, p);
   }
 #undef DASH_DEC_NT
 #undef DASH_DEC

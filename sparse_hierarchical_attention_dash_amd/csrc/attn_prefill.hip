@@ -46,7 +46,95 @@ struct TileGeom {
   int tiles_per_seq;  // ceil(max_seqlen / P)
 };
 
-template <int D>
+// Reference-point slack of the running maximum (log2 units): a row's
+// exponent offset is only moved when its maximum grows by more than this, so
+// the accumulators are rescaled rarely; p = exp2(z - m) then stays <= 2^8.
+constexpr float kRescale = 8.f;
+
+// One visit: a 16-row tile against one staged 64-key block.
+//   MASKED = false: every row of the tile attends every key of the block.
+//   MASKED = true : row r attends key j iff rowon and (!diag or j <= rpos).
+template <int D, bool MASKED>
+__device__ __forceinline__ void visit(const uint16_t* __restrict__ ks_,
+                                      const uint16_t* __restrict__ vt_, int koff, int voff,
+                                      const bf16x8 (&qa)[D / 32], f32x4 (&o)[D / 16],
+                                      f32x4& lacc, float& m, float sl2, float bz, bool rowon,
+                                      bool diag, int kbase, int rpos) {
+  using C = StageCfg<D, kPrefillThreads>;
+  constexpr int KS = D / 32;
+  constexpr int DT = D / 16;
+  // S^T = K Q^T: sacc[t] lane (g, r) = raw score of row r, key 16t + 4g + j
+  f32x4 sacc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const bf16x8 ak = as_bf16x8(
+          *reinterpret_cast<const u32x4*>(ks_ + koff + 16 * t * C::KSTR + 32 * ks));
+      sacc[t] = mfma16x16x32(ak, qa[ks], sacc[t]);
+    }
+  }
+  bool ok[4][4];
+  float amax = -INFINITY;
+  if constexpr (MASKED) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ok[t][j] = rowon && (!diag || kbase + 16 * t + j <= rpos);
+        amax = fmaxf(amax, ok[t][j] ? sacc[t][j] : -INFINITY);
+      }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      amax = fmaxf(amax, fmaxf(fmaxf(sacc[t][0], sacc[t][1]), fmaxf(sacc[t][2], sacc[t][3])));
+  }
+  amax = fmaxf(amax, xor16(amax));
+  amax = fmaxf(amax, xor32(amax));
+  // scale > 0, so the largest logit of the row is amax * scale + bias
+  const float zmax = amax * sl2 + bz;
+  const bool up = zmax > m + kRescale;
+  if (__ballot(up) != 0ull) {
+    const float mn = up ? zmax : m;
+    const float alpha = up ? exp2f(m - mn) : 1.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    lacc *= alpha;
+    m = mn;
+  }
+  const float off = bz - m;
+  uint32_t pk[4][2];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    float pv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      pv[j] = __builtin_amdgcn_exp2f(fmaf(sacc[t][j], sl2, off));
+      if constexpr (MASKED) pv[j] = ok[t][j] ? pv[j] : 0.f;
+    }
+    pk[t][0] = cvt_pk_bf16(pv[0], pv[1]);
+    pk[t][1] = cvt_pk_bf16(pv[2], pv[3]);
+  }
+  // O^T += V^T P^T and, with an all-ones A operand, the row sums of P
+  const u32x4 ones_u = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+  const bf16x8 ones = as_bf16x8(ones_u);
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    const u32x4 pb = {pk[2 * s2][0], pk[2 * s2][1], pk[2 * s2 + 1][0], pk[2 * s2 + 1][1]};
+    const bf16x8 pbv = as_bf16x8(pb);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const bf16x8 av = as_bf16x8(
+          *reinterpret_cast<const u32x4*>(vt_ + voff + 16 * dt * C::VSTR + 32 * s2));
+      o[dt] = mfma16x16x32(av, pbv, o[dt]);
+    }
+    lacc = mfma16x16x32(ones, pbv, lacc);
+  }
+}
+
+template <int D, bool UNI>
 __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_attn_bf16_kernel(
     Geom g, PrefillParams p, TileGeom tg) {
   constexpr int NTH = kPrefillThreads;
@@ -72,17 +160,16 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_attn_bf16_kernel(
   const int64_t T = g.T;
   const int W = g.W;
   const uint16_t* qp = (const uint16_t*)p.q;
-  const uint16_t* kp = (const uint16_t*)p.k;
-  const uint16_t* vp = (const uint16_t*)p.v;
+  const unsigned long long* mask = (const unsigned long long*)p.mask;
 
-  // ---- rows of this lane in each of the wave's tiles
+  // ---- rows of this lane in each of the wave's tiles (UNI: one position per tile)
   int rpos[TWM], rhead[TWM];
   bool rvalid[TWM], tvalid[TWM];
 #pragma unroll
   for (int u = 0; u < TWM; ++u) {
     const int ti = wv * tg.TW + u;
     int pos, head;
-    if (tg.TP == 1) {
+    if (UNI) {
       pos = p0 + ti / tg.HT;
       head = (ti % tg.HT) * 16 + r;
     } else {
@@ -113,8 +200,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_attn_bf16_kernel(
   __syncthreads();
   {
     const int npos = pend - p0;
-    const unsigned long long* mbase =
-        (const unsigned long long*)p.mask + ((int64_t)h * T + si.start + p0) * W;
+    const unsigned long long* mbase = mask + ((int64_t)h * T + si.start + p0) * W;
     for (int idx = tid; idx < npos * W; idx += NTH) {
       const int w = idx % W;
       // only chunks before the workgroup's own chunk are routable
@@ -148,154 +234,103 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_attn_bf16_kernel(
   const int ndiag = (pend - cdiag * g.B + 63) / 64;
   const int NS = nrouted + ndiag;
 
-  // ---- per-tile state
+  // ---- per-tile state: O^T (lane (g, r): row r, dims 16dt + 4g + j), row sums, offsets
   f32x4 o[TWM][DT];
-  float m[TWM], l[TWM];
+  f32x4 lacc[TWM];
+  float m[TWM];
   unsigned long long mword[TWM];
   int mw_idx[TWM];
+  int64_t prow[TWM];  // token row of the tile's position (UNI) / of this lane's row
 #pragma unroll
   for (int u = 0; u < TWM; ++u) {
     m[u] = -INFINITY;
-    l[u] = 0.f;
+    lacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     mword[u] = 0ull;
     mw_idx[u] = -1;
+    prow[u] = (int64_t)h * T + si.start + min(rpos[u], pend - 1);
+    if (UNI) prow[u] = uniform64(prow[u]);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float sl2 = p.scale * kLog2e;
+  const int koff = r * C::KSTR + 8 * gq;
+  const int voff = r * C::VSTR + 8 * gq;
 
+  Stager<D, NTH> stg((const uint16_t*)p.k, (const uint16_t*)p.v, si.start, g.Hkv, h, tid);
   StageRegs<D, NTH> R;
-  auto stage_key0 = [&](int st, int& c, bool& diag) -> int {
+  auto stage_key0 = [&](int st, int& c) -> int {
     if (st < nrouted) {
       c = Blist[st / SB];
-      diag = false;
       return c * g.B + (st % SB) * 64;
     }
     c = cdiag;
-    diag = true;
     return cdiag * g.B + (st - nrouted) * 64;
   };
   if (NS > 0) {
     int c0;
-    bool d0;
-    const int key0 = stage_key0(0, c0, d0);
-    stage_load<D, NTH>(R, kp, vp, si.start, key0, d0 ? pend : si.len, g.Hkv, h, tid);
+    const int key0 = stage_key0(0, c0);
+    if (nrouted > 0) stg.load(R, key0); else stg.load_guarded(R, key0, pend);
   }
   for (int st = 0; st < NS; ++st) {
     const int buf = st & 1;
     int c;
-    bool diag;
-    const int key0 = stage_key0(st, c, diag);
+    const int key0 = stage_key0(st, c);
+    const bool diag = st >= nrouted;
     stage_store<D, NTH>(R, Ks[buf], Vt[buf], tid);
     __syncthreads();
     if (st + 1 < NS) {
       int c1;
-      bool d1;
-      const int k1 = stage_key0(st + 1, c1, d1);
-      stage_load<D, NTH>(R, kp, vp, si.start, k1, d1 ? pend : si.len, g.Hkv, h, tid);
+      const int k1 = stage_key0(st + 1, c1);
+      if (st + 1 < nrouted) stg.load(R, k1); else stg.load_guarded(R, k1, pend);
     }
     const uint16_t* ks_ = Ks[buf];
     const uint16_t* vt_ = Vt[buf];
 #pragma unroll
     for (int u = 0; u < TWM; ++u) {
       if (!tvalid[u]) break;
-      bool rowon = rvalid[u];
-      float bias = 0.f;
       if (!diag) {
         const int wi = c >> 6;
         if (wi != mw_idx[u]) {
           mw_idx[u] = wi;
-          mword[u] = rvalid[u]
-                         ? ((const unsigned long long*)p.mask)[((int64_t)h * T + si.start + rpos[u]) * W + wi]
-                         : 0ull;
+          mword[u] = mask[prow[u] * W + wi];
         }
-        rowon = rowon && ((mword[u] >> (c & 63)) & 1ull);
-        if (rowon)
-          bias = p.log_prior[((int64_t)h * T + si.start + rpos[u]) * g.C_slots + c] * kLog2e;
-      }
-      if (__ballot(rowon) == 0ull) continue;
-      // S^T tiles: sacc[t] lane (g, r) = score of row r, key 16t + 4g + j
-      f32x4 sacc[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const bf16x8 ak = as_bf16x8(
-              *reinterpret_cast<const u32x4*>(ks_ + (16 * t + r) * C::KSTR + 32 * ks + 8 * gq));
-          sacc[t] = mfma16x16x32(ak, qa[u][ks], sacc[t]);
+        const bool rowon = rvalid[u] && ((mword[u] >> (c & 63)) & 1ull);
+        if (UNI) {
+          if (!rowon) continue;  // wave-uniform: the whole tile is one position
+          const float bz = p.log_prior[prow[u] * g.C_slots + c] * kLog2e;
+          visit<D, false>(ks_, vt_, koff, voff, qa[u], o[u], lacc[u], m[u], sl2, bz, true,
+                          false, 0, 0);
+        } else {
+          if (__ballot(rowon) == 0ull) continue;
+          const float bz = rowon ? p.log_prior[prow[u] * g.C_slots + c] * kLog2e : 0.f;
+          visit<D, true>(ks_, vt_, koff, voff, qa[u], o[u], lacc[u], m[u], sl2, bz, rowon,
+                         false, 0, 0);
         }
-      }
-      float zmax = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float z = sacc[t][j] * sl2 + bias;
-          bool ok = rowon;
-          if (diag) ok = ok && (key0 + 16 * t + 4 * gq + j <= rpos[u]);
-          z = ok ? z : -INFINITY;
-          sacc[t][j] = z;
-          zmax = fmaxf(zmax, z);
-        }
-      }
-      zmax = fmaxf(zmax, __shfl_xor(zmax, 16));
-      zmax = fmaxf(zmax, __shfl_xor(zmax, 32));
-      const float mnew = fmaxf(m[u], zmax);
-      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = exp2f(m[u] - muse);
-      float lsum = 0.f;
-      uint32_t pk[4][2];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const float p0_ = exp2f(sacc[t][0] - muse);
-        const float p1_ = exp2f(sacc[t][1] - muse);
-        const float p2_ = exp2f(sacc[t][2] - muse);
-        const float p3_ = exp2f(sacc[t][3] - muse);
-        lsum += (p0_ + p1_) + (p2_ + p3_);
-        pk[t][0] = pack_bf16x2(p0_, p1_);
-        pk[t][1] = pack_bf16x2(p2_, p3_);
-      }
-      l[u] = l[u] * alpha + lsum;
-      m[u] = mnew;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[u][dt] *= alpha;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const u32x4 pb = {pk[2 * s2][0], pk[2 * s2][1], pk[2 * s2 + 1][0], pk[2 * s2 + 1][1]};
-        const bf16x8 pbv = as_bf16x8(pb);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const bf16x8 av = as_bf16x8(
-              *reinterpret_cast<const u32x4*>(vt_ + (16 * dt + r) * C::VSTR + 32 * s2 + 8 * gq));
-          o[u][dt] = mfma16x16x32(av, pbv, o[u][dt]);
-        }
+      } else {
+        if (__ballot(rvalid[u]) == 0ull) continue;
+        visit<D, true>(ks_, vt_, koff, voff, qa[u], o[u], lacc[u], m[u], sl2, 0.f, rvalid[u],
+                       true, key0 + 4 * gq, rpos[u]);
       }
     }
   }
 
-  // ---- epilogue: lane (g, r) holds row r, dims 16dt + 4g + j
+  // ---- epilogue: normalise by the row sums (lacc holds the full sum of row r)
 #pragma unroll
   for (int u = 0; u < TWM; ++u) {
     if (!tvalid[u]) break;
-    float lt = l[u];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
     if (!rvalid[u]) continue;
+    const float lt = lacc[u][0];
     const float inv = 1.f / lt;
     const int64_t tok = si.start + rpos[u];
     uint16_t* orow = (uint16_t*)p.out + (tok * g.Hq + h * g.G + rhead[u]) * (int64_t)D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const u32x2 w = {pack_bf16x2(o[u][dt][0] * inv, o[u][dt][1] * inv),
-                       pack_bf16x2(o[u][dt][2] * inv, o[u][dt][3] * inv)};
+      const u32x2 w = {cvt_pk_bf16(o[u][dt][0] * inv, o[u][dt][1] * inv),
+                       cvt_pk_bf16(o[u][dt][2] * inv, o[u][dt][3] * inv)};
       *reinterpret_cast<u32x2*>(orow + 16 * dt + 4 * gq) = w;
     }
-    if (p.lse && gq == 0) {
-      const float mu = (m[u] == -INFINITY) ? 0.f : m[u];
-      p.lse[(int64_t)(h * g.G + rhead[u]) * T + tok] = (mu + __log2f(lt)) * kLn2;
-    }
+    if (p.lse && gq == 0)
+      p.lse[(int64_t)(h * g.G + rhead[u]) * T + tok] = (m[u] + __log2f(lt)) * kLn2;
   }
 }
 
@@ -403,12 +438,16 @@ hipError_t launch_prefill_attn(const Geom& g, const PrefillParams& p, hipStream_
   if (g.bf16) {
     const TileGeom tg = make_tiles(g);
     dim3 grid(tg.tiles_per_seq, g.num_seqs, g.Hkv);
-    if (g.D == 64)
-      hipLaunchKernelGGL(prefill_attn_bf16_kernel<64>, grid, dim3(kPrefillThreads), 0, st, g,
-                         p, tg);
-    else
-      hipLaunchKernelGGL(prefill_attn_bf16_kernel<128>, grid, dim3(kPrefillThreads), 0, st, g,
-                         p, tg);
+    const bool uni = g.G >= 16;
+#define DASH_PRE(DD, U)                                                                   \
+  hipLaunchKernelGGL((prefill_attn_bf16_kernel<DD, U>), grid, dim3(kPrefillThreads), 0, st, \
+                     g, p, tg)
+    if (g.D == 64) {
+      if (uni) DASH_PRE(64, true); else DASH_PRE(64, false);
+    } else {
+      if (uni) DASH_PRE(128, true); else DASH_PRE(128, false);
+    }
+#undef DASH_PRE
   } else {
     dim3 grid((unsigned)g.T, g.Hq);
     if (g.D == 64)

@@ -71,6 +71,54 @@ __device__ __forceinline__ void stage_load(StageRegs<D, NTH>& R, const uint16_t*
   }
 }
 
+// Global -> registers with this thread's addresses computed once: K row
+// kr + i*NTH/TPR, piece `piece`; V rows kg*KPT + i, piece `vpiece`.  load()
+// reads a block that lies inside the sequence; load_guarded() reads 0 for keys
+// at or past kend.
+template <int D, int NTH>
+struct Stager {
+  using C = StageCfg<D, NTH>;
+  static constexpr int NKG = 64 / C::KPT;
+  const uint16_t* kptr;
+  const uint16_t* vptr;
+  int64_t rowstride;  // elements between consecutive tokens (Hkv * D)
+  int kr, kg;
+  __device__ __forceinline__ Stager(const uint16_t* kp, const uint16_t* vp, int64_t base_row,
+                                    int Hkv, int h, int tid) {
+    const int piece = tid % C::TPR;
+    kr = tid / C::TPR;
+    kg = tid % NKG;
+    const int vpiece = tid / NKG;
+    rowstride = (int64_t)Hkv * D;
+    kptr = kp + (base_row + kr) * rowstride + (int64_t)h * D + piece * 8;
+    vptr = vp + (base_row + kg * C::KPT) * rowstride + (int64_t)h * D + vpiece * 8;
+  }
+  __device__ __forceinline__ void load(StageRegs<D, NTH>& R, int key0) const {
+    const uint16_t* kb = kptr + key0 * rowstride;
+    const uint16_t* vb = vptr + key0 * rowstride;
+#pragma unroll
+    for (int i = 0; i < C::KPT; ++i) R.k[i] = ldg16(kb + i * (NTH / C::TPR) * rowstride);
+#pragma unroll
+    for (int i = 0; i < C::KPT; ++i) R.v[i] = ldg16(vb + i * rowstride);
+  }
+  __device__ __forceinline__ void load_guarded(StageRegs<D, NTH>& R, int key0, int kend) const {
+    const uint16_t* kb = kptr + key0 * rowstride;
+    const uint16_t* vb = vptr + key0 * rowstride;
+#pragma unroll
+    for (int i = 0; i < C::KPT; ++i) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      if (key0 + kr + i * (NTH / C::TPR) < kend) z = ldg16(kb + i * (NTH / C::TPR) * rowstride);
+      R.k[i] = z;
+    }
+#pragma unroll
+    for (int i = 0; i < C::KPT; ++i) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      if (key0 + kg * C::KPT + i < kend) z = ldg16(vb + i * rowstride);
+      R.v[i] = z;
+    }
+  }
+};
+
 // Registers -> LDS.
 template <int D, int NTH>
 __device__ __forceinline__ void stage_store(const StageRegs<D, NTH>& R, uint16_t* Ks,
@@ -87,25 +135,25 @@ __device__ __forceinline__ void stage_store(const StageRegs<D, NTH>& R, uint16_t
   const int kg = tid % NKG;
   const int vpiece = tid / NKG;
   const int col0 = vt_col(kg * C::KPT);
-  // element e of the 8 dims vpiece*8 + e; key i in register R.v[i]
+  // dims vpiece*8 + 2w (low halves) and + 2w + 1 (high halves) of the KPT keys
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int d = vpiece * 8 + e;
-    const int w = e >> 1;
-    const bool hi = e & 1;
+  for (int w = 0; w < 4; ++w) {
+    const int d = vpiece * 8 + 2 * w;
     if constexpr (C::KPT == 4) {
-      uint32_t x0 = hi ? (R.v[0][w] >> 16) : (R.v[0][w] & 0xffffu);
-      uint32_t x1 = hi ? (R.v[1][w] >> 16) : (R.v[1][w] & 0xffffu);
-      uint32_t x2 = hi ? (R.v[2][w] >> 16) : (R.v[2][w] & 0xffffu);
-      uint32_t x3 = hi ? (R.v[3][w] >> 16) : (R.v[3][w] & 0xffffu);
-      u32x2 pk = {x0 | (x1 << 16), x2 | (x3 << 16)};
-      *reinterpret_cast<u32x2*>(Vt + d * C::VSTR + col0) = pk;
+      const u32x2 lo = {__builtin_amdgcn_perm(R.v[1][w], R.v[0][w], 0x05040100u),
+                        __builtin_amdgcn_perm(R.v[3][w], R.v[2][w], 0x05040100u)};
+      const u32x2 hi = {__builtin_amdgcn_perm(R.v[1][w], R.v[0][w], 0x07060302u),
+                        __builtin_amdgcn_perm(R.v[3][w], R.v[2][w], 0x07060302u)};
+      *reinterpret_cast<u32x2*>(Vt + d * C::VSTR + col0) = lo;
+      *reinterpret_cast<u32x2*>(Vt + (d + 1) * C::VSTR + col0) = hi;
     } else if constexpr (C::KPT == 2) {
-      uint32_t x0 = hi ? (R.v[0][w] >> 16) : (R.v[0][w] & 0xffffu);
-      uint32_t x1 = hi ? (R.v[1][w] >> 16) : (R.v[1][w] & 0xffffu);
-      *reinterpret_cast<uint32_t*>(Vt + d * C::VSTR + col0) = x0 | (x1 << 16);
+      *reinterpret_cast<uint32_t*>(Vt + d * C::VSTR + col0) =
+          __builtin_amdgcn_perm(R.v[1][w], R.v[0][w], 0x05040100u);
+      *reinterpret_cast<uint32_t*>(Vt + (d + 1) * C::VSTR + col0) =
+          __builtin_amdgcn_perm(R.v[1][w], R.v[0][w], 0x07060302u);
     } else {
-      Vt[d * C::VSTR + col0] = (uint16_t)(hi ? (R.v[0][w] >> 16) : (R.v[0][w] & 0xffffu));
+      Vt[d * C::VSTR + col0] = (uint16_t)(R.v[0][w] & 0xffffu);
+      Vt[(d + 1) * C::VSTR + col0] = (uint16_t)(R.v[0][w] >> 16);
     }
   }
 }

@@ -189,11 +189,12 @@ dash_status dash_summarize(const dash_shape* shape, const void* k, const float* 
   Geom g;
   dash_status st = check_shape(shape, 1, false, g);
   if (st != DASH_OK) return st;
-  if (!k || !qbar || !kbar) return DASH_ERR_INVALID_ARGUMENT;
-  if (!aligned16(k) || !aligned16(qbar) || !aligned16(kbar)) return DASH_ERR_INVALID_ARGUMENT;
   const size_t need = meta_ws(g);
   if ((st = check_ws(workspace, workspace_bytes, need)) != DASH_OK) return st;
-  if (g.T == 0 || g.num_seqs == 0) return DASH_OK;
+  // nothing to summarise: no pointer is read or written
+  if (g.T == 0 || g.num_seqs == 0 || g.T / g.B == 0) return DASH_OK;
+  if (!k || !qbar || !kbar) return DASH_ERR_INVALID_ARGUMENT;
+  if (!aligned16(k) || !aligned16(qbar) || !aligned16(kbar)) return DASH_ERR_INVALID_ARGUMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (g.cu_seqlens) {
     g.cu_chunks = reinterpret_cast<int32_t*>(workspace);
@@ -213,11 +214,11 @@ dash_status dash_route(const dash_shape* shape, const void* q, const void* kbar,
   dash_status st = check_shape(shape, enable_gqa, false, g);
   if (st != DASH_OK) return st;
   if ((st = check_routing(alpha, gamma, sigma, softmax_scale)) != DASH_OK) return st;
-  if (!q || !kbar || !active_blocks) return DASH_ERR_INVALID_ARGUMENT;
-  if (!aligned16(q) || !aligned16(kbar)) return DASH_ERR_INVALID_ARGUMENT;
   const size_t need = meta_ws(g);
   if ((st = check_ws(workspace, workspace_bytes, need)) != DASH_OK) return st;
   if (g.T == 0 || g.num_seqs == 0) return DASH_OK;
+  if (!q || !active_blocks || (!kbar && g.T / g.B > 0)) return DASH_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(kbar)) return DASH_ERR_INVALID_ARGUMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (g.cu_seqlens) {
     g.cu_chunks = reinterpret_cast<int32_t*>(workspace);
@@ -249,12 +250,12 @@ dash_status dash_attn_prefill(const dash_shape* shape, const void* q, const void
   dash_status st = check_shape(shape, enable_gqa, false, g);
   if (st != DASH_OK) return st;
   if ((st = check_routing(alpha, gamma, sigma, softmax_scale)) != DASH_OK) return st;
+  const PrefillWs w = prefill_ws(g);
+  if ((st = check_ws(workspace, workspace_bytes, w.total)) != DASH_OK) return st;
+  if (g.T == 0 || g.num_seqs == 0) return DASH_OK;  // empty input: nothing is read
   if (!q || !k || !v || !qbar || !out) return DASH_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(qbar))
     return DASH_ERR_INVALID_ARGUMENT;
-  const PrefillWs w = prefill_ws(g);
-  if ((st = check_ws(workspace, workspace_bytes, w.total)) != DASH_OK) return st;
-  if (g.T == 0 || g.num_seqs == 0) return DASH_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (g.cu_seqlens) {
     g.cu_chunks = reinterpret_cast<int32_t*>(at(workspace, w.cu_chunks));
@@ -298,10 +299,10 @@ dash_status dash_attn_sparse(const dash_shape* shape, const void* q, const void*
   dash_status st = check_shape(shape, enable_gqa, false, g);
   if (st != DASH_OK) return st;
   if (std::isnan(softmax_scale)) return DASH_ERR_INVALID_ARGUMENT;
+  if (g.T == 0 || g.num_seqs == 0) return DASH_OK;
   if (!q || !k || !v || !active_blocks || !log_prior || !out) return DASH_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return DASH_ERR_INVALID_ARGUMENT;
-  if (g.T == 0 || g.num_seqs == 0) return DASH_OK;
   dash::PrefillParams pp;
   pp.q = q;
   pp.k = k;
@@ -325,14 +326,14 @@ dash_status dash_attn_decode(const dash_shape* shape, const void* q, const void*
   dash_status st = check_shape(shape, enable_gqa, true, g);
   if (st != DASH_OK) return st;
   if ((st = check_routing(alpha, gamma, sigma, softmax_scale)) != DASH_OK) return st;
+  const DecodeWs w = decode_ws(g);
+  if ((st = check_ws(workspace, workspace_bytes, w.total)) != DASH_OK) return st;
+  if (g.num_seqs == 0) return DASH_OK;
   if (!q || !k_cache || !v_cache || !seqlens || !kbar_cache || !out)
     return DASH_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(kbar_cache) ||
       !aligned16(out))
     return DASH_ERR_INVALID_ARGUMENT;
-  const DecodeWs w = decode_ws(g);
-  if ((st = check_ws(workspace, workspace_bytes, w.total)) != DASH_OK) return st;
-  if (g.num_seqs == 0) return DASH_OK;
   if (g.max_seqlen == 0) return DASH_ERR_INVALID_ARGUMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint64_t* mask = active_blocks ? active_blocks : reinterpret_cast<uint64_t*>(at(workspace, w.mask));

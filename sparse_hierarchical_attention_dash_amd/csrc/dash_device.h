@@ -57,6 +57,68 @@ __device__ __forceinline__ int wave_sum_i(int v) {
   return v;
 }
 
+// Reductions over the 16 lanes of a DPP row (lanes 16r .. 16r+15), every lane
+// of the row receiving the result: quad xor 1, quad xor 2, half-row mirror
+// (lane i <-> 7-i), row mirror (lane i <-> 15-i).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowHalfMirror = 0x141;
+
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<kDppQuadXor1>(v);
+  v += dpp_f<kDppQuadXor2>(v);
+  v += dpp_f<kDppRowHalfMirror>(v);
+  v += dpp_f<kDppRowMirror>(v);
+  return v;
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_f<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp_f<kDppRowHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppRowMirror>(v));
+  return v;
+}
+__device__ __forceinline__ float row16_min(float v) {
+  v = fminf(v, dpp_f<kDppQuadXor1>(v));
+  v = fminf(v, dpp_f<kDppQuadXor2>(v));
+  v = fminf(v, dpp_f<kDppRowHalfMirror>(v));
+  v = fminf(v, dpp_f<kDppRowMirror>(v));
+  return v;
+}
+
+// Cross-row exchanges on gfx950 without LDS: value of lane l ^ 32 and l ^ 16.
+__device__ __forceinline__ float xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  // lanes < 32 get the upper half in r[1]; lanes >= 32 get the lower half in r[0]
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+}
+
+// A 64-bit value every lane holds the same copy of, moved to scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const int lo = __builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const int hi = __builtin_amdgcn_readfirstlane((int)(v >> 32));
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// Two fp32 -> packed bf16x2 (round to nearest even, hardware conversion).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 // ---------------------------------------------------------------- sequences
 
 // Where a sequence lives in the packed token and summary arrays.

@@ -8,7 +8,8 @@
 //      group and the n = floor(i/B) routable chunks, computed 16 heads x 16
 //      chunks at a time with bf16 MFMA (fp32 accumulate; products of bf16 are
 //      exact in fp32) and kept in LDS only, never in HBM;
-//   2. per head, the entmax threshold tau with x = (alpha-1) u: Newton's method
+//   2. per head (16 lanes per head, 4 heads per wave solved side by side with
+//      DPP row reductions), the entmax threshold tau with x = (alpha-1) u: Newton's method
 //      on the convex, decreasing mass f(t) = sum_c [x_c - t]_+^(1/(alpha-1))
 //      started at t0 = max(x) - 1 (where f >= 1) moves monotonically up to the
 //      root; for alpha = 2 (sparsemax) and alpha = 1.5 the threshold is then
@@ -22,16 +23,17 @@
 
 namespace dash {
 
-// d^e and d^(e-1) for d > 0; e = 1, 2, 4 exactly, anything else via exp2/log2.
-__device__ __forceinline__ void pow_pair(float d, float e, int ecls, float& pw,
-                                         float& pd) {
-  if (ecls == 1) {
+// d^e and d^(e-1) for d >= 0 without branches; e = 1, 2, 4 exactly (ECLS),
+// anything else (ECLS = 0) via exp2(e log2 d), which is 0 at d = 0.
+template <int ECLS>
+__device__ __forceinline__ void pow_pair(float d, float e, float& pw, float& pd) {
+  if constexpr (ECLS == 1) {
     pw = d;
-    pd = 1.f;
-  } else if (ecls == 2) {
+    pd = d > 0.f ? 1.f : 0.f;
+  } else if constexpr (ECLS == 2) {
     pw = d * d;
     pd = d;
-  } else if (ecls == 4) {
+  } else if constexpr (ECLS == 4) {
     const float d2 = d * d;
     pw = d2 * d2;
     pd = d2 * d;
@@ -52,76 +54,106 @@ __device__ __forceinline__ float pow_e(float d, float e, int ecls) {
   return exp2f(e * __log2f(d));
 }
 
-// Threshold (x units) of one row whose values xs live in the wave's registers,
-// chunk c = lane + 64k; entries past the row are -inf.
-template <int NK>
-__device__ float solve_tau(const float (&xs)[NK], float xmax, float e, int ecls) {
+// Reductions over the LPH lanes that hold one head's row (LPH = 16: one DPP
+// row; LPH = 32: two rows joined by one cross-row shuffle).
+template <int LPH>
+__device__ __forceinline__ float head_sum(float v) {
+  v = row16_sum(v);
+  if constexpr (LPH == 32) v += __shfl_xor(v, 16);
+  return v;
+}
+template <int LPH>
+__device__ __forceinline__ float head_max(float v) {
+  v = row16_max(v);
+  if constexpr (LPH == 32) v = fmaxf(v, __shfl_xor(v, 16));
+  return v;
+}
+template <int LPH>
+__device__ __forceinline__ float head_min(float v) {
+  v = row16_min(v);
+  if constexpr (LPH == 32) v = fminf(v, __shfl_xor(v, 16));
+  return v;
+}
+
+// Threshold (x units) of one routing row held by LPH lanes, chunk
+// c = (lane % LPH) + LPH k in xs[k] (entries past the row are -1e30).  The
+// rows of a wave (64/LPH query heads) iterate together; a converged row
+// keeps its threshold while the others finish.  Branch-free per element:
+// d = max(x - tau, 0) contributes nothing off the support.
+template <int NK, int LPH, int ECLS>
+__device__ float solve_tau_row(const float (&xs)[NK], float xmax, float e, bool live) {
   float tau = xmax - 1.f;  // the top entry alone has mass 1 here
+  bool done = !live;
   for (int it = 0; it < 200; ++it) {
+    if (__ballot(!done) == 0ull) break;
     float f = 0.f, gd = 0.f;
 #pragma unroll
     for (int k = 0; k < NK; ++k) {
-      const float d = xs[k] - tau;
-      if (d > 0.f) {
-        float pw, pd;
-        pow_pair(d, e, ecls, pw, pd);
-        f += pw;
-        gd += pd;
+      const float d = fmaxf(xs[k] - tau, 0.f);
+      float pw, pd;
+      pow_pair<ECLS>(d, e, pw, pd);
+      f += pw;
+      gd += pd;
+    }
+    f = head_sum<LPH>(f);
+    gd = head_sum<LPH>(gd);
+    if (!done) {
+      const float step = (f - 1.f) / (e * gd);
+      const float nt = tau + step;
+      if (!(step > 0.f) || nt == tau) {
+        done = true;
+      } else {
+        tau = nt;
+        if (step <= 1e-7f * fmaxf(1.f, fabsf(tau))) done = true;
       }
     }
-    f = wave_sum(f);
-    gd = wave_sum(gd);
-    const float step = (f - 1.f) / (e * gd);
-    const float nt = tau + step;
-    if (!(step > 0.f) || nt == tau) break;
-    tau = nt;
-    if (step <= 1e-7f * fmaxf(1.f, fabsf(tau))) break;
   }
-  if (ecls == 1 || ecls == 2) {
+  if constexpr (ECLS == 1 || ECLS == 2) {
     // closed form on the support S = {x > tau}: sparsemax tau = (sum_S x - 1)/|S|;
     // 1.5-entmax tau = M - sqrt((1 - sum_S (x-M)^2)/|S|), M the mean over S
     float s1 = 0.f, cnt = 0.f, mn_in = INFINITY, mx_out = -INFINITY;
 #pragma unroll
     for (int k = 0; k < NK; ++k) {
-      if (xs[k] > tau) {
-        s1 += xs[k];
-        cnt += 1.f;
-        mn_in = fminf(mn_in, xs[k]);
-      } else {
-        mx_out = fmaxf(mx_out, xs[k]);
-      }
+      const bool in = xs[k] > tau;
+      s1 += in ? xs[k] : 0.f;
+      cnt += in ? 1.f : 0.f;
+      mn_in = fminf(mn_in, in ? xs[k] : INFINITY);
+      mx_out = fmaxf(mx_out, in ? -INFINITY : xs[k]);
     }
-    s1 = wave_sum(s1);
-    cnt = wave_sum(cnt);
-    mn_in = wave_min(mn_in);
-    mx_out = wave_max(mx_out);
+    s1 = head_sum<LPH>(s1);
+    cnt = head_sum<LPH>(cnt);
+    mn_in = head_min<LPH>(mn_in);
+    mx_out = head_max<LPH>(mx_out);
     float t2;
-    if (ecls == 1) {
+    if constexpr (ECLS == 1) {
       t2 = (s1 - 1.f) / cnt;
     } else {
       const float M = s1 / cnt;
       float q2 = 0.f;
 #pragma unroll
       for (int k = 0; k < NK; ++k) {
-        if (xs[k] > tau) {
-          const float d = xs[k] - M;
-          q2 = fmaf(d, d, q2);
-        }
+        const float dm = xs[k] > tau ? xs[k] - M : 0.f;
+        q2 = fmaf(dm, dm, q2);
       }
-      q2 = wave_sum(q2);
+      q2 = head_sum<LPH>(q2);
       t2 = M - sqrtf(fmaxf(0.f, (1.f - q2) / cnt));
     }
-    if (cnt > 0.f && t2 < mn_in && t2 >= mx_out) tau = t2;
+    if (live && cnt > 0.f && t2 < mn_in && t2 >= mx_out) tau = t2;
   }
   return tau;
 }
 
+constexpr float kFar = -1e30f;  // "not a routable chunk" in the threshold solve
+
 template <bool BF16, int D, int CP>
 __global__ __launch_bounds__(256) void route_kernel(Geom g, RouteParams p) {
-  constexpr int NK = CP / kWave;
-  __shared__ float U[16][CP];       // logits of one 16-head tile
+  constexpr int LPH = CP > 1024 ? 32 : 16;  // lanes per head in the solve
+  constexpr int HPW = 64 / LPH;             // heads per wave per pass
+  constexpr int NK = CP / LPH;              // values per lane in the solve
+  constexpr int USTR = CP + 16;     // LDS row stride: rows start 16 banks apart
+  __shared__ float U[16 * USTR];    // logits of one 16-head tile
   __shared__ float Wsum[CP];        // sum over the group's heads of p
-  __shared__ uint64_t Bits[NK];     // active bits
+  __shared__ uint64_t Bits[CP / 64];
   __shared__ float TauX[16];        // threshold (x units), or max u (softmax)
   __shared__ float Zs[16];          // softmax denominator (alpha = 1)
 
@@ -163,40 +195,49 @@ __global__ __launch_bounds__(256) void route_kernel(Geom g, RouteParams p) {
   const float xs_scale = smax ? 1.f : am1;
 
   for (int c = tid; c < n; c += 256) Wsum[c] = 0.f;
-  for (int w = tid; w < NK; w += 256) Bits[w] = 0ull;
+  for (int w = tid; w < CP / 64; w += 256) Bits[w] = 0ull;
 
   const int ntile_h = (g.G + 15) / 16;
   for (int ht = 0; ht < ntile_h; ++ht) {
     const int h0 = ht * 16;
     const int nh = min(16, g.G - h0);
     __syncthreads();
-    // ---- 1. logits
+    // ---- 1. logits U[q][c]: 16 heads x 16 chunks per MFMA tile, the
+    //         summary loads of 4 tiles issued before their MFMAs
     if constexpr (BF16) {
+      constexpr int KS = D / 32;
       const int r = lane & 15, gq = lane >> 4;
-      bf16x8 qa[D / 32];
+      bf16x8 qa[KS];
       const uint16_t* qrow =
           (const uint16_t*)p.q + ((tok * g.Hq + h * g.G + h0 + r) * (int64_t)D);
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) {
+      for (int ks = 0; ks < KS; ++ks) {
         u32x4 v = {0u, 0u, 0u, 0u};
         if (r < nh) v = ldg16(qrow + 32 * ks + 8 * gq);
         qa[ks] = as_bf16x8(v);
       }
       const int nct = (n + 15) >> 4;
-      for (int ct = wv; ct < nct; ct += 4) {
-        const int c = ct * 16 + r;
-        const uint16_t* krow =
-            (const uint16_t*)p.kbar + (((kb0 + c) * g.Hkv + h) * (int64_t)D);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int ct0 = 4 * wv; ct0 < nct; ct0 += 16) {
+        u32x4 kv[4][KS];
 #pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) {
-          u32x4 v = {0u, 0u, 0u, 0u};
-          if (c < n) v = ldg16(krow + 32 * ks + 8 * gq);
-          acc = mfma16x16x32(qa[ks], as_bf16x8(v), acc);
+        for (int j = 0; j < 4; ++j) {
+          // clamped to a valid summary row; columns past n are discarded below
+          const int c = min((ct0 + j) * 16 + r, n - 1);
+          const uint16_t* krow =
+              (const uint16_t*)p.kbar + (((kb0 + c) * g.Hkv + h) * (int64_t)D);
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) kv[j][ks] = ldg16(krow + 32 * ks + 8 * gq);
         }
-        if (c < n) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) U[4 * gq + j][c] = acc[j] * p.gamma_scale;
+        for (int j = 0; j < 4; ++j) {
+          const int c = (ct0 + j) * 16 + r;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(qa[ks], as_bf16x8(kv[j][ks]), acc);
+          if (c < n) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) U[(4 * gq + jj) * USTR + c] = acc[jj] * p.gamma_scale;
+          }
         }
       }
     } else {
@@ -214,34 +255,47 @@ __global__ __launch_bounds__(256) void route_kernel(Geom g, RouteParams p) {
           d = fmaf(a4[2], b4[2], d);
           d = fmaf(a4[3], b4[3], d);
         }
-        U[hh][c] = d * p.gamma_scale;
+        U[hh * USTR + c] = d * p.gamma_scale;
       }
     }
     __syncthreads();
-    // ---- 2. thresholds, one head per wave at a time
-    for (int hh = wv; hh < nh; hh += 4) {
+    // ---- 2. thresholds: each pass gives every wave HPW heads, LPH lanes each
+    for (int hb = 0; hb < nh; hb += 4 * HPW) {
+      const int hh = hb + wv * HPW + lane / LPH;
+      const int li = lane % LPH;
+      const bool live = hh < nh;
       float xs[NK];
       float xmax = -INFINITY;
+      const float* urow = U + (hh & 15) * USTR;  // in bounds for every lane
 #pragma unroll
       for (int k = 0; k < NK; ++k) {
-        const int c = lane + 64 * k;
-        const float x = (c < n) ? U[hh][c] * xs_scale : -INFINITY;
+        const int c = li + LPH * k;
+        const float uv = urow[c];
+        // entries past the row get a finite sentinel far below any threshold;
+        // the empty asm keeps the compiler from carrying the (c < n) predicate
+        // of every entry through the solve as a separate scalar mask
+        float x = (live && c < n) ? uv * xs_scale : kFar;
+        asm volatile("" : "+v"(x));
         xs[k] = x;
         xmax = fmaxf(xmax, x);
       }
-      xmax = wave_max(xmax);
+      xmax = head_max<LPH>(xmax);
       if (smax) {
         float z = 0.f;
 #pragma unroll
         for (int k = 0; k < NK; ++k) z += exp2f((xs[k] - xmax) * kLog2e);
-        z = wave_sum(z);
-        if (lane == 0) {
+        z = head_sum<LPH>(z);
+        if (live && li == 0) {
           TauX[hh] = xmax;
           Zs[hh] = z;
         }
       } else {
-        const float tau = solve_tau<NK>(xs, xmax, ex, ecls);
-        if (lane == 0) TauX[hh] = tau;
+        float tau;
+        if (ecls == 2) tau = solve_tau_row<NK, LPH, 2>(xs, xmax, ex, live);
+        else if (ecls == 1) tau = solve_tau_row<NK, LPH, 1>(xs, xmax, ex, live);
+        else if (ecls == 4) tau = solve_tau_row<NK, LPH, 4>(xs, xmax, ex, live);
+        else tau = solve_tau_row<NK, LPH, 0>(xs, xmax, ex, live);
+        if (live && li == 0) TauX[hh] = tau;
       }
     }
     __syncthreads();
@@ -256,14 +310,12 @@ __global__ __launch_bounds__(256) void route_kernel(Geom g, RouteParams p) {
         float ws = 0.f;
         for (int hh = 0; hh < nh; ++hh) {
           if (smax) {
-            ws += exp2f((U[hh][c] - TauX[hh]) * kLog2e) / Zs[hh];
+            ws += exp2f((U[hh * USTR + c] - TauX[hh]) * kLog2e) / Zs[hh];
             on = true;
           } else {
-            const float d = U[hh][c] * am1 - TauX[hh];
-            if (d > 0.f) {
-              on = true;
-              ws += pow_e(d, ex, ecls);
-            }
+            const float d = U[hh * USTR + c] * am1 - TauX[hh];
+            on = on || (d > 0.f);
+            ws += d > 0.f ? pow_e(d, ex, ecls) : 0.f;
           }
         }
         Wsum[c] += ws;
@@ -283,7 +335,7 @@ __global__ __launch_bounds__(256) void route_kernel(Geom g, RouteParams p) {
       lrow[c] = v;
     }
   }
-  for (int w = tid; w < g.W; w += 256) mrow[w] = (w < NK) ? Bits[w] : 0ull;
+  for (int w = tid; w < g.W; w += 256) mrow[w] = (w < CP / 64) ? Bits[w] : 0ull;
 }
 
 hipError_t launch_route(const Geom& g, const RouteParams& p, hipStream_t st) {

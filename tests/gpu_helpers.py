@@ -10,7 +10,11 @@ from sparse_hierarchical_attention_dash_amd import ops
 
 BAND = 1e-4          # mask bits may differ only this close to the threshold
 TOL = {"bf16": 2e-2, "f32": 1e-4}
-LSE_TOL = {"bf16": 2e-3, "f32": 1e-4}
+# LSE: the bf16 kernels normalise by the sum of the bf16-rounded attention
+# weights (the same weights that multiply V), each within 2^-8 relative of its
+# fp32 value, so log(sum) moves by at most 2^-8 = 3.9e-3; fp32 score and
+# accumulation errors add < 1e-4.  fp32 kernels keep fp32 weights.
+LSE_TOL = {"bf16": 2.0 ** -8 + 1e-4, "f32": 1e-4}
 
 
 def to_dev(a, dtype):
@@ -66,15 +70,29 @@ def summary_excuse(kbar_gpu, kbar_ora, Hkv, R, S):
     return ex
 
 
-def check_summaries(kbar_gpu, kbar_ora, dtype):
+def summary_bound(k, B):
+    """Per (chunk, head, dim) bound on the fp32 error of a summary: the
+    weights sum to 1, so the weighted sum of B keys carries at most about
+    B * 2^-24 (accumulation) + 1e-6 (weights) times the largest |key|."""
+    L, Hkv, D = k.shape
+    C = L // B
+    kk = np.abs(k[:C * B]).reshape(C, B, Hkv, D).max(axis=1)
+    return (B * 2.0 ** -24 + 1e-6) * kk
+
+
+def check_summaries(kbar_gpu, kbar_ora, dtype, k=None, B=64):
+    fp = summary_bound(k, B) if k is not None else 2e-6
     if dtype == "f32":
-        np.testing.assert_allclose(kbar_gpu, kbar_ora, atol=2e-6, rtol=1e-5)
+        assert np.all(np.abs(kbar_gpu - kbar_ora) <= fp + 1e-5 * np.abs(kbar_ora))
         return 0
-    # bf16: identical except where fp32 accumulation lands on the other side
-    # of a rounding midpoint, which moves the result by one unit in the last
-    # place (2^-8 relative at most)
+    # bf16: the fp32 result, within the bound above of the exact value, is
+    # rounded once; it can land one unit in the last place (2^-7 relative at
+    # most) away from the rounded exact value, or more where cancellation
+    # makes the value small next to the fp32 error
     d = np.abs(kbar_gpu - kbar_ora)
-    ulp = np.abs(kbar_ora) * 2.0 ** -7 + 1e-30
+    if d.size == 0:
+        return 0.0
+    ulp = np.abs(kbar_ora) * 2.0 ** -7 + 2 * fp
     assert np.all(d <= ulp), float(np.max(d / ulp))
     frac = float(np.mean(d > 0))
     assert frac < 1e-3, frac
@@ -101,7 +119,7 @@ def prefill_case(d, B, alpha, gamma, sigma, dtype, gqa=True, rows=None, scale=0.
                     to_bf16=(dtype == "bf16"), scale=(scale if scale > 0 else None), rows=rows,
                     num_slots=S)
     kb_gpu = kb.to(torch.float64).cpu().numpy()
-    check_summaries(kb_gpu, ref["kbar"], dtype)
+    check_summaries(kb_gpu, ref["kbar"], dtype, kx, B)
     s = scale if scale > 0 else 1.0 / math.sqrt(D)
     margin = O.routing_margin(qx, ref["kbar"], B, gamma, s, G, ref["tau_hat"], rows, S)
     bits = unpack_bits(ab, S)[:, rows, :]
