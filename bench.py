@@ -122,7 +122,7 @@ def main():
     ap.add_argument("--prefill", default="prefill_64k_needles")
     ap.add_argument("--decode", default="decode_128k")
     ap.add_argument("--only", choices=["both", "prefill", "decode"], default="both")
-    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--cpu-rows", type=int, default=1536)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-ref", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (the "

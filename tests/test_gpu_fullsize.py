@@ -1,0 +1,172 @@
+"""GPU parity at the full benchmark sizes, in the launch configuration bench.py
+times, on rows sampled across each sequence (the oracle computes them one by
+one), plus properties checked on every row of the full outputs.
+
+Workloads (see sparse_hierarchical_attention_dash_amd/workloads.py): bf16
+16K prefill, bf16 64K prefill with planted chunks, bf16 decode of 16
+sequences with 128K caches, and packed varlen prefill (8 sequences, 4K-128K,
+B = 128, alpha in {1.25, 1.5, 2}).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sparse_hierarchical_attention_dash_amd import ops
+from sparse_hierarchical_attention_dash_amd import workloads as W
+
+from gpu_helpers import (LSE_TOL, TOL, check_summaries, compare_masks, flush, summary_excuse,
+                         to_dev, unpack_bits)
+
+pytestmark = pytest.mark.gpu
+
+
+def sample_rows(L, B, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.integers(0, L, n).tolist())
+    rows |= {0, B - 1, B, L - 1, L - 2, (L // B - 1) * B, L // 2}
+    return sorted(r for r in rows if 0 <= r < L)
+
+
+def full_mask_properties(bits_all, L, B, start=0):
+    """Every bit past a row's routable range is zero."""
+    n = (np.arange(L) // B)
+    S = bits_all.shape[-1]
+    beyond = np.arange(S)[None, None, :] >= n[None, :, None]
+    assert not (bits_all[:, start:start + L] & beyond).any()
+
+
+@pytest.mark.parametrize("name,nrows", [("prefill_16k", 48), ("prefill_64k_needles", 40)])
+def test_prefill_full_size(name, nrows):
+    flush(f"full-size prefill {name}")
+    d = W.make(name)
+    w = d["workload"]
+    q, qx = to_dev(d["q"], "bf16")
+    k, kx = to_dev(d["k"], "bf16")
+    v, vx = to_dev(d["v"], "bf16")
+    qb = torch.from_numpy(d["qbar"]).cuda()
+    L = w.seqlen
+    out, lse, ab = ops.attn_prefill(q, k, v, qb, w.B, alpha=w.alpha, gamma=w.gamma,
+                                    sigma=w.sigma, return_lse=True, return_active_blocks=True)
+    kb = ops.summarize(k, qb, w.B)
+    torch.cuda.synchronize()
+    del q, k, v
+    S = -(-L // w.B)
+    bits_all = unpack_bits(ab, S)
+    full_mask_properties(bits_all, L, w.B)
+    support = bits_all.sum() / (np.sum(np.arange(L) // w.B) * w.Hkv)
+    assert 0.15 < support < 0.35, support          # calibrated to about 25%
+    rows = sample_rows(L, w.B, nrows, seed=5)
+    ref = O.prefill(qx, kx, vx, d["qbar"], w.B, w.alpha, w.gamma, w.sigma, True, to_bf16=True,
+                    rows=rows, num_slots=S)
+    kbg = kb.to(torch.float64).cpu().numpy()
+    check_summaries(kbg, ref["kbar"], "bf16", kx, w.B)
+    G = w.Hq // w.Hkv
+    margin = O.routing_margin(qx, ref["kbar"], w.B, w.gamma, 1 / math.sqrt(w.D), G,
+                              ref["tau_hat"], rows, S)
+    ex = summary_excuse(kbg, ref["kbar"], w.Hkv, len(rows), S)
+    flips = compare_masks(bits_all[:, rows], ref["mask"][:, rows], margin, ex, name)
+    o = out[rows].to(torch.float64).cpu().numpy()
+    err = float(np.max(np.abs(o - ref["out"])))
+    assert err <= TOL["bf16"], err
+    lerr = float(np.max(np.abs(lse.cpu().numpy()[:, rows] - ref["lse"])))
+    assert lerr <= LSE_TOL["bf16"], lerr
+    flush(f"  {name}: rows {len(rows)} max-abs {err:.2e} lse {lerr:.2e} flips {flips} "
+          f"support {support:.3f}")
+
+
+def test_decode_full_size():
+    flush("full-size decode")
+    d = W.make("decode_128k")
+    w = d["workload"]
+    q, qx = to_dev(d["q"], "bf16")
+    kc = torch.from_numpy(d["k_cache"]).to(torch.bfloat16).cuda()
+    vc = torch.from_numpy(d["v_cache"]).to(torch.bfloat16).cuda()
+    cap = w.seqlen
+    qbt = torch.from_numpy(d["qbar"]).cuda()
+    kbar = ops.summarize(kc.view(-1, w.Hkv, w.D), qbt, w.B, max_seqlen=cap).view(
+        w.batch, cap // w.B, w.Hkv, w.D)
+    # the bench's lengths plus a ragged set in the same launch shape
+    for sl in (d["seqlens"], np.array([cap, 1, 65, cap - 1, 70000, 64, 128, 4097] * 2,
+                                      dtype=np.int32)):
+        seq = torch.from_numpy(sl).cuda()
+        out, lse, ab = ops.attn_decode(q, kc, vc, seq, kbar, w.B, alpha=w.alpha, gamma=w.gamma,
+                                       sigma=w.sigma, return_lse=True, return_active_blocks=True)
+        torch.cuda.synchronize()
+        S = cap // w.B
+        bits = unpack_bits(ab, S)
+        o = out.to(torch.float64).cpu().numpy()
+        le = lse.cpu().numpy()
+        G = w.Hq // w.Hkv
+        for b in (0, 3, 7, 15):
+            L = int(sl[b])
+            kcx = kc[b, :L].to(torch.float64).cpu().numpy()
+            vcx = vc[b, :L].to(torch.float64).cpu().numpy()
+            kbo = O.summarize(kcx, d["qbar"], w.B, to_bf16=True)
+            r = O.decode(qx[b], kcx, vcx, kbo, L, w.B, w.alpha, w.gamma, w.sigma)
+            n = (L - 1) // w.B
+            qq = np.zeros((L, w.Hq, w.D))
+            qq[L - 1] = qx[b]
+            th = np.full((w.Hq, L), np.nan)
+            th[:, L - 1] = r["tau_hat"]
+            margin = O.routing_margin(qq, kbo, w.B, w.gamma, 1 / math.sqrt(w.D), G, th,
+                                      [L - 1], S)
+            om = np.zeros((w.Hkv, 1, S), bool)
+            om[:, 0, :n] = r["mask"]
+            kbg = kbar[b].to(torch.float64).cpu().numpy()[:kbo.shape[0]]
+            ex = summary_excuse(kbg, kbo, w.Hkv, 1, S)
+            compare_masks(bits[:, b:b + 1], om, margin, ex, f"decode b={b} L={L}")
+            assert not bits[:, b, n:].any()
+            err = float(np.max(np.abs(o[b] - r["out"])))
+            assert err <= TOL["bf16"], (b, L, err)
+            assert np.max(np.abs(le[:, b] - r["lse"])) <= LSE_TOL["bf16"]
+        flush(f"  decode lengths {sorted(set(sl.tolist()))[:4]}...: ok")
+
+
+def test_varlen_full_size():
+    flush("full-size varlen")
+    d = W.make("varlen_mixed")
+    w = d["workload"]
+    cu = d["cu_seqlens"]
+    lens = np.diff(cu)
+    q, qx = to_dev(d["q"], "bf16")
+    k, kx = to_dev(d["k"], "bf16")
+    v, vx = to_dev(d["v"], "bf16")
+    qb = torch.from_numpy(d["qbar"]).cuda()
+    cut = torch.from_numpy(cu).cuda()
+    alphas = d["alphas"]
+    out, lse, ab = ops.attn_prefill(q, k, v, qb, w.B, alpha=1.5, gamma=w.gamma, sigma=w.sigma,
+                                    alpha_per_seq=torch.from_numpy(alphas).cuda(),
+                                    cu_seqlens=cut, max_seqlen=int(lens.max()),
+                                    return_lse=True, return_active_blocks=True)
+    kb = ops.summarize(k, qb, w.B, cu_seqlens=cut, max_seqlen=int(lens.max()))
+    torch.cuda.synchronize()
+    S = -(-int(lens.max()) // w.B)
+    bits_all = unpack_bits(ab, S)
+    kbg = kb.to(torch.float64).cpu().numpy()
+    o = out.to(torch.float64).cpu().numpy()
+    le = lse.cpu().numpy()
+    G = w.Hq // w.Hkv
+    off = 0
+    for s in range(len(lens)):
+        a, b = int(cu[s]), int(cu[s + 1])
+        L = b - a
+        full_mask_properties(bits_all, L, w.B, start=a)
+        rows = sample_rows(L, w.B, 6, seed=s)
+        r = O.prefill(qx[a:b], kx[a:b], vx[a:b], d["qbar"], w.B, float(alphas[s]), w.gamma,
+                      w.sigma, True, to_bf16=True, rows=rows, num_slots=S)
+        C = L // w.B
+        check_summaries(kbg[off:off + C], r["kbar"], "bf16", kx[a:b], w.B)
+        margin = O.routing_margin(qx[a:b], r["kbar"], w.B, w.gamma, 1 / math.sqrt(w.D), G,
+                                  r["tau_hat"], rows, S)
+        ex = summary_excuse(kbg[off:off + C], r["kbar"], w.Hkv, len(rows), S)
+        rg = [a + i for i in rows]
+        compare_masks(bits_all[:, rg], r["mask"][:, rows], margin, ex, f"varlen seq {s}")
+        err = float(np.max(np.abs(o[rg] - r["out"])))
+        assert err <= TOL["bf16"], (s, err)
+        assert np.max(np.abs(le[:, rg] - r["lse"])) <= LSE_TOL["bf16"]
+        off += C
+        flush(f"  varlen seq {s} (L={L}, alpha={alphas[s]}): max-abs {err:.2e}")
