@@ -173,6 +173,7 @@ def main():
         logp = torch.empty((wp.Hkv, T, lay.chunk_slots), dtype=torch.float32, device=dev)
         out = torch.empty_like(q)
         ws_route = torch.empty(256, dtype=torch.uint8, device=dev)
+        ws_sparse = ops.sparse_workspace(q, k, wp.B)
         log(f"prefill inputs {wp.name}: T={T} Hq={wp.Hq} Hkv={wp.Hkv} D={wp.D} B={wp.B} "
             f"({time.time() - t0:.1f}s)")
     if do_dec:
@@ -202,7 +203,7 @@ def main():
             ops.route(q, kbar, wp.Hkv, wp.B, alpha=wp.alpha, gamma=wp.gamma, sigma=wp.sigma,
                       mask_out=mask, log_prior_out=logp, log_prior=True, workspace=ws_route)
             ev[2].record(stream)
-            ops.attn_sparse(q, k, v, mask, logp, wp.B, out=out)
+            ops.attn_sparse(q, k, v, mask, logp, wp.B, out=out, workspace=ws_sparse)
             ev[3].record(stream)
         if do_dec:
             ev[4].record(stream)

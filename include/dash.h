@@ -180,11 +180,13 @@ dash_status dash_attn_prefill(const dash_shape* shape, const void* q, const void
  *   log_prior      [Hkv, T, C_slots] fp32          (input; read where a bit is set)
  *   out            [T, Hq, D] dtype                (output)
  *   lse            [Hq, T] fp32 or NULL            (output)
- * Needs no workspace (dash_workspace_size(DASH_OP_SPARSE, ...) is 0). */
+ * The workspace (dash_workspace_size(DASH_OP_SPARSE, ...)) holds a transposed
+ * copy of V for bf16 inputs with a GQA group of 16 or more. */
 dash_status dash_attn_sparse(const dash_shape* shape, const void* q, const void* k,
                              const void* v, const uint64_t* active_blocks,
                              const float* log_prior, float softmax_scale, int enable_gqa,
-                             void* out, float* lse, void* stream);
+                             void* out, float* lse, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /* One incremental decode step: each batch entry b has one new query whose
  * key and value are already written at position seqlens[b]-1 of its cache.

@@ -96,7 +96,7 @@ def lib():
     L.dash_attn_prefill.argtypes = [_SHAPE, _P, _P, _P, _P, _F, _P, _F, _F, _F, _I, _P, _P,
                                     _P, _P, _SZ, _P]
     L.dash_attn_sparse.restype = _I
-    L.dash_attn_sparse.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _F, _I, _P, _P, _P]
+    L.dash_attn_sparse.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _F, _I, _P, _P, _P, _SZ, _P]
     L.dash_attn_decode.restype = _I
     L.dash_attn_decode.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _F, _F, _F, _F, _I, _P, _P, _P,
                                    _P, _SZ, _P]

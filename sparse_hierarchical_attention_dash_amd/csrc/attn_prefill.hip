@@ -334,6 +334,419 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_attn_bf16_kernel(
   }
 }
 
+// ---------------------------------------------------------------- V^T + ring
+
+// First padded column of sequence s in V^T.
+__device__ __forceinline__ int64_t pad_off(const Geom& g, int s) {
+  return g.cu_seqlens ? (int64_t)g.cu_pad[s] : (int64_t)s * ((g.max_seqlen + 63) / 64 * 64);
+}
+
+// V^T[h][d][pad_off(s) + 64 kb + vt_col(j)] = v[start + 64 kb + j][h][d], zero
+// past the sequence end: the PV operand layout, so the attention kernel can
+// copy 128-byte rows of it straight into LDS.  One workgroup per
+// (64-key block, sequence, KV head).
+template <int D>
+__global__ __launch_bounds__(256) void vt_transpose_kernel(Geom g, const uint16_t* __restrict__ v,
+                                                           uint16_t* __restrict__ vt,
+                                                           int64_t Tp) {
+  constexpr int KPT = D / 32;           // keys per thread (4 or 2)
+  constexpr int NKG = 64 / KPT;
+  const int kb = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
+  const SeqInfo si = seq_info(g.cu_seqlens, nullptr, s, g.max_seqlen, g.B);
+  if (kb * 64 >= si.len) return;
+  const int tid = threadIdx.x;
+  const int kg = tid % NKG, vpiece = tid / NKG;
+  u32x4 x[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int key = kb * 64 + kg * KPT + i;
+    u32x4 z = {0u, 0u, 0u, 0u};
+    if (key < si.len) z = ldg16(v + ((si.start + key) * g.Hkv + h) * (int64_t)D + vpiece * 8);
+    x[i] = z;
+  }
+  const int64_t col = pad_off(g, s) + kb * 64 + vt_col(kg * KPT);
+  uint16_t* base = vt + ((int64_t)h * D + vpiece * 8) * Tp + col;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    if constexpr (KPT == 4) {
+      const u32x2 lo = {__builtin_amdgcn_perm(x[1][w], x[0][w], 0x05040100u),
+                        __builtin_amdgcn_perm(x[3][w], x[2][w], 0x05040100u)};
+      const u32x2 hi = {__builtin_amdgcn_perm(x[1][w], x[0][w], 0x07060302u),
+                        __builtin_amdgcn_perm(x[3][w], x[2][w], 0x07060302u)};
+      *reinterpret_cast<u32x2*>(base + (2 * w) * Tp) = lo;
+      *reinterpret_cast<u32x2*>(base + (2 * w + 1) * Tp) = hi;
+    } else {
+      *reinterpret_cast<uint32_t*>(base + (2 * w) * Tp) =
+          __builtin_amdgcn_perm(x[1][w], x[0][w], 0x05040100u);
+      *reinterpret_cast<uint32_t*>(base + (2 * w + 1) * Tp) =
+          __builtin_amdgcn_perm(x[1][w], x[0][w], 0x07060302u);
+    }
+  }
+}
+
+constexpr int kRing = 4;  // LDS slots; up to 3 blocks in flight
+
+template <int D>
+struct RingCfg {
+  static constexpr int KROW = D * 2;                  // bytes per K row
+  static constexpr int KP = KROW / 16;                // 16-byte pieces per K row
+  static constexpr int KBYTES = 64 * KROW;
+  static constexpr int VROW = 128;                    // bytes per V^T row (64 keys)
+  static constexpr int VBYTES = D * VROW;
+  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int KLD = KBYTES / (16 * kPrefillThreads);  // DMA loads per thread
+  static constexpr int VLD = VBYTES / (16 * kPrefillThreads);
+  static constexpr int LPS = KLD + VLD;
+};
+
+// XOR swizzle of the 16-byte pieces of an LDS row: 16 consecutive rows read
+// at one logical piece land in 16 different 4-bank groups.
+template <int P>
+__device__ __forceinline__ int swz(int row) {
+  return P == 16 ? (row & 15) : ((row >> 1) & 7);
+}
+
+// One 16-byte direct global->LDS load per lane: lane l of the wave writes
+// LDS bytes lds_base + 16 l .. +15 (lds_base wave-uniform).  Issued from asm so
+// the compiler neither tracks nor waits on it: the data lands in LDS, no
+// register is written, the address registers are consumed at issue, and the
+// ring's own counted vmcnt waits plus a barrier order it before every read.
+// (Vector-memory operations the compiler does not know about can only make
+// its own counted waits stricter.)
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_base), "v"(gptr)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)p;  // low 32 bits of a flat LDS address = LDS offset
+}
+
+// Direct global->LDS loads of one 64-key block into a ring slot: K rows
+// key0 + krow (clamped to kmax, the last key the workgroup may read) and the
+// block's V^T rows, each thread moving its fixed 16-byte pieces.
+template <int D>
+__device__ __forceinline__ void ring_issue(const uint8_t* kbase, int64_t krs,
+                                           const int (&krow)[RingCfg<D>::KLD],
+                                           const int (&kpiece)[RingCfg<D>::KLD],
+                                           const uint8_t* const (&vbase)[RingCfg<D>::VLD],
+                                           int key0, int kmax, uint8_t* slot, int wv) {
+  using R = RingCfg<D>;
+  const uint32_t sb = __builtin_amdgcn_readfirstlane(lds_addr(slot) + wv * R::KLD * 1024);
+  const uint32_t vb =
+      __builtin_amdgcn_readfirstlane(lds_addr(slot) + R::KBYTES + wv * R::VLD * 1024);
+#pragma unroll
+  for (int i = 0; i < R::KLD; ++i) {
+    const int key = min(key0 + krow[i], kmax);
+    lds_dma16(kbase + key * krs + kpiece[i] * 16, sb + i * 1024);
+  }
+#pragma unroll
+  for (int i = 0; i < R::VLD; ++i) lds_dma16(vbase[i] + (int64_t)key0 * 2, vb + i * 1024);
+}
+
+template <int D, bool MASKED>
+__device__ __forceinline__ void visit_ring(const uint8_t* __restrict__ ks_,
+                                           const uint8_t* __restrict__ vt_,
+                                           const int (&koff)[D / 32], const int (&voff)[2],
+                                           const bf16x8 (&qa)[D / 32], f32x4 (&o)[D / 16],
+                                           f32x4& lacc, float& m, float sl2, float bz,
+                                           int kbase, int rpos) {
+  using R = RingCfg<D>;
+  constexpr int KS = D / 32;
+  constexpr int DT = D / 16;
+  f32x4 sacc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const bf16x8 ak =
+          as_bf16x8(*reinterpret_cast<const u32x4*>(ks_ + koff[ks] + 16 * t * R::KROW));
+      sacc[t] = mfma16x16x32(ak, qa[ks], sacc[t]);
+    }
+  }
+  bool ok[4][4];
+  float amax = -INFINITY;
+  if constexpr (MASKED) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ok[t][j] = kbase + 16 * t + j <= rpos;
+        amax = fmaxf(amax, ok[t][j] ? sacc[t][j] : -INFINITY);
+      }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      amax = fmaxf(amax, fmaxf(fmaxf(sacc[t][0], sacc[t][1]), fmaxf(sacc[t][2], sacc[t][3])));
+  }
+  amax = fmaxf(amax, xor16(amax));
+  amax = fmaxf(amax, xor32(amax));
+  const float zmax = amax * sl2 + bz;
+  const bool up = zmax > m + kRescale;
+  if (__ballot(up) != 0ull) {
+    const float mn = up ? zmax : m;
+    const float alpha = up ? exp2f(m - mn) : 1.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    lacc *= alpha;
+    m = mn;
+  }
+  const float off = bz - m;
+  uint32_t pk[4][2];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    float pv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      pv[j] = __builtin_amdgcn_exp2f(fmaf(sacc[t][j], sl2, off));
+      if constexpr (MASKED) pv[j] = ok[t][j] ? pv[j] : 0.f;
+    }
+    pk[t][0] = cvt_pk_bf16(pv[0], pv[1]);
+    pk[t][1] = cvt_pk_bf16(pv[2], pv[3]);
+  }
+  const u32x4 ones_u = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+  const bf16x8 ones = as_bf16x8(ones_u);
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    const u32x4 pb = {pk[2 * s2][0], pk[2 * s2][1], pk[2 * s2 + 1][0], pk[2 * s2 + 1][1]};
+    const bf16x8 pbv = as_bf16x8(pb);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const bf16x8 av =
+          as_bf16x8(*reinterpret_cast<const u32x4*>(vt_ + voff[s2] + 16 * dt * R::VROW));
+      o[dt] = mfma16x16x32(av, pbv, o[dt]);
+    }
+    lacc = mfma16x16x32(ones, pbv, lacc);
+  }
+}
+
+// Prefill attention for G >= 16 (every 16-row tile is one position's heads):
+// the blocks of the workgroup's list stream through a 4-slot LDS ring filled by
+// direct global->LDS loads (K rows from K, V^T rows from the V^T workspace),
+// three blocks ahead of the one being consumed.  The loop is unrolled by the
+// ring depth so every slot is a distinct LDS array; waits are counted
+// (vmcnt) and the barrier carries no fence.  Mask words and biases are read
+// with scalar loads so that only the ring's loads are vector memory traffic.
+template <int D>
+__global__ __launch_bounds__(kPrefillThreads, 1) void prefill_attn_ring_kernel(
+    Geom g, PrefillParams p, TileGeom tg) {
+  constexpr int NTH = kPrefillThreads;
+  constexpr int TWM = kMaxTilesPerWave;
+  using R = RingCfg<D>;
+  constexpr int KS = D / 32;
+  constexpr int DT = D / 16;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring0[R::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring1[R::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring2[R::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring3[R::STAGE];
+  __shared__ unsigned long long Umask[32];
+  __shared__ int Wpref[33];
+  __shared__ uint16_t Blist[2048];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int r = lane & 15, gq = lane >> 4;
+  const int tile = tg.tiles_per_seq - 1 - (int)blockIdx.x;
+  const int s = blockIdx.y, h = blockIdx.z;
+  const SeqInfo si = seq_info(g.cu_seqlens, nullptr, s, g.max_seqlen, g.B);
+  const int p0 = tile * tg.P;
+  if (p0 >= si.len) return;
+  const int pend = min(p0 + tg.P, si.len);
+  const int cdiag = p0 / g.B;
+  const int64_t T = g.T;
+  const int W = g.W;
+  const unsigned long long* __restrict__ mask = (const unsigned long long*)p.mask;
+  // read-only for the whole kernel: through the constant address space the
+  // wave-uniform mask-word and bias reads of the loop become scalar loads, so
+  // they neither count against nor wait on the ring's vector-memory counter
+  typedef const __attribute__((address_space(4))) unsigned long long cmask_t;
+  typedef const __attribute__((address_space(4))) float cfloat_t;
+  cmask_t* smask = (cmask_t*)p.mask;
+  cfloat_t* slogp = (cfloat_t*)p.log_prior;
+
+  int rpos[TWM], rhead[TWM];
+  bool rvalid[TWM], tvalid[TWM];
+#pragma unroll
+  for (int u = 0; u < TWM; ++u) {
+    const int ti = wv * tg.TW + u;
+    rpos[u] = p0 + ti / tg.HT;
+    rhead[u] = (ti % tg.HT) * 16 + r;
+    tvalid[u] = (u < tg.TW) && (ti < tg.NT);
+    rvalid[u] = tvalid[u] && (rpos[u] < pend);
+  }
+  bf16x8 qa[TWM][KS];
+#pragma unroll
+  for (int u = 0; u < TWM; ++u) {
+    const int64_t qrow = ((si.start + rpos[u]) * g.Hq + h * g.G + rhead[u]) * (int64_t)D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (rvalid[u]) v = ldg16((const uint16_t*)p.q + qrow + 32 * ks + 8 * gq);
+      qa[u][ks] = as_bf16x8(v);
+    }
+  }
+
+  // ---- ordered list of the union of the positions' active chunks
+  if (tid < 32) Umask[tid] = 0ull;
+  __syncthreads();
+  {
+    const int npos = pend - p0;
+    const unsigned long long* mbase = mask + ((int64_t)h * T + si.start + p0) * W;
+    for (int idx = tid; idx < npos * W; idx += NTH) {
+      const int w = idx % W;
+      const unsigned long long v = mbase[idx] & routable_bits(w, cdiag);
+      if (v) atomicOr(&Umask[w], v);
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    int cnt = (tid < W) ? __popcll(Umask[tid]) : 0;
+    int inc = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o);
+      if (lane >= o) inc += y;
+    }
+    if (tid < 33) Wpref[tid] = inc - cnt;
+  }
+  __syncthreads();
+  if (tid < W) {
+    unsigned long long v = Umask[tid];
+    int o = Wpref[tid];
+    while (v) {
+      Blist[o++] = (uint16_t)(tid * 64 + __ffsll(v) - 1);
+      v &= v - 1;
+    }
+  }
+  __syncthreads();
+  const int SB = g.B / 64;
+  const int nrouted = Wpref[W] * SB;
+  const int ndiag = (pend - cdiag * g.B + 63) / 64;
+  const int NS = nrouted + ndiag;
+
+  // ---- per-thread DMA sources (piece layout fixed per thread)
+  const int64_t krs = (int64_t)g.Hkv * D * 2;  // bytes between consecutive keys
+  const uint8_t* kbase = (const uint8_t*)p.k + (si.start * (int64_t)g.Hkv + h) * D * 2;
+  int krow[R::KLD], kpiece[R::KLD];
+#pragma unroll
+  for (int i = 0; i < R::KLD; ++i) {
+    const int o = (wv * R::KLD + i) * 1024 + lane * 16;
+    krow[i] = o / R::KROW;
+    kpiece[i] = ((o % R::KROW) / 16) ^ swz<R::KP>(krow[i]);
+  }
+  const uint8_t* vbase[R::VLD];
+#pragma unroll
+  for (int i = 0; i < R::VLD; ++i) {
+    const int o = (wv * R::VLD + i) * 1024 + lane * 16;
+    const int d = o / R::VROW;
+    const int pc = ((o % R::VROW) / 16) ^ swz<8>(d);
+    vbase[i] = (const uint8_t*)p.vt + (((int64_t)h * D + d) * p.Tp + pad_off(g, s)) * 2 + pc * 16;
+  }
+  auto stage_key0 = [&](int st) -> int {
+    if (st < nrouted) {
+      const int c = Blist[st / SB];
+      return c * g.B + (st % SB) * 64;
+    }
+    return cdiag * g.B + (st - nrouted) * 64;
+  };
+  auto issue = [&](int st, uint8_t* slot) {
+    ring_issue<D>(kbase, krs, krow, kpiece, vbase, stage_key0(st), pend - 1, slot, wv);
+  };
+
+  // ---- per-tile state
+  f32x4 o[TWM][DT];
+  f32x4 lacc[TWM];
+  float m[TWM];
+  unsigned long long mword[TWM];
+  int mw_idx[TWM];
+  int64_t prow[TWM];
+#pragma unroll
+  for (int u = 0; u < TWM; ++u) {
+    m[u] = -INFINITY;
+    lacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mword[u] = 0ull;
+    mw_idx[u] = -1;
+    prow[u] = uniform64((int64_t)h * T + si.start + min(rpos[u], pend - 1));
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float sl2 = p.scale * kLog2e;
+  int koff[KS], voff[2];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = r * R::KROW + (((4 * ks + gq) ^ swz<R::KP>(r)) * 16);
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) voff[s2] = r * R::VROW + (((4 * s2 + gq) ^ swz<8>(r)) * 16);
+
+  // Every step issues exactly one block's loads (past the end of the list it
+  // re-reads the last block into the free slot, which no later step reads), so
+  // when step st waits, exactly two blocks' loads are younger than its own:
+  // one fixed counted wait, and the compiler can prove the slot is complete.
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4));  // Q and mask reads done first
+  issue(0, ring0);
+  issue(min(1, NS - 1), ring1);
+  issue(min(2, NS - 1), ring2);
+
+  auto step = [&](int st, const uint8_t* slot, uint8_t* refill) {
+    // own loads of this slot done (the two younger blocks may stay in flight),
+    // this wave's LDS reads of the slot about to be refilled done
+    __builtin_amdgcn_s_waitcnt(((2 * R::LPS) & 15) | (7 << 4));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(min(st + 3, NS - 1), refill);
+    const bool diag = st >= nrouted;
+    const int c = __builtin_amdgcn_readfirstlane(diag ? cdiag : (int)Blist[st / SB]);
+    const int key0 = stage_key0(st);
+#pragma unroll
+    for (int u = 0; u < TWM; ++u) {
+      if (!tvalid[u]) break;
+      if (!rvalid[u]) continue;
+      if (!diag) {
+        const int wi = c >> 6;
+        if (wi != mw_idx[u]) {
+          mw_idx[u] = wi;
+          mword[u] = smask[prow[u] * W + wi];
+        }
+        if (!((mword[u] >> (c & 63)) & 1ull)) continue;
+        const float bz = slogp[prow[u] * g.C_slots + c] * kLog2e;
+        visit_ring<D, false>(slot, slot + R::KBYTES, koff, voff, qa[u], o[u], lacc[u], m[u], sl2,
+                             bz, 0, 0);
+      } else {
+        visit_ring<D, true>(slot, slot + R::KBYTES, koff, voff, qa[u], o[u], lacc[u], m[u], sl2,
+                            0.f, key0 + 4 * gq, rpos[u]);
+      }
+    }
+  };
+  for (int st = 0; st < NS; st += kRing) {
+    step(st, ring0, ring3);
+    if (st + 1 < NS) step(st + 1, ring1, ring0);
+    if (st + 2 < NS) step(st + 2, ring2, ring1);
+    if (st + 3 < NS) step(st + 3, ring3, ring2);
+  }
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4));  // no ring load outlives the kernel
+
+#pragma unroll
+  for (int u = 0; u < TWM; ++u) {
+    if (!tvalid[u]) break;
+    if (!rvalid[u]) continue;
+    const float lt = lacc[u][0];
+    const float inv = 1.f / lt;
+    const int64_t tok = si.start + rpos[u];
+    uint16_t* orow = (uint16_t*)p.out + (tok * g.Hq + h * g.G + rhead[u]) * (int64_t)D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const u32x2 w = {cvt_pk_bf16(o[u][dt][0] * inv, o[u][dt][1] * inv),
+                       cvt_pk_bf16(o[u][dt][2] * inv, o[u][dt][3] * inv)};
+      *reinterpret_cast<u32x2*>(orow + 16 * dt + 4 * gq) = w;
+    }
+    if (p.lse && gq == 0)
+      p.lse[(int64_t)(h * g.G + rhead[u]) * T + tok] = (m[u] + __log2f(lt)) * kLn2;
+  }
+}
+
 // ---------------------------------------------------------------- fp32 rows
 
 template <int D>
@@ -433,20 +846,32 @@ static TileGeom make_tiles(const Geom& g) {
   return t;
 }
 
+bool prefill_uses_ring(const Geom& g) { return g.bf16 && g.G >= 16; }
+
 hipError_t launch_prefill_attn(const Geom& g, const PrefillParams& p, hipStream_t st) {
   if (g.T == 0) return hipSuccess;
   if (g.bf16) {
     const TileGeom tg = make_tiles(g);
     dim3 grid(tg.tiles_per_seq, g.num_seqs, g.Hkv);
-    const bool uni = g.G >= 16;
+    if (prefill_uses_ring(g)) {
+      dim3 tgrid((g.max_seqlen + 63) / 64, g.num_seqs, g.Hkv);
+      if (g.D == 64) {
+        hipLaunchKernelGGL(vt_transpose_kernel<64>, tgrid, dim3(256), 0, st, g,
+                           (const uint16_t*)p.v, (uint16_t*)p.vt, p.Tp);
+        hipLaunchKernelGGL(prefill_attn_ring_kernel<64>, grid, dim3(kPrefillThreads), 0, st, g,
+                           p, tg);
+      } else {
+        hipLaunchKernelGGL(vt_transpose_kernel<128>, tgrid, dim3(256), 0, st, g,
+                           (const uint16_t*)p.v, (uint16_t*)p.vt, p.Tp);
+        hipLaunchKernelGGL(prefill_attn_ring_kernel<128>, grid, dim3(kPrefillThreads), 0, st, g,
+                           p, tg);
+      }
+      return hipGetLastError();
+    }
 #define DASH_PRE(DD, U)                                                                   \
   hipLaunchKernelGGL((prefill_attn_bf16_kernel<DD, U>), grid, dim3(kPrefillThreads), 0, st, \
                      g, p, tg)
-    if (g.D == 64) {
-      if (uni) DASH_PRE(64, true); else DASH_PRE(64, false);
-    } else {
-      if (uni) DASH_PRE(128, true); else DASH_PRE(128, false);
-    }
+    if (g.D == 64) DASH_PRE(64, false); else DASH_PRE(128, false);
 #undef DASH_PRE
   } else {
     dim3 grid((unsigned)g.T, g.Hq);

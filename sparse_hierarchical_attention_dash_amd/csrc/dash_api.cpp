@@ -86,21 +86,48 @@ float eff_scale(const Geom& g, float scale) {
 size_t elt(const Geom& g) { return g.bf16 ? 2 : 4; }
 
 // Workspace layouts (offsets in bytes; every piece 256-byte aligned).
+// Varlen metadata: cu_chunks then cu_pad, each [num_seqs + 1] int32.
+size_t meta_ws(const Geom& g) {
+  return g.cu_seqlens ? 2 * align_up(sizeof(int32_t) * (g.num_seqs + 1)) : 0;
+}
+int32_t* meta_chunks(void* ws) { return reinterpret_cast<int32_t*>(ws); }
+int32_t* meta_pad(const Geom& g, void* ws) {
+  return reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
+                                    align_up(sizeof(int32_t) * (g.num_seqs + 1)));
+}
+size_t vt_bytes(const Geom& g) {
+  return dash::prefill_uses_ring(g)
+             ? align_up((size_t)g.Hkv * g.D * dash::padded_tokens(g.T, g.num_seqs) * 2)
+             : 0;
+}
+
 struct PrefillWs {
-  size_t cu_chunks, kbar, mask, logp, total;
+  size_t meta, kbar, mask, logp, vt, total;
 };
 PrefillWs prefill_ws(const Geom& g) {
   PrefillWs w{};
   size_t o = 0;
-  w.cu_chunks = o;
-  o += g.cu_seqlens ? align_up(sizeof(int32_t) * (g.num_seqs + 1)) : 0;
+  w.meta = o;
+  o += meta_ws(g);
   w.kbar = o;
   o += align_up((size_t)(g.T / g.B) * g.Hkv * g.D * elt(g));
   w.mask = o;
   o += align_up((size_t)g.Hkv * g.T * g.W * 8);
   w.logp = o;
   o += align_up((size_t)g.Hkv * g.T * g.C_slots * 4);
+  w.vt = o;
+  o += vt_bytes(g);
   w.total = o;
+  return w;
+}
+struct SparseWs {
+  size_t meta, vt, total;
+};
+SparseWs sparse_ws(const Geom& g) {
+  SparseWs w{};
+  w.meta = 0;
+  w.vt = meta_ws(g);
+  w.total = w.vt + vt_bytes(g);
   return w;
 }
 struct DecodeWs {
@@ -122,10 +149,6 @@ DecodeWs decode_ws(const Geom& g) {
   w.total = o;
   return w;
 }
-size_t meta_ws(const Geom& g) {
-  return g.cu_seqlens ? align_up(sizeof(int32_t) * (g.num_seqs + 1)) : 0;
-}
-
 dash_status check_ws(void* ws, size_t have, size_t need) {
   if (have < need) return DASH_ERR_WORKSPACE_TOO_SMALL;
   if (need && !ws) return DASH_ERR_INVALID_ARGUMENT;
@@ -178,7 +201,7 @@ size_t dash_workspace_size(int op, const dash_shape* shape) {
     case DASH_OP_ROUTE: return meta_ws(g);
     case DASH_OP_PREFILL: return prefill_ws(g).total;
     case DASH_OP_DECODE: return decode_ws(g).total;
-    case DASH_OP_SPARSE: return 0;
+    case DASH_OP_SPARSE: return sparse_ws(g).total;
   }
   return 0;
 }
@@ -197,9 +220,9 @@ dash_status dash_summarize(const dash_shape* shape, const void* k, const float* 
   if (!aligned16(k) || !aligned16(qbar) || !aligned16(kbar)) return DASH_ERR_INVALID_ARGUMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (g.cu_seqlens) {
-    g.cu_chunks = reinterpret_cast<int32_t*>(workspace);
-    DASH_HIP(dash::launch_varlen_meta(g.cu_seqlens, g.num_seqs, g.B,
-                                      reinterpret_cast<int32_t*>(workspace), s));
+    g.cu_chunks = meta_chunks(workspace);
+    DASH_HIP(dash::launch_varlen_meta(g.cu_seqlens, g.num_seqs, g.B, meta_chunks(workspace),
+                                      nullptr, s));
   }
   DASH_HIP(dash::launch_summarize(g, k, qbar, kbar, s));
   return DASH_OK;
@@ -221,9 +244,9 @@ dash_status dash_route(const dash_shape* shape, const void* q, const void* kbar,
   if (!aligned16(q) || !aligned16(kbar)) return DASH_ERR_INVALID_ARGUMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (g.cu_seqlens) {
-    g.cu_chunks = reinterpret_cast<int32_t*>(workspace);
-    DASH_HIP(dash::launch_varlen_meta(g.cu_seqlens, g.num_seqs, g.B,
-                                      reinterpret_cast<int32_t*>(workspace), s));
+    g.cu_chunks = meta_chunks(workspace);
+    DASH_HIP(dash::launch_varlen_meta(g.cu_seqlens, g.num_seqs, g.B, meta_chunks(workspace),
+                                      nullptr, s));
   }
   dash::RouteParams p;
   p.q = q;
@@ -258,9 +281,11 @@ dash_status dash_attn_prefill(const dash_shape* shape, const void* q, const void
     return DASH_ERR_INVALID_ARGUMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (g.cu_seqlens) {
-    g.cu_chunks = reinterpret_cast<int32_t*>(at(workspace, w.cu_chunks));
-    DASH_HIP(dash::launch_varlen_meta(g.cu_seqlens, g.num_seqs, g.B,
-                                      const_cast<int32_t*>(g.cu_chunks), s));
+    void* meta = at(workspace, w.meta);
+    g.cu_chunks = meta_chunks(meta);
+    g.cu_pad = meta_pad(g, meta);
+    DASH_HIP(dash::launch_varlen_meta(g.cu_seqlens, g.num_seqs, g.B, meta_chunks(meta),
+                                      meta_pad(g, meta), s));
   }
   void* kbar = at(workspace, w.kbar);
   uint64_t* mask = active_blocks ? active_blocks : reinterpret_cast<uint64_t*>(at(workspace, w.mask));
@@ -287,6 +312,8 @@ dash_status dash_attn_prefill(const dash_shape* shape, const void* q, const void
   pp.out = out;
   pp.lse = lse;
   pp.scale = eff_scale(g, softmax_scale);
+  pp.vt = at(workspace, w.vt);
+  pp.Tp = dash::padded_tokens(g.T, g.num_seqs);
   DASH_HIP(dash::launch_prefill_attn(g, pp, s));
   return DASH_OK;
 }
@@ -294,15 +321,26 @@ dash_status dash_attn_prefill(const dash_shape* shape, const void* q, const void
 dash_status dash_attn_sparse(const dash_shape* shape, const void* q, const void* k,
                              const void* v, const uint64_t* active_blocks,
                              const float* log_prior, float softmax_scale, int enable_gqa,
-                             void* out, float* lse, void* stream) {
+                             void* out, float* lse, void* workspace, size_t workspace_bytes,
+                             void* stream) {
   Geom g;
   dash_status st = check_shape(shape, enable_gqa, false, g);
   if (st != DASH_OK) return st;
   if (std::isnan(softmax_scale)) return DASH_ERR_INVALID_ARGUMENT;
+  const SparseWs w = sparse_ws(g);
+  if ((st = check_ws(workspace, workspace_bytes, w.total)) != DASH_OK) return st;
   if (g.T == 0 || g.num_seqs == 0) return DASH_OK;
   if (!q || !k || !v || !active_blocks || !log_prior || !out) return DASH_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return DASH_ERR_INVALID_ARGUMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (g.cu_seqlens) {
+    void* meta = at(workspace, w.meta);
+    g.cu_chunks = meta_chunks(meta);
+    g.cu_pad = meta_pad(g, meta);
+    DASH_HIP(dash::launch_varlen_meta(g.cu_seqlens, g.num_seqs, g.B, meta_chunks(meta),
+                                      meta_pad(g, meta), s));
+  }
   dash::PrefillParams pp;
   pp.q = q;
   pp.k = k;
@@ -312,7 +350,9 @@ dash_status dash_attn_sparse(const dash_shape* shape, const void* q, const void*
   pp.out = out;
   pp.lse = lse;
   pp.scale = eff_scale(g, softmax_scale);
-  DASH_HIP(dash::launch_prefill_attn(g, pp, static_cast<hipStream_t>(stream)));
+  pp.vt = w.total > w.vt ? at(workspace, w.vt) : nullptr;
+  pp.Tp = dash::padded_tokens(g.T, g.num_seqs);
+  DASH_HIP(dash::launch_prefill_attn(g, pp, s));
   return DASH_OK;
 }
 

@@ -15,15 +15,20 @@ struct Geom {
   int64_t T = 0;                        // packed token rows (prefill / route)
   const int32_t* cu_seqlens = nullptr;  // device [num_seqs+1] or null
   const int32_t* cu_chunks = nullptr;   // device [num_seqs+1] (workspace) or null
+  const int32_t* cu_pad = nullptr;      // device [num_seqs+1]: 64-padded token offsets, or null
   int Hq = 0, Hkv = 0, G = 0, D = 0, B = 0;
   int C_slots = 0;                      // ceil(max_seqlen / B)
   int W = 0;                            // ceil(C_slots / 64)
   bool bf16 = true;
 };
 
-// a0: cu_chunks[s] = sum_{s' < s} floor(L_s' / B).
+// a0: cu_chunks[s] = sum_{s' < s} floor(L_s' / B) and, when cu_pad is not
+// null, cu_pad[s] = sum_{s' < s} 64 * ceil(L_s' / 64).
 hipError_t launch_varlen_meta(const int32_t* cu_seqlens, int num_seqs, int B,
-                              int32_t* cu_chunks, hipStream_t st);
+                              int32_t* cu_chunks, int32_t* cu_pad, hipStream_t st);
+
+// Columns of a sequence's keys in the 64-padded V^T layout.
+inline int64_t padded_tokens(int64_t T, int num_seqs) { return T + 64ll * num_seqs; }
 
 // K0: chunk summaries.
 hipError_t launch_summarize(const Geom& g, const void* k, const float* qbar,
@@ -49,6 +54,8 @@ hipError_t launch_route(const Geom& g, const RouteParams& p, hipStream_t st);
 
 // K2p: prefill attention over the active chunks and the diagonal.
 struct PrefillParams {
+  void* vt = nullptr;                   // workspace V^T [Hkv, D, Tp] (bf16, G >= 16)
+  int64_t Tp = 0;                       // padded columns of vt
   const void* q = nullptr;
   const void* k = nullptr;
   const void* v = nullptr;
@@ -59,6 +66,8 @@ struct PrefillParams {
   float scale = 0.f;
 };
 hipError_t launch_prefill_attn(const Geom& g, const PrefillParams& p, hipStream_t st);
+// True when launch_prefill_attn runs the V^T + LDS-ring path (needs p.vt).
+bool prefill_uses_ring(const Geom& g);
 
 // K2d + K4: split-K decode attention and the combine of the partials.
 struct DecodeParams {

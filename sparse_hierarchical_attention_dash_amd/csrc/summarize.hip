@@ -16,20 +16,25 @@ namespace dash {
 
 __global__ void varlen_meta_kernel(const int32_t* __restrict__ cu_seqlens,
                                    int num_seqs, int B,
-                                   int32_t* __restrict__ cu_chunks) {
+                                   int32_t* __restrict__ cu_chunks,
+                                   int32_t* __restrict__ cu_pad) {
   if (threadIdx.x != 0) return;
-  int32_t acc = 0;
+  int32_t acc = 0, pad = 0;
   cu_chunks[0] = 0;
+  if (cu_pad) cu_pad[0] = 0;
   for (int s = 0; s < num_seqs; ++s) {
-    acc += (cu_seqlens[s + 1] - cu_seqlens[s]) / B;
+    const int32_t L = cu_seqlens[s + 1] - cu_seqlens[s];
+    acc += L / B;
     cu_chunks[s + 1] = acc;
+    pad += (L + 63) / 64 * 64;
+    if (cu_pad) cu_pad[s + 1] = pad;
   }
 }
 
 hipError_t launch_varlen_meta(const int32_t* cu_seqlens, int num_seqs, int B,
-                              int32_t* cu_chunks, hipStream_t st) {
+                              int32_t* cu_chunks, int32_t* cu_pad, hipStream_t st) {
   hipLaunchKernelGGL(varlen_meta_kernel, dim3(1), dim3(64), 0, st, cu_seqlens,
-                     num_seqs, B, cu_chunks);
+                     num_seqs, B, cu_chunks, cu_pad);
   return hipGetLastError();
 }
 

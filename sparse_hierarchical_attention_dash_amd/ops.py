@@ -145,7 +145,7 @@ def attn_prefill(q, k, v, qbar, chunk_size, *, alpha=1.5, gamma=1.0, sigma=1.0,
 
 def attn_sparse(q, k, v, active_blocks, log_prior, chunk_size, *, softmax_scale=0.0,
                 enable_gqa=True, cu_seqlens=None, max_seqlen=None, return_lse=False,
-                out=None):
+                out=None, workspace=None):
     """Phase 2 alone for a given routing (active_blocks [Hkv,T,W] int64 words,
     log_prior [Hkv,T,C_slots] fp32).  Returns (out, lse or None)."""
     _need_cuda(q, k, v, active_blocks, log_prior, cu_seqlens)
@@ -156,10 +156,22 @@ def attn_sparse(q, k, v, active_blocks, log_prior, chunk_size, *, softmax_scale=
     if out is None:
         out = torch.empty_like(q)
     lse = torch.empty((Hq, T), dtype=torch.float32, device=dev) if return_lse else None
+    n = L.workspace_size(L.DASH_OP_SPARSE, shape)
+    if workspace is None or workspace.numel() < n:
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
     L.check("dash_attn_sparse", L.lib().dash_attn_sparse(
         ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(active_blocks), _ptr(log_prior),
-        float(softmax_scale), int(enable_gqa), _ptr(out), _ptr(lse), _stream(dev)))
+        float(softmax_scale), int(enable_gqa), _ptr(out), _ptr(lse), _ptr(workspace), n,
+        _stream(dev)))
     return out, lse
+
+
+def sparse_workspace(q, k, chunk_size, cu_seqlens=None, max_seqlen=None):
+    """Allocate the workspace attn_sparse needs, for reuse across calls."""
+    T, Hq, D = q.shape
+    shape = _seq_shape(q, Hq, k.shape[1], chunk_size, cu_seqlens, max_seqlen)
+    n = L.workspace_size(L.DASH_OP_SPARSE, shape)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
 
 
 def prefill_workspace(q, k, chunk_size, cu_seqlens=None, max_seqlen=None):

@@ -76,13 +76,14 @@ def test_layout_and_workspace_sizes(lib):
     s = shape(T=131072, B=64)
     lay = L.layout(s)
     assert (lay.chunk_slots, lay.mask_words) == (2048, 32)
-    # prefill workspace holds summaries, a mask and the dense log-prior
+    # prefill workspace holds summaries, a mask, the dense log-prior and (bf16,
+    # group >= 16) V transposed into 64-padded columns
     T, Hkv, D, W, C = 1000, 2, 128, 1, 16
     need = L.workspace_size(L.DASH_OP_PREFILL, shape(T=T))
-    parts = [(T // 64) * Hkv * D * 2, Hkv * T * W * 8, Hkv * T * C * 4]
+    parts = [(T // 64) * Hkv * D * 2, Hkv * T * W * 8, Hkv * T * C * 4, Hkv * D * (T + 64) * 2]
     assert need == sum((p + 255) // 256 * 256 for p in parts)
     assert L.workspace_size(L.DASH_OP_SUMMARIZE, shape()) == 0
-    assert L.workspace_size(L.DASH_OP_ROUTE, shape(cu=A, num_seqs=3)) == 256
+    assert L.workspace_size(L.DASH_OP_ROUTE, shape(cu=A, num_seqs=3)) == 512
     assert L.workspace_size(L.DASH_OP_DECODE, shape(T=4, num_seqs=4, max_seqlen=4096)) > 0
     assert L.workspace_size(L.DASH_OP_PREFILL, shape(D=96)) == 0
 
