@@ -384,7 +384,10 @@ __global__ __launch_bounds__(256) void vt_transpose_kernel(Geom g, const uint16_
   }
 }
 
-constexpr int kRing = 4;  // LDS slots; up to 3 blocks in flight
+constexpr int kRing = 4;       // LDS slots; up to 3 blocks in flight
+constexpr int kRingWaves = 8;  // two 16-row tiles per wave
+constexpr int kRingThreads = 64 * kRingWaves;
+constexpr int kRingTiles = 2 * kRingWaves;
 
 template <int D>
 struct RingCfg {
@@ -394,9 +397,10 @@ struct RingCfg {
   static constexpr int VROW = 128;                    // bytes per V^T row (64 keys)
   static constexpr int VBYTES = D * VROW;
   static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int KLD = KBYTES / (16 * kPrefillThreads);  // DMA loads per thread
-  static constexpr int VLD = VBYTES / (16 * kPrefillThreads);
-  static constexpr int LPS = KLD + VLD;
+  static constexpr int NP = STAGE / (16 * kRingThreads);  // 16-byte loads per thread
+  static constexpr int LPS = NP + 1;                      // + the tiles' bias words
+  static_assert(NP * 16 * kRingThreads == STAGE, "slot must split into whole loads");
+  static_assert(KBYTES % (NP * 1024) == 0, "a wave's pieces lie all in K or all in V^T");
 };
 
 // XOR swizzle of the 16-byte pieces of an LDS row: 16 consecutive rows read
@@ -406,148 +410,199 @@ __device__ __forceinline__ int swz(int row) {
   return P == 16 ? (row & 15) : ((row >> 1) & 7);
 }
 
-// One 16-byte direct global->LDS load per lane: lane l of the wave writes
-// LDS bytes lds_base + 16 l .. +15 (lds_base wave-uniform).  Issued from asm so
-// the compiler neither tracks nor waits on it: the data lands in LDS, no
-// register is written, the address registers are consumed at issue, and the
-// ring's own counted vmcnt waits plus a barrier order it before every read.
-// (Vector-memory operations the compiler does not know about can only make
-// its own counted waits stricter.)
+// Direct global->LDS loads, issued from asm so that the compiler neither
+// tracks nor waits on them: the data lands in LDS, no register is written,
+// the address registers are consumed at issue, and the ring's own counted
+// vmcnt waits plus a barrier order them before every read.  (Vector-memory
+// operations the compiler does not know about can only make its own counted
+// waits stricter.)
+//   lds_dma16: lane l writes LDS bytes lds_base + 16 l .. +15
+//   lds_dma4 : lane l writes LDS bytes lds_base + 4 l .. +3
+// (lds_base wave-uniform; lanes outside exec write nothing).
 __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :
                : "s"(lds_base), "v"(gptr)
                : "memory", "m0");
 }
+__device__ __forceinline__ void lds_dma4(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :
+               : "s"(lds_base), "v"(gptr)
+               : "memory", "m0");
+}
 
+// LDS byte offset of a __shared__ object (a compile-time constant for the
+// ring's static arrays).
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)p;  // low 32 bits of a flat LDS address = LDS offset
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// Direct global->LDS loads of one 64-key block into a ring slot: K rows
-// key0 + krow (clamped to kmax, the last key the workgroup may read) and the
-// block's V^T rows, each thread moving its fixed 16-byte pieces.
-template <int D>
-__device__ __forceinline__ void ring_issue(const uint8_t* kbase, int64_t krs,
-                                           const int (&krow)[RingCfg<D>::KLD],
-                                           const int (&kpiece)[RingCfg<D>::KLD],
-                                           const uint8_t* const (&vbase)[RingCfg<D>::VLD],
-                                           int key0, int kmax, uint8_t* slot, int wv) {
-  using R = RingCfg<D>;
-  const uint32_t sb = __builtin_amdgcn_readfirstlane(lds_addr(slot) + wv * R::KLD * 1024);
-  const uint32_t vb =
-      __builtin_amdgcn_readfirstlane(lds_addr(slot) + R::KBYTES + wv * R::VLD * 1024);
-#pragma unroll
-  for (int i = 0; i < R::KLD; ++i) {
-    const int key = min(key0 + krow[i], kmax);
-    lds_dma16(kbase + key * krs + kpiece[i] * 16, sb + i * 1024);
-  }
-#pragma unroll
-  for (int i = 0; i < R::VLD; ++i) lds_dma16(vbase[i] + (int64_t)key0 * 2, vb + i * 1024);
+// LDS pointers proper (address space 3): offsets added to them fold into the
+// reads' offset field.
+typedef const __attribute__((address_space(3))) uint8_t lds_u8;
+__device__ __forceinline__ u32x4 lds_read16(lds_u8* p) {
+  typedef const __attribute__((address_space(3))) u32x4 lds_u32x4;
+  return *reinterpret_cast<lds_u32x4*>(p);
 }
 
-template <int D, bool MASKED>
-__device__ __forceinline__ void visit_ring(const uint8_t* __restrict__ ks_,
-                                           const uint8_t* __restrict__ vt_,
+// One visit of tiles U0 .. U0+NTL-1 of a wave (16 rows each) to one staged
+// 64-key block (ring layout): S^T = K Q^T, online softmax in base 2 with the
+// tile's bias for the block, O^T += V^T P^T.  With two tiles, every K and V^T
+// fragment read from LDS feeds both tiles' MFMAs.
+// The row sum l is accumulated from the same bf16-rounded P that enters the
+// PV product (v_dot2 against (1, 1)); lane (g, r) holds the partial sum of
+// row r over its keys 16t + 4g + j, the four partials are added at the end.
+//   MASKED = false: every row attends every key of the block.
+//   MASKED = true : a row attends key j iff key index <= its position.
+// LDS fragments are read in groups of four 16-byte loads, one group ahead of
+// the MFMAs that consume the previous one (sched_barrier keeps the compiler
+// from collapsing the pipeline); the first V^T group is read during the
+// softmax, which does not need it.
+template <int D, bool MASKED, int U0, int NTL>
+__device__ __forceinline__ void visit_ring(lds_u8* ks_, lds_u8* vt_,
                                            const int (&koff)[D / 32], const int (&voff)[2],
-                                           const bf16x8 (&qa)[D / 32], f32x4 (&o)[D / 16],
-                                           f32x4& lacc, float& m, float sl2, float bz,
-                                           int kbase, int rpos) {
+                                           const bf16x8 (&qa)[2][D / 32], f32x4 (&o)[2][D / 16],
+                                           float (&l)[2], float (&m)[2], float sl2,
+                                           const float (&bz)[2], int kbase, const int (&rpos)[2]) {
   using R = RingCfg<D>;
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
-  f32x4 sacc[4];
+  constexpr int NVG = 2 * DT / 4;  // V^T groups of four fragments
+  auto kload = [&](u32x4 (&f)[4], int ks) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t) sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 4; ++t)
+      f[t] = lds_read16(ks_ + koff[ks] + 16 * t * R::KROW);
+  };
+  // group vg covers s2 = vg / (DT / 4), dt = 4 (vg % (DT / 4)) .. +3
+  auto vload = [&](u32x4 (&f)[4], int vg) {
+    const int s2 = vg / (DT / 4), dt0 = 4 * (vg % (DT / 4));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      f[i] = lds_read16(vt_ + voff[s2] + 16 * (dt0 + i) * R::VROW);
+  };
+  f32x4 sacc[NTL][4];
+#pragma unroll
+  for (int u = 0; u < NTL; ++u)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) sacc[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 fa[4], fb[4];
+  kload(fa, 0);
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
+    u32x4 (&cur)[4] = (ks & 1) ? fb : fa;
+    u32x4 (&nxt)[4] = (ks & 1) ? fa : fb;
+    if (ks + 1 < KS) kload(nxt, ks + 1);
+    else vload(nxt, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int u = 0; u < NTL; ++u)
+        sacc[u][t] = mfma16x16x32(as_bf16x8(cur[t]), qa[U0 + u][ks], sacc[u][t]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // the first V^T group is in flight in the buffer the last K step (ks = KS - 1)
+  // loaded into, the one it did not consume
+  u32x4 (&v0)[4] = ((KS - 1) & 1) ? fa : fb;
+  u32x4 (&v1)[4] = ((KS - 1) & 1) ? fb : fa;
+  uint32_t pk[NTL][4][2];
+#pragma unroll
+  for (int u = 0; u < NTL; ++u) {
+    // causal mask folded into the scores: keys past the row's position get
+    // -inf here and p = 0 below (no per-element mask outlives its compare)
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          sacc[u][t][j] = kbase + 16 * t + j <= rpos[U0 + u] ? sacc[u][t][j] : -INFINITY;
+    }
+    float amax = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      amax = fmaxf(amax, fmaxf(fmaxf(sacc[u][t][0], sacc[u][t][1]),
+                               fmaxf(sacc[u][t][2], sacc[u][t][3])));
+    amax = fmaxf(amax, xor16(amax));
+    amax = fmaxf(amax, xor32(amax));
+    const float zmax = amax * sl2 + bz[U0 + u];
+    float& mu = m[U0 + u];
+    const bool up = zmax > mu + kRescale;
+    if (__ballot(up) != 0ull) {
+      const float mn = up ? zmax : mu;
+      const float alpha = up ? exp2f(mu - mn) : 1.f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[U0 + u][dt] *= alpha;
+      l[U0 + u] *= alpha;
+      mu = mn;
+    }
+    const float off = bz[U0 + u] - mu;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const bf16x8 ak =
-          as_bf16x8(*reinterpret_cast<const u32x4*>(ks_ + koff[ks] + 16 * t * R::KROW));
-      sacc[t] = mfma16x16x32(ak, qa[ks], sacc[t]);
-    }
-  }
-  bool ok[4][4];
-  float amax = -INFINITY;
-  if constexpr (MASKED) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
+      float pv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        ok[t][j] = kbase + 16 * t + j <= rpos;
-        amax = fmaxf(amax, ok[t][j] ? sacc[t][j] : -INFINITY);
+        pv[j] = __builtin_amdgcn_exp2f(fmaf(sacc[u][t][j], sl2, off));
+        if constexpr (MASKED) pv[j] = sacc[u][t][j] == -INFINITY ? 0.f : pv[j];
       }
-  } else {
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      amax = fmaxf(amax, fmaxf(fmaxf(sacc[t][0], sacc[t][1]), fmaxf(sacc[t][2], sacc[t][3])));
-  }
-  amax = fmaxf(amax, xor16(amax));
-  amax = fmaxf(amax, xor32(amax));
-  const float zmax = amax * sl2 + bz;
-  const bool up = zmax > m + kRescale;
-  if (__ballot(up) != 0ull) {
-    const float mn = up ? zmax : m;
-    const float alpha = up ? exp2f(m - mn) : 1.f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-    lacc *= alpha;
-    m = mn;
-  }
-  const float off = bz - m;
-  uint32_t pk[4][2];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    float pv[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      pv[j] = __builtin_amdgcn_exp2f(fmaf(sacc[t][j], sl2, off));
-      if constexpr (MASKED) pv[j] = ok[t][j] ? pv[j] : 0.f;
+      pk[u][t][0] = cvt_pk_bf16(pv[0], pv[1]);
+      pk[u][t][1] = cvt_pk_bf16(pv[2], pv[3]);
     }
-    pk[t][0] = cvt_pk_bf16(pv[0], pv[1]);
-    pk[t][1] = cvt_pk_bf16(pv[2], pv[3]);
-  }
-  const u32x4 ones_u = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
-  const bf16x8 ones = as_bf16x8(ones_u);
+    float la = l[U0 + u], lb = 0.f;
 #pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2) {
-    const u32x4 pb = {pk[2 * s2][0], pk[2 * s2][1], pk[2 * s2 + 1][0], pk[2 * s2 + 1][1]};
-    const bf16x8 pbv = as_bf16x8(pb);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const bf16x8 av =
-          as_bf16x8(*reinterpret_cast<const u32x4*>(vt_ + voff[s2] + 16 * dt * R::VROW));
-      o[dt] = mfma16x16x32(av, pbv, o[dt]);
+    for (int t = 0; t < 4; ++t) {
+      la = dot2_bf16_ones(pk[u][t][0], la);
+      lb = dot2_bf16_ones(pk[u][t][1], lb);
     }
-    lacc = mfma16x16x32(ones, pbv, lacc);
+    l[U0 + u] = la + lb;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int vg = 0; vg < NVG; ++vg) {
+    u32x4 (&cur)[4] = (vg & 1) ? v1 : v0;
+    u32x4 (&nxt)[4] = (vg & 1) ? v0 : v1;
+    if (vg + 1 < NVG) vload(nxt, vg + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const int s2 = vg / (DT / 4), dt0 = 4 * (vg % (DT / 4));
+#pragma unroll
+    for (int u = 0; u < NTL; ++u) {
+      const u32x4 pb = {pk[u][2 * s2][0], pk[u][2 * s2][1], pk[u][2 * s2 + 1][0],
+                        pk[u][2 * s2 + 1][1]};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[U0 + u][dt0 + i] =
+            mfma16x16x32(as_bf16x8(cur[i]), as_bf16x8(pb), o[U0 + u][dt0 + i]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Prefill attention for G >= 16 (every 16-row tile is one position's heads):
-// the blocks of the workgroup's list stream through a 4-slot LDS ring filled by
-// direct global->LDS loads (K rows from K, V^T rows from the V^T workspace),
-// three blocks ahead of the one being consumed.  The loop is unrolled by the
-// ring depth so every slot is a distinct LDS array; waits are counted
-// (vmcnt) and the barrier carries no fence.  Mask words and biases are read
-// with scalar loads so that only the ring's loads are vector memory traffic.
+// Prefill attention for G >= 16 (every 16-row tile is 16 query heads of one
+// position; 16 tiles per workgroup, two per wave).  The blocks of the
+// workgroup's list stream through a 4-slot LDS ring filled by direct
+// global->LDS loads (K rows from K, V^T rows from the V^T workspace, and each
+// tile's bias for the block), three blocks ahead of the one being consumed.
+// Which positions have each listed chunk active is worked out once, up front,
+// into a bitmap in LDS, so the loop reads no memory but LDS.  A wave visits a
+// block with both its tiles at once when both have it active.  The loop is
+// unrolled by the ring depth so every slot is a distinct LDS array; waits are
+// counted (vmcnt) and the barrier carries no fence.
 template <int D>
-__global__ __launch_bounds__(kPrefillThreads, 1) void prefill_attn_ring_kernel(
+__global__ __launch_bounds__(kRingThreads, 1) void prefill_attn_ring_kernel(
     Geom g, PrefillParams p, TileGeom tg) {
-  constexpr int NTH = kPrefillThreads;
-  constexpr int TWM = kMaxTilesPerWave;
+  constexpr int NTH = kRingThreads;
   using R = RingCfg<D>;
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring0[R::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring1[R::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring2[R::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring3[R::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kRing][R::STAGE];
+  __shared__ float bias[kRing][kRingTiles];
   __shared__ unsigned long long Umask[32];
   __shared__ int Wpref[33];
   __shared__ uint16_t Blist[2048];
+  __shared__ uint16_t Act[2048];   // bit t: position p0 + t has chunk Blist[j] active
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in an SGPR
   const int r = lane & 15, gq = lane >> 4;
   const int tile = tg.tiles_per_seq - 1 - (int)blockIdx.x;
   const int s = blockIdx.y, h = blockIdx.z;
@@ -555,31 +610,26 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_attn_ring_kernel(
   const int p0 = tile * tg.P;
   if (p0 >= si.len) return;
   const int pend = min(p0 + tg.P, si.len);
+  const int npos = pend - p0;
   const int cdiag = p0 / g.B;
   const int64_t T = g.T;
   const int W = g.W;
   const unsigned long long* __restrict__ mask = (const unsigned long long*)p.mask;
-  // read-only for the whole kernel: through the constant address space the
-  // wave-uniform mask-word and bias reads of the loop become scalar loads, so
-  // they neither count against nor wait on the ring's vector-memory counter
-  typedef const __attribute__((address_space(4))) unsigned long long cmask_t;
-  typedef const __attribute__((address_space(4))) float cfloat_t;
-  cmask_t* smask = (cmask_t*)p.mask;
-  cfloat_t* slogp = (cfloat_t*)p.log_prior;
 
-  int rpos[TWM], rhead[TWM];
-  bool rvalid[TWM], tvalid[TWM];
+  // this wave's tiles u = 0, 1: 16 heads (rhead) of position rpos = p0 + tpos
+  int tpos[2], rpos[2], rhead[2];
+  bool rvalid[2];
 #pragma unroll
-  for (int u = 0; u < TWM; ++u) {
-    const int ti = wv * tg.TW + u;
-    rpos[u] = p0 + ti / tg.HT;
+  for (int u = 0; u < 2; ++u) {
+    const int ti = 2 * wv + u;
+    tpos[u] = ti / tg.HT;
+    rpos[u] = p0 + tpos[u];
     rhead[u] = (ti % tg.HT) * 16 + r;
-    tvalid[u] = (u < tg.TW) && (ti < tg.NT);
-    rvalid[u] = tvalid[u] && (rpos[u] < pend);
+    rvalid[u] = rpos[u] < pend;
   }
-  bf16x8 qa[TWM][KS];
+  bf16x8 qa[2][KS];
 #pragma unroll
-  for (int u = 0; u < TWM; ++u) {
+  for (int u = 0; u < 2; ++u) {
     const int64_t qrow = ((si.start + rpos[u]) * g.Hq + h * g.G + rhead[u]) * (int64_t)D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -589,17 +639,15 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_attn_ring_kernel(
     }
   }
 
-  // ---- ordered list of the union of the positions' active chunks
+  // ---- ordered list of the union of the positions' active chunks, and for
+  // each listed chunk the positions that have it active
   if (tid < 32) Umask[tid] = 0ull;
   __syncthreads();
-  {
-    const int npos = pend - p0;
-    const unsigned long long* mbase = mask + ((int64_t)h * T + si.start + p0) * W;
-    for (int idx = tid; idx < npos * W; idx += NTH) {
-      const int w = idx % W;
-      const unsigned long long v = mbase[idx] & routable_bits(w, cdiag);
-      if (v) atomicOr(&Umask[w], v);
-    }
+  const unsigned long long* mbase = mask + ((int64_t)h * T + si.start + p0) * W;
+  for (int idx = tid; idx < npos * W; idx += NTH) {
+    const int w = idx % W;
+    const unsigned long long v = mbase[idx] & routable_bits(w, cdiag);
+    if (v) atomicOr(&Umask[w], v);
   }
   __syncthreads();
   if (tid < 64) {
@@ -622,57 +670,70 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_attn_ring_kernel(
     }
   }
   __syncthreads();
-  const int SB = g.B / 64;
-  const int nrouted = Wpref[W] * SB;
+  const int nlist = Wpref[W];
+  for (int j = tid; j < nlist; j += NTH) {
+    const int c = Blist[j];
+    uint32_t bits = 0;
+    for (int t = 0; t < npos; ++t)
+      bits |= (uint32_t)((mbase[t * W + (c >> 6)] >> (c & 63)) & 1ull) << t;
+    Act[j] = (uint16_t)bits;
+  }
+  __syncthreads();
+  const int sbl = g.B == 128 ? 1 : 0;  // log2 of the 64-key blocks per chunk
+  const int nrouted = nlist << sbl;
   const int ndiag = (pend - cdiag * g.B + 63) / 64;
   const int NS = nrouted + ndiag;
 
-  // ---- per-thread DMA sources (piece layout fixed per thread)
+  // ---- per-thread DMA sources (piece layout fixed per thread; a wave's
+  // pieces are all K rows or all V^T rows)
   const int64_t krs = (int64_t)g.Hkv * D * 2;  // bytes between consecutive keys
+  const int64_t vrs = p.Tp * 2;                  // bytes between V^T rows
+  const bool isk = wv * R::NP * 1024 < R::KBYTES;
   const uint8_t* kbase = (const uint8_t*)p.k + (si.start * (int64_t)g.Hkv + h) * D * 2;
-  int krow[R::KLD], kpiece[R::KLD];
+  const uint8_t* vbase = (const uint8_t*)p.vt + ((int64_t)h * D * p.Tp + pad_off(g, s)) * 2;
+  int prow_[R::NP], pcol[R::NP];  // K row or V^T row of the piece, byte column in the row
 #pragma unroll
-  for (int i = 0; i < R::KLD; ++i) {
-    const int o = (wv * R::KLD + i) * 1024 + lane * 16;
-    krow[i] = o / R::KROW;
-    kpiece[i] = ((o % R::KROW) / 16) ^ swz<R::KP>(krow[i]);
-  }
-  const uint8_t* vbase[R::VLD];
-#pragma unroll
-  for (int i = 0; i < R::VLD; ++i) {
-    const int o = (wv * R::VLD + i) * 1024 + lane * 16;
-    const int d = o / R::VROW;
-    const int pc = ((o % R::VROW) / 16) ^ swz<8>(d);
-    vbase[i] = (const uint8_t*)p.vt + (((int64_t)h * D + d) * p.Tp + pad_off(g, s)) * 2 + pc * 16;
-  }
-  auto stage_key0 = [&](int st) -> int {
-    if (st < nrouted) {
-      const int c = Blist[st / SB];
-      return c * g.B + (st % SB) * 64;
+  for (int i = 0; i < R::NP; ++i) {
+    const int o = (wv * R::NP + i) * 1024 + lane * 16;
+    if (isk) {
+      prow_[i] = o / R::KROW;
+      pcol[i] = (((o % R::KROW) / 16) ^ swz<R::KP>(prow_[i])) * 16;
+    } else {
+      const int ov = o - R::KBYTES;
+      prow_[i] = ov / R::VROW;
+      pcol[i] = (((ov % R::VROW) / 16) ^ swz<8>(prow_[i])) * 16;
     }
-    return cdiag * g.B + (st - nrouted) * 64;
-  };
-  auto issue = [&](int st, uint8_t* slot) {
-    ring_issue<D>(kbase, krs, krow, kpiece, vbase, stage_key0(st), pend - 1, slot, wv);
+  }
+  // lane u < 2 loads tile u's bias (its position's row of log_prior)
+  const int bpos = min(rpos[lane & 1], pend - 1);
+  const float* bsrc = p.log_prior + ((int64_t)h * T + si.start + bpos) * g.C_slots;
+  const int kmax = pend - 1;
+  auto issue = [&](int st, uint32_t slot, uint32_t bslot) {
+    int c = 0, key0;
+    if (st < nrouted) {
+      c = __builtin_amdgcn_readfirstlane((int)Blist[st >> sbl]);
+      key0 = c * g.B + ((st & sbl) << 6);
+    } else {
+      key0 = cdiag * g.B + ((st - nrouted) << 6);
+    }
+#pragma unroll
+    for (int i = 0; i < R::NP; ++i) {
+      const uint8_t* gp = isk ? kbase + (int64_t)min(key0 + prow_[i], kmax) * krs + pcol[i]
+                              : vbase + (int64_t)key0 * 2 + (int64_t)prow_[i] * vrs + pcol[i];
+      lds_dma16(gp, slot + (wv * R::NP + i) * 1024);
+    }
+    // the tiles' biases for this block (past the routed blocks: any valid word)
+    if (lane < 2) lds_dma4(bsrc + c, bslot + wv * 8);
   };
 
-  // ---- per-tile state
-  f32x4 o[TWM][DT];
-  f32x4 lacc[TWM];
-  float m[TWM];
-  unsigned long long mword[TWM];
-  int mw_idx[TWM];
-  int64_t prow[TWM];
+  // ---- tile state
+  f32x4 o[2][DT];
+  float l[2] = {0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY};
 #pragma unroll
-  for (int u = 0; u < TWM; ++u) {
-    m[u] = -INFINITY;
-    lacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mword[u] = 0ull;
-    mw_idx[u] = -1;
-    prow[u] = uniform64((int64_t)h * T + si.start + min(rpos[u], pend - 1));
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
   const float sl2 = p.scale * kLog2e;
   int koff[KS], voff[2];
 #pragma unroll
@@ -683,56 +744,62 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_attn_ring_kernel(
   // Every step issues exactly one block's loads (past the end of the list it
   // re-reads the last block into the free slot, which no later step reads), so
   // when step st waits, exactly two blocks' loads are younger than its own:
-  // one fixed counted wait, and the compiler can prove the slot is complete.
+  // one fixed counted wait proves slot st & 3 complete.
+  const uint32_t ring0 = lds_addr(&ring[0][0]), bias0 = lds_addr(&bias[0][0]);
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4));  // Q and mask reads done first
-  issue(0, ring0);
-  issue(min(1, NS - 1), ring1);
-  issue(min(2, NS - 1), ring2);
+  issue(0, ring0, bias0);
+  issue(min(1, NS - 1), ring0 + R::STAGE, bias0 + 4 * kRingTiles);
+  issue(min(2, NS - 1), ring0 + 2 * R::STAGE, bias0 + 8 * kRingTiles);
 
-  auto step = [&](int st, const uint8_t* slot, uint8_t* refill) {
+  // wait for slot st & 3 and for every wave to be done with slot (st + 3) & 3;
+  // returns the slot's LDS offset
+  auto enter = [&](int st) -> lds_u8* {
     // own loads of this slot done (the two younger blocks may stay in flight),
     // this wave's LDS reads of the slot about to be refilled done
     __builtin_amdgcn_s_waitcnt(((2 * R::LPS) & 15) | (7 << 4));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    issue(min(st + 3, NS - 1), refill);
-    const bool diag = st >= nrouted;
-    const int c = __builtin_amdgcn_readfirstlane(diag ? cdiag : (int)Blist[st / SB]);
-    const int key0 = stage_key0(st);
-#pragma unroll
-    for (int u = 0; u < TWM; ++u) {
-      if (!tvalid[u]) break;
-      if (!rvalid[u]) continue;
-      if (!diag) {
-        const int wi = c >> 6;
-        if (wi != mw_idx[u]) {
-          mw_idx[u] = wi;
-          mword[u] = smask[prow[u] * W + wi];
-        }
-        if (!((mword[u] >> (c & 63)) & 1ull)) continue;
-        const float bz = slogp[prow[u] * g.C_slots + c] * kLog2e;
-        visit_ring<D, false>(slot, slot + R::KBYTES, koff, voff, qa[u], o[u], lacc[u], m[u], sl2,
-                             bz, 0, 0);
-      } else {
-        visit_ring<D, true>(slot, slot + R::KBYTES, koff, voff, qa[u], o[u], lacc[u], m[u], sl2,
-                            0.f, key0 + 4 * gq, rpos[u]);
-      }
-    }
+    return (lds_u8*)&ring[st & 3][0];
   };
-  for (int st = 0; st < NS; st += kRing) {
-    step(st, ring0, ring3);
-    if (st + 1 < NS) step(st + 1, ring1, ring0);
-    if (st + 2 < NS) step(st + 2, ring2, ring1);
-    if (st + 3 < NS) step(st + 3, ring3, ring2);
+  // the refill goes out after this wave's visits: the slot it overwrites was
+  // released by every wave at the step's barrier, and issuing it late keeps
+  // the vector-memory queue off the visits' critical path
+  auto leave = [&](int st) {
+    const int sr = st + 3;
+    issue(min(sr, NS - 1), ring0 + (sr & 3) * R::STAGE, bias0 + (sr & 3) * 4 * kRingTiles);
+  };
+  // routed blocks: each tile whose position has the chunk active visits it
+  // with the tile's bias (the two visits, when both are active, run back to
+  // back so that each tile's state is only ever updated in place)
+  for (int st = 0; st < nrouted; ++st) {
+    lds_u8* kv = enter(st);
+    const uint32_t act = Act[st >> sbl];
+    const bool a0 = rvalid[0] && ((act >> tpos[0]) & 1u);
+    const bool a1 = rvalid[1] && ((act >> tpos[1]) & 1u);
+    const float* bs = &bias[st & 3][2 * wv];
+    const float bz[2] = {bs[0] * kLog2e, bs[1] * kLog2e};
+    if (a0) visit_ring<D, false, 0, 1>(kv, kv + R::KBYTES, koff, voff, qa, o, l, m, sl2, bz, 0, rpos);
+    if (a1) visit_ring<D, false, 1, 1>(kv, kv + R::KBYTES, koff, voff, qa, o, l, m, sl2, bz, 0, rpos);
+    leave(st);
+  }
+  // the diagonal chunk: both tiles, causal mask, bias 0, one fused visit
+  for (int st = nrouted; st < NS; ++st) {
+    lds_u8* kv = enter(st);
+    const float bz[2] = {0.f, 0.f};
+    const int key0 = cdiag * g.B + ((st - nrouted) << 6);
+    if (rvalid[0])
+      visit_ring<D, true, 0, 2>(kv, kv + R::KBYTES, koff, voff, qa, o, l, m, sl2, bz,
+                                key0 + 4 * gq, rpos);
+    leave(st);
   }
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4));  // no ring load outlives the kernel
 
 #pragma unroll
-  for (int u = 0; u < TWM; ++u) {
-    if (!tvalid[u]) break;
+  for (int u = 0; u < 2; ++u) {
     if (!rvalid[u]) continue;
-    const float lt = lacc[u][0];
+    float lt = l[u] + xor16(l[u]);
+    lt += xor32(lt);
     const float inv = 1.f / lt;
     const int64_t tok = si.start + rpos[u];
     uint16_t* orow = (uint16_t*)p.out + (tok * g.Hq + h * g.G + rhead[u]) * (int64_t)D;
@@ -846,7 +913,20 @@ static TileGeom make_tiles(const Geom& g) {
   return t;
 }
 
-bool prefill_uses_ring(const Geom& g) { return g.bf16 && g.G >= 16; }
+// Ring kernel (G >= 16): one 16-row tile per wave, 16 tiles, so P = 16 / (G / 16)
+// positions per workgroup.
+static TileGeom make_ring_tiles(const Geom& g) {
+  TileGeom t;
+  t.TP = 1;
+  t.HT = g.G / 16;
+  t.NT = kRingTiles;
+  t.TW = 2;
+  t.P = t.NT / t.HT;
+  t.tiles_per_seq = (g.max_seqlen + t.P - 1) / t.P;
+  return t;
+}
+
+bool prefill_uses_ring(const Geom& g) { return g.bf16 && g.G >= 16 && g.G <= 256; }
 
 hipError_t launch_prefill_attn(const Geom& g, const PrefillParams& p, hipStream_t st) {
   if (g.T == 0) return hipSuccess;
@@ -854,17 +934,19 @@ hipError_t launch_prefill_attn(const Geom& g, const PrefillParams& p, hipStream_
     const TileGeom tg = make_tiles(g);
     dim3 grid(tg.tiles_per_seq, g.num_seqs, g.Hkv);
     if (prefill_uses_ring(g)) {
+      const TileGeom rg = make_ring_tiles(g);
+      dim3 rgrid(rg.tiles_per_seq, g.num_seqs, g.Hkv);
       dim3 tgrid((g.max_seqlen + 63) / 64, g.num_seqs, g.Hkv);
       if (g.D == 64) {
         hipLaunchKernelGGL(vt_transpose_kernel<64>, tgrid, dim3(256), 0, st, g,
                            (const uint16_t*)p.v, (uint16_t*)p.vt, p.Tp);
-        hipLaunchKernelGGL(prefill_attn_ring_kernel<64>, grid, dim3(kPrefillThreads), 0, st, g,
-                           p, tg);
+        hipLaunchKernelGGL(prefill_attn_ring_kernel<64>, rgrid, dim3(kRingThreads), 0, st, g,
+                           p, rg);
       } else {
         hipLaunchKernelGGL(vt_transpose_kernel<128>, tgrid, dim3(256), 0, st, g,
                            (const uint16_t*)p.v, (uint16_t*)p.vt, p.Tp);
-        hipLaunchKernelGGL(prefill_attn_ring_kernel<128>, grid, dim3(kPrefillThreads), 0, st, g,
-                           p, tg);
+        hipLaunchKernelGGL(prefill_attn_ring_kernel<128>, rgrid, dim3(kRingThreads), 0, st, g,
+                           p, rg);
       }
       return hipGetLastError();
     }

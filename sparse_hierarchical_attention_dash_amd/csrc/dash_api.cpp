@@ -6,7 +6,7 @@
 #include <cmath>
 #include <cstdint>
 
-#include "../../include/dash.h"
+#include "dash.h"
 #include "dash_internal.h"
 
 namespace {

@@ -114,6 +114,13 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
 // Two fp32 -> packed bf16x2 (round to nearest even, hardware conversion).
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// c + lo + hi of a packed bf16 pair, in fp32 (v_dot2 against (1, 1)).
+__device__ __forceinline__ float dot2_bf16_ones(uint32_t pk, float c) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk),
+                                         __builtin_bit_cast(bf16x2_t, 0x3f803f80u), c, false);
+}
+
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   const f32x2_t v = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
