@@ -455,10 +455,10 @@ __device__ __forceinline__ u32x4 lds_read16(lds_u8* p) {
 // row r over its keys 16t + 4g + j, the four partials are added at the end.
 //   MASKED = false: every row attends every key of the block.
 //   MASKED = true : a row attends key j iff key index <= its position.
-// LDS fragments are read in groups of four 16-byte loads, one group ahead of
-// the MFMAs that consume the previous one (sched_barrier keeps the compiler
-// from collapsing the pipeline); the first V^T group is read during the
-// softmax, which does not need it.
+// LDS fragments are read in groups of four 16-byte loads, two groups ahead of
+// the MFMAs that consume them (sched_barrier keeps the compiler from
+// collapsing the pipeline); the first two V^T groups are read during the
+// softmax, which does not need them.
 template <int D, bool MASKED, int U0, int NTL>
 __device__ __forceinline__ void visit_ring(lds_u8* ks_, lds_u8* vt_,
                                            const int (&koff)[D / 32], const int (&voff)[2],
@@ -481,31 +481,32 @@ __device__ __forceinline__ void visit_ring(lds_u8* ks_, lds_u8* vt_,
     for (int i = 0; i < 4; ++i)
       f[i] = lds_read16(vt_ + voff[s2] + 16 * (dt0 + i) * R::VROW);
   };
+  // fragment groups 0 .. KS-1 are K (ks = g), KS .. KS+NVG-1 are V^T; three
+  // buffers, two groups in flight ahead of the one being consumed
+  constexpr int NG = KS + NVG;
+  u32x4 fr[3][4];
+  auto gload = [&](int gi) {
+    if (gi < KS) kload(fr[gi % 3], gi);
+    else if (gi < NG) vload(fr[gi % 3], gi - KS);
+  };
   f32x4 sacc[NTL][4];
 #pragma unroll
   for (int u = 0; u < NTL; ++u)
 #pragma unroll
     for (int t = 0; t < 4; ++t) sacc[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  u32x4 fa[4], fb[4];
-  kload(fa, 0);
+  gload(0);
+  gload(1);
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    u32x4 (&cur)[4] = (ks & 1) ? fb : fa;
-    u32x4 (&nxt)[4] = (ks & 1) ? fa : fb;
-    if (ks + 1 < KS) kload(nxt, ks + 1);
-    else vload(nxt, 0);
+    gload(ks + 2);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int u = 0; u < NTL; ++u)
-        sacc[u][t] = mfma16x16x32(as_bf16x8(cur[t]), qa[U0 + u][ks], sacc[u][t]);
+        sacc[u][t] = mfma16x16x32(as_bf16x8(fr[ks % 3][t]), qa[U0 + u][ks], sacc[u][t]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // the first V^T group is in flight in the buffer the last K step (ks = KS - 1)
-  // loaded into, the one it did not consume
-  u32x4 (&v0)[4] = ((KS - 1) & 1) ? fa : fb;
-  u32x4 (&v1)[4] = ((KS - 1) & 1) ? fb : fa;
   uint32_t pk[NTL][4][2];
 #pragma unroll
   for (int u = 0; u < NTL; ++u) {
@@ -559,11 +560,10 @@ __device__ __forceinline__ void visit_ring(lds_u8* ks_, lds_u8* vt_,
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int vg = 0; vg < NVG; ++vg) {
-    u32x4 (&cur)[4] = (vg & 1) ? v1 : v0;
-    u32x4 (&nxt)[4] = (vg & 1) ? v0 : v1;
-    if (vg + 1 < NVG) vload(nxt, vg + 1);
+    gload(KS + vg + 2);
     __builtin_amdgcn_sched_barrier(0);
     const int s2 = vg / (DT / 4), dt0 = 4 * (vg % (DT / 4));
+    u32x4 (&cur)[4] = fr[(KS + vg) % 3];
 #pragma unroll
     for (int u = 0; u < NTL; ++u) {
       const u32x4 pb = {pk[u][2 * s2][0], pk[u][2 * s2][1], pk[u][2 * s2 + 1][0],
@@ -691,39 +691,55 @@ __global__ __launch_bounds__(kRingThreads, 1) void prefill_attn_ring_kernel(
   const bool isk = wv * R::NP * 1024 < R::KBYTES;
   const uint8_t* kbase = (const uint8_t*)p.k + (si.start * (int64_t)g.Hkv + h) * D * 2;
   const uint8_t* vbase = (const uint8_t*)p.vt + ((int64_t)h * D * p.Tp + pad_off(g, s)) * 2;
-  int prow_[R::NP], pcol[R::NP];  // K row or V^T row of the piece, byte column in the row
+  // piece i of this thread: K row or V^T row kr[i] of the block, at source
+  // address pbase[i] + (K: key0 * krs, V^T: key0 * 2) for the block at key0
+  const uint8_t* pbase[R::NP];
+  int kr[R::NP];
 #pragma unroll
   for (int i = 0; i < R::NP; ++i) {
     const int o = (wv * R::NP + i) * 1024 + lane * 16;
     if (isk) {
-      prow_[i] = o / R::KROW;
-      pcol[i] = (((o % R::KROW) / 16) ^ swz<R::KP>(prow_[i])) * 16;
+      kr[i] = o / R::KROW;
+      const int pcol = (((o % R::KROW) / 16) ^ swz<R::KP>(kr[i])) * 16;
+      pbase[i] = kbase + kr[i] * krs + pcol;
     } else {
       const int ov = o - R::KBYTES;
-      prow_[i] = ov / R::VROW;
-      pcol[i] = (((ov % R::VROW) / 16) ^ swz<8>(prow_[i])) * 16;
+      kr[i] = ov / R::VROW;
+      const int pcol = (((ov % R::VROW) / 16) ^ swz<8>(kr[i])) * 16;
+      pbase[i] = vbase + kr[i] * vrs + pcol;
     }
   }
   // lane u < 2 loads tile u's bias (its position's row of log_prior)
   const int bpos = min(rpos[lane & 1], pend - 1);
   const float* bsrc = p.log_prior + ((int64_t)h * T + si.start + bpos) * g.C_slots;
   const int kmax = pend - 1;
-  auto issue = [&](int st, uint32_t slot, uint32_t bslot) {
-    int c = 0, key0;
-    if (st < nrouted) {
-      c = __builtin_amdgcn_readfirstlane((int)Blist[st >> sbl]);
-      key0 = c * g.B + ((st & sbl) << 6);
-    } else {
-      key0 = cdiag * g.B + ((st - nrouted) << 6);
-    }
+  // loads of the block at key0 (chunk c for its bias) into a ring slot
+  auto issue_at = [&](int key0, int c, uint32_t slot, uint32_t bslot) {
+    if (!isk || key0 + 63 <= kmax) {
+      const int64_t off = isk ? (int64_t)key0 * krs : (int64_t)key0 * 2;
 #pragma unroll
-    for (int i = 0; i < R::NP; ++i) {
-      const uint8_t* gp = isk ? kbase + (int64_t)min(key0 + prow_[i], kmax) * krs + pcol[i]
-                              : vbase + (int64_t)key0 * 2 + (int64_t)prow_[i] * vrs + pcol[i];
-      lds_dma16(gp, slot + (wv * R::NP + i) * 1024);
+      for (int i = 0; i < R::NP; ++i) lds_dma16(pbase[i] + off, slot + (wv * R::NP + i) * 1024);
+    } else {
+      // K rows past the sequence end (last chunk of the sequence): repeat the
+      // last key instead of reading beyond it
+#pragma unroll
+      for (int i = 0; i < R::NP; ++i)
+        lds_dma16(pbase[i] + (int64_t)(min(key0 + kr[i], kmax) - kr[i]) * krs,
+                  slot + (wv * R::NP + i) * 1024);
     }
     // the tiles' biases for this block (past the routed blocks: any valid word)
     if (lane < 2) lds_dma4(bsrc + c, bslot + wv * 8);
+  };
+  // first key of step sx's block; c = its chunk for a routed block, else 0
+  auto block_key0 = [&](int sx, int cl) -> int {
+    return sx < nrouted ? cl * g.B + ((sx & sbl) << 6) : cdiag * g.B + ((sx - nrouted) << 6);
+  };
+  auto listed = [&](int sx) -> int {
+    return sx < nrouted ? __builtin_amdgcn_readfirstlane((int)Blist[sx >> sbl]) : 0;
+  };
+  auto issue = [&](int sx, uint32_t slot, uint32_t bslot) {
+    const int c = listed(sx);
+    issue_at(block_key0(sx, c), c, slot, bslot);
   };
 
   // ---- tile state
@@ -762,26 +778,30 @@ __global__ __launch_bounds__(kRingThreads, 1) void prefill_attn_ring_kernel(
     asm volatile("" ::: "memory");
     return (lds_u8*)&ring[st & 3][0];
   };
-  // the refill goes out after this wave's visits: the slot it overwrites was
-  // released by every wave at the step's barrier, and issuing it late keeps
-  // the vector-memory queue off the visits' critical path
-  auto leave = [&](int st) {
-    const int sr = st + 3;
-    issue(min(sr, NS - 1), ring0 + (sr & 3) * R::STAGE, bias0 + (sr & 3) * 4 * kRingTiles);
+  // refill of the slot released at the step's barrier (every wave was done
+  // reading it) with the block three steps ahead
+  auto leave = [&](int st, int cnext) {
+    const int sr = st + 3, sx = min(sr, NS - 1);
+    issue_at(block_key0(sx, cnext), cnext, ring0 + (sr & 3) * R::STAGE,
+             bias0 + (sr & 3) * 4 * kRingTiles);
   };
   // routed blocks: each tile whose position has the chunk active visits it
   // with the tile's bias (the two visits, when both are active, run back to
   // back so that each tile's state is only ever updated in place)
   for (int st = 0; st < nrouted; ++st) {
     lds_u8* kv = enter(st);
+    const int cnext = listed(min(st + 3, NS - 1));  // read now, used by the refill
     const uint32_t act = Act[st >> sbl];
     const bool a0 = rvalid[0] && ((act >> tpos[0]) & 1u);
     const bool a1 = rvalid[1] && ((act >> tpos[1]) & 1u);
     const float* bs = &bias[st & 3][2 * wv];
     const float bz[2] = {bs[0] * kLog2e, bs[1] * kLog2e};
+    // a wave with nothing to visit issues the refill at once; a visiting wave
+    // issues it afterwards, when the other waves' loads have left the queue
+    if (!(a0 || a1)) leave(st, cnext);
     if (a0) visit_ring<D, false, 0, 1>(kv, kv + R::KBYTES, koff, voff, qa, o, l, m, sl2, bz, 0, rpos);
     if (a1) visit_ring<D, false, 1, 1>(kv, kv + R::KBYTES, koff, voff, qa, o, l, m, sl2, bz, 0, rpos);
-    leave(st);
+    if (a0 || a1) leave(st, cnext);
   }
   // the diagonal chunk: both tiles, causal mask, bias 0, one fused visit
   for (int st = nrouted; st < NS; ++st) {
@@ -791,7 +811,7 @@ __global__ __launch_bounds__(kRingThreads, 1) void prefill_attn_ring_kernel(
     if (rvalid[0])
       visit_ring<D, true, 0, 2>(kv, kv + R::KBYTES, koff, voff, qa, o, l, m, sl2, bz,
                                 key0 + 4 * gq, rpos);
-    leave(st);
+    leave(st, 0);
   }
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4));  // no ring load outlives the kernel
 
