@@ -256,7 +256,7 @@ def main():
                 traffic = pmc.get("hbm_bytes_per_launch")
         res["roofline"] = {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
-                           "traffic": traffic, "kernel": "prefill_attn_bf16_kernel<128>",
+                           "traffic": traffic, "kernel": "prefill_attn_ring_kernel<128>",
                            "algorithmic_flops_per_launch": flops,
                            "avg_launch_ms": t_attn}
         config["prefill"] = {"workload": wp.name, "tokens": T, "q_heads": wp.Hq,

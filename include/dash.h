@@ -47,8 +47,8 @@
  * Supported: head_dim in {64, 128}; chunk_size in {64, 128}; dtype bf16 or
  *           fp32 (q, k, v, summaries and out share it; accumulation is fp32);
  *           C_slots <= 2048; alpha in [1, 2].  In bf16 the GQA group size
- *           Hq/Hkv must be 1, 2, 4, 8 or a multiple of 16.  Anything else
- *           returns DASH_ERR_UNSUPPORTED.
+ *           Hq/Hkv must be 1, 2, 4, 8, 16, 32, 64, 128 or 256 (decode: at
+ *           most 64).  Anything else returns DASH_ERR_UNSUPPORTED.
  */
 #ifndef DASH_H_
 #define DASH_H_
