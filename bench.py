@@ -27,6 +27,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -48,10 +49,15 @@ def log(msg):
 
 
 def kernel_hash():
+    """Hash of the attention kernel's sources with comments and blank space
+    removed: a change of code invalidates the stored counters, a comment does not."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "sparse_hierarchical_attention_dash_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "sparse_hierarchical_attention_dash_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -4,29 +4,26 @@
 // the routing bias added to the logits before the softmax, and a separate
 // diagonal branch for the query's own chunk).
 //
-// bf16 kernel.  A workgroup (8 waves) owns P consecutive positions of one
-// chunk of one sequence for one KV head.  Its row tiles are 16 rows each
-// (G query heads of 16/G positions, or 16 heads of one position), up to 16
-// tiles, at most 2 per wave, with the online-softmax state of every tile in
-// registers.
-//   * The union of the P positions' active chunks is listed once in LDS; each
-//     listed 64-key block of K and V is streamed from HBM once per workgroup,
-//     through registers (prefetch of the next block while the current one is
-//     consumed) into double-buffered LDS, V transposed.
-//   * Each wave then runs every tile whose rows have that chunk active:
-//     S^T = K Q^T with 16x16x32 bf16 MFMA (4 key tiles x D/32 steps), adds
-//     s*<q,k>*log2(e) + log_prior*log2(e), updates the running max/sum in
-//     base 2, and accumulates O^T += V^T P^T with the same MFMA.  Rows whose
-//     position lacks the chunk get -inf; a tile with no such row skips it.
-//   * The diagonal chunk follows with bias 0 and a causal mask.
-// The score tiles come out with lane (g, r) holding row r and keys
-// 16t + 4g + j, which is exactly the B operand layout of P^T for the PV MFMA
-// when V^T's columns are stored in that order (attn_stage.h); the output
-// O^T lands with lane (g, r) holding row r, so rescaling and normalising
-// are per-lane.
-//
-// fp32 kernel (the small fp32 configurations): one wave per (token, query
-// head) walking that row's own active chunks and diagonal with VALU math.
+// Three kernels:
+//   * prefill_attn_ring_kernel (bf16, GQA group G >= 16): a 16-row MFMA tile
+//     is the 16 query heads of one position, so tiles share their mask.  A
+//     workgroup of 8 waves owns 16 tiles (two per wave) and streams the union
+//     of its positions' active chunks, then its diagonal blocks, through a
+//     4-slot LDS ring filled by direct global->LDS loads of K rows and of a
+//     transposed V (vt_transpose_kernel writes V^T first).  A per-chunk
+//     activity bitmap built up front tells each wave which of its tiles visit
+//     a staged block.  See the comments at the kernel for the details.
+//   * prefill_attn_bf16_kernel (bf16, G < 16): 16-row tiles of G heads x 16/G
+//     positions; K and V staged through registers into double-buffered LDS.
+//   * rowattn_f32_kernel (fp32): one wave per (token, query head) walking the
+//     row's own active chunks and diagonal with VALU math.
+// Every visit of a 16-row tile to a 64-key block computes S^T = K Q^T with
+// 16x16x32 bf16 MFMA, adds s*<q,k>*log2(e) + log_prior*log2(e), updates the
+// running max/sum in base 2, and accumulates O^T += V^T P^T with the same
+// MFMA.  The score tiles come out with lane (g, r) holding row r and keys
+// 16t + 4g + j, which is exactly the B operand layout of P^T for the PV
+// MFMA when V^T's columns are stored in that order (attn_stage.h); O^T lands
+// with lane (g, r) holding row r, so rescaling and normalising are per-lane.
 #include "attn_stage.h"
 #include "dash_device.h"
 #include "dash_internal.h"
