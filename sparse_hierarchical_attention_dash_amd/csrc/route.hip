@@ -18,6 +18,8 @@
 //      OR_q [x_qc > tau_q] gathered 64 chunks per wave with a ballot into one
 //      mask word, and log_prior_c = sigma*log(w_bar_c) on the active chunks.
 // alpha = 1 is softmax routing: every routable chunk is active.
+#include <type_traits>
+
 #include "dash_device.h"
 #include "dash_internal.h"
 
@@ -42,16 +44,6 @@ __device__ __forceinline__ void pow_pair(float d, float e, float& pw, float& pd)
     pw = exp2f(e * lg);
     pd = exp2f((e - 1.f) * lg);
   }
-}
-
-__device__ __forceinline__ float pow_e(float d, float e, int ecls) {
-  if (ecls == 1) return d;
-  if (ecls == 2) return d * d;
-  if (ecls == 4) {
-    const float d2 = d * d;
-    return d2 * d2;
-  }
-  return exp2f(e * __log2f(d));
 }
 
 // Reductions over the LPH lanes that hold one head's row (LPH = 16: one DPP
@@ -130,9 +122,12 @@ __device__ float solve_tau_row(const float (&xs)[NK], float xmax, float e, bool 
     } else {
       const float M = s1 / cnt;
       float q2 = 0.f;
+      // recompare below rather than keep NK lane masks alive across the sums
+      float tq = tau;
+      asm volatile("" : "+v"(tq));
 #pragma unroll
       for (int k = 0; k < NK; ++k) {
-        const float dm = xs[k] > tau ? xs[k] - M : 0.f;
+        const float dm = xs[k] > tq ? xs[k] - M : 0.f;
         q2 = fmaf(dm, dm, q2);
       }
       q2 = head_sum<LPH>(q2);
@@ -144,6 +139,44 @@ __device__ float solve_tau_row(const float (&xs)[NK], float xmax, float e, bool 
 }
 
 constexpr float kFar = -1e30f;  // "not a routable chunk" in the threshold solve
+
+// Threshold of routing row hh (LPH lanes; chunk c = li + LPH k of U's row in
+// xs[k], k < NKE, where NKE * LPH covers the row's n chunks): x = xs_scale * u;
+// U's entries from n to NKE * LPH hold kFar.  Writes TauX[hh] (or, for softmax routing, the row
+// max and the denominator).
+template <int NKE, int LPH>
+__device__ __forceinline__ void threshold_pass(const float* __restrict__ urow, int li, int n,
+                                               bool live, int hh, bool smax, float xs_scale,
+                                               float ex, int ecls, float* TauX, float* Zs) {
+  float xs[NKE];
+  float xmax = -INFINITY;
+  // U holds kFar past the row's n chunks (up to NKE * LPH), so the values load
+  // without a per-entry predicate
+#pragma unroll
+  for (int k = 0; k < NKE; ++k) {
+    const float x = urow[li + LPH * k] * xs_scale;
+    xs[k] = x;
+    xmax = fmaxf(xmax, x);
+  }
+  xmax = head_max<LPH>(xmax);
+  if (smax) {
+    float z = 0.f;
+#pragma unroll
+    for (int k = 0; k < NKE; ++k) z += exp2f((xs[k] - xmax) * kLog2e);
+    z = head_sum<LPH>(z);
+    if (live && li == 0) {
+      TauX[hh] = xmax;
+      Zs[hh] = z;
+    }
+  } else {
+    float tau;
+    if (ecls == 2) tau = solve_tau_row<NKE, LPH, 2>(xs, xmax, ex, live);
+    else if (ecls == 1) tau = solve_tau_row<NKE, LPH, 1>(xs, xmax, ex, live);
+    else if (ecls == 4) tau = solve_tau_row<NKE, LPH, 4>(xs, xmax, ex, live);
+    else tau = solve_tau_row<NKE, LPH, 0>(xs, xmax, ex, live);
+    if (live && li == 0) TauX[hh] = tau;
+  }
+}
 
 template <bool BF16, int D, int CP>
 __global__ __launch_bounds__(256) void route_kernel(Geom g, RouteParams p) {
@@ -258,71 +291,75 @@ __global__ __launch_bounds__(256) void route_kernel(Geom g, RouteParams p) {
         U[hh * USTR + c] = d * p.gamma_scale;
       }
     }
+    // entries from n up to the row's solve width hold a sentinel far below any
+    // threshold (kFar / xs_scale stays far below after scaling)
+    {
+      const int npad = n <= (NK / 4) * LPH && NK >= 16 ? (NK / 4) * LPH
+                       : n <= (NK / 2) * LPH && NK >= 8 ? (NK / 2) * LPH : CP;
+      const int w = npad - n;
+      for (int idx = tid; idx < 16 * w; idx += 256) {
+        const int hh = idx / w;
+        U[hh * USTR + n + (idx - hh * w)] = kFar;
+      }
+    }
     __syncthreads();
     // ---- 2. thresholds: each pass gives every wave HPW heads, LPH lanes each
     for (int hb = 0; hb < nh; hb += 4 * HPW) {
       const int hh = hb + wv * HPW + lane / LPH;
       const int li = lane % LPH;
       const bool live = hh < nh;
-      float xs[NK];
-      float xmax = -INFINITY;
       const float* urow = U + (hh & 15) * USTR;  // in bounds for every lane
-#pragma unroll
-      for (int k = 0; k < NK; ++k) {
-        const int c = li + LPH * k;
-        const float uv = urow[c];
-        // entries past the row get a finite sentinel far below any threshold;
-        // the empty asm keeps the compiler from carrying the (c < n) predicate
-        // of every entry through the solve as a separate scalar mask
-        float x = (live && c < n) ? uv * xs_scale : kFar;
-        asm volatile("" : "+v"(x));
-        xs[k] = x;
-        xmax = fmaxf(xmax, x);
-      }
-      xmax = head_max<LPH>(xmax);
-      if (smax) {
-        float z = 0.f;
-#pragma unroll
-        for (int k = 0; k < NK; ++k) z += exp2f((xs[k] - xmax) * kLog2e);
-        z = head_sum<LPH>(z);
-        if (live && li == 0) {
-          TauX[hh] = xmax;
-          Zs[hh] = z;
-        }
-      } else {
-        float tau;
-        if (ecls == 2) tau = solve_tau_row<NK, LPH, 2>(xs, xmax, ex, live);
-        else if (ecls == 1) tau = solve_tau_row<NK, LPH, 1>(xs, xmax, ex, live);
-        else if (ecls == 4) tau = solve_tau_row<NK, LPH, 4>(xs, xmax, ex, live);
-        else tau = solve_tau_row<NK, LPH, 0>(xs, xmax, ex, live);
-        if (live && li == 0) TauX[hh] = tau;
-      }
+      // values per lane for this row's n chunks: a quarter, half or all of NK
+      if (n <= (NK / 4) * LPH && NK >= 16)
+        threshold_pass<(NK >= 16 ? NK / 4 : NK), LPH>(urow, li, n, live, hh, smax, xs_scale, ex,
+                                                      ecls, TauX, Zs);
+      else if (n <= (NK / 2) * LPH && NK >= 8)
+        threshold_pass<(NK >= 8 ? NK / 2 : NK), LPH>(urow, li, n, live, hh, smax, xs_scale, ex,
+                                                     ecls, TauX, Zs);
+      else
+        threshold_pass<NK, LPH>(urow, li, n, live, hh, smax, xs_scale, ex, ecls, TauX, Zs);
     }
     __syncthreads();
     if (p.tau && tid < nh)
       p.tau[(int64_t)(h * g.G + h0 + tid) * rows + tok] =
           smax ? -INFINITY : TauX[tid] / am1;
     // ---- 3. group weight numerators and active bits
-    for (int base = 0; base < n; base += 256) {
-      const int c = base + tid;
-      bool on = false;
-      if (c < n) {
-        float ws = 0.f;
-        for (int hh = 0; hh < nh; ++hh) {
-          if (smax) {
-            ws += exp2f((U[hh * USTR + c] - TauX[hh]) * kLog2e) / Zs[hh];
-            on = true;
-          } else {
-            const float d = U[hh * USTR + c] * am1 - TauX[hh];
-            on = on || (d > 0.f);
-            ws += d > 0.f ? pow_e(d, ex, ecls) : 0.f;
+    // (the exponent's form fixed at compile time, heads unrolled: two
+    // independent partial sums, no branch per entry)
+    auto weights = [&](auto ecls_tag) {
+      constexpr int E = decltype(ecls_tag)::value;
+      for (int base = 0; base < n; base += 256) {
+        const int c = base + tid;
+        bool on = false;
+        if (c < n) {
+          float w0 = 0.f, w1 = 0.f;
+#pragma unroll
+          for (int hh = 0; hh < 16; ++hh) {
+            if (hh < nh) {
+              float v;
+              if constexpr (E < 0) {
+                v = exp2f((U[hh * USTR + c] - TauX[hh]) * kLog2e) / Zs[hh];
+                on = true;
+              } else {
+                const float d = U[hh * USTR + c] * am1 - TauX[hh];
+                on = on || (d > 0.f);
+                float pd;
+                pow_pair<E>(fmaxf(d, 0.f), ex, v, pd);
+              }
+              if (hh & 1) w1 += v; else w0 += v;
+            }
           }
+          Wsum[c] += w0 + w1;
         }
-        Wsum[c] += ws;
+        const uint64_t b = __ballot(on);
+        if (lane == 0) Bits[(base >> 6) + wv] |= b;
       }
-      const uint64_t b = __ballot(on);
-      if (lane == 0) Bits[(base >> 6) + wv] |= b;
-    }
+    };
+    if (smax) weights(std::integral_constant<int, -1>());
+    else if (ecls == 2) weights(std::integral_constant<int, 2>());
+    else if (ecls == 1) weights(std::integral_constant<int, 1>());
+    else if (ecls == 4) weights(std::integral_constant<int, 4>());
+    else weights(std::integral_constant<int, 0>());
   }
   __syncthreads();
   if (p.log_prior) {
