@@ -185,7 +185,8 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(Geom g, DecodeParams p
 
   // ---- merge the 4 waves and write this split's partial
   float* Ow = reinterpret_cast<float*>(&Ks[0][0]);  // [4][16][D] floats fit in Ks+Vt
-  const int64_t pbase = (((int64_t)b * g.Hkv + h) * p.nsplit + split) * G;
+  // partials are [batch, Hkv, G, nsplit, *]: one query head's splits are contiguous
+  const int64_t pbase = ((int64_t)b * g.Hkv + h) * G;
 #pragma unroll
   for (int u = 0; u < kMaxDecodeTiles; ++u) {
     if (u >= ntile) break;
@@ -216,50 +217,81 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(Geom g, DecodeParams p
         acc += Ow[(w * 16 + row) * D + d] * sc;
         ls += Lw[w][row] * sc;
       }
-      p.part_acc[(pbase + head) * D + d] = acc;
+      const int64_t pr = (pbase + head) * p.nsplit + split;
+      p.part_acc[pr * D + d] = acc;
       if (d == 0) {
-        p.part_ml[(pbase + head) * 2 + 0] = M;
-        p.part_ml[(pbase + head) * 2 + 1] = ls;
+        p.part_ml[pr * 2 + 0] = M;
+        p.part_ml[pr * 2 + 1] = ls;
       }
     }
     __syncthreads();
   }
 }
 
-// One workgroup per (query head, sequence, KV head), one thread per output
-// dimension: the split maxima/sums are read as broadcasts, the accumulators
-// coalesced.
+// One workgroup per (query head, sequence, KV head).  The head's nsplit
+// partials are contiguous, so every load of the merge is issued in one round:
+// the (max, sum) pairs into LDS, each thread's accumulator pieces (4 dims of
+// some splits) into registers.  Each thread scales and adds its pieces, the
+// split groups are added in LDS, and D threads write the output.
 template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(Geom g, DecodeParams p) {
+__global__ __launch_bounds__(256) void decode_combine_kernel(Geom g, DecodeParams p) {
+  constexpr int NTH = 256;
+  constexpr int TPR = D / 4;        // threads per split row (4 dims each)
+  constexpr int SG = NTH / TPR;     // split groups handled side by side
+  constexpr int MAXS = 64;          // most splits decode_num_splits hands out
+  constexpr int PPT = MAXS / SG;    // split rows per thread
+  __shared__ float Sm[MAXS], Sl[MAXS];
+  __shared__ float Part[SG][D];
   const int q = blockIdx.x, b = blockIdx.y, h = blockIdx.z;
   const int batch = gridDim.y;
-  const int d = threadIdx.x;
+  const int tid = threadIdx.x;
   const int G = g.G;
   const int ns = p.nsplit;
-  const int64_t pb = ((int64_t)b * g.Hkv + h) * ns;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, p.part_ml[((pb + s) * G + q) * 2]);
-  float acc = 0.f, ls = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float ms = p.part_ml[((pb + s) * G + q) * 2];
-    if (ms == -INFINITY) continue;
-    const float sc = exp2f(ms - M);
-    ls += p.part_ml[((pb + s) * G + q) * 2 + 1] * sc;
-    acc += p.part_acc[((pb + s) * G + q) * D + d] * sc;
+  const int64_t row0 = (((int64_t)b * g.Hkv + h) * G + q) * ns;  // first split row
+  const int sg = tid / TPR, d0 = (tid % TPR) * 4;
+  f32x4 x[PPT];
+#pragma unroll
+  for (int k = 0; k < PPT; ++k) {
+    const int sp = sg + SG * k;
+    x[k] = sp < ns ? *reinterpret_cast<const f32x4*>(p.part_acc + (row0 + sp) * D + d0)
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const float v = acc / ls;
-  const int64_t orow = ((int64_t)b * g.Hq + h * G + q) * D;
-  if (g.bf16)
-    ((uint16_t*)p.out)[orow + d] = (uint16_t)f32_to_bf16(v);
-  else
-    ((float*)p.out)[orow + d] = v;
-  if (p.lse && d == 0) p.lse[(int64_t)(h * G + q) * batch + b] = (M + __log2f(ls)) * kLn2;
+  if (tid < MAXS) {
+    Sm[tid] = tid < ns ? p.part_ml[(row0 + tid) * 2] : -INFINITY;
+    Sl[tid] = tid < ns ? p.part_ml[(row0 + tid) * 2 + 1] : 0.f;
+  }
+  __syncthreads();
+  float M = -INFINITY;
+  for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, Sm[sp]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < PPT; ++k) {
+    const int sp = sg + SG * k;
+    if (sp < ns && Sm[sp] != -INFINITY) acc += x[k] * exp2f(Sm[sp] - M);
+  }
+  *reinterpret_cast<f32x4*>(&Part[sg][d0]) = acc;
+  __syncthreads();
+  if (tid < D) {
+    float v = 0.f;
+#pragma unroll
+    for (int k = 0; k < SG; ++k) v += Part[k][tid];
+    float ls = 0.f;
+    for (int sp = 0; sp < ns; ++sp)
+      if (Sm[sp] != -INFINITY) ls += Sl[sp] * exp2f(Sm[sp] - M);
+    v /= ls;
+    const int64_t orow = ((int64_t)b * g.Hq + h * G + q) * D;
+    if (g.bf16)
+      ((uint16_t*)p.out)[orow + tid] = (uint16_t)f32_to_bf16(v);
+    else
+      ((float*)p.out)[orow + tid] = v;
+    if (p.lse && tid == 0) p.lse[(int64_t)(h * G + q) * batch + b] = (M + __log2f(ls)) * kLn2;
+  }
 }
 
 int decode_num_splits(const Geom& g) {
   const int pairs = g.num_seqs * g.Hkv;
   int ns = (1024 + pairs - 1) / max(pairs, 1);
-  ns = max(1, min(ns, 64));
+  ns = max(1, min(ns, 64));  // the combine holds at most 64 splits
   // never more splits than 64-key blocks a sequence can have
   const int maxblocks = (g.max_seqlen + 63) / 64;
   return max(1, min(ns, maxblocks));
@@ -291,11 +323,11 @@ hipError_t launch_decode_attn(const Geom& g, const DecodeParams& p, hipStream_t 
   } while (0)
   if (g.D == 64) {
     DASH_DEC_NT(64);
-    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(g.G, g.num_seqs, g.Hkv), dim3(64), 0, st,
+    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(g.G, g.num_seqs, g.Hkv), dim3(256), 0, st,
                        g, p);
   } else {
     DASH_DEC_NT(128);
-    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(g.G, g.num_seqs, g.Hkv), dim3(128), 0,
+    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(g.G, g.num_seqs, g.Hkv), dim3(256), 0,
                        st, g, p);
   }
 #undef DASH_DEC_NT

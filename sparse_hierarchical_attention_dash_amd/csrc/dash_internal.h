@@ -49,6 +49,7 @@ struct RouteParams {
   float* tau = nullptr;                 // [Hq, rows] or null
   const int32_t* seqlens = nullptr;     // decode mode when non-null
   int64_t rows = 0;                     // T (prefill) or batch (decode)
+  float* ulog = nullptr;                // decode, bf16: logits scratch [rows, Hkv, G, C_slots]
 };
 hipError_t launch_route(const Geom& g, const RouteParams& p, hipStream_t st);
 

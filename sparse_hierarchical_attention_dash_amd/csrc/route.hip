@@ -47,23 +47,26 @@ __device__ __forceinline__ void pow_pair(float d, float e, float& pw, float& pd)
 }
 
 // Reductions over the LPH lanes that hold one head's row (LPH = 16: one DPP
-// row; LPH = 32: two rows joined by one cross-row shuffle).
+// row; 32 or 64: rows joined by cross-row exchanges).
 template <int LPH>
 __device__ __forceinline__ float head_sum(float v) {
   v = row16_sum(v);
-  if constexpr (LPH == 32) v += __shfl_xor(v, 16);
+  if constexpr (LPH >= 32) v += xor16(v);
+  if constexpr (LPH == 64) v += xor32(v);
   return v;
 }
 template <int LPH>
 __device__ __forceinline__ float head_max(float v) {
   v = row16_max(v);
-  if constexpr (LPH == 32) v = fmaxf(v, __shfl_xor(v, 16));
+  if constexpr (LPH >= 32) v = fmaxf(v, xor16(v));
+  if constexpr (LPH == 64) v = fmaxf(v, xor32(v));
   return v;
 }
 template <int LPH>
 __device__ __forceinline__ float head_min(float v) {
   v = row16_min(v);
-  if constexpr (LPH == 32) v = fminf(v, __shfl_xor(v, 16));
+  if constexpr (LPH >= 32) v = fminf(v, xor16(v));
+  if constexpr (LPH == 64) v = fminf(v, xor32(v));
   return v;
 }
 
@@ -151,12 +154,14 @@ __device__ __forceinline__ void threshold_pass(const float* __restrict__ urow, i
   float xs[NKE];
   float xmax = -INFINITY;
   // U holds kFar past the row's n chunks (up to NKE * LPH), so the values load
-  // without a per-entry predicate
+  // without a per-entry predicate; all loads are issued before the first use
+#pragma unroll
+  for (int k = 0; k < NKE; ++k) xs[k] = urow[li + LPH * k];
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int k = 0; k < NKE; ++k) {
-    const float x = urow[li + LPH * k] * xs_scale;
-    xs[k] = x;
-    xmax = fmaxf(xmax, x);
+    xs[k] *= xs_scale;
+    xmax = fmaxf(xmax, xs[k]);
   }
   xmax = head_max<LPH>(xmax);
   if (smax) {
@@ -178,9 +183,13 @@ __device__ __forceinline__ void threshold_pass(const float* __restrict__ urow, i
   }
 }
 
-template <bool BF16, int D, int CP>
-__global__ __launch_bounds__(256) void route_kernel(Geom g, RouteParams p) {
-  constexpr int LPH = CP > 1024 ? 32 : 16;  // lanes per head in the solve
+// NTH = 256 (prefill: many rows) or 1024 (decode: one workgroup per
+// sequence and KV head, so 16 waves share the logits and one wave solves each
+// query head's threshold).
+template <bool BF16, int D, int CP, int NTH, bool UG>
+__global__ __launch_bounds__(NTH) void route_kernel(Geom g, RouteParams p) {
+  constexpr int NW = NTH / 64;              // waves
+  constexpr int LPH = NW == 16 ? 64 : (CP > 1024 ? 32 : 16);  // lanes per head in the solve
   constexpr int HPW = 64 / LPH;             // heads per wave per pass
   constexpr int NK = CP / LPH;              // values per lane in the solve
   constexpr int USTR = CP + 16;     // LDS row stride: rows start 16 banks apart
@@ -215,9 +224,9 @@ __global__ __launch_bounds__(256) void route_kernel(Geom g, RouteParams p) {
   const int n = pos / g.B;
   uint64_t* mrow = p.mask + ((int64_t)h * rows + tok) * g.W;
   if (n <= 0) {
-    for (int w = tid; w < g.W; w += 256) mrow[w] = 0ull;
+    for (int w = tid; w < g.W; w += NTH) mrow[w] = 0ull;
     if (p.tau)
-      for (int q = tid; q < g.G; q += 256)
+      for (int q = tid; q < g.G; q += NTH)
         p.tau[(int64_t)(h * g.G + q) * rows + tok] = INFINITY;
     return;
   }
@@ -227,8 +236,8 @@ __global__ __launch_bounds__(256) void route_kernel(Geom g, RouteParams p) {
   const int ecls = smax ? 0 : (ex == 1.f ? 1 : (ex == 2.f ? 2 : (ex == 4.f ? 4 : 0)));
   const float xs_scale = smax ? 1.f : am1;
 
-  for (int c = tid; c < n; c += 256) Wsum[c] = 0.f;
-  for (int w = tid; w < CP / 64; w += 256) Bits[w] = 0ull;
+  for (int c = tid; c < n; c += NTH) Wsum[c] = 0.f;
+  for (int w = tid; w < CP / 64; w += NTH) Bits[w] = 0ull;
 
   const int ntile_h = (g.G + 15) / 16;
   for (int ht = 0; ht < ntile_h; ++ht) {
@@ -236,8 +245,19 @@ __global__ __launch_bounds__(256) void route_kernel(Geom g, RouteParams p) {
     const int nh = min(16, g.G - h0);
     __syncthreads();
     // ---- 1. logits U[q][c]: 16 heads x 16 chunks per MFMA tile, the
-    //         summary loads of 4 tiles issued before their MFMAs
-    if constexpr (BF16) {
+    //         summary loads of 4 tiles issued before their MFMAs (UG: read
+    //         back from the scratch route_logits_kernel filled)
+    if constexpr (UG) {
+      const float* ug = p.ulog + (((int64_t)tok * g.Hkv + h) * g.G + h0) * g.C_slots;
+      const int n4 = (n + 3) >> 2;  // 16-byte pieces per head row
+      for (int idx = tid; idx < nh * n4; idx += NTH) {
+        const int hh = idx / n4, c4 = (idx - hh * n4) * 4;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(ug + (int64_t)hh * g.C_slots + c4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (c4 + j < n) U[hh * USTR + c4 + j] = v[j];
+      }
+    } else if constexpr (BF16) {
       constexpr int KS = D / 32;
       const int r = lane & 15, gq = lane >> 4;
       bf16x8 qa[KS];
@@ -250,7 +270,7 @@ __global__ __launch_bounds__(256) void route_kernel(Geom g, RouteParams p) {
         qa[ks] = as_bf16x8(v);
       }
       const int nct = (n + 15) >> 4;
-      for (int ct0 = 4 * wv; ct0 < nct; ct0 += 16) {
+      for (int ct0 = 4 * wv; ct0 < nct; ct0 += 4 * NW) {
         u32x4 kv[4][KS];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -274,7 +294,7 @@ __global__ __launch_bounds__(256) void route_kernel(Geom g, RouteParams p) {
         }
       }
     } else {
-      for (int idx = tid; idx < nh * n; idx += 256) {
+      for (int idx = tid; idx < nh * n; idx += NTH) {
         const int hh = idx / n, c = idx - hh * n;
         const float* qr = (const float*)p.q + ((tok * g.Hq + h * g.G + h0 + hh) * (int64_t)D);
         const float* kr = (const float*)p.kbar + (((kb0 + c) * g.Hkv + h) * (int64_t)D);
@@ -297,14 +317,14 @@ __global__ __launch_bounds__(256) void route_kernel(Geom g, RouteParams p) {
       const int npad = n <= (NK / 4) * LPH && NK >= 16 ? (NK / 4) * LPH
                        : n <= (NK / 2) * LPH && NK >= 8 ? (NK / 2) * LPH : CP;
       const int w = npad - n;
-      for (int idx = tid; idx < 16 * w; idx += 256) {
+      for (int idx = tid; idx < 16 * w; idx += NTH) {
         const int hh = idx / w;
         U[hh * USTR + n + (idx - hh * w)] = kFar;
       }
     }
     __syncthreads();
     // ---- 2. thresholds: each pass gives every wave HPW heads, LPH lanes each
-    for (int hb = 0; hb < nh; hb += 4 * HPW) {
+    for (int hb = 0; hb < nh; hb += NW * HPW) {
       const int hh = hb + wv * HPW + lane / LPH;
       const int li = lane % LPH;
       const bool live = hh < nh;
@@ -324,35 +344,46 @@ __global__ __launch_bounds__(256) void route_kernel(Geom g, RouteParams p) {
       p.tau[(int64_t)(h * g.G + h0 + tid) * rows + tok] =
           smax ? -INFINITY : TauX[tid] / am1;
     // ---- 3. group weight numerators and active bits
-    // (the exponent's form fixed at compile time, heads unrolled: two
-    // independent partial sums, no branch per entry)
+    // (the exponent's form fixed at compile time, the 16 rows of the tile read
+    // unconditionally and rows past nh masked by selects: no branch per entry,
+    // all LDS reads of a chunk in flight together)
     auto weights = [&](auto ecls_tag) {
       constexpr int E = decltype(ecls_tag)::value;
-      for (int base = 0; base < n; base += 256) {
-        const int c = base + tid;
-        bool on = false;
-        if (c < n) {
-          float w0 = 0.f, w1 = 0.f;
+      float tx[16], zi[16];
 #pragma unroll
-          for (int hh = 0; hh < 16; ++hh) {
-            if (hh < nh) {
-              float v;
-              if constexpr (E < 0) {
-                v = exp2f((U[hh * USTR + c] - TauX[hh]) * kLog2e) / Zs[hh];
-                on = true;
-              } else {
-                const float d = U[hh * USTR + c] * am1 - TauX[hh];
-                on = on || (d > 0.f);
-                float pd;
-                pow_pair<E>(fmaxf(d, 0.f), ex, v, pd);
-              }
-              if (hh & 1) w1 += v; else w0 += v;
-            }
+      for (int hh = 0; hh < 16; ++hh) {
+        tx[hh] = TauX[hh];
+        zi[hh] = E < 0 ? 1.f / Zs[hh] : 0.f;
+      }
+      for (int base = 0; base < n; base += NTH) {
+        const int c = base + tid;
+        const int cc = min(c, n - 1);
+        float uu[16];
+#pragma unroll
+        for (int hh = 0; hh < 16; ++hh) uu[hh] = U[hh * USTR + cc];
+        __builtin_amdgcn_sched_barrier(0);
+        bool on = false;
+        float w0 = 0.f, w1 = 0.f;
+#pragma unroll
+        for (int hh = 0; hh < 16; ++hh) {
+          const bool valid = hh < nh;
+          float v;
+          if constexpr (E < 0) {
+            v = exp2f((uu[hh] - tx[hh]) * kLog2e) * zi[hh];
+            on = on || valid;
+          } else {
+            const float d = uu[hh] * am1 - tx[hh];
+            on = on || (valid && d > 0.f);
+            float pd;
+            pow_pair<E>(fmaxf(d, 0.f), ex, v, pd);
           }
-          Wsum[c] += w0 + w1;
+          v = valid ? v : 0.f;
+          if (hh & 1) w1 += v; else w0 += v;
         }
+        on = on && c < n;
+        if (c < n) Wsum[c] += w0 + w1;
         const uint64_t b = __ballot(on);
-        if (lane == 0) Bits[(base >> 6) + wv] |= b;
+        if (lane == 0 && (base >> 6) + wv < CP / 64) Bits[(base >> 6) + wv] |= b;
       }
     };
     if (smax) weights(std::integral_constant<int, -1>());
@@ -365,22 +396,79 @@ __global__ __launch_bounds__(256) void route_kernel(Geom g, RouteParams p) {
   if (p.log_prior) {
     float* lrow = p.log_prior + ((int64_t)h * rows + tok) * g.C_slots;
     const float invG = 1.f / (float)g.G;
-    for (int c = tid; c < n; c += 256) {
+    for (int c = tid; c < n; c += NTH) {
       const bool on = (Bits[c >> 6] >> (c & 63)) & 1ull;
       float v = -INFINITY;
       if (on) v = (p.sigma == 0.f) ? 0.f : p.sigma * logf(fmaxf(Wsum[c] * invG, 1e-38f));
       lrow[c] = v;
     }
   }
-  for (int w = tid; w < g.W; w += 256) mrow[w] = (w < CP / 64) ? Bits[w] : 0ull;
+  for (int w = tid; w < g.W; w += NTH) mrow[w] = (w < CP / 64) ? Bits[w] : 0ull;
+}
+
+// Routing logits for a few rows (decode): u[q][c] = gamma*s*<q, k_bar_c> for
+// every routable chunk of each row, 16 heads x 16 chunks per MFMA tile (bf16,
+// fp32 accumulate), one tile per wave and 64 chunks per workgroup, so that the
+// summary reads spread over the whole chip instead of one CU per row.  Written
+// to the scratch [rows, Hkv, G, C_slots] that route_kernel<..., UG> reads.
+template <int D>
+__global__ __launch_bounds__(256) void route_logits_kernel(Geom g, RouteParams p) {
+  constexpr int KS = D / 32;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int r = lane & 15, gq = lane >> 4;
+  const int row = blockIdx.y, h = blockIdx.z;
+  const int n = (p.seqlens[row] - 1) / g.B;
+  const int c0 = (blockIdx.x * 4 + wv) * 16;  // this wave's 16 chunks
+  if (c0 >= n) return;
+  const int64_t kb0 = (int64_t)row * (g.max_seqlen / g.B);
+  // clamped to a valid summary row; columns past n are not written
+  const int c = min(c0 + r, n - 1);
+  const uint16_t* krow = (const uint16_t*)p.kbar + (((kb0 + c) * g.Hkv + h) * (int64_t)D);
+  u32x4 kv[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) kv[ks] = ldg16(krow + 32 * ks + 8 * gq);
+  for (int h0 = 0; h0 < g.G; h0 += 16) {
+    const int nh = min(16, g.G - h0);
+    const uint16_t* qrow =
+        (const uint16_t*)p.q + (((int64_t)row * g.Hq + h * g.G + h0 + r) * D);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (r < nh) v = ldg16(qrow + 32 * ks + 8 * gq);
+      acc = mfma16x16x32(as_bf16x8(v), as_bf16x8(kv[ks]), acc);
+    }
+    // lane (gq, r): heads 4 gq + j, chunk c0 + r
+    if (c0 + r < n) {
+      float* ur = p.ulog + (((int64_t)row * g.Hkv + h) * g.G + h0) * g.C_slots + c0 + r;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (4 * gq + j < nh) ur[(int64_t)(4 * gq + j) * g.C_slots] = acc[j] * p.gamma_scale;
+    }
+  }
 }
 
 hipError_t launch_route(const Geom& g, const RouteParams& p, hipStream_t st) {
   if (p.rows == 0) return hipSuccess;
   dim3 grid((unsigned)p.rows, g.Hkv);
-  dim3 block(256);
-#define DASH_ROUTE(BF, DD, CPV)                                                   \
-  hipLaunchKernelGGL((route_kernel<BF, DD, CPV>), grid, block, 0, st, g, p)
+  // few rows (decode): the logits first, spread over many workgroups, then 16
+  // waves per row for the rest; many rows (prefill): 4 waves per row
+  const bool wide = p.seqlens != nullptr;
+  const bool ug = wide && g.bf16 && p.ulog != nullptr;
+  if (ug) {
+    dim3 lgrid((unsigned)((g.C_slots + 63) / 64), (unsigned)p.rows, g.Hkv);
+    if (g.D == 64) hipLaunchKernelGGL(route_logits_kernel<64>, lgrid, dim3(256), 0, st, g, p);
+    else hipLaunchKernelGGL(route_logits_kernel<128>, lgrid, dim3(256), 0, st, g, p);
+  }
+#define DASH_ROUTE(BF, DD, CPV)                                                                \
+  do {                                                                                         \
+    if (ug)                                                                                    \
+      hipLaunchKernelGGL((route_kernel<BF, DD, CPV, 1024, true>), grid, dim3(1024), 0, st, g, p); \
+    else if (wide)                                                                             \
+      hipLaunchKernelGGL((route_kernel<BF, DD, CPV, 1024, false>), grid, dim3(1024), 0, st, g, p); \
+    else                                                                                       \
+      hipLaunchKernelGGL((route_kernel<BF, DD, CPV, 256, false>), grid, dim3(256), 0, st, g, p);  \
+  } while (0)
 #define DASH_ROUTE_CP(BF, DD)                                                     \
   do {                                                                            \
     if (g.C_slots <= 256) DASH_ROUTE(BF, DD, 256);                                \
