@@ -131,7 +131,7 @@ SparseWs sparse_ws(const Geom& g) {
   return w;
 }
 struct DecodeWs {
-  size_t mask, logp, acc, ml, ulog, total;
+  size_t mask, logp, acc, ml, ulog, tsx, total;
   int nsplit;
 };
 DecodeWs decode_ws(const Geom& g) {
@@ -148,6 +148,8 @@ DecodeWs decode_ws(const Geom& g) {
   o += align_up((size_t)g.num_seqs * g.Hkv * w.nsplit * g.G * 2 * 4);
   w.ulog = o;  // routing logits of the new tokens (bf16 caches)
   if (g.bf16) o += align_up((size_t)g.num_seqs * g.Hkv * g.G * g.C_slots * 4);
+  w.tsx = o;   // their per-head thresholds
+  if (g.bf16) o += align_up((size_t)g.num_seqs * g.Hkv * g.G * 2 * 4);
   w.total = o;
   return w;
 }
@@ -390,7 +392,10 @@ dash_status dash_attn_decode(const dash_shape* shape, const void* q, const void*
   rp.log_prior = logp;
   rp.seqlens = seqlens;
   rp.rows = g.num_seqs;
-  if (g.bf16) rp.ulog = reinterpret_cast<float*>(at(workspace, w.ulog));
+  if (g.bf16) {
+    rp.ulog = reinterpret_cast<float*>(at(workspace, w.ulog));
+    rp.tsx = reinterpret_cast<float*>(at(workspace, w.tsx));
+  }
   DASH_HIP(dash::launch_route(g, rp, s));
   dash::DecodeParams dp;
   dp.q = q;

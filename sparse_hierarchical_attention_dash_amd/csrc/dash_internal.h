@@ -50,6 +50,7 @@ struct RouteParams {
   const int32_t* seqlens = nullptr;     // decode mode when non-null
   int64_t rows = 0;                     // T (prefill) or batch (decode)
   float* ulog = nullptr;                // decode, bf16: logits scratch [rows, Hkv, G, C_slots]
+  float* tsx = nullptr;                 // decode, bf16: per-head threshold scratch [rows, Hkv, G, 2]
 };
 hipError_t launch_route(const Geom& g, const RouteParams& p, hipStream_t st);
 

@@ -70,13 +70,15 @@ __device__ __forceinline__ float head_min(float v) {
   return v;
 }
 
-// Threshold (x units) of one routing row held by LPH lanes, chunk
-// c = (lane % LPH) + LPH k in xs[k] (entries past the row are -1e30).  The
+// Threshold (x units) of one routing row held by LPH lanes in xs[k] (entries
+// past the row are -1e30); xout is the largest value of the row left out of
+// xs (all at or below xmax - 1, so never in the support), -inf if none.  The
 // rows of a wave (64/LPH query heads) iterate together; a converged row
 // keeps its threshold while the others finish.  Branch-free per element:
 // d = max(x - tau, 0) contributes nothing off the support.
 template <int NK, int LPH, int ECLS>
-__device__ float solve_tau_row(const float (&xs)[NK], float xmax, float e, bool live) {
+__device__ float solve_tau_row(const float (&xs)[NK], float xmax, float e, bool live,
+                               float xout) {
   float tau = xmax - 1.f;  // the top entry alone has mass 1 here
   bool done = !live;
   for (int it = 0; it < 200; ++it) {
@@ -118,7 +120,7 @@ __device__ float solve_tau_row(const float (&xs)[NK], float xmax, float e, bool 
     s1 = head_sum<LPH>(s1);
     cnt = head_sum<LPH>(cnt);
     mn_in = head_min<LPH>(mn_in);
-    mx_out = head_max<LPH>(mx_out);
+    mx_out = fmaxf(head_max<LPH>(mx_out), xout);
     float t2;
     if constexpr (ECLS == 1) {
       t2 = (s1 - 1.f) / cnt;
@@ -143,14 +145,31 @@ __device__ float solve_tau_row(const float (&xs)[NK], float xmax, float e, bool 
 
 constexpr float kFar = -1e30f;  // "not a routable chunk" in the threshold solve
 
+// Inclusive prefix sum over the LPH lanes of a head row.
+template <int LPH>
+__device__ __forceinline__ int head_scan(int v, int li) {
+#pragma unroll
+  for (int o = 1; o < LPH; o <<= 1) {
+    const int y = __shfl_up(v, o, LPH);
+    if (li >= o) v += y;
+  }
+  return v;
+}
+
 // Threshold of routing row hh (LPH lanes; chunk c = li + LPH k of U's row in
 // xs[k], k < NKE, where NKE * LPH covers the row's n chunks): x = xs_scale * u;
-// U's entries from n to NKE * LPH hold kFar.  Writes TauX[hh] (or, for softmax routing, the row
-// max and the denominator).
-template <int NKE, int LPH>
+// U's entries from n to NKE * LPH hold kFar.  Writes TauX[hh] (or, for softmax
+// routing, the row max and the denominator).
+// The threshold is at least xmax - 1 (the top entry alone has mass 1 there),
+// so only the candidates x > xmax - 1 can be in the support.  When every row
+// of the wave has at most CAPH of them, they are packed into the row's LDS
+// scratch crow (by a prefix sum over the row's lanes) and the solve runs on
+// CAPH / LPH values per lane instead of NKE.
+template <int NKE, int LPH, int CAPH>
 __device__ __forceinline__ void threshold_pass(const float* __restrict__ urow, int li, int n,
                                                bool live, int hh, bool smax, float xs_scale,
-                                               float ex, int ecls, float* TauX, float* Zs) {
+                                               float ex, int ecls, float* TauX, float* Zs,
+                                               float* crow) {
   float xs[NKE];
   float xmax = -INFINITY;
   // U holds kFar past the row's n chunks (up to NKE * LPH), so the values load
@@ -173,27 +192,65 @@ __device__ __forceinline__ void threshold_pass(const float* __restrict__ urow, i
       TauX[hh] = xmax;
       Zs[hh] = z;
     }
-  } else {
-    float tau;
-    if (ecls == 2) tau = solve_tau_row<NKE, LPH, 2>(xs, xmax, ex, live);
-    else if (ecls == 1) tau = solve_tau_row<NKE, LPH, 1>(xs, xmax, ex, live);
-    else if (ecls == 4) tau = solve_tau_row<NKE, LPH, 4>(xs, xmax, ex, live);
-    else tau = solve_tau_row<NKE, LPH, 0>(xs, xmax, ex, live);
-    if (live && li == 0) TauX[hh] = tau;
+    return;
   }
+  auto solve = [&](const auto& vals, float xout) -> float {
+    constexpr int NV = sizeof(vals) / sizeof(float);
+    if (ecls == 2) return solve_tau_row<NV, LPH, 2>(vals, xmax, ex, live, xout);
+    if (ecls == 1) return solve_tau_row<NV, LPH, 1>(vals, xmax, ex, live, xout);
+    if (ecls == 4) return solve_tau_row<NV, LPH, 4>(vals, xmax, ex, live, xout);
+    return solve_tau_row<NV, LPH, 0>(vals, xmax, ex, live, xout);
+  };
+  float tau;
+  if constexpr (CAPH / LPH < NKE) {
+    const float thr = xmax - 1.f;
+    int cnt = 0;
+    float xo = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NKE; ++k) {
+      const bool c = xs[k] > thr;
+      cnt += c ? 1 : 0;
+      xo = fmaxf(xo, c ? -INFINITY : xs[k]);
+    }
+    const int incl = head_scan<LPH>(cnt, li);
+    const int m = __shfl(incl, (threadIdx.x & 63) | (LPH - 1), 64);  // row total (last lane)
+    if (__ballot(live && m > CAPH) == 0ull) {
+      int pos = incl - cnt;
+#pragma unroll
+      for (int k = 0; k < NKE; ++k) {
+        if (xs[k] > thr) crow[pos] = xs[k];
+        pos += xs[k] > thr ? 1 : 0;
+      }
+      // the wave reads back what its own lanes wrote (LDS ops of a wave are in order)
+      float cv[CAPH / LPH];
+#pragma unroll
+      for (int j = 0; j < CAPH / LPH; ++j) {
+        const int idx = li + LPH * j;
+        cv[j] = idx < m ? crow[idx] : kFar;
+      }
+      tau = solve(cv, head_max<LPH>(xo));
+    } else {
+      tau = solve(xs, -INFINITY);
+    }
+  } else {
+    tau = solve(xs, -INFINITY);
+  }
+  if (live && li == 0) TauX[hh] = tau;
 }
 
 // NTH = 256 (prefill: many rows) or 1024 (decode: one workgroup per
 // sequence and KV head, so 16 waves share the logits and one wave solves each
 // query head's threshold).
-template <bool BF16, int D, int CP, int NTH, bool UG>
+template <bool BF16, int D, int CP, int NTH>
 __global__ __launch_bounds__(NTH) void route_kernel(Geom g, RouteParams p) {
   constexpr int NW = NTH / 64;              // waves
   constexpr int LPH = NW == 16 ? 64 : (CP > 1024 ? 32 : 16);  // lanes per head in the solve
   constexpr int HPW = 64 / LPH;             // heads per wave per pass
   constexpr int NK = CP / LPH;              // values per lane in the solve
   constexpr int USTR = CP + 16;     // LDS row stride: rows start 16 banks apart
+  constexpr int CAPH = LPH == 64 ? 256 : 8 * LPH;  // packed candidates per head row
   __shared__ float U[16 * USTR];    // logits of one 16-head tile
+  __shared__ float Cand[16 * CAPH]; // packed threshold candidates, per head row
   __shared__ float Wsum[CP];        // sum over the group's heads of p
   __shared__ uint64_t Bits[CP / 64];
   __shared__ float TauX[16];        // threshold (x units), or max u (softmax)
@@ -245,19 +302,8 @@ __global__ __launch_bounds__(NTH) void route_kernel(Geom g, RouteParams p) {
     const int nh = min(16, g.G - h0);
     __syncthreads();
     // ---- 1. logits U[q][c]: 16 heads x 16 chunks per MFMA tile, the
-    //         summary loads of 4 tiles issued before their MFMAs (UG: read
-    //         back from the scratch route_logits_kernel filled)
-    if constexpr (UG) {
-      const float* ug = p.ulog + (((int64_t)tok * g.Hkv + h) * g.G + h0) * g.C_slots;
-      const int n4 = (n + 3) >> 2;  // 16-byte pieces per head row
-      for (int idx = tid; idx < nh * n4; idx += NTH) {
-        const int hh = idx / n4, c4 = (idx - hh * n4) * 4;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(ug + (int64_t)hh * g.C_slots + c4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (c4 + j < n) U[hh * USTR + c4 + j] = v[j];
-      }
-    } else if constexpr (BF16) {
+    //         summary loads of 4 tiles issued before their MFMAs
+    if constexpr (BF16) {
       constexpr int KS = D / 32;
       const int r = lane & 15, gq = lane >> 4;
       bf16x8 qa[KS];
@@ -329,15 +375,17 @@ __global__ __launch_bounds__(NTH) void route_kernel(Geom g, RouteParams p) {
       const int li = lane % LPH;
       const bool live = hh < nh;
       const float* urow = U + (hh & 15) * USTR;  // in bounds for every lane
+      float* crow = Cand + (hh & 15) * CAPH;
       // values per lane for this row's n chunks: a quarter, half or all of NK
       if (n <= (NK / 4) * LPH && NK >= 16)
-        threshold_pass<(NK >= 16 ? NK / 4 : NK), LPH>(urow, li, n, live, hh, smax, xs_scale, ex,
-                                                      ecls, TauX, Zs);
+        threshold_pass<(NK >= 16 ? NK / 4 : NK), LPH, CAPH>(urow, li, n, live, hh, smax, xs_scale,
+                                                            ex, ecls, TauX, Zs, crow);
       else if (n <= (NK / 2) * LPH && NK >= 8)
-        threshold_pass<(NK >= 8 ? NK / 2 : NK), LPH>(urow, li, n, live, hh, smax, xs_scale, ex,
-                                                     ecls, TauX, Zs);
+        threshold_pass<(NK >= 8 ? NK / 2 : NK), LPH, CAPH>(urow, li, n, live, hh, smax, xs_scale,
+                                                           ex, ecls, TauX, Zs, crow);
       else
-        threshold_pass<NK, LPH>(urow, li, n, live, hh, smax, xs_scale, ex, ecls, TauX, Zs);
+        threshold_pass<NK, LPH, CAPH>(urow, li, n, live, hh, smax, xs_scale, ex, ecls, TauX, Zs,
+                                      crow);
     }
     __syncthreads();
     if (p.tau && tid < nh)
@@ -410,7 +458,7 @@ __global__ __launch_bounds__(NTH) void route_kernel(Geom g, RouteParams p) {
 // every routable chunk of each row, 16 heads x 16 chunks per MFMA tile (bf16,
 // fp32 accumulate), one tile per wave and 64 chunks per workgroup, so that the
 // summary reads spread over the whole chip instead of one CU per row.  Written
-// to the scratch [rows, Hkv, G, C_slots] that route_kernel<..., UG> reads.
+// to the scratch [rows, Hkv, G, C_slots] that the solve and weight passes read.
 template <int D>
 __global__ __launch_bounds__(256) void route_logits_kernel(Geom g, RouteParams p) {
   constexpr int KS = D / 32;
@@ -448,26 +496,155 @@ __global__ __launch_bounds__(256) void route_logits_kernel(Geom g, RouteParams p
   }
 }
 
+// Decode threshold solve: one wave per (query head, row, KV head) reads the
+// head's logits row from the scratch (CP / 64 values per lane) and writes its
+// threshold in x units (alpha > 1), or its maximum and softmax denominator
+// (alpha = 1), to tsx[row, Hkv, G, 2]; tau (u units) if requested.
+template <int CP>
+__global__ __launch_bounds__(64) void route_solve_kernel(Geom g, RouteParams p) {
+  constexpr int NK = CP / 64;
+  const int q = blockIdx.x, row = blockIdx.y, h = blockIdx.z;
+  const int li = threadIdx.x;
+  const int64_t rows = p.rows;
+  const int n = (p.seqlens[row] - 1) / g.B;
+  float* ts = p.tsx + (((int64_t)row * g.Hkv + h) * g.G + q) * 2;
+  if (n <= 0) {
+    if (li == 0 && p.tau) p.tau[(int64_t)(h * g.G + q) * rows + row] = INFINITY;
+    return;
+  }
+  const float alpha = p.alpha;
+  const bool smax = !(alpha > 1.f);
+  const float am1 = alpha - 1.f;
+  const float ex = smax ? 1.f : 1.f / am1;
+  const int ecls = smax ? 0 : (ex == 1.f ? 1 : (ex == 2.f ? 2 : (ex == 4.f ? 4 : 0)));
+  const float xs_scale = smax ? 1.f : am1;
+  const float* ur = p.ulog + (((int64_t)row * g.Hkv + h) * g.G + q) * g.C_slots;
+  // every load unconditional (clamped to the row) and in flight together;
+  // entries past n become the sentinel afterwards
+  float xs[NK];
+#pragma unroll
+  for (int k = 0; k < NK; ++k) xs[k] = ur[min(li + 64 * k, n - 1)];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < NK; ++k) xs[k] = li + 64 * k < n ? xs[k] * xs_scale : kFar;
+  float xmax = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < NK; ++k) xmax = fmaxf(xmax, xs[k]);
+  xmax = head_max<64>(xmax);
+  if (smax) {
+    float z = 0.f;
+#pragma unroll
+    for (int k = 0; k < NK; ++k) z += exp2f((xs[k] - xmax) * kLog2e);
+    z = head_sum<64>(z);
+    if (li == 0) {
+      ts[0] = xmax;
+      ts[1] = z;
+      if (p.tau) p.tau[(int64_t)(h * g.G + q) * rows + row] = -INFINITY;
+    }
+    return;
+  }
+  float tau;
+  if (ecls == 2) tau = solve_tau_row<NK, 64, 2>(xs, xmax, ex, true, -INFINITY);
+  else if (ecls == 1) tau = solve_tau_row<NK, 64, 1>(xs, xmax, ex, true, -INFINITY);
+  else if (ecls == 4) tau = solve_tau_row<NK, 64, 4>(xs, xmax, ex, true, -INFINITY);
+  else tau = solve_tau_row<NK, 64, 0>(xs, xmax, ex, true, -INFINITY);
+  if (li == 0) {
+    ts[0] = tau;
+    ts[1] = 0.f;
+    if (p.tau) p.tau[(int64_t)(h * g.G + q) * rows + row] = tau / am1;
+  }
+}
+
+// Decode group weights: one thread per routable chunk c of a (row, KV head):
+// w_bar_c = (1/G) sum_q [x_qc - tau_q]_+^(1/(alpha-1)) (softmax: the mean of
+// the heads' softmax probabilities), the active bit OR_q [x_qc > tau_q]
+// gathered 64 chunks per wave into one mask word, and the log-prior
+// sigma*log(w_bar_c) on the active chunks.
+template <int E>
+__global__ __launch_bounds__(256) void route_weights_kernel(Geom g, RouteParams p) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int row = blockIdx.y, h = blockIdx.z;
+  const int64_t rows = p.rows;
+  const int c = blockIdx.x * 256 + tid;
+  const int word = blockIdx.x * 4 + wv;
+  if (word * 64 >= g.C_slots) return;
+  const int n = (p.seqlens[row] - 1) / g.B;
+  const float am1 = p.alpha - 1.f;
+  const float ex = E < 0 ? 1.f : 1.f / am1;
+  const float* ts = p.tsx + ((int64_t)row * g.Hkv + h) * g.G * 2;
+  const float* ur = p.ulog + ((int64_t)row * g.Hkv + h) * g.G * g.C_slots;
+  bool on = false;
+  float w = 0.f;
+  // 16 heads at a time, every load unconditional (clamped) and in flight
+  // together; heads past G and chunks past n are masked by selects
+  const int cc = min(c, max(n - 1, 0));
+  for (int q0 = 0; q0 < g.G; q0 += 16) {
+    float uu[16], t0[16], t1[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int q = min(q0 + j, g.G - 1);
+      uu[j] = ur[(int64_t)q * g.C_slots + cc];
+      t0[j] = ts[2 * q];
+      t1[j] = ts[2 * q + 1];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const bool valid = q0 + j < g.G && c < n;
+      float v;
+      if constexpr (E < 0) {
+        v = exp2f((uu[j] - t0[j]) * kLog2e) / t1[j];
+        on = on || valid;
+      } else {
+        const float d = uu[j] * am1 - t0[j];
+        on = on || (valid && d > 0.f);
+        float pd;
+        pow_pair<E>(fmaxf(d, 0.f), ex, v, pd);
+      }
+      w += valid ? v : 0.f;
+    }
+  }
+  const uint64_t bits = __ballot(on);
+  if (lane == 0) p.mask[((int64_t)h * rows + row) * g.W + word] = bits;
+  if (p.log_prior && c < g.C_slots) {
+    float v = -INFINITY;
+    if (on) v = (p.sigma == 0.f) ? 0.f : p.sigma * logf(fmaxf(w / (float)g.G, 1e-38f));
+    p.log_prior[((int64_t)h * rows + row) * g.C_slots + c] = v;
+  }
+}
+
 hipError_t launch_route(const Geom& g, const RouteParams& p, hipStream_t st) {
   if (p.rows == 0) return hipSuccess;
   dim3 grid((unsigned)p.rows, g.Hkv);
-  // few rows (decode): the logits first, spread over many workgroups, then 16
-  // waves per row for the rest; many rows (prefill): 4 waves per row
+  // few rows (decode, bf16): logits, per-head thresholds and per-chunk
+  // weights as three chip-wide passes through the scratch; few rows in fp32:
+  // one 16-wave workgroup per row; many rows (prefill): 4 waves per row
   const bool wide = p.seqlens != nullptr;
-  const bool ug = wide && g.bf16 && p.ulog != nullptr;
-  if (ug) {
+  if (wide && g.bf16 && p.ulog != nullptr && p.tsx != nullptr) {
     dim3 lgrid((unsigned)((g.C_slots + 63) / 64), (unsigned)p.rows, g.Hkv);
     if (g.D == 64) hipLaunchKernelGGL(route_logits_kernel<64>, lgrid, dim3(256), 0, st, g, p);
     else hipLaunchKernelGGL(route_logits_kernel<128>, lgrid, dim3(256), 0, st, g, p);
+    dim3 sgrid(g.G, (unsigned)p.rows, g.Hkv);
+    if (g.C_slots <= 256) hipLaunchKernelGGL(route_solve_kernel<256>, sgrid, dim3(64), 0, st, g, p);
+    else if (g.C_slots <= 512) hipLaunchKernelGGL(route_solve_kernel<512>, sgrid, dim3(64), 0, st, g, p);
+    else if (g.C_slots <= 1024) hipLaunchKernelGGL(route_solve_kernel<1024>, sgrid, dim3(64), 0, st, g, p);
+    else hipLaunchKernelGGL(route_solve_kernel<2048>, sgrid, dim3(64), 0, st, g, p);
+    dim3 wgrid((unsigned)((g.C_slots + 255) / 256), (unsigned)p.rows, g.Hkv);
+    const float am1 = p.alpha - 1.f;
+    const float ex = am1 > 0.f ? 1.f / am1 : 1.f;
+    if (!(p.alpha > 1.f)) hipLaunchKernelGGL(route_weights_kernel<-1>, wgrid, dim3(256), 0, st, g, p);
+    else if (ex == 2.f) hipLaunchKernelGGL(route_weights_kernel<2>, wgrid, dim3(256), 0, st, g, p);
+    else if (ex == 1.f) hipLaunchKernelGGL(route_weights_kernel<1>, wgrid, dim3(256), 0, st, g, p);
+    else if (ex == 4.f) hipLaunchKernelGGL(route_weights_kernel<4>, wgrid, dim3(256), 0, st, g, p);
+    else hipLaunchKernelGGL(route_weights_kernel<0>, wgrid, dim3(256), 0, st, g, p);
+    return hipGetLastError();
   }
 #define DASH_ROUTE(BF, DD, CPV)                                                                \
   do {                                                                                         \
-    if (ug)                                                                                    \
-      hipLaunchKernelGGL((route_kernel<BF, DD, CPV, 1024, true>), grid, dim3(1024), 0, st, g, p); \
-    else if (wide)                                                                             \
-      hipLaunchKernelGGL((route_kernel<BF, DD, CPV, 1024, false>), grid, dim3(1024), 0, st, g, p); \
+    if (wide)                                                                                  \
+      hipLaunchKernelGGL((route_kernel<BF, DD, CPV, 1024>), grid, dim3(1024), 0, st, g, p);        \
     else                                                                                       \
-      hipLaunchKernelGGL((route_kernel<BF, DD, CPV, 256, false>), grid, dim3(256), 0, st, g, p);  \
+      hipLaunchKernelGGL((route_kernel<BF, DD, CPV, 256>), grid, dim3(256), 0, st, g, p);          \
   } while (0)
 #define DASH_ROUTE_CP(BF, DD)                                                     \
   do {                                                                            \
