@@ -77,7 +77,8 @@ typedef enum {
   DASH_OP_ROUTE = 1,
   DASH_OP_PREFILL = 2,
   DASH_OP_DECODE = 3,
-  DASH_OP_SPARSE = 4
+  DASH_OP_SPARSE = 4,
+  DASH_OP_DECODE_SPARSE = 5
 } dash_op;
 
 typedef struct {
@@ -210,6 +211,53 @@ dash_status dash_attn_decode(const dash_shape* shape, const void* q,
                              float softmax_scale, int enable_gqa, void* out,
                              float* lse, uint64_t* active_blocks, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* Top-k block routing, the comparison mode of the hierarchical methods the
+ * pages set DashAttention against: NSA and InfLLMv2 keep a fixed number of
+ * KV blocks ranked by a coarse score and then run ordinary softmax attention
+ * over the kept tokens ("Technische Samenvatting: DashAttention",
+ * Probleemstelling; the same point in the Paper Overview and in the
+ * aiexpert.news article).  The pages do not define
+ * the coarse score; here it is the group-shared score
+ *     S_c = sum over the G query heads of KV head h of softmax_c(u_c),
+ *     u_c = gamma * s * <q[t,q], k_bar[c,h]>        c < floor(i/B),
+ * the routing logits of dash_route.  The min(topk, floor(i/B)) chunks of
+ * largest S_c are active (equal scores: lower chunk index first) and the
+ * log-prior is 0 on them (-inf elsewhere), so dash_attn_sparse /
+ * dash_attn_decode_sparse then run plain softmax attention over the selected
+ * chunks and the diagonal.  (Dense causal attention on the same kernels is
+ * dash_route with alpha = 1, sigma = 0: every routable chunk, bias 0.)
+ *   topk           >= 1
+ *   decode_seqlens NULL: prefill rows, as dash_route (q [T, Hq, D], kbar
+ *                  [summary_rows, Hkv, D], workspace DASH_OP_ROUTE);
+ *                  device int32 [batch]: one decode row per batch entry at
+ *                  position seqlens[b]-1, shape and kbar as in
+ *                  dash_attn_decode (q [batch, Hq, D]), no workspace.
+ *   active_blocks  [Hkv, rows, W] uint64           (output, required)
+ *   log_prior      [Hkv, rows, C_slots] fp32 or NULL (output) */
+dash_status dash_route_topk(const dash_shape* shape, const void* q, const void* kbar,
+                            int topk, float gamma, float softmax_scale, int enable_gqa,
+                            const int32_t* decode_seqlens, uint64_t* active_blocks,
+                            float* log_prior, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* The attention step of dash_attn_decode ("Fase 2", split-K over the active
+ * chunks plus the diagonal, then the merge of the splits) for a given routing:
+ * dash_attn_decode is its routing of the new tokens followed by this call.
+ * shape as in dash_attn_decode.
+ *   q, k_cache, v_cache, seqlens  as in dash_attn_decode
+ *   active_blocks  [Hkv, batch, W] uint64          (input; bits c >=
+ *                                                   floor((seqlens[b]-1)/B) must be 0)
+ *   log_prior      [Hkv, batch, C_slots] fp32      (input; read where a bit is set)
+ *   out            [batch, Hq, D] dtype            (output)
+ *   lse            [Hq, batch] fp32 or NULL        (output)
+ * Workspace: dash_workspace_size(DASH_OP_DECODE_SPARSE, shape). */
+dash_status dash_attn_decode_sparse(const dash_shape* shape, const void* q,
+                                    const void* k_cache, const void* v_cache,
+                                    const int32_t* seqlens, const uint64_t* active_blocks,
+                                    const float* log_prior, float softmax_scale,
+                                    int enable_gqa, void* out, float* lse, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 /* Workspace bytes that `op` needs for `shape` (0 when none); the same
  * enable_gqa / optional-output choices do not change it. */

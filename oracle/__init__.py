@@ -23,6 +23,7 @@ from .dash_oracle import (  # noqa: F401
     route_position,
     routing_margin,
     route_sequence,
+    route_topk_sequence,
     attention_dense,
     attention_rows,
     prefill,

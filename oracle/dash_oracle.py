@@ -397,6 +397,48 @@ def routing_margin(q, kbar, B, gamma, scale, G, tau_hat, rows, num_slots):
     return out
 
 
+def route_topk_sequence(q, kbar, B, k, gamma, G, scale, rows=None, num_slots=None):
+    """Top-k block routing, the comparison mode.
+
+    The hierarchical methods the pages compare against (NSA, InfLLMv2) pick
+    the top-k KV blocks by coarse attention scores and then run plain softmax
+    attention over the picked tokens ([NL] Probleemstelling; the same passage
+    in the Paper Overview and the aiexpert.news article).  The pages do not
+    define the coarse score or how a GQA group shares it; the reading taken
+    here: each query head's softmax over the routable chunks of its routing
+    logits u = gamma * s * <q, k_bar>, summed over the group's G heads, is the
+    chunk's score S_c; the min(k, n) chunks of largest S_c are active (equal
+    scores: the lower chunk index first), with bias 0.
+
+    Same arguments and layout as route_sequence (k >= 1).  Returns
+    mask [Hkv, L, S] bool, log_prior [Hkv, L, S] (0 on the mask, -inf
+    elsewhere) and score [Hkv, L, S] (S_c on routable chunks, NaN elsewhere).
+    """
+    q = np.asarray(q, dtype=F64)
+    kbar = np.asarray(kbar, dtype=F64)
+    L, Hq, D = q.shape
+    Hkv = kbar.shape[1]
+    S = num_slots if num_slots is not None else -(-L // B)
+    rows = np.arange(L) if rows is None else np.asarray(list(rows), dtype=np.int64)
+    mask = np.zeros((Hkv, L, S), dtype=bool)
+    logp = np.full((Hkv, L, S), -np.inf, dtype=F64)
+    score = np.full((Hkv, L, S), np.nan, dtype=F64)
+    for h in range(Hkv):
+        for i in rows:
+            n = int(i) // B
+            if n == 0:
+                continue
+            sc = np.zeros(n, dtype=F64)
+            for g in range(G):
+                sc += softmax(routing_logits(q[i, h * G + g], kbar[:n, h], gamma, scale))
+            # stable sort on -score: equal scores keep the lower index first
+            top = np.argsort(-sc, kind="stable")[:min(int(k), n)]
+            mask[h, i, top] = True
+            logp[h, i, top] = 0.0
+            score[h, i, :n] = sc
+    return mask, logp, score
+
+
 # ---------------------------------------------------------------------------
 # Phase 2: prior-induced sparse softmax  ([NL] / [ZH] Fase 2 / 阶段 2)
 # ---------------------------------------------------------------------------

@@ -27,10 +27,11 @@ DASH_OP_ROUTE = 1
 DASH_OP_PREFILL = 2
 DASH_OP_DECODE = 3
 DASH_OP_SPARSE = 4
+DASH_OP_DECODE_SPARSE = 5
 
 EXPORTED = ("dash_get_layout", "dash_summarize", "dash_route", "dash_attn_prefill",
-            "dash_attn_sparse", "dash_attn_decode", "dash_workspace_size", "dash_status_string",
-            "dash_abi_version")
+            "dash_attn_sparse", "dash_attn_decode", "dash_route_topk", "dash_attn_decode_sparse",
+            "dash_workspace_size", "dash_status_string", "dash_abi_version")
 
 
 class DashShape(ctypes.Structure):
@@ -100,6 +101,11 @@ def lib():
     L.dash_attn_decode.restype = _I
     L.dash_attn_decode.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _F, _F, _F, _F, _I, _P, _P, _P,
                                    _P, _SZ, _P]
+    L.dash_route_topk.restype = _I
+    L.dash_route_topk.argtypes = [_SHAPE, _P, _P, _I, _F, _F, _I, _P, _P, _P, _P, _SZ, _P]
+    L.dash_attn_decode_sparse.restype = _I
+    L.dash_attn_decode_sparse.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _P, _F, _I, _P, _P, _P,
+                                          _SZ, _P]
     _lib = L
     return L
 

@@ -153,6 +153,22 @@ DecodeWs decode_ws(const Geom& g) {
   w.total = o;
   return w;
 }
+// Decode attention on a given routing: the split partials only.
+struct DecodeSparseWs {
+  size_t acc, ml, total;
+  int nsplit;
+};
+DecodeSparseWs decode_sparse_ws(const Geom& g) {
+  DecodeSparseWs w{};
+  w.nsplit = dash::decode_num_splits(g);
+  size_t o = 0;
+  w.acc = o;
+  o += align_up((size_t)g.num_seqs * g.Hkv * w.nsplit * g.G * g.D * 4);
+  w.ml = o;
+  o += align_up((size_t)g.num_seqs * g.Hkv * w.nsplit * g.G * 2 * 4);
+  w.total = o;
+  return w;
+}
 dash_status check_ws(void* ws, size_t have, size_t need) {
   if (have < need) return DASH_ERR_WORKSPACE_TOO_SMALL;
   if (need && !ws) return DASH_ERR_INVALID_ARGUMENT;
@@ -198,7 +214,7 @@ dash_status dash_get_layout(const dash_shape* shape, int enable_gqa, dash_layout
 
 size_t dash_workspace_size(int op, const dash_shape* shape) {
   Geom g;
-  const bool decode = (op == DASH_OP_DECODE);
+  const bool decode = (op == DASH_OP_DECODE || op == DASH_OP_DECODE_SPARSE);
   if (check_shape(shape, 1, decode, g) != DASH_OK) return 0;
   switch (op) {
     case DASH_OP_SUMMARIZE:
@@ -206,6 +222,7 @@ size_t dash_workspace_size(int op, const dash_shape* shape) {
     case DASH_OP_PREFILL: return prefill_ws(g).total;
     case DASH_OP_DECODE: return decode_ws(g).total;
     case DASH_OP_SPARSE: return sparse_ws(g).total;
+    case DASH_OP_DECODE_SPARSE: return decode_sparse_ws(g).total;
   }
   return 0;
 }
@@ -404,6 +421,81 @@ dash_status dash_attn_decode(const dash_shape* shape, const void* q, const void*
   dp.seqlens = seqlens;
   dp.mask = mask;
   dp.log_prior = logp;
+  dp.out = out;
+  dp.lse = lse;
+  dp.scale = eff_scale(g, softmax_scale);
+  dp.part_acc = reinterpret_cast<float*>(at(workspace, w.acc));
+  dp.part_ml = reinterpret_cast<float*>(at(workspace, w.ml));
+  dp.nsplit = w.nsplit;
+  DASH_HIP(dash::launch_decode_attn(g, dp, s));
+  return DASH_OK;
+}
+
+dash_status dash_route_topk(const dash_shape* shape, const void* q, const void* kbar,
+                            int topk, float gamma, float softmax_scale, int enable_gqa,
+                            const int32_t* decode_seqlens, uint64_t* active_blocks,
+                            float* log_prior, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  const bool decode = decode_seqlens != nullptr;
+  Geom g;
+  dash_status st = check_shape(shape, enable_gqa, decode, g);
+  if (st != DASH_OK) return st;
+  if ((st = check_routing(1.f, gamma, 0.f, softmax_scale)) != DASH_OK) return st;
+  if (topk <= 0) return DASH_ERR_INVALID_ARGUMENT;
+  const size_t need = decode ? 0 : meta_ws(g);
+  if ((st = check_ws(workspace, workspace_bytes, need)) != DASH_OK) return st;
+  if (g.T == 0 || g.num_seqs == 0) return DASH_OK;
+  const bool any_summary = decode ? g.max_seqlen >= g.B : g.T / g.B > 0;
+  if (!q || !active_blocks || (!kbar && any_summary)) return DASH_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(kbar)) return DASH_ERR_INVALID_ARGUMENT;
+  if (decode && g.max_seqlen == 0) return DASH_ERR_INVALID_ARGUMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!decode && g.cu_seqlens) {
+    g.cu_chunks = meta_chunks(workspace);
+    DASH_HIP(dash::launch_varlen_meta(g.cu_seqlens, g.num_seqs, g.B, meta_chunks(workspace),
+                                      nullptr, s));
+  }
+  dash::RouteParams p;
+  p.q = q;
+  p.kbar = kbar;
+  p.alpha = 1.f;
+  p.gamma_scale = gamma * eff_scale(g, softmax_scale);
+  p.sigma = 0.f;
+  p.mask = active_blocks;
+  p.log_prior = log_prior;
+  p.seqlens = decode_seqlens;
+  p.rows = g.T;
+  p.topk = topk;
+  DASH_HIP(dash::launch_route(g, p, s));
+  return DASH_OK;
+}
+
+dash_status dash_attn_decode_sparse(const dash_shape* shape, const void* q,
+                                    const void* k_cache, const void* v_cache,
+                                    const int32_t* seqlens, const uint64_t* active_blocks,
+                                    const float* log_prior, float softmax_scale,
+                                    int enable_gqa, void* out, float* lse, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  Geom g;
+  dash_status st = check_shape(shape, enable_gqa, true, g);
+  if (st != DASH_OK) return st;
+  if (std::isnan(softmax_scale)) return DASH_ERR_INVALID_ARGUMENT;
+  const DecodeSparseWs w = decode_sparse_ws(g);
+  if ((st = check_ws(workspace, workspace_bytes, w.total)) != DASH_OK) return st;
+  if (g.num_seqs == 0) return DASH_OK;
+  if (!q || !k_cache || !v_cache || !seqlens || !active_blocks || !log_prior || !out)
+    return DASH_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return DASH_ERR_INVALID_ARGUMENT;
+  if (g.max_seqlen == 0) return DASH_ERR_INVALID_ARGUMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  dash::DecodeParams dp;
+  dp.q = q;
+  dp.k = k_cache;
+  dp.v = v_cache;
+  dp.seqlens = seqlens;
+  dp.mask = active_blocks;
+  dp.log_prior = log_prior;
   dp.out = out;
   dp.lse = lse;
   dp.scale = eff_scale(g, softmax_scale);

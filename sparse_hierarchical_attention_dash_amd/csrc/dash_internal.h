@@ -51,6 +51,7 @@ struct RouteParams {
   int64_t rows = 0;                     // T (prefill) or batch (decode)
   float* ulog = nullptr;                // decode, bf16: logits scratch [rows, Hkv, G, C_slots]
   float* tsx = nullptr;                 // decode, bf16: per-head threshold scratch [rows, Hkv, G, 2]
+  int topk = 0;                         // > 0: top-k routing (group softmax scores, bias 0)
 };
 hipError_t launch_route(const Geom& g, const RouteParams& p, hipStream_t st);
 

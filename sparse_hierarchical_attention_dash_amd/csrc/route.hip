@@ -18,6 +18,13 @@
 //      OR_q [x_qc > tau_q] gathered 64 chunks per wave with a ballot into one
 //      mask word, and log_prior_c = sigma*log(w_bar_c) on the active chunks.
 // alpha = 1 is softmax routing: every routable chunk is active.
+//
+// Top-k routing (topk > 0; the fixed-size block selection of the hierarchical
+// methods the pages compare against, NSA and InfLLMv2: the top-k blocks by
+// coarse attention scores, then plain softmax attention over them): each
+// head's softmax over the routable chunks, summed over the group's heads, is
+// the chunk's score; the min(k, n) chunks of highest score are active (ties
+// to the lower chunk index), with bias 0.
 #include <type_traits>
 
 #include "dash_device.h"
@@ -238,6 +245,61 @@ __device__ __forceinline__ void threshold_pass(const float* __restrict__ urow, i
   if (live && li == 0) TauX[hh] = tau;
 }
 
+// Top-k selection over the n >= 1 non-negative scores S[0..n): writes the
+// mask words Bits[0 .. ceil(n/64)) with exactly kk bits (kk < n) set: every
+// chunk whose score is above the kk-th largest, then chunks equal to it in
+// index order.  The kk-th largest is found by an MSB-first radix select on
+// the scores' bit patterns (monotone for non-negative floats), 4 bits a pass;
+// the equal ones are ranked by a block-wide prefix count in index order.
+template <int NTH>
+__device__ void topk_select(const float* S, int n, int kk, uint64_t* Bits, uint32_t* hist,
+                            int* wtot) {
+  constexpr int NW = NTH / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  uint32_t prefix = 0, pmask = 0;
+  int need = kk;
+  for (int shift = 28; shift >= 0; shift -= 4) {
+    if (tid < 16) hist[tid] = 0;
+    __syncthreads();
+    for (int c = tid; c < n; c += NTH) {
+      const uint32_t key = __float_as_uint(S[c]);
+      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 15u], 1u);
+    }
+    __syncthreads();
+    int acc = 0, d = 15;
+    for (; d > 0; --d) {
+      const int hd = (int)hist[d];
+      if (acc + hd >= need) break;
+      acc += hd;
+    }
+    need -= acc;
+    prefix |= (uint32_t)d << shift;
+    pmask |= 15u << shift;
+    __syncthreads();  // every thread has read hist before the next pass resets it
+  }
+  // prefix is the kk-th largest key; take all keys above it and the first
+  // `need` keys equal to it
+  int taken = 0;  // equal keys before this pass of NTH chunks
+  for (int base = 0; base < n; base += NTH) {
+    const int c = base + tid;
+    const uint32_t key = c < n ? __float_as_uint(S[c]) : 0u;
+    const bool eq = c < n && key == prefix;
+    const uint64_t eqm = __ballot(eq);
+    if (lane == 0) wtot[wv] = __popcll(eqm);
+    __syncthreads();
+    int before = taken;
+    for (int w = 0; w < wv; ++w) before += wtot[w];
+    int all = taken;
+    for (int w = 0; w < NW; ++w) all += wtot[w];
+    const int rank = before + (int)__popcll(eqm & ((1ull << lane) - 1ull));
+    const bool on = c < n && (key > prefix || (eq && rank < need));
+    const uint64_t b = __ballot(on);
+    if (lane == 0 && (base >> 6) + wv < (n + 63) / 64) Bits[(base >> 6) + wv] = b;
+    taken = all;
+    __syncthreads();  // wtot is rewritten by the next pass
+  }
+}
+
 // NTH = 256 (prefill: many rows) or 1024 (decode: one workgroup per
 // sequence and KV head, so 16 waves share the logits and one wave solves each
 // query head's threshold).
@@ -255,6 +317,8 @@ __global__ __launch_bounds__(NTH) void route_kernel(Geom g, RouteParams p) {
   __shared__ uint64_t Bits[CP / 64];
   __shared__ float TauX[16];        // threshold (x units), or max u (softmax)
   __shared__ float Zs[16];          // softmax denominator (alpha = 1)
+  __shared__ uint32_t Hist[16];     // top-k: radix histogram
+  __shared__ int Wtot[NW];          // top-k: equal keys per wave
 
   const int64_t row = blockIdx.x;
   const int h = blockIdx.y;
@@ -287,6 +351,9 @@ __global__ __launch_bounds__(NTH) void route_kernel(Geom g, RouteParams p) {
         p.tau[(int64_t)(h * g.G + q) * rows + tok] = INFINITY;
     return;
   }
+  // top-k routing scores chunks by the group's summed softmax probabilities
+  const bool topk = p.topk > 0;
+  if (topk) alpha = 1.f;
   const bool smax = !(alpha > 1.f);
   const float am1 = alpha - 1.f;
   const float ex = smax ? 1.f : 1.f / am1;
@@ -390,7 +457,7 @@ __global__ __launch_bounds__(NTH) void route_kernel(Geom g, RouteParams p) {
     __syncthreads();
     if (p.tau && tid < nh)
       p.tau[(int64_t)(h * g.G + h0 + tid) * rows + tok] =
-          smax ? -INFINITY : TauX[tid] / am1;
+          topk ? NAN : (smax ? -INFINITY : TauX[tid] / am1);
     // ---- 3. group weight numerators and active bits
     // (the exponent's form fixed at compile time, the 16 rows of the tile read
     // unconditionally and rows past nh masked by selects: no branch per entry,
@@ -441,13 +508,18 @@ __global__ __launch_bounds__(NTH) void route_kernel(Geom g, RouteParams p) {
     else weights(std::integral_constant<int, 0>());
   }
   __syncthreads();
+  if (topk && p.topk < n) {
+    topk_select<NTH>(Wsum, n, p.topk, Bits, Hist, Wtot);
+    __syncthreads();
+  }
   if (p.log_prior) {
     float* lrow = p.log_prior + ((int64_t)h * rows + tok) * g.C_slots;
     const float invG = 1.f / (float)g.G;
     for (int c = tid; c < n; c += NTH) {
       const bool on = (Bits[c >> 6] >> (c & 63)) & 1ull;
       float v = -INFINITY;
-      if (on) v = (p.sigma == 0.f) ? 0.f : p.sigma * logf(fmaxf(Wsum[c] * invG, 1e-38f));
+      if (on)
+        v = (topk || p.sigma == 0.f) ? 0.f : p.sigma * logf(fmaxf(Wsum[c] * invG, 1e-38f));
       lrow[c] = v;
     }
   }

@@ -1,5 +1,5 @@
-"""Torch-facing wrappers of the C ABI: dash.summarize / route / attn_prefill /
-attn_decode.
+"""Torch-facing wrappers of the C ABI: dash.summarize / route / route_topk /
+attn_prefill / attn_sparse / attn_decode / attn_decode_sparse.
 
 Torch supplies device memory (inputs, outputs, the workspace) and the current
 stream; every computation runs in libdash.so.  Shapes follow include/dash.h:
@@ -117,6 +117,49 @@ def route(q, kbar, num_kv_heads, chunk_size, *, alpha=1.5, gamma=1.0, sigma=1.0,
     return mask, lp, ta
 
 
+def route_topk(q, kbar, num_kv_heads, chunk_size, topk, *, gamma=1.0, softmax_scale=0.0,
+               enable_gqa=True, cu_seqlens=None, max_seqlen=None, decode_seqlens=None,
+               cache_len=None, log_prior=True, mask_out=None, log_prior_out=None,
+               workspace=None):
+    """Top-k block routing (the comparison mode).  Prefill rows as route();
+    with decode_seqlens (int32 [batch]) one decode row per batch entry, q
+    [batch, Hq, D], kbar the summary cache [batch, cache_len/B, Hkv, D].
+    Returns (active_blocks int64 words, log_prior or None)."""
+    _need_cuda(q, kbar, cu_seqlens, decode_seqlens, mask_out, log_prior_out)
+    rows, Hq, D = q.shape
+    dev = q.device
+    if decode_seqlens is None:
+        shape = _seq_shape(q, Hq, num_kv_heads, chunk_size, cu_seqlens, max_seqlen)
+        lay = L.layout(shape, enable_gqa)
+        op_ws = L.DASH_OP_ROUTE
+    else:
+        if cache_len is None:
+            raise ValueError("cache_len is required with decode_seqlens")
+        shape = L.make_shape(rows, cache_len, rows, None, Hq, num_kv_heads, D, chunk_size,
+                             _dtype_code(q))
+        lay = L.layout(L.make_shape(rows, cache_len, rows * cache_len, None, Hq, num_kv_heads,
+                                    D, chunk_size, _dtype_code(q)), enable_gqa)
+        op_ws = None
+    mask = mask_out if mask_out is not None else torch.empty(
+        (num_kv_heads, rows, lay.mask_words), dtype=torch.int64, device=dev)
+    if log_prior_out is not None:
+        lp = log_prior_out
+    else:
+        lp = (torch.full((num_kv_heads, rows, lay.chunk_slots), float("nan"), device=dev)
+              if log_prior else None)
+    if op_ws is None:
+        ws, n = None, 0
+    elif workspace is None:
+        ws, n = _workspace(op_ws, shape, dev)
+    else:
+        ws, n = workspace, L.workspace_size(op_ws, shape)
+    L.check("dash_route_topk", L.lib().dash_route_topk(
+        ctypes.byref(shape), _ptr(q), _ptr(kbar), int(topk), float(gamma),
+        float(softmax_scale), int(enable_gqa), _ptr(decode_seqlens), _ptr(mask), _ptr(lp),
+        _ptr(ws), n, _stream(dev)))
+    return mask, lp
+
+
 def attn_prefill(q, k, v, qbar, chunk_size, *, alpha=1.5, gamma=1.0, sigma=1.0,
                  softmax_scale=0.0, enable_gqa=True, alpha_per_seq=None, cu_seqlens=None,
                  max_seqlen=None, return_lse=False, return_active_blocks=False,
@@ -219,3 +262,25 @@ def attn_decode(q, k_cache, v_cache, seqlens, kbar_cache, chunk_size, *, alpha=1
 def decode_workspace(q, k_cache, chunk_size):
     n = L.workspace_size(L.DASH_OP_DECODE, decode_shape(q, k_cache, chunk_size))
     return torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+
+
+def attn_decode_sparse(q, k_cache, v_cache, seqlens, active_blocks, log_prior, chunk_size, *,
+                       softmax_scale=0.0, enable_gqa=True, return_lse=False, workspace=None,
+                       out=None):
+    """The attention step of a decode for a given routing (active_blocks
+    [Hkv, batch, W] int64 words, log_prior [Hkv, batch, C_slots])."""
+    _need_cuda(q, k_cache, v_cache, seqlens, active_blocks, log_prior)
+    batch, Hq, D = q.shape
+    shape = decode_shape(q, k_cache, chunk_size)
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty((Hq, batch), dtype=torch.float32, device=dev) if return_lse else None
+    n = L.workspace_size(L.DASH_OP_DECODE_SPARSE, shape)
+    if workspace is None or workspace.numel() < n:
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    L.check("dash_attn_decode_sparse", L.lib().dash_attn_decode_sparse(
+        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens),
+        _ptr(active_blocks), _ptr(log_prior), float(softmax_scale), int(enable_gqa), _ptr(out),
+        _ptr(lse), _ptr(workspace), n, _stream(dev)))
+    return out, lse

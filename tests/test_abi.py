@@ -168,3 +168,55 @@ def test_decode_checks(lib):
         L.DASH_ERR_INVALID_ARGUMENT                                   # no cu_seqlens
     assert dec(L.make_shape(4, 4096, 4, None, 128, 1, 128, 64, BF16)) == \
         L.DASH_ERR_UNSUPPORTED                                        # group > 64
+
+
+def test_topk_route_checks(lib):
+    s = shape()
+    need = L.workspace_size(L.DASH_OP_ROUTE, s)
+
+    def rt(sh, **kw):
+        a = dict(q=A, kb=A, k=8, gamma=1.0, scale=0.0, gqa=1, sl=None, m=A, lp=None, ws=A,
+                 n=need)
+        a.update(kw)
+        return lib.dash_route_topk(ctypes.byref(sh), a["q"], a["kb"], a["k"], a["gamma"],
+                                   a["scale"], a["gqa"], a["sl"], a["m"], a["lp"], a["ws"],
+                                   a["n"], None)
+
+    assert rt(s, k=0) == L.DASH_ERR_INVALID_ARGUMENT
+    assert rt(s, k=-3) == L.DASH_ERR_INVALID_ARGUMENT
+    assert rt(s, m=None) == L.DASH_ERR_INVALID_ARGUMENT
+    assert rt(s, q=None) == L.DASH_ERR_INVALID_ARGUMENT
+    assert rt(s, q=A + 4) == L.DASH_ERR_INVALID_ARGUMENT
+    assert rt(s, gamma=0.0) == L.DASH_ERR_INVALID_ARGUMENT
+    assert rt(s, scale=math.nan) == L.DASH_ERR_INVALID_ARGUMENT
+    assert rt(s, gqa=0) == L.DASH_ERR_INVALID_ARGUMENT
+    assert rt(shape(D=96)) == L.DASH_ERR_UNSUPPORTED
+    v = shape(cu=A, num_seqs=3)
+    assert rt(v, n=0, ws=None) == L.DASH_ERR_WORKSPACE_TOO_SMALL     # varlen needs metadata
+    z = shape(T=0, num_seqs=0, max_seqlen=0)
+    assert rt(z) == L.DASH_OK                                        # empty: no HIP call
+    d = L.make_shape(4, 4096, 4, None, 32, 2, 128, 64, BF16)
+    assert rt(d, sl=A, kb=None) == L.DASH_ERR_INVALID_ARGUMENT
+
+
+def test_sparse_decode_checks(lib):
+    s = L.make_shape(4, 4096, 4, None, 32, 2, 128, 64, BF16)
+    need = L.workspace_size(L.DASH_OP_DECODE_SPARSE, s)
+    assert 0 < need < L.workspace_size(L.DASH_OP_DECODE, s)   # no routing buffers
+
+    def ds(sh, **kw):
+        a = dict(q=A, k=A, v=A, sl=A, m=A, lp=A, scale=0.0, gqa=1, out=A, ws=A, n=need)
+        a.update(kw)
+        return lib.dash_attn_decode_sparse(ctypes.byref(sh), a["q"], a["k"], a["v"], a["sl"],
+                                           a["m"], a["lp"], a["scale"], a["gqa"], a["out"],
+                                           None, a["ws"], a["n"], None)
+
+    for key in ("q", "k", "v", "sl", "m", "lp", "out"):
+        assert ds(s, **{key: None}) == L.DASH_ERR_INVALID_ARGUMENT, key
+    assert ds(s, v=A + 8) == L.DASH_ERR_INVALID_ARGUMENT
+    assert ds(s, scale=math.nan) == L.DASH_ERR_INVALID_ARGUMENT
+    assert ds(s, n=need - 1) == L.DASH_ERR_WORKSPACE_TOO_SMALL
+    assert ds(s, ws=A + 16) == L.DASH_ERR_INVALID_ARGUMENT
+    assert ds(L.make_shape(4, 4000, 4, None, 32, 2, 128, 64, BF16)) == \
+        L.DASH_ERR_INVALID_ARGUMENT                                   # capacity % B
+    assert ds(L.make_shape(0, 4096, 0, None, 32, 2, 128, 64, BF16)) == L.DASH_OK

@@ -305,6 +305,89 @@ def test_routable_range_and_head_mapping():
     assert not mask[0, L - 1, :(L - 1) // B].all() or (L - 1) // B == 1
 
 
+# ------------------------------------------------- top-k comparison routing
+
+def _topk_by_hand():
+    # kv head 0 with G = 2; q_g = e_g and gamma * s = 1 make u_g[c] = kbar[c, g].
+    # head 0: u = (ln 8, 0, 0)   -> softmax (8/10, 1/10, 1/10)
+    # head 1: u = (0, ln 2, ln 2) -> softmax (1/5, 2/5, 2/5)
+    # group score S = (1, 1/2, 1/2): chunks 1 and 2 tie.
+    B, L, D = 1, 4, 4
+    q = np.zeros((L, 2, D))
+    q[:, 0, 0], q[:, 1, 1] = 1.0, 1.0
+    kb = np.zeros((L, 1, D))
+    kb[:3, 0, 0] = (math.log(8.0), 0.0, 0.0)
+    kb[:3, 0, 1] = (0.0, math.log(2.0), math.log(2.0))
+    return q, kb, B
+
+
+def test_topk_scores_and_selection_by_hand():
+    q, kb, B = _topk_by_hand()
+    for k, want in ((1, [0]), (2, [0, 1]), (3, [0, 1, 2]), (9, [0, 1, 2])):
+        mask, logp, score = O.route_topk_sequence(q, kb, B, k, gamma=2.0, G=2,
+                                                  scale=0.5, rows=[3])
+        np.testing.assert_allclose(score[0, 3, :3], [1.0, 0.5, 0.5], atol=1e-15)
+        assert np.flatnonzero(mask[0, 3]).tolist() == want   # tie -> lower index
+        assert np.all(logp[0, 3, want] == 0.0)
+        assert np.all(np.isneginf(np.delete(logp[0, 3], want)))
+        assert np.isnan(score[0, 3, 3])                     # diagonal chunk
+
+
+def test_topk_single_head_is_topk_of_logits():
+    # G = 1: softmax is monotone, so the k largest scores are the k largest
+    # logits; enumerate the k-subsets and keep the one of largest logit sum.
+    rng = np.random.default_rng(21)
+    B, L, D, k = 2, 16, 6, 3
+    q = rng.standard_normal((L, 1, D))
+    kb = rng.standard_normal((L // B, 1, D))
+    mask, _, _ = O.route_topk_sequence(q, kb, B, k, gamma=3.0, G=1, scale=0.4)
+    for i in range(L):
+        n = i // B
+        u = [0.4 * 3.0 * float(q[i, 0] @ kb[c, 0]) for c in range(n)]
+        if n <= k:
+            assert mask[0, i].tolist() == [c < n for c in range(L // B)]
+            continue
+        best = max(itertools.combinations(range(n), k), key=lambda t: sum(u[c] for c in t))
+        assert np.flatnonzero(mask[0, i]).tolist() == list(best)
+
+
+def test_topk_invariants():
+    rng = np.random.default_rng(22)
+    B, L, D, G, k = 4, 64, 8, 4, 5
+    q = rng.standard_normal((L, 2 * G, D))
+    kb = rng.standard_normal((L // B, 2, D))
+    # zero summaries on kv head 1 give equal scores: the lowest indices win
+    kb[:, 1, :] = 0.0
+    mask, logp, score = O.route_topk_sequence(q, kb, B, k, gamma=5.0, G=G, scale=0.3)
+    for h in range(2):
+        for i in range(L):
+            n = i // B
+            sel = mask[h, i]
+            assert not sel[n:].any()
+            assert sel.sum() == min(k, n)
+            if n == 0:
+                continue
+            np.testing.assert_allclose(score[h, i, :n].sum(), G, atol=1e-12)
+            s = score[h, i, :n]
+            if sel[:n].all():
+                continue
+            assert s[sel[:n]].min() >= s[~sel[:n]].max()
+            if h == 1:
+                assert np.flatnonzero(sel).tolist() == list(range(min(k, n)))
+
+
+def test_topk_covering_all_chunks_equals_softmax_routing():
+    # k >= n: every routable chunk is active, as under alpha = 1 routing
+    rng = np.random.default_rng(23)
+    B, L, D = 4, 32, 8
+    q = rng.standard_normal((L, 4, D))
+    kb = rng.standard_normal((L // B, 2, D))
+    m1, lp1, _ = O.route_topk_sequence(q, kb, B, L, gamma=4.0, G=2, scale=0.3)
+    m2, _, _ = O.route_sequence(q, kb, B, 1.0, 4.0, 0.0, 2, 0.3)
+    assert np.array_equal(m1, m2)
+    assert np.all(lp1[m1] == 0.0)
+
+
 # ---------------------------------------------------------------- phase 2
 
 def _tiny(seed, L=40, Hq=4, Hkv=2, D=8):
