@@ -80,6 +80,59 @@ def to_bf16_dev(a):
     return torch.from_numpy(a).to(torch.bfloat16).cuda()
 
 
+def matched_topk(n_rows, target_blocks, copies):
+    """The k whose top-k routing activates as many blocks as the entmax
+    routing did: copies * sum_i min(k, n_i) closest to target_blocks."""
+    n_rows = np.asarray(n_rows, dtype=np.int64)
+    best, best_err = 1, None
+    for k in range(1, int(n_rows.max(initial=1)) + 1):
+        err = abs(copies * float(np.minimum(n_rows, k).sum()) - target_blocks)
+        if best_err is None or err < best_err:
+            best, best_err = k, err
+    return best
+
+
+def time_it(stream, fn, reps):
+    """Mean milliseconds of fn() over reps runs after one warm-up, from HIP
+    events on the stream the work is launched on."""
+    import torch
+    fn()
+    a = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    a[0].record(stream)
+    for r in range(reps):
+        fn()
+        a[r + 1].record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a[r].elapsed_time(a[r + 1]) for r in range(reps)]))
+
+
+def graph_time(stream, fn, outs, reps):
+    """Mean milliseconds of one replay of fn() captured as a HIP graph (GPU
+    time without Python launch gaps).  Two replays are first checked to give
+    the eager result bit for bit (outs: the tensors fn writes)."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(2):
+        for o in outs:
+            o.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, r in zip(outs, ref):
+            assert torch.equal(o, r), "graph replay differs from the eager run"
+    a = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    a[0].record(stream)
+    for r in range(reps):
+        g.replay()
+        a[r + 1].record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a[r].elapsed_time(a[r + 1]) for r in range(reps)]))
+
+
 def cpu_baseline(d, w, gamma, rows_n, seed=0):
     """Time the oracle on a stratified sample of prefill rows; returns the
     oracle's active TFLOP/s on that sample (summaries prorated per row)."""
@@ -130,6 +183,8 @@ def main():
     ap.add_argument("--only", choices=["both", "prefill", "decode"], default="both")
     ap.add_argument("--cpu-rows", type=int, default=1536)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip the dense and top-k comparison timings")
     ap.add_argument("--copy-ref", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (the "
                          "reference for scaling HBM byte counters) and exit")
@@ -302,6 +357,101 @@ def main():
             res.update(value=t_dec * 1e3 / wd.batch, unit="us/token", higher_is_better=False)
     res["config"] = config
     res["wall_s"] = wall
+    if not args.no_compare:
+        # Comparison modes on the same kernels (untimed for value): dense
+        # causal attention -- the attention kernel alone over every chunk with
+        # bias 0 (the routing of alpha = 1, sigma = 0, made once, untimed), as a
+        # flash-style dense kernel would run -- and top-k routing with k
+        # matched to the entmax routing's active block count, as a whole step
+        # (summaries, routing, attention).
+        log("comparison modes ...")
+        cmp = {}
+        reps = 3
+        if do_pre:
+            n_i = np.arange(T) // wp.B
+            kp = matched_topk(n_i, float(pop.sum()), wp.Hkv)
+            m2 = torch.empty_like(mask)
+            l2 = torch.empty_like(logp)
+            ops.route(q, kbar, wp.Hkv, wp.B, alpha=1.0, gamma=wp.gamma, sigma=0.0,
+                      mask_out=m2, log_prior_out=l2, log_prior=True, workspace=ws_route)
+
+            def dense_pre():
+                ops.attn_sparse(q, k, v, m2, l2, wp.B, out=out, workspace=ws_sparse)
+
+            def topk_pre():
+                ops.summarize(k, qbar, wp.B, out=kbar, workspace=ws_route)
+                ops.route_topk(q, kbar, wp.Hkv, wp.B, kp, gamma=wp.gamma, mask_out=m2,
+                               log_prior_out=l2, workspace=ws_route)
+                ops.attn_sparse(q, k, v, m2, l2, wp.B, out=out, workspace=ws_sparse)
+
+            pop_dense = popcounts(m2.cpu().numpy())
+            t_dense = time_it(stream, dense_pre, reps)
+            assert np.array_equal(pop_dense, np.broadcast_to(n_i, pop_dense.shape))
+            dense_flops = prefill_active_flops(pop_dense, wp.B, wp.D, G)
+            t_topk = time_it(stream, topk_pre, reps)
+            pop_k = popcounts(m2.cpu().numpy())
+            t_topk_route = time_it(stream, lambda: ops.route_topk(
+                q, kbar, wp.Hkv, wp.B, kp, gamma=wp.gamma, mask_out=m2, log_prior_out=l2,
+                workspace=ws_route), reps)
+            cmp["prefill"] = {
+                "dash_ms": t_pre,
+                "dense_ms": t_dense, "dense_flops": dense_flops,
+                "dense_tflops": dense_flops / (t_dense * 1e-3) / 1e12,
+                "speedup_vs_dense": t_dense / t_pre,
+                "topk_k": kp, "topk_ms": t_topk, "topk_route_ms": t_topk_route,
+                "topk_active_blocks": int(pop_k.sum()), "dash_active_blocks": int(pop.sum()),
+                "speedup_vs_topk": t_topk / t_pre}
+        if do_dec:
+            n_b = (dd["seqlens"].astype(np.int64) - 1) // wd.B
+            kd = matched_topk(n_b, float(popd.sum()), wd.Hkv)
+            ws_ds = ops.decode_sparse_workspace(qd, kc, wd.B)
+            ws_rd = ops.route_topk_decode_workspace(qd, wd.Hkv, wd.B, cap)
+            md = torch.empty_like(abd)
+            ld = torch.empty((wd.Hkv, wd.batch, cap // wd.B), dtype=torch.float32, device=dev)
+            # k at least n: every routable chunk, bias 0
+            md_all, ld_all = ops.route_topk(qd, kbar_c, wd.Hkv, wd.B, cap // wd.B,
+                                            gamma=wd.gamma, decode_seqlens=seqlens,
+                                            cache_len=cap, workspace=ws_rd)
+            torch.cuda.synchronize()
+            assert np.array_equal(popcounts(md_all.cpu().numpy()),
+                                  np.broadcast_to(n_b, (wd.Hkv, wd.batch)))
+
+            def dense_dec():
+                ops.attn_decode_sparse(qd, kc, vc, seqlens, md_all, ld_all, wd.B,
+                                       workspace=ws_ds, out=out_d)
+
+            def topk_dec():
+                ops.route_topk(qd, kbar_c, wd.Hkv, wd.B, kd, gamma=wd.gamma,
+                               decode_seqlens=seqlens, cache_len=cap, mask_out=md,
+                               log_prior_out=ld, workspace=ws_rd)
+                ops.attn_decode_sparse(qd, kc, vc, seqlens, md, ld, wd.B, workspace=ws_ds,
+                                       out=out_d)
+
+            def dash_dec():
+                ops.attn_decode(qd, kc, vc, seqlens, kbar_c, wd.B, alpha=wd.alpha,
+                                gamma=wd.gamma, sigma=wd.sigma, workspace=ws_dec, out=out_d)
+
+            t_dd = time_it(stream, dense_dec, 5)
+            t_kd = time_it(stream, topk_dec, 5)
+            # the same three steps as graph replays: GPU time alone
+            g_dash = graph_time(stream, dash_dec, [out_d], 10)
+            g_dense = graph_time(stream, dense_dec, [out_d], 10)
+            g_topk = graph_time(stream, topk_dec, [out_d, md], 10)
+            dense_bytes = float(np.sum(wd.B * n_b + ((dd["seqlens"] - 1) % wd.B) + 1)) \
+                * wd.Hkv * wd.D * 2 * 2
+            cmp["decode"] = {
+                "dash_us": t_dec * 1e3, "dense_us": t_dd * 1e3,
+                "dense_GB_per_s": dense_bytes / (t_dd * 1e-3) / 1e9,
+                "speedup_vs_dense": t_dd / t_dec,
+                "topk_k": kd, "topk_us": t_kd * 1e3,
+                "topk_active_blocks": int(popcounts(md.cpu().numpy()).sum()),
+                "dash_active_blocks": int(popd.sum()),
+                "speedup_vs_topk": t_kd / t_dec,
+                "graph_us": {"dash": g_dash * 1e3, "dense": g_dense * 1e3,
+                             "topk": g_topk * 1e3},
+                "graph_speedup_vs_dense": g_dense / g_dash,
+                "graph_speedup_vs_topk": g_topk / g_dash}
+        res["compare"] = cmp
     if do_pre and not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         res["cpu_baseline"] = cpu_baseline(dp, wp, wp.gamma, args.cpu_rows)

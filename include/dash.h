@@ -78,7 +78,8 @@ typedef enum {
   DASH_OP_PREFILL = 2,
   DASH_OP_DECODE = 3,
   DASH_OP_SPARSE = 4,
-  DASH_OP_DECODE_SPARSE = 5
+  DASH_OP_DECODE_SPARSE = 5,
+  DASH_OP_ROUTE_DECODE = 6     /* dash_route_topk on decode rows */
 } dash_op;
 
 typedef struct {
@@ -232,7 +233,8 @@ dash_status dash_attn_decode(const dash_shape* shape, const void* q,
  *                  [summary_rows, Hkv, D], workspace DASH_OP_ROUTE);
  *                  device int32 [batch]: one decode row per batch entry at
  *                  position seqlens[b]-1, shape and kbar as in
- *                  dash_attn_decode (q [batch, Hq, D]), no workspace.
+ *                  dash_attn_decode (q [batch, Hq, D]), workspace
+ *                  DASH_OP_ROUTE_DECODE (logits and scores of the rows).
  *   active_blocks  [Hkv, rows, W] uint64           (output, required)
  *   log_prior      [Hkv, rows, C_slots] fp32 or NULL (output) */
 dash_status dash_route_topk(const dash_shape* shape, const void* q, const void* kbar,

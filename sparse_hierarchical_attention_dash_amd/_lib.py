@@ -28,6 +28,7 @@ DASH_OP_PREFILL = 2
 DASH_OP_DECODE = 3
 DASH_OP_SPARSE = 4
 DASH_OP_DECODE_SPARSE = 5
+DASH_OP_ROUTE_DECODE = 6
 
 EXPORTED = ("dash_get_layout", "dash_summarize", "dash_route", "dash_attn_prefill",
             "dash_attn_sparse", "dash_attn_decode", "dash_route_topk", "dash_attn_decode_sparse",

@@ -153,6 +153,23 @@ DecodeWs decode_ws(const Geom& g) {
   w.total = o;
   return w;
 }
+// Top-k routing of decode rows (bf16): logits, per-head softmax statistics
+// and group scores of the new tokens.
+struct RouteDecodeWs {
+  size_t ulog, tsx, score, total;
+};
+RouteDecodeWs route_decode_ws(const Geom& g) {
+  RouteDecodeWs w{};
+  size_t o = 0;
+  w.ulog = o;
+  if (g.bf16) o += align_up((size_t)g.num_seqs * g.Hkv * g.G * g.C_slots * 4);
+  w.tsx = o;
+  if (g.bf16) o += align_up((size_t)g.num_seqs * g.Hkv * g.G * 2 * 4);
+  w.score = o;
+  if (g.bf16) o += align_up((size_t)g.num_seqs * g.Hkv * g.C_slots * 4);
+  w.total = o;
+  return w;
+}
 // Decode attention on a given routing: the split partials only.
 struct DecodeSparseWs {
   size_t acc, ml, total;
@@ -214,7 +231,8 @@ dash_status dash_get_layout(const dash_shape* shape, int enable_gqa, dash_layout
 
 size_t dash_workspace_size(int op, const dash_shape* shape) {
   Geom g;
-  const bool decode = (op == DASH_OP_DECODE || op == DASH_OP_DECODE_SPARSE);
+  const bool decode = (op == DASH_OP_DECODE || op == DASH_OP_DECODE_SPARSE ||
+                       op == DASH_OP_ROUTE_DECODE);
   if (check_shape(shape, 1, decode, g) != DASH_OK) return 0;
   switch (op) {
     case DASH_OP_SUMMARIZE:
@@ -223,6 +241,7 @@ size_t dash_workspace_size(int op, const dash_shape* shape) {
     case DASH_OP_DECODE: return decode_ws(g).total;
     case DASH_OP_SPARSE: return sparse_ws(g).total;
     case DASH_OP_DECODE_SPARSE: return decode_sparse_ws(g).total;
+    case DASH_OP_ROUTE_DECODE: return route_decode_ws(g).total;
   }
   return 0;
 }
@@ -442,7 +461,8 @@ dash_status dash_route_topk(const dash_shape* shape, const void* q, const void* 
   if (st != DASH_OK) return st;
   if ((st = check_routing(1.f, gamma, 0.f, softmax_scale)) != DASH_OK) return st;
   if (topk <= 0) return DASH_ERR_INVALID_ARGUMENT;
-  const size_t need = decode ? 0 : meta_ws(g);
+  const RouteDecodeWs dw = route_decode_ws(g);
+  const size_t need = decode ? dw.total : meta_ws(g);
   if ((st = check_ws(workspace, workspace_bytes, need)) != DASH_OK) return st;
   if (g.T == 0 || g.num_seqs == 0) return DASH_OK;
   const bool any_summary = decode ? g.max_seqlen >= g.B : g.T / g.B > 0;
@@ -466,6 +486,11 @@ dash_status dash_route_topk(const dash_shape* shape, const void* q, const void* 
   p.seqlens = decode_seqlens;
   p.rows = g.T;
   p.topk = topk;
+  if (decode && g.bf16) {
+    p.ulog = reinterpret_cast<float*>(at(workspace, dw.ulog));
+    p.tsx = reinterpret_cast<float*>(at(workspace, dw.tsx));
+    p.score = reinterpret_cast<float*>(at(workspace, dw.score));
+  }
   DASH_HIP(dash::launch_route(g, p, s));
   return DASH_OK;
 }

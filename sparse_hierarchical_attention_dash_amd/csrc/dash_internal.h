@@ -52,6 +52,7 @@ struct RouteParams {
   float* ulog = nullptr;                // decode, bf16: logits scratch [rows, Hkv, G, C_slots]
   float* tsx = nullptr;                 // decode, bf16: per-head threshold scratch [rows, Hkv, G, 2]
   int topk = 0;                         // > 0: top-k routing (group softmax scores, bias 0)
+  float* score = nullptr;               // decode, bf16, top-k: group scores scratch [rows, Hkv, C_slots]
 };
 hipError_t launch_route(const Geom& g, const RouteParams& p, hipStream_t st);
 

@@ -245,58 +245,120 @@ __device__ __forceinline__ void threshold_pass(const float* __restrict__ urow, i
   if (live && li == 0) TauX[hh] = tau;
 }
 
-// Top-k selection over the n >= 1 non-negative scores S[0..n): writes the
-// mask words Bits[0 .. ceil(n/64)) with exactly kk bits (kk < n) set: every
-// chunk whose score is above the kk-th largest, then chunks equal to it in
-// index order.  The kk-th largest is found by an MSB-first radix select on
-// the scores' bit patterns (monotone for non-negative floats), 4 bits a pass;
-// the equal ones are ranked by a block-wide prefix count in index order.
-template <int NTH>
-__device__ void topk_select(const float* S, int n, int kk, uint64_t* Bits, uint32_t* hist,
-                            int* wtot) {
+// Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele inside each
+// 16-lane DPP row (row shifts read 0 past the row's start), then the totals
+// of the rows below added from lanes 15, 31 and 47.
+template <int S>
+__device__ __forceinline__ uint32_t dpp_row_shr(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x110 + S, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += dpp_row_shr<1>(v);
+  v += dpp_row_shr<2>(v);
+  v += dpp_row_shr<4>(v);
+  v += dpp_row_shr<8>(v);
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return v + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
+// Top-k selection over the n >= 1 non-negative scores S[0..n) (n <= CP; S
+// in LDS or global memory): writes the mask words Bits[0 .. ceil(n/64)) with
+// exactly kk bits (kk < n) set: every chunk whose score is above the kk-th
+// largest, then chunks equal to it in index order.
+// The kk-th largest is found by an MSB-first radix select on the scores' bit
+// patterns (monotone for non-negative floats), 8 bits a pass, on keys held in
+// registers (chunk tid + NTH k in key[k]).  A pass adds its keys to the
+// pass's own 256-bin histogram in LDS; wave 0 then scans the bins from the
+// top (4 per lane, one wave-wide prefix sum) and publishes the bin of the
+// needed key; two barriers a pass.  The passes stop early once that bin holds
+// exactly the keys still needed.  Keys equal to the resolved prefix are then
+// ranked in index order by one block-wide count.
+// hist: 1024 words of LDS; wtot: KPT * NTH / 64 + 3 words.
+template <int NTH, int CP>
+__device__ __forceinline__ void topk_select(const float* S, int n, int kk, uint64_t* Bits,
+                                            uint32_t* hist, int* wtot) {
   constexpr int NW = NTH / 64;
+  constexpr int KPT = (CP + NTH - 1) / NTH;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int* sel = wtot + KPT * NW;  // digit, keys still needed, keys in its bin
+  uint32_t key[KPT];
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) key[k] = __float_as_uint(S[min(tid + NTH * k, n - 1)]);
+  for (int i = tid; i < 1024; i += NTH) hist[i] = 0;
+  __syncthreads();
   uint32_t prefix = 0, pmask = 0;
   int need = kk;
-  for (int shift = 28; shift >= 0; shift -= 4) {
-    if (tid < 16) hist[tid] = 0;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    uint32_t* hp = hist + 256 * pass;
+#pragma unroll
+    for (int k = 0; k < KPT; ++k)
+      if (tid + NTH * k < n && (key[k] & pmask) == prefix)
+        atomicAdd(&hp[(key[k] >> shift) & 255u], 1u);
     __syncthreads();
-    for (int c = tid; c < n; c += NTH) {
-      const uint32_t key = __float_as_uint(S[c]);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 15u], 1u);
+    if (wv == 0) {
+      // lane l holds bins 255-4l (largest) down to 252-4l
+      const int top = 255 - 4 * lane;
+      const uint32_t h3 = hp[top], h2 = hp[top - 1], h1 = hp[top - 2], h0 = hp[top - 3];
+      const uint32_t incl = wave_incl_scan(h0 + h1 + h2 + h3);
+      uint32_t a = incl - (h0 + h1 + h2 + h3);  // keys in the bins above this lane's
+      const uint32_t nd = (uint32_t)need;
+      if (a < nd && nd <= incl) {  // exactly one lane
+        int dd;
+        uint32_t cnt;
+        if (a + h3 >= nd) {
+          dd = top; cnt = h3;
+        } else if (a + h3 + h2 >= nd) {
+          a += h3; dd = top - 1; cnt = h2;
+        } else if (a + h3 + h2 + h1 >= nd) {
+          a += h3 + h2; dd = top - 2; cnt = h1;
+        } else {
+          a += h3 + h2 + h1; dd = top - 3; cnt = h0;
+        }
+        sel[0] = dd;
+        sel[1] = (int)(nd - a);
+        sel[2] = (int)cnt;
+      }
     }
     __syncthreads();
-    int acc = 0, d = 15;
-    for (; d > 0; --d) {
-      const int hd = (int)hist[d];
-      if (acc + hd >= need) break;
-      acc += hd;
-    }
-    need -= acc;
+    const int d = sel[0], hd = sel[2];
+    need = sel[1];
     prefix |= (uint32_t)d << shift;
-    pmask |= 15u << shift;
-    __syncthreads();  // every thread has read hist before the next pass resets it
+    pmask |= 255u << shift;
+    if (hd == need) break;  // the whole bin is taken (same on every thread)
   }
-  // prefix is the kk-th largest key; take all keys above it and the first
-  // `need` keys equal to it
-  int taken = 0;  // equal keys before this pass of NTH chunks
-  for (int base = 0; base < n; base += NTH) {
-    const int c = base + tid;
-    const uint32_t key = c < n ? __float_as_uint(S[c]) : 0u;
-    const bool eq = c < n && key == prefix;
-    const uint64_t eqm = __ballot(eq);
-    if (lane == 0) wtot[wv] = __popcll(eqm);
-    __syncthreads();
-    int before = taken;
-    for (int w = 0; w < wv; ++w) before += wtot[w];
-    int all = taken;
-    for (int w = 0; w < NW; ++w) all += wtot[w];
-    const int rank = before + (int)__popcll(eqm & ((1ull << lane) - 1ull));
-    const bool on = c < n && (key > prefix || (eq && rank < need));
+  // every key above the prefix on the resolved bits, and the first `need`
+  // keys equal to it there
+  uint64_t eqm[KPT];
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const bool eq = tid + NTH * k < n && (key[k] & pmask) == prefix;
+    eqm[k] = __ballot(eq);
+    if (lane == 0) wtot[k * NW + wv] = __popcll(eqm[k]);
+  }
+  __syncthreads();
+  int before = 0;  // equal keys in the blocks k' < k
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const int c = tid + NTH * k;
+    int pre = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int t = wtot[k * NW + w];
+      pre += w < wv ? t : 0;
+      all += t;
+    }
+    const uint32_t km = key[k] & pmask;
+    const bool eq = (eqm[k] >> lane) & 1ull;
+    const int rank = before + pre + (int)__popcll(eqm[k] & ((1ull << lane) - 1ull));
+    const bool on = c < n && (km > prefix || (eq && rank < need));
     const uint64_t b = __ballot(on);
-    if (lane == 0 && (base >> 6) + wv < (n + 63) / 64) Bits[(base >> 6) + wv] = b;
-    taken = all;
-    __syncthreads();  // wtot is rewritten by the next pass
+    const int word = k * NW + wv;
+    if (lane == 0 && word < (n + 63) / 64) Bits[word] = b;
+    before += all;
   }
 }
 
@@ -317,8 +379,7 @@ __global__ __launch_bounds__(NTH) void route_kernel(Geom g, RouteParams p) {
   __shared__ uint64_t Bits[CP / 64];
   __shared__ float TauX[16];        // threshold (x units), or max u (softmax)
   __shared__ float Zs[16];          // softmax denominator (alpha = 1)
-  __shared__ uint32_t Hist[16];     // top-k: radix histogram
-  __shared__ int Wtot[NW];          // top-k: equal keys per wave
+  __shared__ int Wtot[((CP + NTH - 1) / NTH) * NW + 3];  // top-k: equal keys per wave
 
   const int64_t row = blockIdx.x;
   const int h = blockIdx.y;
@@ -509,7 +570,9 @@ __global__ __launch_bounds__(NTH) void route_kernel(Geom g, RouteParams p) {
   }
   __syncthreads();
   if (topk && p.topk < n) {
-    topk_select<NTH>(Wsum, n, p.topk, Bits, Hist, Wtot);
+    // the candidate scratch (free by now) holds the radix histograms
+    static_assert(16 * CAPH >= 1024, "histogram space");
+    topk_select<NTH, CP>(Wsum, n, p.topk, Bits, reinterpret_cast<uint32_t*>(Cand), Wtot);
     __syncthreads();
   }
   if (p.log_prior) {
@@ -676,6 +739,10 @@ __global__ __launch_bounds__(256) void route_weights_kernel(Geom g, RouteParams 
       w += valid ? v : 0.f;
     }
   }
+  if (p.topk > 0) {  // top-k: the group score, selected by the next pass
+    if (c < n) p.score[((int64_t)row * g.Hkv + h) * g.C_slots + c] = w;
+    return;
+  }
   const uint64_t bits = __ballot(on);
   if (lane == 0) p.mask[((int64_t)h * rows + row) * g.W + word] = bits;
   if (p.log_prior && c < g.C_slots) {
@@ -685,6 +752,49 @@ __global__ __launch_bounds__(256) void route_weights_kernel(Geom g, RouteParams 
   }
 }
 
+// Decode top-k selection: one 4-wave workgroup per (row, KV head) keeps the
+// min(k, n) largest group scores of the row (ties to the lower chunk index),
+// read straight from the scratch, and writes the mask words and the
+// log-prior (0 on the kept chunks, -inf on the other routable ones).
+template <int CP>
+__global__ __launch_bounds__(256) void route_topk_select_kernel(Geom g, RouteParams p) {
+  constexpr int NTH = 256;
+  __shared__ uint64_t Bits[CP / 64];
+  constexpr int KPT = (CP + NTH - 1) / NTH;
+  __shared__ uint32_t Hist[1024];
+  __shared__ int Wtot[KPT * (NTH / 64) + 3];
+  const int row = blockIdx.x, h = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int64_t rows = p.rows;
+  const int n = (p.seqlens[row] - 1) / g.B;
+  uint64_t* mrow = p.mask + ((int64_t)h * rows + row) * g.W;
+  if (n <= 0) {
+    for (int w = tid; w < g.W; w += NTH) mrow[w] = 0ull;
+    return;
+  }
+  // every routable chunk when k >= n; the selection overwrites words < ceil(n/64)
+  for (int w = tid; w < CP / 64; w += NTH) {
+    const int lo = 64 * w;
+    Bits[w] = lo + 64 <= n ? ~0ull : (lo < n ? (1ull << (n - lo)) - 1ull : 0ull);
+  }
+  if (p.topk < n)
+    topk_select<NTH, CP>(p.score + ((int64_t)row * g.Hkv + h) * g.C_slots, n, p.topk, Bits,
+                         Hist, Wtot);
+  __syncthreads();
+  if (p.log_prior) {
+    float* lrow = p.log_prior + ((int64_t)h * rows + row) * g.C_slots;
+    uint64_t wd[KPT];
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) wd[k] = Bits[min((tid + NTH * k) >> 6, CP / 64 - 1)];
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+      const int c = tid + NTH * k;
+      if (c < n) lrow[c] = ((wd[k] >> (c & 63)) & 1ull) ? 0.f : -INFINITY;
+    }
+  }
+  for (int w = tid; w < g.W; w += NTH) mrow[w] = (w < CP / 64) ? Bits[w] : 0ull;
+}
+
 hipError_t launch_route(const Geom& g, const RouteParams& p, hipStream_t st) {
   if (p.rows == 0) return hipSuccess;
   dim3 grid((unsigned)p.rows, g.Hkv);
@@ -692,7 +802,8 @@ hipError_t launch_route(const Geom& g, const RouteParams& p, hipStream_t st) {
   // weights as three chip-wide passes through the scratch; few rows in fp32:
   // one 16-wave workgroup per row; many rows (prefill): 4 waves per row
   const bool wide = p.seqlens != nullptr;
-  if (wide && g.bf16 && p.ulog != nullptr && p.tsx != nullptr) {
+  if (wide && g.bf16 && p.ulog != nullptr && p.tsx != nullptr &&
+      (p.topk <= 0 || p.score != nullptr)) {
     dim3 lgrid((unsigned)((g.C_slots + 63) / 64), (unsigned)p.rows, g.Hkv);
     if (g.D == 64) hipLaunchKernelGGL(route_logits_kernel<64>, lgrid, dim3(256), 0, st, g, p);
     else hipLaunchKernelGGL(route_logits_kernel<128>, lgrid, dim3(256), 0, st, g, p);
@@ -709,6 +820,13 @@ hipError_t launch_route(const Geom& g, const RouteParams& p, hipStream_t st) {
     else if (ex == 1.f) hipLaunchKernelGGL(route_weights_kernel<1>, wgrid, dim3(256), 0, st, g, p);
     else if (ex == 4.f) hipLaunchKernelGGL(route_weights_kernel<4>, wgrid, dim3(256), 0, st, g, p);
     else hipLaunchKernelGGL(route_weights_kernel<0>, wgrid, dim3(256), 0, st, g, p);
+    if (p.topk > 0) {
+      dim3 tgrid((unsigned)p.rows, g.Hkv);
+      if (g.C_slots <= 256) hipLaunchKernelGGL(route_topk_select_kernel<256>, tgrid, dim3(256), 0, st, g, p);
+      else if (g.C_slots <= 512) hipLaunchKernelGGL(route_topk_select_kernel<512>, tgrid, dim3(256), 0, st, g, p);
+      else if (g.C_slots <= 1024) hipLaunchKernelGGL(route_topk_select_kernel<1024>, tgrid, dim3(256), 0, st, g, p);
+      else hipLaunchKernelGGL(route_topk_select_kernel<2048>, tgrid, dim3(256), 0, st, g, p);
+    }
     return hipGetLastError();
   }
 #define DASH_ROUTE(BF, DD, CPV)                                                                \

@@ -139,7 +139,7 @@ def route_topk(q, kbar, num_kv_heads, chunk_size, topk, *, gamma=1.0, softmax_sc
                              _dtype_code(q))
         lay = L.layout(L.make_shape(rows, cache_len, rows * cache_len, None, Hq, num_kv_heads,
                                     D, chunk_size, _dtype_code(q)), enable_gqa)
-        op_ws = None
+        op_ws = L.DASH_OP_ROUTE_DECODE
     mask = mask_out if mask_out is not None else torch.empty(
         (num_kv_heads, rows, lay.mask_words), dtype=torch.int64, device=dev)
     if log_prior_out is not None:
@@ -147,9 +147,7 @@ def route_topk(q, kbar, num_kv_heads, chunk_size, topk, *, gamma=1.0, softmax_sc
     else:
         lp = (torch.full((num_kv_heads, rows, lay.chunk_slots), float("nan"), device=dev)
               if log_prior else None)
-    if op_ws is None:
-        ws, n = None, 0
-    elif workspace is None:
+    if workspace is None:
         ws, n = _workspace(op_ws, shape, dev)
     else:
         ws, n = workspace, L.workspace_size(op_ws, shape)
@@ -158,6 +156,15 @@ def route_topk(q, kbar, num_kv_heads, chunk_size, topk, *, gamma=1.0, softmax_sc
         float(softmax_scale), int(enable_gqa), _ptr(decode_seqlens), _ptr(mask), _ptr(lp),
         _ptr(ws), n, _stream(dev)))
     return mask, lp
+
+
+def route_topk_decode_workspace(q, num_kv_heads, chunk_size, cache_len):
+    """Allocate the workspace route_topk needs for decode rows (q [batch, Hq, D])."""
+    batch, Hq, D = q.shape
+    shape = L.make_shape(batch, cache_len, batch, None, Hq, num_kv_heads, D, chunk_size,
+                         _dtype_code(q))
+    n = L.workspace_size(L.DASH_OP_ROUTE_DECODE, shape)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
 
 
 def attn_prefill(q, k, v, qbar, chunk_size, *, alpha=1.5, gamma=1.0, sigma=1.0,
@@ -261,6 +268,11 @@ def attn_decode(q, k_cache, v_cache, seqlens, kbar_cache, chunk_size, *, alpha=1
 
 def decode_workspace(q, k_cache, chunk_size):
     n = L.workspace_size(L.DASH_OP_DECODE, decode_shape(q, k_cache, chunk_size))
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+
+
+def decode_sparse_workspace(q, k_cache, chunk_size):
+    n = L.workspace_size(L.DASH_OP_DECODE_SPARSE, decode_shape(q, k_cache, chunk_size))
     return torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
 
 

@@ -196,7 +196,13 @@ def test_topk_route_checks(lib):
     z = shape(T=0, num_seqs=0, max_seqlen=0)
     assert rt(z) == L.DASH_OK                                        # empty: no HIP call
     d = L.make_shape(4, 4096, 4, None, 32, 2, 128, 64, BF16)
-    assert rt(d, sl=A, kb=None) == L.DASH_ERR_INVALID_ARGUMENT
+    nd = L.workspace_size(L.DASH_OP_ROUTE_DECODE, d)
+    # logits [4, 2, 16, 64] + softmax statistics [4, 2, 16, 2] + scores [4, 2, 64], fp32
+    assert nd == 4 * 2 * 16 * 64 * 4 + 256 * -(-(4 * 2 * 16 * 2 * 4) // 256) + 4 * 2 * 64 * 4
+    assert rt(d, sl=A, n=nd - 1) == L.DASH_ERR_WORKSPACE_TOO_SMALL
+    assert rt(d, sl=A, kb=None, n=nd) == L.DASH_ERR_INVALID_ARGUMENT
+    assert L.workspace_size(L.DASH_OP_ROUTE_DECODE,
+                            L.make_shape(4, 4096, 4, None, 4, 2, 64, 64, F32)) == 0
 
 
 def test_sparse_decode_checks(lib):
