@@ -437,6 +437,23 @@ def main():
             g_dash = graph_time(stream, dash_dec, [out_d], 10)
             g_dense = graph_time(stream, dense_dec, [out_d], 10)
             g_topk = graph_time(stream, topk_dec, [out_d, md], 10)
+            # decode-cache upkeep: append each sequence's token at seqlens-1 (its
+            # own row again, so the caches keep their contents) before the step
+            ar = torch.arange(wd.batch, device=dev)
+            last = (seqlens.long() - 1)
+            kn = kc[ar, last].contiguous()
+            vn = vc[ar, last].contiguous()
+            qbar_d = torch.from_numpy(dd["qbar"]).cuda()
+
+            def append():
+                ops.cache_append(kn, vn, seqlens, qbar_d, kc, vc, kbar_c, wd.B)
+
+            def append_dec():
+                append()
+                dash_dec()
+
+            t_app = time_it(stream, append, 10)
+            g_app = graph_time(stream, append_dec, [out_d], 10)
             dense_bytes = float(np.sum(wd.B * n_b + ((dd["seqlens"] - 1) % wd.B) + 1)) \
                 * wd.Hkv * wd.D * 2 * 2
             cmp["decode"] = {
@@ -449,6 +466,7 @@ def main():
                 "speedup_vs_topk": t_kd / t_dec,
                 "graph_us": {"dash": g_dash * 1e3, "dense": g_dense * 1e3,
                              "topk": g_topk * 1e3},
+                "append_us": t_app * 1e3, "graph_us_append_and_step": g_app * 1e3,
                 "graph_speedup_vs_dense": g_dense / g_dash,
                 "graph_speedup_vs_topk": g_topk / g_dash}
         res["compare"] = cmp

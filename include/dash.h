@@ -213,6 +213,28 @@ dash_status dash_attn_decode(const dash_shape* shape, const void* q,
                              float* lse, uint64_t* active_blocks, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* Decode-cache upkeep for incremental decoding: appends one new token per
+ * batch entry to the K/V caches and keeps the summary cache current.  A
+ * chunk's summary is fixed once the chunk is complete, so it is computed once,
+ * by the append that completes it, and cached ("Fase 0", Efficientie bullet;
+ * incremental decoding: "Belangrijkste Bijdragen", the GPU implementation
+ * item, of the same page).  With L = seqlens[b]
+ * (the length after the append, 1 <= L <= capacity), the token's key and
+ * value go to position L-1; when L % B == 0 the summary of chunk L/B - 1 is
+ * computed from the chunk's B keys (as dash_summarize does) and written to
+ * kbar_cache.  Call it before dash_attn_decode with the same seqlens.
+ * shape as in dash_attn_decode.
+ *   k_new, v_new   [batch, Hkv, D] dtype           (input)
+ *   seqlens        device int32 [batch]            (input; entries are not checked)
+ *   qbar           [Hkv, D] fp32                   (input)
+ *   k_cache,v_cache[batch, capacity, Hkv, D] dtype (in/out: row L-1 written)
+ *   kbar_cache     [batch, capacity/B, Hkv, D] dtype (in/out: row L/B-1 written when
+ *                                                   L % B == 0)
+ * No workspace.  Calls on one stream see each other's writes in order. */
+dash_status dash_cache_append(const dash_shape* shape, const void* k_new, const void* v_new,
+                              const int32_t* seqlens, const float* qbar, void* k_cache,
+                              void* v_cache, void* kbar_cache, void* stream);
+
 /* Top-k block routing, the comparison mode of the hierarchical methods the
  * pages set DashAttention against: NSA and InfLLMv2 keep a fixed number of
  * KV blocks ranked by a coarse score and then run ordinary softmax attention

@@ -32,6 +32,7 @@ DASH_OP_ROUTE_DECODE = 6
 
 EXPORTED = ("dash_get_layout", "dash_summarize", "dash_route", "dash_attn_prefill",
             "dash_attn_sparse", "dash_attn_decode", "dash_route_topk", "dash_attn_decode_sparse",
+            "dash_cache_append",
             "dash_workspace_size", "dash_status_string", "dash_abi_version")
 
 
@@ -107,6 +108,8 @@ def lib():
     L.dash_attn_decode_sparse.restype = _I
     L.dash_attn_decode_sparse.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _P, _F, _I, _P, _P, _P,
                                           _SZ, _P]
+    L.dash_cache_append.restype = _I
+    L.dash_cache_append.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _P, _P, _P]
     _lib = L
     return L
 

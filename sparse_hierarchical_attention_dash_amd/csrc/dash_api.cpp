@@ -495,6 +495,24 @@ dash_status dash_route_topk(const dash_shape* shape, const void* q, const void* 
   return DASH_OK;
 }
 
+dash_status dash_cache_append(const dash_shape* shape, const void* k_new, const void* v_new,
+                              const int32_t* seqlens, const float* qbar, void* k_cache,
+                              void* v_cache, void* kbar_cache, void* stream) {
+  Geom g;
+  dash_status st = check_shape(shape, 1, true, g);
+  if (st != DASH_OK) return st;
+  if (g.num_seqs == 0) return DASH_OK;
+  if (!k_new || !v_new || !seqlens || !qbar || !k_cache || !v_cache || !kbar_cache)
+    return DASH_ERR_INVALID_ARGUMENT;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned16(kbar_cache) || !aligned16(qbar))
+    return DASH_ERR_INVALID_ARGUMENT;
+  if (g.max_seqlen == 0) return DASH_ERR_INVALID_ARGUMENT;
+  DASH_HIP(dash::launch_cache_append(g, k_new, v_new, seqlens, qbar, k_cache, v_cache,
+                                     kbar_cache, static_cast<hipStream_t>(stream)));
+  return DASH_OK;
+}
+
 dash_status dash_attn_decode_sparse(const dash_shape* shape, const void* q,
                                     const void* k_cache, const void* v_cache,
                                     const int32_t* seqlens, const uint64_t* active_blocks,

@@ -34,6 +34,12 @@ inline int64_t padded_tokens(int64_t T, int num_seqs) { return T + 64ll * num_se
 hipError_t launch_summarize(const Geom& g, const void* k, const float* qbar,
                             void* kbar, hipStream_t st);
 
+// Decode-cache upkeep: append the new tokens' K/V rows (position seqlens[b]-1
+// of caches [batch, cap, Hkv, D]) and summarise each chunk they complete.
+hipError_t launch_cache_append(const Geom& g, const void* k_new, const void* v_new,
+                               const int32_t* seqlens, const float* qbar, void* k_cache,
+                               void* v_cache, void* kbar_cache, hipStream_t st);
+
 // K1: routing.  Prefill mode routes every packed token row; decode mode
 // (seqlens != null) routes batch entry b at position seqlens[b] - 1 against
 // summary rows b * (max_seqlen / B) ...

@@ -38,61 +38,66 @@ hipError_t launch_varlen_meta(const int32_t* cu_seqlens, int num_seqs, int B,
   return hipGetLastError();
 }
 
-template <bool BF16, int D>
-__global__ __launch_bounds__(64) void summarize_kernel(
-    const void* __restrict__ kp, const float* __restrict__ qbar,
-    void* __restrict__ kbarp, const int32_t* __restrict__ cu_seqlens,
-    const int32_t* __restrict__ cu_chunks, int max_seqlen, int Hkv, int B) {
+// One wave summarises one chunk of B keys: key t's row (this KV head, D
+// elements) starts at row(t).  Lane group kr (LPR lanes, one key row per load
+// instruction) takes keys kr, kr + KPI, ...; each group keeps a running
+// (max, sum, weighted key) in base 2, the groups merge by shuffles, and lanes
+// 0 .. LPR-1 write the result, rounded once, to out.
+template <bool BF16, int D, class RowFn>
+__device__ __forceinline__ void summarize_chunk(RowFn row, const float* __restrict__ qbar_h, int B,
+                                                void* __restrict__ out) {
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int EPL = 16 / ESZ;   // elements per 16-byte load
   constexpr int LPR = D / EPL;    // lanes per key row
   constexpr int KPI = kWave / LPR;  // keys per load instruction
-  const int c = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
-  const SeqInfo si = seq_info(cu_seqlens, cu_chunks, s, max_seqlen, B);
-  if ((c + 1) * B > si.len) return;
-
   const int lane = threadIdx.x;
   const int sub = lane % LPR;
   const int kr = lane / LPR;
   float qv[EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) qv[e] = qbar[h * D + sub * EPL + e];
+  for (int e = 0; e < EPL; ++e) qv[e] = qbar_h[sub * EPL + e];
   const float sc = kLog2e / sqrtf((float)D);
 
   float m = -INFINITY, l = 0.f, acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
 
-  const int64_t row0 = si.start + (int64_t)c * B;
+  // the loads of GRP keys per lane group are issued together, then folded in
+  // key order (iters is a multiple of GRP for every supported B, D, dtype)
+  constexpr int GRP = 8;
   const int iters = B / KPI;
-  for (int it = 0; it < iters; ++it) {
-    const int key = it * KPI + kr;
-    const char* src = (const char*)kp + (((row0 + key) * Hkv + h) * D + sub * EPL) * ESZ;
-    const u32x4 raw = ldg16(src);
-    float x[EPL];
-    if constexpr (BF16) {
+  for (int it0 = 0; it0 < iters; it0 += GRP) {
+    u32x4 raw[GRP];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        x[2 * w] = bf16lo(raw[w]);
-        x[2 * w + 1] = bf16hi(raw[w]);
+    for (int j = 0; j < GRP; ++j)
+      raw[j] = ldg16((const char*)row((it0 + j) * KPI + kr) + sub * EPL * ESZ);
+#pragma unroll
+    for (int j = 0; j < GRP; ++j) {
+      float x[EPL];
+      if constexpr (BF16) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          x[2 * w] = bf16lo(raw[j][w]);
+          x[2 * w + 1] = bf16hi(raw[j][w]);
+        }
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) x[w] = __uint_as_float(raw[j][w]);
       }
-    } else {
+      float d = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) x[w] = __uint_as_float(raw[w]);
+      for (int e = 0; e < EPL; ++e) d = fmaf(x[e], qv[e], d);
+#pragma unroll
+      for (int o = 1; o < LPR; o <<= 1) d += __shfl_xor(d, o);
+      const float z = d * sc;
+      const float mn = fmaxf(m, z);
+      const float a = exp2f(m - mn);
+      const float p = exp2f(z - mn);
+      l = l * a + p;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, x[e], acc[e] * a);
+      m = mn;
     }
-    float d = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) d = fmaf(x[e], qv[e], d);
-#pragma unroll
-    for (int o = 1; o < LPR; o <<= 1) d += __shfl_xor(d, o);
-    const float z = d * sc;
-    const float mn = fmaxf(m, z);
-    const float a = exp2f(m - mn);
-    const float p = exp2f(z - mn);
-    l = l * a + p;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, x[e], acc[e] * a);
-    m = mn;
   }
   // merge the KPI key groups
 #pragma unroll
@@ -111,20 +116,90 @@ __global__ __launch_bounds__(64) void summarize_kernel(
   }
   if (lane < LPR) {
     const float inv = 1.f / l;
-    const int64_t orow = (si.chunk_off + c) * Hkv + h;
     if constexpr (BF16) {
       u32x4 w;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         w[q] = pack_bf16x2(acc[2 * q] * inv, acc[2 * q + 1] * inv);
-      *reinterpret_cast<u32x4*>((char*)kbarp + (orow * D + sub * EPL) * 2) = w;
+      *reinterpret_cast<u32x4*>((char*)out + sub * EPL * 2) = w;
     } else {
       f32x4 w;
 #pragma unroll
       for (int q = 0; q < 4; ++q) w[q] = acc[q] * inv;
-      *reinterpret_cast<f32x4*>((char*)kbarp + (orow * D + sub * EPL) * 4) = w;
+      *reinterpret_cast<f32x4*>((char*)out + sub * EPL * 4) = w;
     }
   }
+}
+
+template <bool BF16, int D>
+__global__ __launch_bounds__(64) void summarize_kernel(
+    const void* __restrict__ kp, const float* __restrict__ qbar,
+    void* __restrict__ kbarp, const int32_t* __restrict__ cu_seqlens,
+    const int32_t* __restrict__ cu_chunks, int max_seqlen, int Hkv, int B) {
+  constexpr int ESZ = BF16 ? 2 : 4;
+  const int c = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
+  const SeqInfo si = seq_info(cu_seqlens, cu_chunks, s, max_seqlen, B);
+  if ((c + 1) * B > si.len) return;
+  const int64_t row0 = si.start + (int64_t)c * B;
+  auto row = [&](int key) -> const void* {
+    return (const char*)kp + ((row0 + key) * Hkv + h) * (int64_t)D * ESZ;
+  };
+  const int64_t orow = (si.chunk_off + c) * Hkv + h;
+  summarize_chunk<BF16, D>(row, qbar + h * D, B, (char*)kbarp + orow * D * ESZ);
+}
+
+// Decode-cache upkeep: one wave per (batch entry b, KV head h).  The new
+// token's key and value rows go to position L - 1 of the caches (L =
+// seqlens[b], the length after the append); when the token completes its
+// chunk (L % B == 0), the chunk's summary is computed and cached, with the
+// new key taken from k_new itself (the rows before it from the cache).
+template <bool BF16, int D>
+__global__ __launch_bounds__(64) void cache_append_kernel(
+    Geom g, const void* __restrict__ knew, const void* __restrict__ vnew,
+    const int32_t* __restrict__ seqlens, const float* __restrict__ qbar,
+    void* __restrict__ kc, void* __restrict__ vc, void* __restrict__ kbar) {
+  constexpr int ESZ = BF16 ? 2 : 4;
+  constexpr int RB = D * ESZ / 16;  // 16-byte pieces per row
+  const int b = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const int L = seqlens[b];
+  const int64_t cap = g.max_seqlen;
+  const int64_t src = ((int64_t)b * g.Hkv + h) * D * ESZ;              // byte offset in k_new
+  const int64_t dst = (((int64_t)b * cap + (L - 1)) * g.Hkv + h) * D * ESZ;
+  if (lane < RB) {
+    const u32x4 w = ldg16((const char*)knew + src + lane * 16);
+    *reinterpret_cast<u32x4*>((char*)kc + dst + lane * 16) = w;
+  } else if (lane < 2 * RB) {
+    const int pc = lane - RB;
+    const u32x4 w = ldg16((const char*)vnew + src + pc * 16);
+    *reinterpret_cast<u32x4*>((char*)vc + dst + pc * 16) = w;
+  }
+  if (L % g.B != 0) return;
+  const int c = L / g.B - 1;
+  const int64_t row0 = (int64_t)b * cap + (int64_t)c * g.B;
+  const int last = g.B - 1;
+  auto row = [&](int key) -> const void* {
+    return key == last ? (const char*)knew + src
+                       : (const char*)kc + ((row0 + key) * g.Hkv + h) * (int64_t)D * ESZ;
+  };
+  const int64_t orow = ((int64_t)b * (cap / g.B) + c) * g.Hkv + h;
+  summarize_chunk<BF16, D>(row, qbar + h * D, g.B, (char*)kbar + orow * D * ESZ);
+}
+
+hipError_t launch_cache_append(const Geom& g, const void* knew, const void* vnew,
+                               const int32_t* seqlens, const float* qbar, void* kc, void* vc,
+                               void* kbar, hipStream_t st) {
+  if (g.num_seqs == 0) return hipSuccess;
+  dim3 grid(g.num_seqs, g.Hkv);
+#define DASH_APP(BF, DD)                                                                    \
+  hipLaunchKernelGGL((cache_append_kernel<BF, DD>), grid, dim3(kWave), 0, st, g, knew, vnew, \
+                     seqlens, qbar, kc, vc, kbar)
+  if (g.bf16) {
+    if (g.D == 64) DASH_APP(true, 64); else DASH_APP(true, 128);
+  } else {
+    if (g.D == 64) DASH_APP(false, 64); else DASH_APP(false, 128);
+  }
+#undef DASH_APP
+  return hipGetLastError();
 }
 
 hipError_t launch_summarize(const Geom& g, const void* k, const float* qbar,

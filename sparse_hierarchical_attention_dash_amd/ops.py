@@ -271,6 +271,21 @@ def decode_workspace(q, k_cache, chunk_size):
     return torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
 
 
+def cache_append(k_new, v_new, seqlens, qbar, k_cache, v_cache, kbar_cache, chunk_size):
+    """Decode-cache upkeep: write each batch entry's new key/value (k_new,
+    v_new [batch, Hkv, D]) at position seqlens[b]-1 of the caches [batch, cap,
+    Hkv, D] and, when that completes a chunk, its summary into kbar_cache
+    [batch, cap/B, Hkv, D].  seqlens (int32 [batch]) are the lengths after the
+    append.  Updates the caches in place."""
+    _need_cuda(k_new, v_new, seqlens, qbar, k_cache, v_cache, kbar_cache)
+    batch, cap, Hkv, D = k_cache.shape
+    shape = L.make_shape(batch, cap, batch, None, Hkv, Hkv, D, chunk_size, _dtype_code(k_cache))
+    qb = qbar if qbar.dtype == torch.float32 else qbar.float().contiguous()
+    L.check("dash_cache_append", L.lib().dash_cache_append(
+        ctypes.byref(shape), _ptr(k_new), _ptr(v_new), _ptr(seqlens), _ptr(qb), _ptr(k_cache),
+        _ptr(v_cache), _ptr(kbar_cache), _stream(k_cache.device)))
+
+
 def decode_sparse_workspace(q, k_cache, chunk_size):
     n = L.workspace_size(L.DASH_OP_DECODE_SPARSE, decode_shape(q, k_cache, chunk_size))
     return torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)

@@ -226,3 +226,23 @@ def test_sparse_decode_checks(lib):
     assert ds(L.make_shape(4, 4000, 4, None, 32, 2, 128, 64, BF16)) == \
         L.DASH_ERR_INVALID_ARGUMENT                                   # capacity % B
     assert ds(L.make_shape(0, 4096, 0, None, 32, 2, 128, 64, BF16)) == L.DASH_OK
+
+
+def test_cache_append_checks(lib):
+    s = L.make_shape(4, 4096, 4, None, 32, 2, 128, 64, BF16)
+
+    def ap(sh, **kw):
+        a = dict(kn=A, vn=A, sl=A, qb=A, kc=A, vc=A, kb=A)
+        a.update(kw)
+        return lib.dash_cache_append(ctypes.byref(sh), a["kn"], a["vn"], a["sl"], a["qb"],
+                                     a["kc"], a["vc"], a["kb"], None)
+
+    for key in ("kn", "vn", "sl", "qb", "kc", "vc", "kb"):
+        assert ap(s, **{key: None}) == L.DASH_ERR_INVALID_ARGUMENT, key
+    assert ap(s, kc=A + 8) == L.DASH_ERR_INVALID_ARGUMENT
+    assert ap(L.make_shape(4, 4000, 4, None, 32, 2, 128, 64, BF16)) == \
+        L.DASH_ERR_INVALID_ARGUMENT                                   # capacity % B
+    assert ap(L.make_shape(4, 4096, 4, A, 32, 2, 128, 64, BF16)) == \
+        L.DASH_ERR_INVALID_ARGUMENT                                   # no cu_seqlens
+    assert ap(L.make_shape(4, 4096, 4, None, 32, 2, 96, 64, BF16)) == L.DASH_ERR_UNSUPPORTED
+    assert ap(L.make_shape(0, 4096, 0, None, 32, 2, 128, 64, BF16)) == L.DASH_OK
