@@ -14,6 +14,7 @@ from .dash_oracle import (  # noqa: F401
     softmax,
     summarize,
     summarize_varlen,
+    summarize_diagonal,
     routing_logits,
     entmax_threshold_bisect,
     sparsemax_sort,

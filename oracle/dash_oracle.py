@@ -124,6 +124,33 @@ def summarize_varlen(k, qbar, cu_seqlens, B, to_bf16=False):
     return np.concatenate(parts, axis=0)
 
 
+def summarize_diagonal(k, qbar, B, to_bf16=False):
+    """Estimated summary of every position's own, partial, chunk.
+
+    The interface carries an ``estimate_diagonal`` flag for a diagonal
+    correction of the alpha-entmax normalisation ([ES] aiexpert.news, the
+    interface paragraph); the pages say no more.  Reading taken here: the
+    chunk that holds position i has no summary yet, so it gets an estimate,
+    the same phase-0 attention of q_bar restricted to the keys of that chunk
+    at or before i (keys cB .. i, c = floor(i / B)).  At i = cB the estimate
+    is k_i itself; at the chunk's last position it is the chunk's summary.
+
+    k [L, Hkv, D], qbar [Hkv, D] -> [L, Hkv, D] (rounded like a summary).
+    """
+    k = np.asarray(k, dtype=F64)
+    qbar = np.asarray(qbar, dtype=F64)
+    L, Hkv, D = k.shape
+    s = 1.0 / math.sqrt(D)
+    out = np.zeros((L, Hkv, D), dtype=F64)
+    for i in range(L):
+        c0 = (i // B) * B
+        for h in range(Hkv):
+            keys = k[c0:i + 1, h, :]
+            weights = softmax(s * (keys @ qbar[h]))
+            out[i, h] = weights @ keys
+    return round_to_bf16(out) if to_bf16 else out
+
+
 # ---------------------------------------------------------------------------
 # Phase 1: alpha-entmax routing  ([NL] / [ZH] Fase 1 / 阶段 1)
 # ---------------------------------------------------------------------------
@@ -296,12 +323,17 @@ def entmax_rows(U, n, alpha):
     return P, tau_hat
 
 
-def route_position(q_group, kbar_h, alpha, gamma, scale):
+def route_position(q_group, kbar_h, alpha, gamma, scale, kdiag_h=None):
     """Route one position for one KV group.
 
     q_group : [G, D] the query heads of one KV head at this position
     kbar_h  : [n, D] that KV head's summaries of the routable chunks
-    Returns dict(u [G, n], tau_hat [G], p [G, n], wbar [n], mask [n] bool).
+    kdiag_h : [D] or None: the estimated summary of the position's own chunk
+              (``summarize_diagonal``); when given and n > 0 it enters each
+              head's entmax as one more entry, after the routed chunks, and
+              takes its share of the probability mass
+    Returns dict(u [G, n], tau_hat [G], p [G, n], wbar [n], mask [n] bool,
+    p_diag [G] or None).
 
     Each query head gets its own entmax distribution; the group shares the
     average of the G distributions, and a chunk is active when any head
@@ -313,21 +345,32 @@ def route_position(q_group, kbar_h, alpha, gamma, scale):
     u = np.zeros((G, n), dtype=F64)
     for g in range(G):
         u[g] = routing_logits(q_group[g], kbar_h, gamma, scale)
-    p, tau_hat = entmax_rows(u, np.full(G, n), alpha)
+    p_diag = None
+    if kdiag_h is not None and n > 0:
+        ud = np.array([routing_logits(q_group[g], np.asarray(kdiag_h, dtype=F64)[None, :],
+                                      gamma, scale)[0] for g in range(G)])
+        pf, tau_hat = entmax_rows(np.concatenate([u, ud[:, None]], axis=1),
+                                  np.full(G, n + 1), alpha)
+        p, p_diag = pf[:, :n], pf[:, n]
+    else:
+        p, tau_hat = entmax_rows(u, np.full(G, n), alpha)
     wbar = p.mean(axis=0) if n else np.zeros(0, dtype=F64)
     if alpha == 1.0:
         mask = np.ones(n, dtype=bool)
     else:
         mask = np.any(u > tau_hat[:, None], axis=0) if n else np.zeros(0, bool)
-    return dict(u=u, tau_hat=tau_hat, p=p, wbar=wbar, mask=mask)
+    return dict(u=u, tau_hat=tau_hat, p=p, wbar=wbar, mask=mask, p_diag=p_diag)
 
 
 def route_sequence(q, kbar, B, alpha, gamma, sigma, G, scale, rows=None,
-                   num_slots=None):
+                   num_slots=None, kdiag=None):
     """Phase 1 for one sequence.
 
     q    : [L, Hq, D];  kbar : [C, Hkv, D] summaries of the complete chunks
     rows : positions to route (default: all)
+    kdiag: [L, Hkv, D] or None: estimated summaries of each position's own
+           chunk (``summarize_diagonal``), an extra entmax entry of every
+           row that has routable chunks (see ``route_position``)
     Returns mask [Hkv, L, S] bool, log_prior [Hkv, L, S] (-inf off the
     support) and tau_hat [Hq, L] (NaN for rows not routed), S = num_slots
     (default ceil(L / B)).  Position i routes to chunks c < floor(i / B).
@@ -347,15 +390,22 @@ def route_sequence(q, kbar, B, alpha, gamma, sigma, G, scale, rows=None,
     ns = rows // B                    # routable chunks of each row
     for h in range(Hkv):
         # u[row, g, c] = gamma * s * <q[row, hG+g], kbar[c, h]>, c < n_row
-        u = np.zeros((rows.size, G, max(C, 1)), dtype=F64)
+        u = np.zeros((rows.size, G, max(C, 1) + 1), dtype=F64)
         if C:
             u[:, :, :C] = gamma * scale * np.einsum(
                 "rgd,cd->rgc", q[rows, h * G:(h + 1) * G, :], kbar[:C, h, :])
-        P, th = entmax_rows(u.reshape(rows.size * G, -1), np.repeat(ns, G), alpha)
+        lens = ns.copy()
+        if kdiag is not None:
+            # the diagonal estimate goes right after each row's routed chunks
+            ud = gamma * scale * np.einsum("rgd,rd->rg", q[rows, h * G:(h + 1) * G, :],
+                                           np.asarray(kdiag, dtype=F64)[rows, h, :])
+            u[np.arange(rows.size), :, ns] = ud
+            lens = ns + (ns > 0)
+        P, th = entmax_rows(u.reshape(rows.size * G, -1), np.repeat(lens, G), alpha)
         P = P.reshape(rows.size, G, -1)
         th = th.reshape(rows.size, G)
         tau_hat[h * G:(h + 1) * G, rows] = th.T
-        wbar = P.mean(axis=1)                                  # [rows, C]
+        wbar = P.mean(axis=1)                                  # [rows, C + 1]
         if alpha == 1.0:
             on = np.arange(u.shape[2])[None, :] < ns[:, None]
         else:
@@ -530,14 +580,17 @@ def _group_size(Hq, Hkv, enable_gqa):
 
 
 def prefill(q, k, v, qbar, B, alpha, gamma, sigma, enable_gqa=True,
-            to_bf16=False, scale=None, rows=None, dense=False, num_slots=None):
+            to_bf16=False, scale=None, rows=None, dense=False, num_slots=None,
+            estimate_diagonal=False):
     """Phases 0-2 for one sequence (causal prefill).
 
     q [L, Hq, D], k/v [L, Hkv, D], qbar [Hkv, D].  ``to_bf16`` rounds the
     summaries to bfloat16 (inputs stored in bfloat16).  ``rows`` limits
     routing and attention to the given positions (row-sparse form);
     ``dense=True`` uses the dense score-matrix form for every row instead.
-    Returns dict(kbar, mask, log_prior, tau_hat, out, lse, rows).
+    ``estimate_diagonal`` adds each row's estimated own-chunk summary to its
+    routing (``route_position``).
+    Returns dict(kbar, kdiag, mask, log_prior, tau_hat, out, lse, rows).
     """
     q = np.asarray(q, dtype=F64)
     L, Hq, D = q.shape
@@ -545,21 +598,22 @@ def prefill(q, k, v, qbar, B, alpha, gamma, sigma, enable_gqa=True,
     G = _group_size(Hq, Hkv, enable_gqa)
     s = _default_scale(D, scale)
     kbar = summarize(k, qbar, B, to_bf16)
+    kdiag = summarize_diagonal(k, qbar, B, to_bf16) if estimate_diagonal else None
     rows = list(range(L)) if rows is None else list(rows)
     mask, logp, tau_hat = route_sequence(q, kbar, B, alpha, gamma, sigma, G, s,
-                                         rows=rows, num_slots=num_slots)
+                                         rows=rows, num_slots=num_slots, kdiag=kdiag)
     if dense:
         out, lse = attention_dense(q, k, v, mask, logp, B, s, G)
         out, lse = out[rows], lse[:, rows]
     else:
         out, lse = attention_rows(q, k, v, mask, logp, B, s, G, rows)
-    return dict(kbar=kbar, mask=mask, log_prior=logp, tau_hat=tau_hat,
+    return dict(kbar=kbar, kdiag=kdiag, mask=mask, log_prior=logp, tau_hat=tau_hat,
                 out=out, lse=lse, rows=rows)
 
 
 def prefill_varlen(q, k, v, qbar, cu_seqlens, B, alphas, gamma, sigma,
                    enable_gqa=True, to_bf16=False, scale=None,
-                   rows_per_seq=None, num_slots=None):
+                   rows_per_seq=None, num_slots=None, estimate_diagonal=False):
     """Packed variable-length prefill: every sequence is independent.
 
     alphas[s] is sequence s's entmax alpha.  ``rows_per_seq[s]`` lists
@@ -572,19 +626,22 @@ def prefill_varlen(q, k, v, qbar, cu_seqlens, B, alphas, gamma, sigma,
         rows = None if rows_per_seq is None else rows_per_seq[s]
         res.append(prefill(q[a:b], k[a:b], v[a:b], qbar, B, float(alphas[s]),
                            gamma, sigma, enable_gqa, to_bf16, scale, rows,
-                           num_slots=num_slots))
+                           num_slots=num_slots, estimate_diagonal=estimate_diagonal))
     return res
 
 
 def decode(q_new, k_cache, v_cache, kbar_cache, L, B, alpha, gamma, sigma,
-           enable_gqa=True, scale=None):
+           enable_gqa=True, scale=None, kdiag=None):
     """One decode step: the row i = L - 1 of a sequence of length L.
 
     q_new [Hq, D]; k_cache / v_cache [>= L, Hkv, D] hold the L tokens
     (the new token's key and value at position L - 1); kbar_cache
     [>= floor((L-1)/B), Hkv, D] holds the cached summaries of the complete
-    chunks.  Returns dict(out [Hq, D], lse [Hq], mask [Hkv, n],
-    log_prior [Hkv, n], tau_hat [Hq]) with n = floor((L-1)/B).
+    chunks.  ``kdiag`` [Hkv, D], when given, is the estimated summary of the
+    row's own chunk (``summarize_diagonal`` of the cached keys at its last
+    position), which then enters the routing (``route_position``).
+    Returns dict(out [Hq, D], lse [Hq], mask [Hkv, n], log_prior [Hkv, n],
+    tau_hat [Hq]) with n = floor((L-1)/B).
     """
     q_new = np.asarray(q_new, dtype=F64)
     Hq, D = q_new.shape
@@ -598,7 +655,8 @@ def decode(q_new, k_cache, v_cache, kbar_cache, L, B, alpha, gamma, sigma,
     logp = np.full((Hkv, n), -np.inf, dtype=F64)
     tau_hat = np.zeros(Hq, dtype=F64)
     for h in range(Hkv):
-        r = route_position(q_new[h * G:(h + 1) * G], kb[:, h, :], alpha, gamma, s)
+        r = route_position(q_new[h * G:(h + 1) * G], kb[:, h, :], alpha, gamma, s,
+                           None if kdiag is None else kdiag[h])
         mask[h] = r["mask"]
         tau_hat[h * G:(h + 1) * G] = r["tau_hat"]
         with np.errstate(divide="ignore"):

@@ -305,6 +305,94 @@ def test_routable_range_and_head_mapping():
     assert not mask[0, L - 1, :(L - 1) // B].all() or (L - 1) // B == 1
 
 
+# ------------------------------------------------- estimated diagonal summary
+
+def test_diagonal_estimate_closed_forms():
+    rng = np.random.default_rng(24)
+    B, L, Hkv, D = 8, 29, 2, 6
+    k = rng.standard_normal((L, Hkv, D))
+    qb = rng.standard_normal((Hkv, D))
+    kd = O.summarize_diagonal(k, qb, B)
+    for c in range(-(-L // B)):
+        # the first key of a chunk is its own estimate
+        np.testing.assert_allclose(kd[c * B], k[c * B], atol=1e-15)
+    # at a chunk's last position the estimate is the chunk summary
+    full = O.summarize(k, qb, B)
+    for c in range(L // B):
+        np.testing.assert_allclose(kd[c * B + B - 1], full[c], atol=1e-13)
+    # q_bar = 0: the running mean of the chunk's keys so far
+    kz = O.summarize_diagonal(k, np.zeros((Hkv, D)), B)
+    for i in range(L):
+        c0 = (i // B) * B
+        np.testing.assert_allclose(kz[i], k[c0:i + 1].sum(axis=0) / (i + 1 - c0), atol=1e-13)
+    # a sharp q_bar picks the prefix key of largest <q_bar, k>
+    ks = O.summarize_diagonal(k, 1e4 * qb, B)
+    for i in (3, 12, 28):
+        c0 = (i // B) * B
+        for h in range(Hkv):
+            j = c0 + int(np.argmax(k[c0:i + 1, h] @ qb[h]))
+            np.testing.assert_allclose(ks[i, h], k[j, h], atol=1e-9)
+
+
+def test_diagonal_entry_shares_the_entmax_mass():
+    # sparsemax, one head, routed logits (0, 0) and a diagonal logit 0:
+    # p = (1/3, 1/3, 1/3); without the diagonal entry p = (1/2, 1/2)
+    D = 4
+    q = np.zeros((1, D))
+    q[0, 0] = 1.0
+    kb = np.zeros((2, D))
+    r = O.route_position(q, kb, 2.0, gamma=1.0, scale=1.0, kdiag_h=np.zeros(D))
+    np.testing.assert_allclose(r["wbar"], [1 / 3, 1 / 3], atol=1e-12)
+    np.testing.assert_allclose(r["p_diag"], [1 / 3], atol=1e-12)
+    r0 = O.route_position(q, kb, 2.0, gamma=1.0, scale=1.0)
+    np.testing.assert_allclose(r0["wbar"], [0.5, 0.5], atol=1e-12)
+    # a diagonal logit 1 above the others takes all of the sparsemax mass
+    kd = np.zeros(D)
+    kd[0] = 1.0
+    r1 = O.route_position(q, kb, 2.0, gamma=1.0, scale=1.0, kdiag_h=kd)
+    assert not r1["mask"].any()
+    np.testing.assert_allclose(r1["p_diag"], [1.0], atol=1e-12)
+
+
+def test_diagonal_entry_below_the_support_changes_nothing():
+    # a diagonal estimate with a far negative logit stays outside every
+    # head's support: mask, prior and threshold equal plain routing
+    rng = np.random.default_rng(25)
+    B, L, D, G = 4, 40, 8, 2
+    q = rng.standard_normal((L, 2 * G, D))
+    kbar = rng.standard_normal((L // B, 2, D))
+    kd = np.zeros((L, 2, D))
+    for i in range(L):
+        for h in range(2):
+            kd[i, h] = -50.0 * q[i, h * G:(h + 1) * G].sum(axis=0)
+    for alpha in (1.5, 2.0, 1.25):
+        m0, l0, t0 = O.route_sequence(q, kbar, B, alpha, 3.0, 1.0, G, 0.5)
+        m1, l1, t1 = O.route_sequence(q, kbar, B, alpha, 3.0, 1.0, G, 0.5, kdiag=kd)
+        assert np.array_equal(m0, m1)
+        np.testing.assert_allclose(l1[m1], l0[m0], atol=1e-9)
+        np.testing.assert_allclose(t1, t0, atol=1e-9)
+
+
+def test_diagonal_entry_sequence_matches_single_positions():
+    rng = np.random.default_rng(26)
+    B, L, D, G = 4, 36, 8, 2
+    q = rng.standard_normal((L, 2 * G, D))
+    kbar = rng.standard_normal((L // B, 2, D))
+    kd = rng.standard_normal((L, 2, D))
+    mask, logp, tau = O.route_sequence(q, kbar, B, 1.5, 4.0, 0.7, G, 0.5, kdiag=kd)
+    for i in (4, 9, 17, 35):
+        n = i // B
+        for h in range(2):
+            r = O.route_position(q[i, h * G:(h + 1) * G], kbar[:n, h], 1.5, 4.0, 0.5,
+                                 kdiag_h=kd[i, h])
+            assert np.array_equal(mask[h, i, :n], r["mask"])
+            np.testing.assert_allclose(logp[h, i, :n][r["mask"]],
+                                       0.7 * np.log(r["wbar"][r["mask"]]), atol=1e-10)
+            np.testing.assert_allclose(tau[h * G:(h + 1) * G, i], r["tau_hat"], atol=1e-10)
+            # the routed chunks and the diagonal share each head's unit mass
+            np.testing.assert_allclose(r["p"].sum(axis=1) + r["p_diag"], 1.0, atol=1e-12)
+
+
 # ------------------------------------------------- top-k comparison routing
 
 def _topk_by_hand():
