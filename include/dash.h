@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define DASH_ABI_VERSION 1
+#define DASH_ABI_VERSION 2
 
 typedef enum {
   DASH_OK = 0,
@@ -126,6 +126,21 @@ dash_status dash_summarize(const dash_shape* shape, const void* k, const float* 
                            void* kbar, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* Estimated summary of each position's own, partial chunk, for the
+ * estimate_diagonal option.  The interface carries estimate_diagonal as a
+ * diagonal correction of the alpha-entmax normalisation (aiexpert.news
+ * article, the interface paragraph); the pages define it no further.  The
+ * reading taken: position i's chunk c = floor(i/B) has no summary yet, so it
+ * gets phase 0's attention over the keys it has so far,
+ *     k_diag[t,h] = sum_{j=cB..i} softmax_j(<q_bar[h], k[j,h]> / sqrt(D)) k[j,h],
+ * which equals k[t,h] at i = cB and the chunk's summary at i = cB + B - 1.
+ * Passed to dash_route it enters every head's entmax as one more entry.
+ *   k      [T, Hkv, D] dtype                 (input)
+ *   qbar   [Hkv, D] fp32                     (input)
+ *   kdiag  [T, Hkv, D] dtype                 (output) */
+dash_status dash_summarize_diagonal(const dash_shape* shape, const void* k, const float* qbar,
+                                    void* kdiag, void* stream);
+
 /* Phase 1 ("Fase 1: Entmax Chunk Routering").  For token t at local position
  * i and query head q (KV head h):
  *     u_c     = gamma * s * <q[t,q], k_bar[c,h]>            c < floor(i/B)
@@ -134,9 +149,13 @@ dash_status dash_summarize(const dash_shape* shape, const void* k, const float* 
  *     w_bar_c = mean over the G query heads of KV head h of p_c
  *     bit_c   = OR over those heads of [u_c > tau_hat],  tau_hat = tau/(alpha-1)
  *     log_prior_c = sigma * log(w_bar_c) where bit_c = 1
- * s = softmax_scale, or 1/sqrt(D) when softmax_scale <= 0.
+ * s = softmax_scale, or 1/sqrt(D) when softmax_scale <= 0.  With kdiag, a row
+ * with routable chunks also has the entry u_d = gamma * s * <q[t,q],
+ * kdiag[t,h]> in each head's entmax (after the routed chunks); it takes its
+ * share of the unit mass and enters tau, but never a mask bit or a prior.
  *   q              [T, Hq, D] dtype                (input)
  *   kbar           [summary_rows, Hkv, D] dtype    (input)
+ *   kdiag          [T, Hkv, D] dtype or NULL       (input, dash_summarize_diagonal)
  *   alpha          used when alpha_per_seq is NULL; 1 <= alpha <= 2
  *   alpha_per_seq  device fp32 [num_seqs] or NULL
  *   active_blocks  [Hkv, T, W] uint64              (output, required)
@@ -147,8 +166,8 @@ dash_status dash_summarize(const dash_shape* shape, const void* k, const float* 
  *                                                   +inf when no chunk is
  *                                                   routable, -inf for alpha=1) */
 dash_status dash_route(const dash_shape* shape, const void* q, const void* kbar,
-                       float alpha, const float* alpha_per_seq, float gamma,
-                       float sigma, float softmax_scale, int enable_gqa,
+                       const void* kdiag, float alpha, const float* alpha_per_seq,
+                       float gamma, float sigma, float softmax_scale, int enable_gqa,
                        uint64_t* active_blocks, float* log_prior, float* tau,
                        void* workspace, size_t workspace_bytes, void* stream);
 
@@ -160,6 +179,7 @@ dash_status dash_route(const dash_shape* shape, const void* q, const void* kbar,
  * and the causal diagonal chunk floor(i/B)*B <= j <= i (b_j = 0).
  *   q, k, v        [T, Hq|Hkv, D] dtype            (input)
  *   qbar           [Hkv, D] fp32                   (input)
+ *   estimate_diagonal  nonzero: route with dash_summarize_diagonal's estimates
  *   out            [T, Hq, D] dtype                (output)
  *   lse            [Hq, T] fp32 or NULL            (output, natural log of the
  *                                                   softmax denominator)
@@ -167,8 +187,8 @@ dash_status dash_route(const dash_shape* shape, const void* q, const void* kbar,
 dash_status dash_attn_prefill(const dash_shape* shape, const void* q, const void* k,
                               const void* v, const float* qbar, float alpha,
                               const float* alpha_per_seq, float gamma, float sigma,
-                              float softmax_scale, int enable_gqa, void* out,
-                              float* lse, uint64_t* active_blocks, void* workspace,
+                              float softmax_scale, int enable_gqa, int estimate_diagonal,
+                              void* out, float* lse, uint64_t* active_blocks, void* workspace,
                               size_t workspace_bytes, void* stream);
 
 /* Phase 2 alone ("Fase 2: Prior-Geinduceerde Spaarzame Softmax", the
@@ -202,15 +222,19 @@ dash_status dash_attn_sparse(const dash_shape* shape, const void* q, const void*
  *   seqlens        device int32 [batch], 1 <= seqlens[b] <= capacity
  *   kbar_cache     [batch, capacity/B, Hkv, D] dtype (input; rows c <
  *                                                   floor((seqlens[b]-1)/B) read)
+ *   qbar           [Hkv, D] fp32 (input; read only with estimate_diagonal)
+ *   estimate_diagonal  nonzero: the new row's own-chunk estimate (keys
+ *                  floor((L-1)/B)*B .. L-1 of its cache, as
+ *                  dash_summarize_diagonal) joins its routing
  *   out            [batch, Hq, D] dtype            (output)
  *   lse            [Hq, batch] fp32 or NULL        (output)
  *   active_blocks  [Hkv, batch, W] uint64 or NULL  (output) */
 dash_status dash_attn_decode(const dash_shape* shape, const void* q,
                              const void* k_cache, const void* v_cache,
                              const int32_t* seqlens, const void* kbar_cache,
-                             float alpha, float gamma, float sigma,
-                             float softmax_scale, int enable_gqa, void* out,
-                             float* lse, uint64_t* active_blocks, void* workspace,
+                             const float* qbar, float alpha, float gamma, float sigma,
+                             float softmax_scale, int enable_gqa, int estimate_diagonal,
+                             void* out, float* lse, uint64_t* active_blocks, void* workspace,
                              size_t workspace_bytes, void* stream);
 
 /* Decode-cache upkeep for incremental decoding: appends one new token per

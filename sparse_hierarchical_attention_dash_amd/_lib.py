@@ -32,7 +32,7 @@ DASH_OP_ROUTE_DECODE = 6
 
 EXPORTED = ("dash_get_layout", "dash_summarize", "dash_route", "dash_attn_prefill",
             "dash_attn_sparse", "dash_attn_decode", "dash_route_topk", "dash_attn_decode_sparse",
-            "dash_cache_append",
+            "dash_cache_append", "dash_summarize_diagonal",
             "dash_workspace_size", "dash_status_string", "dash_abi_version")
 
 
@@ -94,15 +94,18 @@ def lib():
     L.dash_summarize.restype = _I
     L.dash_summarize.argtypes = [_SHAPE, _P, _P, _P, _P, _SZ, _P]
     L.dash_route.restype = _I
-    L.dash_route.argtypes = [_SHAPE, _P, _P, _F, _P, _F, _F, _F, _I, _P, _P, _P, _P, _SZ, _P]
+    L.dash_summarize_diagonal.restype = _I
+    L.dash_summarize_diagonal.argtypes = [_SHAPE, _P, _P, _P, _P]
+    L.dash_route.argtypes = [_SHAPE, _P, _P, _P, _F, _P, _F, _F, _F, _I, _P, _P, _P, _P, _SZ,
+                             _P]
     L.dash_attn_prefill.restype = _I
-    L.dash_attn_prefill.argtypes = [_SHAPE, _P, _P, _P, _P, _F, _P, _F, _F, _F, _I, _P, _P,
-                                    _P, _P, _SZ, _P]
+    L.dash_attn_prefill.argtypes = [_SHAPE, _P, _P, _P, _P, _F, _P, _F, _F, _F, _I, _I, _P,
+                                    _P, _P, _P, _SZ, _P]
     L.dash_attn_sparse.restype = _I
     L.dash_attn_sparse.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _F, _I, _P, _P, _P, _SZ, _P]
     L.dash_attn_decode.restype = _I
-    L.dash_attn_decode.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _F, _F, _F, _F, _I, _P, _P, _P,
-                                   _P, _SZ, _P]
+    L.dash_attn_decode.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _P, _F, _F, _F, _F, _I, _I, _P,
+                                   _P, _P, _P, _SZ, _P]
     L.dash_route_topk.restype = _I
     L.dash_route_topk.argtypes = [_SHAPE, _P, _P, _I, _F, _F, _I, _P, _P, _P, _P, _SZ, _P]
     L.dash_attn_decode_sparse.restype = _I

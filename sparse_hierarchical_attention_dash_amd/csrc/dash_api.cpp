@@ -102,7 +102,7 @@ size_t vt_bytes(const Geom& g) {
 }
 
 struct PrefillWs {
-  size_t meta, kbar, mask, logp, vt, total;
+  size_t meta, kbar, mask, logp, vt, kdiag, total;
 };
 PrefillWs prefill_ws(const Geom& g) {
   PrefillWs w{};
@@ -117,6 +117,8 @@ PrefillWs prefill_ws(const Geom& g) {
   o += align_up((size_t)g.Hkv * g.T * g.C_slots * 4);
   w.vt = o;
   o += vt_bytes(g);
+  w.kdiag = o;  // estimated own-chunk summaries (estimate_diagonal)
+  o += align_up((size_t)g.T * g.Hkv * g.D * elt(g));
   w.total = o;
   return w;
 }
@@ -131,7 +133,7 @@ SparseWs sparse_ws(const Geom& g) {
   return w;
 }
 struct DecodeWs {
-  size_t mask, logp, acc, ml, ulog, tsx, total;
+  size_t mask, logp, acc, ml, ulog, tsx, kdiag, total;
   int nsplit;
 };
 DecodeWs decode_ws(const Geom& g) {
@@ -150,6 +152,8 @@ DecodeWs decode_ws(const Geom& g) {
   if (g.bf16) o += align_up((size_t)g.num_seqs * g.Hkv * g.G * g.C_slots * 4);
   w.tsx = o;   // their per-head thresholds
   if (g.bf16) o += align_up((size_t)g.num_seqs * g.Hkv * g.G * 2 * 4);
+  w.kdiag = o;  // the new rows' own-chunk estimates (estimate_diagonal)
+  o += align_up((size_t)g.num_seqs * g.Hkv * g.D * elt(g));
   w.total = o;
   return w;
 }
@@ -268,10 +272,21 @@ dash_status dash_summarize(const dash_shape* shape, const void* k, const float* 
   return DASH_OK;
 }
 
-dash_status dash_route(const dash_shape* shape, const void* q, const void* kbar, float alpha,
-                       const float* alpha_per_seq, float gamma, float sigma,
-                       float softmax_scale, int enable_gqa, uint64_t* active_blocks,
-                       float* log_prior, float* tau, void* workspace,
+dash_status dash_summarize_diagonal(const dash_shape* shape, const void* k, const float* qbar,
+                                    void* kdiag, void* stream) {
+  Geom g;
+  dash_status st = check_shape(shape, 1, false, g);
+  if (st != DASH_OK) return st;
+  if (g.T == 0 || g.num_seqs == 0) return DASH_OK;
+  if (!k || !qbar || !kdiag) return DASH_ERR_INVALID_ARGUMENT;
+  if (!aligned16(k) || !aligned16(qbar) || !aligned16(kdiag)) return DASH_ERR_INVALID_ARGUMENT;
+  DASH_HIP(dash::launch_diag_summary(g, k, qbar, kdiag, static_cast<hipStream_t>(stream)));
+  return DASH_OK;
+}
+dash_status dash_route(const dash_shape* shape, const void* q, const void* kbar,
+                       const void* kdiag, float alpha, const float* alpha_per_seq, float gamma,
+                       float sigma, float softmax_scale, int enable_gqa,
+                       uint64_t* active_blocks, float* log_prior, float* tau, void* workspace,
                        size_t workspace_bytes, void* stream) {
   Geom g;
   dash_status st = check_shape(shape, enable_gqa, false, g);
@@ -281,7 +296,7 @@ dash_status dash_route(const dash_shape* shape, const void* q, const void* kbar,
   if ((st = check_ws(workspace, workspace_bytes, need)) != DASH_OK) return st;
   if (g.T == 0 || g.num_seqs == 0) return DASH_OK;
   if (!q || !active_blocks || (!kbar && g.T / g.B > 0)) return DASH_ERR_INVALID_ARGUMENT;
-  if (!aligned16(q) || !aligned16(kbar)) return DASH_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(kbar) || !aligned16(kdiag)) return DASH_ERR_INVALID_ARGUMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (g.cu_seqlens) {
     g.cu_chunks = meta_chunks(workspace);
@@ -291,6 +306,7 @@ dash_status dash_route(const dash_shape* shape, const void* q, const void* kbar,
   dash::RouteParams p;
   p.q = q;
   p.kbar = kbar;
+  p.kdiag = kdiag;
   p.alpha = alpha;
   p.alpha_per_seq = alpha_per_seq;
   p.gamma_scale = gamma * eff_scale(g, softmax_scale);
@@ -306,8 +322,8 @@ dash_status dash_route(const dash_shape* shape, const void* q, const void* kbar,
 dash_status dash_attn_prefill(const dash_shape* shape, const void* q, const void* k,
                               const void* v, const float* qbar, float alpha,
                               const float* alpha_per_seq, float gamma, float sigma,
-                              float softmax_scale, int enable_gqa, void* out, float* lse,
-                              uint64_t* active_blocks, void* workspace,
+                              float softmax_scale, int enable_gqa, int estimate_diagonal,
+                              void* out, float* lse, uint64_t* active_blocks, void* workspace,
                               size_t workspace_bytes, void* stream) {
   Geom g;
   dash_status st = check_shape(shape, enable_gqa, false, g);
@@ -332,6 +348,11 @@ dash_status dash_attn_prefill(const dash_shape* shape, const void* q, const void
   float* logp = reinterpret_cast<float*>(at(workspace, w.logp));
   DASH_HIP(dash::launch_summarize(g, k, qbar, kbar, s));
   dash::RouteParams rp;
+  if (estimate_diagonal) {
+    void* kdiag = at(workspace, w.kdiag);
+    DASH_HIP(dash::launch_diag_summary(g, k, qbar, kdiag, s));
+    rp.kdiag = kdiag;
+  }
   rp.q = q;
   rp.kbar = kbar;
   rp.alpha = alpha;
@@ -398,8 +419,9 @@ dash_status dash_attn_sparse(const dash_shape* shape, const void* q, const void*
 
 dash_status dash_attn_decode(const dash_shape* shape, const void* q, const void* k_cache,
                              const void* v_cache, const int32_t* seqlens,
-                             const void* kbar_cache, float alpha, float gamma, float sigma,
-                             float softmax_scale, int enable_gqa, void* out, float* lse,
+                             const void* kbar_cache, const float* qbar, float alpha,
+                             float gamma, float sigma, float softmax_scale, int enable_gqa,
+                             int estimate_diagonal, void* out, float* lse,
                              uint64_t* active_blocks, void* workspace,
                              size_t workspace_bytes, void* stream) {
   Geom g;
@@ -411,14 +433,20 @@ dash_status dash_attn_decode(const dash_shape* shape, const void* q, const void*
   if (g.num_seqs == 0) return DASH_OK;
   if (!q || !k_cache || !v_cache || !seqlens || !kbar_cache || !out)
     return DASH_ERR_INVALID_ARGUMENT;
+  if (estimate_diagonal && !qbar) return DASH_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(kbar_cache) ||
-      !aligned16(out))
+      !aligned16(out) || !aligned16(qbar))
     return DASH_ERR_INVALID_ARGUMENT;
   if (g.max_seqlen == 0) return DASH_ERR_INVALID_ARGUMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint64_t* mask = active_blocks ? active_blocks : reinterpret_cast<uint64_t*>(at(workspace, w.mask));
   float* logp = reinterpret_cast<float*>(at(workspace, w.logp));
   dash::RouteParams rp;
+  if (estimate_diagonal) {
+    void* kdiag = at(workspace, w.kdiag);
+    DASH_HIP(dash::launch_decode_diag(g, k_cache, seqlens, qbar, kdiag, s));
+    rp.kdiag = kdiag;
+  }
   rp.q = q;
   rp.kbar = kbar_cache;
   rp.alpha = alpha;

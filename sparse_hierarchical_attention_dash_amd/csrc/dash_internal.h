@@ -34,6 +34,15 @@ inline int64_t padded_tokens(int64_t T, int num_seqs) { return T + 64ll * num_se
 hipError_t launch_summarize(const Geom& g, const void* k, const float* qbar,
                             void* kbar, hipStream_t st);
 
+// Estimated summary of each position's own partial chunk (the learned-query
+// attention over its chunk's keys up to the position): prefill, every token
+// row, kdiag [T, Hkv, D]; decode, the new row of each batch entry from its
+// cache, kdiag [batch, Hkv, D].
+hipError_t launch_diag_summary(const Geom& g, const void* k, const float* qbar, void* kdiag,
+                               hipStream_t st);
+hipError_t launch_decode_diag(const Geom& g, const void* k_cache, const int32_t* seqlens,
+                              const float* qbar, void* kdiag, hipStream_t st);
+
 // Decode-cache upkeep: append the new tokens' K/V rows (position seqlens[b]-1
 // of caches [batch, cap, Hkv, D]) and summarise each chunk they complete.
 hipError_t launch_cache_append(const Geom& g, const void* k_new, const void* v_new,
@@ -59,6 +68,8 @@ struct RouteParams {
   float* tsx = nullptr;                 // decode, bf16: per-head threshold scratch [rows, Hkv, G, 2]
   int topk = 0;                         // > 0: top-k routing (group softmax scores, bias 0)
   float* score = nullptr;               // decode, bf16, top-k: group scores scratch [rows, Hkv, C_slots]
+  const void* kdiag = nullptr;          // [rows, Hkv, D] estimated own-chunk summaries, or null:
+                                        // one more entmax entry per row (after the routed chunks)
 };
 hipError_t launch_route(const Geom& g, const RouteParams& p, hipStream_t st);
 

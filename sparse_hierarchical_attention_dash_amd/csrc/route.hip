@@ -412,6 +412,10 @@ __global__ __launch_bounds__(NTH) void route_kernel(Geom g, RouteParams p) {
         p.tau[(int64_t)(h * g.G + q) * rows + tok] = INFINITY;
     return;
   }
+  // entries of each head's entmax: the routed chunks, then the estimated
+  // summary of the row's own chunk when given (column n of U)
+  const int ns = p.kdiag ? n + 1 : n;
+  const uint16_t* kdrow = (const uint16_t*)p.kdiag + ((tok * g.Hkv + h) * (int64_t)D) * (BF16 ? 1 : 2);
   // top-k routing scores chunks by the group's summed softmax probabilities
   const bool topk = p.topk > 0;
   if (topk) alpha = 1.f;
@@ -443,15 +447,15 @@ __global__ __launch_bounds__(NTH) void route_kernel(Geom g, RouteParams p) {
         if (r < nh) v = ldg16(qrow + 32 * ks + 8 * gq);
         qa[ks] = as_bf16x8(v);
       }
-      const int nct = (n + 15) >> 4;
+      const int nct = (ns + 15) >> 4;
       for (int ct0 = 4 * wv; ct0 < nct; ct0 += 4 * NW) {
         u32x4 kv[4][KS];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          // clamped to a valid summary row; columns past n are discarded below
-          const int c = min((ct0 + j) * 16 + r, n - 1);
+          // clamped to a valid entry; columns past ns are discarded below
+          const int c = min((ct0 + j) * 16 + r, ns - 1);
           const uint16_t* krow =
-              (const uint16_t*)p.kbar + (((kb0 + c) * g.Hkv + h) * (int64_t)D);
+              c == n ? kdrow : (const uint16_t*)p.kbar + (((kb0 + c) * g.Hkv + h) * (int64_t)D);
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) kv[j][ks] = ldg16(krow + 32 * ks + 8 * gq);
         }
@@ -461,17 +465,18 @@ __global__ __launch_bounds__(NTH) void route_kernel(Geom g, RouteParams p) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(qa[ks], as_bf16x8(kv[j][ks]), acc);
-          if (c < n) {
+          if (c < ns) {
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) U[(4 * gq + jj) * USTR + c] = acc[jj] * p.gamma_scale;
           }
         }
       }
     } else {
-      for (int idx = tid; idx < nh * n; idx += NTH) {
-        const int hh = idx / n, c = idx - hh * n;
+      for (int idx = tid; idx < nh * ns; idx += NTH) {
+        const int hh = idx / ns, c = idx - hh * ns;
         const float* qr = (const float*)p.q + ((tok * g.Hq + h * g.G + h0 + hh) * (int64_t)D);
-        const float* kr = (const float*)p.kbar + (((kb0 + c) * g.Hkv + h) * (int64_t)D);
+        const float* kr = c == n ? (const float*)kdrow
+                                 : (const float*)p.kbar + (((kb0 + c) * g.Hkv + h) * (int64_t)D);
         float d = 0.f;
 #pragma unroll 8
         for (int e = 0; e < D; e += 4) {
@@ -485,15 +490,15 @@ __global__ __launch_bounds__(NTH) void route_kernel(Geom g, RouteParams p) {
         U[hh * USTR + c] = d * p.gamma_scale;
       }
     }
-    // entries from n up to the row's solve width hold a sentinel far below any
+    // entries from ns up to the row's solve width hold a sentinel far below any
     // threshold (kFar / xs_scale stays far below after scaling)
     {
-      const int npad = n <= (NK / 4) * LPH && NK >= 16 ? (NK / 4) * LPH
-                       : n <= (NK / 2) * LPH && NK >= 8 ? (NK / 2) * LPH : CP;
-      const int w = npad - n;
+      const int npad = ns <= (NK / 4) * LPH && NK >= 16 ? (NK / 4) * LPH
+                       : ns <= (NK / 2) * LPH && NK >= 8 ? (NK / 2) * LPH : CP;
+      const int w = npad - ns;
       for (int idx = tid; idx < 16 * w; idx += NTH) {
         const int hh = idx / w;
-        U[hh * USTR + n + (idx - hh * w)] = kFar;
+        U[hh * USTR + ns + (idx - hh * w)] = kFar;
       }
     }
     __syncthreads();
@@ -504,15 +509,15 @@ __global__ __launch_bounds__(NTH) void route_kernel(Geom g, RouteParams p) {
       const bool live = hh < nh;
       const float* urow = U + (hh & 15) * USTR;  // in bounds for every lane
       float* crow = Cand + (hh & 15) * CAPH;
-      // values per lane for this row's n chunks: a quarter, half or all of NK
-      if (n <= (NK / 4) * LPH && NK >= 16)
-        threshold_pass<(NK >= 16 ? NK / 4 : NK), LPH, CAPH>(urow, li, n, live, hh, smax, xs_scale,
+      // values per lane for this row's ns entries: a quarter, half or all of NK
+      if (ns <= (NK / 4) * LPH && NK >= 16)
+        threshold_pass<(NK >= 16 ? NK / 4 : NK), LPH, CAPH>(urow, li, ns, live, hh, smax, xs_scale,
                                                             ex, ecls, TauX, Zs, crow);
-      else if (n <= (NK / 2) * LPH && NK >= 8)
-        threshold_pass<(NK >= 8 ? NK / 2 : NK), LPH, CAPH>(urow, li, n, live, hh, smax, xs_scale,
+      else if (ns <= (NK / 2) * LPH && NK >= 8)
+        threshold_pass<(NK >= 8 ? NK / 2 : NK), LPH, CAPH>(urow, li, ns, live, hh, smax, xs_scale,
                                                            ex, ecls, TauX, Zs, crow);
       else
-        threshold_pass<NK, LPH, CAPH>(urow, li, n, live, hh, smax, xs_scale, ex, ecls, TauX, Zs,
+        threshold_pass<NK, LPH, CAPH>(urow, li, ns, live, hh, smax, xs_scale, ex, ecls, TauX, Zs,
                                       crow);
     }
     __syncthreads();
@@ -601,12 +606,16 @@ __global__ __launch_bounds__(256) void route_logits_kernel(Geom g, RouteParams p
   const int r = lane & 15, gq = lane >> 4;
   const int row = blockIdx.y, h = blockIdx.z;
   const int n = (p.seqlens[row] - 1) / g.B;
+  // entries: the routed chunks, then the row's own-chunk estimate when given
+  const int ns = (p.kdiag && n > 0) ? n + 1 : n;
   const int c0 = (blockIdx.x * 4 + wv) * 16;  // this wave's 16 chunks
-  if (c0 >= n) return;
+  if (c0 >= ns) return;
   const int64_t kb0 = (int64_t)row * (g.max_seqlen / g.B);
-  // clamped to a valid summary row; columns past n are not written
-  const int c = min(c0 + r, n - 1);
-  const uint16_t* krow = (const uint16_t*)p.kbar + (((kb0 + c) * g.Hkv + h) * (int64_t)D);
+  // clamped to a valid entry; columns past ns are not written
+  const int c = min(c0 + r, ns - 1);
+  const uint16_t* krow =
+      c == n ? (const uint16_t*)p.kdiag + (((int64_t)row * g.Hkv + h) * D)
+             : (const uint16_t*)p.kbar + (((kb0 + c) * g.Hkv + h) * (int64_t)D);
   u32x4 kv[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) kv[ks] = ldg16(krow + 32 * ks + 8 * gq);
@@ -622,7 +631,7 @@ __global__ __launch_bounds__(256) void route_logits_kernel(Geom g, RouteParams p
       acc = mfma16x16x32(as_bf16x8(v), as_bf16x8(kv[ks]), acc);
     }
     // lane (gq, r): heads 4 gq + j, chunk c0 + r
-    if (c0 + r < n) {
+    if (c0 + r < ns) {
       float* ur = p.ulog + (((int64_t)row * g.Hkv + h) * g.G + h0) * g.C_slots + c0 + r;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -654,14 +663,16 @@ __global__ __launch_bounds__(64) void route_solve_kernel(Geom g, RouteParams p) 
   const int ecls = smax ? 0 : (ex == 1.f ? 1 : (ex == 2.f ? 2 : (ex == 4.f ? 4 : 0)));
   const float xs_scale = smax ? 1.f : am1;
   const float* ur = p.ulog + (((int64_t)row * g.Hkv + h) * g.G + q) * g.C_slots;
+  // entries: the routed chunks, then the own-chunk estimate when given
+  const int ns = p.kdiag ? n + 1 : n;
   // every load unconditional (clamped to the row) and in flight together;
-  // entries past n become the sentinel afterwards
+  // entries past ns become the sentinel afterwards
   float xs[NK];
 #pragma unroll
-  for (int k = 0; k < NK; ++k) xs[k] = ur[min(li + 64 * k, n - 1)];
+  for (int k = 0; k < NK; ++k) xs[k] = ur[min(li + 64 * k, ns - 1)];
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int k = 0; k < NK; ++k) xs[k] = li + 64 * k < n ? xs[k] * xs_scale : kFar;
+  for (int k = 0; k < NK; ++k) xs[k] = li + 64 * k < ns ? xs[k] * xs_scale : kFar;
   float xmax = -INFINITY;
 #pragma unroll
   for (int k = 0; k < NK; ++k) xmax = fmaxf(xmax, xs[k]);

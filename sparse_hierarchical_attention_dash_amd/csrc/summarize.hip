@@ -185,6 +185,156 @@ __global__ __launch_bounds__(64) void cache_append_kernel(
   summarize_chunk<BF16, D>(row, qbar + h * D, g.B, (char*)kbar + orow * D * ESZ);
 }
 
+// Estimated summary of a position's own, partial chunk: q_bar's phase-0
+// attention over the chunk's keys up to the position.  One wave scans keys
+// key(0) .. key(len-1) of one chunk in order with a running (max, sum,
+// weighted key) in base 2, lane l holding dimensions EPL l .. EPL l + EPL - 1;
+// after key t the normalised running value is position t's estimate, written
+// to out(t) when ALL (else only after the last key), rounded once.
+template <bool BF16, int D, bool ALL, class KeyFn, class OutFn>
+__device__ __forceinline__ void diag_scan(KeyFn key, int len, const float* __restrict__ qbar_h,
+                                          OutFn out) {
+  constexpr int EPL = D / kWave;  // 1 or 2 elements per lane
+  constexpr int GRP = 8;          // keys whose loads are issued together
+  const int lane = threadIdx.x;
+  float qv[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) qv[e] = qbar_h[EPL * lane + e];
+  const float sc = kLog2e / sqrtf((float)D);
+  float m = -INFINITY, l = 0.f, acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  auto load = [&](int t, float (&x)[EPL]) {
+    const char* row = (const char*)key(t);
+    if constexpr (BF16) {
+      if constexpr (EPL == 2) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(row + 4 * lane);
+        x[0] = bf16lo(w);
+        x[1] = bf16hi(w);
+      } else {
+        x[0] = bf16_to_f32(*reinterpret_cast<const uint16_t*>(row + 2 * lane));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e)
+        x[e] = reinterpret_cast<const float*>(row)[EPL * lane + e];
+    }
+  };
+  for (int t0 = 0; t0 < len; t0 += GRP) {
+    float xs[GRP][EPL];
+#pragma unroll
+    for (int j = 0; j < GRP; ++j) load(min(t0 + j, len - 1), xs[j]);
+#pragma unroll
+    for (int j = 0; j < GRP; ++j) {
+      const int t = t0 + j;
+      if (t >= len) break;
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) d = fmaf(xs[j][e], qv[e], d);
+      d = row16_sum(d);
+      d += xor16(d);
+      d += xor32(d);
+      const float z = d * sc;
+      const float mn = fmaxf(m, z);
+      const float a = exp2f(m - mn);
+      const float p = exp2f(z - mn);
+      l = l * a + p;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, xs[j][e], acc[e] * a);
+      m = mn;
+      if (ALL || t == len - 1) {
+        const float inv = 1.f / l;
+        char* o = (char*)out(t);
+        if constexpr (BF16) {
+          if constexpr (EPL == 2)
+            *reinterpret_cast<uint32_t*>(o + 4 * lane) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+          else
+            *reinterpret_cast<uint16_t*>(o + 2 * lane) = (uint16_t)f32_to_bf16(acc[0] * inv);
+        } else {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e)
+            reinterpret_cast<float*>(o)[EPL * lane + e] = acc[e] * inv;
+        }
+      }
+    }
+  }
+}
+
+// Prefill: every position's estimate, kdiag [T, Hkv, D]; one wave per
+// (chunk, sequence, KV head), the last chunk of a sequence possibly partial.
+template <bool BF16, int D>
+__global__ __launch_bounds__(64) void diag_summary_kernel(
+    const void* __restrict__ kp, const float* __restrict__ qbar, void* __restrict__ kdiag,
+    const int32_t* __restrict__ cu_seqlens, int max_seqlen, int Hkv, int B) {
+  constexpr int ESZ = BF16 ? 2 : 4;
+  const int c = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
+  const SeqInfo si = seq_info(cu_seqlens, nullptr, s, max_seqlen, B);
+  const int t0 = c * B;
+  if (t0 >= si.len) return;
+  const int len = min(B, si.len - t0);
+  const int64_t row0 = si.start + t0;
+  auto key = [&](int t) -> const void* {
+    return (const char*)kp + ((row0 + t) * Hkv + h) * (int64_t)D * ESZ;
+  };
+  auto out = [&](int t) -> void* {
+    return (char*)kdiag + ((row0 + t) * Hkv + h) * (int64_t)D * ESZ;
+  };
+  diag_scan<BF16, D, true>(key, len, qbar + h * D, out);
+}
+
+// Decode: the estimate at each batch entry's new position L-1 from the
+// cached keys n B .. L-1 (n = floor((L-1)/B)), kdiag [batch, Hkv, D].
+template <bool BF16, int D>
+__global__ __launch_bounds__(64) void decode_diag_kernel(
+    const void* __restrict__ kc, const int32_t* __restrict__ seqlens,
+    const float* __restrict__ qbar, void* __restrict__ kdiag, int cap, int Hkv, int B) {
+  constexpr int ESZ = BF16 ? 2 : 4;
+  const int b = blockIdx.x, h = blockIdx.y;
+  const int L = seqlens[b];
+  const int t0 = ((L - 1) / B) * B;
+  const int64_t row0 = (int64_t)b * cap + t0;
+  auto key = [&](int t) -> const void* {
+    return (const char*)kc + ((row0 + t) * Hkv + h) * (int64_t)D * ESZ;
+  };
+  auto out = [&](int) -> void* {
+    return (char*)kdiag + ((int64_t)b * Hkv + h) * D * ESZ;
+  };
+  diag_scan<BF16, D, false>(key, L - t0, qbar + h * D, out);
+}
+
+hipError_t launch_diag_summary(const Geom& g, const void* k, const float* qbar, void* kdiag,
+                               hipStream_t st) {
+  const int maxC = (g.max_seqlen + g.B - 1) / g.B;
+  if (maxC == 0 || g.num_seqs == 0) return hipSuccess;
+  dim3 grid(maxC, g.num_seqs, g.Hkv);
+#define DASH_DIAG(BF, DD)                                                                   \
+  hipLaunchKernelGGL((diag_summary_kernel<BF, DD>), grid, dim3(kWave), 0, st, k, qbar, kdiag, \
+                     g.cu_seqlens, g.max_seqlen, g.Hkv, g.B)
+  if (g.bf16) {
+    if (g.D == 64) DASH_DIAG(true, 64); else DASH_DIAG(true, 128);
+  } else {
+    if (g.D == 64) DASH_DIAG(false, 64); else DASH_DIAG(false, 128);
+  }
+#undef DASH_DIAG
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_diag(const Geom& g, const void* k_cache, const int32_t* seqlens,
+                              const float* qbar, void* kdiag, hipStream_t st) {
+  if (g.num_seqs == 0) return hipSuccess;
+  dim3 grid(g.num_seqs, g.Hkv);
+#define DASH_DDIAG(BF, DD)                                                                \
+  hipLaunchKernelGGL((decode_diag_kernel<BF, DD>), grid, dim3(kWave), 0, st, k_cache, seqlens, \
+                     qbar, kdiag, g.max_seqlen, g.Hkv, g.B)
+  if (g.bf16) {
+    if (g.D == 64) DASH_DDIAG(true, 64); else DASH_DDIAG(true, 128);
+  } else {
+    if (g.D == 64) DASH_DDIAG(false, 64); else DASH_DDIAG(false, 128);
+  }
+#undef DASH_DDIAG
+  return hipGetLastError();
+}
+
 hipError_t launch_cache_append(const Geom& g, const void* knew, const void* vnew,
                                const int32_t* seqlens, const float* qbar, void* kc, void* vc,
                                void* kbar, hipStream_t st) {

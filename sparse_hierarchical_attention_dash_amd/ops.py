@@ -86,13 +86,29 @@ def summarize(k, qbar, chunk_size, cu_seqlens=None, max_seqlen=None, out=None,
     return out
 
 
+def summarize_diagonal(k, qbar, chunk_size, cu_seqlens=None, max_seqlen=None, out=None):
+    """Estimated summary of every position's own partial chunk (for
+    estimate_diagonal routing); returns k_diag [T, Hkv, D] (k's dtype)."""
+    _need_cuda(k, qbar, cu_seqlens)
+    T, Hkv, D = k.shape
+    shape = _seq_shape(k, Hkv, Hkv, chunk_size, cu_seqlens, max_seqlen)
+    if out is None:
+        out = torch.empty_like(k)
+    qb = qbar if qbar.dtype == torch.float32 else qbar.float().contiguous()
+    L.check("dash_summarize_diagonal", L.lib().dash_summarize_diagonal(
+        ctypes.byref(shape), _ptr(k), _ptr(qb), _ptr(out), _stream(k.device)))
+    return out
+
+
 def route(q, kbar, num_kv_heads, chunk_size, *, alpha=1.5, gamma=1.0, sigma=1.0,
           softmax_scale=0.0, enable_gqa=True, alpha_per_seq=None, cu_seqlens=None,
           max_seqlen=None, log_prior=False, tau=False, mask_out=None, log_prior_out=None,
-          workspace=None):
+          workspace=None, kdiag=None):
     """Phase-1 routing.  Returns (active_blocks [Hkv,T,W] int64 view of the
-    uint64 words, log_prior [Hkv,T,C_slots] or None, tau [Hq,T] or None)."""
-    _need_cuda(q, kbar, alpha_per_seq, cu_seqlens, mask_out, log_prior_out)
+    uint64 words, log_prior [Hkv,T,C_slots] or None, tau [Hq,T] or None).
+    kdiag [T, Hkv, D] (summarize_diagonal) adds each row's own-chunk estimate
+    to its entmax."""
+    _need_cuda(q, kbar, alpha_per_seq, cu_seqlens, mask_out, log_prior_out, kdiag)
     T, Hq, D = q.shape
     shape = _seq_shape(q, Hq, num_kv_heads, chunk_size, cu_seqlens, max_seqlen)
     dev = q.device
@@ -111,7 +127,7 @@ def route(q, kbar, num_kv_heads, chunk_size, *, alpha=1.5, gamma=1.0, sigma=1.0,
     else:
         ws, n = workspace, L.workspace_size(L.DASH_OP_ROUTE, shape)
     L.check("dash_route", L.lib().dash_route(
-        ctypes.byref(shape), _ptr(q), _ptr(kbar), float(alpha), _ptr(alpha_per_seq),
+        ctypes.byref(shape), _ptr(q), _ptr(kbar), _ptr(kdiag), float(alpha), _ptr(alpha_per_seq),
         float(gamma), float(sigma), float(softmax_scale), int(enable_gqa), _ptr(mask),
         _ptr(lp), _ptr(ta), _ptr(ws), n, _stream(dev)))
     return mask, lp, ta
@@ -170,8 +186,9 @@ def route_topk_decode_workspace(q, num_kv_heads, chunk_size, cache_len):
 def attn_prefill(q, k, v, qbar, chunk_size, *, alpha=1.5, gamma=1.0, sigma=1.0,
                  softmax_scale=0.0, enable_gqa=True, alpha_per_seq=None, cu_seqlens=None,
                  max_seqlen=None, return_lse=False, return_active_blocks=False,
-                 workspace=None):
-    """Phases 0-2, causal prefill.  Returns (out, lse or None, active_blocks or None)."""
+                 workspace=None, estimate_diagonal=False):
+    """Phases 0-2, causal prefill.  Returns (out, lse or None, active_blocks or None).
+    estimate_diagonal routes every row with its own-chunk estimate too."""
     _need_cuda(q, k, v, qbar, alpha_per_seq, cu_seqlens)
     T, Hq, D = q.shape
     Hkv = k.shape[1]
@@ -188,8 +205,8 @@ def attn_prefill(q, k, v, qbar, chunk_size, *, alpha=1.5, gamma=1.0, sigma=1.0,
     L.check("dash_attn_prefill", L.lib().dash_attn_prefill(
         ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(qbar), float(alpha),
         _ptr(alpha_per_seq), float(gamma), float(sigma), float(softmax_scale),
-        int(enable_gqa), _ptr(out), _ptr(lse), _ptr(ab), _ptr(workspace), n,
-        _stream(dev)))
+        int(enable_gqa), int(estimate_diagonal), _ptr(out), _ptr(lse), _ptr(ab),
+        _ptr(workspace), n, _stream(dev)))
     return out, lse, ab
 
 
@@ -240,10 +257,16 @@ def decode_shape(q, k_cache, chunk_size):
 
 def attn_decode(q, k_cache, v_cache, seqlens, kbar_cache, chunk_size, *, alpha=1.5,
                 gamma=1.0, sigma=1.0, softmax_scale=0.0, enable_gqa=True,
-                return_lse=False, return_active_blocks=False, workspace=None, out=None):
+                return_lse=False, return_active_blocks=False, workspace=None, out=None,
+                estimate_diagonal=False, qbar=None):
     """One decode step.  q [batch, Hq, D]; caches [batch, cap, Hkv, D];
-    seqlens int32 [batch]; kbar_cache [batch, cap/B, Hkv, D]."""
-    _need_cuda(q, k_cache, v_cache, seqlens, kbar_cache)
+    seqlens int32 [batch]; kbar_cache [batch, cap/B, Hkv, D].  With
+    estimate_diagonal, qbar [Hkv, D] gives the new rows' own-chunk estimates."""
+    if estimate_diagonal and qbar is None:
+        raise ValueError("estimate_diagonal needs qbar")
+    qb = None if qbar is None else (qbar if qbar.dtype == torch.float32
+                                    else qbar.float().contiguous())
+    _need_cuda(q, k_cache, v_cache, seqlens, kbar_cache, qb)
     batch, Hq, D = q.shape
     Hkv = k_cache.shape[2]
     shape = decode_shape(q, k_cache, chunk_size)
@@ -260,9 +283,9 @@ def attn_decode(q, k_cache, v_cache, seqlens, kbar_cache, chunk_size, *, alpha=1
         workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
     L.check("dash_attn_decode", L.lib().dash_attn_decode(
         ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens),
-        _ptr(kbar_cache), float(alpha), float(gamma), float(sigma), float(softmax_scale),
-        int(enable_gqa), _ptr(out), _ptr(lse), _ptr(ab), _ptr(workspace), n,
-        _stream(dev)))
+        _ptr(kbar_cache), _ptr(qb), float(alpha), float(gamma), float(sigma),
+        float(softmax_scale), int(enable_gqa), int(estimate_diagonal), _ptr(out), _ptr(lse),
+        _ptr(ab), _ptr(workspace), n, _stream(dev)))
     return out, lse, ab
 
 

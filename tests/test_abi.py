@@ -40,12 +40,12 @@ _DEFAULT = object()
 
 
 def prefill(lib, s, *, q=A, k=A, v=A, qbar=A, out=A, alpha=1.5, gamma=1.0, sigma=1.0,
-            scale=0.0, gqa=1, ws=_DEFAULT, ws_bytes=None):
+            scale=0.0, gqa=1, diag=0, ws=_DEFAULT, ws_bytes=None):
     need = L.workspace_size(L.DASH_OP_PREFILL, s)
     ws = A if ws is _DEFAULT else ws
     ws_bytes = need if ws_bytes is None else ws_bytes
     return lib.dash_attn_prefill(ctypes.byref(s), q, k, v, qbar, alpha, None, gamma, sigma,
-                                 scale, gqa, out, None, None, ws, ws_bytes, None)
+                                 scale, gqa, diag, out, None, None, ws, ws_bytes, None)
 
 
 def test_header_declares_the_four_operations():
@@ -62,7 +62,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dash_abi_version() == 1
+    assert lib.dash_abi_version() == 2
     for code, text in ((0, "ok"), (1, "invalid argument"), (2, "unsupported configuration"),
                        (3, "workspace too small"), (4, "HIP launch error")):
         assert L.status_string(code) == text
@@ -76,11 +76,13 @@ def test_layout_and_workspace_sizes(lib):
     s = shape(T=131072, B=64)
     lay = L.layout(s)
     assert (lay.chunk_slots, lay.mask_words) == (2048, 32)
-    # prefill workspace holds summaries, a mask, the dense log-prior and (bf16,
-    # group >= 16) V transposed into 64-padded columns
+    # prefill workspace holds summaries, a mask, the dense log-prior, (bf16,
+    # group >= 16) V transposed into 64-padded columns, and the own-chunk
+    # estimates of estimate_diagonal
     T, Hkv, D, W, C = 1000, 2, 128, 1, 16
     need = L.workspace_size(L.DASH_OP_PREFILL, shape(T=T))
-    parts = [(T // 64) * Hkv * D * 2, Hkv * T * W * 8, Hkv * T * C * 4, Hkv * D * (T + 64) * 2]
+    parts = [(T // 64) * Hkv * D * 2, Hkv * T * W * 8, Hkv * T * C * 4, Hkv * D * (T + 64) * 2,
+             T * Hkv * D * 2]
     assert need == sum((p + 255) // 256 * 256 for p in parts)
     assert L.workspace_size(L.DASH_OP_SUMMARIZE, shape()) == 0
     assert L.workspace_size(L.DASH_OP_ROUTE, shape(cu=A, num_seqs=3)) == 512
@@ -103,8 +105,8 @@ def test_prefill_rejects_bad_shapes(lib, kw, status):
 
 def test_prefill_rejects_bad_arguments(lib):
     s = shape()
-    assert lib.dash_attn_prefill(None, A, A, A, A, 1.5, None, 1.0, 1.0, 0.0, 1, A, None, None,
-                                 A, 1 << 30, None) == L.DASH_ERR_INVALID_ARGUMENT
+    assert lib.dash_attn_prefill(None, A, A, A, A, 1.5, None, 1.0, 1.0, 0.0, 1, 0, A, None,
+                                 None, A, 1 << 30, None) == L.DASH_ERR_INVALID_ARGUMENT
     assert prefill(lib, s, q=None) == L.DASH_ERR_INVALID_ARGUMENT
     assert prefill(lib, s, out=None) == L.DASH_ERR_INVALID_ARGUMENT
     assert prefill(lib, s, qbar=None) == L.DASH_ERR_INVALID_ARGUMENT
@@ -130,16 +132,24 @@ def test_empty_input_is_a_no_op(lib):
     assert prefill(lib, shape(T=0, num_seqs=0, max_seqlen=0)) == L.DASH_OK
     s = shape(T=0, num_seqs=0, max_seqlen=0)
     assert lib.dash_summarize(ctypes.byref(s), A, A, A, None, 0, None) == L.DASH_OK
-    assert lib.dash_route(ctypes.byref(s), A, A, 1.5, None, 1.0, 1.0, 0.0, 1, A, None, None,
-                          None, 0, None) == L.DASH_OK
+    assert lib.dash_route(ctypes.byref(s), A, A, None, 1.5, None, 1.0, 1.0, 0.0, 1, A, None,
+                          None, None, 0, None) == L.DASH_OK
+    assert lib.dash_summarize_diagonal(ctypes.byref(s), A, A, A, None) == L.DASH_OK
 
 
 def test_route_and_summarize_checks(lib):
     s = shape()
-    assert lib.dash_route(ctypes.byref(s), A, A, 1.5, None, 1.0, 1.0, 0.0, 1, None, None, None,
-                          None, 0, None) == L.DASH_ERR_INVALID_ARGUMENT   # mask is required
-    assert lib.dash_route(ctypes.byref(s), A, A, 2.5, None, 1.0, 1.0, 0.0, 1, A, None, None,
-                          None, 0, None) == L.DASH_ERR_UNSUPPORTED
+    assert lib.dash_route(ctypes.byref(s), A, A, None, 1.5, None, 1.0, 1.0, 0.0, 1, None, None,
+                          None, None, 0, None) == L.DASH_ERR_INVALID_ARGUMENT   # mask is required
+    assert lib.dash_route(ctypes.byref(s), A, A, None, 2.5, None, 1.0, 1.0, 0.0, 1, A, None,
+                          None, None, 0, None) == L.DASH_ERR_UNSUPPORTED
+    assert lib.dash_route(ctypes.byref(s), A, A, A + 4, 1.5, None, 1.0, 1.0, 0.0, 1, A, None,
+                          None, None, 0, None) == L.DASH_ERR_INVALID_ARGUMENT  # kdiag misaligned
+    for args in ((None, A, A), (A, None, A), (A, A, None), (A + 2, A, A)):
+        assert lib.dash_summarize_diagonal(ctypes.byref(s), *args, None) == \
+            L.DASH_ERR_INVALID_ARGUMENT
+    assert lib.dash_summarize_diagonal(ctypes.byref(shape(D=96)), A, A, A, None) == \
+        L.DASH_ERR_UNSUPPORTED
     assert lib.dash_summarize(ctypes.byref(s), None, A, A, None, 0, None) == \
         L.DASH_ERR_INVALID_ARGUMENT
     v = shape(cu=A, num_seqs=3)
@@ -152,11 +162,14 @@ def test_decode_checks(lib):
     need = L.workspace_size(L.DASH_OP_DECODE, s)
 
     def dec(sh, **kw):
-        a = dict(q=A, k=A, v=A, sl=A, kb=A, out=A, ws=A, n=need, alpha=1.5)
+        a = dict(q=A, k=A, v=A, sl=A, kb=A, qb=None, diag=0, out=A, ws=A, n=need, alpha=1.5)
         a.update(kw)
         return lib.dash_attn_decode(ctypes.byref(sh), a["q"], a["k"], a["v"], a["sl"], a["kb"],
-                                    a["alpha"], 1.0, 1.0, 0.0, 1, a["out"], None, None, a["ws"],
-                                    a["n"], None)
+                                    a["qb"], a["alpha"], 1.0, 1.0, 0.0, 1, a["diag"], a["out"],
+                                    None, None, a["ws"], a["n"], None)
+
+    assert dec(s, diag=1) == L.DASH_ERR_INVALID_ARGUMENT            # q_bar needed
+    assert dec(s, diag=1, qb=A + 4) == L.DASH_ERR_INVALID_ARGUMENT  # misaligned
 
     assert dec(s, sl=None) == L.DASH_ERR_INVALID_ARGUMENT
     assert dec(s, kb=None) == L.DASH_ERR_INVALID_ARGUMENT
