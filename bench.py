@@ -393,6 +393,27 @@ def main():
             t_topk_route = time_it(stream, lambda: ops.route_topk(
                 q, kbar, wp.Hkv, wp.B, kp, gamma=wp.gamma, mask_out=m2, log_prior_out=l2,
                 workspace=ws_route), reps)
+            # estimate_diagonal: the own-chunk estimates join every row's routing
+            kd = torch.empty_like(k)
+
+            def diag_pre():
+                ops.summarize(k, qbar, wp.B, out=kbar, workspace=ws_route)
+                ops.summarize_diagonal(k, qbar, wp.B, out=kd)
+                ops.route(q, kbar, wp.Hkv, wp.B, alpha=wp.alpha, gamma=wp.gamma, sigma=wp.sigma,
+                          mask_out=m2, log_prior_out=l2, log_prior=True, workspace=ws_route,
+                          kdiag=kd)
+                ops.attn_sparse(q, k, v, m2, l2, wp.B, out=out, workspace=ws_sparse)
+
+            t_diag = time_it(stream, diag_pre, reps)
+            pop_dg = popcounts(m2.cpu().numpy())
+            flops_dg = prefill_active_flops(pop_dg, wp.B, wp.D, G)
+            t_dsum = time_it(stream, lambda: ops.summarize_diagonal(k, qbar, wp.B, out=kd), reps)
+            t_droute = time_it(stream, lambda: ops.route(
+                q, kbar, wp.Hkv, wp.B, alpha=wp.alpha, gamma=wp.gamma, sigma=wp.sigma,
+                mask_out=m2, log_prior_out=l2, log_prior=True, workspace=ws_route, kdiag=kd), reps)
+            cmp["estimate_diagonal"] = {
+                "prefill_ms": t_diag, "diag_summary_ms": t_dsum, "route_ms": t_droute,
+                "active_blocks": int(pop_dg.sum()), "tflops": flops_dg / (t_diag * 1e-3) / 1e12}
             cmp["prefill"] = {
                 "dash_ms": t_pre,
                 "dense_ms": t_dense, "dense_flops": dense_flops,
@@ -454,6 +475,16 @@ def main():
 
             t_app = time_it(stream, append, 10)
             g_app = graph_time(stream, append_dec, [out_d], 10)
+
+            def diag_dec():
+                ops.attn_decode(qd, kc, vc, seqlens, kbar_c, wd.B, alpha=wd.alpha,
+                                gamma=wd.gamma, sigma=wd.sigma, workspace=ws_dec, out=out_d,
+                                estimate_diagonal=True, qbar=qbar_d)
+
+            t_ddiag = time_it(stream, diag_dec, 5)
+            g_ddiag = graph_time(stream, diag_dec, [out_d], 10)
+            cmp.setdefault("estimate_diagonal", {}).update(
+                decode_us=t_ddiag * 1e3, decode_graph_us=g_ddiag * 1e3)
             dense_bytes = float(np.sum(wd.B * n_b + ((dd["seqlens"] - 1) % wd.B) + 1)) \
                 * wd.Hkv * wd.D * 2 * 2
             cmp["decode"] = {

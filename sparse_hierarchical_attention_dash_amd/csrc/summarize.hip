@@ -191,11 +191,10 @@ __global__ __launch_bounds__(64) void cache_append_kernel(
 // weighted key) in base 2, lane l holding dimensions EPL l .. EPL l + EPL - 1;
 // after key t the normalised running value is position t's estimate, written
 // to out(t) when ALL (else only after the last key), rounded once.
-template <bool BF16, int D, bool ALL, class KeyFn, class OutFn>
+template <bool BF16, int D, int MAXK, bool ALL, class KeyFn, class OutFn>
 __device__ __forceinline__ void diag_scan(KeyFn key, int len, const float* __restrict__ qbar_h,
                                           OutFn out) {
   constexpr int EPL = D / kWave;  // 1 or 2 elements per lane
-  constexpr int GRP = 8;          // keys whose loads are issued together
   const int lane = threadIdx.x;
   float qv[EPL];
 #pragma unroll
@@ -204,57 +203,98 @@ __device__ __forceinline__ void diag_scan(KeyFn key, int len, const float* __res
   float m = -INFINITY, l = 0.f, acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  auto load = [&](int t, float (&x)[EPL]) {
-    const char* row = (const char*)key(t);
-    if constexpr (BF16) {
-      if constexpr (EPL == 2) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(row + 4 * lane);
-        x[0] = bf16lo(w);
-        x[1] = bf16hi(w);
-      } else {
-        x[0] = bf16_to_f32(*reinterpret_cast<const uint16_t*>(row + 2 * lane));
-      }
-    } else {
+  // the key's score in log2 units (a wave reduction)
+  auto score = [&](const float (&x)[EPL]) -> float {
+    float d = 0.f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e)
-        x[e] = reinterpret_cast<const float*>(row)[EPL * lane + e];
+    for (int e = 0; e < EPL; ++e) d = fmaf(x[e], qv[e], d);
+    d = row16_sum(d);
+    d += xor16(d);
+    d += xor32(d);
+    return d * sc;
+  };
+  // fold key t (its EPL elements in x, score z) into the running state;
+  // write out(t)
+  auto step = [&](int t, const float (&x)[EPL], float z) {
+    const float mn = fmaxf(m, z);
+    const float a = exp2f(m - mn);
+    const float p = exp2f(z - mn);
+    l = l * a + p;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, x[e], acc[e] * a);
+    m = mn;
+    if (ALL || t == len - 1) {
+      const float inv = 1.f / l;
+      char* o = (char*)out(t);
+      if constexpr (BF16) {
+        if constexpr (EPL == 2)
+          *reinterpret_cast<uint32_t*>(o + 4 * lane) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+        else
+          *reinterpret_cast<uint16_t*>(o + 2 * lane) = (uint16_t)f32_to_bf16(acc[0] * inv);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+          reinterpret_cast<float*>(o)[EPL * lane + e] = acc[e] * inv;
+      }
     }
   };
-  for (int t0 = 0; t0 < len; t0 += GRP) {
-    float xs[GRP][EPL];
+  if constexpr (BF16) {
+    // every key's elements (one 32- or 16-bit word per lane) are loaded up
+    // front, so the scan waits for memory once (len <= MAXK = B)
+    uint32_t raw[MAXK];
 #pragma unroll
-    for (int j = 0; j < GRP; ++j) load(min(t0 + j, len - 1), xs[j]);
+    for (int t = 0; t < MAXK; ++t) {
+      if (t < len) {
+        const char* row = (const char*)key(t);
+        raw[t] = EPL == 2 ? *reinterpret_cast<const uint32_t*>(row + 4 * lane)
+                          : (uint32_t)*reinterpret_cast<const uint16_t*>(row + 2 * lane);
+      }
+    }
+    auto unpack = [&](int t, float (&x)[EPL]) {
+      if constexpr (EPL == 2) {
+        x[0] = bf16lo(raw[t]);
+        x[1] = bf16hi(raw[t]);
+      } else {
+        x[0] = bf16_to_f32(raw[t]);
+      }
+    };
+    // 32 keys at a time: their scores as independent reductions, then the
+    // running update (a short dependent chain) key by key
+    constexpr int SG = 32;
 #pragma unroll
-    for (int j = 0; j < GRP; ++j) {
-      const int t = t0 + j;
-      if (t >= len) break;
-      float d = 0.f;
+    for (int t0 = 0; t0 < MAXK; t0 += SG) {
+      if (t0 < len) {
+        float z[SG];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) d = fmaf(xs[j][e], qv[e], d);
-      d = row16_sum(d);
-      d += xor16(d);
-      d += xor32(d);
-      const float z = d * sc;
-      const float mn = fmaxf(m, z);
-      const float a = exp2f(m - mn);
-      const float p = exp2f(z - mn);
-      l = l * a + p;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, xs[j][e], acc[e] * a);
-      m = mn;
-      if (ALL || t == len - 1) {
-        const float inv = 1.f / l;
-        char* o = (char*)out(t);
-        if constexpr (BF16) {
-          if constexpr (EPL == 2)
-            *reinterpret_cast<uint32_t*>(o + 4 * lane) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-          else
-            *reinterpret_cast<uint16_t*>(o + 2 * lane) = (uint16_t)f32_to_bf16(acc[0] * inv);
-        } else {
-#pragma unroll
-          for (int e = 0; e < EPL; ++e)
-            reinterpret_cast<float*>(o)[EPL * lane + e] = acc[e] * inv;
+        for (int j = 0; j < SG; ++j) {
+          float x[EPL];
+          unpack(t0 + j, x);
+          z[j] = score(x);
         }
+#pragma unroll
+        for (int j = 0; j < SG; ++j) {
+          if (t0 + j < len) {
+            float x[EPL];
+            unpack(t0 + j, x);
+            step(t0 + j, x, z[j]);
+          }
+        }
+      }
+    }
+  } else {
+    constexpr int GRP = 8;  // keys whose loads are issued together
+    for (int t0 = 0; t0 < len; t0 += GRP) {
+      float xs[GRP][EPL];
+#pragma unroll
+      for (int j = 0; j < GRP; ++j) {
+        const float* row = (const float*)key(min(t0 + j, len - 1));
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) xs[j][e] = row[EPL * lane + e];
+      }
+#pragma unroll
+      for (int j = 0; j < GRP; ++j) {
+        if (t0 + j >= len) break;
+        step(t0 + j, xs[j], score(xs[j]));
       }
     }
   }
@@ -262,7 +302,7 @@ __device__ __forceinline__ void diag_scan(KeyFn key, int len, const float* __res
 
 // Prefill: every position's estimate, kdiag [T, Hkv, D]; one wave per
 // (chunk, sequence, KV head), the last chunk of a sequence possibly partial.
-template <bool BF16, int D>
+template <bool BF16, int D, int BB>
 __global__ __launch_bounds__(64) void diag_summary_kernel(
     const void* __restrict__ kp, const float* __restrict__ qbar, void* __restrict__ kdiag,
     const int32_t* __restrict__ cu_seqlens, int max_seqlen, int Hkv, int B) {
@@ -279,12 +319,12 @@ __global__ __launch_bounds__(64) void diag_summary_kernel(
   auto out = [&](int t) -> void* {
     return (char*)kdiag + ((row0 + t) * Hkv + h) * (int64_t)D * ESZ;
   };
-  diag_scan<BF16, D, true>(key, len, qbar + h * D, out);
+  diag_scan<BF16, D, BB, true>(key, len, qbar + h * D, out);
 }
 
 // Decode: the estimate at each batch entry's new position L-1 from the
 // cached keys n B .. L-1 (n = floor((L-1)/B)), kdiag [batch, Hkv, D].
-template <bool BF16, int D>
+template <bool BF16, int D, int BB>
 __global__ __launch_bounds__(64) void decode_diag_kernel(
     const void* __restrict__ kc, const int32_t* __restrict__ seqlens,
     const float* __restrict__ qbar, void* __restrict__ kdiag, int cap, int Hkv, int B) {
@@ -299,7 +339,7 @@ __global__ __launch_bounds__(64) void decode_diag_kernel(
   auto out = [&](int) -> void* {
     return (char*)kdiag + ((int64_t)b * Hkv + h) * D * ESZ;
   };
-  diag_scan<BF16, D, false>(key, L - t0, qbar + h * D, out);
+  diag_scan<BF16, D, BB, false>(key, L - t0, qbar + h * D, out);
 }
 
 hipError_t launch_diag_summary(const Geom& g, const void* k, const float* qbar, void* kdiag,
@@ -307,14 +347,17 @@ hipError_t launch_diag_summary(const Geom& g, const void* k, const float* qbar, 
   const int maxC = (g.max_seqlen + g.B - 1) / g.B;
   if (maxC == 0 || g.num_seqs == 0) return hipSuccess;
   dim3 grid(maxC, g.num_seqs, g.Hkv);
-#define DASH_DIAG(BF, DD)                                                                   \
-  hipLaunchKernelGGL((diag_summary_kernel<BF, DD>), grid, dim3(kWave), 0, st, k, qbar, kdiag, \
-                     g.cu_seqlens, g.max_seqlen, g.Hkv, g.B)
+#define DASH_DIAG(BF, DD, BB)                                                               \
+  hipLaunchKernelGGL((diag_summary_kernel<BF, DD, BB>), grid, dim3(kWave), 0, st, k, qbar,    \
+                     kdiag, g.cu_seqlens, g.max_seqlen, g.Hkv, g.B)
+#define DASH_DIAG_B(BF, DD) \
+  do { if (g.B == 64) DASH_DIAG(BF, DD, 64); else DASH_DIAG(BF, DD, 128); } while (0)
   if (g.bf16) {
-    if (g.D == 64) DASH_DIAG(true, 64); else DASH_DIAG(true, 128);
+    if (g.D == 64) DASH_DIAG_B(true, 64); else DASH_DIAG_B(true, 128);
   } else {
-    if (g.D == 64) DASH_DIAG(false, 64); else DASH_DIAG(false, 128);
+    if (g.D == 64) DASH_DIAG_B(false, 64); else DASH_DIAG_B(false, 128);
   }
+#undef DASH_DIAG_B
 #undef DASH_DIAG
   return hipGetLastError();
 }
@@ -323,14 +366,17 @@ hipError_t launch_decode_diag(const Geom& g, const void* k_cache, const int32_t*
                               const float* qbar, void* kdiag, hipStream_t st) {
   if (g.num_seqs == 0) return hipSuccess;
   dim3 grid(g.num_seqs, g.Hkv);
-#define DASH_DDIAG(BF, DD)                                                                \
-  hipLaunchKernelGGL((decode_diag_kernel<BF, DD>), grid, dim3(kWave), 0, st, k_cache, seqlens, \
-                     qbar, kdiag, g.max_seqlen, g.Hkv, g.B)
+#define DASH_DDIAG(BF, DD, BB)                                                            \
+  hipLaunchKernelGGL((decode_diag_kernel<BF, DD, BB>), grid, dim3(kWave), 0, st, k_cache,    \
+                     seqlens, qbar, kdiag, g.max_seqlen, g.Hkv, g.B)
+#define DASH_DDIAG_B(BF, DD) \
+  do { if (g.B == 64) DASH_DDIAG(BF, DD, 64); else DASH_DDIAG(BF, DD, 128); } while (0)
   if (g.bf16) {
-    if (g.D == 64) DASH_DDIAG(true, 64); else DASH_DDIAG(true, 128);
+    if (g.D == 64) DASH_DDIAG_B(true, 64); else DASH_DDIAG_B(true, 128);
   } else {
-    if (g.D == 64) DASH_DDIAG(false, 64); else DASH_DDIAG(false, 128);
+    if (g.D == 64) DASH_DDIAG_B(false, 64); else DASH_DDIAG_B(false, 128);
   }
+#undef DASH_DDIAG_B
 #undef DASH_DDIAG
   return hipGetLastError();
 }
