@@ -31,3 +31,5 @@ from .dash_oracle import (  # noqa: F401
     prefill_varlen,
     decode,
 )
+
+from . import dash_backward  # noqa: F401,E402

@@ -1,0 +1,174 @@
+"""CPU oracle for the backward pass of the DashAttention forward path.
+
+Test infrastructure only, like ``dash_oracle`` (plain NumPy, float64).  The
+pages make differentiability the method's central claim: alpha-entmax lets
+gradients flow from the second-stage attention back through the routing to
+the phase-0 summaries ([NL] "Technische Samenvatting: DashAttention", Fase 1,
+Differentieerbaarheid bullet; Belangrijkste Bijdragen, item 1).  They print
+no backward formulas; each step below is the derivative of the matching
+forward step in ``dash_oracle``, taken in reverse order:
+
+  phase 2  o = sum_j P_j v_j, P = softmax(s <q, k_j> + b_j):
+           dv_j += P_j do;  dP_j = <do, v_j>;  D = <do, o>;
+           dS_j = P_j (dP_j - D);  dq += s sum_j dS_j k_j;  dk_j += s dS_j q;
+           db_c  = sum over the chunk's keys (and the group's heads) of dS
+  prior    b_c = sigma log w_bar_c on the active chunks: dw_bar_c = sigma db_c / w_bar_c
+  GQA      w_bar = mean over the G heads of p:  dp_q = dw_bar / G
+  entmax   the Jacobian of p = alpha-entmax(u) on the support (Peters,
+           Niculae & Martins 2019): dp/du = diag(r) - r r^T / sum(r),
+           r = p^(2 - alpha) on the support, 0 off it (alpha = 1: r = p)
+  logits   u_c = gamma s <q, k_bar_c>:  dq += gamma s sum_c du_c k_bar_c;
+           dk_bar_c += gamma s du_c q
+  phase 0  k_bar = sum_t pi_t k_t, pi = softmax(s <q_bar, k_t>):
+           dpi_t = <dk_bar, k_t>;  dz = pi (dpi - <pi, dpi>);
+           dk_t += pi_t dk_bar + s dz_t q_bar;  dq_bar += s sum_t dz_t k_t
+
+The support (the mask) is piecewise constant in the inputs, so it carries no
+gradient of its own: it enters only through p.  Rounding of summaries to the
+storage dtype is passed through as the identity.  The estimate_diagonal
+option is not covered.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .dash_oracle import (F64, _default_scale, _group_size, _row_keys_and_bias,
+                          route_position, route_sequence, softmax, summarize)
+
+
+def attention_backward_rows(q, k, v, mask, log_prior, B, scale, G, dout):
+    """Backward of phase 2 (``attention_rows``) for a given routing, all rows.
+
+    q/dout [L, Hq, D], k/v [L, Hkv, D], mask/log_prior [Hkv, L, S].
+    Returns dict(dq, dk, dv, dbias [Hkv, L, S] (the gradient of each active
+    routed chunk's bias, 0 elsewhere), delta [Hq, L] = <do, o>).
+    """
+    q = np.asarray(q, dtype=F64)
+    k = np.asarray(k, dtype=F64)
+    v = np.asarray(v, dtype=F64)
+    dout = np.asarray(dout, dtype=F64)
+    L, Hq, D = q.shape
+    Hkv = k.shape[1]
+    S = mask.shape[2]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dbias = np.zeros((Hkv, L, S), dtype=F64)
+    delta = np.zeros((Hq, L), dtype=F64)
+    for i in range(L):
+        for h in range(Hkv):
+            idx, bias = _row_keys_and_bias(i, B, mask[h, i], log_prior[h, i])
+            chunk = idx // B
+            for qh in range(h * G, (h + 1) * G):
+                p = softmax(scale * (k[idx, h, :] @ q[i, qh]) + bias)
+                o = p @ v[idx, h, :]
+                dp = v[idx, h, :] @ dout[i, qh]
+                dlt = float(dout[i, qh] @ o)
+                ds = p * (dp - dlt)
+                dq[i, qh] += scale * (ds @ k[idx, h, :])
+                dk[idx, h, :] += scale * np.outer(ds, q[i, qh])
+                dv[idx, h, :] += np.outer(p, dout[i, qh])
+                delta[qh, i] = dlt
+                routed = chunk < i // B
+                np.add.at(dbias[h, i], chunk[routed], ds[routed])
+    return dict(dq=dq, dk=dk, dv=dv, dbias=dbias, delta=delta)
+
+
+def entmax_backward(p, dp, alpha):
+    """du for p = alpha-entmax(u) (one row): J^T dp with the symmetric
+    Jacobian diag(r) - r r^T / sum(r), r = p^(2 - alpha) on the support."""
+    p = np.asarray(p, dtype=F64)
+    dp = np.asarray(dp, dtype=F64)
+    r = np.where(p > 0, p ** (2.0 - alpha), 0.0)
+    sr = r.sum()
+    if sr == 0.0:
+        return np.zeros_like(p)
+    return r * dp - r * (r @ dp) / sr
+
+
+def routing_backward(q, kbar, B, alpha, gamma, sigma, G, scale, dbias):
+    """Backward of the log-prior of ``route_sequence`` (b = sigma log w_bar on
+    the active chunks) to the queries and the summaries.
+
+    dbias [Hkv, L, S].  Returns dict(dq [L, Hq, D], dkbar [C, Hkv, D],
+    du [Hq, L, S] (zero past each row's routable chunks)).
+    """
+    q = np.asarray(q, dtype=F64)
+    kbar = np.asarray(kbar, dtype=F64)
+    L, Hq, D = q.shape
+    Hkv = kbar.shape[1]
+    S = dbias.shape[2]
+    dq = np.zeros_like(q)
+    dkbar = np.zeros_like(kbar)
+    du = np.zeros((Hq, L, S), dtype=F64)
+    gs = gamma * scale
+    for i in range(L):
+        n = i // B
+        if n == 0:
+            continue
+        for h in range(Hkv):
+            r = route_position(q[i, h * G:(h + 1) * G], kbar[:n, h, :], alpha, gamma, scale)
+            m = r["mask"]
+            dw = np.zeros(n, dtype=F64)
+            dw[m] = sigma * dbias[h, i, :n][m] / r["wbar"][m]
+            dp = dw / G
+            for g in range(G):
+                qh = h * G + g
+                d = entmax_backward(r["p"][g], dp, alpha)
+                du[qh, i, :n] = d
+                dq[i, qh] += gs * (d @ kbar[:n, h, :])
+                dkbar[:n, h, :] += gs * np.outer(d, q[i, qh])
+    return dict(dq=dq, dkbar=dkbar, du=du)
+
+
+def summarize_backward(k, qbar, B, dkbar):
+    """Backward of ``summarize`` (complete chunks only).
+
+    Returns dict(dk [L, Hkv, D], dqbar [Hkv, D])."""
+    k = np.asarray(k, dtype=F64)
+    qbar = np.asarray(qbar, dtype=F64)
+    dkbar = np.asarray(dkbar, dtype=F64)
+    L, Hkv, D = k.shape
+    s = 1.0 / math.sqrt(D)
+    dk = np.zeros_like(k)
+    dqbar = np.zeros_like(qbar)
+    for c in range(L // B):
+        for h in range(Hkv):
+            keys = k[c * B:(c + 1) * B, h, :]
+            pi = softmax(s * (keys @ qbar[h]))
+            dpi = keys @ dkbar[c, h]
+            dz = pi * (dpi - pi @ dpi)
+            dk[c * B:(c + 1) * B, h, :] += np.outer(pi, dkbar[c, h]) + s * np.outer(dz, qbar[h])
+            dqbar[h] += s * (dz @ keys)
+    return dict(dk=dk, dqbar=dqbar)
+
+
+def prefill_backward(q, k, v, qbar, B, alpha, gamma, sigma, dout, enable_gqa=True,
+                     scale=None):
+    """Gradients of sum(dout * o) for the causal prefill of one sequence
+    (``dash_oracle.prefill`` without storage rounding) with respect to q, k,
+    v and q_bar, plus the intermediate gradients of the stages.
+
+    Returns dict(dq, dk, dv, dqbar, dbias, dkbar, du, delta, out, lse, mask,
+    log_prior)."""
+    from .dash_oracle import attention_rows
+
+    q = np.asarray(q, dtype=F64)
+    k = np.asarray(k, dtype=F64)
+    v = np.asarray(v, dtype=F64)
+    L, Hq, D = q.shape
+    Hkv = k.shape[1]
+    G = _group_size(Hq, Hkv, enable_gqa)
+    s = _default_scale(D, scale)
+    kbar = summarize(k, qbar, B)
+    mask, logp, _ = route_sequence(q, kbar, B, alpha, gamma, sigma, G, s)
+    out, lse = attention_rows(q, k, v, mask, logp, B, s, G, list(range(L)))
+    a = attention_backward_rows(q, k, v, mask, logp, B, s, G, dout)
+    r = routing_backward(q, kbar, B, alpha, gamma, sigma, G, s, a["dbias"])
+    m = summarize_backward(k, qbar, B, r["dkbar"])
+    return dict(dq=a["dq"] + r["dq"], dk=a["dk"] + m["dk"], dv=a["dv"], dqbar=m["dqbar"],
+                dbias=a["dbias"], dkbar=r["dkbar"], du=r["du"], delta=a["delta"],
+                out=out, lse=lse, mask=mask, log_prior=logp)
