@@ -79,7 +79,8 @@ typedef enum {
   DASH_OP_DECODE = 3,
   DASH_OP_SPARSE = 4,
   DASH_OP_DECODE_SPARSE = 5,
-  DASH_OP_ROUTE_DECODE = 6     /* dash_route_topk on decode rows */
+  DASH_OP_ROUTE_DECODE = 6,    /* dash_route_topk on decode rows */
+  DASH_OP_BACKWARD = 7         /* dash_attn_sparse_backward */
 } dash_op;
 
 typedef struct {
@@ -306,6 +307,34 @@ dash_status dash_attn_decode_sparse(const dash_shape* shape, const void* q,
                                     const float* log_prior, float softmax_scale,
                                     int enable_gqa, void* out, float* lse, void* workspace,
                                     size_t workspace_bytes, void* stream);
+
+/* Backward of phase 2 for a given routing: the gradients of sum(dout * out)
+ * for out = dash_attn_sparse(q, k, v, active_blocks, log_prior), with respect
+ * to q, k, v and to the log-prior of every active routed chunk.  The pages
+ * make the whole hierarchy differentiable (alpha-entmax instead of top-k lets
+ * gradients reach the routing: "Technische Samenvatting: DashAttention",
+ * Fase 1, Differentieerbaarheid bullet); for the attention step this is the
+ * derivative of the softmax with an additive bias:
+ *     P = softmax(s q k^T + b),  D_i = <dO_i, O_i>,  dS = P (dO v^T - D),
+ *     dq = s dS k,  dk = s dS^T q,  dv = P^T dO,
+ *     dbias[h,i,c] = sum over the chunk's keys and the group's heads of dS.
+ * bf16 inputs, GQA group 16 or 32, cu_seqlens = NULL; anything else returns
+ * DASH_ERR_UNSUPPORTED.
+ *   q, k, v, active_blocks, log_prior  as in dash_attn_sparse   (input)
+ *   out            [T, Hq, D] dtype    (input: the forward output)
+ *   dout           [T, Hq, D] dtype    (input)
+ *   lse            [Hq, T] fp32        (input: the forward's LSE)
+ *   dq             [T, Hq, D] dtype    (output)
+ *   dk, dv         [T, Hkv, D] dtype   (output)
+ *   dbias          [Hkv, T, C_slots] fp32 (output; 0 off the active routed chunks)
+ * Workspace: dash_workspace_size(DASH_OP_BACKWARD, shape). */
+dash_status dash_attn_sparse_backward(const dash_shape* shape, const void* q, const void* k,
+                                      const void* v, const void* out, const void* dout,
+                                      const float* lse, const uint64_t* active_blocks,
+                                      const float* log_prior, float softmax_scale,
+                                      int enable_gqa, void* dq, void* dk, void* dv,
+                                      float* dbias, void* workspace, size_t workspace_bytes,
+                                      void* stream);
 
 /* Workspace bytes that `op` needs for `shape` (0 when none); the same
  * enable_gqa / optional-output choices do not change it. */

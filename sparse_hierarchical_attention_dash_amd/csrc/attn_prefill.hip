@@ -429,6 +429,15 @@ __device__ __forceinline__ void lds_dma4(const void* gptr, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+// The same with a wave-uniform 64-bit base (SGPRs) and a 32-bit per-lane byte
+// offset: address = sbase + voff.
+__device__ __forceinline__ void lds_dma16s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_base), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+
 // LDS byte offset of a __shared__ object (a compile-time constant for the
 // ring's static arrays).
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -831,6 +840,297 @@ __global__ __launch_bounds__(kRingThreads, 1) void prefill_attn_ring_kernel(
   }
 }
 
+// ---------------------------------------------------------------- backward: dQ
+
+// Backward of phase 2 for the queries, G >= 16, bf16 (the derivative of the
+// prior-induced softmax attention: dS = P (dP - D), dQ = s dS K, and each
+// routed chunk's bias gradient, the sum of dS over its keys and the group's
+// heads).  The layout of work follows the forward ring kernel: 16 row tiles
+// per workgroup (two per wave) walk the union of their positions' active
+// blocks and the diagonal.  A block's K rows, V rows (both in the K layout)
+// and K^T rows (from the transposed-K workspace, in the V^T layout) are staged
+// in LDS, double-buffered, by plain vector loads.  Visit of an active tile:
+// S^T = K Q^T and dP^T = V dO^T (16 MFMAs each), P^T = exp2(s S^T + b - LSE)
+// from the forward's LSE, dS^T = P^T (dP^T - D) with D = <dO, O>, the tile's
+// bias gradient sum(dS^T) added to dbias, and dQ^T += K^T dS^T (16 MFMAs).
+// dQ (times s) is written in fp32 for the routing backward to add to.
+// Blocks are staged by direct global->LDS loads (the swizzle applied on the
+// source side), one block ahead, with a full vmcnt wait before each barrier.
+constexpr int kBqWaves = 8;
+constexpr int kBqThreads = 64 * kBqWaves;
+constexpr int kBqTiles = 2 * kBqWaves;
+
+template <int D>
+__global__ __launch_bounds__(kBqThreads, 1) void bwd_dq_kernel(Geom g, BwdParams p, TileGeom tg) {
+  constexpr int NTH = kBqThreads;
+  using R = RingCfg<D>;
+  constexpr int KS = D / 32;
+  constexpr int DT = D / 16;
+  constexpr int KB = R::KBYTES;           // K rows; V rows follow, then K^T rows
+  constexpr int SB = 2 * KB + R::VBYTES;  // bytes of one staged block
+  constexpr int NPC = SB / (16 * NTH);    // 16-byte pieces per thread
+  static_assert(NPC * 16 * NTH == SB, "a block splits into whole pieces");
+  __shared__ __attribute__((aligned(1024))) uint8_t stage[2][SB];
+  __shared__ unsigned long long Umask[32];
+  __shared__ int Wpref[33];
+  __shared__ uint16_t Blist[2048];
+  __shared__ uint16_t Act[2048];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, gq = lane >> 4;
+  const int tile = tg.tiles_per_seq - 1 - (int)blockIdx.x;
+  const int s = blockIdx.y, h = blockIdx.z;
+  const SeqInfo si = seq_info(g.cu_seqlens, nullptr, s, g.max_seqlen, g.B);
+  const int p0 = tile * tg.P;
+  if (p0 >= si.len) return;
+  const int pend = min(p0 + tg.P, si.len);
+  const int npos = pend - p0;
+  const int cdiag = p0 / g.B;
+  const int64_t T = g.T;
+  const int W = g.W;
+  const unsigned long long* __restrict__ mask = (const unsigned long long*)p.mask;
+
+  int tpos[2], rpos[2], rhead[2];
+  bool rvalid[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int ti = 2 * wv + u;
+    tpos[u] = ti / tg.HT;
+    rpos[u] = p0 + tpos[u];
+    rhead[u] = (ti % tg.HT) * 16 + r;
+    rvalid[u] = rpos[u] < pend;
+  }
+  // Q and dO operands (B of S^T = K Q^T and dP^T = V dO^T), the forward's LSE
+  // and D = <dO, O> of the lane's head, in log2 units where they meet exp2
+  bf16x8 qa[2][KS], da[2][KS];
+  float lse2[2], dlt[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int64_t tok = si.start + min(rpos[u], pend - 1);
+    const int64_t row = (tok * g.Hq + h * g.G + rhead[u]) * (int64_t)D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+      if (rvalid[u]) {
+        a = ldg16((const uint16_t*)p.q + row + 32 * ks + 8 * gq);
+        b = ldg16((const uint16_t*)p.dout + row + 32 * ks + 8 * gq);
+      }
+      qa[u][ks] = as_bf16x8(a);
+      da[u][ks] = as_bf16x8(b);
+    }
+    const int64_t hr = (int64_t)(h * g.G + rhead[u]) * T + tok;
+    lse2[u] = p.lse[hr] * kLog2e;
+    dlt[u] = p.delta[hr];
+  }
+
+  // ---- the union of the positions' active chunks and their bitmap (as in
+  // the forward kernel)
+  if (tid < 32) Umask[tid] = 0ull;
+  __syncthreads();
+  const unsigned long long* mbase = mask + ((int64_t)h * T + si.start + p0) * W;
+  for (int idx = tid; idx < npos * W; idx += NTH) {
+    const int w = idx % W;
+    const unsigned long long v = mbase[idx] & routable_bits(w, cdiag);
+    if (v) atomicOr(&Umask[w], v);
+  }
+  __syncthreads();
+  if (tid < 64) {
+    int cnt = (tid < W) ? __popcll(Umask[tid]) : 0;
+    int inc = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o);
+      if (lane >= o) inc += y;
+    }
+    if (tid < 33) Wpref[tid] = inc - cnt;
+  }
+  __syncthreads();
+  if (tid < W) {
+    unsigned long long v = Umask[tid];
+    int o = Wpref[tid];
+    while (v) {
+      Blist[o++] = (uint16_t)(tid * 64 + __ffsll(v) - 1);
+      v &= v - 1;
+    }
+  }
+  __syncthreads();
+  const int nlist = Wpref[W];
+  for (int j = tid; j < nlist; j += NTH) {
+    const int c = Blist[j];
+    uint32_t bits = 0;
+    for (int t = 0; t < npos; ++t)
+      bits |= (uint32_t)((mbase[t * W + (c >> 6)] >> (c & 63)) & 1ull) << t;
+    Act[j] = (uint16_t)bits;
+  }
+  __syncthreads();
+  const int sbl = g.B == 128 ? 1 : 0;
+  const int nrouted = nlist << sbl;
+  const int ndiag = (pend - cdiag * g.B + 63) / 64;
+  const int NS = nrouted + ndiag;
+
+  // ---- staging: segment i of this wave is the 1 KB at (8 i + wv) KB of
+  // the block; lane l fills its 16 bytes at l * 16, from the source piece that
+  // the swizzled layout puts there (K and V rows in the K layout, K^T rows in
+  // the V^T layout)
+  const int kmax = pend - 1;  // last key of the sequence this workgroup may see
+  const uint8_t* kb8 = (const uint8_t*)p.k + (si.start * (int64_t)g.Hkv + h) * D * 2;
+  const uint8_t* vb8 = (const uint8_t*)p.v + (si.start * (int64_t)g.Hkv + h) * D * 2;
+  const uint8_t* tb8 = (const uint8_t*)p.kt + (((int64_t)h * D) * p.Tp + pad_off(g, s)) * 2;
+  auto block_key0 = [&](int sx) -> int {
+    return sx < nrouted ? (int)Blist[sx >> sbl] * g.B + ((sx & sbl) << 6)
+                        : cdiag * g.B + ((sx - nrouted) << 6);
+  };
+  const uint32_t krs = (uint32_t)(g.Hkv * D * 2);  // bytes between consecutive keys
+  const uint32_t trs = (uint32_t)(p.Tp * 2);        // bytes between K^T rows
+  auto sload = [&](int sx, int buf) {
+    const int key0 = block_key0(sx);
+    const uint32_t base = lds_addr(&stage[buf][0]);
+#pragma unroll
+    for (int i = 0; i < NPC; ++i) {
+      const int seg = 8 * i + wv;  // wave-uniform: the segment lies in one region
+      const int o = seg * 1024 + lane * 16;
+      if (seg * 1024 < 2 * KB) {
+        const int ok = o % KB;
+        const int kr = ok / R::KROW;
+        const int pc = ((ok % R::KROW) / 16) ^ swz<R::KP>(kr);
+        const uint32_t key = (uint32_t)min(key0 + kr, kmax);
+        lds_dma16s(seg * 1024 < KB ? kb8 : vb8, key * krs + (uint32_t)(pc * 16),
+                   base + (uint32_t)(seg * 1024));
+      } else {
+        const int ot = o - 2 * KB;
+        const int d = ot / R::VROW;
+        const int pc = ((ot % R::VROW) / 16) ^ swz<8>(d);
+        lds_dma16s(tb8, (uint32_t)d * trs + (uint32_t)(key0 * 2 + pc * 16),
+                   base + (uint32_t)(seg * 1024));
+      }
+    }
+  };
+
+  f32x4 o[2][DT];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float sl2 = p.scale * kLog2e;
+  int koff[KS], voff[2];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = r * R::KROW + (((4 * ks + gq) ^ swz<R::KP>(r)) * 16);
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) voff[s2] = r * R::VROW + (((4 * s2 + gq) ^ swz<8>(r)) * 16);
+  float* dbias = p.dbias;
+
+  // one tile's visit of the staged block kv; returns the tile's sum of dS
+  auto visit = [&](auto masked_tag, auto u_tag, lds_u8* kv, float bz, int kbase0) -> float {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    constexpr int U = decltype(u_tag)::value;
+    f32x4 sacc[4], pacc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      pacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 f[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) f[t] = lds_read16(kv + koff[ks] + 16 * t * R::KROW);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) sacc[t] = mfma16x16x32(as_bf16x8(f[t]), qa[U][ks], sacc[t]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) f[t] = lds_read16(kv + KB + koff[ks] + 16 * t * R::KROW);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) pacc[t] = mfma16x16x32(as_bf16x8(f[t]), da[U][ks], pacc[t]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    uint32_t pk[4][2];
+    float dsum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float ds[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float pv = __builtin_amdgcn_exp2f(fmaf(sacc[t][j], sl2, bz - lse2[U]));
+        if constexpr (MASKED) pv = kbase0 + 16 * t + j <= rpos[U] ? pv : 0.f;
+        ds[j] = pv * (pacc[t][j] - dlt[U]);
+        dsum += ds[j];
+      }
+      pk[t][0] = cvt_pk_bf16(ds[0], ds[1]);
+      pk[t][1] = cvt_pk_bf16(ds[2], ds[3]);
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const u32x4 pb = {pk[2 * s2][0], pk[2 * s2][1], pk[2 * s2 + 1][0], pk[2 * s2 + 1][1]};
+#pragma unroll
+      for (int d0 = 0; d0 < DT; d0 += 4) {
+        u32x4 a[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          a[i] = lds_read16(kv + 2 * KB + voff[s2] + 16 * (d0 + i) * R::VROW);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          o[U][d0 + i] = mfma16x16x32(as_bf16x8(a[i]), as_bf16x8(pb), o[U][d0 + i]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // the tile's sum of dS over its 16 heads and the block's keys
+    dsum = row16_sum(dsum);
+    dsum += xor16(dsum);
+    dsum += xor32(dsum);
+    return dsum;
+  };
+  using F = std::false_type;
+  using Tr = std::true_type;
+  using U0 = std::integral_constant<int, 0>;
+  using U1 = std::integral_constant<int, 1>;
+
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4));  // operand and mask reads done
+  sload(0, 0);
+  for (int st = 0; st < NS; ++st) {
+    const int buf = st & 1;
+    // this block's loads landed, every wave is done with the other buffer
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (st + 1 < NS) sload(st + 1, buf ^ 1);
+    lds_u8* kv = (lds_u8*)&stage[buf][0];
+    if (st < nrouted) {
+      const int c = Blist[st >> sbl];
+      const uint32_t act = Act[st >> sbl];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (!(rvalid[u] && ((act >> tpos[u]) & 1u))) continue;
+        const int64_t brow = ((int64_t)h * T + si.start + rpos[u]) * g.C_slots + c;
+        const float bz = p.log_prior[brow] * kLog2e;
+        const float d = u == 0 ? visit(F(), U0(), kv, bz, 0) : visit(F(), U1(), kv, bz, 0);
+        if (lane == 0) atomicAdd(&dbias[brow], d);
+      }
+    } else {
+      const int key0 = cdiag * g.B + ((st - nrouted) << 6);
+      if (rvalid[0]) visit(Tr(), U0(), kv, 0.f, key0 + 4 * gq);
+      if (rvalid[1]) visit(Tr(), U1(), kv, 0.f, key0 + 4 * gq);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4));  // no staging load outlives the kernel
+
+  // dQ = s dQ^T^T, fp32: lane (gq, r) holds dims 16 dt + 4 gq .. +3 of head r
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    if (!rvalid[u]) continue;
+    const int64_t tok = si.start + rpos[u];
+    float* drow = p.dq + (tok * g.Hq + h * g.G + rhead[u]) * (int64_t)D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      f32x4 w = o[u][dt];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] *= p.scale;
+      *reinterpret_cast<f32x4*>(drow + 16 * dt + 4 * gq) = w;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- fp32 rows
 
 template <int D>
@@ -944,6 +1244,29 @@ static TileGeom make_ring_tiles(const Geom& g) {
 }
 
 bool prefill_uses_ring(const Geom& g) { return g.bf16 && g.G >= 16 && g.G <= 256; }
+
+hipError_t launch_vt_transpose(const Geom& g, const void* src, void* dst, int64_t Tp,
+                               hipStream_t st) {
+  dim3 tgrid((g.max_seqlen + 63) / 64, g.num_seqs, g.Hkv);
+  if (g.D == 64)
+    hipLaunchKernelGGL(vt_transpose_kernel<64>, tgrid, dim3(256), 0, st, g,
+                       (const uint16_t*)src, (uint16_t*)dst, Tp);
+  else
+    hipLaunchKernelGGL(vt_transpose_kernel<128>, tgrid, dim3(256), 0, st, g,
+                       (const uint16_t*)src, (uint16_t*)dst, Tp);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const Geom& g, const BwdParams& p, hipStream_t st) {
+  if (g.T == 0) return hipSuccess;
+  const TileGeom rg = make_ring_tiles(g);
+  dim3 grid(rg.tiles_per_seq, g.num_seqs, g.Hkv);
+  if (g.D == 64)
+    hipLaunchKernelGGL(bwd_dq_kernel<64>, grid, dim3(kBqThreads), 0, st, g, p, rg);
+  else
+    hipLaunchKernelGGL(bwd_dq_kernel<128>, grid, dim3(kBqThreads), 0, st, g, p, rg);
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill_attn(const Geom& g, const PrefillParams& p, hipStream_t st) {
   if (g.T == 0) return hipSuccess;

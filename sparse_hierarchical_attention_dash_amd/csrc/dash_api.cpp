@@ -174,6 +174,29 @@ RouteDecodeWs route_decode_ws(const Geom& g) {
   w.total = o;
   return w;
 }
+// Backward of phase 2: K^T, D = <dO, O>, and fp32 dQ / dK / dV.
+struct BackwardWs {
+  size_t kt, delta, dq, dk, dv, total;
+};
+BackwardWs backward_ws(const Geom& g) {
+  BackwardWs w{};
+  size_t o = 0;
+  w.kt = o;
+  o += align_up((size_t)g.Hkv * g.D * dash::padded_tokens(g.T, g.num_seqs) * 2);
+  w.delta = o;
+  o += align_up((size_t)g.Hq * g.T * 4);
+  w.dq = o;
+  o += align_up((size_t)g.T * g.Hq * g.D * 4);
+  w.dk = o;
+  o += align_up((size_t)g.T * g.Hkv * g.D * 4);
+  w.dv = o;
+  o += align_up((size_t)g.T * g.Hkv * g.D * 4);
+  w.total = o;
+  return w;
+}
+bool backward_supported(const Geom& g) {
+  return g.bf16 && (g.G == 16 || g.G == 32) && !g.cu_seqlens;
+}
 // Decode attention on a given routing: the split partials only.
 struct DecodeSparseWs {
   size_t acc, ml, total;
@@ -246,6 +269,7 @@ size_t dash_workspace_size(int op, const dash_shape* shape) {
     case DASH_OP_SPARSE: return sparse_ws(g).total;
     case DASH_OP_DECODE_SPARSE: return decode_sparse_ws(g).total;
     case DASH_OP_ROUTE_DECODE: return route_decode_ws(g).total;
+    case DASH_OP_BACKWARD: return backward_ws(g).total;
   }
   return 0;
 }
@@ -538,6 +562,55 @@ dash_status dash_cache_append(const dash_shape* shape, const void* k_new, const 
   if (g.max_seqlen == 0) return DASH_ERR_INVALID_ARGUMENT;
   DASH_HIP(dash::launch_cache_append(g, k_new, v_new, seqlens, qbar, k_cache, v_cache,
                                      kbar_cache, static_cast<hipStream_t>(stream)));
+  return DASH_OK;
+}
+
+dash_status dash_attn_sparse_backward(const dash_shape* shape, const void* q, const void* k,
+                                      const void* v, const void* out, const void* dout,
+                                      const float* lse, const uint64_t* active_blocks,
+                                      const float* log_prior, float softmax_scale,
+                                      int enable_gqa, void* dq, void* dk, void* dv,
+                                      float* dbias, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  Geom g;
+  dash_status st = check_shape(shape, enable_gqa, false, g);
+  if (st != DASH_OK) return st;
+  if (std::isnan(softmax_scale)) return DASH_ERR_INVALID_ARGUMENT;
+  if (g.T > 0 && !backward_supported(g)) return DASH_ERR_UNSUPPORTED;
+  const BackwardWs w = backward_ws(g);
+  if ((st = check_ws(workspace, workspace_bytes, w.total)) != DASH_OK) return st;
+  if (g.T == 0 || g.num_seqs == 0) return DASH_OK;
+  if (!q || !k || !v || !out || !dout || !lse || !active_blocks || !log_prior || !dq || !dk ||
+      !dv || !dbias)
+    return DASH_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(dbias))
+    return DASH_ERR_INVALID_ARGUMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  dash::BwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.kt = at(workspace, w.kt);
+  p.Tp = dash::padded_tokens(g.T, g.num_seqs);
+  p.dout = dout;
+  p.lse = lse;
+  p.delta = reinterpret_cast<float*>(at(workspace, w.delta));
+  p.mask = active_blocks;
+  p.log_prior = log_prior;
+  p.scale = eff_scale(g, softmax_scale);
+  p.dq = reinterpret_cast<float*>(at(workspace, w.dq));
+  p.dbias = dbias;
+  float* dkw = reinterpret_cast<float*>(at(workspace, w.dk));
+  float* dvw = reinterpret_cast<float*>(at(workspace, w.dv));
+  DASH_HIP(dash::launch_vt_transpose(g, k, at(workspace, w.kt), p.Tp, s));
+  DASH_HIP(dash::launch_bwd_delta(g, out, dout, reinterpret_cast<float*>(at(workspace, w.delta)), s));
+  DASH_HIP(dash::launch_zero(dbias, (int64_t)g.Hkv * g.T * g.C_slots, s));
+  DASH_HIP(dash::launch_bwd_dq(g, p, s));
+  DASH_HIP(dash::launch_bwd_dkdv(g, p, dkw, dvw, s));
+  DASH_HIP(dash::launch_to_bf16(p.dq, dq, g.T * g.Hq * g.D, s));
+  DASH_HIP(dash::launch_to_bf16(dkw, dk, g.T * g.Hkv * g.D, s));
+  DASH_HIP(dash::launch_to_bf16(dvw, dv, g.T * g.Hkv * g.D, s));
   return DASH_OK;
 }
 

@@ -90,6 +90,32 @@ hipError_t launch_prefill_attn(const Geom& g, const PrefillParams& p, hipStream_
 // True when launch_prefill_attn runs the V^T + LDS-ring path (needs p.vt).
 bool prefill_uses_ring(const Geom& g);
 
+// Backward of phase 2 for a given routing (bf16, G >= 16).
+struct BwdParams {
+  const void* q = nullptr;              // [T, Hq, D]
+  const void* k = nullptr;              // [T, Hkv, D]
+  const void* v = nullptr;
+  const void* kt = nullptr;             // K^T workspace [Hkv, D, Tp] (the V^T layout)
+  int64_t Tp = 0;
+  const void* dout = nullptr;           // [T, Hq, D]
+  const float* lse = nullptr;           // [Hq, T] natural log, from the forward
+  const float* delta = nullptr;         // [Hq, T] <dO, O>
+  const uint64_t* mask = nullptr;       // [Hkv, T, W]
+  const float* log_prior = nullptr;     // [Hkv, T, C_slots]
+  float scale = 0.f;
+  float* dq = nullptr;                  // [T, Hq, D] fp32 (written)
+  float* dbias = nullptr;               // [Hkv, T, C_slots] fp32 (accumulated; zeroed first)
+};
+hipError_t launch_bwd_dq(const Geom& g, const BwdParams& p, hipStream_t st);
+hipError_t launch_bwd_delta(const Geom& g, const void* out, const void* dout, float* delta,
+                            hipStream_t st);
+hipError_t launch_bwd_dkdv(const Geom& g, const BwdParams& p, float* dk, float* dv,
+                           hipStream_t st);
+hipError_t launch_to_bf16(const float* src, void* dst, int64_t n, hipStream_t st);
+hipError_t launch_zero(float* x, int64_t n, hipStream_t st);
+hipError_t launch_vt_transpose(const Geom& g, const void* src, void* dst, int64_t Tp,
+                               hipStream_t st);
+
 // K2d + K4: split-K decode attention and the combine of the partials.
 struct DecodeParams {
   const void* q = nullptr;              // [batch, Hq, D]

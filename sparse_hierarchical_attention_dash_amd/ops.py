@@ -210,6 +210,29 @@ def attn_prefill(q, k, v, qbar, chunk_size, *, alpha=1.5, gamma=1.0, sigma=1.0,
     return out, lse, ab
 
 
+def attn_sparse_backward(q, k, v, out, dout, lse, active_blocks, log_prior, chunk_size, *,
+                         softmax_scale=0.0, enable_gqa=True, workspace=None):
+    """Backward of attn_sparse: returns (dq, dk, dv, dbias [Hkv, T, C_slots])."""
+    _need_cuda(q, k, v, out, dout, lse, active_blocks, log_prior)
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    shape = _seq_shape(q, Hq, Hkv, chunk_size, None, None)
+    lay = L.layout(shape, enable_gqa)
+    dev = q.device
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dbias = torch.empty((Hkv, T, lay.chunk_slots), dtype=torch.float32, device=dev)
+    n = L.workspace_size(L.DASH_OP_BACKWARD, shape)
+    if workspace is None or workspace.numel() < n:
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    L.check("dash_attn_sparse_backward", L.lib().dash_attn_sparse_backward(
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+        _ptr(active_blocks), _ptr(log_prior), float(softmax_scale), int(enable_gqa), _ptr(dq),
+        _ptr(dk), _ptr(dv), _ptr(dbias), _ptr(workspace), n, _stream(dev)))
+    return dq, dk, dv, dbias
+
+
 def attn_sparse(q, k, v, active_blocks, log_prior, chunk_size, *, softmax_scale=0.0,
                 enable_gqa=True, cu_seqlens=None, max_seqlen=None, return_lse=False,
                 out=None, workspace=None):

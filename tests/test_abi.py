@@ -259,3 +259,27 @@ def test_cache_append_checks(lib):
         L.DASH_ERR_INVALID_ARGUMENT                                   # no cu_seqlens
     assert ap(L.make_shape(4, 4096, 4, None, 32, 2, 96, 64, BF16)) == L.DASH_ERR_UNSUPPORTED
     assert ap(L.make_shape(0, 4096, 0, None, 32, 2, 128, 64, BF16)) == L.DASH_OK
+
+
+def test_sparse_backward_checks(lib):
+    s = shape()
+    need = L.workspace_size(L.DASH_OP_BACKWARD, s)
+    assert need > 0
+
+    def bw(sh, **kw):
+        a = dict(q=A, k=A, v=A, o=A, do=A, lse=A, m=A, lp=A, dq=A, dk=A, dv=A, db=A, ws=A,
+                 n=need, gqa=1)
+        a.update(kw)
+        return lib.dash_attn_sparse_backward(ctypes.byref(sh), a["q"], a["k"], a["v"], a["o"],
+                                             a["do"], a["lse"], a["m"], a["lp"], 0.0, a["gqa"],
+                                             a["dq"], a["dk"], a["dv"], a["db"], a["ws"], a["n"],
+                                             None)
+
+    for key in ("q", "k", "v", "o", "do", "lse", "m", "lp", "dq", "dk", "dv", "db"):
+        assert bw(s, **{key: None}) == L.DASH_ERR_INVALID_ARGUMENT, key
+    assert bw(s, dk=A + 8) == L.DASH_ERR_INVALID_ARGUMENT
+    assert bw(s, n=need - 1) == L.DASH_ERR_WORKSPACE_TOO_SMALL
+    assert bw(shape(Hq=8, Hkv=2)) == L.DASH_ERR_UNSUPPORTED            # group of 4
+    assert bw(shape(dtype=F32, Hq=32, Hkv=2)) == L.DASH_ERR_UNSUPPORTED
+    assert bw(shape(cu=A, num_seqs=3)) == L.DASH_ERR_UNSUPPORTED       # varlen
+    assert bw(shape(T=0, num_seqs=0, max_seqlen=0)) == L.DASH_OK
