@@ -411,6 +411,30 @@ def main():
             t_droute = time_it(stream, lambda: ops.route(
                 q, kbar, wp.Hkv, wp.B, alpha=wp.alpha, gamma=wp.gamma, sigma=wp.sigma,
                 mask_out=m2, log_prior_out=l2, log_prior=True, workspace=ws_route, kdiag=kd), reps)
+            # backward: the whole prefill backward (routing recomputed, attention,
+            # prior, entmax routing and summaries), and, for scale, phase 2's
+            # backward alone over every chunk (dense causal attention backward)
+            dout = torch.randn_like(q)
+            o_b, lse_b, _ = ops.attn_prefill(q, k, v, qbar, wp.B, alpha=wp.alpha, gamma=wp.gamma,
+                                             sigma=wp.sigma, return_lse=True)
+            ws_pb = torch.empty(L.workspace_size(L.DASH_OP_PREFILL_BACKWARD, shp),
+                                dtype=torch.uint8, device=dev)
+            t_bwd = time_it(stream, lambda: ops.attn_prefill_backward(
+                q, k, v, qbar, o_b, dout, lse_b, wp.B, alpha=wp.alpha, gamma=wp.gamma,
+                sigma=wp.sigma, workspace=ws_pb), reps)
+            ops.route(q, kbar, wp.Hkv, wp.B, alpha=1.0, gamma=wp.gamma, sigma=0.0,
+                      mask_out=m2, log_prior_out=l2, log_prior=True, workspace=ws_route)
+            o_d, lse_d = ops.attn_sparse(q, k, v, m2, l2, wp.B, return_lse=True)
+            t_dbwd = time_it(stream, lambda: ops.attn_sparse_backward(
+                q, k, v, o_d, dout, lse_d, m2, l2, wp.B), reps)
+            del ws_pb, o_b, lse_b, o_d, lse_d, dout
+            # the usual count of an attention backward: 2.5 times the forward's
+            # products (S, dP, dV, dQ, dK; S is recomputed)
+            cmp["backward"] = {
+                "dash_ms": t_bwd, "dense_attention_ms": t_dbwd,
+                "dash_tflops": 2.5 * flops / (t_bwd * 1e-3) / 1e12,
+                "dense_tflops": 2.5 * dense_flops / (t_dbwd * 1e-3) / 1e12,
+                "speedup_vs_dense": t_dbwd / t_bwd}
             cmp["estimate_diagonal"] = {
                 "prefill_ms": t_diag, "diag_summary_ms": t_dsum, "route_ms": t_droute,
                 "active_blocks": int(pop_dg.sum()), "tflops": flops_dg / (t_diag * 1e-3) / 1e12}

@@ -80,7 +80,8 @@ typedef enum {
   DASH_OP_SPARSE = 4,
   DASH_OP_DECODE_SPARSE = 5,
   DASH_OP_ROUTE_DECODE = 6,    /* dash_route_topk on decode rows */
-  DASH_OP_BACKWARD = 7         /* dash_attn_sparse_backward */
+  DASH_OP_BACKWARD = 7,        /* dash_attn_sparse_backward */
+  DASH_OP_PREFILL_BACKWARD = 8 /* dash_attn_prefill_backward */
 } dash_op;
 
 typedef struct {
@@ -335,6 +336,32 @@ dash_status dash_attn_sparse_backward(const dash_shape* shape, const void* q, co
                                       int enable_gqa, void* dq, void* dk, void* dv,
                                       float* dbias, void* workspace, size_t workspace_bytes,
                                       void* stream);
+
+/* Backward of the whole causal prefill (dash_attn_prefill): the gradients of
+ * sum(dout * out) with respect to q, k, v and q_bar, through the attention,
+ * the log-prior, the GQA mean, the alpha-entmax routing and the phase-0
+ * summaries.  This is the differentiable path the pages build the method on
+ * (alpha-entmax in place of top-k lets the attention's gradient reach the
+ * routing and the summaries: "Technische Samenvatting: DashAttention", Fase 1,
+ * Differentieerbaarheid bullet; Belangrijkste Bijdragen, item 1).  The routing
+ * is recomputed from the inputs; the mask is piecewise constant and carries no
+ * gradient of its own; bf16 rounding of the summaries passes gradients
+ * unchanged.  The support: as dash_attn_sparse_backward.
+ *   q, k, v, qbar, alpha, gamma, sigma, softmax_scale, enable_gqa
+ *                  as in dash_attn_prefill (input)
+ *   out, lse       the forward's output and LSE (input)
+ *   dout           [T, Hq, D] dtype    (input)
+ *   dq             [T, Hq, D] dtype    (output)
+ *   dk, dv         [T, Hkv, D] dtype   (output)
+ *   dqbar          [Hkv, D] fp32       (output)
+ * Workspace: dash_workspace_size(DASH_OP_PREFILL_BACKWARD, shape). */
+dash_status dash_attn_prefill_backward(const dash_shape* shape, const void* q, const void* k,
+                                       const void* v, const float* qbar, float alpha,
+                                       float gamma, float sigma, float softmax_scale,
+                                       int enable_gqa, const void* out, const void* dout,
+                                       const float* lse, void* dq, void* dk, void* dv,
+                                       float* dqbar, void* workspace, size_t workspace_bytes,
+                                       void* stream);
 
 /* Workspace bytes that `op` needs for `shape` (0 when none); the same
  * enable_gqa / optional-output choices do not change it. */

@@ -30,10 +30,12 @@ DASH_OP_SPARSE = 4
 DASH_OP_DECODE_SPARSE = 5
 DASH_OP_ROUTE_DECODE = 6
 DASH_OP_BACKWARD = 7
+DASH_OP_PREFILL_BACKWARD = 8
 
 EXPORTED = ("dash_get_layout", "dash_summarize", "dash_route", "dash_attn_prefill",
             "dash_attn_sparse", "dash_attn_decode", "dash_route_topk", "dash_attn_decode_sparse",
             "dash_cache_append", "dash_summarize_diagonal", "dash_attn_sparse_backward",
+            "dash_attn_prefill_backward",
             "dash_workspace_size", "dash_status_string", "dash_abi_version")
 
 
@@ -115,6 +117,9 @@ def lib():
     L.dash_attn_sparse_backward.restype = _I
     L.dash_attn_sparse_backward.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _P, _P, _P, _F, _I,
                                             _P, _P, _P, _P, _P, _SZ, _P]
+    L.dash_attn_prefill_backward.restype = _I
+    L.dash_attn_prefill_backward.argtypes = [_SHAPE, _P, _P, _P, _P, _F, _F, _F, _F, _I, _P,
+                                             _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
     L.dash_cache_append.restype = _I
     L.dash_cache_append.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _P, _P, _P]
     _lib = L

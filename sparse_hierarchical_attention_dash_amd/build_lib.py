@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libdash.so")
 
 SOURCES = ["dash_api.cpp", "summarize.hip", "route.hip", "attn_prefill.hip",
-           "attn_decode.hip", "attn_backward.hip"]
+           "attn_decode.hip", "attn_backward.hip", "route_backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("DASH_OFFLOAD_ARCH", "gfx950")

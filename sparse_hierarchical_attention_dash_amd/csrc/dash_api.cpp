@@ -194,6 +194,32 @@ BackwardWs backward_ws(const Geom& g) {
   w.total = o;
   return w;
 }
+// Whole prefill backward: the forward's routing recomputed (summaries, mask,
+// log-prior, thresholds), the phase-2 backward, the bias gradient and the
+// per-head terms of the routing backward.
+struct PrefillBwdWs {
+  BackwardWs a;
+  size_t kbar, mask, logp, tau, db, sc, total;
+};
+PrefillBwdWs prefill_bwd_ws(const Geom& g) {
+  PrefillBwdWs w{};
+  w.a = backward_ws(g);
+  size_t o = w.a.total;
+  w.kbar = o;
+  o += align_up((size_t)(g.T / g.B) * g.Hkv * g.D * elt(g));
+  w.mask = o;
+  o += align_up((size_t)g.Hkv * g.T * g.W * 8);
+  w.logp = o;
+  o += align_up((size_t)g.Hkv * g.T * g.C_slots * 4);
+  w.tau = o;
+  o += align_up((size_t)g.Hq * g.T * 4);
+  w.db = o;
+  o += align_up((size_t)g.Hkv * g.T * g.C_slots * 4);
+  w.sc = o;
+  o += align_up((size_t)g.Hq * g.T * 16);
+  w.total = o;
+  return w;
+}
 bool backward_supported(const Geom& g) {
   return g.bf16 && (g.G == 16 || g.G == 32) && !g.cu_seqlens;
 }
@@ -270,6 +296,7 @@ size_t dash_workspace_size(int op, const dash_shape* shape) {
     case DASH_OP_DECODE_SPARSE: return decode_sparse_ws(g).total;
     case DASH_OP_ROUTE_DECODE: return route_decode_ws(g).total;
     case DASH_OP_BACKWARD: return backward_ws(g).total;
+    case DASH_OP_PREFILL_BACKWARD: return prefill_bwd_ws(g).total;
   }
   return 0;
 }
@@ -608,6 +635,91 @@ dash_status dash_attn_sparse_backward(const dash_shape* shape, const void* q, co
   DASH_HIP(dash::launch_zero(dbias, (int64_t)g.Hkv * g.T * g.C_slots, s));
   DASH_HIP(dash::launch_bwd_dq(g, p, s));
   DASH_HIP(dash::launch_bwd_dkdv(g, p, dkw, dvw, s));
+  DASH_HIP(dash::launch_to_bf16(p.dq, dq, g.T * g.Hq * g.D, s));
+  DASH_HIP(dash::launch_to_bf16(dkw, dk, g.T * g.Hkv * g.D, s));
+  DASH_HIP(dash::launch_to_bf16(dvw, dv, g.T * g.Hkv * g.D, s));
+  return DASH_OK;
+}
+
+dash_status dash_attn_prefill_backward(const dash_shape* shape, const void* q, const void* k,
+                                       const void* v, const float* qbar, float alpha,
+                                       float gamma, float sigma, float softmax_scale,
+                                       int enable_gqa, const void* out, const void* dout,
+                                       const float* lse, void* dq, void* dk, void* dv,
+                                       float* dqbar, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  Geom g;
+  dash_status st = check_shape(shape, enable_gqa, false, g);
+  if (st != DASH_OK) return st;
+  if ((st = check_routing(alpha, gamma, sigma, softmax_scale)) != DASH_OK) return st;
+  if (g.T > 0 && !backward_supported(g)) return DASH_ERR_UNSUPPORTED;
+  const PrefillBwdWs w = prefill_bwd_ws(g);
+  if ((st = check_ws(workspace, workspace_bytes, w.total)) != DASH_OK) return st;
+  if (g.T == 0 || g.num_seqs == 0) return DASH_OK;
+  if (!q || !k || !v || !qbar || !out || !dout || !lse || !dq || !dk || !dv || !dqbar)
+    return DASH_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(qbar) || !aligned16(out) ||
+      !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      !aligned16(dqbar))
+    return DASH_ERR_INVALID_ARGUMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the forward's routing, recomputed
+  void* kbar = at(workspace, w.kbar);
+  uint64_t* mask = reinterpret_cast<uint64_t*>(at(workspace, w.mask));
+  float* logp = reinterpret_cast<float*>(at(workspace, w.logp));
+  float* tau = reinterpret_cast<float*>(at(workspace, w.tau));
+  DASH_HIP(dash::launch_summarize(g, k, qbar, kbar, s));
+  dash::RouteParams rp;
+  rp.q = q;
+  rp.kbar = kbar;
+  rp.alpha = alpha;
+  rp.gamma_scale = gamma * eff_scale(g, softmax_scale);
+  rp.sigma = sigma;
+  rp.mask = mask;
+  rp.log_prior = logp;
+  rp.tau = tau;
+  rp.rows = g.T;
+  DASH_HIP(dash::launch_route(g, rp, s));
+  // phase 2
+  dash::BwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.kt = at(workspace, w.a.kt);
+  p.Tp = dash::padded_tokens(g.T, g.num_seqs);
+  p.dout = dout;
+  p.lse = lse;
+  p.delta = reinterpret_cast<float*>(at(workspace, w.a.delta));
+  p.mask = mask;
+  p.log_prior = logp;
+  p.scale = eff_scale(g, softmax_scale);
+  p.dq = reinterpret_cast<float*>(at(workspace, w.a.dq));
+  p.dbias = reinterpret_cast<float*>(at(workspace, w.db));
+  float* dkw = reinterpret_cast<float*>(at(workspace, w.a.dk));
+  float* dvw = reinterpret_cast<float*>(at(workspace, w.a.dv));
+  DASH_HIP(dash::launch_vt_transpose(g, k, at(workspace, w.a.kt), p.Tp, s));
+  DASH_HIP(dash::launch_bwd_delta(g, out, dout, reinterpret_cast<float*>(at(workspace, w.a.delta)), s));
+  DASH_HIP(dash::launch_zero(p.dbias, (int64_t)g.Hkv * g.T * g.C_slots, s));
+  DASH_HIP(dash::launch_bwd_dq(g, p, s));
+  DASH_HIP(dash::launch_bwd_dkdv(g, p, dkw, dvw, s));
+  // phases 1 and 0
+  dash::RouteBwdParams rb;
+  rb.q = q;
+  rb.kbar = kbar;
+  rb.k = k;
+  rb.qbar = qbar;
+  rb.tau = tau;
+  rb.mask = reinterpret_cast<const unsigned long long*>(mask);
+  rb.db = p.dbias;
+  rb.sc = reinterpret_cast<float4*>(at(workspace, w.sc));
+  rb.dq = p.dq;
+  rb.dk = dkw;
+  rb.dqbar = dqbar;
+  rb.alpha = alpha;
+  rb.gamma_scale = rp.gamma_scale;
+  rb.sigma = sigma;
+  DASH_HIP(dash::launch_zero(dqbar, (int64_t)g.Hkv * g.D, s));
+  DASH_HIP(dash::launch_route_bwd(g, rb, s));
   DASH_HIP(dash::launch_to_bf16(p.dq, dq, g.T * g.Hq * g.D, s));
   DASH_HIP(dash::launch_to_bf16(dkw, dk, g.T * g.Hkv * g.D, s));
   DASH_HIP(dash::launch_to_bf16(dvw, dv, g.T * g.Hkv * g.D, s));

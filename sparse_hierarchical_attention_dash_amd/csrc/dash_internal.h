@@ -113,6 +113,25 @@ hipError_t launch_bwd_dkdv(const Geom& g, const BwdParams& p, float* dk, float* 
                            hipStream_t st);
 hipError_t launch_to_bf16(const float* src, void* dst, int64_t n, hipStream_t st);
 hipError_t launch_zero(float* x, int64_t n, hipStream_t st);
+
+// Backward of phases 1 and 0 (bf16, G = 16 or 32, fixed-length sequences).
+struct RouteBwdParams {
+  const void* q = nullptr;              // [T, Hq, D]
+  const void* kbar = nullptr;           // [T/B rows, Hkv, D]
+  const void* k = nullptr;              // [T, Hkv, D]
+  const float* qbar = nullptr;          // [Hkv, D]
+  const float* tau = nullptr;           // [Hq, T] the forward's thresholds (u units)
+  const unsigned long long* mask = nullptr;  // [Hkv, T, W]
+  float* db = nullptr;                  // [Hkv, T, C_slots] bias gradient in, dp out
+  float4* sc = nullptr;                 // [Hq, T] per head: threshold or max, softmax sum, rho
+  float* dq = nullptr;                  // [T, Hq, D] fp32, accumulated
+  float* dk = nullptr;                  // [T, Hkv, D] fp32, accumulated
+  float* dqbar = nullptr;               // [Hkv, D] fp32, accumulated (zeroed first)
+  float alpha = 1.5f;
+  float gamma_scale = 1.f;              // gamma * s
+  float sigma = 1.f;
+};
+hipError_t launch_route_bwd(const Geom& g, const RouteBwdParams& p, hipStream_t st);
 hipError_t launch_vt_transpose(const Geom& g, const void* src, void* dst, int64_t Tp,
                                hipStream_t st);
 

@@ -283,3 +283,28 @@ def test_sparse_backward_checks(lib):
     assert bw(shape(dtype=F32, Hq=32, Hkv=2)) == L.DASH_ERR_UNSUPPORTED
     assert bw(shape(cu=A, num_seqs=3)) == L.DASH_ERR_UNSUPPORTED       # varlen
     assert bw(shape(T=0, num_seqs=0, max_seqlen=0)) == L.DASH_OK
+
+
+def test_prefill_backward_checks(lib):
+    s = shape()
+    need = L.workspace_size(L.DASH_OP_PREFILL_BACKWARD, s)
+    assert need > L.workspace_size(L.DASH_OP_BACKWARD, s)
+
+    def bw(sh, alpha=1.5, gamma=1.0, sigma=1.0, **kw):
+        a = dict(q=A, k=A, v=A, qb=A, o=A, do=A, lse=A, dq=A, dk=A, dv=A, dqb=A, ws=A,
+                 n=need, gqa=1)
+        a.update(kw)
+        return lib.dash_attn_prefill_backward(ctypes.byref(sh), a["q"], a["k"], a["v"], a["qb"],
+                                              alpha, gamma, sigma, 0.0, a["gqa"], a["o"],
+                                              a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                                              a["dqb"], a["ws"], a["n"], None)
+
+    for key in ("q", "k", "v", "qb", "o", "do", "lse", "dq", "dk", "dv", "dqb"):
+        assert bw(s, **{key: None}) == L.DASH_ERR_INVALID_ARGUMENT, key
+    assert bw(s, dqb=A + 8) == L.DASH_ERR_INVALID_ARGUMENT
+    assert bw(s, n=need - 1) == L.DASH_ERR_WORKSPACE_TOO_SMALL
+    assert bw(s, alpha=0.5) == L.DASH_ERR_INVALID_ARGUMENT
+    assert bw(shape(Hq=8, Hkv=2)) == L.DASH_ERR_UNSUPPORTED            # group of 4
+    assert bw(shape(dtype=F32, Hq=32, Hkv=2)) == L.DASH_ERR_UNSUPPORTED
+    assert bw(shape(cu=A, num_seqs=3)) == L.DASH_ERR_UNSUPPORTED       # varlen
+    assert bw(shape(T=0, num_seqs=0, max_seqlen=0)) == L.DASH_OK

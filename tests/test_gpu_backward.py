@@ -69,3 +69,79 @@ def test_attention_backward(case):
     errs["dbias"] = rel_err(gb[bits], ref["dbias"][bits]) if bits.any() else 0.0
     assert errs["dbias"] <= REL, errs["dbias"]
     flush(f"  backward {name}: " + " ".join(f"{k_} {v_:.2e}" for k_, v_ in errs.items()))
+
+
+PCASES = [
+    # name, L, Hq, Hkv, D, B, alpha, gamma, sigma, seqs
+    ("g16-d128-a1.5", 512, 16, 1, 128, 64, 1.5, 30.0, 1.0, 1),
+    ("g32-d64-b128-a2", 512, 32, 1, 64, 128, 2.0, 20.0, 1.0, 1),
+    ("g16-softmax", 384, 32, 2, 128, 64, 1.0, 8.0, 1.0, 1),
+    ("g16-a1.25-s0.5", 448, 16, 1, 128, 64, 1.25, 20.0, 0.5, 1),
+    ("g16-ragged", 333, 32, 2, 128, 64, 1.5, 20.0, 1.0, 1),
+    ("g16-2seqs", 256, 16, 1, 128, 64, 1.5, 20.0, 1.0, 2),
+]
+
+
+@pytest.mark.parametrize("case", PCASES, ids=lambda c: c[0])
+def test_prefill_backward(case):
+    """The whole backward (attention, prior, GQA mean, entmax routing, summaries)
+    against the oracle's stages run on the GPU's bf16 summaries, which the
+    gradient passes through unchanged.  Every routing decision of the data is
+    at least 3e-5 (logit units) from its threshold, well beyond the fp32
+    error of the GPU's logits, so both sides take the same support.  The
+    cases keep (1 + sigma - alpha) / (alpha - 1) >= 0: the gradient through a
+    chunk whose weight goes to zero at its threshold then stays bounded."""
+    from oracle import dash_oracle as O
+
+    name, L, Hq, Hkv, D, B, alpha, gamma, sigma, seqs = case
+    flush(f"prefill backward {name}")
+    T = L * seqs
+    d = W.gen_prefill(T, Hq, Hkv, D, seed=71)
+    q, qx = to_dev(d["q"], "bf16")
+    k, kx = to_dev(d["k"], "bf16")
+    v, vx = to_dev(d["v"], "bf16")
+    rng = np.random.default_rng(72)
+    do, dox = to_dev(rng.standard_normal((T, Hq, D)).astype(np.float32), "bf16")
+    qb = torch.from_numpy(d["qbar"]).cuda()
+    ml = L if seqs > 1 else None
+    out, lse, ab = ops.attn_prefill(q, k, v, qb, B, alpha=alpha, gamma=gamma, sigma=sigma,
+                                    max_seqlen=ml, return_lse=True, return_active_blocks=True)
+    dq, dk, dv, dqb = ops.attn_prefill_backward(q, k, v, qb, out, do, lse, B, alpha=alpha,
+                                                gamma=gamma, sigma=sigma, max_seqlen=ml)
+    kb = ops.summarize(k, qb, B, max_seqlen=ml)
+    torch.cuda.synchronize()
+    G, s = Hq // Hkv, 1 / math.sqrt(D)
+    S = -(-L // B)
+    bits_all = unpack_bits(ab, S)
+    kbx_all = kb.to(torch.float64).cpu().numpy()
+    ref = {n_: np.zeros(a_.shape) for n_, a_ in (("dq", qx), ("dk", kx), ("dv", vx))}
+    ref["dqbar"] = np.zeros((Hkv, D))
+    rfrac, kfrac = [], []
+    for sq in range(seqs):
+        sl = slice(sq * L, (sq + 1) * L)
+        kbx = kbx_all[sq * (L // B):(sq + 1) * (L // B)]
+        mask, logp, th = O.route_sequence(qx[sl], kbx, B, alpha, gamma, sigma, G, s)
+        if alpha > 1.0:
+            mg = O.routing_margin(qx[sl], kbx, B, gamma, s, G, th, list(range(L)), S)
+            assert np.min(mg) > 3e-5, "test data too close to a routing threshold"
+        assert np.array_equal(bits_all[:, sl], mask)
+        a = OB.attention_backward_rows(qx[sl], kx[sl], vx[sl], mask, logp, B, s, G, dox[sl])
+        r = OB.routing_backward(qx[sl], kbx, B, alpha, gamma, sigma, G, s, a["dbias"])
+        m = OB.summarize_backward(kx[sl], d["qbar"], B, r["dkbar"])
+        ref["dq"][sl] = a["dq"] + r["dq"]
+        ref["dk"][sl] = a["dk"] + m["dk"]
+        ref["dv"][sl] = a["dv"]
+        ref["dqbar"] += m["dqbar"]
+        rfrac.append(np.max(np.abs(r["dq"])) / np.max(np.abs(a["dq"])))
+        kfrac.append(np.max(np.abs(m["dk"])) / np.max(np.abs(a["dk"])))
+    if sigma > 0:
+        # the routing's parts of dq and dk are not negligible, so a dropped
+        # term shows
+        assert max(rfrac) > 0.05, rfrac
+        assert max(kfrac) > 0.02, kfrac
+    errs = {}
+    for nm, gt in (("dq", dq), ("dk", dk), ("dv", dv), ("dqbar", dqb)):
+        errs[nm] = rel_err(gt.to(torch.float64).cpu().numpy(), ref[nm])
+        assert errs[nm] <= REL, (nm, errs[nm])
+    flush(f"  prefill backward {name}: " + " ".join(f"{k_} {v_:.2e}" for k_, v_ in errs.items())
+          + f" routing/attention dq {max(rfrac):.2f} dk {max(kfrac):.2f}")
