@@ -10,17 +10,26 @@
 //   the rows that have j's chunk active (bias b = log_prior) and the rows of
 //   j's own chunk at or after j (bias 0).
 //
-// bwd_dkdv_kernel: one workgroup of 4 waves per (64-key block, sequence, KV
-// head); wave w owns keys 16w .. 16w+15 of the block and holds their K and V
-// rows as MFMA operands for the whole kernel.  It scans the sequence's mask
-// 256 rows at a time, compacts the rows that see the block (ballots and a
-// block-wide prefix, in row order, so the sums are deterministic), and for
-// each such row stages q_i, dO_i and their transposes in LDS:
+// bwd_headt_kernel: Q and dO copied per (token, KV head) as contiguous blocks
+// of their transposes (units of two dims x four heads).
+// bwd_dkdv_kernel: one workgroup of 4 waves per (64-key block, slice of 4096
+// rows, sequence, KV head); wave w owns keys 16w .. 16w+15 of the block and
+// holds their K and V rows as MFMA operands for the whole kernel.  It scans
+// its slice's mask words 1024 rows at a time, compacts the rows that see the
+// block (ballots and a block-wide prefix, in row order), and streams those
+// rows through a ring of LDS stages filled by direct global->LDS loads (q_i
+// and dO_i XOR-swizzled, their transposes in the unit order of
+// bwd_headt_kernel, so that the operand reads below are free of bank
+// conflicts; the row's LSE, D and bias beside them), several rows ahead of
+// the one computed:
 //   S  = Q_i K_w^T and dP = dO_i V_w^T   (16 heads x 16 keys, 16x16x32 MFMA;
 //                                         the accumulators of S are exactly
 //                                         the operand layout P needs below)
 //   P  = exp2(s S + b - LSE),  dS = P (dP - D)
 //   dV_w^T += dO_i^T P,  dK_w^T += Q_i^T dS   (16x16x16 MFMA over the heads)
+// The slices of a block add their sums into the zeroed fp32 dK and dV by
+// atomics: a block that most rows route to (an early or planted chunk) would
+// otherwise hold one workgroup for the whole sequence.
 // The group's heads go in tiles of 16 (G = 16 or 32).
 #include "dash_device.h"
 #include "dash_internal.h"
@@ -51,32 +60,87 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(Geom g, const uint16_t* 
   delta[(int64_t)qh * g.T + t] = acc;
 }
 
+__global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ x, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) x[i] = 0.f;
+}
+
 constexpr int kBkThreads = 256;
+constexpr int kDkdvSlice = 4096;  // rows per workgroup of bwd_dkdv_kernel
+
+// The transposed copy of one (token, KV head): 16-byte units of two adjacent
+// dims x four heads, unit (quad, pair) at (quad D/2 + pair) 16 bytes,
+//   xt[(h T + t) G D + 8 (quad D/2 + pair) + 4 parity + jj]
+//     = x[t, h G + 4 quad + jj, 2 pair + parity],
+// so that the 16 lanes of an MFMA operand read (16 consecutive dims, one
+// head quad, 8 bytes each) cover one contiguous 128 bytes of LDS.
+template <int D, int G>
+__global__ __launch_bounds__(256) void bwd_headt_kernel(Geom g, const uint16_t* __restrict__ x,
+                                                        uint16_t* __restrict__ xt) {
+  constexpr int ROW = D + 8;
+  constexpr int NU = G * D / 8;  // 16-byte units
+  __shared__ __align__(16) uint16_t tile[G * ROW];
+  const int64_t tok = blockIdx.x;
+  const int h = blockIdx.y, tid = threadIdx.x;
+  for (int u = tid; u < NU; u += 256) {
+    const int j = u / (D / 8), d0 = (u % (D / 8)) * 8;
+    *reinterpret_cast<u32x4*>(&tile[j * ROW + d0]) =
+        ldg16(x + (tok * g.Hq + h * G + j) * (int64_t)D + d0);
+  }
+  __syncthreads();
+  uint16_t* dst = xt + ((int64_t)h * g.T + tok) * (D * G);
+  for (int u = tid; u < NU; u += 256) {
+    const int quad = u / (D / 2), pair = u % (D / 2);
+    u32x4 o;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int par = w >> 1, jj = 2 * (w & 1);
+      const int d = 2 * pair + par, j = 4 * quad + jj;
+      o[w] = (uint32_t)tile[j * ROW + d] | ((uint32_t)tile[(j + 1) * ROW + d] << 16);
+    }
+    *reinterpret_cast<u32x4*>(dst + 8 * u) = o;
+  }
+}
+
+template <int D, int HT>
+struct DkdvCfg {
+  static constexpr int G = 16 * HT;
+  static constexpr int NS = HT == 1 ? 4 : 3;           // ring stages, one row each
+  static constexpr int ABYTES = G * D * 2;             // one array of one row
+  static constexpr int SBYTES = 4 * ABYTES;            // Q, dO, Q^T, dO^T
+  static constexpr int AU = ABYTES / 16;               // 16-byte units per array
+  static constexpr int NUT = 4 * AU / kBkThreads;      // unit loads per thread per stage
+  static constexpr int PER = NUT + 2;                  // loads per wave per stage
+  static_assert(4 * AU % kBkThreads == 0, "units per stage");
+};
 
 template <int D, int HT>
 __global__ __launch_bounds__(kBkThreads) void bwd_dkdv_kernel(Geom g, BwdParams p, float* dk,
                                                               float* dv) {
-  constexpr int G = 16 * HT;
+  using C = DkdvCfg<D, HT>;
+  constexpr int G = C::G;
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
+  constexpr int NS = C::NS;
   constexpr int NTH = kBkThreads;
-  constexpr int QROW = D + 8;   // LDS row stride (elements) of Q / dO: [head][d]
-  constexpr int TROW = G + 4;   // LDS row stride (elements) of Q^T / dO^T: [d][head]
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[G * QROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Ds[G * QROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[D * TROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Dt[D * TROW];
-  __shared__ float Ls[G], Dl[G];
-  __shared__ float Bias;
-  __shared__ int Rows[NTH];
-  __shared__ int Wcnt[NTH / 64];
+  constexpr int UPH = D / 8;      // units per head row of Q / dO
+  constexpr int NR = 1024;        // rows scanned per compaction
+  __shared__ __align__(16) uint8_t Ring[NS * C::SBYTES];
+  __shared__ __align__(16) float Sc[NS][4][64];  // per wave: LSE (lanes < G), D (G .. 2G-1)
+  __shared__ __align__(16) float Bz[NS][4][4];   // per wave: the row's bias
+  __shared__ int Rows[NR];
+  __shared__ int Wcnt[NR / 256][NTH / 64];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = lane & 15, gq = lane >> 4;
-  const int blk = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
+  const int blk = blockIdx.x, s = blockIdx.z / g.Hkv, h = blockIdx.z % g.Hkv;
   const SeqInfo si = seq_info(g.cu_seqlens, nullptr, s, g.max_seqlen, g.B);
   const int key0 = blk * 64;
   if (key0 >= si.len) return;
+  // this workgroup's slice of the rows that may see the block
+  const int rlo = max(key0, (int)blockIdx.y * kDkdvSlice);
+  const int rhi = min(si.len, ((int)blockIdx.y + 1) * kDkdvSlice);
+  if (rlo >= rhi) return;
   const int c = key0 / g.B;            // the block's chunk
   const int cend = min((c + 1) * g.B, si.len);
   const int kmax = si.len - 1;
@@ -94,6 +158,9 @@ __global__ __launch_bounds__(kBkThreads) void bwd_dkdv_kernel(Geom g, BwdParams 
       vf[ks] = as_bf16x8(ldg16((const uint16_t*)p.v + row + 32 * ks + 8 * gq));
     }
   }
+  // the operand loads complete here, so that the compiler's own waits for them
+  // do not land inside the ring loop, where they would also wait for the ring
+  wait_vm<0>();
   f32x4 adk[DT], adv[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
@@ -101,134 +168,144 @@ __global__ __launch_bounds__(kBkThreads) void bwd_dkdv_kernel(Geom g, BwdParams 
     adv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float sl2 = p.scale * kLog2e;
-  const int first = key0;  // rows before the block see none of its keys
+  const uint16_t* qg = (const uint16_t*)p.q;
+  const uint16_t* dg = (const uint16_t*)p.dout;
+  const uint16_t* qtg = (const uint16_t*)p.qt;
+  const uint16_t* dtg = (const uint16_t*)p.dot;
 
-  // staging of one row: registers (fetch, one row ahead) -> LDS (put)
-  constexpr int NPC = (G * D / 8 + NTH - 1) / NTH;  // 16-byte pieces per thread
-  u32x4 ra[NPC], rb[NPC];
-  float rl = 0.f, rd = 0.f, rbias = 0.f;
-  auto fetch = [&](int row) {
+  // one row into ring slot `slot`: thread tid loads units tid + 256 e
+  auto issue = [&](int row, int slot) {
     const int64_t tok = si.start + row;
+    const uint32_t base = lds_addr(Ring) + (uint32_t)(slot * C::SBYTES);
 #pragma unroll
-    for (int n = 0; n < NPC; ++n) {
-      const int pc = tid + NTH * n;
-      if (pc < G * D / 8) {
-        const int hh = pc / (D / 8), d0 = (pc % (D / 8)) * 8;
-        const int64_t src = (tok * g.Hq + h * G + hh) * (int64_t)D + d0;
-        ra[n] = ldg16((const uint16_t*)p.q + src);
-        rb[n] = ldg16((const uint16_t*)p.dout + src);
-      }
-    }
-    if (tid < G) {
-      const int64_t hr = (int64_t)(h * G + tid) * T + tok;
-      rl = p.lse[hr] * kLog2e;
-      rd = p.delta[hr];
-    }
-    if (tid == 0)
-      rbias = row < cend ? 0.f : p.log_prior[((int64_t)h * T + tok) * g.C_slots + c] * kLog2e;
-  };
-  auto put = [&](int) {
-#pragma unroll
-    for (int n = 0; n < NPC; ++n) {
-      const int pc = tid + NTH * n;
-      if (pc < G * D / 8) {
-        const int hh = pc / (D / 8), d0 = (pc % (D / 8)) * 8;
-        const u32x4 a = ra[n], b = rb[n];
-        *reinterpret_cast<u32x4*>(&Qs[hh * QROW + d0]) = a;
-        *reinterpret_cast<u32x4*>(&Ds[hh * QROW + d0]) = b;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          Qt[(d0 + 2 * w) * TROW + hh] = (uint16_t)(a[w] & 0xFFFFu);
-          Qt[(d0 + 2 * w + 1) * TROW + hh] = (uint16_t)(a[w] >> 16);
-          Dt[(d0 + 2 * w) * TROW + hh] = (uint16_t)(b[w] & 0xFFFFu);
-          Dt[(d0 + 2 * w + 1) * TROW + hh] = (uint16_t)(b[w] >> 16);
-        }
-      }
-    }
-    if (tid < G) {
-      Ls[tid] = rl;
-      Dl[tid] = rd;
-    }
-    if (tid == 0) Bias = rbias;
-  };
-
-  for (int r0 = first; r0 < si.len; r0 += NTH) {
-    // ---- rows r0 .. r0+255 that see the block, compacted in order
-    const int i = r0 + tid;
-    bool on = false;
-    if (i < si.len) {
-      if (i < cend) {
-        on = true;  // the block's own chunk: causal (i >= key0 here)
+    for (int e = 0; e < C::NUT; ++e) {
+      const int U = tid + NTH * e;
+      const int arr = U / C::AU, u = U % C::AU;
+      const uint16_t* src;
+      if (arr < 2) {
+        // row-major: head j, 16-byte piece (u % UPH) ^ (j % UPH)
+        const int j = u / UPH, pc = (u % UPH) ^ (j % UPH);
+        src = (arr == 0 ? qg : dg) + (tok * g.Hq + h * G + j) * (int64_t)D + 8 * pc;
       } else {
-        const unsigned long long w = mask[((int64_t)h * T + si.start + i) * g.W + (c >> 6)];
-        on = (w >> (c & 63)) & 1ull;
+        // transposed: the units in their order (see bwd_headt_kernel)
+        src = (arr == 2 ? qtg : dtg) + ((int64_t)h * T + tok) * (D * G) + 8 * u;
       }
+      lds_dma16(src, __builtin_amdgcn_readfirstlane(base + (uint32_t)(16 * (NTH * e + 64 * wv))));
     }
-    const uint64_t bal = __ballot(on);
-    if (lane == 0) Wcnt[wv] = __popcll(bal);
-    __syncthreads();
-    int before = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < NTH / 64; ++w) {
-      before += w < wv ? Wcnt[w] : 0;
-      total += Wcnt[w];
+    if (lane < 2 * G) {
+      const float* src = lane < G ? p.lse + (int64_t)(h * G + lane) * T + tok
+                                  : p.delta + (int64_t)(h * G + lane - G) * T + tok;
+      lds_dma4(src, __builtin_amdgcn_readfirstlane(lds_addr(&Sc[slot][wv][0])));
     }
-    if (on) Rows[before + __popcll(bal & ((1ull << lane) - 1ull))] = i;
-    __syncthreads();
+    if (lane == 0)  // the bias (any valid word for rows of the block's own chunk)
+      lds_dma4(p.log_prior + ((int64_t)h * T + tok) * g.C_slots + c,
+               __builtin_amdgcn_readfirstlane(lds_addr(&Bz[slot][wv][0])));
+  };
 
-    for (int k = 0; k < total; ++k) {
-      const int row = Rows[k];
-      if (k == 0) fetch(row);
-      put(row);
-      __syncthreads();
-      if (k + 1 < total) fetch(Rows[k + 1]);  // in flight while this row computes
-      const float bz = Bias;
-      const bool masked = row < cend;  // the block's own chunk: keys after the row are unseen
+  auto compute = [&](int slot, int row) {
+    const uint8_t* st = Ring + slot * C::SBYTES;
+    lds_u8* Qs = (lds_u8*)(st);
+    lds_u8* Ds = (lds_u8*)(st + C::ABYTES);
+    lds_u8* Qt = (lds_u8*)(st + 2 * C::ABYTES);
+    lds_u8* Dt = (lds_u8*)(st + 3 * C::ABYTES);
+    const bool own = row < cend;  // the block's own chunk: keys after the row are unseen
+    const float bz = own ? 0.f : Bz[slot][wv][0] * kLog2e;
 #pragma unroll
-      for (int ht = 0; ht < HT; ++ht) {
-        f32x4 sacc = {0.f, 0.f, 0.f, 0.f}, pacc = {0.f, 0.f, 0.f, 0.f};
+    for (int ht = 0; ht < HT; ++ht) {
+      f32x4 sacc = {0.f, 0.f, 0.f, 0.f}, pacc = {0.f, 0.f, 0.f, 0.f};
+      const int j = 16 * ht + r;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const u32x4 qa = *reinterpret_cast<const u32x4*>(&Qs[(16 * ht + r) * QROW + 32 * ks + 8 * gq]);
-          const u32x4 da = *reinterpret_cast<const u32x4*>(&Ds[(16 * ht + r) * QROW + 32 * ks + 8 * gq]);
-          sacc = mfma16x16x32(as_bf16x8(qa), kf[ks], sacc);
-          pacc = mfma16x16x32(as_bf16x8(da), vf[ks], pacc);
-        }
-        // lane (gq, r): heads 16 ht + 4 gq + j, key mykey
-        float pv[4], ds[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int hh = 16 * ht + 4 * gq + j;
-          float e = __builtin_amdgcn_exp2f(fmaf(sacc[j], sl2, bz - Ls[hh]));
-          if (masked) e = mykey <= row ? e : 0.f;
-          e = mykey <= kmax ? e : 0.f;
-          pv[j] = e;
-          ds[j] = e * (pacc[j] - Dl[hh]);
-        }
-        const u32x2 pb = {cvt_pk_bf16(pv[0], pv[1]), cvt_pk_bf16(pv[2], pv[3])};
-        const u32x2 sb = {cvt_pk_bf16(ds[0], ds[1]), cvt_pk_bf16(ds[2], ds[3])};
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          // A = X^T tile: dims 16 dt + r, heads 16 ht + 4 gq .. +3
-          const u32x2 ta = *reinterpret_cast<const u32x2*>(&Dt[(16 * dt + r) * TROW + 16 * ht + 4 * gq]);
-          const u32x2 tq = *reinterpret_cast<const u32x2*>(&Qt[(16 * dt + r) * TROW + 16 * ht + 4 * gq]);
-          adv[dt] = mfma16x16x16(as_s16x4(ta), as_s16x4(pb), adv[dt]);
-          adk[dt] = mfma16x16x16(as_s16x4(tq), as_s16x4(sb), adk[dt]);
-        }
+      for (int ks = 0; ks < KS; ++ks) {
+        const int off = 16 * (j * UPH + ((4 * ks + gq) ^ (j % UPH)));
+        sacc = mfma16x16x32(as_bf16x8(lds_read16(Qs + off)), kf[ks], sacc);
+        pacc = mfma16x16x32(as_bf16x8(lds_read16(Ds + off)), vf[ks], pacc);
       }
-      __syncthreads();  // the staging buffers are refilled for the next row
+      // lane (gq, r): heads 16 ht + 4 gq + j, key mykey
+      float pv[4], ds[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int hh = 16 * ht + 4 * gq + jj;
+        float e = __builtin_amdgcn_exp2f(fmaf(sacc[jj], sl2, bz - Sc[slot][wv][hh] * kLog2e));
+        if (own) e = mykey <= row ? e : 0.f;
+        e = mykey <= kmax ? e : 0.f;
+        pv[jj] = e;
+        ds[jj] = e * (pacc[jj] - Sc[slot][wv][G + hh]);
+      }
+      const u32x2 pb = {cvt_pk_bf16(pv[0], pv[1]), cvt_pk_bf16(pv[2], pv[3])};
+      const u32x2 sb = {cvt_pk_bf16(ds[0], ds[1]), cvt_pk_bf16(ds[2], ds[3])};
+      const int quad = 4 * ht + gq;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        // A = X^T tile: dims 16 dt + r, heads 16 ht + 4 gq .. +3
+        const int off = 16 * (quad * (D / 2) + 8 * dt + (r >> 1)) + 8 * (r & 1);
+        typedef const __attribute__((address_space(3))) u32x2 lds_u32x2;
+        const u32x2 ta = *reinterpret_cast<lds_u32x2*>(Dt + off);
+        const u32x2 tq = *reinterpret_cast<lds_u32x2*>(Qt + off);
+        adv[dt] = mfma16x16x16(as_s16x4(ta), as_s16x4(pb), adv[dt]);
+        adk[dt] = mfma16x16x16(as_s16x4(tq), as_s16x4(sb), adk[dt]);
+      }
     }
+  };
+
+  int seen = 0;  // rows this workgroup visited
+  for (int r0 = rlo; r0 < rhi; r0 += NR) {
+    // ---- rows r0 .. r0+1023 that see the block, compacted in order
+    bool on[NR / 256];
+    uint64_t bal[NR / 256];
+    unsigned long long mw[NR / 256];
+#pragma unroll
+    for (int q = 0; q < NR / 256; ++q) {  // the mask words first, all in flight
+      const int i = r0 + 256 * q + tid;
+      mw[q] = i >= cend && i < rhi ? mask[((int64_t)h * T + si.start + i) * g.W + (c >> 6)] : 0ull;
+    }
+#pragma unroll
+    for (int q = 0; q < NR / 256; ++q) {
+      const int i = r0 + 256 * q + tid;
+      // the block's own chunk: causal (i >= key0 here); later rows: the mask
+      on[q] = i < rhi && (i < cend || ((mw[q] >> (c & 63)) & 1ull));
+      bal[q] = __ballot(on[q]);
+      if (lane == 0) Wcnt[q][wv] = __popcll(bal[q]);
+    }
+    __syncthreads();
+    int total = 0;
+#pragma unroll
+    for (int q = 0; q < NR / 256; ++q) {
+      int before = total;
+#pragma unroll
+      for (int w = 0; w < NTH / 64; ++w) {
+        before += w < wv ? Wcnt[q][w] : 0;
+        total += Wcnt[q][w];
+      }
+      if (on[q]) Rows[before + __popcll(bal[q] & ((1ull << lane) - 1ull))] = r0 + 256 * q + tid;
+    }
+    __syncthreads();
+    seen += total;
+
+    for (int k = 0; k < NS - 1 && k < total; ++k) issue(Rows[k], k);
+    for (int k = 0; k < total; ++k) {
+      // this wave's loads of row k have landed once at most the later
+      // stages' loads are outstanding; the barrier then covers every wave's
+      const int ahead = min(NS - 2, total - 1 - k);
+      if (ahead >= 2) wait_vm<2 * C::PER>();
+      else if (ahead == 1) wait_vm<C::PER>();
+      else wait_vm<0>();
+      __syncthreads();
+      if (k + NS - 1 < total) issue(Rows[k + NS - 1], (k + NS - 1) % NS);
+      compute(k % NS, Rows[k]);
+    }
+    __syncthreads();  // the ring and Rows are refilled
   }
-  // ---- write this wave's keys: lane (gq, r) holds dims 16 dt + 4 gq .. +3 of key mykey
-  if (mykey <= kmax) {
+  // ---- add this slice's sums for the wave's keys: lane (gq, r) holds dims
+  // 16 dt + 4 gq .. +3 of key mykey
+  if (seen > 0 && mykey <= kmax) {
     const int64_t row = ((si.start + mykey) * g.Hkv + h) * (int64_t)D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      f32x4 wk = adk[dt];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wk[j] *= p.scale;
-      *reinterpret_cast<f32x4*>(dk + row + 16 * dt + 4 * gq) = wk;
-      *reinterpret_cast<f32x4*>(dv + row + 16 * dt + 4 * gq) = adv[dt];
+      for (int j = 0; j < 4; ++j) {
+        atomicAdd(dk + row + 16 * dt + 4 * gq + j, adk[dt][j] * p.scale);
+        atomicAdd(dv + row + 16 * dt + 4 * gq + j, adv[dt][j]);
+      }
     }
   }
 }
@@ -257,10 +334,29 @@ hipError_t launch_bwd_delta(const Geom& g, const void* out, const void* dout, fl
   return hipGetLastError();
 }
 
+hipError_t launch_bwd_headt(const Geom& g, const void* x, void* xt, hipStream_t st) {
+  if (g.T == 0) return hipSuccess;
+  dim3 grid((unsigned)g.T, g.Hkv);
+#define DASH_HT(DD, GG) \
+  hipLaunchKernelGGL((bwd_headt_kernel<DD, GG>), grid, dim3(256), 0, st, g, (const uint16_t*)x, (uint16_t*)xt)
+  if (g.G == 16) {
+    if (g.D == 64) DASH_HT(64, 16); else DASH_HT(128, 16);
+  } else {
+    if (g.D == 64) DASH_HT(64, 32); else DASH_HT(128, 32);
+  }
+#undef DASH_HT
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_dkdv(const Geom& g, const BwdParams& p, float* dk, float* dv,
                            hipStream_t st) {
   if (g.T == 0) return hipSuccess;
-  dim3 grid((g.max_seqlen + 63) / 64, g.num_seqs, g.Hkv);
+  // the row slices of a key block meet by atomics in the zeroed outputs
+  const int64_t n = g.T * g.Hkv * g.D;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dk, n);
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dv, n);
+  dim3 grid((g.max_seqlen + 63) / 64, (g.max_seqlen + kDkdvSlice - 1) / kDkdvSlice,
+            g.num_seqs * g.Hkv);
 #define DASH_BK(DD, HH)                                                                    \
   hipLaunchKernelGGL((bwd_dkdv_kernel<DD, HH>), grid, dim3(kBkThreads), 0, st, g, p, dk, dv)
   if (g.G == 16) {
@@ -270,11 +366,6 @@ hipError_t launch_bwd_dkdv(const Geom& g, const BwdParams& p, float* dk, float* 
   }
 #undef DASH_BK
   return hipGetLastError();
-}
-
-__global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ x, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) x[i] = 0.f;
 }
 
 hipError_t launch_zero(float* x, int64_t n, hipStream_t st) {

@@ -407,51 +407,6 @@ __device__ __forceinline__ int swz(int row) {
   return P == 16 ? (row & 15) : ((row >> 1) & 7);
 }
 
-// Direct global->LDS loads, issued from asm so that the compiler neither
-// tracks nor waits on them: the data lands in LDS, no register is written,
-// the address registers are consumed at issue, and the ring's own counted
-// vmcnt waits plus a barrier order them before every read.  (Vector-memory
-// operations the compiler does not know about can only make its own counted
-// waits stricter.)
-//   lds_dma16: lane l writes LDS bytes lds_base + 16 l .. +15
-//   lds_dma4 : lane l writes LDS bytes lds_base + 4 l .. +3
-// (lds_base wave-uniform; lanes outside exec write nothing).
-__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(lds_base), "v"(gptr)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void lds_dma4(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-               :
-               : "s"(lds_base), "v"(gptr)
-               : "memory", "m0");
-}
-
-// The same with a wave-uniform 64-bit base (SGPRs) and a 32-bit per-lane byte
-// offset: address = sbase + voff.
-__device__ __forceinline__ void lds_dma16s(const void* sbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(lds_base), "v"(voff), "s"(sbase)
-               : "memory", "m0");
-}
-
-// LDS byte offset of a __shared__ object (a compile-time constant for the
-// ring's static arrays).
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// LDS pointers proper (address space 3): offsets added to them fold into the
-// reads' offset field.
-typedef const __attribute__((address_space(3))) uint8_t lds_u8;
-__device__ __forceinline__ u32x4 lds_read16(lds_u8* p) {
-  typedef const __attribute__((address_space(3))) u32x4 lds_u32x4;
-  return *reinterpret_cast<lds_u32x4*>(p);
-}
-
 // One visit of tiles U0 .. U0+NTL-1 of a wave (16 rows each) to one staged
 // 64-key block (ring layout): S^T = K Q^T, online softmax in base 2 with the
 // tile's bias for the block, O^T += V^T P^T.  With two tiles, every K and V^T
@@ -875,6 +830,7 @@ __global__ __launch_bounds__(kBqThreads, 1) void bwd_dq_kernel(Geom g, BwdParams
   __shared__ int Wpref[33];
   __shared__ uint16_t Blist[2048];
   __shared__ uint16_t Act[2048];
+  __shared__ float Bz[2][64];   // the staged block's bias per position (routed blocks)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1005,6 +961,13 @@ __global__ __launch_bounds__(kBqThreads, 1) void bwd_dq_kernel(Geom g, BwdParams
                    base + (uint32_t)(seg * 1024));
       }
     }
+    // a routed block's bias for each position, beside it (a load in the loop
+    // itself would make the compiler wait for the whole staging)
+    if (sx < nrouted && wv == 0 && lane < npos) {
+      const int c = Blist[sx >> sbl];
+      lds_dma4(p.log_prior + ((int64_t)h * T + si.start + p0 + lane) * g.C_slots + c,
+               __builtin_amdgcn_readfirstlane(lds_addr(&Bz[buf][0])));
+    }
   };
 
   f32x4 o[2][DT];
@@ -1103,7 +1066,7 @@ __global__ __launch_bounds__(kBqThreads, 1) void bwd_dq_kernel(Geom g, BwdParams
       for (int u = 0; u < 2; ++u) {
         if (!(rvalid[u] && ((act >> tpos[u]) & 1u))) continue;
         const int64_t brow = ((int64_t)h * T + si.start + rpos[u]) * g.C_slots + c;
-        const float bz = p.log_prior[brow] * kLog2e;
+        const float bz = Bz[buf][tpos[u]] * kLog2e;
         const float d = u == 0 ? visit(F(), U0(), kv, bz, 0) : visit(F(), U1(), kv, bz, 0);
         if (lane == 0) atomicAdd(&dbias[brow], d);
       }

@@ -176,7 +176,7 @@ RouteDecodeWs route_decode_ws(const Geom& g) {
 }
 // Backward of phase 2: K^T, D = <dO, O>, and fp32 dQ / dK / dV.
 struct BackwardWs {
-  size_t kt, delta, dq, dk, dv, total;
+  size_t kt, delta, dq, dk, dv, qt, dot, total;
 };
 BackwardWs backward_ws(const Geom& g) {
   BackwardWs w{};
@@ -191,6 +191,10 @@ BackwardWs backward_ws(const Geom& g) {
   o += align_up((size_t)g.T * g.Hkv * g.D * 4);
   w.dv = o;
   o += align_up((size_t)g.T * g.Hkv * g.D * 4);
+  w.qt = o;
+  o += align_up((size_t)g.T * g.Hq * g.D * 2);
+  w.dot = o;
+  o += align_up((size_t)g.T * g.Hq * g.D * 2);
   w.total = o;
   return w;
 }
@@ -199,7 +203,7 @@ BackwardWs backward_ws(const Geom& g) {
 // per-head terms of the routing backward.
 struct PrefillBwdWs {
   BackwardWs a;
-  size_t kbar, mask, logp, tau, db, sc, total;
+  size_t kbar, mask, logp, tau, db, sc, kbt, dkb, total;
 };
 PrefillBwdWs prefill_bwd_ws(const Geom& g) {
   PrefillBwdWs w{};
@@ -217,6 +221,10 @@ PrefillBwdWs prefill_bwd_ws(const Geom& g) {
   o += align_up((size_t)g.Hkv * g.T * g.C_slots * 4);
   w.sc = o;
   o += align_up((size_t)g.Hq * g.T * 16);
+  w.kbt = o;
+  o += align_up((size_t)g.num_seqs * g.Hkv * g.D * dash::route_bwd_cpad(g) * 2);
+  w.dkb = o;
+  o += align_up((size_t)(g.T / g.B) * g.Hkv * g.D * 4);
   w.total = o;
   return w;
 }
@@ -634,6 +642,10 @@ dash_status dash_attn_sparse_backward(const dash_shape* shape, const void* q, co
   DASH_HIP(dash::launch_bwd_delta(g, out, dout, reinterpret_cast<float*>(at(workspace, w.delta)), s));
   DASH_HIP(dash::launch_zero(dbias, (int64_t)g.Hkv * g.T * g.C_slots, s));
   DASH_HIP(dash::launch_bwd_dq(g, p, s));
+  DASH_HIP(dash::launch_bwd_headt(g, q, at(workspace, w.qt), s));
+  DASH_HIP(dash::launch_bwd_headt(g, dout, at(workspace, w.dot), s));
+  p.qt = at(workspace, w.qt);
+  p.dot = at(workspace, w.dot);
   DASH_HIP(dash::launch_bwd_dkdv(g, p, dkw, dvw, s));
   DASH_HIP(dash::launch_to_bf16(p.dq, dq, g.T * g.Hq * g.D, s));
   DASH_HIP(dash::launch_to_bf16(dkw, dk, g.T * g.Hkv * g.D, s));
@@ -701,6 +713,10 @@ dash_status dash_attn_prefill_backward(const dash_shape* shape, const void* q, c
   DASH_HIP(dash::launch_bwd_delta(g, out, dout, reinterpret_cast<float*>(at(workspace, w.a.delta)), s));
   DASH_HIP(dash::launch_zero(p.dbias, (int64_t)g.Hkv * g.T * g.C_slots, s));
   DASH_HIP(dash::launch_bwd_dq(g, p, s));
+  DASH_HIP(dash::launch_bwd_headt(g, q, at(workspace, w.a.qt), s));
+  DASH_HIP(dash::launch_bwd_headt(g, dout, at(workspace, w.a.dot), s));
+  p.qt = at(workspace, w.a.qt);
+  p.dot = at(workspace, w.a.dot);
   DASH_HIP(dash::launch_bwd_dkdv(g, p, dkw, dvw, s));
   // phases 1 and 0
   dash::RouteBwdParams rb;
@@ -718,7 +734,11 @@ dash_status dash_attn_prefill_backward(const dash_shape* shape, const void* q, c
   rb.alpha = alpha;
   rb.gamma_scale = rp.gamma_scale;
   rb.sigma = sigma;
+  rb.kbt = reinterpret_cast<const uint16_t*>(at(workspace, w.kbt));
+  rb.dkb = reinterpret_cast<float*>(at(workspace, w.dkb));
+  rb.cpad = dash::route_bwd_cpad(g);
   DASH_HIP(dash::launch_zero(dqbar, (int64_t)g.Hkv * g.D, s));
+  DASH_HIP(dash::launch_zero(rb.dkb, (int64_t)(g.T / g.B) * g.Hkv * g.D, s));
   DASH_HIP(dash::launch_route_bwd(g, rb, s));
   DASH_HIP(dash::launch_to_bf16(p.dq, dq, g.T * g.Hq * g.D, s));
   DASH_HIP(dash::launch_to_bf16(dkw, dk, g.T * g.Hkv * g.D, s));

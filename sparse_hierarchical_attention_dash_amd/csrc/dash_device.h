@@ -197,4 +197,61 @@ __device__ __forceinline__ f32x4 mfma16x16x16(s16x4 a, s16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
+// (the asm below sets M0 on purpose: its clobber is declared)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// Direct global->LDS loads, issued from asm so that the compiler neither
+// tracks nor waits on them: the data lands in LDS, no register is written,
+// the address registers are consumed at issue, and the ring's own counted
+// vmcnt waits plus a barrier order them before every read.  (Vector-memory
+// operations the compiler does not know about can only make its own counted
+// waits stricter.)
+//   lds_dma16: lane l writes LDS bytes lds_base + 16 l .. +15
+//   lds_dma4 : lane l writes LDS bytes lds_base + 4 l .. +3
+// (lds_base wave-uniform; lanes outside exec write nothing).
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_base), "v"(gptr)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :
+               : "s"(lds_base), "v"(gptr)
+               : "memory", "m0");
+}
+
+// The same with a wave-uniform 64-bit base (SGPRs) and a 32-bit per-lane byte
+// offset: address = sbase + voff.
+__device__ __forceinline__ void lds_dma16s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_base), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// LDS byte offset of a __shared__ object (a compile-time constant for the
+// ring's static arrays).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// LDS pointers proper (address space 3): offsets added to them fold into the
+// reads' offset field.
+typedef const __attribute__((address_space(3))) uint8_t lds_u8;
+__device__ __forceinline__ u32x4 lds_read16(lds_u8* p) {
+  typedef const __attribute__((address_space(3))) u32x4 lds_u32x4;
+  return *reinterpret_cast<lds_u32x4*>(p);
+}
+
+// s_waitcnt for at most N outstanding vector-memory operations (N < 64) and
+// no outstanding LDS operation
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
 }  // namespace dash

@@ -98,6 +98,8 @@ struct BwdParams {
   const void* kt = nullptr;             // K^T workspace [Hkv, D, Tp] (the V^T layout)
   int64_t Tp = 0;
   const void* dout = nullptr;           // [T, Hq, D]
+  const void* qt = nullptr;             // Q and dO with the group's heads innermost:
+  const void* dot = nullptr;            //   [Hkv, T, D, G] (launch_bwd_headt)
   const float* lse = nullptr;           // [Hq, T] natural log, from the forward
   const float* delta = nullptr;         // [Hq, T] <dO, O>
   const uint64_t* mask = nullptr;       // [Hkv, T, W]
@@ -109,6 +111,7 @@ struct BwdParams {
 hipError_t launch_bwd_dq(const Geom& g, const BwdParams& p, hipStream_t st);
 hipError_t launch_bwd_delta(const Geom& g, const void* out, const void* dout, float* delta,
                             hipStream_t st);
+hipError_t launch_bwd_headt(const Geom& g, const void* x, void* xt, hipStream_t st);
 hipError_t launch_bwd_dkdv(const Geom& g, const BwdParams& p, float* dk, float* dv,
                            hipStream_t st);
 hipError_t launch_to_bf16(const float* src, void* dst, int64_t n, hipStream_t st);
@@ -127,10 +130,14 @@ struct RouteBwdParams {
   float* dq = nullptr;                  // [T, Hq, D] fp32, accumulated
   float* dk = nullptr;                  // [T, Hkv, D] fp32, accumulated
   float* dqbar = nullptr;               // [Hkv, D] fp32, accumulated (zeroed first)
+  const uint16_t* kbt = nullptr;        // [seqs, Hkv, D, cpad] bf16 (filled here)
+  float* dkb = nullptr;                 // [T/B rows, Hkv, D] fp32 dk_bar (zeroed first)
+  int cpad = 0;                         // route_bwd_cpad(g)
   float alpha = 1.5f;
   float gamma_scale = 1.f;              // gamma * s
   float sigma = 1.f;
 };
+int route_bwd_cpad(const Geom& g);  // complete chunks per sequence, rounded up to 32
 hipError_t launch_route_bwd(const Geom& g, const RouteBwdParams& p, hipStream_t st);
 hipError_t launch_vt_transpose(const Geom& g, const void* src, void* dst, int64_t Tp,
                                hipStream_t st);

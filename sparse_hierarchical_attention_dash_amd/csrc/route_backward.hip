@@ -15,24 +15,52 @@
 //            dk_t += pi_t dk_bar + dz_t q_bar / sqrt(D),
 //            dq_bar += sum_t dz_t k_t / sqrt(D)
 //
+// kbar_t_kernel: K_bar transposed per sequence and KV head, [D][C padded to
+// 32] bf16, the B operand of du K_bar.
 // route_bwd_kernel (one workgroup per row and KV head): recomputes the row's
 // logits (MFMA) and, from the forward's thresholds, each head's p; forms
-// w_bar, dp, and per head r, rho and du (in LDS); adds gamma s du K_bar to
-// dq; stores dp (over db) and each head's (threshold, softmax sum, rho) for
-// the chunk pass.
-// kbar_bwd_kernel (one workgroup per complete chunk and KV head): scans the
-// rows that route to the chunk, recomputes their du for it from the stored
-// per-head terms, accumulates dk_bar, then runs the summary's backward.
+// w_bar, dp, and per head r, rho and du (in LDS); adds gamma s du K_bar to dq
+// (MFMA, du rounded to bf16); stores dp (over db) and each head's
+// (threshold, softmax sum, rho) for the chunk pass.
+// kbar_grad_kernel (one workgroup per 64 chunks, KV head and slice of rows):
+// walks the rows that route to any of its chunks, recomputes their logits
+// and du for its chunks (the same MFMA, so the same r as above), and
+// accumulates dk_bar = gamma s du^T Q (MFMA); slices meet by atomics.
+// kbar_sum_bwd_kernel (one workgroup per complete chunk and KV head): the
+// summary's backward into dk and dq_bar.
 // bf16, G = 16 or 32, fixed-length sequences.
 #include "dash_device.h"
 #include "dash_internal.h"
 
+#include <algorithm>
+
 namespace dash {
 
-// d^e for d >= 0 (0 at d = 0 unless e = 0, where it is the support indicator)
+// d^e for d >= 0 (0 at d = 0 unless e = 0, where it is the support indicator);
+// the exponents of alpha = 1.5 (1 and 2) and alpha = 2 (0 and 1) directly
 __device__ __forceinline__ float pow_pos(float d, float e) {
-  if (e == 0.f) return d > 0.f ? 1.f : 0.f;
-  return d > 0.f ? exp2f(e * __log2f(d)) : 0.f;
+  if (!(d > 0.f)) return 0.f;
+  if (e == 1.f) return d;
+  if (e == 2.f) return d * d;
+  if (e == 0.f) return 1.f;
+  return exp2f(e * __log2f(d));
+}
+
+// K_bar^T: kbt[((s Hkv + h) D + d) cpad + c], zero past the sequence's chunks
+__global__ __launch_bounds__(256) void kbar_t_kernel(Geom g, const uint16_t* __restrict__ kbar,
+                                                     uint16_t* __restrict__ kbt, int cpad) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t n = (int64_t)g.num_seqs * g.Hkv * g.D * cpad;
+  if (idx >= n) return;
+  const int c = (int)(idx % cpad);
+  const int64_t r = idx / cpad;
+  const int d = (int)(r % g.D);
+  const int sh = (int)(r / g.D);
+  const int h = sh % g.Hkv, s = sh / g.Hkv;
+  const int cs = g.max_seqlen / g.B;
+  uint16_t v = 0;
+  if (c < cs) v = kbar[(((int64_t)s * cs + c) * g.Hkv + h) * g.D + d];
+  kbt[idx] = v;
 }
 
 template <int D, int CP>
@@ -40,8 +68,9 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
   constexpr int NTH = 256;
   constexpr int KS = D / 32;
   constexpr int USTR = CP + 16;
-  __shared__ float U[16 * USTR];   // logits, then du, of one 16-head tile
+  __shared__ __align__(16) float U[16 * USTR];   // logits, then du, of one 16-head tile
   __shared__ float Wp[CP];         // sum over the group's heads of p, then dp
+  __shared__ uint8_t On[CP];       // the row's active chunks
   __shared__ float Hp[16][2];      // per head: threshold (x units) or max u; softmax sum
   const int row = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -49,7 +78,8 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
   const int64_t T = g.T;
   const int s = row / g.max_seqlen;
   const int pos = row - s * g.max_seqlen;
-  const int64_t kb0 = (int64_t)s * (g.max_seqlen / g.B);
+  const int cs = g.max_seqlen / g.B;
+  const int64_t kb0 = (int64_t)s * cs;
   const int n = pos / g.B;
   const int G = g.G;
   float4* sc = p.sc;
@@ -63,6 +93,7 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
   const float ep = smax ? 1.f : 1.f / am1;            // p = d^ep
   const float er = smax ? 1.f : (2.f - alpha) / am1;  // r = d^er
   const int HT = G / 16;
+  const int n32 = (n + 31) & ~31;
 
   // logits of head tile ht into U (16 heads x n chunks, MFMA)
   auto logits = [&](int ht) {
@@ -110,7 +141,11 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
   };
 
   // ---- pass 1: w_bar (as G w_bar) over all head tiles
-  for (int c = tid; c < n; c += NTH) Wp[c] = 0.f;
+  const unsigned long long* mrow = p.mask + ((int64_t)h * T + row) * g.W;
+  for (int c = tid; c < n; c += NTH) {
+    Wp[c] = 0.f;
+    On[c] = (uint8_t)((mrow[c >> 6] >> (c & 63)) & 1ull);
+  }
   for (int ht = 0; ht < HT; ++ht) {
     __syncthreads();
     logits(ht);
@@ -126,11 +161,9 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
   }
   __syncthreads();
   // ---- dp on the active chunks (written over db)
-  const unsigned long long* mrow = p.mask + ((int64_t)h * T + row) * g.W;
   float* drow = p.db + ((int64_t)h * T + row) * g.C_slots;
   for (int c = tid; c < n; c += NTH) {
-    const bool on = (mrow[c >> 6] >> (c & 63)) & 1ull;
-    const float dp = on ? p.sigma * drow[c] / Wp[c] : 0.f;
+    const float dp = On[c] ? p.sigma * drow[c] / Wp[c] : 0.f;
     Wp[c] = dp;
     drow[c] = dp;
   }
@@ -148,7 +181,7 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
       float* ur = U + hh * USTR;
       float num = 0.f, den = 0.f;
       for (int c = r; c < n; c += 16) {
-        const float rr = rterm(ur[c], hh);
+        const float rr = On[c] ? rterm(ur[c], hh) : 0.f;
         num = fmaf(rr, Wp[c], num);
         den += rr;
       }
@@ -156,85 +189,128 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
       den = row16_sum(den);
       const float rho = den > 0.f ? num / den : 0.f;
       // every lane of the head has read its U entries above; du overwrites them
-      for (int c = r; c < n; c += 16) {
-        const float rr = rterm(ur[c], hh);
-        ur[c] = rr * (Wp[c] - rho);
+      for (int c = r; c < n32; c += 16) {
+        float du = 0.f;
+        if (c < n && On[c]) du = rterm(ur[c], hh) * (Wp[c] - rho);
+        ur[c] = du;
       }
       if (r == 0)
         sc[(int64_t)(h * G + 16 * ht + hh) * T + row] = make_float4(Hp[hh][0], Hp[hh][1], rho, 0.f);
     }
     __syncthreads();
-    // thread (head hh, dims 8 j .. 8 j + 7) for D = 128 (4 dims for D = 64)
-    constexpr int DPT = D / 16;
-    const int hh = tid >> 4, j = tid & 15;
-    float acc[DPT];
+    // dq tile (16 heads x 16 dims) = du (16 x n32) K_bar (n32 x 16), K_bar^T rows
+    // as the B operand; wave wv: dim tiles wv, wv + 4
+    constexpr int NT = D / 16;
+    const uint16_t* kt = p.kbt + ((int64_t)(s * g.Hkv + h) * D) * p.cpad;
+    for (int dt = wv; dt < NT; dt += 4) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const uint16_t* ktr = kt + (int64_t)(16 * dt + r) * p.cpad + 8 * gq;
+      const float* ua = U + r * USTR + 8 * gq;
+      for (int c0 = 0; c0 < n32; c0 += 32) {
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(ua + c0);
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(ua + c0 + 4);
+        const u32x4 av = {cvt_pk_bf16(a0[0], a0[1]), cvt_pk_bf16(a0[2], a0[3]),
+                          cvt_pk_bf16(a1[0], a1[1]), cvt_pk_bf16(a1[2], a1[3])};
+        acc = mfma16x16x32(as_bf16x8(av), as_bf16x8(ldg16(ktr + c0)), acc);
+      }
+      // lane (gq, r): heads 16 ht + 4 gq + j, dim 16 dt + r
 #pragma unroll
-    for (int e = 0; e < DPT; ++e) acc[e] = 0.f;
-    const float* ur = U + hh * USTR;
-    for (int c = 0; c < n; ++c) {
-      const float du = ur[c];
-      if (du == 0.f) continue;  // off every head's support (wave-divergent skip)
-      const uint16_t* krow =
-          (const uint16_t*)p.kbar + (((kb0 + c) * g.Hkv + h) * (int64_t)D) + DPT * j;
-      if constexpr (DPT == 8) {
-        const u32x4 kv = ldg16(krow);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          acc[2 * w] = fmaf(du, bf16lo(kv[w]), acc[2 * w]);
-          acc[2 * w + 1] = fmaf(du, bf16hi(kv[w]), acc[2 * w + 1]);
-        }
-      } else {
-        const u32x2 kv = *reinterpret_cast<const u32x2*>(krow);
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          acc[2 * w] = fmaf(du, bf16lo(kv[w]), acc[2 * w]);
-          acc[2 * w + 1] = fmaf(du, bf16hi(kv[w]), acc[2 * w + 1]);
-        }
+      for (int j = 0; j < 4; ++j) {
+        float* dq = p.dq + ((int64_t)row * g.Hq + h * G + 16 * ht + 4 * gq + j) * D + 16 * dt + r;
+        *dq += p.gamma_scale * acc[j];
       }
     }
-    float* dq = p.dq + ((int64_t)row * g.Hq + h * G + 16 * ht + hh) * D + DPT * j;
-#pragma unroll
-    for (int e = 0; e < DPT; ++e) dq[e] += p.gamma_scale * acc[e];
   }
 }
 
+// dk_bar of 64 chunks: rows that route to any of them, in slices over blockIdx.y
 template <int D, int HT>
-__global__ __launch_bounds__(256) void kbar_bwd_kernel(Geom g, RouteBwdParams p) {
+__global__ __launch_bounds__(256) void kbar_grad_kernel(Geom g, RouteBwdParams p) {
   constexpr int NTH = 256;
   constexpr int G = 16 * HT;
-  constexpr int DPT = D / 16;        // dims per thread in the (head, dims) layout
-  __shared__ float Kb[D];            // the chunk's summary (fp32)
-  __shared__ float Qs[G * D];        // one row's queries of the group
-  __shared__ float Du[G];
-  __shared__ float Acc[16][D];       // dk_bar partial sums, per head-row of threads
+  constexpr int KS = D / 32;
+  constexpr int NT = D / 16;
+  constexpr int QROW = D + 8;        // row-major copy, padded
+  constexpr int TROW = G + 4;        // transposed copy, padded (8-byte aligned reads)
+  constexpr int NPC = (G * D / 8 + NTH - 1) / NTH;
+  __shared__ __align__(16) uint16_t Qr[2][G * QROW];
+  __shared__ __align__(16) uint16_t Qt[2][D * TROW];
+  __shared__ float4 Sc[2][G];
   __shared__ int Rows[NTH];
+  __shared__ unsigned long long Words[NTH];
   __shared__ int Wcnt[NTH / 64];
-  __shared__ float Red[NTH];
-  const int c = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
+  const int tile = blockIdx.x;
+  const int h = blockIdx.z % g.Hkv, s = blockIdx.z / g.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int r = lane & 15, gq = lane >> 4;
   const int len = g.max_seqlen;
-  if ((c + 1) * g.B > len) return;   // complete chunks only
+  const int cs = len / g.B;
+  const int c0 = tile * 64;
+  if (c0 >= cs) return;
   const int64_t T = g.T;
   const int64_t start = (int64_t)s * len;
-  const int64_t kbrow = ((int64_t)s * (len / g.B) + c) * g.Hkv + h;
-  for (int d = tid; d < D; d += NTH)
-    Kb[d] = bf16_to_f32(((const uint16_t*)p.kbar)[kbrow * D + d]);
-  const int hh = tid >> 4, j = tid & 15;   // thread (head row, dims DPT j ..)
-  float acc[DPT];
-#pragma unroll
-  for (int e = 0; e < DPT; ++e) acc[e] = 0.f;
+  const int64_t kb0 = (int64_t)s * cs;
+  // rows that may route to the tile: n(i) > c0
+  const int rbeg = (c0 + 1) * g.B;
+  const int per = (len - rbeg + (int)gridDim.y - 1) / (int)gridDim.y;
+  const int rlo = rbeg + (int)blockIdx.y * per;
+  const int rhi = min(len, rlo + per);
+  if (rlo >= rhi) return;
   const float am1 = p.alpha - 1.f;
   const bool smax = !(p.alpha > 1.f);
   const float er = smax ? 1.f : (2.f - p.alpha) / am1;
-  __syncthreads();
+  const float gs = p.gamma_scale;
 
-  for (int r0 = (c + 1) * g.B; r0 < len; r0 += NTH) {
-    const int i = r0 + tid;
-    bool on = false;
-    if (i < len) {
-      const unsigned long long w = p.mask[((int64_t)h * T + start + i) * g.W + (c >> 6)];
-      on = (w >> (c & 63)) & 1ull;
+  // this wave's 16 chunks as the B operand of Q K_bar^T
+  const int myc = c0 + 16 * wv + r;
+  bf16x8 kb[KS];
+  {
+    const uint16_t* krow =
+        (const uint16_t*)p.kbar + ((kb0 + min(myc, cs - 1)) * g.Hkv + h) * (int64_t)D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kb[ks] = as_bf16x8(ldg16(krow + 32 * ks + 8 * gq));
+  }
+  f32x4 acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 ra[NPC];
+  float4 rsc = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto fetch = [&](int i) {
+    const int64_t tok = start + i;
+#pragma unroll
+    for (int e = 0; e < NPC; ++e) {
+      const int pc = tid + NTH * e;
+      if (pc < G * D / 8)
+        ra[e] = ldg16((const uint16_t*)p.q + (tok * g.Hq + h * G) * (int64_t)D + 8 * pc);
     }
+    if (tid < G) rsc = p.sc[(int64_t)(h * G + tid) * T + tok];
+  };
+  auto put = [&](int b) {
+#pragma unroll
+    for (int e = 0; e < NPC; ++e) {
+      const int pc = tid + NTH * e;
+      if (pc < G * D / 8) {
+        const int hh = pc / (D / 8), d0 = (pc % (D / 8)) * 8;
+        const u32x4 a = ra[e];
+        *reinterpret_cast<u32x4*>(&Qr[b][hh * QROW + d0]) = a;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          Qt[b][(d0 + 2 * w) * TROW + hh] = (uint16_t)(a[w] & 0xFFFFu);
+          Qt[b][(d0 + 2 * w + 1) * TROW + hh] = (uint16_t)(a[w] >> 16);
+        }
+      }
+    }
+    if (tid < G) Sc[b][tid] = rsc;
+  };
+
+  int parity = 0;
+  for (int r0 = rlo; r0 < rhi; r0 += NTH) {
+    // rows r0 .. r0+255 with any of the tile's chunks active, compacted in order
+    const int i = r0 + tid;
+    unsigned long long word = 0ull;
+    if (i < rhi) word = p.mask[((int64_t)h * T + start + i) * g.W + tile];
+    const bool on = word != 0ull;
     const uint64_t bal = __ballot(on);
     if (lane == 0) Wcnt[wv] = __popcll(bal);
     __syncthreads();
@@ -244,69 +320,97 @@ __global__ __launch_bounds__(256) void kbar_bwd_kernel(Geom g, RouteBwdParams p)
       before += w < wv ? Wcnt[w] : 0;
       total += Wcnt[w];
     }
-    if (on) Rows[before + __popcll(bal & ((1ull << lane) - 1ull))] = i;
+    if (on) {
+      const int at = before + __popcll(bal & ((1ull << lane) - 1ull));
+      Rows[at] = i;
+      Words[at] = word;
+    }
     __syncthreads();
     for (int k = 0; k < total; ++k) {
-      const int64_t tok = start + Rows[k];
-      for (int e = tid; e < G * D; e += NTH)
-        Qs[e] = bf16_to_f32(((const uint16_t*)p.q)[(tok * g.Hq + h * G) * D + e]);
+      const int b = parity;
+      parity ^= 1;
+      if (k == 0) fetch(Rows[0]);
+      put(b);
       __syncthreads();
-      // du of each head for this chunk: u = gamma s <q, k_bar>, r, dp - rho
-      for (int q = wv; q < G; q += NTH / 64) {
-        float d = 0.f;
-        for (int e = lane; e < D; e += 64) d = fmaf(Qs[q * D + e], Kb[e], d);
-        d = row16_sum(d);
-        d += xor16(d);
-        d += xor32(d);
-        if (lane == 0) {
-          const float u = d * p.gamma_scale;
-          const float4 t = p.sc[(int64_t)(h * G + q) * T + tok];
-          const float rr = smax ? exp2f((u - t.x) * kLog2e) / t.y : pow_pos(u * am1 - t.x, er);
-          const float dp = p.db[((int64_t)h * T + tok) * g.C_slots + c];
-          Du[q] = rr * (dp - t.z);
+      const int row = Rows[k];
+      const unsigned long long wbits = Words[k];
+      if (k + 1 < total) fetch(Rows[k + 1]);  // in flight while this row computes
+      const int64_t tok = start + row;
+      // dp of this lane's chunk (0 where the chunk is not active)
+      const bool act = (wbits >> (16 * wv + r)) & 1ull;
+      const float dp = act ? p.db[((int64_t)h * T + tok) * g.C_slots + myc] : 0.f;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        f32x4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4 qa = *reinterpret_cast<const u32x4*>(&Qr[b][(16 * ht + r) * QROW + 32 * ks + 8 * gq]);
+          u = mfma16x16x32(as_bf16x8(qa), kb[ks], u);
+        }
+        // lane (gq, r): heads 16 ht + 4 gq + j, chunk myc
+        float du[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 t = Sc[b][16 * ht + 4 * gq + j];
+          const float x = u[j] * gs;
+          const float rr = smax ? exp2f((x - t.x) * kLog2e) / t.y : pow_pos(x * am1 - t.x, er);
+          du[j] = act ? rr * (dp - t.z) : 0.f;
+        }
+        const u32x2 da = {cvt_pk_bf16(du[0], du[1]), cvt_pk_bf16(du[2], du[3])};
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const u32x2 qb = *reinterpret_cast<const u32x2*>(&Qt[b][(16 * nt + r) * TROW + 16 * ht + 4 * gq]);
+          acc[nt] = mfma16x16x16(as_s16x4(da), as_s16x4(qb), acc[nt]);
         }
       }
-      __syncthreads();
-      // dk_bar partial: heads hh, hh + 16 (G = 32), dims DPT j ..
+    }
+    __syncthreads();  // Rows and Words are refilled
+  }
+  // lane (gq, r) holds dk_bar of chunks c0 + 16 wv + 4 gq + j, dims 16 nt + r
 #pragma unroll
-      for (int t2 = 0; t2 < HT; ++t2) {
-        const int q = hh + 16 * t2;
-        const float du = Du[q];
+  for (int j = 0; j < 4; ++j) {
+    const int c = c0 + 16 * wv + 4 * gq + j;
+    if (c < cs) {
+      float* dst = p.dkb + ((kb0 + c) * g.Hkv + h) * (int64_t)D + r;
 #pragma unroll
-        for (int e = 0; e < DPT; ++e) acc[e] = fmaf(du, Qs[q * D + DPT * j + e], acc[e]);
-      }
-      __syncthreads();
+      for (int nt = 0; nt < NT; ++nt) atomicAdd(dst + 16 * nt, gs * acc[nt][j]);
     }
   }
-  // dk_bar = gamma s * (sum over the 16 head rows of threads)
-#pragma unroll
-  for (int e = 0; e < DPT; ++e) Acc[hh][DPT * j + e] = acc[e];
-  __syncthreads();
+}
+
+// the summary's backward for one complete chunk and KV head
+template <int D>
+__global__ __launch_bounds__(256) void kbar_sum_bwd_kernel(Geom g, RouteBwdParams p) {
+  constexpr int NTH = 256;
   __shared__ float Dkb[D];
+  __shared__ float Qb[D];
+  __shared__ float Pi[256], Dz[256];
+  __shared__ float Red[NTH];
+  const int c = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int len = g.max_seqlen;
+  const int B = g.B;
+  if ((c + 1) * B > len) return;   // complete chunks only
+  const int64_t start = (int64_t)s * len;
+  const int64_t kbrow = ((int64_t)s * (len / B) + c) * g.Hkv + h;
   for (int d = tid; d < D; d += NTH) {
-    float t = 0.f;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) t += Acc[q][d];
-    Dkb[d] = t * p.gamma_scale;
+    Dkb[d] = p.dkb[kbrow * D + d];
+    Qb[d] = p.qbar[h * D + d];
   }
   __syncthreads();
-
-  // ---- the summary's backward over the chunk's B keys (thread t: key t)
-  const int B = g.B;
   const float sD = 1.f / sqrtf((float)D);
-  const float* qb = p.qbar + h * D;
+  // thread t < B: key t's summary logit and <dk_bar, k_t>
   float z = -INFINITY, dpi = 0.f;
-  const uint16_t* krow = nullptr;
   if (tid < B) {
-    krow = (const uint16_t*)p.k + ((start + (int64_t)c * B + tid) * g.Hkv + h) * D;
+    const uint16_t* krow = (const uint16_t*)p.k + ((start + (int64_t)c * B + tid) * g.Hkv + h) * D;
     float a = 0.f, b = 0.f;
     for (int e = 0; e < D; e += 8) {
       const u32x4 kv = ldg16(krow + e);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const float x0 = bf16lo(kv[w]), x1 = bf16hi(kv[w]);
-        a = fmaf(x0, qb[e + 2 * w], a);
-        a = fmaf(x1, qb[e + 2 * w + 1], a);
+        a = fmaf(x0, Qb[e + 2 * w], a);
+        a = fmaf(x1, Qb[e + 2 * w + 1], a);
         b = fmaf(x0, Dkb[e + 2 * w], b);
         b = fmaf(x1, Dkb[e + 2 * w + 1], b);
       }
@@ -314,7 +418,7 @@ __global__ __launch_bounds__(256) void kbar_bwd_kernel(Geom g, RouteBwdParams p)
     z = a * sD;
     dpi = b;
   }
-  // softmax over the chunk's keys (block reductions through Red)
+  // softmax over the chunk's keys, block reductions through Red
   Red[tid] = z;
   __syncthreads();
   for (int o = NTH / 2; o > 0; o >>= 1) {
@@ -340,27 +444,37 @@ __global__ __launch_bounds__(256) void kbar_bwd_kernel(Geom g, RouteBwdParams p)
     __syncthreads();
   }
   const float pdp = Red[0];
-  __syncthreads();
-  const float dz = pi * (dpi - pdp);
-  // dk_t += pi_t dk_bar + sD dz_t q_bar (the key rows of this chunk and head
-  // belong to this workgroup alone)
   if (tid < B) {
-    float* dkr = p.dk + ((start + (int64_t)c * B + tid) * g.Hkv + h) * D;
-    for (int e = 0; e < D; ++e) dkr[e] += pi * Dkb[e] + sD * dz * qb[e];
+    Pi[tid] = pi;
+    Dz[tid] = pi * (dpi - pdp);
   }
-  // dq_bar += sD sum_t dz_t k_t: thread d sums over the keys through LDS
-  Red[tid] = dz;
   __syncthreads();
+  // dk_t += pi_t dk_bar + sD dz_t q_bar (this chunk's rows of this head are
+  // this workgroup's alone), coalesced over the dims
+  for (int idx = tid; idx < B * D; idx += NTH) {
+    const int t = idx / D, d = idx - (idx / D) * D;
+    float* dk = p.dk + ((start + (int64_t)c * B + t) * g.Hkv + h) * D + d;
+    *dk += Pi[t] * Dkb[d] + sD * Dz[t] * Qb[d];
+  }
+  // dq_bar += sD sum_t dz_t k_t
   for (int d = tid; d < D; d += NTH) {
     float t = 0.f;
     for (int kk = 0; kk < B; ++kk)
-      t = fmaf(Red[kk], bf16_to_f32(((const uint16_t*)p.k)[((start + (int64_t)c * B + kk) * g.Hkv + h) * D + d]), t);
+      t = fmaf(Dz[kk], bf16_to_f32(((const uint16_t*)p.k)[((start + (int64_t)c * B + kk) * g.Hkv + h) * D + d]), t);
     atomicAdd(&p.dqbar[h * D + d], sD * t);
   }
 }
 
+int route_bwd_cpad(const Geom& g) { return ((g.max_seqlen / g.B) + 31) & ~31; }
+
 hipError_t launch_route_bwd(const Geom& g, const RouteBwdParams& p, hipStream_t st) {
   if (g.T == 0) return hipSuccess;
+  const int cs = g.max_seqlen / g.B;
+  if (cs > 0) {
+    const int64_t n = (int64_t)g.num_seqs * g.Hkv * g.D * p.cpad;
+    hipLaunchKernelGGL(kbar_t_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, g,
+                       (const uint16_t*)p.kbar, const_cast<uint16_t*>(p.kbt), p.cpad);
+  }
   dim3 grid((unsigned)g.T, g.Hkv);
 #define DASH_RB(DD, CPV) hipLaunchKernelGGL((route_bwd_kernel<DD, CPV>), grid, dim3(256), 0, st, g, p)
 #define DASH_RB_CP(DD)                                  \
@@ -373,16 +487,24 @@ hipError_t launch_route_bwd(const Geom& g, const RouteBwdParams& p, hipStream_t 
   if (g.D == 64) DASH_RB_CP(64); else DASH_RB_CP(128);
 #undef DASH_RB_CP
 #undef DASH_RB
-  const int C = g.max_seqlen / g.B;
-  if (C == 0) return hipGetLastError();
-  dim3 cgrid(C, g.num_seqs, g.Hkv);
-#define DASH_KB(DD, HH) hipLaunchKernelGGL((kbar_bwd_kernel<DD, HH>), cgrid, dim3(256), 0, st, g, p)
+  if (cs == 0) return hipGetLastError();
+  // chunk pass: 64-chunk tiles x row slices, about 2048 workgroups in all
+  const int tiles = (cs + 63) / 64;
+  const int base = tiles * g.num_seqs * g.Hkv;
+  const int slices = std::max(1, std::min(g.max_seqlen / 256 + 1, (2048 + base - 1) / base));
+  dim3 ggrid(tiles, slices, g.num_seqs * g.Hkv);
+#define DASH_KG(DD, HH) hipLaunchKernelGGL((kbar_grad_kernel<DD, HH>), ggrid, dim3(256), 0, st, g, p)
   if (g.G == 16) {
-    if (g.D == 64) DASH_KB(64, 1); else DASH_KB(128, 1);
+    if (g.D == 64) DASH_KG(64, 1); else DASH_KG(128, 1);
   } else {
-    if (g.D == 64) DASH_KB(64, 2); else DASH_KB(128, 2);
+    if (g.D == 64) DASH_KG(64, 2); else DASH_KG(128, 2);
   }
-#undef DASH_KB
+#undef DASH_KG
+  dim3 cgrid(cs, g.num_seqs, g.Hkv);
+  if (g.D == 64)
+    hipLaunchKernelGGL(kbar_sum_bwd_kernel<64>, cgrid, dim3(256), 0, st, g, p);
+  else
+    hipLaunchKernelGGL(kbar_sum_bwd_kernel<128>, cgrid, dim3(256), 0, st, g, p);
   return hipGetLastError();
 }
 
