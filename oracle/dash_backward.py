@@ -39,12 +39,14 @@ from .dash_oracle import (F64, _default_scale, _group_size, _row_keys_and_bias,
                           route_position, route_sequence, softmax, summarize)
 
 
-def attention_backward_rows(q, k, v, mask, log_prior, B, scale, G, dout):
-    """Backward of phase 2 (``attention_rows``) for a given routing, all rows.
+def attention_backward_rows(q, k, v, mask, log_prior, B, scale, G, dout, rows=None):
+    """Backward of phase 2 (``attention_rows``) for a given routing.
 
     q/dout [L, Hq, D], k/v [L, Hkv, D], mask/log_prior [Hkv, L, S].
     Returns dict(dq, dk, dv, dbias [Hkv, L, S] (the gradient of each active
-    routed chunk's bias, 0 elsewhere), delta [Hq, L] = <do, o>).
+    routed chunk's bias, 0 elsewhere), delta [Hq, L] = <do, o>).  With
+    ``rows`` only those query rows are taken: their dq, dbias and delta are
+    complete, while dk and dv hold just those rows' contributions.
     """
     q = np.asarray(q, dtype=F64)
     k = np.asarray(k, dtype=F64)
@@ -58,7 +60,7 @@ def attention_backward_rows(q, k, v, mask, log_prior, B, scale, G, dout):
     dv = np.zeros_like(v)
     dbias = np.zeros((Hkv, L, S), dtype=F64)
     delta = np.zeros((Hq, L), dtype=F64)
-    for i in range(L):
+    for i in (range(L) if rows is None else rows):
         for h in range(Hkv):
             idx, bias = _row_keys_and_bias(i, B, mask[h, i], log_prior[h, i])
             chunk = idx // B
@@ -77,6 +79,51 @@ def attention_backward_rows(q, k, v, mask, log_prior, B, scale, G, dout):
     return dict(dq=dq, dk=dk, dv=dv, dbias=dbias, delta=delta)
 
 
+def attention_backward_keys(q, k, v, mask, log_prior, B, scale, G, dout, lse, out, keys):
+    """dk and dv of the given key positions from phase 2's backward, taken
+    column by column: for key j, every query row i that sees it (rows of j's
+    own chunk at or after j, bias 0; later rows with j's chunk active, bias
+    log_prior), with P_ij = exp(s <q_i, k_j> + b_ij - lse_i) and
+    dS_ij = P_ij (<do_i, v_j> - <do_i, o_i>), from the forward's lse [Hq, L]
+    (natural log) and output o [L, Hq, D].
+
+    Returns dict(dk [len(keys), Hkv, D], dv [len(keys), Hkv, D]); the same
+    quantities as ``attention_backward_rows`` summed the other way round.
+    """
+    q = np.asarray(q, dtype=F64)
+    k = np.asarray(k, dtype=F64)
+    v = np.asarray(v, dtype=F64)
+    dout = np.asarray(dout, dtype=F64)
+    lse = np.asarray(lse, dtype=F64)
+    out = np.asarray(out, dtype=F64)
+    L, Hq, D = q.shape
+    Hkv = k.shape[1]
+    dk = np.zeros((len(keys), Hkv, D), dtype=F64)
+    dv = np.zeros((len(keys), Hkv, D), dtype=F64)
+    for h in range(Hkv):
+        # the rows that see each key, with their bias
+        seen = []
+        for j in keys:
+            c = j // B
+            own = np.arange(j, min((c + 1) * B, L))
+            later = np.arange((c + 1) * B, L)
+            later = later[mask[h, later, c]] if later.size else later
+            seen.append((np.concatenate([own, later]).astype(np.int64),
+                         np.concatenate([np.zeros(own.size), log_prior[h, later, c]])))
+        for qh in range(h * G, (h + 1) * G):
+            qh_q = np.ascontiguousarray(q[:, qh, :])
+            qh_do = np.ascontiguousarray(dout[:, qh, :])
+            dlt = np.einsum("rd,rd->r", qh_do, out[:, qh, :])   # <do_i, o_i>
+            for n, j in enumerate(keys):
+                rows, bias = seen[n]
+                qi, doi = qh_q[rows], qh_do[rows]
+                p = np.exp(scale * (qi @ k[j, h]) + bias - lse[qh, rows])
+                ds = p * (doi @ v[j, h] - dlt[rows])
+                dv[n, h] += p @ doi
+                dk[n, h] += scale * (ds @ qi)
+    return dict(dk=dk, dv=dv)
+
+
 def entmax_backward(p, dp, alpha):
     """du for p = alpha-entmax(u) (one row): J^T dp with the symmetric
     Jacobian diag(r) - r r^T / sum(r), r = p^(2 - alpha) on the support."""
@@ -89,12 +136,13 @@ def entmax_backward(p, dp, alpha):
     return r * dp - r * (r @ dp) / sr
 
 
-def routing_backward(q, kbar, B, alpha, gamma, sigma, G, scale, dbias):
+def routing_backward(q, kbar, B, alpha, gamma, sigma, G, scale, dbias, rows=None):
     """Backward of the log-prior of ``route_sequence`` (b = sigma log w_bar on
     the active chunks) to the queries and the summaries.
 
     dbias [Hkv, L, S].  Returns dict(dq [L, Hq, D], dkbar [C, Hkv, D],
-    du [Hq, L, S] (zero past each row's routable chunks)).
+    du [Hq, L, S] (zero past each row's routable chunks)).  With ``rows`` only
+    those rows are taken (their dq and du complete, dkbar partial).
     """
     q = np.asarray(q, dtype=F64)
     kbar = np.asarray(kbar, dtype=F64)
@@ -105,7 +153,7 @@ def routing_backward(q, kbar, B, alpha, gamma, sigma, G, scale, dbias):
     dkbar = np.zeros_like(kbar)
     du = np.zeros((Hq, L, S), dtype=F64)
     gs = gamma * scale
-    for i in range(L):
+    for i in (range(L) if rows is None else rows):
         n = i // B
         if n == 0:
             continue

@@ -145,3 +145,69 @@ def test_prefill_backward(case):
         assert errs[nm] <= REL, (nm, errs[nm])
     flush(f"  prefill backward {name}: " + " ".join(f"{k_} {v_:.2e}" for k_, v_ in errs.items())
           + f" routing/attention dq {max(rfrac):.2f} dk {max(kfrac):.2f}")
+
+
+def test_backward_full_size_64k():
+    """The benchmark's 64K prefill (planted chunks) in the launch configuration
+    bench.py times: the whole prefill backward and phase 2's backward alone.
+    The oracle takes sampled query rows for dq (row by row: phase 2 on the
+    GPU's routing; the whole backward on the GPU's summaries, on the rows whose
+    routing decisions all lie 3e-5 or more from their thresholds) and sampled
+    keys for dk and dv (column by column from the forward's LSE and output,
+    every row that sees the key)."""
+    from oracle import dash_oracle as O
+
+    flush("full-size backward prefill_64k_needles")
+    d = W.make("prefill_64k_needles")
+    w = d["workload"]
+    L, B, G = w.seqlen, w.B, w.Hq // w.Hkv
+    q, qx = to_dev(d["q"], "bf16")
+    k, kx = to_dev(d["k"], "bf16")
+    v, vx = to_dev(d["v"], "bf16")
+    rng = np.random.default_rng(81)
+    do, dox = to_dev(rng.standard_normal((L, w.Hq, w.D)).astype(np.float32), "bf16")
+    qb = torch.from_numpy(d["qbar"]).cuda()
+    out, lse, _ = ops.attn_prefill(q, k, v, qb, B, alpha=w.alpha, gamma=w.gamma, sigma=w.sigma,
+                                   return_lse=True)
+    dq, dk, dv, dqb = ops.attn_prefill_backward(q, k, v, qb, out, do, lse, B, alpha=w.alpha,
+                                                gamma=w.gamma, sigma=w.sigma)
+    kb = ops.summarize(k, qb, B)
+    mask, lp, _ = ops.route(q, kb, w.Hkv, B, alpha=w.alpha, gamma=w.gamma, sigma=w.sigma,
+                            log_prior=True)
+    dq2, dk2, dv2, _ = ops.attn_sparse_backward(q, k, v, out, do, lse, mask, lp, B)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv, dqb):
+        assert torch.isfinite(t).all()
+    S = -(-L // B)
+    bits = unpack_bits(mask, S)
+    lpx = np.where(bits, lp.cpu().numpy().astype(np.float64), -np.inf)
+    kbx = kb.to(torch.float64).cpu().numpy()
+    s = 1 / math.sqrt(w.D)
+
+    # dq on sampled rows
+    rng = np.random.default_rng(82)
+    rows = sorted(set(rng.integers(B, L, 20).tolist()) | {B, 2 * B - 1, L // 2, L - 1})
+    a = OB.attention_backward_rows(qx, kx, vx, bits, lpx, B, s, G, dox, rows=rows)
+    e = rel_err(dq2[rows].to(torch.float64).cpu().numpy(), a["dq"][rows])
+    assert e <= REL, ("phase-2 dq", e)
+    _, _, th = O.route_sequence(qx, kbx, B, w.alpha, w.gamma, w.sigma, G, s, rows=rows,
+                                num_slots=S)
+    mg = O.routing_margin(qx, kbx, B, w.gamma, s, G, th, rows, S)
+    clear = [i for n_, i in enumerate(rows) if np.min(mg[:, n_]) >= 3e-5]
+    assert len(clear) >= len(rows) // 2, (len(clear), len(rows))
+    r = OB.routing_backward(qx, kbx, B, w.alpha, w.gamma, w.sigma, G, s, a["dbias"], rows=clear)
+    full = a["dq"][clear] + r["dq"][clear]
+    e_full = rel_err(dq[clear].to(torch.float64).cpu().numpy(), full)
+    assert e_full <= REL, ("dq", e_full)
+
+    # dk and dv on sampled keys (chunk 0, a planted-chunk neighbourhood, the tail)
+    keys = sorted(set(rng.integers(0, L, 6).tolist()) | {0, 63, L // 3, L - 1})
+    outx = out.to(torch.float64).cpu().numpy()
+    cols = OB.attention_backward_keys(qx, kx, vx, bits, lpx, B, s, G, dox,
+                                      lse.cpu().numpy().astype(np.float64), outx, keys)
+    errs = {}
+    for nm, gt, rt in (("dk", dk2, cols["dk"]), ("dv", dv2, cols["dv"]), ("dv whole", dv, cols["dv"])):
+        errs[nm] = rel_err(gt[keys].to(torch.float64).cpu().numpy(), rt)
+        assert errs[nm] <= REL, (nm, errs[nm])
+    flush(f"  full-size backward: phase-2 dq {e:.2e}, dq {e_full:.2e} on {len(clear)} rows, "
+          + " ".join(f"{k_} {v_:.2e}" for k_, v_ in errs.items()) + f" on {len(keys)} keys")

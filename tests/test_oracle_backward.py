@@ -123,3 +123,41 @@ def test_sigma_zero_routing_carries_no_gradient():
                                    x["dout"])
     np.testing.assert_allclose(g["dq"], a["dq"], atol=0)
     np.testing.assert_allclose(g["dk"], a["dk"], atol=0)
+
+
+def test_row_subsets_match_the_full_pass():
+    # the rows option of the stage functions takes exactly those rows
+    B = 4
+    x = _inputs(35)
+    s = 1.0 / math.sqrt(6)
+    kbar = O.summarize(x["k"], x["qbar"], B)
+    mask, logp, _ = O.route_sequence(x["q"], kbar, B, 1.5, 4.0, 1.0, 2, s)
+    full = OB.attention_backward_rows(x["q"], x["k"], x["v"], mask, logp, B, s, 2, x["dout"])
+    rows = [0, 5, 13, 19]
+    part = OB.attention_backward_rows(x["q"], x["k"], x["v"], mask, logp, B, s, 2, x["dout"],
+                                      rows=rows)
+    for key in ("dq", "delta"):
+        ax = 0 if key == "dq" else 1
+        np.testing.assert_array_equal(np.take(part[key], rows, axis=ax),
+                                      np.take(full[key], rows, axis=ax))
+    np.testing.assert_array_equal(part["dbias"][:, rows], full["dbias"][:, rows])
+    rf = OB.routing_backward(x["q"], kbar, B, 1.5, 4.0, 1.0, 2, s, full["dbias"])
+    rp = OB.routing_backward(x["q"], kbar, B, 1.5, 4.0, 1.0, 2, s, full["dbias"], rows=rows)
+    np.testing.assert_array_equal(rp["dq"][rows], rf["dq"][rows])
+
+
+def test_key_columns_match_the_row_pass():
+    # the column form (per key, from the forward's lse and output) against the
+    # row form; the ragged tail and both bias kinds are in range
+    B = 4
+    x = _inputs(36, L=22)
+    s = 1.0 / math.sqrt(6)
+    kbar = O.summarize(x["k"], x["qbar"], B)
+    mask, logp, _ = O.route_sequence(x["q"], kbar, B, 1.5, 4.0, 1.0, 2, s)
+    out, lse = O.attention_rows(x["q"], x["k"], x["v"], mask, logp, B, s, 2, list(range(22)))
+    rows = OB.attention_backward_rows(x["q"], x["k"], x["v"], mask, logp, B, s, 2, x["dout"])
+    keys = [0, 3, 4, 9, 15, 19, 21]
+    cols = OB.attention_backward_keys(x["q"], x["k"], x["v"], mask, logp, B, s, 2, x["dout"],
+                                      lse, out, keys)
+    np.testing.assert_allclose(cols["dk"], rows["dk"][keys], atol=1e-12)
+    np.testing.assert_allclose(cols["dv"], rows["dv"][keys], atol=1e-12)
