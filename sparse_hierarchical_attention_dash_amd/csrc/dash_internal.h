@@ -70,6 +70,7 @@ struct RouteParams {
   float* score = nullptr;               // decode, bf16, top-k: group scores scratch [rows, Hkv, C_slots]
   const void* kdiag = nullptr;          // [rows, Hkv, D] estimated own-chunk summaries, or null:
                                         // one more entmax entry per row (after the routed chunks)
+  int64_t row0 = 0;                     // first row of the launch (prefill row ranges)
 };
 hipError_t launch_route(const Geom& g, const RouteParams& p, hipStream_t st);
 

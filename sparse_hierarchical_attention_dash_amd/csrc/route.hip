@@ -25,6 +25,7 @@
 // head's softmax over the routable chunks, summed over the group's heads, is
 // the chunk's score; the min(k, n) chunks of highest score are active (ties
 // to the lower chunk index), with bias 0.
+#include <algorithm>
 #include <type_traits>
 
 #include "dash_device.h"
@@ -381,7 +382,7 @@ __global__ __launch_bounds__(NTH) void route_kernel(Geom g, RouteParams p) {
   __shared__ float Zs[16];          // softmax denominator (alpha = 1)
   __shared__ int Wtot[((CP + NTH - 1) / NTH) * NW + 3];  // top-k: equal keys per wave
 
-  const int64_t row = blockIdx.x;
+  const int64_t row = p.row0 + blockIdx.x;
   const int h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t rows = p.rows;
@@ -854,6 +855,38 @@ hipError_t launch_route(const Geom& g, const RouteParams& p, hipStream_t st) {
     else if (g.C_slots <= 1024) DASH_ROUTE(BF, DD, 1024);                         \
     else DASH_ROUTE(BF, DD, 2048);                                                \
   } while (0)
+  if (!wide && !g.cu_seqlens && g.num_seqs == 1 && p.rows == g.T && p.row0 == 0 &&
+      g.C_slots > 256) {
+    // one sequence: a row at position i has floor(i/B) routable chunks, so the
+    // rows below CP*B fit the CP-wide variant (less LDS, a shorter candidate
+    // scan); each range runs its own variant, the longest rows first
+    for (int cp = 2048; cp >= 256; cp /= 2) {
+      if (cp > 256 && (int64_t)(cp / 2) >= g.C_slots) continue;
+      const int64_t hi = std::min<int64_t>(p.rows, (int64_t)cp * g.B);
+      const int64_t lo = cp == 256 ? 0 : std::min<int64_t>(p.rows, (int64_t)(cp / 2) * g.B);
+      if (hi <= lo) continue;
+      RouteParams q = p;
+      q.row0 = lo;
+      dim3 rgrid((unsigned)(hi - lo), g.Hkv);
+#define DASH_RANGE(BF, DD, CPV) \
+  hipLaunchKernelGGL((route_kernel<BF, DD, CPV, 256>), rgrid, dim3(256), 0, st, g, q)
+#define DASH_RANGE_CP(BF, DD)                   \
+  do {                                          \
+    if (cp == 256) DASH_RANGE(BF, DD, 256);     \
+    else if (cp == 512) DASH_RANGE(BF, DD, 512); \
+    else if (cp == 1024) DASH_RANGE(BF, DD, 1024); \
+    else DASH_RANGE(BF, DD, 2048);              \
+  } while (0)
+      if (g.bf16) {
+        if (g.D == 64) DASH_RANGE_CP(true, 64); else DASH_RANGE_CP(true, 128);
+      } else {
+        if (g.D == 64) DASH_RANGE_CP(false, 64); else DASH_RANGE_CP(false, 128);
+      }
+#undef DASH_RANGE_CP
+#undef DASH_RANGE
+    }
+    return hipGetLastError();
+  }
   if (g.bf16) {
     if (g.D == 64) DASH_ROUTE_CP(true, 64); else DASH_ROUTE_CP(true, 128);
   } else {
