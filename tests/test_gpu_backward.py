@@ -211,3 +211,45 @@ def test_backward_full_size_64k():
         assert errs[nm] <= REL, (nm, errs[nm])
     flush(f"  full-size backward: phase-2 dq {e:.2e}, dq {e_full:.2e} on {len(clear)} rows, "
           + " ".join(f"{k_} {v_:.2e}" for k_, v_ in errs.items()) + f" on {len(keys)} keys")
+
+
+@pytest.mark.parametrize("L", [40, 64, 65, 129])
+def test_prefill_backward_degenerate_lengths(L):
+    """Sequences with no summary (L < B), one complete chunk and no routed
+    row (L = B), one routed row (L = B + 1) and a chunk plus one routed chunk:
+    the routing backward must add nothing where nothing was routed."""
+    from oracle import dash_oracle as O
+
+    flush(f"prefill backward degenerate L={L}")
+    B, Hq, Hkv, D = 64, 16, 1, 128
+    d = W.gen_prefill(L, Hq, Hkv, D, seed=91)
+    q, qx = to_dev(d["q"], "bf16")
+    k, kx = to_dev(d["k"], "bf16")
+    v, vx = to_dev(d["v"], "bf16")
+    rng = np.random.default_rng(92)
+    do, dox = to_dev(rng.standard_normal((L, Hq, D)).astype(np.float32), "bf16")
+    qb = torch.from_numpy(d["qbar"]).cuda()
+    out, lse, _ = ops.attn_prefill(q, k, v, qb, B, alpha=1.5, gamma=20.0, sigma=1.0,
+                                   return_lse=True)
+    dq, dk, dv, dqb = ops.attn_prefill_backward(q, k, v, qb, out, do, lse, B, alpha=1.5,
+                                                gamma=20.0, sigma=1.0)
+    torch.cuda.synchronize()
+    s = 1 / math.sqrt(D)
+    if L >= B:
+        kbx = ops.summarize(k, qb, B).to(torch.float64).cpu().numpy()
+    else:
+        kbx = np.zeros((0, Hkv, D))
+    mask, logp, _ = O.route_sequence(qx, kbx, B, 1.5, 20.0, 1.0, Hq // Hkv, s)
+    a = OB.attention_backward_rows(qx, kx, vx, mask, logp, B, s, Hq // Hkv, dox)
+    r = OB.routing_backward(qx, kbx, B, 1.5, 20.0, 1.0, Hq // Hkv, s, a["dbias"])
+    m = OB.summarize_backward(kx, d["qbar"], B, r["dkbar"])
+    ref = {"dq": a["dq"] + r["dq"], "dk": a["dk"] + m["dk"], "dv": a["dv"]}
+    for nm, gt in (("dq", dq), ("dk", dk), ("dv", dv)):
+        e = rel_err(gt.to(torch.float64).cpu().numpy(), ref[nm])
+        assert e <= REL, (nm, e)
+    gq = dqb.cpu().numpy().astype(np.float64)
+    # (one routed chunk: entmax over one entry is constant, so dq_bar is 0 up to
+    # rounding of rho = r dp / r)
+    assert np.max(np.abs(gq - m["dqbar"])) <= REL * max(np.max(np.abs(m["dqbar"])), 1e-4)
+    if L <= B:
+        assert np.all(gq == 0.0)   # no routed row: no gradient reaches q_bar
