@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define DASH_ABI_VERSION 2
+#define DASH_ABI_VERSION 3
 
 typedef enum {
   DASH_OK = 0,
@@ -319,8 +319,8 @@ dash_status dash_attn_decode_sparse(const dash_shape* shape, const void* q,
  *     P = softmax(s q k^T + b),  D_i = <dO_i, O_i>,  dS = P (dO v^T - D),
  *     dq = s dS k,  dk = s dS^T q,  dv = P^T dO,
  *     dbias[h,i,c] = sum over the chunk's keys and the group's heads of dS.
- * bf16 inputs, GQA group 16 or 32, cu_seqlens = NULL; anything else returns
- * DASH_ERR_UNSUPPORTED.
+ * bf16 inputs, GQA group 16 or 32, fixed-length or packed (cu_seqlens)
+ * sequences; anything else returns DASH_ERR_UNSUPPORTED.
  *   q, k, v, active_blocks, log_prior  as in dash_attn_sparse   (input)
  *   out            [T, Hq, D] dtype    (input: the forward output)
  *   dout           [T, Hq, D] dtype    (input)
@@ -347,8 +347,8 @@ dash_status dash_attn_sparse_backward(const dash_shape* shape, const void* q, co
  * is recomputed from the inputs; the mask is piecewise constant and carries no
  * gradient of its own; bf16 rounding of the summaries passes gradients
  * unchanged.  The support: as dash_attn_sparse_backward.
- *   q, k, v, qbar, alpha, gamma, sigma, softmax_scale, enable_gqa
- *                  as in dash_attn_prefill (input)
+ *   q, k, v, qbar, alpha, alpha_per_seq, gamma, sigma, softmax_scale,
+ *   enable_gqa     as in dash_attn_prefill (input)
  *   out, lse       the forward's output and LSE (input)
  *   dout           [T, Hq, D] dtype    (input)
  *   dq             [T, Hq, D] dtype    (output)
@@ -357,7 +357,8 @@ dash_status dash_attn_sparse_backward(const dash_shape* shape, const void* q, co
  * Workspace: dash_workspace_size(DASH_OP_PREFILL_BACKWARD, shape). */
 dash_status dash_attn_prefill_backward(const dash_shape* shape, const void* q, const void* k,
                                        const void* v, const float* qbar, float alpha,
-                                       float gamma, float sigma, float softmax_scale,
+                                       const float* alpha_per_seq, float gamma, float sigma,
+                                       float softmax_scale,
                                        int enable_gqa, const void* out, const void* dout,
                                        const float* lse, void* dq, void* dk, void* dv,
                                        float* dqbar, void* workspace, size_t workspace_bytes,

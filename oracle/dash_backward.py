@@ -26,7 +26,8 @@ forward step in ``dash_oracle``, taken in reverse order:
 The support (the mask) is piecewise constant in the inputs, so it carries no
 gradient of its own: it enters only through p.  Rounding of summaries to the
 storage dtype is passed through as the identity.  The estimate_diagonal
-option is not covered.
+option is not covered.  Packed sequences are independent: each is the
+one-sequence case.
 """
 
 from __future__ import annotations

@@ -176,11 +176,13 @@ RouteDecodeWs route_decode_ws(const Geom& g) {
 }
 // Backward of phase 2: K^T, D = <dO, O>, and fp32 dQ / dK / dV.
 struct BackwardWs {
-  size_t kt, delta, dq, dk, dv, qt, dot, total;
+  size_t meta, kt, delta, dq, dk, dv, qt, dot, total;
 };
 BackwardWs backward_ws(const Geom& g) {
   BackwardWs w{};
   size_t o = 0;
+  w.meta = o;
+  o += meta_ws(g);
   w.kt = o;
   o += align_up((size_t)g.Hkv * g.D * dash::padded_tokens(g.T, g.num_seqs) * 2);
   w.delta = o;
@@ -228,9 +230,7 @@ PrefillBwdWs prefill_bwd_ws(const Geom& g) {
   w.total = o;
   return w;
 }
-bool backward_supported(const Geom& g) {
-  return g.bf16 && (g.G == 16 || g.G == 32) && !g.cu_seqlens;
-}
+bool backward_supported(const Geom& g) { return g.bf16 && (g.G == 16 || g.G == 32); }
 // Decode attention on a given routing: the split partials only.
 struct DecodeSparseWs {
   size_t acc, ml, total;
@@ -622,6 +622,13 @@ dash_status dash_attn_sparse_backward(const dash_shape* shape, const void* q, co
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(dbias))
     return DASH_ERR_INVALID_ARGUMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (g.cu_seqlens) {
+    void* meta = at(workspace, w.meta);
+    g.cu_chunks = meta_chunks(meta);
+    g.cu_pad = meta_pad(g, meta);
+    DASH_HIP(dash::launch_varlen_meta(g.cu_seqlens, g.num_seqs, g.B, meta_chunks(meta),
+                                      meta_pad(g, meta), s));
+  }
   dash::BwdParams p;
   p.q = q;
   p.k = k;
@@ -655,7 +662,8 @@ dash_status dash_attn_sparse_backward(const dash_shape* shape, const void* q, co
 
 dash_status dash_attn_prefill_backward(const dash_shape* shape, const void* q, const void* k,
                                        const void* v, const float* qbar, float alpha,
-                                       float gamma, float sigma, float softmax_scale,
+                                       const float* alpha_per_seq, float gamma, float sigma,
+                                       float softmax_scale,
                                        int enable_gqa, const void* out, const void* dout,
                                        const float* lse, void* dq, void* dk, void* dv,
                                        float* dqbar, void* workspace, size_t workspace_bytes,
@@ -675,6 +683,13 @@ dash_status dash_attn_prefill_backward(const dash_shape* shape, const void* q, c
       !aligned16(dqbar))
     return DASH_ERR_INVALID_ARGUMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (g.cu_seqlens) {
+    void* meta = at(workspace, w.a.meta);
+    g.cu_chunks = meta_chunks(meta);
+    g.cu_pad = meta_pad(g, meta);
+    DASH_HIP(dash::launch_varlen_meta(g.cu_seqlens, g.num_seqs, g.B, meta_chunks(meta),
+                                      meta_pad(g, meta), s));
+  }
   // the forward's routing, recomputed
   void* kbar = at(workspace, w.kbar);
   uint64_t* mask = reinterpret_cast<uint64_t*>(at(workspace, w.mask));
@@ -685,6 +700,7 @@ dash_status dash_attn_prefill_backward(const dash_shape* shape, const void* q, c
   rp.q = q;
   rp.kbar = kbar;
   rp.alpha = alpha;
+  rp.alpha_per_seq = alpha_per_seq;
   rp.gamma_scale = gamma * eff_scale(g, softmax_scale);
   rp.sigma = sigma;
   rp.mask = mask;
@@ -732,6 +748,7 @@ dash_status dash_attn_prefill_backward(const dash_shape* shape, const void* q, c
   rb.dk = dkw;
   rb.dqbar = dqbar;
   rb.alpha = alpha;
+  rb.alpha_per_seq = alpha_per_seq;
   rb.gamma_scale = rp.gamma_scale;
   rb.sigma = sigma;
   rb.kbt = reinterpret_cast<const uint16_t*>(at(workspace, w.kbt));

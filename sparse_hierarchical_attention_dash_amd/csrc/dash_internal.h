@@ -118,7 +118,7 @@ hipError_t launch_bwd_dkdv(const Geom& g, const BwdParams& p, float* dk, float* 
 hipError_t launch_to_bf16(const float* src, void* dst, int64_t n, hipStream_t st);
 hipError_t launch_zero(float* x, int64_t n, hipStream_t st);
 
-// Backward of phases 1 and 0 (bf16, G = 16 or 32, fixed-length sequences).
+// Backward of phases 1 and 0 (bf16, G = 16 or 32).
 struct RouteBwdParams {
   const void* q = nullptr;              // [T, Hq, D]
   const void* kbar = nullptr;           // [T/B rows, Hkv, D]
@@ -135,6 +135,7 @@ struct RouteBwdParams {
   float* dkb = nullptr;                 // [T/B rows, Hkv, D] fp32 dk_bar (zeroed first)
   int cpad = 0;                         // route_bwd_cpad(g)
   float alpha = 1.5f;
+  const float* alpha_per_seq = nullptr; // [num_seqs] or null (varlen)
   float gamma_scale = 1.f;              // gamma * s
   float sigma = 1.f;
 };

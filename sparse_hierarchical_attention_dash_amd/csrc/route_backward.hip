@@ -28,7 +28,7 @@
 // accumulates dk_bar = gamma s du^T Q (MFMA); slices meet by atomics.
 // kbar_sum_bwd_kernel (one workgroup per complete chunk and KV head): the
 // summary's backward into dk and dq_bar.
-// bf16, G = 16 or 32, fixed-length sequences.
+// bf16, G = 16 or 32; fixed-length or packed (varlen) sequences.
 #include "dash_device.h"
 #include "dash_internal.h"
 
@@ -57,9 +57,9 @@ __global__ __launch_bounds__(256) void kbar_t_kernel(Geom g, const uint16_t* __r
   const int d = (int)(r % g.D);
   const int sh = (int)(r / g.D);
   const int h = sh % g.Hkv, s = sh / g.Hkv;
-  const int cs = g.max_seqlen / g.B;
+  const SeqInfo si = seq_info(g.cu_seqlens, g.cu_chunks, s, g.max_seqlen, g.B);
   uint16_t v = 0;
-  if (c < cs) v = kbar[(((int64_t)s * cs + c) * g.Hkv + h) * g.D + d];
+  if (c < si.len / g.B) v = kbar[((si.chunk_off + c) * g.Hkv + h) * g.D + d];
   kbt[idx] = v;
 }
 
@@ -76,10 +76,10 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = lane & 15, gq = lane >> 4;
   const int64_t T = g.T;
-  const int s = row / g.max_seqlen;
-  const int pos = row - s * g.max_seqlen;
-  const int cs = g.max_seqlen / g.B;
-  const int64_t kb0 = (int64_t)s * cs;
+  const int s = g.cu_seqlens ? find_seq(g.cu_seqlens, g.num_seqs, row) : row / g.max_seqlen;
+  const SeqInfo si = seq_info(g.cu_seqlens, g.cu_chunks, s, g.max_seqlen, g.B);
+  const int pos = (int)(row - si.start);
+  const int64_t kb0 = si.chunk_off;
   const int n = pos / g.B;
   const int G = g.G;
   float4* sc = p.sc;
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
     if (tid < G) sc[(int64_t)(h * G + tid) * T + row] = make_float4(0.f, 0.f, 0.f, 0.f);
     return;
   }
-  const float alpha = p.alpha;
+  const float alpha = p.alpha_per_seq ? p.alpha_per_seq[s] : p.alpha;
   const bool smax = !(alpha > 1.f);
   const float am1 = alpha - 1.f;
   const float ep = smax ? 1.f : 1.f / am1;            // p = d^ep
@@ -243,22 +243,24 @@ __global__ __launch_bounds__(256) void kbar_grad_kernel(Geom g, RouteBwdParams p
   const int h = blockIdx.z % g.Hkv, s = blockIdx.z / g.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = lane & 15, gq = lane >> 4;
-  const int len = g.max_seqlen;
+  const SeqInfo si = seq_info(g.cu_seqlens, g.cu_chunks, s, g.max_seqlen, g.B);
+  const int len = si.len;
   const int cs = len / g.B;
   const int c0 = tile * 64;
   if (c0 >= cs) return;
   const int64_t T = g.T;
-  const int64_t start = (int64_t)s * len;
-  const int64_t kb0 = (int64_t)s * cs;
+  const int64_t start = si.start;
+  const int64_t kb0 = si.chunk_off;
   // rows that may route to the tile: n(i) > c0
   const int rbeg = (c0 + 1) * g.B;
   const int per = (len - rbeg + (int)gridDim.y - 1) / (int)gridDim.y;
   const int rlo = rbeg + (int)blockIdx.y * per;
   const int rhi = min(len, rlo + per);
   if (rlo >= rhi) return;
-  const float am1 = p.alpha - 1.f;
-  const bool smax = !(p.alpha > 1.f);
-  const float er = smax ? 1.f : (2.f - p.alpha) / am1;
+  const float alpha = p.alpha_per_seq ? p.alpha_per_seq[s] : p.alpha;
+  const float am1 = alpha - 1.f;
+  const bool smax = !(alpha > 1.f);
+  const float er = smax ? 1.f : (2.f - alpha) / am1;
   const float gs = p.gamma_scale;
 
   // this wave's 16 chunks as the B operand of Q K_bar^T
@@ -388,11 +390,11 @@ __global__ __launch_bounds__(256) void kbar_sum_bwd_kernel(Geom g, RouteBwdParam
   __shared__ float Red[NTH];
   const int c = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
   const int tid = threadIdx.x;
-  const int len = g.max_seqlen;
+  const SeqInfo si = seq_info(g.cu_seqlens, g.cu_chunks, s, g.max_seqlen, g.B);
   const int B = g.B;
-  if ((c + 1) * B > len) return;   // complete chunks only
-  const int64_t start = (int64_t)s * len;
-  const int64_t kbrow = ((int64_t)s * (len / B) + c) * g.Hkv + h;
+  if ((c + 1) * B > si.len) return;   // complete chunks only
+  const int64_t start = si.start;
+  const int64_t kbrow = (si.chunk_off + c) * g.Hkv + h;
   for (int d = tid; d < D; d += NTH) {
     Dkb[d] = p.dkb[kbrow * D + d];
     Qb[d] = p.qbar[h * D + d];

@@ -211,14 +211,15 @@ def attn_prefill(q, k, v, qbar, chunk_size, *, alpha=1.5, gamma=1.0, sigma=1.0,
 
 
 def attn_prefill_backward(q, k, v, qbar, out, dout, lse, chunk_size, *, alpha=1.5, gamma=1.0,
-                          sigma=1.0, softmax_scale=0.0, enable_gqa=True, max_seqlen=None,
-                          workspace=None):
+                          sigma=1.0, softmax_scale=0.0, enable_gqa=True, alpha_per_seq=None,
+                          cu_seqlens=None, max_seqlen=None, workspace=None):
     """Backward of attn_prefill (fixed-length sequences of max_seqlen tokens,
-    one of T if None): returns (dq, dk, dv, dqbar [Hkv, D] fp32)."""
-    _need_cuda(q, k, v, qbar, out, dout, lse)
+    one of T if None, or packed by cu_seqlens): returns (dq, dk, dv, dqbar
+    [Hkv, D] fp32)."""
+    _need_cuda(q, k, v, qbar, out, dout, lse, alpha_per_seq, cu_seqlens)
     T, Hq, D = q.shape
     Hkv = k.shape[1]
-    shape = _seq_shape(q, Hq, Hkv, chunk_size, None, max_seqlen)
+    shape = _seq_shape(q, Hq, Hkv, chunk_size, cu_seqlens, max_seqlen)
     dev = q.device
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
@@ -229,19 +230,21 @@ def attn_prefill_backward(q, k, v, qbar, out, dout, lse, chunk_size, *, alpha=1.
     if workspace is None or workspace.numel() < n:
         workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
     L.check("dash_attn_prefill_backward", L.lib().dash_attn_prefill_backward(
-        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(qb), float(alpha), float(gamma),
-        float(sigma), float(softmax_scale), int(enable_gqa), _ptr(out), _ptr(dout), _ptr(lse),
-        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dqbar), _ptr(workspace), n, _stream(dev)))
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(qb), float(alpha),
+        _ptr(alpha_per_seq), float(gamma), float(sigma), float(softmax_scale), int(enable_gqa),
+        _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dqbar),
+        _ptr(workspace), n, _stream(dev)))
     return dq, dk, dv, dqbar
 
 
 def attn_sparse_backward(q, k, v, out, dout, lse, active_blocks, log_prior, chunk_size, *,
-                         softmax_scale=0.0, enable_gqa=True, workspace=None):
+                         softmax_scale=0.0, enable_gqa=True, cu_seqlens=None, max_seqlen=None,
+                         workspace=None):
     """Backward of attn_sparse: returns (dq, dk, dv, dbias [Hkv, T, C_slots])."""
-    _need_cuda(q, k, v, out, dout, lse, active_blocks, log_prior)
+    _need_cuda(q, k, v, out, dout, lse, active_blocks, log_prior, cu_seqlens)
     T, Hq, D = q.shape
     Hkv = k.shape[1]
-    shape = _seq_shape(q, Hq, Hkv, chunk_size, None, None)
+    shape = _seq_shape(q, Hq, Hkv, chunk_size, cu_seqlens, max_seqlen)
     lay = L.layout(shape, enable_gqa)
     dev = q.device
     dq = torch.empty_like(q)

@@ -62,7 +62,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dash_abi_version() == 2
+    assert lib.dash_abi_version() == 3
     for code, text in ((0, "ok"), (1, "invalid argument"), (2, "unsupported configuration"),
                        (3, "workspace too small"), (4, "HIP launch error")):
         assert L.status_string(code) == text
@@ -281,7 +281,8 @@ def test_sparse_backward_checks(lib):
     assert bw(s, n=need - 1) == L.DASH_ERR_WORKSPACE_TOO_SMALL
     assert bw(shape(Hq=8, Hkv=2)) == L.DASH_ERR_UNSUPPORTED            # group of 4
     assert bw(shape(dtype=F32, Hq=32, Hkv=2)) == L.DASH_ERR_UNSUPPORTED
-    assert bw(shape(cu=A, num_seqs=3)) == L.DASH_ERR_UNSUPPORTED       # varlen
+    vs = shape(cu=A, num_seqs=3)                                       # varlen: metadata
+    assert bw(vs, n=L.workspace_size(L.DASH_OP_BACKWARD, vs) - 1) == L.DASH_ERR_WORKSPACE_TOO_SMALL
     assert bw(shape(T=0, num_seqs=0, max_seqlen=0)) == L.DASH_OK
 
 
@@ -295,7 +296,7 @@ def test_prefill_backward_checks(lib):
                  n=need, gqa=1)
         a.update(kw)
         return lib.dash_attn_prefill_backward(ctypes.byref(sh), a["q"], a["k"], a["v"], a["qb"],
-                                              alpha, gamma, sigma, 0.0, a["gqa"], a["o"],
+                                              alpha, None, gamma, sigma, 0.0, a["gqa"], a["o"],
                                               a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
                                               a["dqb"], a["ws"], a["n"], None)
 
@@ -306,5 +307,7 @@ def test_prefill_backward_checks(lib):
     assert bw(s, alpha=0.5) == L.DASH_ERR_INVALID_ARGUMENT
     assert bw(shape(Hq=8, Hkv=2)) == L.DASH_ERR_UNSUPPORTED            # group of 4
     assert bw(shape(dtype=F32, Hq=32, Hkv=2)) == L.DASH_ERR_UNSUPPORTED
-    assert bw(shape(cu=A, num_seqs=3)) == L.DASH_ERR_UNSUPPORTED       # varlen
+    vs = shape(cu=A, num_seqs=3)                                       # varlen: metadata
+    assert bw(vs, n=L.workspace_size(L.DASH_OP_PREFILL_BACKWARD, vs) - 1) == \
+        L.DASH_ERR_WORKSPACE_TOO_SMALL
     assert bw(shape(T=0, num_seqs=0, max_seqlen=0)) == L.DASH_OK

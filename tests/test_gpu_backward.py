@@ -253,3 +253,90 @@ def test_prefill_backward_degenerate_lengths(L):
     assert np.max(np.abs(gq - m["dqbar"])) <= REL * max(np.max(np.abs(m["dqbar"])), 1e-4)
     if L <= B:
         assert np.all(gq == 0.0)   # no routed row: no gradient reaches q_bar
+
+
+VARLEN = [
+    # lengths, alphas, B, D, Hq, Hkv
+    ((300, 64, 517, 40), (1.5, 2.0, 1.25, 1.5), 64, 128, 16, 1),
+    ((257, 700), (1.5, 1.0), 128, 64, 32, 2),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN, ids=lambda c: "-".join(map(str, c[0])))
+def test_backward_varlen(case):
+    """Packed sequences of mixed lengths with an alpha per sequence: phase 2's
+    backward on the GPU's routing and the whole prefill backward on the GPU's
+    summaries, each sequence against the oracle on its own (the sequences
+    are independent).  Rows closer than 3e-5 to a routing threshold are left
+    out of the whole-backward dq check, and the dk/dq_bar checks run only on
+    sequences with none."""
+    from oracle import dash_oracle as O
+
+    lens, alphas, B, D, Hq, Hkv = case
+    flush(f"backward varlen {lens}")
+    G, gamma, sigma, s = Hq // Hkv, 20.0, 1.0, 1 / math.sqrt(D)
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    d = W.gen_prefill(T, Hq, Hkv, D, seed=101)
+    q, qx = to_dev(d["q"], "bf16")
+    k, kx = to_dev(d["k"], "bf16")
+    v, vx = to_dev(d["v"], "bf16")
+    rng = np.random.default_rng(102)
+    do, dox = to_dev(rng.standard_normal((T, Hq, D)).astype(np.float32), "bf16")
+    qb = torch.from_numpy(d["qbar"]).cuda()
+    cu_t = torch.from_numpy(cu).cuda()
+    al_t = torch.tensor(alphas, dtype=torch.float32).cuda()
+    ml = max(lens)
+    kw = dict(cu_seqlens=cu_t, max_seqlen=ml)
+    out, lse, _ = ops.attn_prefill(q, k, v, qb, B, alpha=1.5, alpha_per_seq=al_t, gamma=gamma,
+                                   sigma=sigma, return_lse=True, **kw)
+    dq, dk, dv, dqb = ops.attn_prefill_backward(q, k, v, qb, out, do, lse, B, alpha=1.5,
+                                                alpha_per_seq=al_t, gamma=gamma, sigma=sigma,
+                                                **kw)
+    kb = ops.summarize(k, qb, B, **kw)
+    mask, lp, _ = ops.route(q, kb, Hkv, B, alpha=1.5, alpha_per_seq=al_t, gamma=gamma,
+                            sigma=sigma, log_prior=True, **kw)
+    dq2, dk2, dv2, db2 = ops.attn_sparse_backward(q, k, v, out, do, lse, mask, lp, B, **kw)
+    torch.cuda.synchronize()
+    S = -(-ml // B)
+    bits_all = unpack_bits(mask, S)
+    lp_all = lp.cpu().numpy().astype(np.float64)
+    kbx_all = kb.to(torch.float64).cpu().numpy()
+    g = {nm: t.to(torch.float64).cpu().numpy() for nm, t in
+         (("dq", dq), ("dk", dk), ("dv", dv), ("dq2", dq2), ("dk2", dk2), ("dv2", dv2))}
+    ref_dqbar = np.zeros((Hkv, D))
+    all_clear = True
+    coff = 0
+    for sq, (Ls, al) in enumerate(zip(lens, alphas)):
+        sl = slice(cu[sq], cu[sq + 1])
+        bits = bits_all[:, sl]
+        lpx = np.where(bits, lp_all[:, sl], -np.inf)
+        a = OB.attention_backward_rows(qx[sl], kx[sl], vx[sl], bits, lpx, B, s, G, dox[sl])
+        for nm in ("dq", "dk", "dv"):
+            e = rel_err(g[nm + "2"][sl], a[nm])
+            assert e <= REL, ("phase 2", sq, nm, e)
+        nc = Ls // B
+        kbx = kbx_all[coff:coff + nc]
+        coff += nc
+        mk, _, th = O.route_sequence(qx[sl], kbx, B, al, gamma, sigma, G, s, num_slots=S)
+        if al > 1.0 and Ls > B:
+            mg = O.routing_margin(qx[sl], kbx, B, gamma, s, G, th, list(range(Ls)), S)
+            rows_ok = np.min(mg, axis=(0, 2)) >= 3e-5
+        else:
+            rows_ok = np.ones(Ls, bool)
+        all_clear &= bool(rows_ok.all())
+        r = OB.routing_backward(qx[sl], kbx, B, al, gamma, sigma, G, s, a["dbias"])
+        m = OB.summarize_backward(kx[sl], d["qbar"], B, r["dkbar"])
+        ref_dq = a["dq"] + r["dq"]
+        e = rel_err(g["dq"][sl][rows_ok], ref_dq[rows_ok])
+        assert e <= REL, ("dq", sq, e)
+        e = rel_err(g["dv"][sl], a["dv"])
+        assert e <= REL, ("dv", sq, e)
+        if rows_ok.all():
+            e = rel_err(g["dk"][sl], a["dk"] + m["dk"])
+            assert e <= REL, ("dk", sq, e)
+        ref_dqbar += m["dqbar"]
+    if all_clear:
+        e = rel_err(dqb.cpu().numpy().astype(np.float64), ref_dqbar)
+        assert e <= REL, ("dqbar", e)
+    flush(f"  varlen backward {lens}: ok (all rows clear of thresholds: {all_clear})")
