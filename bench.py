@@ -42,17 +42,19 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 PMC_FILE = os.path.join(ROOT, "profiles", "prefill_attn_pmc.json")
 KERNEL_SOURCES = ["attn_prefill.hip", "attn_stage.h", "dash_device.h"]
+DEC_PMC_FILE = os.path.join(ROOT, "profiles", "decode_attn_pmc.json")
+DEC_KERNEL_SOURCES = ["attn_decode.hip", "attn_stage.h", "dash_device.h"]
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_hash():
-    """Hash of the attention kernel's sources with comments and blank space
-    removed: a change of code invalidates the stored counters, a comment does not."""
+def kernel_hash(sources=KERNEL_SOURCES):
+    """Hash of a kernel's sources with comments and blank space removed: a
+    change of code invalidates the stored counters, a comment does not."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, "sparse_hierarchical_attention_dash_amd", "csrc", f)) as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -344,12 +346,19 @@ def main():
         kv_bytes = float(np.sum(wd.B * popd + diag[None, :])) * wd.D * 2 * 2
         gbs = kv_bytes / (t_dec * 1e-3) / 1e9
         routable = float(np.sum((sl - 1) // wd.B)) * wd.Hkv
+        dec_traffic = None
+        if os.path.exists(DEC_PMC_FILE):
+            pmc = json.load(open(DEC_PMC_FILE))
+            if (pmc.get("kernel_hash") == kernel_hash(DEC_KERNEL_SOURCES)
+                    and pmc.get("workload") == wd.name):
+                dec_traffic = pmc.get("hbm_bytes_per_launch")
         res["decode"] = {"us_per_step": t_dec * 1e3, "us_per_token": t_dec * 1e3 / wd.batch,
                          "active_kv_bytes": kv_bytes, "GB_per_s": gbs,
                          "block_support": float(popd.sum()) / routable,
                          "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
                                       "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
-                                      "traffic": None}}
+                                      "traffic": dec_traffic,
+                                      "traffic_kernel": "decode_attn_kernel<128, 1>"}}
         config["decode"] = {"workload": wd.name, "batch": wd.batch, "cache_tokens": cap,
                             "q_heads": wd.Hq, "kv_heads": wd.Hkv, "head_dim": wd.D,
                             "chunk": wd.B, "alpha": wd.alpha, "gamma": wd.gamma}
