@@ -25,9 +25,16 @@ forward step in ``dash_oracle``, taken in reverse order:
 
 The support (the mask) is piecewise constant in the inputs, so it carries no
 gradient of its own: it enters only through p.  Rounding of summaries to the
-storage dtype is passed through as the identity.  The estimate_diagonal
-option is not covered.  Packed sequences are independent: each is the
-one-sequence case.
+storage dtype is passed through as the identity.  Packed sequences are
+independent: each is the one-sequence case.
+
+With estimate_diagonal (reading E1) each routed row's entmax has one more
+entry, u_d = gamma s <q, k_hat_i>, whose probability feeds no prior: its dp
+is 0, so du_d = -r_d rho, and rho's denominator includes r_d.  Then
+dq += gamma s du_d k_hat_i, dk_hat_i = gamma s sum over the group's heads of
+du_d q, and k_hat_i = sum_{t = cB..i} pi_t k_t (the running summary of the
+row's own chunk) passes it back like a summary:
+dk_t += pi_t dk_hat_i + s dz_t q_bar, dq_bar += s sum_t dz_t k_t.
 """
 
 from __future__ import annotations
@@ -37,7 +44,8 @@ import math
 import numpy as np
 
 from .dash_oracle import (F64, _default_scale, _group_size, _row_keys_and_bias,
-                          route_position, route_sequence, softmax, summarize)
+                          route_position, route_sequence, softmax, summarize,
+                          summarize_diagonal)
 
 
 def attention_backward_rows(q, k, v, mask, log_prior, B, scale, G, dout, rows=None):
@@ -137,13 +145,15 @@ def entmax_backward(p, dp, alpha):
     return r * dp - r * (r @ dp) / sr
 
 
-def routing_backward(q, kbar, B, alpha, gamma, sigma, G, scale, dbias, rows=None):
+def routing_backward(q, kbar, B, alpha, gamma, sigma, G, scale, dbias, rows=None, kdiag=None):
     """Backward of the log-prior of ``route_sequence`` (b = sigma log w_bar on
     the active chunks) to the queries and the summaries.
 
     dbias [Hkv, L, S].  Returns dict(dq [L, Hq, D], dkbar [C, Hkv, D],
-    du [Hq, L, S] (zero past each row's routable chunks)).  With ``rows`` only
-    those rows are taken (their dq and du complete, dkbar partial).
+    du [Hq, L, S] (zero past each row's routable chunks), dkdiag [L, Hkv, D]
+    (the gradient of each row's own-chunk estimate when ``kdiag`` is given,
+    else None)).  With ``rows`` only those rows are taken (their dq, du and
+    dkdiag complete, dkbar partial).
     """
     q = np.asarray(q, dtype=F64)
     kbar = np.asarray(kbar, dtype=F64)
@@ -153,24 +163,35 @@ def routing_backward(q, kbar, B, alpha, gamma, sigma, G, scale, dbias, rows=None
     dq = np.zeros_like(q)
     dkbar = np.zeros_like(kbar)
     du = np.zeros((Hq, L, S), dtype=F64)
+    dkdiag = None if kdiag is None else np.zeros((L, Hkv, q.shape[2]), dtype=F64)
     gs = gamma * scale
     for i in (range(L) if rows is None else rows):
         n = i // B
         if n == 0:
             continue
         for h in range(Hkv):
-            r = route_position(q[i, h * G:(h + 1) * G], kbar[:n, h, :], alpha, gamma, scale)
+            kd = None if kdiag is None else np.asarray(kdiag[i, h], dtype=F64)
+            r = route_position(q[i, h * G:(h + 1) * G], kbar[:n, h, :], alpha, gamma, scale,
+                               kdiag_h=kd)
             m = r["mask"]
             dw = np.zeros(n, dtype=F64)
             dw[m] = sigma * dbias[h, i, :n][m] / r["wbar"][m]
             dp = dw / G
             for g in range(G):
                 qh = h * G + g
-                d = entmax_backward(r["p"][g], dp, alpha)
+                if kd is None:
+                    d = entmax_backward(r["p"][g], dp, alpha)
+                    dq[i, qh] += gs * (d @ kbar[:n, h, :])
+                else:
+                    # the own-chunk entry: in the entmax, no prior (dp 0)
+                    d = entmax_backward(np.append(r["p"][g], r["p_diag"][g]),
+                                        np.append(dp, 0.0), alpha)
+                    dq[i, qh] += gs * (d[:n] @ kbar[:n, h, :] + d[n] * kd)
+                    dkdiag[i, h] += gs * d[n] * q[i, qh]
+                    d = d[:n]
                 du[qh, i, :n] = d
-                dq[i, qh] += gs * (d @ kbar[:n, h, :])
                 dkbar[:n, h, :] += gs * np.outer(d, q[i, qh])
-    return dict(dq=dq, dkbar=dkbar, du=du)
+    return dict(dq=dq, dkbar=dkbar, du=du, dkdiag=dkdiag)
 
 
 def summarize_backward(k, qbar, B, dkbar):
@@ -195,8 +216,32 @@ def summarize_backward(k, qbar, B, dkbar):
     return dict(dk=dk, dqbar=dqbar)
 
 
+def summarize_diagonal_backward(k, qbar, B, dkdiag):
+    """Backward of ``summarize_diagonal``: every row i's estimate of its own
+    chunk, k_hat_i = sum_{t = cB..i} pi_t k_t, pi = softmax(s <q_bar, k_t>).
+
+    Returns dict(dk [L, Hkv, D], dqbar [Hkv, D])."""
+    k = np.asarray(k, dtype=F64)
+    qbar = np.asarray(qbar, dtype=F64)
+    dkdiag = np.asarray(dkdiag, dtype=F64)
+    L, Hkv, D = k.shape
+    s = 1.0 / math.sqrt(D)
+    dk = np.zeros_like(k)
+    dqbar = np.zeros_like(qbar)
+    for i in range(L):
+        c0 = (i // B) * B
+        for h in range(Hkv):
+            keys = k[c0:i + 1, h, :]
+            pi = softmax(s * (keys @ qbar[h]))
+            dpi = keys @ dkdiag[i, h]
+            dz = pi * (dpi - pi @ dpi)
+            dk[c0:i + 1, h, :] += np.outer(pi, dkdiag[i, h]) + s * np.outer(dz, qbar[h])
+            dqbar[h] += s * (dz @ keys)
+    return dict(dk=dk, dqbar=dqbar)
+
+
 def prefill_backward(q, k, v, qbar, B, alpha, gamma, sigma, dout, enable_gqa=True,
-                     scale=None):
+                     scale=None, estimate_diagonal=False):
     """Gradients of sum(dout * o) for the causal prefill of one sequence
     (``dash_oracle.prefill`` without storage rounding) with respect to q, k,
     v and q_bar, plus the intermediate gradients of the stages.
@@ -213,11 +258,16 @@ def prefill_backward(q, k, v, qbar, B, alpha, gamma, sigma, dout, enable_gqa=Tru
     G = _group_size(Hq, Hkv, enable_gqa)
     s = _default_scale(D, scale)
     kbar = summarize(k, qbar, B)
-    mask, logp, _ = route_sequence(q, kbar, B, alpha, gamma, sigma, G, s)
+    kdiag = summarize_diagonal(k, qbar, B) if estimate_diagonal else None
+    mask, logp, _ = route_sequence(q, kbar, B, alpha, gamma, sigma, G, s, kdiag=kdiag)
     out, lse = attention_rows(q, k, v, mask, logp, B, s, G, list(range(L)))
     a = attention_backward_rows(q, k, v, mask, logp, B, s, G, dout)
-    r = routing_backward(q, kbar, B, alpha, gamma, sigma, G, s, a["dbias"])
+    r = routing_backward(q, kbar, B, alpha, gamma, sigma, G, s, a["dbias"], kdiag=kdiag)
     m = summarize_backward(k, qbar, B, r["dkbar"])
-    return dict(dq=a["dq"] + r["dq"], dk=a["dk"] + m["dk"], dv=a["dv"], dqbar=m["dqbar"],
-                dbias=a["dbias"], dkbar=r["dkbar"], du=r["du"], delta=a["delta"],
-                out=out, lse=lse, mask=mask, log_prior=logp)
+    dk, dqbar = a["dk"] + m["dk"], m["dqbar"]
+    if kdiag is not None:
+        md = summarize_diagonal_backward(k, qbar, B, r["dkdiag"])
+        dk, dqbar = dk + md["dk"], dqbar + md["dqbar"]
+    return dict(dq=a["dq"] + r["dq"], dk=dk, dv=a["dv"], dqbar=dqbar,
+                dbias=a["dbias"], dkbar=r["dkbar"], du=r["du"], dkdiag=r["dkdiag"],
+                delta=a["delta"], out=out, lse=lse, mask=mask, log_prior=logp)

@@ -20,8 +20,9 @@ def _inputs(seed, L=20, Hq=4, Hkv=2, D=6):
                 dout=rng.standard_normal((L, Hq, D)))
 
 
-def _loss(x, B, alpha, gamma, sigma):
-    r = O.prefill(x["q"], x["k"], x["v"], x["qbar"], B, alpha, gamma, sigma)
+def _loss(x, B, alpha, gamma, sigma, diag=False):
+    r = O.prefill(x["q"], x["k"], x["v"], x["qbar"], B, alpha, gamma, sigma,
+                  estimate_diagonal=diag)
     return float(np.sum(x["dout"] * r["out"]))
 
 
@@ -161,3 +162,53 @@ def test_key_columns_match_the_row_pass():
                                       lse, out, keys)
     np.testing.assert_allclose(cols["dk"], rows["dk"][keys], atol=1e-12)
     np.testing.assert_allclose(cols["dv"], rows["dv"][keys], atol=1e-12)
+
+
+@pytest.mark.parametrize("alpha,gamma,sigma", [(1.5, 4.0, 1.0), (2.0, 5.0, 1.0), (1.0, 2.0, 0.7)])
+def test_estimate_diagonal_backward_matches_finite_differences(alpha, gamma, sigma):
+    # the own-chunk entry of every routed row (reading E1) and its running
+    # summary are differentiated too
+    B = 4
+    x = _inputs(37)
+    s = 1.0 / math.sqrt(6)
+    kbar = O.summarize(x["k"], x["qbar"], B)
+    kd = O.summarize_diagonal(x["k"], x["qbar"], B)
+    _, _, th = O.route_sequence(x["q"], kbar, B, alpha, gamma, sigma, 2, s, kdiag=kd)
+    if alpha > 1.0:
+        # no routing decision (routed chunks or the own-chunk entry) near a threshold
+        mg = O.routing_margin(x["q"], kbar, B, gamma, s, 2, th, list(range(20)), 5)
+        assert np.min(mg) > 1e-4
+        ud = gamma * s * np.einsum("lgd,lgd->gl", x["q"], np.repeat(kd, 2, axis=1))
+        assert np.min(np.abs(ud - th)[:, B:]) > 1e-4
+    g = OB.prefill_backward(x["q"], x["k"], x["v"], x["qbar"], B, alpha, gamma, sigma,
+                            x["dout"], estimate_diagonal=True)
+    assert np.max(np.abs(g["dkdiag"])) > 0.0
+    rng = np.random.default_rng(8)
+    eps = 1e-6
+    for name, grad in (("q", g["dq"]), ("k", g["dk"]), ("qbar", g["dqbar"])):
+        arr = x[name]
+        for _ in range(12):
+            idx = tuple(int(rng.integers(0, n)) for n in arr.shape)
+            old = arr[idx]
+            arr[idx] = old + eps
+            lp = _loss(x, B, alpha, gamma, sigma, True)
+            arr[idx] = old - eps
+            lm = _loss(x, B, alpha, gamma, sigma, True)
+            arr[idx] = old
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - grad[idx]) <= 1e-6 + 1e-5 * abs(fd), (name, idx, fd, grad[idx])
+
+
+def test_diagonal_summary_backward_is_the_summary_backward_on_full_chunks():
+    # at a chunk's last row the running estimate is the chunk's summary, so
+    # a gradient placed only on those rows back-propagates as the summary's
+    B = 4
+    x = _inputs(38)
+    dkd = np.zeros((20, 2, 6))
+    dkb = np.random.default_rng(9).standard_normal((5, 2, 6))
+    for c in range(5):
+        dkd[c * B + B - 1] = dkb[c]
+    a = OB.summarize_diagonal_backward(x["k"], x["qbar"], B, dkd)
+    b = OB.summarize_backward(x["k"], x["qbar"], B, dkb)
+    np.testing.assert_allclose(a["dk"], b["dk"], atol=1e-12)
+    np.testing.assert_allclose(a["dqbar"], b["dqbar"], atol=1e-12)
