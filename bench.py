@@ -431,6 +431,14 @@ def main():
             t_bwd = time_it(stream, lambda: ops.attn_prefill_backward(
                 q, k, v, qbar, o_b, dout, lse_b, wp.B, alpha=wp.alpha, gamma=wp.gamma,
                 sigma=wp.sigma, workspace=ws_pb), reps)
+            # with estimate_diagonal: its own forward's output and LSE
+            o_g, lse_g, _ = ops.attn_prefill(q, k, v, qbar, wp.B, alpha=wp.alpha, gamma=wp.gamma,
+                                             sigma=wp.sigma, return_lse=True,
+                                             estimate_diagonal=True)
+            t_bwd_diag = time_it(stream, lambda: ops.attn_prefill_backward(
+                q, k, v, qbar, o_g, dout, lse_g, wp.B, alpha=wp.alpha, gamma=wp.gamma,
+                sigma=wp.sigma, estimate_diagonal=True, workspace=ws_pb), reps)
+            del o_g, lse_g
             ops.route(q, kbar, wp.Hkv, wp.B, alpha=1.0, gamma=wp.gamma, sigma=0.0,
                       mask_out=m2, log_prior_out=l2, log_prior=True, workspace=ws_route)
             o_d, lse_d = ops.attn_sparse(q, k, v, m2, l2, wp.B, return_lse=True)
@@ -440,7 +448,8 @@ def main():
             # the usual count of an attention backward: 2.5 times the forward's
             # products (S, dP, dV, dQ, dK; S is recomputed)
             cmp["backward"] = {
-                "dash_ms": t_bwd, "dense_attention_ms": t_dbwd,
+                "dash_ms": t_bwd, "dash_estimate_diagonal_ms": t_bwd_diag,
+                "dense_attention_ms": t_dbwd,
                 "dash_tflops": 2.5 * flops / (t_bwd * 1e-3) / 1e12,
                 "dense_tflops": 2.5 * dense_flops / (t_dbwd * 1e-3) / 1e12,
                 "speedup_vs_dense": t_dbwd / t_bwd}

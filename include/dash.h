@@ -348,7 +348,10 @@ dash_status dash_attn_sparse_backward(const dash_shape* shape, const void* q, co
  * gradient of its own; bf16 rounding of the summaries passes gradients
  * unchanged.  The support: as dash_attn_sparse_backward.
  *   q, k, v, qbar, alpha, alpha_per_seq, gamma, sigma, softmax_scale,
- *   enable_gqa     as in dash_attn_prefill (input)
+ *   enable_gqa, estimate_diagonal
+ *                  as in dash_attn_prefill (input); with estimate_diagonal the
+ *                  gradient also flows through each row's own-chunk entry of
+ *                  the entmax (it feeds no prior) and its running summary
  *   out, lse       the forward's output and LSE (input)
  *   dout           [T, Hq, D] dtype    (input)
  *   dq             [T, Hq, D] dtype    (output)
@@ -358,8 +361,8 @@ dash_status dash_attn_sparse_backward(const dash_shape* shape, const void* q, co
 dash_status dash_attn_prefill_backward(const dash_shape* shape, const void* q, const void* k,
                                        const void* v, const float* qbar, float alpha,
                                        const float* alpha_per_seq, float gamma, float sigma,
-                                       float softmax_scale,
-                                       int enable_gqa, const void* out, const void* dout,
+                                       float softmax_scale, int enable_gqa,
+                                       int estimate_diagonal, const void* out, const void* dout,
                                        const float* lse, void* dq, void* dk, void* dv,
                                        float* dqbar, void* workspace, size_t workspace_bytes,
                                        void* stream);

@@ -119,7 +119,7 @@ def lib():
                                             _P, _P, _P, _P, _P, _SZ, _P]
     L.dash_attn_prefill_backward.restype = _I
     L.dash_attn_prefill_backward.argtypes = [_SHAPE, _P, _P, _P, _P, _F, _P, _F, _F, _F, _I,
-                                             _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+                                             _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
     L.dash_cache_append.restype = _I
     L.dash_cache_append.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _P, _P, _P]
     _lib = L

@@ -205,7 +205,7 @@ BackwardWs backward_ws(const Geom& g) {
 // per-head terms of the routing backward.
 struct PrefillBwdWs {
   BackwardWs a;
-  size_t kbar, mask, logp, tau, db, sc, kbt, dkb, total;
+  size_t kbar, mask, logp, tau, db, sc, kbt, dkb, kdiag, dkdiag, total;
 };
 PrefillBwdWs prefill_bwd_ws(const Geom& g) {
   PrefillBwdWs w{};
@@ -227,6 +227,10 @@ PrefillBwdWs prefill_bwd_ws(const Geom& g) {
   o += align_up((size_t)g.num_seqs * g.Hkv * g.D * dash::route_bwd_cpad(g) * 2);
   w.dkb = o;
   o += align_up((size_t)(g.T / g.B) * g.Hkv * g.D * 4);
+  w.kdiag = o;  // estimate_diagonal: the rows' own-chunk estimates and their gradient
+  o += align_up((size_t)g.T * g.Hkv * g.D * elt(g));
+  w.dkdiag = o;
+  o += align_up((size_t)g.T * g.Hkv * g.D * 4);
   w.total = o;
   return w;
 }
@@ -663,8 +667,8 @@ dash_status dash_attn_sparse_backward(const dash_shape* shape, const void* q, co
 dash_status dash_attn_prefill_backward(const dash_shape* shape, const void* q, const void* k,
                                        const void* v, const float* qbar, float alpha,
                                        const float* alpha_per_seq, float gamma, float sigma,
-                                       float softmax_scale,
-                                       int enable_gqa, const void* out, const void* dout,
+                                       float softmax_scale, int enable_gqa,
+                                       int estimate_diagonal, const void* out, const void* dout,
                                        const float* lse, void* dq, void* dk, void* dv,
                                        float* dqbar, void* workspace, size_t workspace_bytes,
                                        void* stream) {
@@ -697,6 +701,12 @@ dash_status dash_attn_prefill_backward(const dash_shape* shape, const void* q, c
   float* tau = reinterpret_cast<float*>(at(workspace, w.tau));
   DASH_HIP(dash::launch_summarize(g, k, qbar, kbar, s));
   dash::RouteParams rp;
+  void* kdiag = nullptr;
+  if (estimate_diagonal) {
+    kdiag = at(workspace, w.kdiag);
+    DASH_HIP(dash::launch_diag_summary(g, k, qbar, kdiag, s));
+    rp.kdiag = kdiag;
+  }
   rp.q = q;
   rp.kbar = kbar;
   rp.alpha = alpha;
@@ -754,6 +764,8 @@ dash_status dash_attn_prefill_backward(const dash_shape* shape, const void* q, c
   rb.kbt = reinterpret_cast<const uint16_t*>(at(workspace, w.kbt));
   rb.dkb = reinterpret_cast<float*>(at(workspace, w.dkb));
   rb.cpad = dash::route_bwd_cpad(g);
+  rb.kdiag = kdiag;
+  rb.dkdiag = reinterpret_cast<float*>(at(workspace, w.dkdiag));
   DASH_HIP(dash::launch_zero(dqbar, (int64_t)g.Hkv * g.D, s));
   DASH_HIP(dash::launch_zero(rb.dkb, (int64_t)(g.T / g.B) * g.Hkv * g.D, s));
   DASH_HIP(dash::launch_route_bwd(g, rb, s));

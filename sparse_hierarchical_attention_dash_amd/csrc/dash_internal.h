@@ -132,6 +132,8 @@ struct RouteBwdParams {
   float* dk = nullptr;                  // [T, Hkv, D] fp32, accumulated
   float* dqbar = nullptr;               // [Hkv, D] fp32, accumulated (zeroed first)
   const uint16_t* kbt = nullptr;        // [seqs, Hkv, D, cpad] bf16 (filled here)
+  const void* kdiag = nullptr;          // [T, Hkv, D] own-chunk estimates, or null
+  float* dkdiag = nullptr;              // [T, Hkv, D] fp32, their gradient (written)
   float* dkb = nullptr;                 // [T/B rows, Hkv, D] fp32 dk_bar (zeroed first)
   int cpad = 0;                         // route_bwd_cpad(g)
   float alpha = 1.5f;

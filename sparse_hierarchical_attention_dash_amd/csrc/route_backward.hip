@@ -28,6 +28,10 @@
 // accumulates dk_bar = gamma s du^T Q (MFMA); slices meet by atomics.
 // kbar_sum_bwd_kernel (one workgroup per complete chunk and KV head): the
 // summary's backward into dk and dq_bar.
+// With estimate_diagonal, route_bwd_kernel also differentiates each row's
+// own-chunk entry (du_d = -r_d rho: it feeds no prior) into dq and the
+// estimate's gradient, and diag_sum_bwd_kernel takes that back through the
+// running summaries into dk and dq_bar.
 // bf16, G = 16 or 32; fixed-length or packed (varlen) sequences.
 #include "dash_device.h"
 #include "dash_internal.h"
@@ -72,6 +76,7 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
   __shared__ float Wp[CP];         // sum over the group's heads of p, then dp
   __shared__ uint8_t On[CP];       // the row's active chunks
   __shared__ float Hp[16][2];      // per head: threshold (x units) or max u; softmax sum
+  __shared__ float Dd[16];         // per head: du of the own-chunk entry
   const int row = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = lane & 15, gq = lane >> 4;
@@ -85,8 +90,12 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
   float4* sc = p.sc;
   if (n == 0) {
     if (tid < G) sc[(int64_t)(h * G + tid) * T + row] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (p.kdiag && tid < D) p.dkdiag[((int64_t)row * g.Hkv + h) * D + tid] = 0.f;
     return;
   }
+  // the row's own-chunk estimate, when given, is entry n of every head's entmax
+  const int ns = p.kdiag ? n + 1 : n;
+  const uint16_t* kdrow = (const uint16_t*)p.kdiag + ((int64_t)row * g.Hkv + h) * D;
   const float alpha = p.alpha_per_seq ? p.alpha_per_seq[s] : p.alpha;
   const bool smax = !(alpha > 1.f);
   const float am1 = alpha - 1.f;
@@ -101,15 +110,16 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
     bf16x8 qa[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qa[ks] = as_bf16x8(ldg16(qrow + 32 * ks + 8 * gq));
-    const int nct = (n + 15) >> 4;
+    const int nct = (ns + 15) >> 4;
     for (int ct = wv; ct < nct; ct += 4) {
-      const int c = min(ct * 16 + r, n - 1);
-      const uint16_t* krow = (const uint16_t*)p.kbar + (((kb0 + c) * g.Hkv + h) * (int64_t)D);
+      const int c = min(ct * 16 + r, ns - 1);
+      const uint16_t* krow =
+          c == n ? kdrow : (const uint16_t*)p.kbar + (((kb0 + c) * g.Hkv + h) * (int64_t)D);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         acc = mfma16x16x32(qa[ks], as_bf16x8(ldg16(krow + 32 * ks + 8 * gq)), acc);
-      if (ct * 16 + r < n) {
+      if (ct * 16 + r < ns) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) U[(4 * gq + j) * USTR + ct * 16 + r] = acc[j] * p.gamma_scale;
       }
@@ -122,10 +132,10 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
     const int qh = h * G + 16 * ht + hh;
     if (smax) {
       float mx = -INFINITY;
-      for (int c = r; c < n; c += 16) mx = fmaxf(mx, ur[c]);
+      for (int c = r; c < ns; c += 16) mx = fmaxf(mx, ur[c]);
       mx = row16_max(mx);
       float z = 0.f;
-      for (int c = r; c < n; c += 16) z += exp2f((ur[c] - mx) * kLog2e);
+      for (int c = r; c < ns; c += 16) z += exp2f((ur[c] - mx) * kLog2e);
       z = row16_sum(z);
       if (r == 0) { Hp[hh][0] = mx; Hp[hh][1] = z; }
     } else if (r == 0) {
@@ -168,6 +178,7 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
     drow[c] = dp;
   }
   // ---- pass 2 per head tile: r, rho, du; dq += gamma s du K_bar
+  float dkd = 0.f;  // thread tid < D: dim tid of the estimate's gradient
   for (int ht = 0; ht < HT; ++ht) {
     __syncthreads();
     if (HT > 1) {
@@ -185,9 +196,13 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
         num = fmaf(rr, Wp[c], num);
         den += rr;
       }
+      // the own-chunk entry: in the entmax, no prior (its dp is 0)
+      const float rd = (p.kdiag && r == 0) ? rterm(ur[n], hh) : 0.f;
+      den += rd;
       num = row16_sum(num);
       den = row16_sum(den);
       const float rho = den > 0.f ? num / den : 0.f;
+      if (p.kdiag && r == 0) Dd[hh] = -rd * rho;
       // every lane of the head has read its U entries above; du overwrites them
       for (int c = r; c < n32; c += 16) {
         float du = 0.f;
@@ -214,13 +229,22 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
         acc = mfma16x16x32(as_bf16x8(av), as_bf16x8(ldg16(ktr + c0)), acc);
       }
       // lane (gq, r): heads 16 ht + 4 gq + j, dim 16 dt + r
+      const float kd = p.kdiag ? bf16_to_f32(kdrow[16 * dt + r]) : 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float* dq = p.dq + ((int64_t)row * g.Hq + h * G + 16 * ht + 4 * gq + j) * D + 16 * dt + r;
-        *dq += p.gamma_scale * acc[j];
+        const float add = p.kdiag ? fmaf(Dd[4 * gq + j], kd, acc[j]) : acc[j];
+        *dq += p.gamma_scale * add;
       }
     }
+    // the estimate's gradient: gamma s sum over the tile's heads of du_d q
+    if (p.kdiag && tid < D) {
+      const uint16_t* qh = (const uint16_t*)p.q + ((int64_t)row * g.Hq + h * G + 16 * ht) * D + tid;
+#pragma unroll 4
+      for (int hh = 0; hh < 16; ++hh) dkd = fmaf(Dd[hh], bf16_to_f32(qh[hh * D]), dkd);
+    }
   }
+  if (p.kdiag && tid < D) p.dkdiag[((int64_t)row * g.Hkv + h) * D + tid] = p.gamma_scale * dkd;
 }
 
 // dk_bar of 64 chunks: rows that route to any of them, in slices over blockIdx.y
@@ -467,6 +491,101 @@ __global__ __launch_bounds__(256) void kbar_sum_bwd_kernel(Geom g, RouteBwdParam
   }
 }
 
+// The backward of every row's own-chunk estimate (k_hat_i = sum over the
+// chunk's keys t <= i of pi_it k_t, pi_i = softmax(s <q_bar, k_t>) over those
+// keys): one workgroup per chunk and KV head.  Row i's prefix softmax comes
+// from the keys' logits z and its running max and sum; thread i forms
+// dpi_it = <dk_hat_i, k_t> (dk_hat_i in registers), c_i = sum_t pi dpi and
+// the column sums of dz_it = pi_it (dpi_it - c_i); then
+// dk_t += sum_{i >= t} pi_it dk_hat_i + s colsum_t q_bar and
+// dq_bar += s sum_t colsum_t k_t.
+template <int D>
+__global__ __launch_bounds__(256) void diag_sum_bwd_kernel(Geom g, RouteBwdParams p) {
+  constexpr int NTH = 256;
+  constexpr int KROW = D + 8;
+  __shared__ __align__(16) uint16_t Ks[128 * KROW];
+  __shared__ float Z[128], Mx[128], Sm[128], Cs[128], Qb[D];
+  const int c = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
+  const int tid = threadIdx.x;
+  const SeqInfo si = seq_info(g.cu_seqlens, g.cu_chunks, s, g.max_seqlen, g.B);
+  const int B = g.B;
+  const int r0 = c * B;
+  if (c == 0 || r0 >= si.len) return;  // rows of a sequence's first chunk route nothing
+  const int nr = min(B, si.len - r0);
+  const int64_t tok0 = si.start + r0;
+  const float sD = 1.f / sqrtf((float)D);
+  // the chunk's keys (bf16, padded rows) and q_bar
+  for (int idx = tid; idx < nr * (D / 8); idx += NTH) {
+    const int t = idx / (D / 8), d0 = (idx % (D / 8)) * 8;
+    *reinterpret_cast<u32x4*>(&Ks[t * KROW + d0]) =
+        ldg16((const uint16_t*)p.k + ((tok0 + t) * g.Hkv + h) * (int64_t)D + d0);
+  }
+  for (int d = tid; d < D; d += NTH) Qb[d] = p.qbar[h * D + d];
+  if (tid < 128) Cs[tid] = 0.f;
+  __syncthreads();
+  if (tid < nr) {
+    float a = 0.f;
+    for (int d = 0; d < D; ++d) a = fmaf(bf16_to_f32(Ks[tid * KROW + d]), Qb[d], a);
+    Z[tid] = a * sD;
+  }
+  __syncthreads();
+  // row i's running max and sum over keys t <= i
+  if (tid < nr) {
+    float m = -INFINITY;
+    for (int t = 0; t <= tid; ++t) m = fmaxf(m, Z[t]);
+    float sum = 0.f;
+    for (int t = 0; t <= tid; ++t) sum += __expf(Z[t] - m);
+    Mx[tid] = m;
+    Sm[tid] = sum;
+  }
+  __syncthreads();
+  if (tid < nr) {
+    const int i = tid;
+    float dkh[D];
+    const float* src = p.dkdiag + ((tok0 + i) * g.Hkv + h) * (int64_t)D;
+#pragma unroll
+    for (int d = 0; d < D; d += 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(src + d);
+      dkh[d] = v[0];
+      dkh[d + 1] = v[1];
+      dkh[d + 2] = v[2];
+      dkh[d + 3] = v[3];
+    }
+    const float m = Mx[i], inv = 1.f / Sm[i];
+    // c_i = sum_t pi dpi, then the column sums of dz
+    float ci = 0.f;
+    for (int t = 0; t <= i; ++t) {
+      float dp = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) dp = fmaf(dkh[d], bf16_to_f32(Ks[t * KROW + d]), dp);
+      ci = fmaf(__expf(Z[t] - m) * inv, dp, ci);
+    }
+    for (int t = 0; t <= i; ++t) {
+      float dp = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) dp = fmaf(dkh[d], bf16_to_f32(Ks[t * KROW + d]), dp);
+      const float pi = __expf(Z[t] - m) * inv;
+      atomicAdd(&Cs[t], pi * (dp - ci));
+    }
+  }
+  __syncthreads();
+  // dk_t += sum_{i >= t} pi_it dk_hat_i + s Cs_t q_bar: thread (t, d), d fastest
+  for (int idx = tid; idx < nr * D; idx += NTH) {
+    const int t = idx / D, d = idx - (idx / D) * D;
+    float acc = sD * Cs[t] * Qb[d];
+    for (int i = t; i < nr; ++i)
+      acc = fmaf(__expf(Z[t] - Mx[i]) / Sm[i],
+                 p.dkdiag[((tok0 + i) * g.Hkv + h) * (int64_t)D + d], acc);
+    p.dk[((tok0 + t) * g.Hkv + h) * (int64_t)D + d] += acc;
+  }
+  // dq_bar += s sum_t Cs_t k_t
+  for (int d = tid; d < D; d += NTH) {
+    float acc = 0.f;
+    for (int t = 0; t < nr; ++t) acc = fmaf(Cs[t], bf16_to_f32(Ks[t * KROW + d]), acc);
+    atomicAdd(&p.dqbar[h * D + d], sD * acc);
+  }
+}
+
 int route_bwd_cpad(const Geom& g) { return ((g.max_seqlen / g.B) + 31) & ~31; }
 
 hipError_t launch_route_bwd(const Geom& g, const RouteBwdParams& p, hipStream_t st) {
@@ -507,6 +626,14 @@ hipError_t launch_route_bwd(const Geom& g, const RouteBwdParams& p, hipStream_t 
     hipLaunchKernelGGL(kbar_sum_bwd_kernel<64>, cgrid, dim3(256), 0, st, g, p);
   else
     hipLaunchKernelGGL(kbar_sum_bwd_kernel<128>, cgrid, dim3(256), 0, st, g, p);
+  if (p.kdiag) {
+    // every chunk, the last partial one included
+    dim3 dgrid((g.max_seqlen + g.B - 1) / g.B, g.num_seqs, g.Hkv);
+    if (g.D == 64)
+      hipLaunchKernelGGL(diag_sum_bwd_kernel<64>, dgrid, dim3(256), 0, st, g, p);
+    else
+      hipLaunchKernelGGL(diag_sum_bwd_kernel<128>, dgrid, dim3(256), 0, st, g, p);
+  }
   return hipGetLastError();
 }
 

@@ -212,7 +212,8 @@ def attn_prefill(q, k, v, qbar, chunk_size, *, alpha=1.5, gamma=1.0, sigma=1.0,
 
 def attn_prefill_backward(q, k, v, qbar, out, dout, lse, chunk_size, *, alpha=1.5, gamma=1.0,
                           sigma=1.0, softmax_scale=0.0, enable_gqa=True, alpha_per_seq=None,
-                          cu_seqlens=None, max_seqlen=None, workspace=None):
+                          cu_seqlens=None, max_seqlen=None, estimate_diagonal=False,
+                          workspace=None):
     """Backward of attn_prefill (fixed-length sequences of max_seqlen tokens,
     one of T if None, or packed by cu_seqlens): returns (dq, dk, dv, dqbar
     [Hkv, D] fp32)."""
@@ -232,7 +233,8 @@ def attn_prefill_backward(q, k, v, qbar, out, dout, lse, chunk_size, *, alpha=1.
     L.check("dash_attn_prefill_backward", L.lib().dash_attn_prefill_backward(
         ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(qb), float(alpha),
         _ptr(alpha_per_seq), float(gamma), float(sigma), float(softmax_scale), int(enable_gqa),
-        _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dqbar),
+        int(estimate_diagonal), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(dqbar),
         _ptr(workspace), n, _stream(dev)))
     return dq, dk, dv, dqbar
 

@@ -296,7 +296,7 @@ def test_prefill_backward_checks(lib):
                  n=need, gqa=1)
         a.update(kw)
         return lib.dash_attn_prefill_backward(ctypes.byref(sh), a["q"], a["k"], a["v"], a["qb"],
-                                              alpha, None, gamma, sigma, 0.0, a["gqa"], a["o"],
+                                              alpha, None, gamma, sigma, 0.0, a["gqa"], 0, a["o"],
                                               a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
                                               a["dqb"], a["ws"], a["n"], None)
 

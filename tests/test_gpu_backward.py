@@ -340,3 +340,59 @@ def test_backward_varlen(case):
         e = rel_err(dqb.cpu().numpy().astype(np.float64), ref_dqbar)
         assert e <= REL, ("dqbar", e)
     flush(f"  varlen backward {lens}: ok (all rows clear of thresholds: {all_clear})")
+
+
+DCASES = [
+    # name, L, Hq, Hkv, D, B, alpha, gamma, sigma, seed
+    ("diag-g16-d128-a1.5", 448, 16, 1, 128, 64, 1.5, 20.0, 1.0, 111),
+    ("diag-g32-d64-b128-a2", 400, 32, 1, 64, 128, 2.0, 20.0, 1.0, 115),
+    ("diag-g16-softmax-ragged", 333, 32, 2, 128, 64, 1.0, 8.0, 1.0, 111),
+]
+
+
+@pytest.mark.parametrize("case", DCASES, ids=lambda c: c[0])
+def test_prefill_backward_estimate_diagonal(case):
+    """The whole backward with estimate_diagonal (reading E1): the oracle's
+    stages on the GPU's summaries and own-chunk estimates, which the gradient
+    passes through unchanged.  Routing decisions (routed chunks and the
+    own-chunk entry) at least 3e-5 from their thresholds."""
+    from oracle import dash_oracle as O
+
+    name, L, Hq, Hkv, D, B, alpha, gamma, sigma, seed = case
+    flush(f"prefill backward {name}")
+    d = W.gen_prefill(L, Hq, Hkv, D, seed=seed)
+    q, qx = to_dev(d["q"], "bf16")
+    k, kx = to_dev(d["k"], "bf16")
+    v, vx = to_dev(d["v"], "bf16")
+    rng = np.random.default_rng(112)
+    do, dox = to_dev(rng.standard_normal((L, Hq, D)).astype(np.float32), "bf16")
+    qb = torch.from_numpy(d["qbar"]).cuda()
+    out, lse, _ = ops.attn_prefill(q, k, v, qb, B, alpha=alpha, gamma=gamma, sigma=sigma,
+                                   return_lse=True, estimate_diagonal=True)
+    dq, dk, dv, dqb = ops.attn_prefill_backward(q, k, v, qb, out, do, lse, B, alpha=alpha,
+                                                gamma=gamma, sigma=sigma,
+                                                estimate_diagonal=True)
+    kbx = ops.summarize(k, qb, B).to(torch.float64).cpu().numpy()
+    kdx = ops.summarize_diagonal(k, qb, B).to(torch.float64).cpu().numpy()
+    torch.cuda.synchronize()
+    G, s = Hq // Hkv, 1 / math.sqrt(D)
+    S = -(-L // B)
+    mask, logp, th = O.route_sequence(qx, kbx, B, alpha, gamma, sigma, G, s, kdiag=kdx)
+    if alpha > 1.0:
+        mg = O.routing_margin(qx, kbx, B, gamma, s, G, th, list(range(L)), S)
+        assert np.min(mg) > 3e-5, "test data too close to a routing threshold"
+        ud = gamma * s * np.einsum("lgd,lgd->gl", qx, np.repeat(kdx, G, axis=1))
+        assert np.min(np.abs(ud - th)[:, B:]) > 3e-5, "own-chunk entry too close to a threshold"
+    a = OB.attention_backward_rows(qx, kx, vx, mask, logp, B, s, G, dox)
+    r = OB.routing_backward(qx, kbx, B, alpha, gamma, sigma, G, s, a["dbias"], kdiag=kdx)
+    m = OB.summarize_backward(kx, d["qbar"], B, r["dkbar"])
+    md = OB.summarize_diagonal_backward(kx, d["qbar"], B, r["dkdiag"])
+    ref = {"dq": a["dq"] + r["dq"], "dk": a["dk"] + m["dk"] + md["dk"], "dv": a["dv"],
+           "dqbar": m["dqbar"] + md["dqbar"]}
+    # the own-chunk path's share is visible, so that a dropped term fails
+    assert np.max(np.abs(md["dk"])) > 0.02 * np.max(np.abs(a["dk"]))
+    errs = {}
+    for nm, gt in (("dq", dq), ("dk", dk), ("dv", dv), ("dqbar", dqb)):
+        errs[nm] = rel_err(gt.to(torch.float64).cpu().numpy(), ref[nm])
+        assert errs[nm] <= REL, (nm, errs[nm])
+    flush(f"  prefill backward {name}: " + " ".join(f"{k_} {v_:.2e}" for k_, v_ in errs.items()))
