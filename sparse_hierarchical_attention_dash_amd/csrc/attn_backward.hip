@@ -65,8 +65,8 @@ __global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ x, int64_
   if (i < n) x[i] = 0.f;
 }
 
-constexpr int kBkThreads = 256;
 constexpr int kDkdvSlice = 4096;  // rows per workgroup of bwd_dkdv_kernel
+constexpr int kDkdvTiles = 1;     // 16-key tiles per wave of bwd_dkdv_kernel (2: slower)
 
 // The transposed copy of one (token, KV head): 16-byte units of two adjacent
 // dims x four heads, unit (quad, pair) at (quad D/2 + pair) 16 bytes,
@@ -102,34 +102,38 @@ __global__ __launch_bounds__(256) void bwd_headt_kernel(Geom g, const uint16_t* 
   }
 }
 
-template <int D, int HT>
+template <int D, int HT, int KT>
 struct DkdvCfg {
+  static constexpr int NW = 4 / KT;                    // waves: KT 16-key tiles each
+  static constexpr int NTH = 64 * NW;
   static constexpr int G = 16 * HT;
   static constexpr int NS = HT == 1 ? 4 : 3;           // ring stages, one row each
   static constexpr int ABYTES = G * D * 2;             // one array of one row
   static constexpr int SBYTES = 4 * ABYTES;            // Q, dO, Q^T, dO^T
   static constexpr int AU = ABYTES / 16;               // 16-byte units per array
-  static constexpr int NUT = 4 * AU / kBkThreads;      // unit loads per thread per stage
+  static constexpr int NUT = 4 * AU / NTH;             // unit loads per thread per stage
   static constexpr int PER = NUT + 2;                  // loads per wave per stage
-  static_assert(4 * AU % kBkThreads == 0, "units per stage");
+  static_assert(4 * AU % NTH == 0, "units per stage");
 };
 
-template <int D, int HT>
-__global__ __launch_bounds__(kBkThreads) void bwd_dkdv_kernel(Geom g, BwdParams p, float* dk,
-                                                              float* dv) {
-  using C = DkdvCfg<D, HT>;
+template <int D, int HT, int KT>
+__global__ __launch_bounds__(256 / KT) void bwd_dkdv_kernel(Geom g, BwdParams p, float* dk,
+                                                            float* dv) {
+  using C = DkdvCfg<D, HT, KT>;
+  static_assert(C::NTH == 256 / KT, "launch bounds");
   constexpr int G = C::G;
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   constexpr int NS = C::NS;
-  constexpr int NTH = kBkThreads;
+  constexpr int NTH = C::NTH;
+  constexpr int NW = C::NW;
   constexpr int UPH = D / 8;      // units per head row of Q / dO
   constexpr int NR = 1024;        // rows scanned per compaction
   __shared__ __align__(16) uint8_t Ring[NS * C::SBYTES];
-  __shared__ __align__(16) float Sc[NS][4][64];  // per wave: LSE (lanes < G), D (G .. 2G-1)
-  __shared__ __align__(16) float Bz[NS][4][4];   // per wave: the row's bias
+  __shared__ __align__(16) float Sc[NS][NW][64];  // per wave: LSE (lanes < G), D (G .. 2G-1)
+  __shared__ __align__(16) float Bz[NS][NW][4];   // per wave: the row's bias
   __shared__ int Rows[NR];
-  __shared__ int Wcnt[NR / 256][NTH / 64];
+  __shared__ int Wcnt[NR / NTH][NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = lane & 15, gq = lane >> 4;
@@ -147,26 +151,31 @@ __global__ __launch_bounds__(kBkThreads) void bwd_dkdv_kernel(Geom g, BwdParams 
   const int64_t T = g.T;
   const unsigned long long* __restrict__ mask = (const unsigned long long*)p.mask;
 
-  // this wave's 16 keys: K and V rows as the B operand of Q K^T and dO V^T
-  const int mykey = key0 + 16 * wv + r;
-  bf16x8 kf[KS], vf[KS];
-  {
-    const int64_t row = ((si.start + min(mykey, kmax)) * g.Hkv + h) * (int64_t)D;
+  // this wave's KT tiles of 16 keys: K and V rows as the B operand of Q K^T
+  // and dO V^T
+  int mykey[KT];
+  bf16x8 kf[KT][KS], vf[KT][KS];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    mykey[kt] = key0 + 16 * (KT * wv + kt) + r;
+    const int64_t row = ((si.start + min(mykey[kt], kmax)) * g.Hkv + h) * (int64_t)D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      kf[ks] = as_bf16x8(ldg16((const uint16_t*)p.k + row + 32 * ks + 8 * gq));
-      vf[ks] = as_bf16x8(ldg16((const uint16_t*)p.v + row + 32 * ks + 8 * gq));
+      kf[kt][ks] = as_bf16x8(ldg16((const uint16_t*)p.k + row + 32 * ks + 8 * gq));
+      vf[kt][ks] = as_bf16x8(ldg16((const uint16_t*)p.v + row + 32 * ks + 8 * gq));
     }
   }
   // the operand loads complete here, so that the compiler's own waits for them
   // do not land inside the ring loop, where they would also wait for the ring
   wait_vm<0>();
-  f32x4 adk[DT], adv[DT];
+  f32x4 adk[KT][DT], adv[KT][DT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    adk[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    adv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      adk[kt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      adv[kt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
   const float sl2 = p.scale * kLog2e;
   const uint16_t* qg = (const uint16_t*)p.q;
   const uint16_t* dg = (const uint16_t*)p.dout;
@@ -212,37 +221,55 @@ __global__ __launch_bounds__(kBkThreads) void bwd_dkdv_kernel(Geom g, BwdParams 
     const float bz = own ? 0.f : Bz[slot][wv][0] * kLog2e;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-      f32x4 sacc = {0.f, 0.f, 0.f, 0.f}, pacc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 sacc[KT], pacc[KT];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        pacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
       const int j = 16 * ht + r;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
+        // one read of the row's Q and dO fragments serves the wave's KT key tiles
         const int off = 16 * (j * UPH + ((4 * ks + gq) ^ (j % UPH)));
-        sacc = mfma16x16x32(as_bf16x8(lds_read16(Qs + off)), kf[ks], sacc);
-        pacc = mfma16x16x32(as_bf16x8(lds_read16(Ds + off)), vf[ks], pacc);
-      }
-      // lane (gq, r): heads 16 ht + 4 gq + j, key mykey
-      float pv[4], ds[4];
+        const bf16x8 qf = as_bf16x8(lds_read16(Qs + off)), df = as_bf16x8(lds_read16(Ds + off));
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int hh = 16 * ht + 4 * gq + jj;
-        float e = __builtin_amdgcn_exp2f(fmaf(sacc[jj], sl2, bz - Sc[slot][wv][hh] * kLog2e));
-        if (own) e = mykey <= row ? e : 0.f;
-        e = mykey <= kmax ? e : 0.f;
-        pv[jj] = e;
-        ds[jj] = e * (pacc[jj] - Sc[slot][wv][G + hh]);
+        for (int kt = 0; kt < KT; ++kt) {
+          sacc[kt] = mfma16x16x32(qf, kf[kt][ks], sacc[kt]);
+          pacc[kt] = mfma16x16x32(df, vf[kt][ks], pacc[kt]);
+        }
       }
-      const u32x2 pb = {cvt_pk_bf16(pv[0], pv[1]), cvt_pk_bf16(pv[2], pv[3])};
-      const u32x2 sb = {cvt_pk_bf16(ds[0], ds[1]), cvt_pk_bf16(ds[2], ds[3])};
+      // lane (gq, r): heads 16 ht + 4 gq + j, key mykey[kt]
+      u32x2 pb[KT], sb[KT];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        float pv[4], ds[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int hh = 16 * ht + 4 * gq + jj;
+          float e = __builtin_amdgcn_exp2f(fmaf(sacc[kt][jj], sl2, bz - Sc[slot][wv][hh] * kLog2e));
+          if (own) e = mykey[kt] <= row ? e : 0.f;
+          e = mykey[kt] <= kmax ? e : 0.f;
+          pv[jj] = e;
+          ds[jj] = e * (pacc[kt][jj] - Sc[slot][wv][G + hh]);
+        }
+        pb[kt] = u32x2{cvt_pk_bf16(pv[0], pv[1]), cvt_pk_bf16(pv[2], pv[3])};
+        sb[kt] = u32x2{cvt_pk_bf16(ds[0], ds[1]), cvt_pk_bf16(ds[2], ds[3])};
+      }
       const int quad = 4 * ht + gq;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        // A = X^T tile: dims 16 dt + r, heads 16 ht + 4 gq .. +3
+        // A = X^T tile: dims 16 dt + r, heads 16 ht + 4 gq .. +3 (one read for
+        // the KT key tiles)
         const int off = 16 * (quad * (D / 2) + 8 * dt + (r >> 1)) + 8 * (r & 1);
         typedef const __attribute__((address_space(3))) u32x2 lds_u32x2;
         const u32x2 ta = *reinterpret_cast<lds_u32x2*>(Dt + off);
         const u32x2 tq = *reinterpret_cast<lds_u32x2*>(Qt + off);
-        adv[dt] = mfma16x16x16(as_s16x4(ta), as_s16x4(pb), adv[dt]);
-        adk[dt] = mfma16x16x16(as_s16x4(tq), as_s16x4(sb), adk[dt]);
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+          adv[kt][dt] = mfma16x16x16(as_s16x4(ta), as_s16x4(pb[kt]), adv[kt][dt]);
+          adk[kt][dt] = mfma16x16x16(as_s16x4(tq), as_s16x4(sb[kt]), adk[kt][dt]);
+        }
       }
     }
   };
@@ -250,17 +277,18 @@ __global__ __launch_bounds__(kBkThreads) void bwd_dkdv_kernel(Geom g, BwdParams 
   int seen = 0;  // rows this workgroup visited
   for (int r0 = rlo; r0 < rhi; r0 += NR) {
     // ---- rows r0 .. r0+1023 that see the block, compacted in order
-    bool on[NR / 256];
-    uint64_t bal[NR / 256];
-    unsigned long long mw[NR / 256];
+    constexpr int NQ = NR / NTH;
+    bool on[NQ];
+    uint64_t bal[NQ];
+    unsigned long long mw[NQ];
 #pragma unroll
-    for (int q = 0; q < NR / 256; ++q) {  // the mask words first, all in flight
-      const int i = r0 + 256 * q + tid;
+    for (int q = 0; q < NQ; ++q) {  // the mask words first, all in flight
+      const int i = r0 + NTH * q + tid;
       mw[q] = i >= cend && i < rhi ? mask[((int64_t)h * T + si.start + i) * g.W + (c >> 6)] : 0ull;
     }
 #pragma unroll
-    for (int q = 0; q < NR / 256; ++q) {
-      const int i = r0 + 256 * q + tid;
+    for (int q = 0; q < NQ; ++q) {
+      const int i = r0 + NTH * q + tid;
       // the block's own chunk: causal (i >= key0 here); later rows: the mask
       on[q] = i < rhi && (i < cend || ((mw[q] >> (c & 63)) & 1ull));
       bal[q] = __ballot(on[q]);
@@ -269,14 +297,14 @@ __global__ __launch_bounds__(kBkThreads) void bwd_dkdv_kernel(Geom g, BwdParams 
     __syncthreads();
     int total = 0;
 #pragma unroll
-    for (int q = 0; q < NR / 256; ++q) {
+    for (int q = 0; q < NQ; ++q) {
       int before = total;
 #pragma unroll
-      for (int w = 0; w < NTH / 64; ++w) {
+      for (int w = 0; w < NW; ++w) {
         before += w < wv ? Wcnt[q][w] : 0;
         total += Wcnt[q][w];
       }
-      if (on[q]) Rows[before + __popcll(bal[q] & ((1ull << lane) - 1ull))] = r0 + 256 * q + tid;
+      if (on[q]) Rows[before + __popcll(bal[q] & ((1ull << lane) - 1ull))] = r0 + NTH * q + tid;
     }
     __syncthreads();
     seen += total;
@@ -297,14 +325,17 @@ __global__ __launch_bounds__(kBkThreads) void bwd_dkdv_kernel(Geom g, BwdParams 
   }
   // ---- add this slice's sums for the wave's keys: lane (gq, r) holds dims
   // 16 dt + 4 gq .. +3 of key mykey
-  if (seen > 0 && mykey <= kmax) {
-    const int64_t row = ((si.start + mykey) * g.Hkv + h) * (int64_t)D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+  for (int kt = 0; kt < KT; ++kt) {
+    if (seen > 0 && mykey[kt] <= kmax) {
+      const int64_t row = ((si.start + mykey[kt]) * g.Hkv + h) * (int64_t)D;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        atomicAdd(dk + row + 16 * dt + 4 * gq + j, adk[dt][j] * p.scale);
-        atomicAdd(dv + row + 16 * dt + 4 * gq + j, adv[dt][j]);
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          atomicAdd(dk + row + 16 * dt + 4 * gq + j, adk[kt][dt][j] * p.scale);
+          atomicAdd(dv + row + 16 * dt + 4 * gq + j, adv[kt][dt][j]);
+        }
       }
     }
   }
@@ -357,8 +388,9 @@ hipError_t launch_bwd_dkdv(const Geom& g, const BwdParams& p, float* dk, float* 
   hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dv, n);
   dim3 grid((g.max_seqlen + 63) / 64, (g.max_seqlen + kDkdvSlice - 1) / kDkdvSlice,
             g.num_seqs * g.Hkv);
-#define DASH_BK(DD, HH)                                                                    \
-  hipLaunchKernelGGL((bwd_dkdv_kernel<DD, HH>), grid, dim3(kBkThreads), 0, st, g, p, dk, dv)
+#define DASH_BK(DD, HH)                                                              \
+  hipLaunchKernelGGL((bwd_dkdv_kernel<DD, HH, kDkdvTiles>), grid,                      \
+                     dim3(DkdvCfg<DD, HH, kDkdvTiles>::NTH), 0, st, g, p, dk, dv)
   if (g.G == 16) {
     if (g.D == 64) DASH_BK(64, 1); else DASH_BK(128, 1);
   } else {
