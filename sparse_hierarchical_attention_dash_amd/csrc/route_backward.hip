@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void kbar_t_kernel(Geom g, const uint16_t* __r
 }
 
 template <int D, int CP>
-__global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p) {
+__global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p, int row0) {
   constexpr int NTH = 256;
   constexpr int KS = D / 32;
   constexpr int USTR = CP + 16;
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
   __shared__ uint8_t On[CP];       // the row's active chunks
   __shared__ float Hp[16][2];      // per head: threshold (x units) or max u; softmax sum
   __shared__ float Dd[16];         // per head: du of the own-chunk entry
-  const int row = blockIdx.x, h = blockIdx.y;
+  const int row = row0 + (int)blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = lane & 15, gq = lane >> 4;
   const int64_t T = g.T;
@@ -596,18 +596,36 @@ hipError_t launch_route_bwd(const Geom& g, const RouteBwdParams& p, hipStream_t 
     hipLaunchKernelGGL(kbar_t_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, g,
                        (const uint16_t*)p.kbar, const_cast<uint16_t*>(p.kbt), p.cpad);
   }
-  dim3 grid((unsigned)g.T, g.Hkv);
-#define DASH_RB(DD, CPV) hipLaunchKernelGGL((route_bwd_kernel<DD, CPV>), grid, dim3(256), 0, st, g, p)
-#define DASH_RB_CP(DD)                                  \
-  do {                                                  \
-    if (g.C_slots <= 256) DASH_RB(DD, 256);             \
-    else if (g.C_slots <= 512) DASH_RB(DD, 512);        \
-    else if (g.C_slots <= 1024) DASH_RB(DD, 1024);      \
-    else DASH_RB(DD, 2048);                             \
+  // rows by range of routable chunks (one sequence): a row at position i has
+  // floor(i/B) of them, so the rows below CP*B fit the CP-wide variant (less
+  // LDS, more workgroups per CU); the longest rows first
+  auto launch_rows = [&](int cp, int64_t lo, int64_t hi) {
+    if (hi <= lo) return;
+    dim3 grid((unsigned)(hi - lo), g.Hkv);
+    const int r0 = (int)lo;
+#define DASH_RB(DD, CPV) \
+  hipLaunchKernelGGL((route_bwd_kernel<DD, CPV>), grid, dim3(256), 0, st, g, p, r0)
+#define DASH_RB_CP(DD)                   \
+  do {                                   \
+    if (cp == 256) DASH_RB(DD, 256);     \
+    else if (cp == 512) DASH_RB(DD, 512); \
+    else if (cp == 1024) DASH_RB(DD, 1024); \
+    else DASH_RB(DD, 2048);              \
   } while (0)
-  if (g.D == 64) DASH_RB_CP(64); else DASH_RB_CP(128);
+    if (g.D == 64) DASH_RB_CP(64); else DASH_RB_CP(128);
 #undef DASH_RB_CP
 #undef DASH_RB
+  };
+  const int cpmax = g.C_slots <= 256 ? 256 : g.C_slots <= 512 ? 512 : g.C_slots <= 1024 ? 1024 : 2048;
+  if (!g.cu_seqlens && g.num_seqs == 1) {
+    for (int cp = cpmax; cp >= 256; cp /= 2) {
+      const int64_t hi = std::min<int64_t>(g.T, (int64_t)cp * g.B);
+      const int64_t lo = cp == 256 ? 0 : std::min<int64_t>(g.T, (int64_t)(cp / 2) * g.B);
+      launch_rows(cp, lo, hi);
+    }
+  } else {
+    launch_rows(cpmax, 0, g.T);
+  }
   if (cs == 0) return hipGetLastError();
   // chunk pass: 64-chunk tiles x row slices, about 2048 workgroups in all
   const int tiles = (cs + 63) / 64;
