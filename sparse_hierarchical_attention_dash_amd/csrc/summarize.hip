@@ -213,6 +213,20 @@ __device__ __forceinline__ void diag_scan(KeyFn key, int len, const float* __res
     d += xor32(d);
     return d * sc;
   };
+  // write position t's estimate from the running state
+  auto emit = [&](int t) {
+    const float inv = 1.f / l;
+    char* o = (char*)out(t);
+    if constexpr (BF16) {
+      if constexpr (EPL == 2)
+        *reinterpret_cast<uint32_t*>(o + 4 * lane) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+      else
+        *reinterpret_cast<uint16_t*>(o + 2 * lane) = (uint16_t)f32_to_bf16(acc[0] * inv);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) reinterpret_cast<float*>(o)[EPL * lane + e] = acc[e] * inv;
+    }
+  };
   // fold key t (its EPL elements in x, score z) into the running state;
   // write out(t)
   auto step = [&](int t, const float (&x)[EPL], float z) {
@@ -223,33 +237,22 @@ __device__ __forceinline__ void diag_scan(KeyFn key, int len, const float* __res
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, x[e], acc[e] * a);
     m = mn;
-    if (ALL || t == len - 1) {
-      const float inv = 1.f / l;
-      char* o = (char*)out(t);
-      if constexpr (BF16) {
-        if constexpr (EPL == 2)
-          *reinterpret_cast<uint32_t*>(o + 4 * lane) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-        else
-          *reinterpret_cast<uint16_t*>(o + 2 * lane) = (uint16_t)f32_to_bf16(acc[0] * inv);
-      } else {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e)
-          reinterpret_cast<float*>(o)[EPL * lane + e] = acc[e] * inv;
-      }
-    }
+    if (ALL || t == len - 1) emit(t);
   };
   if constexpr (BF16) {
     // every key's elements (one 32- or 16-bit word per lane) are loaded up
-    // front, so the scan waits for memory once (len <= MAXK = B)
+    // front, so the scan waits for memory once (len <= MAXK = B); the loads
+    // are unconditional, keys past len re-reading key len - 1
+    const char* kbase = (const char*)key(0);
+    const int64_t kstride = (const char*)key(1) - kbase;
     uint32_t raw[MAXK];
 #pragma unroll
     for (int t = 0; t < MAXK; ++t) {
-      if (t < len) {
-        const char* row = (const char*)key(t);
-        raw[t] = EPL == 2 ? *reinterpret_cast<const uint32_t*>(row + 4 * lane)
-                          : (uint32_t)*reinterpret_cast<const uint16_t*>(row + 2 * lane);
-      }
+      const char* row = kbase + (int64_t)min(t, len - 1) * kstride;
+      raw[t] = EPL == 2 ? *reinterpret_cast<const uint32_t*>(row + 4 * lane)
+                        : (uint32_t)*reinterpret_cast<const uint16_t*>(row + 2 * lane);
     }
+    __builtin_amdgcn_sched_barrier(0);  // every load issued before the first use
     auto unpack = [&](int t, float (&x)[EPL]) {
       if constexpr (EPL == 2) {
         x[0] = bf16lo(raw[t]);
@@ -258,29 +261,54 @@ __device__ __forceinline__ void diag_scan(KeyFn key, int len, const float* __res
         x[0] = bf16_to_f32(raw[t]);
       }
     };
-    // 32 keys at a time: their scores as independent reductions, then the
-    // running update (a short dependent chain) key by key
-    constexpr int SG = 32;
+    auto lanef = [](float v, int j) {
+      return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j));
+    };
+    // 64 keys at a time, key t0 + j in lane j: its score (the same wave
+    // reduction per key), the running max after it (a prefix max over the
+    // lanes, exact in any order), and so each key's rescale factor
+    // a = 2^(m_before - m_after) and weight p = 2^(z - m_after) with two
+    // exponentials for all 64 keys.  The sums l and acc then take the keys in
+    // order, with the same multiply-adds as a key-by-key running softmax.
 #pragma unroll
-    for (int t0 = 0; t0 < MAXK; t0 += SG) {
+    for (int t0 = 0; t0 < MAXK; t0 += kWave) {
       if (t0 < len) {
-        float z[SG];
+        float zl = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < SG; ++j) {
+        for (int j = 0; j < kWave; ++j) {
           float x[EPL];
           unpack(t0 + j, x);
-          z[j] = score(x);
+          const float z = score(x);
+          zl = lane == j ? z : zl;
         }
+        if (t0 + lane >= len) zl = -INFINITY;  // (copies of key len - 1)
+        float mt = zl;
 #pragma unroll
-        for (int j = 0; j < SG; ++j) {
+        for (int o = 1; o < kWave; o <<= 1) {
+          const float y = __shfl_up(mt, o);
+          if (lane >= o) mt = fmaxf(mt, y);
+        }
+        mt = fmaxf(mt, m);
+        float mb = __shfl_up(mt, 1);
+        if (lane == 0) mb = m;
+        const float av = exp2f(mb - mt);
+        const float pv = exp2f(zl - mt);
+#pragma unroll
+        for (int j = 0; j < kWave; ++j) {
           if (t0 + j < len) {
+            const float a = lanef(av, j), pj = lanef(pv, j);
             float x[EPL];
             unpack(t0 + j, x);
-            step(t0 + j, x, z[j]);
+            l = l * a + pj;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[e] = fmaf(pj, x[e], acc[e] * a);
+            if (ALL) emit(t0 + j);
           }
         }
+        m = lanef(mt, kWave - 1);
       }
     }
+    if (!ALL) emit(len - 1);
   } else {
     constexpr int GRP = 8;  // keys whose loads are issued together
     for (int t0 = 0; t0 < len; t0 += GRP) {
