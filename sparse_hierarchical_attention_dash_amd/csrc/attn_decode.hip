@@ -25,8 +25,10 @@ namespace dash {
 hipError_t launch_rowattn_f32_decode(const Geom& g, const PrefillParams& p,
                                      const int32_t* seqlens, int64_t batch, hipStream_t st);
 
+// two workgroups fit a CU (LDS); groups of up to 32 heads keep their registers
+// within the matching budget (the two-tile variant took 260 without it)
 template <int D, int NT>
-__global__ __launch_bounds__(256) void decode_attn_kernel(Geom g, DecodeParams p) {
+__global__ __launch_bounds__(256, NT <= 2 ? 2 : 1) void decode_attn_kernel(Geom g, DecodeParams p) {
   constexpr int NTH = 256;
   constexpr int kMaxDecodeTiles = NT;  // ceil(G / 16)
   const int ntile = NT;
