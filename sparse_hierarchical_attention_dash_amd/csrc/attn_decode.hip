@@ -25,11 +25,16 @@ namespace dash {
 hipError_t launch_rowattn_f32_decode(const Geom& g, const PrefillParams& p,
                                      const int32_t* seqlens, int64_t batch, hipStream_t st);
 
-// two workgroups fit a CU (LDS); groups of up to 32 heads keep their registers
-// within the matching budget (the two-tile variant took 260 without it)
+// Two workgroups fit a CU (LDS).  The second launch-bounds argument is the
+// minimum number of waves per SIMD (amdgpu_waves_per_eu), not CUDA's blocks
+// per multiprocessor: with 256 threads a workgroup puts one wave on each of
+// the four SIMDs, so 2 waves per SIMD is two workgroups per CU.  Groups of up
+// to 32 heads keep their registers within that budget (the two-tile variant
+// took 260 without it).
 template <int D, int NT>
 __global__ __launch_bounds__(256, NT <= 2 ? 2 : 1) void decode_attn_kernel(Geom g, DecodeParams p) {
   constexpr int NTH = 256;
+  static_assert(NTH == 256, "two waves per SIMD means two workgroups per CU only at 256 threads");
   constexpr int kMaxDecodeTiles = NT;  // ceil(G / 16)
   const int ntile = NT;
   using C = StageCfg<D, NTH>;

@@ -36,10 +36,8 @@ dash_status check_shape(const dash_shape* s, int enable_gqa, bool decode, Geom& 
   }
   const int G = s->num_q_heads / s->num_kv_heads;
   if (s->dtype == DASH_BF16) {
-    const bool small = (G == 1 || G == 2 || G == 4 || G == 8);
-    const bool big = (G >= 16 && G % 16 == 0 && ((G / 16) & (G / 16 - 1)) == 0 && G <= 256);
-    if (!small && !big) return DASH_ERR_UNSUPPORTED;
-    if (decode && G > 64) return DASH_ERR_UNSUPPORTED;
+    // the group sizes the bf16 kernels are built and tested for
+    if (!(G == 1 || G == 2 || G == 4 || G == 8 || G == 16 || G == 32)) return DASH_ERR_UNSUPPORTED;
   }
   const int64_t C_slots = ((int64_t)s->max_seqlen + s->chunk_size - 1) / s->chunk_size;
   if (C_slots > 2048) return DASH_ERR_UNSUPPORTED;

@@ -96,6 +96,8 @@ def test_layout_and_workspace_sizes(lib):
     (dict(dtype=7), L.DASH_ERR_UNSUPPORTED),
     (dict(Hq=6, Hkv=2), L.DASH_ERR_UNSUPPORTED),          # bf16 group of 3
     (dict(Hq=48, Hkv=1), L.DASH_ERR_UNSUPPORTED),         # bf16 group of 48
+    (dict(Hq=64, Hkv=1), L.DASH_ERR_UNSUPPORTED),         # bf16 groups above 32
+    (dict(Hq=256, Hkv=1), L.DASH_ERR_UNSUPPORTED),
     (dict(Hq=5, Hkv=2), L.DASH_ERR_INVALID_ARGUMENT),
     (dict(T=200000, B=64), L.DASH_ERR_UNSUPPORTED),       # more than 2048 chunk slots
 ])

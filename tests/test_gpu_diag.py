@@ -107,7 +107,7 @@ def test_route_with_diagonal_estimate(case):
                                     num_slots=S, kdiag=kdx)
     margin = O.routing_margin(qx, kbx, B, gamma, s, G, oth, rows, S)
     bits = unpack_bits(mask, S)
-    flips = compare_masks(bits, om, margin, None, f"route+diag {name}")
+    flips = compare_masks(bits, om, margin, f"route+diag {name}")
     th = tau.cpu().numpy().astype(np.float64)
     fin = np.isfinite(oth)
     assert np.array_equal(np.isfinite(th), fin)
@@ -155,7 +155,7 @@ def test_prefill_with_diagonal_estimate(dtype, Hq, Hkv, D, B, L):
                                     num_slots=S, kdiag=kdx)
     margin = O.routing_margin(qx, kbx, B, gamma, s, G, oth, rows, S)
     bits = unpack_bits(ab, S)[:, rows]
-    compare_masks(bits, om[:, rows], margin, None, "prefill+diag")
+    compare_masks(bits, om[:, rows], margin, "prefill+diag")
     # attention on the GPU's own routing (its bits, the oracle's prior there)
     mfull = np.zeros((Hkv, L, S), bool)
     mfull[:, rows] = bits
@@ -209,7 +209,7 @@ def test_decode_with_diagonal_estimate():
         margin = O.routing_margin(qq, kbx[b], B, gamma, 1 / math.sqrt(D), G, th, [L - 1], S)
         om = np.zeros((Hkv, 1, S), bool)
         om[:, 0, :n] = r["mask"]
-        flips = compare_masks(bits[:, b:b + 1], om, margin, None, f"decode+diag b={b}")
+        flips = compare_masks(bits[:, b:b + 1], om, margin, f"decode+diag b={b}")
         if flips == 0:
             assert np.max(np.abs(o[b] - r["out"])) <= TOL["bf16"]
             assert np.max(np.abs(le[:, b] - r["lse"])) <= LSE_TOL["bf16"]

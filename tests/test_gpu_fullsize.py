@@ -18,7 +18,7 @@ import oracle as O
 from sparse_hierarchical_attention_dash_amd import ops
 from sparse_hierarchical_attention_dash_amd import workloads as W
 
-from gpu_helpers import (LSE_TOL, TOL, check_summaries, compare_masks, flush, summary_excuse,
+from gpu_helpers import (LSE_TOL, TOL, check_summaries, compare_masks, flush, oracle_mask_on,
                          to_dev, unpack_bits)
 
 pytestmark = pytest.mark.gpu
@@ -39,7 +39,7 @@ def full_mask_properties(bits_all, L, B, start=0):
     assert not (bits_all[:, start:start + L] & beyond).any()
 
 
-@pytest.mark.parametrize("name,nrows", [("prefill_16k", 48), ("prefill_64k_needles", 40)])
+@pytest.mark.parametrize("name,nrows", [("prefill_16k", 96), ("prefill_64k_needles", 160)])
 def test_prefill_full_size(name, nrows):
     flush(f"full-size prefill {name}")
     d = W.make(name)
@@ -65,10 +65,9 @@ def test_prefill_full_size(name, nrows):
     kbg = kb.to(torch.float64).cpu().numpy()
     check_summaries(kbg, ref["kbar"], "bf16", kx, w.B)
     G = w.Hq // w.Hkv
-    margin = O.routing_margin(qx, ref["kbar"], w.B, w.gamma, 1 / math.sqrt(w.D), G,
-                              ref["tau_hat"], rows, S)
-    ex = summary_excuse(kbg, ref["kbar"], w.Hkv, len(rows), S)
-    flips = compare_masks(bits_all[:, rows], ref["mask"][:, rows], margin, ex, name)
+    om, margin, _ = oracle_mask_on(qx, kbg, w.B, w.alpha, w.gamma, w.sigma, G,
+                                   1 / math.sqrt(w.D), rows, S)
+    flips = compare_masks(bits_all[:, rows], om, margin, name)
     o = out[rows].to(torch.float64).cpu().numpy()
     err = float(np.max(np.abs(o - ref["out"])))
     assert err <= TOL["bf16"], err
@@ -101,24 +100,20 @@ def test_decode_full_size():
         o = out.to(torch.float64).cpu().numpy()
         le = lse.cpu().numpy()
         G = w.Hq // w.Hkv
-        for b in (0, 3, 7, 15):
+        for b in range(0, 16, 2):
             L = int(sl[b])
             kcx = kc[b, :L].to(torch.float64).cpu().numpy()
             vcx = vc[b, :L].to(torch.float64).cpu().numpy()
             kbo = O.summarize(kcx, d["qbar"], w.B, to_bf16=True)
             r = O.decode(qx[b], kcx, vcx, kbo, L, w.B, w.alpha, w.gamma, w.sigma)
             n = (L - 1) // w.B
+            kbg = kbar[b].to(torch.float64).cpu().numpy()[:kbo.shape[0]]
+            check_summaries(kbg, kbo, "bf16", kcx, w.B)
             qq = np.zeros((L, w.Hq, w.D))
             qq[L - 1] = qx[b]
-            th = np.full((w.Hq, L), np.nan)
-            th[:, L - 1] = r["tau_hat"]
-            margin = O.routing_margin(qq, kbo, w.B, w.gamma, 1 / math.sqrt(w.D), G, th,
-                                      [L - 1], S)
-            om = np.zeros((w.Hkv, 1, S), bool)
-            om[:, 0, :n] = r["mask"]
-            kbg = kbar[b].to(torch.float64).cpu().numpy()[:kbo.shape[0]]
-            ex = summary_excuse(kbg, kbo, w.Hkv, 1, S)
-            compare_masks(bits[:, b:b + 1], om, margin, ex, f"decode b={b} L={L}")
+            om, margin, _ = oracle_mask_on(qq, kbg, w.B, w.alpha, w.gamma, w.sigma, G,
+                                           1 / math.sqrt(w.D), [L - 1], S)
+            compare_masks(bits[:, b:b + 1], om, margin, f"decode b={b} L={L}")
             assert not bits[:, b, n:].any()
             err = float(np.max(np.abs(o[b] - r["out"])))
             assert err <= TOL["bf16"], (b, L, err)
@@ -155,16 +150,15 @@ def test_varlen_full_size():
         a, b = int(cu[s]), int(cu[s + 1])
         L = b - a
         full_mask_properties(bits_all, L, w.B, start=a)
-        rows = sample_rows(L, w.B, 6, seed=s)
+        rows = sample_rows(L, w.B, 24, seed=s)
         r = O.prefill(qx[a:b], kx[a:b], vx[a:b], d["qbar"], w.B, float(alphas[s]), w.gamma,
                       w.sigma, True, to_bf16=True, rows=rows, num_slots=S)
         C = L // w.B
         check_summaries(kbg[off:off + C], r["kbar"], "bf16", kx[a:b], w.B)
-        margin = O.routing_margin(qx[a:b], r["kbar"], w.B, w.gamma, 1 / math.sqrt(w.D), G,
-                                  r["tau_hat"], rows, S)
-        ex = summary_excuse(kbg[off:off + C], r["kbar"], w.Hkv, len(rows), S)
+        om, margin, _ = oracle_mask_on(qx[a:b], kbg[off:off + C], w.B, float(alphas[s]),
+                                       w.gamma, w.sigma, G, 1 / math.sqrt(w.D), rows, S)
         rg = [a + i for i in rows]
-        compare_masks(bits_all[:, rg], r["mask"][:, rows], margin, ex, f"varlen seq {s}")
+        compare_masks(bits_all[:, rg], om, margin, f"varlen seq {s}")
         err = float(np.max(np.abs(o[rg] - r["out"])))
         assert err <= TOL["bf16"], (s, err)
         assert np.max(np.abs(le[:, rg] - r["lse"])) <= LSE_TOL["bf16"]

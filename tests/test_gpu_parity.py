@@ -17,7 +17,7 @@ from sparse_hierarchical_attention_dash_amd import ops
 from sparse_hierarchical_attention_dash_amd import workloads as W
 
 from gpu_helpers import (BAND, LSE_TOL, TOL, check_summaries, compare_masks, flush, pack_bits,
-                         prefill_case, summary_excuse, to_dev, unpack_bits)
+                         prefill_case, oracle_mask_on, to_dev, unpack_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -94,7 +94,7 @@ def test_route_stage(case):
                                     num_slots=S)
     margin = O.routing_margin(qx, kbx, B, gamma, s, G, oth, rows, S)
     bits = unpack_bits(mask, S)[:, rows]
-    flips = compare_masks(bits, om[:, rows], margin, None, f"route {name}")
+    flips = compare_masks(bits, om[:, rows], margin, f"route {name}")
     # bits of chunks a row cannot route to are zero, also past the slots
     W_ = mask.shape[2]
     allbits = unpack_bits(mask, W_ * 64)
@@ -227,10 +227,10 @@ def test_prefill_varlen_mixed_alpha():
         a, b = int(cu[sidx]), int(cu[sidx + 1])
         C = (b - a) // 64
         G = 16
-        margin = O.routing_margin(qx[a:b], r["kbar"], 64, 25.0, 1 / math.sqrt(128), G,
-                                  r["tau_hat"], list(range(b - a)), S)
-        ex = summary_excuse(kbg[off:off + C], r["kbar"], 2, b - a, S)
-        compare_masks(bits[:, a:b], r["mask"], margin, ex, f"varlen seq {sidx}")
+        check_summaries(kbg[off:off + C], r["kbar"], "bf16", kx[a:b], 64)
+        om, margin, _ = oracle_mask_on(qx[a:b], kbg[off:off + C], 64, float(alphas[sidx]),
+                                       25.0, 1.0, G, 1 / math.sqrt(128), list(range(b - a)), S)
+        compare_masks(bits[:, a:b], om, margin, f"varlen seq {sidx}")
         assert np.max(np.abs(o[a:b] - r["out"])) <= TOL["bf16"]
         assert np.max(np.abs(le[:, a:b] - r["lse"])) <= LSE_TOL["bf16"]
         off += C
@@ -300,7 +300,7 @@ def test_decode_stage(case):
         margin = O.routing_margin(qq, kbx[b], B, gamma, 1 / math.sqrt(D), G, th, [L - 1], S)
         om = np.zeros((Hkv, 1, S), bool)
         om[:, 0, :n] = r["mask"]
-        compare_masks(bits[:, b:b + 1], om, margin, None, f"decode {name} b={b}")
+        compare_masks(bits[:, b:b + 1], om, margin, f"decode {name} b={b}")
         err = np.max(np.abs(o[b] - r["out"]))
         assert err <= TOL[dtype], err
         assert np.max(np.abs(le[:, b] - r["lse"])) <= LSE_TOL[dtype]

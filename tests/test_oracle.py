@@ -271,6 +271,77 @@ def test_gqa_average_and_or_mask_golden():
     assert list(r["mask"]) == g["mask"]
 
 
+def test_routing_margin_golden_two_heads():
+    # The golden rows as one GQA group of two heads at position 3 with B = 1
+    # (chunks 0..2 routable).  u = gamma * s * <q, kbar>: kbar_c = e_c and
+    # q_g = u_g / (gamma * s).  With the hand-derived thresholds of the two
+    # rows (entmax15_3a, entmax15_3b), the margin of chunk c is
+    # min over the heads of |u_gc - tau_hat_g|, worked out here by hand:
+    #   head 0: |1 + 0.641941|, |0.5 + 0.641941|, |-1 + 0.641941|
+    #   head 1: |-1 + 1.158858|, |0.2 + 1.158858|, |0.3 + 1.158858|
+    #   min   : 0.158858 (head 1), 1.141941 (head 0), 0.358059 (head 0)
+    cases = {c["name"]: c for c in GOLD["cases"]}
+    a, b = cases["entmax15_3a"], cases["entmax15_3b"]
+    gamma, s, D, B, L = 2.0, 0.25, 3, 1, 4
+    kb = np.zeros((3, 2, D))                 # KV head 1 is a decoy
+    kb[:, 0, :] = np.eye(3)
+    kb[:, 1, :] = 7.0
+    q = np.zeros((L, 4, D))
+    q[3, 0] = np.array(a["u"]) / (gamma * s)
+    q[3, 1] = np.array(b["u"]) / (gamma * s)
+    q[3, 2:] = 5.0
+    th = np.full((4, L), np.nan)
+    th[0, 3], th[1, 3] = a["tau_hat"], b["tau_hat"]
+    th[2:, 3] = 0.0
+    mg = O.routing_margin(q, kb, B, gamma, s, 2, th, [3, 1], 5)
+    assert mg.shape == (2, 2, 5)
+    want = [1.1588584044091477 - 1.0, 0.5 + 0.6419410907075054, 1.0 - 0.6419410907075054]
+    np.testing.assert_allclose(mg[0, 0, :3], want, atol=1e-15)
+    assert np.all(np.isinf(mg[0, 0, 3:]))      # past the routable range
+    assert np.all(np.isinf(mg[:, 1, :]))       # row 1 has no routable chunk
+    # heads 2, 3 of KV head 1: u = gamma * s * (3 * 5 * 7) = 0.5 * 105, tau 0
+    np.testing.assert_allclose(mg[1, 0, :3], 52.5, atol=1e-12)
+    # the thresholds the oracle's own routing finds give the same margins
+    _, _, th2 = O.route_sequence(q, kb, B, 1.5, gamma, 1.0, 2, s, rows=[3], num_slots=5)
+    np.testing.assert_allclose(O.routing_margin(q, kb, B, gamma, s, 2, th2, [3], 5)[0, 0, :3],
+                               want, atol=1e-12)
+    # softmax routing thresholds nothing: every margin is infinite
+    th[:, 3] = -np.inf
+    assert np.all(np.isinf(O.routing_margin(q, kb, B, gamma, s, 2, th, [3], 5)))
+
+
+def test_summarize_varlen_restarts_the_chunk_grid():
+    # Keys constant inside each of a sequence's own chunks (value = 10 * seq +
+    # chunk index + head offset), so any summary, whatever q_bar, is that
+    # constant; a grid that did not restart at a sequence start would mix two
+    # chunks' values.  Sequences: shorter than B (no chunk), exactly B (one
+    # chunk), and 2B + 5 (two chunks and a partial tail).
+    B, D, Hkv = 8, 4, 2
+    lens = [5, 8, 21]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    k = np.zeros((cu[-1], Hkv, D))
+    expect = []
+    for sq, n in enumerate(lens):
+        for t in range(n):
+            c = t // B
+            for h in range(Hkv):
+                k[cu[sq] + t, h, :] = 10.0 * sq + c + 100.0 * h
+        for c in range(n // B):
+            expect.append([[10.0 * sq + c + 100.0 * h] * D for h in range(Hkv)])
+    qbar = np.array([[0.3, -1.0, 2.0, 0.5], [1.5, 0.0, -0.7, 0.2]])
+    kb = O.summarize_varlen(k, qbar, cu, B)
+    np.testing.assert_allclose(kb, np.array(expect), atol=1e-12)
+    # mean pooling (q_bar = 0) on ramp keys: chunk c of sequence s averages
+    # the packed positions cu[s] + cB ... cu[s] + cB + B - 1
+    ramp = np.repeat(np.arange(cu[-1], dtype=float)[:, None, None], Hkv, 1).repeat(D, 2)
+    kbm = O.summarize_varlen(ramp, np.zeros((Hkv, D)), cu, B)
+    starts = [cu[sq] + c * B for sq, n in enumerate(lens) for c in range(n // B)]
+    np.testing.assert_allclose(kbm[:, 0, 0], np.array(starts) + (B - 1) / 2.0, atol=1e-12)
+    # bf16 storage rounds each value once
+    kbr = O.summarize_varlen(k + 0.001, qbar, cu, B, to_bf16=True)
+    np.testing.assert_array_equal(kbr, O.round_to_bf16(np.array(expect) + 0.001))
+
+
 def test_routing_mask_is_union_of_head_supports():
     rng = np.random.default_rng(9)
     qg = rng.standard_normal((4, 16))
