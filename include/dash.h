@@ -41,9 +41,12 @@
  *           an error nothing is enqueued and nothing is written.  A failed
  *           kernel launch returns DASH_ERR_HIP.  Device-side contents
  *           (cu_seqlens, seqlens, alpha_per_seq) are preconditions and are
- *           not checked.  The library holds no mutable global state, so calls
- *           from several host threads are safe; calls that share output or
- *           workspace buffers must be ordered by the caller.
+ *           not checked.  The only global state is the per-device scratch
+ *           of dash_attn_decode_noalloc (its address, looked up once per
+ *           device under a lock); every other entry point uses only its
+ *           arguments, so calls from several host threads are safe; calls
+ *           that share output or workspace buffers must be ordered by the
+ *           caller.
  * Supported: head_dim in {64, 128}; chunk_size in {64, 128}; dtype bf16 or
  *           fp32 (q, k, v, summaries and out share it; accumulation is fp32);
  *           C_slots <= 2048; alpha in [1, 2].  In bf16 the GQA group size
@@ -238,6 +241,37 @@ dash_status dash_attn_decode(const dash_shape* shape, const void* q,
                              float softmax_scale, int enable_gqa, int estimate_diagonal,
                              void* out, float* lse, uint64_t* active_blocks, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* dash_attn_decode for callers that cannot allocate device memory: code that
+ * runs under HIP graph capture, tight serving loops, and hosts that forbid
+ * allocation.  Same arguments, layout and results as dash_attn_decode, without
+ * the workspace: its intermediates (routing logits and thresholds, mask and
+ * log-prior, split-K partials) live in a scratch array of
+ * DASH_NOALLOC_SCRATCH_BYTES that the library holds in device memory, one
+ * copy per GPU, for the life of the process.  Nothing is allocated or freed
+ * by this call.
+ *   Limit: a shape whose decode workspace (dash_noalloc_scratch_need) exceeds
+ *          DASH_NOALLOC_SCRATCH_BYTES returns DASH_ERR_UNSUPPORTED; use
+ *          dash_attn_decode with a workspace of its size instead.
+ *   The stream's device must be the current device (else
+ *          DASH_ERR_INVALID_ARGUMENT); the first call on a device looks up the
+ *          scratch's address there (under a lock), later calls reuse it.
+ *   Every call on one GPU shares that GPU's scratch and leaves its last
+ *          contents there: calls that overlap in time on one GPU (on
+ *          different streams, or from several host threads without ordering)
+ *          race and give undefined results.  Calls on one stream are ordered
+ *          and safe.  No part of the scratch needs to start at zero. */
+#define DASH_NOALLOC_SCRATCH_BYTES (32u << 20)
+dash_status dash_attn_decode_noalloc(const dash_shape* shape, const void* q,
+                                     const void* k_cache, const void* v_cache,
+                                     const int32_t* seqlens, const void* kbar_cache,
+                                     const float* qbar, float alpha, float gamma, float sigma,
+                                     float softmax_scale, int enable_gqa,
+                                     int estimate_diagonal, void* out, float* lse,
+                                     uint64_t* active_blocks, void* stream);
+/* Scratch bytes dash_attn_decode_noalloc needs for a decode shape (0 if the
+ * shape is invalid or unsupported). */
+size_t dash_noalloc_scratch_need(const dash_shape* shape);
 
 /* Decode-cache upkeep for incremental decoding: appends one new token per
  * batch entry to the K/V caches and keeps the summary cache current.  A

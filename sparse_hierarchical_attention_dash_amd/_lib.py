@@ -31,11 +31,12 @@ DASH_OP_DECODE_SPARSE = 5
 DASH_OP_ROUTE_DECODE = 6
 DASH_OP_BACKWARD = 7
 DASH_OP_PREFILL_BACKWARD = 8
+DASH_NOALLOC_SCRATCH_BYTES = 32 << 20   # include/dash.h
 
 EXPORTED = ("dash_get_layout", "dash_summarize", "dash_route", "dash_attn_prefill",
             "dash_attn_sparse", "dash_attn_decode", "dash_route_topk", "dash_attn_decode_sparse",
             "dash_cache_append", "dash_summarize_diagonal", "dash_attn_sparse_backward",
-            "dash_attn_prefill_backward",
+            "dash_attn_prefill_backward", "dash_attn_decode_noalloc", "dash_noalloc_scratch_need",
             "dash_workspace_size", "dash_status_string", "dash_abi_version")
 
 
@@ -109,6 +110,11 @@ def lib():
     L.dash_attn_decode.restype = _I
     L.dash_attn_decode.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _P, _F, _F, _F, _F, _I, _I, _P,
                                    _P, _P, _P, _SZ, _P]
+    L.dash_attn_decode_noalloc.restype = _I
+    L.dash_attn_decode_noalloc.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _P, _F, _F, _F, _F, _I,
+                                           _I, _P, _P, _P, _P]
+    L.dash_noalloc_scratch_need.restype = _SZ
+    L.dash_noalloc_scratch_need.argtypes = [_SHAPE]
     L.dash_route_topk.restype = _I
     L.dash_route_topk.argtypes = [_SHAPE, _P, _P, _I, _F, _F, _I, _P, _P, _P, _P, _SZ, _P]
     L.dash_attn_decode_sparse.restype = _I

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "dash.h"
 #include "dash_internal.h"
@@ -263,6 +264,108 @@ char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
     if ((call) != hipSuccess) return DASH_ERR_HIP;  \
   } while (0)
 
+// The decode step on a given workspace (already checked to be large enough).
+dash_status decode_run(Geom& g, const DecodeWs& w, const void* q, const void* k_cache,
+                       const void* v_cache, const int32_t* seqlens, const void* kbar_cache,
+                       const float* qbar, float alpha, float gamma, float sigma,
+                       float softmax_scale, int estimate_diagonal, void* out, float* lse,
+                       uint64_t* active_blocks, void* workspace, hipStream_t s) {
+  uint64_t* mask = active_blocks ? active_blocks : reinterpret_cast<uint64_t*>(at(workspace, w.mask));
+  float* logp = reinterpret_cast<float*>(at(workspace, w.logp));
+  dash::RouteParams rp;
+  if (estimate_diagonal) {
+    void* kdiag = at(workspace, w.kdiag);
+    DASH_HIP(dash::launch_decode_diag(g, k_cache, seqlens, qbar, kdiag, s));
+    rp.kdiag = kdiag;
+  }
+  rp.q = q;
+  rp.kbar = kbar_cache;
+  rp.alpha = alpha;
+  rp.gamma_scale = gamma * eff_scale(g, softmax_scale);
+  rp.sigma = sigma;
+  rp.mask = mask;
+  rp.log_prior = logp;
+  rp.seqlens = seqlens;
+  rp.rows = g.num_seqs;
+  if (g.bf16) {
+    rp.ulog = reinterpret_cast<float*>(at(workspace, w.ulog));
+    rp.tsx = reinterpret_cast<float*>(at(workspace, w.tsx));
+  }
+  DASH_HIP(dash::launch_route(g, rp, s));
+  dash::DecodeParams dp;
+  dp.q = q;
+  dp.k = k_cache;
+  dp.v = v_cache;
+  dp.seqlens = seqlens;
+  dp.mask = mask;
+  dp.log_prior = logp;
+  dp.out = out;
+  dp.lse = lse;
+  dp.scale = eff_scale(g, softmax_scale);
+  dp.part_acc = reinterpret_cast<float*>(at(workspace, w.acc));
+  dp.part_ml = reinterpret_cast<float*>(at(workspace, w.ml));
+  dp.nsplit = w.nsplit;
+  DASH_HIP(dash::launch_decode_attn(g, dp, s));
+  return DASH_OK;
+}
+
+// Argument checks of a decode step that do not involve the workspace.
+dash_status decode_check(const dash_shape* shape, const void* q, const void* k_cache,
+                         const void* v_cache, const int32_t* seqlens, const void* kbar_cache,
+                         const float* qbar, float alpha, float gamma, float sigma,
+                         float softmax_scale, int enable_gqa, int estimate_diagonal,
+                         const void* out, Geom& g) {
+  dash_status st = check_shape(shape, enable_gqa, true, g);
+  if (st != DASH_OK) return st;
+  if ((st = check_routing(alpha, gamma, sigma, softmax_scale)) != DASH_OK) return st;
+  if (g.num_seqs == 0) return DASH_OK;
+  if (!q || !k_cache || !v_cache || !seqlens || !kbar_cache || !out)
+    return DASH_ERR_INVALID_ARGUMENT;
+  if (estimate_diagonal && !qbar) return DASH_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(kbar_cache) ||
+      !aligned16(out) || !aligned16(qbar))
+    return DASH_ERR_INVALID_ARGUMENT;
+  if (g.max_seqlen == 0) return DASH_ERR_INVALID_ARGUMENT;
+  return DASH_OK;
+}
+
+}  // namespace
+
+// ---- the library's own scratch for the allocation-free decode entry point.
+// Each GPU that runs the library holds its own copy of this array until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in for the symbol): the device address is looked up
+// once per device with hipGetSymbolAddress and kept in scratch_dev_ptr.
+static __device__ __align__(256) uint8_t scratch[DASH_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on that device, under a lock; later calls read the kept pointer).
+dash_status scratch_dev_ptr(hipStream_t s, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return DASH_ERR_HIP;
+  if (s != nullptr) {
+    int sdev = -1;
+    if (hipStreamGetDevice(s, &sdev) != hipSuccess) return DASH_ERR_HIP;
+    if (sdev != dev) return DASH_ERR_INVALID_ARGUMENT;  // the stream's device must be current
+  }
+  if (dev < 0 || dev >= kMaxDevices) return DASH_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+      return DASH_ERR_HIP;
+    g_scratch_dev_ptr[dev] = ptr;
+  }
+  *out = g_scratch_dev_ptr[dev];
+  return DASH_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -486,57 +589,44 @@ dash_status dash_attn_decode(const dash_shape* shape, const void* q, const void*
                              uint64_t* active_blocks, void* workspace,
                              size_t workspace_bytes, void* stream) {
   Geom g;
-  dash_status st = check_shape(shape, enable_gqa, true, g);
+  dash_status st = decode_check(shape, q, k_cache, v_cache, seqlens, kbar_cache, qbar, alpha,
+                                gamma, sigma, softmax_scale, enable_gqa, estimate_diagonal, out,
+                                g);
   if (st != DASH_OK) return st;
-  if ((st = check_routing(alpha, gamma, sigma, softmax_scale)) != DASH_OK) return st;
   const DecodeWs w = decode_ws(g);
   if ((st = check_ws(workspace, workspace_bytes, w.total)) != DASH_OK) return st;
   if (g.num_seqs == 0) return DASH_OK;
-  if (!q || !k_cache || !v_cache || !seqlens || !kbar_cache || !out)
-    return DASH_ERR_INVALID_ARGUMENT;
-  if (estimate_diagonal && !qbar) return DASH_ERR_INVALID_ARGUMENT;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(kbar_cache) ||
-      !aligned16(out) || !aligned16(qbar))
-    return DASH_ERR_INVALID_ARGUMENT;
-  if (g.max_seqlen == 0) return DASH_ERR_INVALID_ARGUMENT;
+  return decode_run(g, w, q, k_cache, v_cache, seqlens, kbar_cache, qbar, alpha, gamma, sigma,
+                    softmax_scale, estimate_diagonal, out, lse, active_blocks, workspace,
+                    static_cast<hipStream_t>(stream));
+}
+
+dash_status dash_attn_decode_noalloc(const dash_shape* shape, const void* q,
+                                     const void* k_cache, const void* v_cache,
+                                     const int32_t* seqlens, const void* kbar_cache,
+                                     const float* qbar, float alpha, float gamma, float sigma,
+                                     float softmax_scale, int enable_gqa,
+                                     int estimate_diagonal, void* out, float* lse,
+                                     uint64_t* active_blocks, void* stream) {
+  Geom g;
+  dash_status st = decode_check(shape, q, k_cache, v_cache, seqlens, kbar_cache, qbar, alpha,
+                                gamma, sigma, softmax_scale, enable_gqa, estimate_diagonal, out,
+                                g);
+  if (st != DASH_OK) return st;
+  const DecodeWs w = decode_ws(g);
+  if (w.total > (size_t)DASH_NOALLOC_SCRATCH_BYTES) return DASH_ERR_UNSUPPORTED;
+  if (g.num_seqs == 0) return DASH_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  uint64_t* mask = active_blocks ? active_blocks : reinterpret_cast<uint64_t*>(at(workspace, w.mask));
-  float* logp = reinterpret_cast<float*>(at(workspace, w.logp));
-  dash::RouteParams rp;
-  if (estimate_diagonal) {
-    void* kdiag = at(workspace, w.kdiag);
-    DASH_HIP(dash::launch_decode_diag(g, k_cache, seqlens, qbar, kdiag, s));
-    rp.kdiag = kdiag;
-  }
-  rp.q = q;
-  rp.kbar = kbar_cache;
-  rp.alpha = alpha;
-  rp.gamma_scale = gamma * eff_scale(g, softmax_scale);
-  rp.sigma = sigma;
-  rp.mask = mask;
-  rp.log_prior = logp;
-  rp.seqlens = seqlens;
-  rp.rows = g.num_seqs;
-  if (g.bf16) {
-    rp.ulog = reinterpret_cast<float*>(at(workspace, w.ulog));
-    rp.tsx = reinterpret_cast<float*>(at(workspace, w.tsx));
-  }
-  DASH_HIP(dash::launch_route(g, rp, s));
-  dash::DecodeParams dp;
-  dp.q = q;
-  dp.k = k_cache;
-  dp.v = v_cache;
-  dp.seqlens = seqlens;
-  dp.mask = mask;
-  dp.log_prior = logp;
-  dp.out = out;
-  dp.lse = lse;
-  dp.scale = eff_scale(g, softmax_scale);
-  dp.part_acc = reinterpret_cast<float*>(at(workspace, w.acc));
-  dp.part_ml = reinterpret_cast<float*>(at(workspace, w.ml));
-  dp.nsplit = w.nsplit;
-  DASH_HIP(dash::launch_decode_attn(g, dp, s));
-  return DASH_OK;
+  void* ws = nullptr;
+  if ((st = scratch_dev_ptr(s, &ws)) != DASH_OK) return st;
+  return decode_run(g, w, q, k_cache, v_cache, seqlens, kbar_cache, qbar, alpha, gamma, sigma,
+                    softmax_scale, estimate_diagonal, out, lse, active_blocks, ws, s);
+}
+
+size_t dash_noalloc_scratch_need(const dash_shape* shape) {
+  Geom g;
+  if (check_shape(shape, 1, true, g) != DASH_OK) return 0;
+  return decode_ws(g).total;
 }
 
 dash_status dash_route_topk(const dash_shape* shape, const void* q, const void* kbar,

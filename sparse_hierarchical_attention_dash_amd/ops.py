@@ -342,6 +342,25 @@ def attn_decode(q, k_cache, v_cache, seqlens, kbar_cache, chunk_size, *, alpha=1
     return out, lse, ab
 
 
+def attn_decode_noalloc(q, k_cache, v_cache, seqlens, kbar_cache, chunk_size, out, *,
+                        alpha=1.5, gamma=1.0, sigma=1.0, softmax_scale=0.0, enable_gqa=True,
+                        lse=None, active_blocks=None, estimate_diagonal=False, qbar=None):
+    """dash_attn_decode_noalloc: one decode step whose intermediates live in the
+    library's own per-device scratch (no workspace, nothing allocated here
+    either: the caller passes out [batch, Hq, D] and, optionally, lse
+    [Hq, batch] fp32 and active_blocks [Hkv, batch, W] int64)."""
+    if estimate_diagonal and (qbar is None or qbar.dtype != torch.float32):
+        raise ValueError("estimate_diagonal needs an fp32 qbar")
+    _need_cuda(q, k_cache, v_cache, seqlens, kbar_cache, qbar, out, lse, active_blocks)
+    shape = decode_shape(q, k_cache, chunk_size)
+    L.check("dash_attn_decode_noalloc", L.lib().dash_attn_decode_noalloc(
+        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens),
+        _ptr(kbar_cache), _ptr(qbar), float(alpha), float(gamma), float(sigma),
+        float(softmax_scale), int(enable_gqa), int(estimate_diagonal), _ptr(out), _ptr(lse),
+        _ptr(active_blocks), _stream(q.device)))
+    return out
+
+
 def decode_workspace(q, k_cache, chunk_size):
     n = L.workspace_size(L.DASH_OP_DECODE, decode_shape(q, k_cache, chunk_size))
     return torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)

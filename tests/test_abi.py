@@ -313,3 +313,33 @@ def test_prefill_backward_checks(lib):
     assert bw(vs, n=L.workspace_size(L.DASH_OP_PREFILL_BACKWARD, vs) - 1) == \
         L.DASH_ERR_WORKSPACE_TOO_SMALL
     assert bw(shape(T=0, num_seqs=0, max_seqlen=0)) == L.DASH_OK
+
+
+def test_noalloc_decode_checks(lib):
+    # everything is checked on the host before the scratch is looked up
+    m = re.search(r"#define DASH_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == L.DASH_NOALLOC_SCRATCH_BYTES
+    s = L.make_shape(4, 4096, 4, None, 32, 2, 128, 64, BF16)
+    need = lib.dash_noalloc_scratch_need(ctypes.byref(s))
+    assert 0 < need <= L.DASH_NOALLOC_SCRATCH_BYTES
+    assert need == L.workspace_size(L.DASH_OP_DECODE, s)
+
+    def na(shape, **kw):
+        a = dict(q=A, k=A, v=A, sl=A, kb=A, qbar=None, alpha=1.5, gamma=1.0, sigma=1.0,
+                 scale=0.0, gqa=1, diag=0, out=A, lse=None, ab=None)
+        a.update(kw)
+        return lib.dash_attn_decode_noalloc(ctypes.byref(shape), a["q"], a["k"], a["v"],
+                                            a["sl"], a["kb"], a["qbar"], a["alpha"],
+                                            a["gamma"], a["sigma"], a["scale"], a["gqa"],
+                                            a["diag"], a["out"], a["lse"], a["ab"], None)
+    assert na(s, q=None) == L.DASH_ERR_INVALID_ARGUMENT
+    assert na(s, out=None) == L.DASH_ERR_INVALID_ARGUMENT
+    assert na(s, diag=1) == L.DASH_ERR_INVALID_ARGUMENT          # estimate_diagonal, no qbar
+    assert na(s, alpha=3.0) == L.DASH_ERR_UNSUPPORTED
+    assert na(L.make_shape(4, 4000, 4, None, 32, 2, 128, 64, BF16)) == \
+        L.DASH_ERR_INVALID_ARGUMENT                                # capacity not whole chunks
+    # a shape whose workspace exceeds the fixed scratch is refused
+    big = L.make_shape(512, 131072, 512, None, 32, 2, 128, 64, BF16)
+    assert lib.dash_noalloc_scratch_need(ctypes.byref(big)) > L.DASH_NOALLOC_SCRATCH_BYTES
+    assert na(big) == L.DASH_ERR_UNSUPPORTED
+    assert na(L.make_shape(0, 4096, 0, None, 32, 2, 128, 64, BF16)) == L.DASH_OK
