@@ -40,6 +40,7 @@ METRIC = ("prefill TFLOP/s (active) + decode µs/token at 64K–128K, 75% sparsi
           "% roofline")
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PEAK_F32_VALU_TFLOPS = 157.3  # MI355X fp32 vector
 PMC_FILE = os.path.join(ROOT, "profiles", "prefill_attn_pmc.json")
 KERNEL_SOURCES = ["attn_prefill.hip", "attn_stage.h", "dash_device.h"]
 DEC_PMC_FILE = os.path.join(ROOT, "profiles", "decode_attn_pmc.json")
@@ -77,6 +78,130 @@ def prefill_active_flops(pop, B, D, G):
     return 4.0 * D * G * float(per.sum())
 
 
+def local_positions(cu, T):
+    """Position of every packed row inside its own sequence."""
+    pos = np.empty(T, dtype=np.int64)
+    for a, b in zip(cu[:-1], cu[1:]):
+        pos[a:b] = np.arange(b - a)
+    return pos
+
+
+def active_flops_at(pop, pos, B, D, G):
+    """pop [Hkv, T] active routed chunks; pos [T] local positions."""
+    per = B * pop.astype(np.int64) + ((pos % B) + 1)[None, :]
+    return 4.0 * D * G * float(per.sum())
+
+
+def extra_config(name, stream, reps, cpu_rows, do_cpu):
+    """One more configuration timed as a whole fused dash_attn_prefill
+    (summaries, routing and attention), with its active FLOPs, its roofline
+    fraction and the oracle timed on a sample of its rows."""
+    import torch
+    import oracle as O
+    from sparse_hierarchical_attention_dash_amd import ops
+    from sparse_hierarchical_attention_dash_amd import workloads as W
+    d = W.make(name)
+    w = d["workload"]
+    bf = w.dtype == "bf16"
+    conv = (lambda a: torch.from_numpy(a).to(torch.bfloat16)) if bf else torch.from_numpy
+    qh, kh, vh = conv(d["q"]), conv(d["k"]), conv(d["v"])
+    q, k, v = qh.cuda(), kh.cuda(), vh.cuda()
+    qbar = torch.from_numpy(d["qbar"]).cuda()
+    T = q.shape[0]
+    G = w.Hq // w.Hkv
+    kw = {}
+    if w.kind == "varlen":
+        cu = d["cu_seqlens"]
+        kw = dict(cu_seqlens=torch.from_numpy(cu).cuda(), max_seqlen=int(np.diff(cu).max()),
+                  alpha_per_seq=torch.from_numpy(d["alphas"]).cuda())
+    else:
+        cu = np.array([0, T], dtype=np.int64)
+    lens = np.diff(cu)
+    pos = local_positions(cu, T)
+    shp = ops._seq_shape(q, w.Hq, w.Hkv, w.B, kw.get("cu_seqlens"), kw.get("max_seqlen"))
+    from sparse_hierarchical_attention_dash_amd import _lib as L
+    ws = torch.empty(L.workspace_size(L.DASH_OP_PREFILL, shp), dtype=torch.uint8, device="cuda")
+    _, _, ab = ops.attn_prefill(q, k, v, qbar, w.B, alpha=w.alpha, gamma=w.gamma, sigma=w.sigma,
+                                return_active_blocks=True, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    pop = popcounts(ab.cpu().numpy())
+    flops = active_flops_at(pop, pos, w.B, w.D, G)
+    t = stats(time_reps(stream, lambda: ops.attn_prefill(
+        q, k, v, qbar, w.B, alpha=w.alpha, gamma=w.gamma, sigma=w.sigma, workspace=ws, **kw),
+        reps, warm=3))
+    routable = float(np.sum(pos // w.B)) * w.Hkv
+    tfl = flops / (t["median"] * 1e-3) / 1e12
+    peak, bound = (PEAK_BF16_TFLOPS, "mfma") if bf else (PEAK_F32_VALU_TFLOPS, "alu")
+    r = {"workload": name, "tokens": T, "sequences": int(len(lens)), "dtype": w.dtype,
+         "B": w.B, "ms": t, "active_flops": flops, "tflops_at_median": tfl,
+         "roofline": {"bound": bound, "peak": peak, "frac": tfl / peak},
+         "block_support": float(pop.sum()) / max(routable, 1.0),
+         "support_histogram": support_histogram(pop, w.B, pos)}
+    if do_cpu:
+        # oracle: a stratified sample of rows of every sequence (all of them
+        # when the sequence is short), summaries prorated per row
+        qx = qh.to(torch.float64).numpy()
+        kx = kh.to(torch.float64).numpy()
+        vx = vh.to(torch.float64).numpy()
+        rng = np.random.default_rng(0)
+        s = 1.0 / math.sqrt(w.D)
+        alphas = d.get("alphas", np.full(len(lens), w.alpha))
+        tot_rows, secs, fl = 0, 0.0, 0.0
+        per_seq = max(1, cpu_rows // len(lens))
+        full = T <= cpu_rows
+        for si, (a, b) in enumerate(zip(cu[:-1], cu[1:])):
+            Ls = int(b - a)
+            if full or Ls <= per_seq:
+                rows = list(range(Ls))
+            else:
+                edges = np.linspace(0, Ls, per_seq + 1).astype(int)
+                rows = sorted(int(rng.integers(x, max(x + 1, y)))
+                              for x, y in zip(edges[:-1], edges[1:]))
+            t0 = time.perf_counter()
+            kbar = O.summarize(kx[a:b], d["qbar"], w.B, to_bf16=bf)
+            t_sum = time.perf_counter() - t0
+            t0 = time.perf_counter()
+            m_, lp_, _ = O.route_sequence(qx[a:b], kbar, w.B, float(alphas[si]), w.gamma,
+                                          w.sigma, G, s, rows=rows)
+            O.attention_rows(qx[a:b], kx[a:b], vx[a:b], m_, lp_, w.B, s, G, rows)
+            secs += time.perf_counter() - t0 + t_sum * len(rows) / Ls
+            tot_rows += len(rows)
+            for i in rows:
+                for h in range(w.Hkv):
+                    fl += 4.0 * w.D * G * (w.B * int(m_[h, i].sum()) + (i % w.B) + 1)
+        r["cpu"] = {"value": fl / secs / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+                    "cpu_model": cpu_model(), "kind": "oracle", "seconds": secs,
+                    "extrapolated_full_seconds": secs * flops / max(fl, 1.0),
+                    "sample": ("every row" if tot_rows == T else
+                               f"{tot_rows} stratified rows of {T} (routing + attention in "
+                               "float64 NumPy, summaries prorated per row); the full time is "
+                               "extrapolated by active FLOPs")}
+    return r
+
+
+def decode_oracle_time(dd, wd):
+    """The oracle's decode step (routing of each new token against the cached
+    summaries, then attention over its active blocks) for every sequence of
+    the batch, in float64 NumPy; the summary cache is built beforehand, as it
+    is cached in decode."""
+    import torch
+    import oracle as O
+    secs = 0.0
+    for b in range(wd.batch):
+        L = int(dd["seqlens"][b])
+        kx = torch.from_numpy(dd["k_cache"][b, :L]).to(torch.bfloat16).to(torch.float64).numpy()
+        vx = torch.from_numpy(dd["v_cache"][b, :L]).to(torch.bfloat16).to(torch.float64).numpy()
+        qx = torch.from_numpy(dd["q"][b]).to(torch.bfloat16).to(torch.float64).numpy()
+        kb = O.summarize(kx, dd["qbar"], wd.B, to_bf16=True)
+        t0 = time.perf_counter()
+        O.decode(qx, kx, vx, kb, L, wd.B, wd.alpha, wd.gamma, wd.sigma)
+        secs += time.perf_counter() - t0
+    return {"us_per_step": secs * 1e6, "unit": "us/step", "cores": blas_threads(),
+            "cpu_model": cpu_model(), "kind": "oracle",
+            "sample": f"the whole step: all {wd.batch} sequences (routing + attention, "
+                      "float64 NumPy; summary cache built beforehand, untimed)"}
+
+
 def to_bf16_dev(a):
     import torch
     return torch.from_numpy(a).to(torch.bfloat16).cuda()
@@ -106,6 +231,114 @@ def time_it(stream, fn, reps):
         a[r + 1].record(stream)
     torch.cuda.synchronize()
     return float(np.mean([a[r].elapsed_time(a[r + 1]) for r in range(reps)]))
+
+
+def stats(ms):
+    """mean / median / min of a list of milliseconds."""
+    a = np.asarray(ms, dtype=np.float64)
+    return {"mean": float(a.mean()), "median": float(np.median(a)), "min": float(a.min())}
+
+
+def time_reps(stream, fn, reps, warm=2, before=None):
+    """Per-rep milliseconds of fn() from HIP events on its stream; before(),
+    when given, runs ahead of every rep outside the timed interval."""
+    import torch
+    for _ in range(warm):
+        fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        if before is not None:
+            before()
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def measured_peaks(stream):
+    """Achievable peaks on this GPU, next to the spec values: the library's
+    probes (an MFMA issue loop of the attention kernels' 16x16x32 bf16
+    instruction; an HBM read stream of 1 GiB) and, for scale, a large bf16
+    GEMM through torch (the vendor BLAS) and a 1 GiB device copy."""
+    import ctypes
+    import torch
+    from sparse_hierarchical_attention_dash_amd import _lib as L
+    lib = L.lib()
+    sink = torch.empty(256, dtype=torch.float32, device="cuda")
+    work = ctypes.c_double(0.0)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def probe(kind, src, nbytes, iters):
+        L.check("dash_probe_peak", lib.dash_probe_peak(
+            kind, ctypes.c_void_p(0 if src is None else src.data_ptr()), nbytes, iters,
+            ctypes.c_void_p(sink.data_ptr()), 1024, ctypes.byref(work), sp))
+
+    probe(0, None, 0, 20000)
+    t_m = stats(time_reps(stream, lambda: probe(0, None, 0, 20000), 5, warm=1))
+    mfma = work.value / (t_m["min"] * 1e-3) / 1e12
+    nb = 1 << 30
+    buf = torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(1)
+    t_r = stats(time_reps(stream, lambda: probe(1, buf, nb, 0), 10, warm=2))
+    rd = work.value / (t_r["min"] * 1e-3) / 1e9
+    dst = torch.empty_like(buf)
+    t2 = stats(time_reps(stream, lambda: dst.copy_(buf), 10, warm=3))
+    copy = 2.0 * nb / (t2["min"] * 1e-3) / 1e9
+    del buf, dst
+    n = 8192
+    a = torch.randn((n, n), device="cuda", dtype=torch.bfloat16)
+    b = torch.randn((n, n), device="cuda", dtype=torch.bfloat16)
+    c = torch.empty((n, n), device="cuda", dtype=torch.bfloat16)
+    t = stats(time_reps(stream, lambda: torch.matmul(a, b, out=c), 10, warm=3))
+    gemm = 2.0 * n ** 3 / (t["min"] * 1e-3) / 1e12
+    del a, b, c
+    return {"mfma_bf16_tflops": mfma,
+            "mfma_bf16": "dash_probe_peak kind 0: 16x16x32 bf16 MFMA, two chains per wave, "
+                         "two waves per SIMD, best of 5",
+            "hbm_read_GB_per_s": rd,
+            "hbm_read": "dash_probe_peak kind 1: 1 GiB read with 16-byte loads, best of 10",
+            "torch_gemm_bf16_tflops": gemm, "torch_gemm": f"torch.matmul {n}x{n}x{n}, best of 10",
+            "copy_GB_per_s": copy, "copy": "1 GiB device copy (read + write bytes), best of 10"}
+
+
+def support_histogram(pop, B, starts=None):
+    """Per-(KV head, row) active routed chunks over the rows that have at
+    least one routable chunk: percentiles and a log2-binned histogram."""
+    T = pop.shape[1]
+    pos = np.arange(T) if starts is None else starts
+    n = pos // B
+    vals = pop[:, n >= 1].ravel()
+    if vals.size == 0:
+        return None
+    edges = [0, 1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048]
+    hist, _ = np.histogram(vals, bins=edges)
+    rel = (pop[:, n >= 1] / n[None, n >= 1]).ravel()
+    return {"bins": edges, "counts": hist.tolist(),
+            "percentiles": {str(p): float(np.percentile(vals, p)) for p in (1, 10, 50, 90, 99)},
+            "min": int(vals.min()), "max": int(vals.max()), "mean": float(vals.mean()),
+            "relative_percentiles": {str(p): float(np.percentile(rel, p))
+                                     for p in (1, 10, 50, 90, 99)}}
 
 
 def graph_time(stream, fn, outs, reps):
@@ -187,6 +420,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip the dense and top-k comparison timings")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the timings of the other configurations (16K, varlen, tiny)")
+    ap.add_argument("--configs", default="tiny_f32,prefill_16k,varlen_mixed")
     ap.add_argument("--copy-ref", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (the "
                          "reference for scaling HBM byte counters) and exit")
@@ -245,7 +481,6 @@ def main():
         qd = to_bf16_dev(dd["q"])
         kc = to_bf16_dev(dd["k_cache"])
         vc = to_bf16_dev(dd["v_cache"])
-        del dd["k_cache"], dd["v_cache"]
         seqlens = torch.from_numpy(dd["seqlens"]).cuda()
         cap = kc.shape[1]
         # the summary cache is built once (summaries of complete chunks are fixed)
@@ -296,9 +531,11 @@ def main():
     config = {"workload": " + ".join(x for x in (args.prefill if do_pre else None,
                                                 args.decode if do_dec else None) if x)}
     if do_pre:
-        t_sum = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-        t_route = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-        t_attn = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+        s_sum = stats([e[0].elapsed_time(e[1]) for e in evs])
+        s_route = stats([e[1].elapsed_time(e[2]) for e in evs])
+        s_attn = stats([e[2].elapsed_time(e[3]) for e in evs])
+        s_pre = stats([e[0].elapsed_time(e[3]) for e in evs])
+        t_sum, t_route, t_attn = s_sum["mean"], s_route["mean"], s_attn["mean"]
         t_pre = t_sum + t_route + t_attn
         # parity of the staged launches with the fused entry point (untimed)
         out2, _, ab2 = ops.attn_prefill(q, k, v, qbar, wp.B, alpha=wp.alpha, gamma=wp.gamma,
@@ -330,9 +567,13 @@ def main():
                           "attention_ms": t_attn, "active_flops": flops,
                           "block_support": support, "block_sparsity": 1.0 - support,
                           "dense_causal_flops": 4.0 * wp.D * wp.Hq * T * (T + 1) / 2,
-                          "attention_tflops": attn_tflops}
+                          "attention_tflops": attn_tflops,
+                          "ms_stats": s_pre, "summarize_ms_stats": s_sum,
+                          "route_ms_stats": s_route, "attention_ms_stats": s_attn,
+                          "support_histogram": support_histogram(pop, wp.B)}
     if do_dec:
-        t_dec = float(np.mean([e[4].elapsed_time(e[5]) for e in evs]))
+        s_dec = stats([e[4].elapsed_time(e[5]) for e in evs])
+        t_dec = s_dec["mean"]
         ops.attn_decode(qd, kc, vc, seqlens, kbar_c, wd.B, alpha=wd.alpha, gamma=wd.gamma,
                         sigma=wd.sigma, workspace=ws_dec, out=out_d)
         # active blocks of the decode step (untimed run returning the mask)
@@ -352,7 +593,20 @@ def main():
             if (pmc.get("kernel_hash") == kernel_hash(DEC_KERNEL_SOURCES)
                     and pmc.get("workload") == wd.name):
                 dec_traffic = pmc.get("hbm_bytes_per_launch")
+        # the decode step alone with the last-level cache flushed before every
+        # rep: a 512 MiB buffer is read between reps (outside the timed
+        # interval), which leaves only its clean lines in the cache (a written
+        # buffer would leave dirty lines whose write-back lands in the step)
+        flush_buf = torch.ones(128 << 20, dtype=torch.int32, device=dev)
+        flush_out = torch.empty((), dtype=torch.int64, device=dev)
+        s_fl = stats(time_reps(stream, lambda: ops.attn_decode(
+            qd, kc, vc, seqlens, kbar_c, wd.B, alpha=wd.alpha, gamma=wd.gamma, sigma=wd.sigma,
+            workspace=ws_dec, out=out_d), 20, warm=3,
+            before=lambda: flush_out.copy_(flush_buf.sum(dtype=torch.int64))))
+        del flush_buf, flush_out
         res["decode"] = {"us_per_step": t_dec * 1e3, "us_per_token": t_dec * 1e3 / wd.batch,
+                         "us_stats": {k_: v_ * 1e3 for k_, v_ in s_dec.items()},
+                         "us_stats_flushed": {k_: v_ * 1e3 for k_, v_ in s_fl.items()},
                          "active_kv_bytes": kv_bytes, "GB_per_s": gbs,
                          "block_support": float(popd.sum()) / routable,
                          "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
@@ -543,11 +797,30 @@ def main():
                 "graph_speedup_vs_dense": g_dense / g_dash,
                 "graph_speedup_vs_topk": g_topk / g_dash}
         res["compare"] = cmp
+    if not args.no_configs and do_pre:
+        log("other configurations ...")
+        res["configs"] = {}
+        for name in [x for x in args.configs.split(",") if x]:
+            log(f"  {name}")
+            res["configs"][name] = extra_config(name, stream, 20, 256,
+                                                not args.no_cpu_baseline)
+    log("measured peaks ...")
+    res["peaks_measured"] = measured_peaks(stream)
+    if "roofline" in res:
+        res["roofline"]["frac_of_measured_peak"] = (
+            res["roofline"]["achieved"] / res["peaks_measured"]["mfma_bf16_tflops"])
+    if do_dec:
+        res["decode"]["roofline"]["frac_of_measured_peak"] = (
+            res["decode"]["roofline"]["achieved"] / res["peaks_measured"]["hbm_read_GB_per_s"])
     if do_pre and not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         res["cpu_baseline"] = cpu_baseline(dp, wp, wp.gamma, args.cpu_rows)
+        res["cpu_baseline"]["cpu_model"] = cpu_model()
     else:
         res["cpu_baseline"] = None
+    if do_dec and not args.no_cpu_baseline:
+        log("cpu baseline, decode (oracle) ...")
+        res["cpu_baseline_decode"] = decode_oracle_time(dd, wd)
     print(json.dumps(res), flush=True)
 
 

@@ -273,6 +273,37 @@ dash_status dash_attn_decode_noalloc(const dash_shape* shape, const void* q,
  * shape is invalid or unsupported). */
 size_t dash_noalloc_scratch_need(const dash_shape* shape);
 
+/* The work list the G >= 16 bf16 prefill attention runs a packed (varlen)
+ * batch by (exposed for inspection): one entry per (sequence, tile of P
+ * consecutive positions), (sequence << 16) | tile, cost-sorted -- the
+ * sequences longest first (by tile count, ties by index), each sequence's
+ * tiles from its last (a tile's rows see more keys the later it starts) down
+ * to its first -- then 0xffffffff up to `capacity`.  The grid is sized by
+ * this list, not by num_seqs x max_seqlen.  The scheduling side of "iterate
+ * over the active chunks" ("Fase 2", the implementation bullet of the
+ * gist.science summary) for sequences of mixed lengths.
+ *   shape          varlen prefill shape (cu_seqlens set), bf16, G in {16, 32},
+ *                  num_seqs <= 1024 (else DASH_ERR_UNSUPPORTED)
+ *   items          device uint32 [capacity]          (output)
+ *   capacity       >= ceil(T / 8) + num_seqs (else DASH_ERR_WORKSPACE_TOO_SMALL)
+ *   positions_per_tile  host int                     (output: P) */
+dash_status dash_prefill_schedule(const dash_shape* shape, int enable_gqa, uint32_t* items,
+                                  size_t capacity, int* positions_per_tile, void* stream);
+
+/* Measurement probe (not part of the attention path): one launch that
+ * measures an achievable peak of this GPU, to read the kernels' roofline
+ * fractions against next to the published peaks.
+ *   kind 0: MFMA issue loop, two independent 16x16x32 bf16 accumulator
+ *           chains per wave, two waves per SIMD, `iters` rounds (src unused);
+ *   kind 1: HBM read stream of `bytes` (a multiple of 16) from src with
+ *           16-byte loads (iters unused).
+ *   sink   >= 1024 bytes of device memory (written only on a bit pattern the
+ *          probes never produce)
+ *   work   host double: FLOPs (kind 0) or bytes (kind 1) the launch processes
+ * Time the launch with events on `stream`. */
+dash_status dash_probe_peak(int kind, const void* src, size_t bytes, int iters, void* sink,
+                           size_t sink_bytes, double* work, void* stream);
+
 /* Decode-cache upkeep for incremental decoding: appends one new token per
  * batch entry to the K/V caches and keeps the summary cache current.  A
  * chunk's summary is fixed once the chunk is complete, so it is computed once,

@@ -36,7 +36,8 @@ DASH_NOALLOC_SCRATCH_BYTES = 32 << 20   # include/dash.h
 EXPORTED = ("dash_get_layout", "dash_summarize", "dash_route", "dash_attn_prefill",
             "dash_attn_sparse", "dash_attn_decode", "dash_route_topk", "dash_attn_decode_sparse",
             "dash_cache_append", "dash_summarize_diagonal", "dash_attn_sparse_backward",
-            "dash_attn_prefill_backward", "dash_attn_decode_noalloc", "dash_noalloc_scratch_need",
+            "dash_attn_prefill_backward", "dash_attn_decode_noalloc", "dash_noalloc_scratch_need", "dash_probe_peak",
+            "dash_prefill_schedule",
             "dash_workspace_size", "dash_status_string", "dash_abi_version")
 
 
@@ -113,6 +114,10 @@ def lib():
     L.dash_attn_decode_noalloc.restype = _I
     L.dash_attn_decode_noalloc.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _P, _F, _F, _F, _F, _I,
                                            _I, _P, _P, _P, _P]
+    L.dash_prefill_schedule.restype = _I
+    L.dash_prefill_schedule.argtypes = [_SHAPE, _I, _P, _SZ, ctypes.POINTER(ctypes.c_int), _P]
+    L.dash_probe_peak.restype = _I
+    L.dash_probe_peak.argtypes = [_I, _P, _SZ, _I, _P, _SZ, ctypes.POINTER(ctypes.c_double), _P]
     L.dash_noalloc_scratch_need.restype = _SZ
     L.dash_noalloc_scratch_need.argtypes = [_SHAPE]
     L.dash_route_topk.restype = _I

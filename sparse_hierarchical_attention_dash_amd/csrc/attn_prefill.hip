@@ -386,6 +386,7 @@ constexpr int kRingWaves = 8;  // two 16-row tiles per wave
 constexpr int kRingThreads = 64 * kRingWaves;
 constexpr int kRingTiles = 2 * kRingWaves;
 
+// LDS layout of one staged 64-key block: K rows, then V^T rows.
 template <int D>
 struct RingCfg {
   static constexpr int KROW = D * 2;                  // bytes per K row
@@ -394,10 +395,16 @@ struct RingCfg {
   static constexpr int VROW = 128;                    // bytes per V^T row (64 keys)
   static constexpr int VBYTES = D * VROW;
   static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int NP = STAGE / (16 * kRingThreads);  // 16-byte loads per thread
-  static constexpr int LPS = NP + 1;                      // + the tiles' bias words
-  static_assert(NP * 16 * kRingThreads == STAGE, "slot must split into whole loads");
-  static_assert(KBYTES % (NP * 1024) == 0, "a wave's pieces lie all in K or all in V^T");
+};
+// How NTH threads split a block's staging: NP 16-byte loads each, a wave's
+// pieces lying all in K or all in V^T.
+template <int D, int NTH>
+struct RingSplit {
+  using R = RingCfg<D>;
+  static constexpr int NP = R::STAGE / (16 * NTH);  // 16-byte loads per thread
+  static constexpr int LPS = NP + 1;                 // + the tiles' bias words
+  static_assert(NP * 16 * NTH == R::STAGE, "slot must split into whole loads");
+  static_assert(R::KBYTES % (NP * 1024) == 0, "a wave's pieces lie all in K or all in V^T");
 };
 
 // XOR swizzle of the 16-byte pieces of an LDS row: 16 consecutive rows read
@@ -420,12 +427,13 @@ __device__ __forceinline__ int swz(int row) {
 // the MFMAs that consume them (sched_barrier keeps the compiler from
 // collapsing the pipeline); the first two V^T groups are read during the
 // softmax, which does not need them.
-template <int D, bool MASKED, int U0, int NTL>
+template <int D, bool MASKED, int U0, int NTL, int TWN = 2, int NFR = 3>
 __device__ __forceinline__ void visit_ring(lds_u8* ks_, lds_u8* vt_,
                                            const int (&koff)[D / 32], const int (&voff)[2],
-                                           const bf16x8 (&qa)[2][D / 32], f32x4 (&o)[2][D / 16],
-                                           float (&l)[2], float (&m)[2], float sl2,
-                                           const float (&bz)[2], int kbase, const int (&rpos)[2]) {
+                                           const bf16x8 (&qa)[TWN][D / 32],
+                                           f32x4 (&o)[TWN][D / 16], float (&l)[TWN],
+                                           float (&m)[TWN], float sl2, const float (&bz)[TWN],
+                                           int kbase, const int (&rpos)[TWN]) {
   using R = RingCfg<D>;
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
@@ -442,30 +450,31 @@ __device__ __forceinline__ void visit_ring(lds_u8* ks_, lds_u8* vt_,
     for (int i = 0; i < 4; ++i)
       f[i] = lds_read16(vt_ + voff[s2] + 16 * (dt0 + i) * R::VROW);
   };
-  // fragment groups 0 .. KS-1 are K (ks = g), KS .. KS+NVG-1 are V^T; three
-  // buffers, two groups in flight ahead of the one being consumed
+  // fragment groups 0 .. KS-1 are K (ks = g), KS .. KS+NVG-1 are V^T; NFR
+  // buffers, NFR - 1 groups in flight ahead of the one being consumed
   constexpr int NG = KS + NVG;
-  u32x4 fr[3][4];
+  constexpr int AH = NFR - 1;
+  u32x4 fr[NFR][4];
   auto gload = [&](int gi) {
-    if (gi < KS) kload(fr[gi % 3], gi);
-    else if (gi < NG) vload(fr[gi % 3], gi - KS);
+    if (gi < KS) kload(fr[gi % NFR], gi);
+    else if (gi < NG) vload(fr[gi % NFR], gi - KS);
   };
   f32x4 sacc[NTL][4];
 #pragma unroll
   for (int u = 0; u < NTL; ++u)
 #pragma unroll
     for (int t = 0; t < 4; ++t) sacc[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  gload(0);
-  gload(1);
+#pragma unroll
+  for (int a = 0; a < AH; ++a) gload(a);
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    gload(ks + 2);
+    gload(ks + AH);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int u = 0; u < NTL; ++u)
-        sacc[u][t] = mfma16x16x32(as_bf16x8(fr[ks % 3][t]), qa[U0 + u][ks], sacc[u][t]);
+        sacc[u][t] = mfma16x16x32(as_bf16x8(fr[ks % NFR][t]), qa[U0 + u][ks], sacc[u][t]);
     __builtin_amdgcn_sched_barrier(0);
   }
   uint32_t pk[NTL][4][2];
@@ -521,10 +530,10 @@ __device__ __forceinline__ void visit_ring(lds_u8* ks_, lds_u8* vt_,
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int vg = 0; vg < NVG; ++vg) {
-    gload(KS + vg + 2);
+    gload(KS + vg + AH);
     __builtin_amdgcn_sched_barrier(0);
     const int s2 = vg / (DT / 4), dt0 = 4 * (vg % (DT / 4));
-    u32x4 (&cur)[4] = fr[(KS + vg) % 3];
+    u32x4 (&cur)[4] = fr[(KS + vg) % NFR];
 #pragma unroll
     for (int u = 0; u < NTL; ++u) {
       const u32x4 pb = {pk[u][2 * s2][0], pk[u][2 * s2][1], pk[u][2 * s2 + 1][0],
@@ -539,34 +548,60 @@ __device__ __forceinline__ void visit_ring(lds_u8* ks_, lds_u8* vt_,
 }
 
 // Prefill attention for G >= 16 (every 16-row tile is 16 query heads of one
-// position; 16 tiles per workgroup, two per wave).  The blocks of the
-// workgroup's list stream through a 4-slot LDS ring filled by direct
-// global->LDS loads (K rows from K, V^T rows from the V^T workspace, and each
-// tile's bias for the block), three blocks ahead of the one being consumed.
-// Which positions have each listed chunk active is worked out once, up front,
-// into a bitmap in LDS, so the loop reads no memory but LDS.  A wave visits a
-// block with both its tiles at once when both have it active.  The loop is
-// unrolled by the ring depth so every slot is a distinct LDS array; waits are
-// counted (vmcnt) and the barrier carries no fence.
-template <int D>
-__global__ __launch_bounds__(kRingThreads, 1) void prefill_attn_ring_kernel(
-    Geom g, PrefillParams p, TileGeom tg) {
-  constexpr int NTH = kRingThreads;
+// position).  A workgroup of NWV waves owns NT = NWV * TW tiles, TW per wave,
+// so P = NT / (G / 16) positions (P divides B: the positions share one
+// diagonal chunk).  The blocks of the workgroup's list stream through a
+// 4-slot LDS ring filled by direct global->LDS loads (K rows from K, V^T rows
+// from the V^T workspace, and each tile's bias for the block), three blocks
+// ahead of the one being consumed.  Which positions have each listed chunk
+// active is worked out once, up front, into a bitmap in LDS, so the loop reads
+// no memory but LDS.  Waits are counted (vmcnt) and the barrier carries no
+// fence.
+//   PAIR: a wave's tiles 2k and 2k+1 always share their position (G = 32), so
+//         they visit together and every LDS fragment feeds both; otherwise
+//         each active tile visits alone.
+//   NFR : LDS fragment groups in flight per visit (register budget).
+// Work items: `items` (varlen packs) lists (sequence << 16 | tile) in the
+// cost-sorted order of prefill_schedule_kernel, 0xffffffff past its end;
+// without it a fixed-length batch maps item w to tile tiles_per_seq - 1 -
+// w % tiles_per_seq of sequence w / tiles_per_seq (each sequence's tiles
+// costliest first).  blockIdx.x = item, blockIdx.y = KV head (one head's
+// keys and values at a time in the caches).
+template <int D, int NWV, int TW, bool PAIR, int NFR>
+__global__ __launch_bounds__(64 * NWV, 1) void prefill_attn_ring_kernel(
+    Geom g, PrefillParams p, TileGeom tg, const uint32_t* __restrict__ items) {
+  constexpr int NTH = 64 * NWV;
+  constexpr int NT = NWV * TW;
   using R = RingCfg<D>;
+  using RS = RingSplit<D, NTH>;
+  constexpr int NP = RS::NP;
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
+  static_assert(NT <= 32, "one activity word per listed chunk");
+  static_assert(!PAIR || TW % 2 == 0, "pairs of tiles");
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kRing][R::STAGE];
-  __shared__ float bias[kRing][kRingTiles];
+  __shared__ float bias[kRing][NT];
   __shared__ unsigned long long Umask[32];
   __shared__ int Wpref[33];
   __shared__ uint16_t Blist[2048];
-  __shared__ uint16_t Act[2048];   // bit t: position p0 + t has chunk Blist[j] active
+  using ActT = typename std::conditional<NT <= 16, uint16_t, uint32_t>::type;
+  __shared__ ActT Act[2048];   // bit t: position p0 + t has chunk Blist[j] active
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in an SGPR
   const int r = lane & 15, gq = lane >> 4;
-  const int tile = tg.tiles_per_seq - 1 - (int)blockIdx.x;
-  const int s = blockIdx.y, h = blockIdx.z;
+  const int h = blockIdx.y;
+  const int w_item = blockIdx.x;
+  int s, tile;
+  if (items) {
+    const uint32_t it = items[w_item];
+    if (it == 0xffffffffu) return;
+    s = (int)(it >> 16);
+    tile = (int)(it & 0xffffu);
+  } else {
+    s = w_item / tg.tiles_per_seq;
+    tile = tg.tiles_per_seq - 1 - w_item % tg.tiles_per_seq;
+  }
   const SeqInfo si = seq_info(g.cu_seqlens, nullptr, s, g.max_seqlen, g.B);
   const int p0 = tile * tg.P;
   if (p0 >= si.len) return;
@@ -577,20 +612,20 @@ __global__ __launch_bounds__(kRingThreads, 1) void prefill_attn_ring_kernel(
   const int W = g.W;
   const unsigned long long* __restrict__ mask = (const unsigned long long*)p.mask;
 
-  // this wave's tiles u = 0, 1: 16 heads (rhead) of position rpos = p0 + tpos
-  int tpos[2], rpos[2], rhead[2];
-  bool rvalid[2];
+  // this wave's tiles u < TW: 16 heads (rhead) of position rpos = p0 + tpos
+  int tpos[TW], rpos[TW], rhead[TW];
+  bool rvalid[TW];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int ti = 2 * wv + u;
+  for (int u = 0; u < TW; ++u) {
+    const int ti = TW * wv + u;
     tpos[u] = ti / tg.HT;
     rpos[u] = p0 + tpos[u];
     rhead[u] = (ti % tg.HT) * 16 + r;
     rvalid[u] = rpos[u] < pend;
   }
-  bf16x8 qa[2][KS];
+  bf16x8 qa[TW][KS];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < TW; ++u) {
     const int64_t qrow = ((si.start + rpos[u]) * g.Hq + h * g.G + rhead[u]) * (int64_t)D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -637,7 +672,7 @@ __global__ __launch_bounds__(kRingThreads, 1) void prefill_attn_ring_kernel(
     uint32_t bits = 0;
     for (int t = 0; t < npos; ++t)
       bits |= (uint32_t)((mbase[t * W + (c >> 6)] >> (c & 63)) & 1ull) << t;
-    Act[j] = (uint16_t)bits;
+    Act[j] = (ActT)bits;
   }
   __syncthreads();
   const int sbl = g.B == 128 ? 1 : 0;  // log2 of the 64-key blocks per chunk
@@ -649,29 +684,30 @@ __global__ __launch_bounds__(kRingThreads, 1) void prefill_attn_ring_kernel(
   // pieces are all K rows or all V^T rows)
   const int64_t krs = (int64_t)g.Hkv * D * 2;  // bytes between consecutive keys
   const int64_t vrs = p.Tp * 2;                  // bytes between V^T rows
-  const bool isk = wv * R::NP * 1024 < R::KBYTES;
+  const bool isk = wv * NP * 1024 < R::KBYTES;
   const uint8_t* kbase = (const uint8_t*)p.k + (si.start * (int64_t)g.Hkv + h) * D * 2;
   const uint8_t* vbase = (const uint8_t*)p.vt + ((int64_t)h * D * p.Tp + pad_off(g, s)) * 2;
-  // piece i of this thread: K row or V^T row kr[i] of the block, at source
+  // piece i of this thread: K row or V^T row kr(i) of the block, at source
   // address pbase[i] + (K: key0 * krs, V^T: key0 * 2) for the block at key0
-  const uint8_t* pbase[R::NP];
-  int kr[R::NP];
+  auto krow = [&](int i) -> int {
+    const int o = (wv * NP + i) * 1024 + lane * 16;
+    return isk ? o / R::KROW : (o - R::KBYTES) / R::VROW;
+  };
+  const uint8_t* pbase[NP];
 #pragma unroll
-  for (int i = 0; i < R::NP; ++i) {
-    const int o = (wv * R::NP + i) * 1024 + lane * 16;
+  for (int i = 0; i < NP; ++i) {
+    const int o = (wv * NP + i) * 1024 + lane * 16;
+    const int kr = krow(i);
     if (isk) {
-      kr[i] = o / R::KROW;
-      const int pcol = (((o % R::KROW) / 16) ^ swz<R::KP>(kr[i])) * 16;
-      pbase[i] = kbase + kr[i] * krs + pcol;
+      const int pcol = (((o % R::KROW) / 16) ^ swz<R::KP>(kr)) * 16;
+      pbase[i] = kbase + kr * krs + pcol;
     } else {
-      const int ov = o - R::KBYTES;
-      kr[i] = ov / R::VROW;
-      const int pcol = (((ov % R::VROW) / 16) ^ swz<8>(kr[i])) * 16;
-      pbase[i] = vbase + kr[i] * vrs + pcol;
+      const int pcol = ((((o - R::KBYTES) % R::VROW) / 16) ^ swz<8>(kr)) * 16;
+      pbase[i] = vbase + kr * vrs + pcol;
     }
   }
-  // lane u < 2 loads tile u's bias (its position's row of log_prior)
-  const int bpos = min(rpos[lane & 1], pend - 1);
+  // lane u < TW loads tile (TW * wv + u)'s bias (its position's row of log_prior)
+  const int bpos = min(p0 + (TW * wv + min(lane, TW - 1)) / tg.HT, pend - 1);
   const float* bsrc = p.log_prior + ((int64_t)h * T + si.start + bpos) * g.C_slots;
   const int kmax = pend - 1;
   // loads of the block at key0 (chunk c for its bias) into a ring slot
@@ -679,17 +715,19 @@ __global__ __launch_bounds__(kRingThreads, 1) void prefill_attn_ring_kernel(
     if (!isk || key0 + 63 <= kmax) {
       const int64_t off = isk ? (int64_t)key0 * krs : (int64_t)key0 * 2;
 #pragma unroll
-      for (int i = 0; i < R::NP; ++i) lds_dma16(pbase[i] + off, slot + (wv * R::NP + i) * 1024);
+      for (int i = 0; i < NP; ++i) lds_dma16(pbase[i] + off, slot + (wv * NP + i) * 1024);
     } else {
       // K rows past the sequence end (last chunk of the sequence): repeat the
       // last key instead of reading beyond it
 #pragma unroll
-      for (int i = 0; i < R::NP; ++i)
-        lds_dma16(pbase[i] + (int64_t)(min(key0 + kr[i], kmax) - kr[i]) * krs,
-                  slot + (wv * R::NP + i) * 1024);
+      for (int i = 0; i < NP; ++i) {
+        const int kr = krow(i);
+        lds_dma16(pbase[i] + (int64_t)(min(key0 + kr, kmax) - kr) * krs,
+                  slot + (wv * NP + i) * 1024);
+      }
     }
     // the tiles' biases for this block (past the routed blocks: any valid word)
-    if (lane < 2) lds_dma4(bsrc + c, bslot + wv * 8);
+    if (lane < TW) lds_dma4(bsrc + c, bslot + wv * TW * 4);
   };
   // first key of step sx's block; c = its chunk for a routed block, else 0
   auto block_key0 = [&](int sx, int cl) -> int {
@@ -704,13 +742,15 @@ __global__ __launch_bounds__(kRingThreads, 1) void prefill_attn_ring_kernel(
   };
 
   // ---- tile state
-  f32x4 o[2][DT];
-  float l[2] = {0.f, 0.f};
-  float m[2] = {-INFINITY, -INFINITY};
+  f32x4 o[TW][DT];
+  float l[TW], m[TW];
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int u = 0; u < TW; ++u) {
+    l[u] = 0.f;
+    m[u] = -INFINITY;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   const float sl2 = p.scale * kLog2e;
   int koff[KS], voff[2];
 #pragma unroll
@@ -718,66 +758,90 @@ __global__ __launch_bounds__(kRingThreads, 1) void prefill_attn_ring_kernel(
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2) voff[s2] = r * R::VROW + (((4 * s2 + gq) ^ swz<8>(r)) * 16);
 
+  const uint32_t ring0 = lds_addr(&ring[0][0]), bias0 = lds_addr(&bias[0][0]);
+  // the wave's tiles whose position has listed chunk j active (bit u: tile u)
+  auto active_mask = [&](int j) -> uint32_t {
+    const uint32_t act = Act[j];
+    uint32_t am = 0;
+#pragma unroll
+    for (int u = 0; u < TW; ++u)
+      am |= (rvalid[u] && ((act >> tpos[u]) & 1u)) ? (1u << u) : 0u;
+    return am;
+  };
+  // routed block of step st in slot kv: the active tiles visit it with their
+  // biases; tiles of one position (PAIR) visit together, every LDS fragment
+  // feeding both.  (Two tiles of different positions visiting together when
+  // both are active measured slower than one after the other: the fused visit
+  // fits the register budget only without fragment prefetch.)
+  auto routed_step = [&](int st, lds_u8* kv, uint32_t am) {
+    float bz[TW];
+    const float* bs = &bias[st & 3][TW * wv];
+#pragma unroll
+    for (int u = 0; u < TW; ++u) bz[u] = bs[u] * kLog2e;
+    static_for<0, (PAIR ? TW / 2 : TW)>([&](auto k_) {
+      constexpr int U0 = PAIR ? 2 * decltype(k_)::value : decltype(k_)::value;
+      if ((am >> U0) & 1u)
+        visit_ring<D, false, U0, PAIR ? 2 : 1, TW, NFR>(kv, kv + R::KBYTES, koff, voff, qa, o, l,
+                                                         m, sl2, bz, 0, rpos);
+    });
+  };
+  // diagonal block of step st: every tile, causal mask, bias 0 (two at a time)
+  auto diag_step = [&](int st, lds_u8* kv) {
+    float bz[TW];
+#pragma unroll
+    for (int u = 0; u < TW; ++u) bz[u] = 0.f;
+    const int key0 = cdiag * g.B + ((st - nrouted) << 6);
+    static_for<0, TW / 2>([&](auto k_) {
+      constexpr int U0 = 2 * decltype(k_)::value;
+      if (rvalid[U0])
+        visit_ring<D, true, U0, 2, TW, NFR>(kv, kv + R::KBYTES, koff, voff, qa, o, l, m, sl2, bz,
+                                            key0 + 4 * gq, rpos);
+    });
+  };
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4));  // Q and mask reads done first
   // Every step issues exactly one block's loads (past the end of the list it
   // re-reads the last block into the free slot, which no later step reads), so
   // when step st waits, exactly two blocks' loads are younger than its own:
   // one fixed counted wait proves slot st & 3 complete.
-  const uint32_t ring0 = lds_addr(&ring[0][0]), bias0 = lds_addr(&bias[0][0]);
-  __builtin_amdgcn_s_waitcnt(0 | (7 << 4));  // Q and mask reads done first
   issue(0, ring0, bias0);
-  issue(min(1, NS - 1), ring0 + R::STAGE, bias0 + 4 * kRingTiles);
-  issue(min(2, NS - 1), ring0 + 2 * R::STAGE, bias0 + 8 * kRingTiles);
-
-  // wait for slot st & 3 and for every wave to be done with slot (st + 3) & 3;
-  // returns the slot's LDS offset
+  issue(min(1, NS - 1), ring0 + R::STAGE, bias0 + 4 * NT);
+  issue(min(2, NS - 1), ring0 + 2 * R::STAGE, bias0 + 8 * NT);
+  // wait for slot st & 3 and for every wave to be done with slot (st + 3) & 3
   auto enter = [&](int st) -> lds_u8* {
-    // own loads of this slot done (the two younger blocks may stay in flight),
-    // this wave's LDS reads of the slot about to be refilled done
-    __builtin_amdgcn_s_waitcnt(((2 * R::LPS) & 15) | (7 << 4));
+    // own loads of this slot done (the two younger blocks may stay in
+    // flight), this wave's LDS reads of the slot about to be refilled done
+    wait_vm<2 * RS::LPS>();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     return (lds_u8*)&ring[st & 3][0];
   };
-  // refill of the slot released at the step's barrier (every wave was done
-  // reading it) with the block three steps ahead
+  // refill of the slot released at the step's barrier with the block three
+  // steps ahead
   auto leave = [&](int st, int cnext) {
     const int sr = st + 3, sx = min(sr, NS - 1);
     issue_at(block_key0(sx, cnext), cnext, ring0 + (sr & 3) * R::STAGE,
-             bias0 + (sr & 3) * 4 * kRingTiles);
+             bias0 + (sr & 3) * 4 * NT);
   };
-  // routed blocks: each tile whose position has the chunk active visits it
-  // with the tile's bias (the two visits, when both are active, run back to
-  // back so that each tile's state is only ever updated in place)
   for (int st = 0; st < nrouted; ++st) {
     lds_u8* kv = enter(st);
     const int cnext = listed(min(st + 3, NS - 1));  // read now, used by the refill
-    const uint32_t act = Act[st >> sbl];
-    const bool a0 = rvalid[0] && ((act >> tpos[0]) & 1u);
-    const bool a1 = rvalid[1] && ((act >> tpos[1]) & 1u);
-    const float* bs = &bias[st & 3][2 * wv];
-    const float bz[2] = {bs[0] * kLog2e, bs[1] * kLog2e};
+    const uint32_t am = active_mask(st >> sbl);
     // a wave with nothing to visit issues the refill at once; a visiting wave
     // issues it afterwards, when the other waves' loads have left the queue
-    if (!(a0 || a1)) leave(st, cnext);
-    if (a0) visit_ring<D, false, 0, 1>(kv, kv + R::KBYTES, koff, voff, qa, o, l, m, sl2, bz, 0, rpos);
-    if (a1) visit_ring<D, false, 1, 1>(kv, kv + R::KBYTES, koff, voff, qa, o, l, m, sl2, bz, 0, rpos);
-    if (a0 || a1) leave(st, cnext);
+    if (!am) leave(st, cnext);
+    routed_step(st, kv, am);
+    if (am) leave(st, cnext);
   }
-  // the diagonal chunk: both tiles, causal mask, bias 0, one fused visit
   for (int st = nrouted; st < NS; ++st) {
     lds_u8* kv = enter(st);
-    const float bz[2] = {0.f, 0.f};
-    const int key0 = cdiag * g.B + ((st - nrouted) << 6);
-    if (rvalid[0])
-      visit_ring<D, true, 0, 2>(kv, kv + R::KBYTES, koff, voff, qa, o, l, m, sl2, bz,
-                                key0 + 4 * gq, rpos);
+    diag_step(st, kv);
     leave(st, 0);
   }
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4));  // no ring load outlives the kernel
 
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < TW; ++u) {
     if (!rvalid[u]) continue;
     float lt = l[u] + xor16(l[u]);
     lt += xor32(lt);
@@ -1193,20 +1257,100 @@ static TileGeom make_tiles(const Geom& g) {
   return t;
 }
 
-// Ring kernel (G >= 16): one 16-row tile per wave, 16 tiles, so P = 16 / (G / 16)
-// positions per workgroup.
-static TileGeom make_ring_tiles(const Geom& g) {
+// Ring kernels (G >= 16): NT 16-row tiles per workgroup, so P = NT / (G / 16)
+// positions.
+static TileGeom make_ring_tiles(const Geom& g, int NT = kRingTiles, int TW = 2) {
   TileGeom t;
   t.TP = 1;
   t.HT = g.G / 16;
-  t.NT = kRingTiles;
-  t.TW = 2;
+  t.NT = NT;
+  t.TW = TW;
   t.P = t.NT / t.HT;
   t.tiles_per_seq = (g.max_seqlen + t.P - 1) / t.P;
   return t;
 }
 
-bool prefill_uses_ring(const Geom& g) { return g.bf16 && g.G >= 16 && g.G <= 256; }
+// varlen packs of at most this many sequences get a longest-first work list
+constexpr int kScheduleMaxSeqs = 1024;
+
+int64_t prefill_items_capacity(const Geom& g) {
+  if (!g.cu_seqlens || g.num_seqs > kScheduleMaxSeqs || !(g.bf16 && g.G >= 16)) return 0;
+  return (g.T + 7) / 8 + g.num_seqs;  // sum_s ceil(L_s / P) for any P >= 8
+}
+
+// Cost-sorted work list of a varlen pack (one workgroup of 1024 threads,
+// num_seqs <= 1024).  A tile's cost grows with its first position (its rows
+// see that many keys).  The sequences are taken longest first (by tile count,
+// ties by index), and each sequence's tiles from its last (costliest) down to
+// its first, so the grid ends on the short tiles of the short sequences while
+// the workgroups running at any one time share one sequence's keys and
+// values in the caches (interleaving sequences, or heads, by tile cost
+// measured slower: the working set outgrows the L2).
+//   n_s = ceil(L_s / P) tiles of sequence s; perm = sequences by n desc;
+//   off_k = sum_{k' < k} n_perm[k']; entry off_k + j = (perm[k] << 16) |
+//   (n_perm[k] - 1 - j); entries from sum_s n_s up to cap hold 0xffffffff.
+__global__ __launch_bounds__(1024) void prefill_schedule_kernel(const int32_t* __restrict__ cu,
+                                                                int num_seqs, int P,
+                                                                uint32_t* __restrict__ items,
+                                                                int64_t cap) {
+  constexpr int NTH = 1024;
+  __shared__ int nt[kScheduleMaxSeqs];         // tiles per sequence
+  __shared__ int perm[kScheduleMaxSeqs];       // sequences by tile count, desc
+  __shared__ int off[kScheduleMaxSeqs];        // first entry of each sorted sequence
+  const int tid = threadIdx.x;
+  for (int i = tid; i < num_seqs; i += NTH) nt[i] = (cu[i + 1] - cu[i] + P - 1) / P;
+  __syncthreads();
+  for (int i = tid; i < num_seqs; i += NTH) {
+    const int n = nt[i];
+    int rank = 0;
+    for (int j = 0; j < num_seqs; ++j) {
+      const int m = nt[j];
+      rank += (m > n || (m == n && j < i)) ? 1 : 0;
+    }
+    perm[rank] = i;
+  }
+  __syncthreads();
+  // exclusive prefix of the sorted counts (Hillis-Steele over <= 1024 entries)
+  const int mine = tid < num_seqs ? nt[perm[tid]] : 0;
+  off[tid] = mine;
+  __syncthreads();
+  for (int o = 1; o < NTH; o <<= 1) {
+    const int y = tid >= o ? off[tid - o] : 0;
+    __syncthreads();
+    off[tid] += y;
+    __syncthreads();
+  }
+  const int total = off[NTH - 1];
+  const int first = off[tid] - mine;
+  __syncthreads();
+  off[tid] = first;
+  __syncthreads();
+  // entries: sorted sequence k's tiles, highest first (all threads share the
+  // work of every sequence)
+  for (int k = 0; k < num_seqs; ++k) {
+    const int s = perm[k], n = nt[s], o = off[k];
+    for (int j = tid; j < n; j += NTH)
+      if (o + j < cap) items[o + j] = ((uint32_t)s << 16) | (uint32_t)(n - 1 - j);
+  }
+  for (int64_t i = total + tid; i < cap; i += NTH) items[i] = 0xffffffffu;
+}
+
+// The forward launch: eight waves of two tiles (four waves of eight tiles hold
+// 384 of the 512 registers of a lane in Q and O alone at D = 128 and spill).
+constexpr int kFwdWaves = kRingWaves, kFwdTW = 2, kFwdNFR = 3;
+
+int prefill_positions_per_tile(const Geom& g) {
+  return make_ring_tiles(g, kFwdWaves * kFwdTW, kFwdTW).P;
+}
+
+hipError_t launch_prefill_schedule(const Geom& g, int P, uint32_t* items, int64_t cap,
+                                   hipStream_t st) {
+  hipLaunchKernelGGL(prefill_schedule_kernel, dim3(1), dim3(1024), 0, st, g.cu_seqlens,
+                     g.num_seqs, P, items, cap);
+  return hipGetLastError();
+}
+
+bool prefill_uses_ring(const Geom& g) { return g.bf16 && g.G >= 16; }
 
 hipError_t launch_vt_transpose(const Geom& g, const void* src, void* dst, int64_t Tp,
                                hipStream_t st) {
@@ -1237,20 +1381,32 @@ hipError_t launch_prefill_attn(const Geom& g, const PrefillParams& p, hipStream_
     const TileGeom tg = make_tiles(g);
     dim3 grid(tg.tiles_per_seq, g.num_seqs, g.Hkv);
     if (prefill_uses_ring(g)) {
-      const TileGeom rg = make_ring_tiles(g);
-      dim3 rgrid(rg.tiles_per_seq, g.num_seqs, g.Hkv);
+      constexpr int NWV = kFwdWaves, TW = kFwdTW, NFR = kFwdNFR;
+      const TileGeom rg = make_ring_tiles(g, NWV * TW, TW);
+      const int64_t cap = prefill_items_capacity(g);
+      const uint32_t* items = nullptr;
+      int64_t nwork = (int64_t)rg.tiles_per_seq * g.num_seqs;
+      if (cap > 0 && p.items) {
+        hipError_t e = launch_prefill_schedule(g, rg.P, p.items, cap, st);
+        if (e != hipSuccess) return e;
+        items = p.items;
+        nwork = cap;
+      }
+      dim3 rgrid((unsigned)nwork, g.Hkv);
       dim3 tgrid((g.max_seqlen + 63) / 64, g.num_seqs, g.Hkv);
+#define DASH_RING(DD, PAIR)                                                                 \
+  hipLaunchKernelGGL((prefill_attn_ring_kernel<DD, NWV, TW, PAIR, NFR>), rgrid,            \
+                     dim3(64 * NWV), 0, st, g, p, rg, items)
       if (g.D == 64) {
         hipLaunchKernelGGL(vt_transpose_kernel<64>, tgrid, dim3(256), 0, st, g,
                            (const uint16_t*)p.v, (uint16_t*)p.vt, p.Tp);
-        hipLaunchKernelGGL(prefill_attn_ring_kernel<64>, rgrid, dim3(kRingThreads), 0, st, g,
-                           p, rg);
+        if (rg.HT == 2) DASH_RING(64, true); else DASH_RING(64, false);
       } else {
         hipLaunchKernelGGL(vt_transpose_kernel<128>, tgrid, dim3(256), 0, st, g,
                            (const uint16_t*)p.v, (uint16_t*)p.vt, p.Tp);
-        hipLaunchKernelGGL(prefill_attn_ring_kernel<128>, rgrid, dim3(kRingThreads), 0, st, g,
-                           p, rg);
+        if (rg.HT == 2) DASH_RING(128, true); else DASH_RING(128, false);
       }
+#undef DASH_RING
       return hipGetLastError();
     }
 #define DASH_PRE(DD, U)                                                                   \

@@ -100,8 +100,10 @@ size_t vt_bytes(const Geom& g) {
              : 0;
 }
 
+size_t items_bytes(const Geom& g) { return align_up((size_t)dash::prefill_items_capacity(g) * 4); }
+
 struct PrefillWs {
-  size_t meta, kbar, mask, logp, vt, kdiag, total;
+  size_t meta, kbar, mask, logp, vt, kdiag, items, total;
 };
 PrefillWs prefill_ws(const Geom& g) {
   PrefillWs w{};
@@ -118,17 +120,20 @@ PrefillWs prefill_ws(const Geom& g) {
   o += vt_bytes(g);
   w.kdiag = o;  // estimated own-chunk summaries (estimate_diagonal)
   o += align_up((size_t)g.T * g.Hkv * g.D * elt(g));
+  w.items = o;  // the attention kernel's varlen work list
+  o += items_bytes(g);
   w.total = o;
   return w;
 }
 struct SparseWs {
-  size_t meta, vt, total;
+  size_t meta, vt, items, total;
 };
 SparseWs sparse_ws(const Geom& g) {
   SparseWs w{};
   w.meta = 0;
   w.vt = meta_ws(g);
-  w.total = w.vt + vt_bytes(g);
+  w.items = w.vt + vt_bytes(g);
+  w.total = w.items + items_bytes(g);
   return w;
 }
 struct DecodeWs {
@@ -539,6 +544,7 @@ dash_status dash_attn_prefill(const dash_shape* shape, const void* q, const void
   pp.scale = eff_scale(g, softmax_scale);
   pp.vt = at(workspace, w.vt);
   pp.Tp = dash::padded_tokens(g.T, g.num_seqs);
+  pp.items = reinterpret_cast<uint32_t*>(at(workspace, w.items));
   DASH_HIP(dash::launch_prefill_attn(g, pp, s));
   return DASH_OK;
 }
@@ -575,8 +581,9 @@ dash_status dash_attn_sparse(const dash_shape* shape, const void* q, const void*
   pp.out = out;
   pp.lse = lse;
   pp.scale = eff_scale(g, softmax_scale);
-  pp.vt = w.total > w.vt ? at(workspace, w.vt) : nullptr;
+  pp.vt = w.items > w.vt ? at(workspace, w.vt) : nullptr;
   pp.Tp = dash::padded_tokens(g.T, g.num_seqs);
+  pp.items = w.total > w.items ? reinterpret_cast<uint32_t*>(at(workspace, w.items)) : nullptr;
   DASH_HIP(dash::launch_prefill_attn(g, pp, s));
   return DASH_OK;
 }
@@ -621,6 +628,37 @@ dash_status dash_attn_decode_noalloc(const dash_shape* shape, const void* q,
   if ((st = scratch_dev_ptr(s, &ws)) != DASH_OK) return st;
   return decode_run(g, w, q, k_cache, v_cache, seqlens, kbar_cache, qbar, alpha, gamma, sigma,
                     softmax_scale, estimate_diagonal, out, lse, active_blocks, ws, s);
+}
+
+dash_status dash_prefill_schedule(const dash_shape* shape, int enable_gqa, uint32_t* items,
+                                  size_t capacity, int* positions_per_tile, void* stream) {
+  Geom g;
+  dash_status st = check_shape(shape, enable_gqa, false, g);
+  if (st != DASH_OK) return st;
+  if (!positions_per_tile) return DASH_ERR_INVALID_ARGUMENT;
+  const int64_t cap = dash::prefill_items_capacity(g);
+  if (cap <= 0) return DASH_ERR_UNSUPPORTED;
+  if (capacity < (size_t)cap) return DASH_ERR_WORKSPACE_TOO_SMALL;
+  if (!items) return DASH_ERR_INVALID_ARGUMENT;
+  const int P = dash::prefill_positions_per_tile(g);
+  *positions_per_tile = P;
+  DASH_HIP(dash::launch_prefill_schedule(g, P, items, cap, static_cast<hipStream_t>(stream)));
+  return DASH_OK;
+}
+
+dash_status dash_probe_peak(int kind, const void* src, size_t bytes, int iters, void* sink,
+                           size_t sink_bytes, double* work, void* stream) {
+  if (!work || !sink || sink_bytes < 1024 || !aligned16(sink)) return DASH_ERR_INVALID_ARGUMENT;
+  if (kind == 0) {
+    if (iters <= 0) return DASH_ERR_INVALID_ARGUMENT;
+  } else if (kind == 1) {
+    if (!src || !aligned16(src) || bytes < 16) return DASH_ERR_INVALID_ARGUMENT;
+  } else {
+    return DASH_ERR_INVALID_ARGUMENT;
+  }
+  DASH_HIP(dash::launch_probe(kind, src, bytes, iters, sink, work,
+                              static_cast<hipStream_t>(stream)));
+  return DASH_OK;
 }
 
 size_t dash_noalloc_scratch_need(const dash_shape* shape) {

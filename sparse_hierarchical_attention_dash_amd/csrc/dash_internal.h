@@ -43,6 +43,11 @@ hipError_t launch_diag_summary(const Geom& g, const void* k, const float* qbar, 
 hipError_t launch_decode_diag(const Geom& g, const void* k_cache, const int32_t* seqlens,
                               const float* qbar, void* kdiag, hipStream_t st);
 
+// measurement probes (probe.hip): kind 0 = MFMA issue loop, 1 = HBM read stream;
+// *work receives the FLOPs (0) or bytes (1) one launch processes
+hipError_t launch_probe(int kind, const void* src, size_t bytes, int iters, void* sink,
+                        double* work, hipStream_t st);
+
 // Decode-cache upkeep: append the new tokens' K/V rows (position seqlens[b]-1
 // of caches [batch, cap, Hkv, D]) and summarise each chunk they complete.
 hipError_t launch_cache_append(const Geom& g, const void* k_new, const void* v_new,
@@ -86,8 +91,18 @@ struct PrefillParams {
   void* out = nullptr;
   float* lse = nullptr;                 // [Hq, T] or null
   float scale = 0.f;
+  uint32_t* items = nullptr;            // workspace: varlen work list (prefill_items_capacity)
 };
 hipError_t launch_prefill_attn(const Geom& g, const PrefillParams& p, hipStream_t st);
+// Entries of the varlen work list of the G >= 16 prefill kernels (0 when the
+// call does not use one): ceil(T / 8) + num_seqs, enough for P >= 8.
+int64_t prefill_items_capacity(const Geom& g);
+// Positions per workgroup tile of the G >= 16 prefill attention kernel.
+int prefill_positions_per_tile(const Geom& g);
+// The longest-first work list of a varlen pack with P positions per tile
+// (entries (sequence << 16) | tile, 0xffffffff past the end), cap entries.
+hipError_t launch_prefill_schedule(const Geom& g, int P, uint32_t* items, int64_t cap,
+                                   hipStream_t st);
 // True when launch_prefill_attn runs the V^T + LDS-ring path (needs p.vt).
 bool prefill_uses_ring(const Geom& g);
 

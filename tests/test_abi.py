@@ -343,3 +343,25 @@ def test_noalloc_decode_checks(lib):
     assert lib.dash_noalloc_scratch_need(ctypes.byref(big)) > L.DASH_NOALLOC_SCRATCH_BYTES
     assert na(big) == L.DASH_ERR_UNSUPPORTED
     assert na(L.make_shape(0, 4096, 0, None, 32, 2, 128, 64, BF16)) == L.DASH_OK
+
+
+def test_prefill_schedule_checks(lib):
+    P = ctypes.c_int(0)
+    # fixed-length shapes have no work list
+    assert lib.dash_prefill_schedule(ctypes.byref(shape()), 1, A, 1 << 20, ctypes.byref(P),
+                                     None) == L.DASH_ERR_UNSUPPORTED
+    v = shape(T=5000, cu=A, num_seqs=3, max_seqlen=4000)
+    need = -(-5000 // 8) + 3
+    assert lib.dash_prefill_schedule(ctypes.byref(v), 1, A, need - 1, ctypes.byref(P),
+                                     None) == L.DASH_ERR_WORKSPACE_TOO_SMALL
+    assert lib.dash_prefill_schedule(ctypes.byref(v), 1, None, need, ctypes.byref(P),
+                                     None) == L.DASH_ERR_INVALID_ARGUMENT
+    assert lib.dash_prefill_schedule(ctypes.byref(v), 1, A, need, None,
+                                     None) == L.DASH_ERR_INVALID_ARGUMENT
+    # more sequences than the list is built for
+    many = shape(T=5000, cu=A, num_seqs=2000, max_seqlen=4000)
+    assert lib.dash_prefill_schedule(ctypes.byref(many), 1, A, 1 << 20, ctypes.byref(P),
+                                     None) == L.DASH_ERR_UNSUPPORTED
+    # the prefill workspaces hold the list for varlen packs
+    base = L.workspace_size(L.DASH_OP_SPARSE, shape(T=5000, num_seqs=1, max_seqlen=5000))
+    assert L.workspace_size(L.DASH_OP_SPARSE, v) >= need * 4

@@ -198,10 +198,11 @@ def test_prefill_custom_scale_and_needles():
     flush(f"  max-abs {r['err']:.2e} flips {r['flips']}")
 
 
-def test_prefill_varlen_mixed_alpha():
-    flush("prefill varlen")
+@pytest.mark.parametrize("Hkv", [2, 1])
+def test_prefill_varlen_mixed_alpha(Hkv):
+    flush(f"prefill varlen, G = {32 // Hkv}")
     lens = [1, 63, 64, 65, 700, 1300]
-    d = W.gen_varlen(lens, 32, 2, 128, seed=41, B=64)
+    d = W.gen_varlen(lens, 32, Hkv, 128, seed=41, B=64)
     alphas = np.array([1.25, 1.5, 2.0, 1.5, 1.25, 2.0], np.float32)
     cu = d["cu_seqlens"]
     q, qx = to_dev(d["q"], "bf16")
@@ -226,7 +227,7 @@ def test_prefill_varlen_mixed_alpha():
     for sidx, r in enumerate(res):
         a, b = int(cu[sidx]), int(cu[sidx + 1])
         C = (b - a) // 64
-        G = 16
+        G = 32 // Hkv
         check_summaries(kbg[off:off + C], r["kbar"], "bf16", kx[a:b], 64)
         om, margin, _ = oracle_mask_on(qx[a:b], kbg[off:off + C], 64, float(alphas[sidx]),
                                        25.0, 1.0, G, 1 / math.sqrt(128), list(range(b - a)), S)
