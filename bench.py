@@ -471,7 +471,8 @@ def main():
         mask = torch.empty((wp.Hkv, T, lay.mask_words), dtype=torch.int64, device=dev)
         logp = torch.empty((wp.Hkv, T, lay.chunk_slots), dtype=torch.float32, device=dev)
         out = torch.empty_like(q)
-        ws_route = torch.empty(256, dtype=torch.uint8, device=dev)
+        ws_route = torch.empty(max(256, L.workspace_size(L.DASH_OP_ROUTE, shp)),
+                               dtype=torch.uint8, device=dev)
         ws_sparse = ops.sparse_workspace(q, k, wp.B)
         log(f"prefill inputs {wp.name}: T={T} Hq={wp.Hq} Hkv={wp.Hkv} D={wp.D} B={wp.B} "
             f"({time.time() - t0:.1f}s)")

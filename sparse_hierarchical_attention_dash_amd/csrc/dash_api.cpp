@@ -94,6 +94,23 @@ int32_t* meta_pad(const Geom& g, void* ws) {
   return reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
                                     align_up(sizeof(int32_t) * (g.num_seqs + 1)));
 }
+// Row-group flags of the streaming prefill routing (bf16, G = 16 or 32).
+size_t flag_bytes(const Geom& g) {
+  return (g.bf16 && (g.G == 16 || g.G == 32)) ? align_up((size_t)dash::route_rows_flag_bytes(g))
+                                                : 0;
+}
+// Routing of prefill rows: the streaming kernel (plus its fallback for the
+// row groups it flags) where it applies, else one workgroup per row.
+hipError_t run_route(const Geom& g, const dash::RouteParams& p, void* flags, hipStream_t s) {
+  if (flags && dash::route_rows_supported(g, p)) {
+    hipError_t e = dash::launch_route_rows(g, p, static_cast<uint8_t*>(flags), s);
+    if (e != hipSuccess) return e;
+    return dash::launch_route_fallback(g, p, static_cast<const uint8_t*>(flags), s);
+  }
+  return dash::launch_route(g, p, s);
+}
+size_t route_ws(const Geom& g) { return meta_ws(g) + flag_bytes(g); }
+
 size_t vt_bytes(const Geom& g) {
   return dash::prefill_uses_ring(g)
              ? align_up((size_t)g.Hkv * g.D * dash::padded_tokens(g.T, g.num_seqs) * 2)
@@ -103,7 +120,7 @@ size_t vt_bytes(const Geom& g) {
 size_t items_bytes(const Geom& g) { return align_up((size_t)dash::prefill_items_capacity(g) * 4); }
 
 struct PrefillWs {
-  size_t meta, kbar, mask, logp, vt, kdiag, items, total;
+  size_t meta, kbar, mask, logp, vt, kdiag, items, flags, total;
 };
 PrefillWs prefill_ws(const Geom& g) {
   PrefillWs w{};
@@ -122,6 +139,8 @@ PrefillWs prefill_ws(const Geom& g) {
   o += align_up((size_t)g.T * g.Hkv * g.D * elt(g));
   w.items = o;  // the attention kernel's varlen work list
   o += items_bytes(g);
+  w.flags = o;  // the routing's row-group flags
+  o += flag_bytes(g);
   w.total = o;
   return w;
 }
@@ -406,8 +425,8 @@ size_t dash_workspace_size(int op, const dash_shape* shape) {
                        op == DASH_OP_ROUTE_DECODE);
   if (check_shape(shape, 1, decode, g) != DASH_OK) return 0;
   switch (op) {
-    case DASH_OP_SUMMARIZE:
-    case DASH_OP_ROUTE: return meta_ws(g);
+    case DASH_OP_SUMMARIZE: return meta_ws(g);
+    case DASH_OP_ROUTE: return route_ws(g);
     case DASH_OP_PREFILL: return prefill_ws(g).total;
     case DASH_OP_DECODE: return decode_ws(g).total;
     case DASH_OP_SPARSE: return sparse_ws(g).total;
@@ -461,7 +480,7 @@ dash_status dash_route(const dash_shape* shape, const void* q, const void* kbar,
   dash_status st = check_shape(shape, enable_gqa, false, g);
   if (st != DASH_OK) return st;
   if ((st = check_routing(alpha, gamma, sigma, softmax_scale)) != DASH_OK) return st;
-  const size_t need = meta_ws(g);
+  const size_t need = route_ws(g);
   if ((st = check_ws(workspace, workspace_bytes, need)) != DASH_OK) return st;
   if (g.T == 0 || g.num_seqs == 0) return DASH_OK;
   if (!q || !active_blocks || (!kbar && g.T / g.B > 0)) return DASH_ERR_INVALID_ARGUMENT;
@@ -484,7 +503,7 @@ dash_status dash_route(const dash_shape* shape, const void* q, const void* kbar,
   p.log_prior = log_prior;
   p.tau = tau;
   p.rows = g.T;
-  DASH_HIP(dash::launch_route(g, p, s));
+  DASH_HIP(run_route(g, p, flag_bytes(g) ? at(workspace, meta_ws(g)) : nullptr, s));
   return DASH_OK;
 }
 
@@ -532,7 +551,7 @@ dash_status dash_attn_prefill(const dash_shape* shape, const void* q, const void
   rp.log_prior = logp;
   rp.tau = nullptr;
   rp.rows = g.T;
-  DASH_HIP(dash::launch_route(g, rp, s));
+  DASH_HIP(run_route(g, rp, w.flags < w.total ? at(workspace, w.flags) : nullptr, s));
   dash::PrefillParams pp;
   pp.q = q;
   pp.k = k;

@@ -78,6 +78,17 @@ struct RouteParams {
   int64_t row0 = 0;                     // first row of the launch (prefill row ranges)
 };
 hipError_t launch_route(const Geom& g, const RouteParams& p, hipStream_t st);
+// Streaming routing of prefill rows (route_rows.hip) where it applies (bf16,
+// G = 16 or 32, entmax, no own-chunk estimates, all rows of the call), with
+// route_fallback_kernel for the row groups it flags.  flags: workspace of
+// route_rows_flag_bytes(g) bytes (no initial contents needed).
+bool route_rows_supported(const Geom& g, const RouteParams& p);
+int route_rows_per_group(const Geom& g);
+int64_t route_rows_flag_bytes(const Geom& g);
+hipError_t launch_route_rows(const Geom& g, const RouteParams& p, uint8_t* flags,
+                             hipStream_t st);
+hipError_t launch_route_fallback(const Geom& g, const RouteParams& p, const uint8_t* flags,
+                                 hipStream_t st);
 
 // K2p: prefill attention over the active chunks and the diagonal.
 struct PrefillParams {

@@ -367,7 +367,7 @@ __device__ __forceinline__ void topk_select(const float* S, int n, int kk, uint6
 // sequence and KV head, so 16 waves share the logits and one wave solves each
 // query head's threshold).
 template <bool BF16, int D, int CP, int NTH>
-__global__ __launch_bounds__(NTH) void route_kernel(Geom g, RouteParams p) {
+__device__ void route_row(const Geom& g, const RouteParams& p, int64_t row, int h) {
   constexpr int NW = NTH / 64;              // waves
   constexpr int LPH = NW == 16 ? 64 : (CP > 1024 ? 32 : 16);  // lanes per head in the solve
   constexpr int HPW = 64 / LPH;             // heads per wave per pass
@@ -382,8 +382,6 @@ __global__ __launch_bounds__(NTH) void route_kernel(Geom g, RouteParams p) {
   __shared__ float Zs[16];          // softmax denominator (alpha = 1)
   __shared__ int Wtot[((CP + NTH - 1) / NTH) * NW + 3];  // top-k: equal keys per wave
 
-  const int64_t row = p.row0 + blockIdx.x;
-  const int h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t rows = p.rows;
 
@@ -593,6 +591,26 @@ __global__ __launch_bounds__(NTH) void route_kernel(Geom g, RouteParams p) {
     }
   }
   for (int w = tid; w < g.W; w += NTH) mrow[w] = (w < CP / 64) ? Bits[w] : 0ull;
+}
+
+template <bool BF16, int D, int CP, int NTH>
+__global__ __launch_bounds__(NTH) void route_kernel(Geom g, RouteParams p) {
+  route_row<BF16, D, CP, NTH>(g, p, p.row0 + blockIdx.x, blockIdx.y);
+}
+
+// The rows the streaming routing flagged (a head's candidate list outgrew
+// its capacity, or softmax routing), routed again one workgroup per row with
+// the whole logit row in LDS.  Persistent: workgroup x walks the rows x,
+// x + gridDim.x, ... of KV head blockIdx.y and takes the flagged ones.
+template <int D, int CP>
+__global__ __launch_bounds__(256) void route_fallback_kernel(Geom g, RouteParams p,
+                                                             const uint8_t* __restrict__ flags) {
+  const int h = blockIdx.y;
+  for (int64_t row = blockIdx.x; row < p.rows; row += gridDim.x) {
+    if (!flags[(int64_t)h * p.rows + row]) continue;
+    __syncthreads();
+    route_row<true, D, CP, 256>(g, p, row, h);
+  }
 }
 
 // Routing logits for a few rows (decode): u[q][c] = gamma*s*<q, k_bar_c> for
@@ -805,6 +823,24 @@ __global__ __launch_bounds__(256) void route_topk_select_kernel(Geom g, RoutePar
     }
   }
   for (int w = tid; w < g.W; w += NTH) mrow[w] = (w < CP / 64) ? Bits[w] : 0ull;
+}
+
+hipError_t launch_route_fallback(const Geom& g, const RouteParams& p, const uint8_t* flags,
+                                 hipStream_t st) {
+  dim3 grid((unsigned)std::min<int64_t>(p.rows, 2048), g.Hkv);
+#define DASH_FB(DD, CPV) \
+  hipLaunchKernelGGL((route_fallback_kernel<DD, CPV>), grid, dim3(256), 0, st, g, p, flags)
+#define DASH_FB_CP(DD)                                 \
+  do {                                                 \
+    if (g.C_slots <= 256) DASH_FB(DD, 256);            \
+    else if (g.C_slots <= 512) DASH_FB(DD, 512);       \
+    else if (g.C_slots <= 1024) DASH_FB(DD, 1024);     \
+    else DASH_FB(DD, 2048);                            \
+  } while (0)
+  if (g.D == 64) DASH_FB_CP(64); else DASH_FB_CP(128);
+#undef DASH_FB_CP
+#undef DASH_FB
+  return hipGetLastError();
 }
 
 hipError_t launch_route(const Geom& g, const RouteParams& p, hipStream_t st) {

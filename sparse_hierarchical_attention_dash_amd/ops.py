@@ -79,7 +79,9 @@ def summarize(k, qbar, chunk_size, cu_seqlens=None, max_seqlen=None, out=None,
     if workspace is None:
         ws, n = _workspace(L.DASH_OP_SUMMARIZE, shape, k.device)
     else:
-        ws, n = workspace, L.workspace_size(L.DASH_OP_SUMMARIZE, shape)
+        # a caller's workspace is used only when it is large enough
+        n = L.workspace_size(L.DASH_OP_SUMMARIZE, shape)
+        ws = workspace if workspace.numel() >= n else _workspace(L.DASH_OP_SUMMARIZE, shape, k.device)[0]
     L.check("dash_summarize", L.lib().dash_summarize(
         ctypes.byref(shape), _ptr(k), _ptr(qbar.float().contiguous() if qbar.dtype != torch.float32 else qbar),
         _ptr(out), _ptr(ws), n, _stream(k.device)))
@@ -125,7 +127,9 @@ def route(q, kbar, num_kv_heads, chunk_size, *, alpha=1.5, gamma=1.0, sigma=1.0,
     if workspace is None:
         ws, n = _workspace(L.DASH_OP_ROUTE, shape, dev)
     else:
-        ws, n = workspace, L.workspace_size(L.DASH_OP_ROUTE, shape)
+        # a caller's workspace is used only when it is large enough
+        n = L.workspace_size(L.DASH_OP_ROUTE, shape)
+        ws = workspace if workspace.numel() >= n else _workspace(L.DASH_OP_ROUTE, shape, dev)[0]
     L.check("dash_route", L.lib().dash_route(
         ctypes.byref(shape), _ptr(q), _ptr(kbar), _ptr(kdiag), float(alpha), _ptr(alpha_per_seq),
         float(gamma), float(sigma), float(softmax_scale), int(enable_gqa), _ptr(mask),
@@ -166,7 +170,9 @@ def route_topk(q, kbar, num_kv_heads, chunk_size, topk, *, gamma=1.0, softmax_sc
     if workspace is None:
         ws, n = _workspace(op_ws, shape, dev)
     else:
-        ws, n = workspace, L.workspace_size(op_ws, shape)
+        # a caller's workspace is used only when it is large enough
+        n = L.workspace_size(op_ws, shape)
+        ws = workspace if workspace.numel() >= n else _workspace(op_ws, shape, dev)[0]
     L.check("dash_route_topk", L.lib().dash_route_topk(
         ctypes.byref(shape), _ptr(q), _ptr(kbar), int(topk), float(gamma),
         float(softmax_scale), int(enable_gqa), _ptr(decode_seqlens), _ptr(mask), _ptr(lp),

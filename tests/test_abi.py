@@ -77,15 +77,19 @@ def test_layout_and_workspace_sizes(lib):
     lay = L.layout(s)
     assert (lay.chunk_slots, lay.mask_words) == (2048, 32)
     # prefill workspace holds summaries, a mask, the dense log-prior, (bf16,
-    # group >= 16) V transposed into 64-padded columns, and the own-chunk
-    # estimates of estimate_diagonal
+    # group >= 16) V transposed into 64-padded columns, the own-chunk
+    # estimates of estimate_diagonal, and (bf16, group 16 or 32) one flag per
+    # row and KV head of the streaming routing
     T, Hkv, D, W, C = 1000, 2, 128, 1, 16
     need = L.workspace_size(L.DASH_OP_PREFILL, shape(T=T))
+    flags = T * Hkv
     parts = [(T // 64) * Hkv * D * 2, Hkv * T * W * 8, Hkv * T * C * 4, Hkv * D * (T + 64) * 2,
-             T * Hkv * D * 2]
+             T * Hkv * D * 2, flags]
     assert need == sum((p + 255) // 256 * 256 for p in parts)
     assert L.workspace_size(L.DASH_OP_SUMMARIZE, shape()) == 0
-    assert L.workspace_size(L.DASH_OP_ROUTE, shape(cu=A, num_seqs=3)) == 512
+    # route: the varlen prefix arrays, then the row flags (256 rows x 2 heads)
+    assert L.workspace_size(L.DASH_OP_ROUTE, shape(cu=A, num_seqs=3)) == 512 + 512
+    assert L.workspace_size(L.DASH_OP_ROUTE, shape(Hq=8)) == 0   # group of 4: one row per workgroup
     assert L.workspace_size(L.DASH_OP_DECODE, shape(T=4, num_seqs=4, max_seqlen=4096)) > 0
     assert L.workspace_size(L.DASH_OP_PREFILL, shape(D=96)) == 0
 
@@ -141,12 +145,16 @@ def test_empty_input_is_a_no_op(lib):
 
 def test_route_and_summarize_checks(lib):
     s = shape()
+    n = L.workspace_size(L.DASH_OP_ROUTE, s)   # the streaming routing's row flags
+    assert n == 512
     assert lib.dash_route(ctypes.byref(s), A, A, None, 1.5, None, 1.0, 1.0, 0.0, 1, None, None,
-                          None, None, 0, None) == L.DASH_ERR_INVALID_ARGUMENT   # mask is required
+                          None, A, n, None) == L.DASH_ERR_INVALID_ARGUMENT   # mask is required
     assert lib.dash_route(ctypes.byref(s), A, A, None, 2.5, None, 1.0, 1.0, 0.0, 1, A, None,
-                          None, None, 0, None) == L.DASH_ERR_UNSUPPORTED
+                          None, A, n, None) == L.DASH_ERR_UNSUPPORTED
     assert lib.dash_route(ctypes.byref(s), A, A, A + 4, 1.5, None, 1.0, 1.0, 0.0, 1, A, None,
-                          None, None, 0, None) == L.DASH_ERR_INVALID_ARGUMENT  # kdiag misaligned
+                          None, A, n, None) == L.DASH_ERR_INVALID_ARGUMENT  # kdiag misaligned
+    assert lib.dash_route(ctypes.byref(s), A, A, None, 1.5, None, 1.0, 1.0, 0.0, 1, A, None,
+                          None, A, n - 1, None) == L.DASH_ERR_WORKSPACE_TOO_SMALL
     for args in ((None, A, A), (A, None, A), (A, A, None), (A + 2, A, A)):
         assert lib.dash_summarize_diagonal(ctypes.byref(s), *args, None) == \
             L.DASH_ERR_INVALID_ARGUMENT

@@ -69,6 +69,13 @@ ROUTE_CASES = [
     ("g1-a1", "bf16", 700, 2, 2, 128, 128, 1.0, 5.0, 1.0),
     ("g2-f32", "f32", 777, 4, 2, 64, 64, 1.5, 25.0, 2.0),
     ("g16-words", "bf16", 64 * 140 + 9, 32, 2, 128, 64, 1.5, 30.0, 1.0),  # 3 mask words
+    ("g32-a2", "bf16", 1000, 32, 1, 128, 64, 2.0, 30.0, 1.0),
+    ("g16-d64-a2", "bf16", 900, 32, 2, 64, 64, 2.0, 40.0, 0.5),
+    ("g16-b128", "bf16", 2000, 32, 2, 128, 128, 1.5, 30.0, 1.0),
+    # nearly flat logits: most chunks are threshold candidates, so the
+    # streaming routing hands its row groups to the one-row-per-workgroup path
+    ("g16-flat", "bf16", 64 * 100 + 9, 32, 2, 128, 64, 1.5, 0.3, 1.0),
+    ("g32-flat-a125", "bf16", 64 * 90, 32, 1, 128, 64, 1.25, 0.5, 1.0),
 ]
 
 
@@ -198,12 +205,16 @@ def test_prefill_custom_scale_and_needles():
     flush(f"  max-abs {r['err']:.2e} flips {r['flips']}")
 
 
-@pytest.mark.parametrize("Hkv", [2, 1])
-def test_prefill_varlen_mixed_alpha(Hkv):
-    flush(f"prefill varlen, G = {32 // Hkv}")
+@pytest.mark.parametrize("Hkv,alphas", [
+    (2, [1.25, 1.5, 2.0, 1.5, 1.25, 2.0]),
+    (1, [1.25, 1.5, 2.0, 1.5, 1.25, 2.0]),
+    (2, [1.5, 1.0, 2.0, 1.25, 1.0, 1.5]),   # softmax routing for two of the sequences
+])
+def test_prefill_varlen_mixed_alpha(Hkv, alphas):
+    flush(f"prefill varlen, G = {32 // Hkv}, alphas {alphas}")
     lens = [1, 63, 64, 65, 700, 1300]
     d = W.gen_varlen(lens, 32, Hkv, 128, seed=41, B=64)
-    alphas = np.array([1.25, 1.5, 2.0, 1.5, 1.25, 2.0], np.float32)
+    alphas = np.array(alphas, np.float32)
     cu = d["cu_seqlens"]
     q, qx = to_dev(d["q"], "bf16")
     k, kx = to_dev(d["k"], "bf16")
