@@ -6,7 +6,7 @@
 // sequence against one KV head's summaries; each wave owns RPW rows and all
 // G = 16 * HT query heads of its KV head.  No row of logits is kept: the
 // logits u = gamma * s * <q, k_bar> (16 heads x 16 chunks per bf16 MFMA tile,
-// fp32 accumulate, the summaries read straight from global memory one tile
+// fp32 accumulate, the summaries read straight from global memory three tiles
 // ahead) are recomputed in three passes over the chunks, and in x = (alpha-1) u:
 //   1. each lane keeps, per (row, head), the largest x of the chunks it
 //      holds (chunk 16 t + lane % 16): 16 partial maxima per (row, head).
@@ -19,7 +19,7 @@
 //   3. tau from the candidates alone (Newton from b, then the sort-free
 //      closed form of alpha = 2 and alpha = 1.5 on the support found); the
 //      third pass forms, per chunk, p_qc = [x_qc - tau_q]_+^(1/(alpha-1)),
-//      w_bar_c = mean over the G heads, the active bit OR_q [x_qc > tau_q]
+//      w_bar_c = mean over the G heads, the active bit w_bar_c > 0
 //      and the log-prior sigma * log(w_bar_c), and writes the mask words and
 //      the prior row directly.
 // A row with a head whose candidates outgrow the list (nearly uniform
@@ -128,8 +128,8 @@ __device__ __forceinline__ void route_rows_body(const Geom& g, const RouteParams
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) f[ks] = ldg16(krow + 32 * ks);
   };
-  // one pass over the chunk tiles: body(t, j, ht, x[4]) with x the logits of
-  // heads 16 ht + 4 gq + jj, chunk 16 t + r, in x units
+  // one pass over the chunk tiles: body(t, j, ht, a[4]) with a the logits of
+  // heads 16 ht + 4 gq + jj, chunk 16 t + r, as accumulated (x = a * xsc)
   auto pass = [&](auto&& body) {
     if (ntile == 0) return;
     constexpr int NB = kRrAhead + 1;
@@ -172,10 +172,10 @@ __device__ __forceinline__ void route_rows_body(const Geom& g, const RouteParams
         for (int j = 0; j < RPW; ++j)
 #pragma unroll
           for (int ht = 0; ht < HT; ++ht) {
-            float x[4];
+            float a[4];
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) x[jj] = acc[j][ht][jj] * xsc;
-            body(t, j, ht, x);
+            for (int jj = 0; jj < 4; ++jj) a[jj] = acc[j][ht][jj];
+            body(t, j, ht, a);
           }
       });
     }
@@ -189,10 +189,12 @@ __device__ __forceinline__ void route_rows_body(const Geom& g, const RouteParams
     for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) mx[j][ht][jj] = -INFINITY;
-  pass([&](int t, int j, int ht, const float (&x)[4]) {
+  // (the maximum of the accumulated logits, scaled once after the pass: the
+  // scale is positive, so this is the maximum of the scaled ones)
+  pass([&](int t, int j, int ht, const float (&a)[4]) {
     const bool ok = 16 * t + r < n[j];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) mx[j][ht][jj] = fmaxf(mx[j][ht][jj], ok ? x[jj] : -INFINITY);
+    for (int jj = 0; jj < 4; ++jj) mx[j][ht][jj] = fmaxf(mx[j][ht][jj], ok ? a[jj] : -INFINITY);
   });
   // the 16 lanes of a lane group hold one (row, head)'s partial maxima
 #pragma unroll
@@ -201,7 +203,7 @@ __device__ __forceinline__ void route_rows_body(const Geom& g, const RouteParams
     for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const float v = mx[j][ht][jj];
+        const float v = mx[j][ht][jj] * xsc;
         const float top = row16_max(v);
         float b = top - 1.f;  // the top value alone has mass 1 here
 #pragma unroll
@@ -228,14 +230,26 @@ __device__ __forceinline__ void route_rows_body(const Geom& g, const RouteParams
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) cnt[j][ht][jj] = 0;
   const uint32_t below = (1u << r) - 1u;
-  pass([&](int t, int j, int ht, const float (&x)[4]) {
+  // the bound in accumulated units: x > tau implies x > b plus the bound's
+  // margin, far above the rounding of either scaling, so comparing a with
+  // b / xsc still keeps every x > tau
+  float braw[RPW][HT][4];
+#pragma unroll
+  for (int j = 0; j < RPW; ++j)
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) braw[j][ht][jj] = mx[j][ht][jj] / xsc;
+  pass([&](int t, int j, int ht, const float (&a)[4]) {
     const bool ok = 16 * t + r < n[j];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const bool c = ok && x[jj] > mx[j][ht][jj];
-      const uint32_t grp = (uint32_t)(__ballot(c) >> (16 * gq)) & 0xffffu;
-      const int slot = cnt[j][ht][jj] + __popc(grp & below);
-      if (c && slot < kRrCap) Cand[wv][j * NH + 16 * ht + 4 * gq + jj][slot] = x[jj];
+      const bool c = ok && a[jj] > braw[j][ht][jj];
+      const uint32_t grp =
+          (uint32_t)(__builtin_amdgcn_ballot_w64(c) >> (16 * gq)) & 0xffffu;
+      // past the capacity: the row's pad word (the count records the overflow)
+      const int slot = ::min(cnt[j][ht][jj] + (int)__popc(grp & below), kRrCap);
+      if (c) Cand[wv][j * NH + 16 * ht + 4 * gq + jj][slot] = a[jj] * xsc;
       cnt[j][ht][jj] += __popc(grp);
     }
   });
@@ -362,29 +376,24 @@ __device__ __forceinline__ void route_rows_body(const Geom& g, const RouteParams
   const float invG = 1.f / (float)g.G;
   uint64_t word[RPW];
   float wsum[RPW];
-  bool on[RPW];
 #pragma unroll
   for (int j = 0; j < RPW; ++j) word[j] = 0ull;
-  pass([&](int t, int j, int ht, const float (&x)[4]) {
-    if (ht == 0) {
-      wsum[j] = 0.f;
-      on[j] = false;
-    }
+  pass([&](int t, int j, int ht, const float (&a)[4]) {
+    if (ht == 0) wsum[j] = 0.f;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const float d = x[jj] - tq[j][ht][jj];
+      const float d = a[jj] * xsc - tq[j][ht][jj];
       float pw, pd;
       rr_pow<ECLS>(fmaxf(d, 0.f), ex, pw, pd);
       wsum[j] += pw;
-      on[j] = on[j] || d > 0.f;
     }
     if (ht != HT - 1) return;
-    // sum over the four lane groups (the group's heads), in a fixed order
+    // sum over the four lane groups (the group's heads), in a fixed order;
+    // the chunk is active iff some head's weight is positive
     float w = wsum[j] + xor16(wsum[j]);
     w += xor32(w);
     const int c = 16 * t + r;
-    const uint64_t bb = __ballot(on[j] && c < n[j]);
-    const uint32_t act = (uint32_t)((bb | (bb >> 16) | (bb >> 32) | (bb >> 48)) & 0xffffull);
+    const uint32_t act = (uint32_t)(__builtin_amdgcn_ballot_w64(w > 0.f && c < n[j]) & 0xffffull);
     // the row's lane group (j % 4) writes its 16 chunks of the prior
     if (p.log_prior && gq == (j & 3) && c < n[j] && !ovr[j]) {
       const bool a = (act >> r) & 1u;
