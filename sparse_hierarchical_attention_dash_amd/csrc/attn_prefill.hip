@@ -552,11 +552,12 @@ __device__ __forceinline__ void visit_ring(lds_u8* ks_, lds_u8* vt_,
 // so P = NT / (G / 16) positions (P divides B: the positions share one
 // diagonal chunk).  The blocks of the workgroup's list stream through a
 // 4-slot LDS ring filled by direct global->LDS loads (K rows from K, V^T rows
-// from the V^T workspace, and each tile's bias for the block), three blocks
-// ahead of the one being consumed.  Which positions have each listed chunk
-// active is worked out once, up front, into a bitmap in LDS, so the loop reads
-// no memory but LDS.  Waits are counted (vmcnt) and the barrier carries no
-// fence.
+// from the V^T workspace, and each tile's bias for the block): with 64-key
+// chunks two blocks per barrier, the next two loading meanwhile; with
+// 128-key chunks one block per barrier, three blocks ahead.  Which positions
+// have each listed chunk active is worked out once, up front, into a bitmap
+// in LDS, so the loop reads no memory but LDS.  Waits are counted (vmcnt) and
+// the barrier carries no fence.
 //   PAIR: a wave's tiles 2k and 2k+1 always share their position (G = 32), so
 //         they visit together and every LDS fragment feeds both; otherwise
 //         each active tile visits alone.
@@ -799,44 +800,80 @@ __global__ __launch_bounds__(64 * NWV, 1) void prefill_attn_ring_kernel(
     });
   };
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4));  // Q and mask reads done first
-  // Every step issues exactly one block's loads (past the end of the list it
-  // re-reads the last block into the free slot, which no later step reads), so
-  // when step st waits, exactly two blocks' loads are younger than its own:
-  // one fixed counted wait proves slot st & 3 complete.
-  issue(0, ring0, bias0);
-  issue(min(1, NS - 1), ring0 + R::STAGE, bias0 + 4 * NT);
-  issue(min(2, NS - 1), ring0 + 2 * R::STAGE, bias0 + 8 * NT);
-  // wait for slot st & 3 and for every wave to be done with slot (st + 3) & 3
-  auto enter = [&](int st) -> lds_u8* {
-    // own loads of this slot done (the two younger blocks may stay in
-    // flight), this wave's LDS reads of the slot about to be refilled done
-    wait_vm<2 * RS::LPS>();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    return (lds_u8*)&ring[st & 3][0];
-  };
-  // refill of the slot released at the step's barrier with the block three
-  // steps ahead
-  auto leave = [&](int st, int cnext) {
-    const int sr = st + 3, sx = min(sr, NS - 1);
-    issue_at(block_key0(sx, cnext), cnext, ring0 + (sr & 3) * R::STAGE,
-             bias0 + (sr & 3) * 4 * NT);
-  };
-  for (int st = 0; st < nrouted; ++st) {
-    lds_u8* kv = enter(st);
-    const int cnext = listed(min(st + 3, NS - 1));  // read now, used by the refill
-    const uint32_t am = active_mask(st >> sbl);
-    // a wave with nothing to visit issues the refill at once; a visiting wave
-    // issues it afterwards, when the other waves' loads have left the queue
-    if (!am) leave(st, cnext);
-    routed_step(st, kv, am);
-    if (am) leave(st, cnext);
-  }
-  for (int st = nrouted; st < NS; ++st) {
-    lds_u8* kv = enter(st);
-    diag_step(st, kv);
-    leave(st, 0);
+  if (sbl == 0) {
+    // Chunks of 64 keys: two blocks per barrier.  Step st (even) waits for
+    // its own loads of blocks st and st + 1, and at its barrier every wave has
+    // left blocks st - 2 and st - 1, whose slots then take blocks st + 2 and
+    // st + 3.  A wave then visits its tiles of both blocks before the next
+    // barrier, so the wait at a barrier is for the busiest wave over two
+    // blocks rather than over each one (the active tiles of two different
+    // chunks even out between the waves; 64K prefill 18.4 -> 16.5 ms).
+    issue(0, ring0, bias0);
+    if (NS > 1) issue(1, ring0 + R::STAGE, bias0 + 4 * NT);
+    auto pair_enter = [&](int st) {
+      if (st & 1) return;
+      wait_vm<0>();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+#pragma unroll 1
+      for (int b = st + 2; b < min(st + 4, NS); ++b)
+        issue(b, ring0 + (b & 3) * R::STAGE, bias0 + (b & 3) * 4 * NT);
+    };
+    // (one visit per iteration: a loop over the pair's two blocks made the
+    // compiler move every O accumulator between registers each step)
+    for (int st = 0; st < nrouted; ++st) {
+      pair_enter(st);
+      routed_step(st, (lds_u8*)&ring[st & 3][0], active_mask(st));
+    }
+    for (int st = nrouted; st < NS; ++st) {
+      pair_enter(st);
+      diag_step(st, (lds_u8*)&ring[st & 3][0]);
+    }
+  } else {
+    // Chunks of 128 keys: both blocks of a chunk have the same active tiles,
+    // so pairing them evens nothing out; one block per barrier, loads three
+    // blocks ahead.  Every step issues exactly one block's loads (past the end
+    // of the list it re-reads the last block into the free slot, which no
+    // later step reads), so when step st waits, exactly two blocks' loads are
+    // younger than its own: one fixed counted wait proves slot st & 3
+    // complete.
+    issue(0, ring0, bias0);
+    issue(min(1, NS - 1), ring0 + R::STAGE, bias0 + 4 * NT);
+    issue(min(2, NS - 1), ring0 + 2 * R::STAGE, bias0 + 8 * NT);
+    // wait for slot st & 3 and for every wave to be done with slot (st + 3) & 3
+    auto enter = [&](int st) -> lds_u8* {
+      // own loads of this slot done (the two younger blocks may stay in
+      // flight), this wave's LDS reads of the slot about to be refilled done
+      wait_vm<2 * RS::LPS>();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      return (lds_u8*)&ring[st & 3][0];
+    };
+    // refill of the slot released at the step's barrier with the block three
+    // steps ahead
+    auto leave = [&](int st, int cnext) {
+      const int sr = st + 3, sx = min(sr, NS - 1);
+      issue_at(block_key0(sx, cnext), cnext, ring0 + (sr & 3) * R::STAGE,
+               bias0 + (sr & 3) * 4 * NT);
+    };
+    for (int st = 0; st < nrouted; ++st) {
+      lds_u8* kv = enter(st);
+      const int cnext = listed(min(st + 3, NS - 1));  // read now, used by the refill
+      const uint32_t am = active_mask(st >> sbl);
+      // a wave with nothing to visit issues the refill at once; a visiting
+      // wave issues it afterwards, when the other waves' loads have left the
+      // queue
+      if (!am) leave(st, cnext);
+      routed_step(st, kv, am);
+      if (am) leave(st, cnext);
+    }
+    for (int st = nrouted; st < NS; ++st) {
+      lds_u8* kv = enter(st);
+      diag_step(st, kv);
+      leave(st, 0);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4));  // no ring load outlives the kernel
 
@@ -1337,7 +1374,7 @@ __global__ __launch_bounds__(1024) void prefill_schedule_kernel(const int32_t* _
 
 // The forward launch: eight waves of two tiles (four waves of eight tiles hold
 // 384 of the 512 registers of a lane in Q and O alone at D = 128 and spill).
-constexpr int kFwdWaves = kRingWaves, kFwdTW = 2, kFwdNFR = 3;
+constexpr int kFwdWaves = kRingWaves, kFwdTW = 2, kFwdNFR = 2;
 
 int prefill_positions_per_tile(const Geom& g) {
   return make_ring_tiles(g, kFwdWaves * kFwdTW, kFwdTW).P;
