@@ -600,14 +600,53 @@ __global__ __launch_bounds__(NTH) void route_kernel(Geom g, RouteParams p) {
 
 // The rows the streaming routing flagged (a head's candidate list outgrew
 // its capacity, or softmax routing), routed again one workgroup per row with
-// the whole logit row in LDS.  Persistent: workgroup x walks the rows x,
-// x + gridDim.x, ... of KV head blockIdx.y and takes the flagged ones.
+// the whole logit row in LDS.  Every workgroup of KV head blockIdx.y counts
+// the head's flagged rows (thread t over a contiguous range of rows) and
+// takes those of rank blockIdx.x, blockIdx.x + gridDim.x, ...: the flagged
+// rows spread evenly over the grid however they cluster, and a workgroup
+// with none of them is done after one read of the flags.
 template <int D, int CP>
 __global__ __launch_bounds__(256) void route_fallback_kernel(Geom g, RouteParams p,
                                                              const uint8_t* __restrict__ flags) {
+  __shared__ int wsum[4];
+  __shared__ int64_t pick;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int h = blockIdx.y;
-  for (int64_t row = blockIdx.x; row < p.rows; row += gridDim.x) {
-    if (!flags[(int64_t)h * p.rows + row]) continue;
+  const uint8_t* f = flags + (int64_t)h * p.rows;
+  const int64_t per = (p.rows + 255) / 256;
+  const int64_t r0 = min(p.rows, (int64_t)tid * per), r1 = min(p.rows, r0 + per);
+  int cnt = 0;
+  for (int64_t r = r0; r < r1; ++r) cnt += f[r] ? 1 : 0;
+  int inc = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) wsum[wv] = inc;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    before += w < wv ? wsum[w] : 0;
+    total += wsum[w];
+  }
+  const int base = before + inc - cnt;  // rank of this thread's first flagged row
+  for (int k = blockIdx.x; k < total; k += gridDim.x) {
+    if (k >= base && k < base + cnt) {
+      int want = k - base;
+      for (int64_t r = r0; r < r1; ++r) {
+        if (f[r]) {
+          if (want == 0) {
+            pick = r;
+            break;
+          }
+          --want;
+        }
+      }
+    }
+    __syncthreads();
+    const int64_t row = pick;
     __syncthreads();
     route_row<true, D, CP, 256>(g, p, row, h);
   }
@@ -827,7 +866,7 @@ __global__ __launch_bounds__(256) void route_topk_select_kernel(Geom g, RoutePar
 
 hipError_t launch_route_fallback(const Geom& g, const RouteParams& p, const uint8_t* flags,
                                  hipStream_t st) {
-  dim3 grid((unsigned)std::min<int64_t>(p.rows, 2048), g.Hkv);
+  dim3 grid((unsigned)std::min<int64_t>(p.rows, 256), g.Hkv);
 #define DASH_FB(DD, CPV) \
   hipLaunchKernelGGL((route_fallback_kernel<DD, CPV>), grid, dim3(256), 0, st, g, p, flags)
 #define DASH_FB_CP(DD)                                 \
