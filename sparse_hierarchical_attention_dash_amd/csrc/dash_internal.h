@@ -83,6 +83,9 @@ hipError_t launch_route(const Geom& g, const RouteParams& p, hipStream_t st);
 // route_fallback_kernel for the row groups it flags.  flags: workspace of
 // route_rows_flag_bytes(g) bytes (no initial contents needed).
 bool route_rows_supported(const Geom& g, const RouteParams& p);
+// Bytes between two KV heads' flag rows (flags[h * stride + row], 0 or 1):
+// whole 16-byte words, so that the fallback reads them four rows at a time.
+__host__ __device__ inline int64_t route_flag_stride(int64_t rows) { return (rows + 15) & ~(int64_t)15; }
 int route_rows_per_group(const Geom& g);
 int64_t route_rows_flag_bytes(const Geom& g);
 hipError_t launch_route_rows(const Geom& g, const RouteParams& p, uint8_t* flags,

@@ -601,10 +601,11 @@ __global__ __launch_bounds__(NTH) void route_kernel(Geom g, RouteParams p) {
 // The rows the streaming routing flagged (a head's candidate list outgrew
 // its capacity, or softmax routing), routed again one workgroup per row with
 // the whole logit row in LDS.  Every workgroup of KV head blockIdx.y counts
-// the head's flagged rows (thread t over a contiguous range of rows) and
-// takes those of rank blockIdx.x, blockIdx.x + gridDim.x, ...: the flagged
-// rows spread evenly over the grid however they cluster, and a workgroup
-// with none of them is done after one read of the flags.
+// the head's flagged rows (thread t reads the flag words t, t + 256, ...,
+// four rows a word) and takes those of rank blockIdx.x, blockIdx.x +
+// gridDim.x, ... in that order: the flagged rows spread evenly over the grid
+// however they cluster, and a workgroup with none of them is done after one
+// read of the flags.
 template <int D, int CP>
 __global__ __launch_bounds__(256) void route_fallback_kernel(Geom g, RouteParams p,
                                                              const uint8_t* __restrict__ flags) {
@@ -612,11 +613,15 @@ __global__ __launch_bounds__(256) void route_fallback_kernel(Geom g, RouteParams
   __shared__ int64_t pick;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int h = blockIdx.y;
-  const uint8_t* f = flags + (int64_t)h * p.rows;
-  const int64_t per = (p.rows + 255) / 256;
-  const int64_t r0 = min(p.rows, (int64_t)tid * per), r1 = min(p.rows, r0 + per);
+  const uint32_t* fw = (const uint32_t*)(flags + (int64_t)h * route_flag_stride(p.rows));
+  const int64_t nw = (p.rows + 3) / 4;
+  // word w's flags (one byte per row, 0 or 1), bytes past the last row cleared
+  auto word = [&](int64_t w) -> uint32_t {
+    const int64_t left = p.rows - 4 * w;
+    return fw[w] & (left >= 4 ? 0xffffffffu : (1u << (8 * left)) - 1u);
+  };
   int cnt = 0;
-  for (int64_t r = r0; r < r1; ++r) cnt += f[r] ? 1 : 0;
+  for (int64_t w = tid; w < nw; w += 256) cnt += __popc(word(w));
   int inc = cnt;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -635,14 +640,15 @@ __global__ __launch_bounds__(256) void route_fallback_kernel(Geom g, RouteParams
   for (int k = blockIdx.x; k < total; k += gridDim.x) {
     if (k >= base && k < base + cnt) {
       int want = k - base;
-      for (int64_t r = r0; r < r1; ++r) {
-        if (f[r]) {
-          if (want == 0) {
-            pick = r;
-            break;
-          }
-          --want;
+      for (int64_t w = tid; w < nw; w += 256) {
+        uint32_t v = word(w);
+        const int c = __popc(v);
+        if (want < c) {
+          for (; want > 0; --want) v &= v - 1;
+          pick = 4 * w + (__ffs(v) - 1) / 8;
+          break;
         }
+        want -= c;
       }
     }
     __syncthreads();

@@ -269,7 +269,7 @@ __device__ __forceinline__ void route_rows_body(const Geom& g, const RouteParams
         }
       }
     ovr[j] = __ballot(over) != 0ull;
-    if (lane == 0 && pos[j] < si.len) flags[(int64_t)h * rows + tok[j]] = ovr[j] ? 1 : 0;
+    if (lane == 0 && pos[j] < si.len) flags[(int64_t)h * route_flag_stride(rows) + tok[j]] = ovr[j] ? 1 : 0;
   }
 
   // ---- 3a. thresholds: lane l solves (row l / NH, head l % NH) on its list,
@@ -434,7 +434,7 @@ __global__ __launch_bounds__(64 * kRrWaves) void route_rows_kernel(Geom g, Route
       const int pos0 = (gps - 1 - blockIdx.x % gps) * R;
       const SeqInfo si = seq_info(g.cu_seqlens, g.cu_chunks, s, g.max_seqlen, g.B);
       const int i = pos0 + threadIdx.x;
-      if (threadIdx.x < R && i < si.len) flags[(int64_t)blockIdx.y * p.rows + si.start + i] = 1;
+      if (threadIdx.x < R && i < si.len) flags[(int64_t)blockIdx.y * route_flag_stride(p.rows) + si.start + i] = 1;
       return;
     }
     if (e == 1.f) route_rows_body<D, RPW, HT, 1>(g, p, flags, sh);
@@ -451,7 +451,7 @@ bool route_rows_supported(const Geom& g, const RouteParams& p) {
 
 int route_rows_per_group(const Geom& g) { return kRrWaves * (g.G == 32 ? 2 : 4); }
 
-int64_t route_rows_flag_bytes(const Geom& g) { return g.T * g.Hkv; }
+int64_t route_rows_flag_bytes(const Geom& g) { return route_flag_stride(g.T) * g.Hkv; }
 
 hipError_t launch_route_rows(const Geom& g, const RouteParams& p, uint8_t* flags,
                              hipStream_t st) {

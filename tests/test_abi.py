@@ -79,10 +79,11 @@ def test_layout_and_workspace_sizes(lib):
     # prefill workspace holds summaries, a mask, the dense log-prior, (bf16,
     # group >= 16) V transposed into 64-padded columns, the own-chunk
     # estimates of estimate_diagonal, and (bf16, group 16 or 32) one flag per
-    # row and KV head of the streaming routing
+    # row and KV head of the streaming routing (each head's row of flags
+    # padded to 16 bytes)
     T, Hkv, D, W, C = 1000, 2, 128, 1, 16
     need = L.workspace_size(L.DASH_OP_PREFILL, shape(T=T))
-    flags = T * Hkv
+    flags = (T + 15) // 16 * 16 * Hkv
     parts = [(T // 64) * Hkv * D * 2, Hkv * T * W * 8, Hkv * T * C * 4, Hkv * D * (T + 64) * 2,
              T * Hkv * D * 2, flags]
     assert need == sum((p + 255) // 256 * 256 for p in parts)
