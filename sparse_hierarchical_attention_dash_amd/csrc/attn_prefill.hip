@@ -587,6 +587,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void prefill_attn_ring_kernel(
   __shared__ uint16_t Blist[2048];
   using ActT = typename std::conditional<NT <= 16, uint16_t, uint32_t>::type;
   __shared__ ActT Act[2048];   // bit t: position p0 + t has chunk Blist[j] active
+  __shared__ uint16_t Ord[2048];  // visiting order of the list (64-key chunks)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in an SGPR
@@ -677,6 +678,76 @@ __global__ __launch_bounds__(64 * NWV, 1) void prefill_attn_ring_kernel(
   }
   __syncthreads();
   const int sbl = g.B == 128 ? 1 : 0;  // log2 of the 64-key blocks per chunk
+
+  // ---- visiting order (64-key chunks).  The loop below takes two listed
+  // chunks per barrier, so the wait at a barrier is for the busiest wave over
+  // both; they are paired so that their active tiles fall on different
+  // waves.  Wave w pairs the entries of list blocks w, w + NWV, ... (64
+  // entries each) greedily: the first unpaired entry i of the block takes
+  // the first unpaired entry after it whose pairing keeps every wave at one
+  // visit, else at two, else any.  vw packs per wave (4 bits each) the tile
+  // visits of an entry; a sum of two never carries between the fields.
+  if (sbl == 0 && nlist > 2) {
+    for (int b = wv; b * 64 < nlist; b += NWV) {
+      const int e = b * 64 + lane;
+      uint32_t v = 0;
+      if (e < nlist) {
+        const uint32_t act = Act[e];
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) {
+          uint32_t c = 0;
+#pragma unroll
+          for (int u = 0; u < TW; ++u) c += (act >> ((TW * w + u) / tg.HT)) & 1u;
+          v |= c << (4 * w);
+        }
+      }
+      uint64_t taken = ~__ballot(e < nlist);
+      int out = b * 64;
+      while (~taken) {
+        const int i = __ffsll((long long)~taken) - 1;
+        taken |= 1ull << i;
+        const uint32_t t = (uint32_t)__builtin_amdgcn_readlane((int)v, i) + v;
+        // 1: no wave visits twice, 2: at most twice, 3: more; 4: taken
+        const bool ge2 = ((t + 0x66666666u) & 0x88888888u) != 0u;
+        const bool ge3 = ((t + 0x55555555u) & 0x88888888u) != 0u;
+        const int k = ((taken >> lane) & 1ull) ? 4 : (ge3 ? 3 : (ge2 ? 2 : 1));
+        int j = -1;
+        for (int cls = 1; cls <= 3 && j < 0; ++cls) {
+          const uint64_t bm = __ballot(k <= cls);
+          if (bm) j = __ffsll((long long)bm) - 1;
+        }
+        if (lane == 0) {
+          Ord[out] = (uint16_t)(b * 64 + i);
+          if (j >= 0) Ord[out + 1] = (uint16_t)(b * 64 + j);
+        }
+        out += j >= 0 ? 2 : 1;
+        if (j >= 0) taken |= 1ull << j;
+      }
+    }
+    __syncthreads();
+    constexpr int PER = (2048 + NTH - 1) / NTH;
+    uint16_t tb[PER];
+    ActT ta[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int j = tid + q * NTH;
+      if (j < nlist) {
+        const int o = Ord[j];
+        tb[q] = Blist[o];
+        ta[q] = Act[o];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int j = tid + q * NTH;
+      if (j < nlist) {
+        Blist[j] = tb[q];
+        Act[j] = ta[q];
+      }
+    }
+    __syncthreads();
+  }
   const int nrouted = nlist << sbl;
   const int ndiag = (pend - cdiag * g.B + 63) / 64;
   const int NS = nrouted + ndiag;
