@@ -367,7 +367,7 @@ __device__ __forceinline__ void topk_select(const float* S, int n, int kk, uint6
 // sequence and KV head, so 16 waves share the logits and one wave solves each
 // query head's threshold).
 template <bool BF16, int D, int CP, int NTH>
-__device__ void route_row(const Geom& g, const RouteParams& p, int64_t row, int h) {
+__device__ __forceinline__ void route_row(const Geom& g, const RouteParams& p, int64_t row, int h) {
   constexpr int NW = NTH / 64;              // waves
   constexpr int LPH = NW == 16 ? 64 : (CP > 1024 ? 32 : 16);  // lanes per head in the solve
   constexpr int HPW = 64 / LPH;             // heads per wave per pass
