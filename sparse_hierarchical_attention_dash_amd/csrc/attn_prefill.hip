@@ -686,9 +686,12 @@ __global__ __launch_bounds__(64 * NWV, 1) void prefill_attn_ring_kernel(
   // both; they are paired so that their active tiles fall on different
   // waves.  Wave w pairs the entries of list blocks w, w + NWV, ... (64
   // entries each) greedily: the first unpaired entry i of the block takes
-  // the first unpaired entry after it whose pairing keeps every wave at one
-  // visit, else at two, else any.  vw packs per wave (4 bits each) the tile
-  // visits of an entry; a sum of two never carries between the fields.
+  // the first unpaired entry after it that keeps the pair's load lowest.
+  // With two tiles a wave: every wave at one visit, else at two, else any
+  // (v packs per wave, 4 bits each, the tile visits of an entry; a sum of two
+  // never carries between the fields).  With one tile a wave: the busiest
+  // SIMD's visits, then whether some wave visits twice (16 waves x 1 tile:
+  // 64K attention 15.1 -> 14.9 ms against the wave rule alone).
   if (sbl == 0 && nlist > 2) {
     for (int b = wv; b * 64 < nlist; b += NWV) {
       const int e = b * 64 + lane;
@@ -710,20 +713,38 @@ __global__ __launch_bounds__(64 * NWV, 1) void prefill_attn_ring_kernel(
         }
       }
       uint64_t taken = ~__ballot(e < nlist);
+      // one tile a wave: the visits per SIMD too (4 bits each), taking wave w
+      // to run on SIMD w % 4 (waves are placed on the four SIMDs in turn)
+      uint32_t sl = 0;
+      if constexpr (TW == 1) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sl |= (uint32_t)__popc(v & (0x1111u << q)) << (4 * q);
+      }
       int out = b * 64;
       while (~taken) {
         const int i = __ffsll((long long)~taken) - 1;
         taken |= 1ull << i;
         const uint32_t vi = (uint32_t)__builtin_amdgcn_readlane((int)v, i);
         const uint32_t t = vi + v;
+        int j = -1;
+        if constexpr (TW == 1) {
+          // the partner keeping the busiest SIMD lowest, then no wave twice
+          const uint32_t ts = (uint32_t)__builtin_amdgcn_readlane((int)sl, i) + sl;
+          const uint32_t mx = max(max(ts & 15u, (ts >> 4) & 15u), max((ts >> 8) & 15u, ts >> 12));
+          int k = ((taken >> lane) & 1ull) ? 64 : (int)(2 * mx + ((vi & v) ? 1u : 0u));
+          int km = k;
+#pragma unroll
+          for (int o = 1; o < 64; o <<= 1) km = min(km, __shfl_xor(km, o));
+          if (km < 64) j = __ffsll((long long)__ballot(k == km)) - 1;
+        } else {
         // 1: no wave visits twice, 2: at most twice, 3: more; 4: taken
         const bool ge2 = TW == 1 ? (vi & v) != 0u : ((t + 0x66666666u) & 0x88888888u) != 0u;
         const bool ge3 = TW == 1 ? false : ((t + 0x55555555u) & 0x88888888u) != 0u;
         const int k = ((taken >> lane) & 1ull) ? 4 : (ge3 ? 3 : (ge2 ? 2 : 1));
-        int j = -1;
         for (int cls = 1; cls <= 3 && j < 0; ++cls) {
           const uint64_t bm = __ballot(k <= cls);
           if (bm) j = __ffsll((long long)bm) - 1;
+        }
         }
         if (lane == 0) {
           Ord[out] = (uint16_t)(b * 64 + i);
