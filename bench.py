@@ -773,6 +773,16 @@ def main():
             t_app = time_it(stream, append, 10)
             g_app = graph_time(stream, append_dec, [out_d], 10)
 
+            # the same append + step as one fused call (dash_attn_decode_append)
+            def fused_dec():
+                ops.attn_decode_append(qd, kn, vn, kc, vc, seqlens, kbar_c, qbar_d, wd.B,
+                                       alpha=wd.alpha, gamma=wd.gamma, sigma=wd.sigma,
+                                       workspace=ws_dec, out=out_d)
+
+            t_app_dec = time_it(stream, append_dec, 10)
+            t_fused = time_it(stream, fused_dec, 10)
+            g_fused = graph_time(stream, fused_dec, [out_d], 10)
+
             def diag_dec():
                 ops.attn_decode(qd, kc, vc, seqlens, kbar_c, wd.B, alpha=wd.alpha,
                                 gamma=wd.gamma, sigma=wd.sigma, workspace=ws_dec, out=out_d,
@@ -795,6 +805,8 @@ def main():
                 "graph_us": {"dash": g_dash * 1e3, "dense": g_dense * 1e3,
                              "topk": g_topk * 1e3},
                 "append_us": t_app * 1e3, "graph_us_append_and_step": g_app * 1e3,
+                "append_then_step_us": t_app_dec * 1e3, "fused_append_step_us": t_fused * 1e3,
+                "graph_us_fused_append_step": g_fused * 1e3,
                 "graph_speedup_vs_dense": g_dense / g_dash,
                 "graph_speedup_vs_topk": g_topk / g_dash}
         res["compare"] = cmp

@@ -242,6 +242,34 @@ dash_status dash_attn_decode(const dash_shape* shape, const void* q,
                              void* out, float* lse, uint64_t* active_blocks, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* dash_cache_append and dash_attn_decode as one fused step: the new tokens'
+ * K/V rows go to position seqlens[b]-1 of the caches, the chunk each of them
+ * completes is summarised into kbar_cache, and the new queries are decoded
+ * over the updated caches.  A chunk's summary is computed once, by the step
+ * whose token completes it, "fused into the decode step" (incremental
+ * decoding: "Belangrijkste Bijdragen", the GPU implementation item, of the
+ * gist.science summary; "Fase 0", Efficientie bullet, for the cached
+ * summaries).  For bf16 without estimate_diagonal the append runs inside the
+ * routing's first launch, beside the logits (which never read what it
+ * writes: a query routes only the chunks before its own); otherwise it is a
+ * launch of its own before the step.  Results equal dash_cache_append then
+ * dash_attn_decode with the same arguments, bit for bit.
+ * Arguments as dash_attn_decode and dash_cache_append, with:
+ *   k_new, v_new   [batch, Hkv, D] dtype            (input)
+ *   k_cache,v_cache[batch, capacity, Hkv, D] dtype  (in/out: row L-1 written)
+ *   kbar_cache     [batch, capacity/B, Hkv, D] dtype (in/out: row L/B-1 written
+ *                                                    when L % B == 0)
+ *   qbar           [Hkv, D] fp32                    (input, required)
+ *   workspace      dash_workspace_size(DASH_OP_DECODE, shape) bytes
+ * NULL or misaligned k_new / v_new / qbar: DASH_ERR_INVALID_ARGUMENT. */
+dash_status dash_attn_decode_append(const dash_shape* shape, const void* q, const void* k_new,
+                                    const void* v_new, void* k_cache, void* v_cache,
+                                    const int32_t* seqlens, void* kbar_cache, const float* qbar,
+                                    float alpha, float gamma, float sigma, float softmax_scale,
+                                    int enable_gqa, int estimate_diagonal, void* out, float* lse,
+                                    uint64_t* active_blocks, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
 /* dash_attn_decode for callers that cannot allocate device memory: code that
  * runs under HIP graph capture, tight serving loops, and hosts that forbid
  * allocation.  Same arguments, layout and results as dash_attn_decode, without

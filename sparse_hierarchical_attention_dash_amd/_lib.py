@@ -37,7 +37,7 @@ EXPORTED = ("dash_get_layout", "dash_summarize", "dash_route", "dash_attn_prefil
             "dash_attn_sparse", "dash_attn_decode", "dash_route_topk", "dash_attn_decode_sparse",
             "dash_cache_append", "dash_summarize_diagonal", "dash_attn_sparse_backward",
             "dash_attn_prefill_backward", "dash_attn_decode_noalloc", "dash_noalloc_scratch_need", "dash_probe_peak",
-            "dash_prefill_schedule",
+            "dash_prefill_schedule", "dash_attn_decode_append",
             "dash_workspace_size", "dash_status_string", "dash_abi_version")
 
 
@@ -111,6 +111,9 @@ def lib():
     L.dash_attn_decode.restype = _I
     L.dash_attn_decode.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _P, _F, _F, _F, _F, _I, _I, _P,
                                    _P, _P, _P, _SZ, _P]
+    L.dash_attn_decode_append.restype = _I
+    L.dash_attn_decode_append.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _P, _P, _P, _F, _F, _F,
+                                          _F, _I, _I, _P, _P, _P, _P, _SZ, _P]
     L.dash_attn_decode_noalloc.restype = _I
     L.dash_attn_decode_noalloc.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _P, _F, _F, _F, _F, _I,
                                            _I, _P, _P, _P, _P]

@@ -288,15 +288,40 @@ char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
     if ((call) != hipSuccess) return DASH_ERR_HIP;  \
   } while (0)
 
+// The new tokens a fused decode step appends (dash_attn_decode_append).
+struct DecodeAppend {
+  const void* k_new = nullptr;
+  const void* v_new = nullptr;
+  void* k_cache = nullptr;
+  void* v_cache = nullptr;
+  void* kbar_cache = nullptr;
+};
+
 // The decode step on a given workspace (already checked to be large enough).
+// app: the step's cache append, or null.  It runs inside the routing's logits
+// pass where that pass is the step's first launch (bf16, no own-chunk
+// estimates), else as its own launch first.
 dash_status decode_run(Geom& g, const DecodeWs& w, const void* q, const void* k_cache,
                        const void* v_cache, const int32_t* seqlens, const void* kbar_cache,
                        const float* qbar, float alpha, float gamma, float sigma,
                        float softmax_scale, int estimate_diagonal, void* out, float* lse,
-                       uint64_t* active_blocks, void* workspace, hipStream_t s) {
+                       uint64_t* active_blocks, void* workspace, hipStream_t s,
+                       const DecodeAppend* app = nullptr) {
   uint64_t* mask = active_blocks ? active_blocks : reinterpret_cast<uint64_t*>(at(workspace, w.mask));
   float* logp = reinterpret_cast<float*>(at(workspace, w.logp));
   dash::RouteParams rp;
+  const bool fuse = app && g.bf16 && !estimate_diagonal;
+  if (app && !fuse)
+    DASH_HIP(dash::launch_cache_append(g, app->k_new, app->v_new, seqlens, qbar, app->k_cache,
+                                       app->v_cache, app->kbar_cache, s));
+  if (fuse) {
+    rp.app_knew = app->k_new;
+    rp.app_vnew = app->v_new;
+    rp.app_qbar = qbar;
+    rp.app_kc = app->k_cache;
+    rp.app_vc = app->v_cache;
+    rp.app_kbar = app->kbar_cache;
+  }
   if (estimate_diagonal) {
     void* kdiag = at(workspace, w.kdiag);
     DASH_HIP(dash::launch_decode_diag(g, k_cache, seqlens, qbar, kdiag, s));
@@ -625,6 +650,35 @@ dash_status dash_attn_decode(const dash_shape* shape, const void* q, const void*
   return decode_run(g, w, q, k_cache, v_cache, seqlens, kbar_cache, qbar, alpha, gamma, sigma,
                     softmax_scale, estimate_diagonal, out, lse, active_blocks, workspace,
                     static_cast<hipStream_t>(stream));
+}
+
+dash_status dash_attn_decode_append(const dash_shape* shape, const void* q, const void* k_new,
+                                    const void* v_new, void* k_cache, void* v_cache,
+                                    const int32_t* seqlens, void* kbar_cache, const float* qbar,
+                                    float alpha, float gamma, float sigma, float softmax_scale,
+                                    int enable_gqa, int estimate_diagonal, void* out, float* lse,
+                                    uint64_t* active_blocks, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  Geom g;
+  dash_status st = decode_check(shape, q, k_cache, v_cache, seqlens, kbar_cache, qbar, alpha,
+                                gamma, sigma, softmax_scale, enable_gqa, estimate_diagonal, out,
+                                g);
+  if (st != DASH_OK) return st;
+  if (g.num_seqs > 0 &&
+      (!k_new || !v_new || !qbar || !aligned16(k_new) || !aligned16(v_new)))
+    return DASH_ERR_INVALID_ARGUMENT;
+  const DecodeWs w = decode_ws(g);
+  if ((st = check_ws(workspace, workspace_bytes, w.total)) != DASH_OK) return st;
+  if (g.num_seqs == 0) return DASH_OK;
+  DecodeAppend app;
+  app.k_new = k_new;
+  app.v_new = v_new;
+  app.k_cache = k_cache;
+  app.v_cache = v_cache;
+  app.kbar_cache = kbar_cache;
+  return decode_run(g, w, q, k_cache, v_cache, seqlens, kbar_cache, qbar, alpha, gamma, sigma,
+                    softmax_scale, estimate_diagonal, out, lse, active_blocks, workspace,
+                    static_cast<hipStream_t>(stream), &app);
 }
 
 dash_status dash_attn_decode_noalloc(const dash_shape* shape, const void* q,

@@ -76,6 +76,16 @@ struct RouteParams {
   const void* kdiag = nullptr;          // [rows, Hkv, D] estimated own-chunk summaries, or null:
                                         // one more entmax entry per row (after the routed chunks)
   int64_t row0 = 0;                     // first row of the launch (prefill row ranges)
+  // decode, bf16, no own-chunk estimates: the append of the step's new tokens
+  // (append_token), run by one more column of the logits pass's workgroups,
+  // or null.  The logits never read what it writes: a query routes only the
+  // chunks before its own, and the append completes at most the query's own.
+  const void* app_knew = nullptr;       // [rows, Hkv, D]
+  const void* app_vnew = nullptr;
+  const float* app_qbar = nullptr;      // [Hkv, D]
+  void* app_kc = nullptr;               // caches [rows, cap, Hkv, D] (written)
+  void* app_vc = nullptr;
+  void* app_kbar = nullptr;             // [rows, cap / B, Hkv, D] (written)
 };
 hipError_t launch_route(const Geom& g, const RouteParams& p, hipStream_t st);
 // Streaming routing of prefill rows (route_rows.hip) where it applies (bf16,

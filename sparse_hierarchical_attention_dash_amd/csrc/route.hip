@@ -28,6 +28,7 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "chunk_summary.h"
 #include "dash_device.h"
 #include "dash_internal.h"
 
@@ -663,12 +664,21 @@ __global__ __launch_bounds__(256) void route_fallback_kernel(Geom g, RouteParams
 // fp32 accumulate), one tile per wave and 64 chunks per workgroup, so that the
 // summary reads spread over the whole chip instead of one CU per row.  Written
 // to the scratch [rows, Hkv, G, C_slots] that the solve and weight passes read.
+// With p.app_knew, one more workgroup per (row, KV head), the last of its grid
+// row, appends the row's new token to the caches (append_token), fused into
+// the step.
 template <int D>
 __global__ __launch_bounds__(256) void route_logits_kernel(Geom g, RouteParams p) {
   constexpr int KS = D / 32;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = lane & 15, gq = lane >> 4;
   const int row = blockIdx.y, h = blockIdx.z;
+  if (p.app_knew && blockIdx.x == gridDim.x - 1) {  // the fused append's column
+    if (tid < kWave)
+      append_token<true, D>(g, p.app_knew, p.app_vnew, p.seqlens, p.app_qbar, p.app_kc,
+                            p.app_vc, p.app_kbar, row, h);
+    return;
+  }
   const int n = (p.seqlens[row] - 1) / g.B;
   // entries: the routed chunks, then the row's own-chunk estimate when given
   const int ns = (p.kdiag && n > 0) ? n + 1 : n;
@@ -897,7 +907,7 @@ hipError_t launch_route(const Geom& g, const RouteParams& p, hipStream_t st) {
   const bool wide = p.seqlens != nullptr;
   if (wide && g.bf16 && p.ulog != nullptr && p.tsx != nullptr &&
       (p.topk <= 0 || p.score != nullptr)) {
-    dim3 lgrid((unsigned)((g.C_slots + 63) / 64), (unsigned)p.rows, g.Hkv);
+    dim3 lgrid((unsigned)((g.C_slots + 63) / 64 + (p.app_knew ? 1 : 0)), (unsigned)p.rows, g.Hkv);
     if (g.D == 64) hipLaunchKernelGGL(route_logits_kernel<64>, lgrid, dim3(256), 0, st, g, p);
     else hipLaunchKernelGGL(route_logits_kernel<128>, lgrid, dim3(256), 0, st, g, p);
     dim3 sgrid(g.G, (unsigned)p.rows, g.Hkv);

@@ -348,6 +348,38 @@ def attn_decode(q, k_cache, v_cache, seqlens, kbar_cache, chunk_size, *, alpha=1
     return out, lse, ab
 
 
+def attn_decode_append(q, k_new, v_new, k_cache, v_cache, seqlens, kbar_cache, qbar,
+                       chunk_size, *, alpha=1.5, gamma=1.0, sigma=1.0, softmax_scale=0.0,
+                       enable_gqa=True, return_lse=False, return_active_blocks=False,
+                       workspace=None, out=None, estimate_diagonal=False):
+    """dash_attn_decode_append: cache_append and attn_decode as one fused step.
+    Writes the new tokens' K/V rows (k_new, v_new [batch, Hkv, D]) at position
+    seqlens[b]-1 of the caches and the summary of each chunk they complete
+    into kbar_cache, then decodes q over the updated caches."""
+    qb = qbar if qbar.dtype == torch.float32 else qbar.float().contiguous()
+    _need_cuda(q, k_new, v_new, k_cache, v_cache, seqlens, kbar_cache, qb)
+    batch, Hq, D = q.shape
+    Hkv = k_cache.shape[2]
+    shape = decode_shape(q, k_cache, chunk_size)
+    lay = L.layout(L.make_shape(batch, k_cache.shape[1], batch * k_cache.shape[1], None, Hq,
+                                Hkv, D, chunk_size, _dtype_code(q)), enable_gqa)
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty((Hq, batch), dtype=torch.float32, device=dev) if return_lse else None
+    ab = (torch.empty((Hkv, batch, lay.mask_words), dtype=torch.int64, device=dev)
+          if return_active_blocks else None)
+    n = L.workspace_size(L.DASH_OP_DECODE, shape)
+    if workspace is None or workspace.numel() < n:
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    L.check("dash_attn_decode_append", L.lib().dash_attn_decode_append(
+        ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+        _ptr(seqlens), _ptr(kbar_cache), _ptr(qb), float(alpha), float(gamma), float(sigma),
+        float(softmax_scale), int(enable_gqa), int(estimate_diagonal), _ptr(out), _ptr(lse),
+        _ptr(ab), _ptr(workspace), n, _stream(dev)))
+    return out, lse, ab
+
+
 def attn_decode_noalloc(q, k_cache, v_cache, seqlens, kbar_cache, chunk_size, out, *,
                         alpha=1.5, gamma=1.0, sigma=1.0, softmax_scale=0.0, enable_gqa=True,
                         lse=None, active_blocks=None, estimate_diagonal=False, qbar=None):

@@ -194,6 +194,32 @@ def test_decode_checks(lib):
         L.DASH_ERR_UNSUPPORTED                                        # group > 64
 
 
+def test_decode_append_checks(lib):
+    # the fused append + decode step: the decode checks, plus k_new, v_new and
+    # qbar required and aligned (no compute: every call here is refused)
+    s = L.make_shape(4, 4096, 4, None, 32, 2, 128, 64, BF16)
+    need = L.workspace_size(L.DASH_OP_DECODE, s)
+
+    def dap(sh, **kw):
+        a = dict(q=A, kn=A, vn=A, k=A, v=A, sl=A, kb=A, qb=A, out=A, ws=A, n=need)
+        a.update(kw)
+        return lib.dash_attn_decode_append(ctypes.byref(sh), a["q"], a["kn"], a["vn"], a["k"],
+                                           a["v"], a["sl"], a["kb"], a["qb"], 1.5, 1.0, 1.0,
+                                           0.0, 1, 0, a["out"], None, None, a["ws"], a["n"],
+                                           None)
+
+    assert dap(s, kn=None) == L.DASH_ERR_INVALID_ARGUMENT
+    assert dap(s, vn=None) == L.DASH_ERR_INVALID_ARGUMENT
+    assert dap(s, qb=None) == L.DASH_ERR_INVALID_ARGUMENT
+    assert dap(s, kn=A + 4) == L.DASH_ERR_INVALID_ARGUMENT
+    assert dap(s, sl=None) == L.DASH_ERR_INVALID_ARGUMENT
+    assert dap(s, n=need - 1) == L.DASH_ERR_WORKSPACE_TOO_SMALL
+    assert dap(L.make_shape(4, 4000, 4, None, 32, 2, 128, 64, BF16)) == \
+        L.DASH_ERR_INVALID_ARGUMENT                                   # capacity % B
+    # an empty batch does nothing
+    assert dap(L.make_shape(0, 4096, 0, None, 32, 2, 128, 64, BF16), kn=None) == L.DASH_OK
+
+
 def test_topk_route_checks(lib):
     s = shape()
     need = L.workspace_size(L.DASH_OP_ROUTE, s)

@@ -132,3 +132,64 @@ def test_generation_loop_matches_oracle_decode():
         C = n // B
         ora = O.summarize(kx[b, :C * B], d["qbar"].astype(np.float64), B, to_bf16=True)
         check_summaries(kb[b, :C].to(torch.float64).cpu().numpy(), ora, "bf16", kx[b, :C * B], B)
+
+
+FUSED_CASES = [
+    # name, dtype, batch, cap, Hq, Hkv, D, B, start lengths, steps, estimate_diagonal
+    ("bf16-g16", "bf16", 3, 512, 32, 2, 128, 64, [1, 62, 300], 70, False),
+    ("bf16-g16-diag", "bf16", 2, 512, 32, 2, 128, 64, [60, 200], 40, True),
+    ("bf16-d64-b128-g4", "bf16", 2, 512, 8, 2, 64, 128, [126, 0], 40, False),
+    ("f32-g1", "f32", 2, 256, 2, 2, 64, 64, [62, 5], 20, False),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: c[0])
+def test_fused_append_step_equals_append_then_decode(case):
+    # dash_attn_decode_append against dash_cache_append + dash_attn_decode on
+    # twin caches: outputs, LSE, masks and all three caches bit for bit, over
+    # steps that complete chunks (the fused path for bf16 without estimates,
+    # the separate launch otherwise)
+    name, dtype, batch, cap, Hq, Hkv, D, B, start, steps, diag = case
+    flush(f"fused append step {name}")
+    rng = np.random.default_rng(53)
+    seq_k = rng.standard_normal((batch, cap, Hkv, D)).astype(np.float32)
+    seq_v = rng.standard_normal((batch, cap, Hkv, D)).astype(np.float32)
+    qs = rng.standard_normal((steps, batch, Hq, D)).astype(np.float32)
+    qbar = (0.1 * rng.standard_normal((Hkv, D))).astype(np.float32)
+    kdev, _ = to_dev(seq_k, dtype)
+    vdev, _ = to_dev(seq_v, dtype)
+    qdev, _ = to_dev(qs, dtype)
+    qb = torch.from_numpy(qbar).cuda()
+    kc = torch.full((batch, cap, Hkv, D), SENTINEL, dtype=_dt(dtype), device="cuda")
+    vc = torch.full_like(kc, SENTINEL)
+    kb = torch.full((batch, cap // B, Hkv, D), SENTINEL, dtype=_dt(dtype), device="cuda")
+    for b in range(batch):
+        n0 = start[b]
+        kc[b, :n0] = kdev[b, :n0]
+        vc[b, :n0] = vdev[b, :n0]
+        if n0 >= B:
+            kb[b, :n0 // B] = ops.summarize(kc[b, :n0 // B * B].contiguous(), qb, B)
+    kc2, vc2, kb2 = kc.clone(), vc.clone(), kb.clone()
+    ws = ops.decode_workspace(qdev[0], kc, B)
+    ws2 = ops.decode_workspace(qdev[0], kc, B)
+    ar = torch.arange(batch, device="cuda")
+    kw = dict(alpha=1.5, gamma=8.0, sigma=1.0, return_lse=True, return_active_blocks=True,
+              estimate_diagonal=diag)
+    completed = 0
+    for t in range(steps):
+        L = [start[b] + t + 1 for b in range(batch)]
+        completed += sum(1 for x in L if x % B == 0)
+        sl = torch.tensor(L, dtype=torch.int32, device="cuda")
+        idx = torch.tensor([x - 1 for x in L], device="cuda")
+        kn, vn = kdev[ar, idx].contiguous(), vdev[ar, idx].contiguous()
+        ops.cache_append(kn, vn, sl, qb, kc, vc, kb, B)
+        o1, l1, a1 = ops.attn_decode(qdev[t], kc, vc, sl, kb, B, workspace=ws, qbar=qb, **kw)
+        o2, l2, a2 = ops.attn_decode_append(qdev[t], kn, vn, kc2, vc2, sl, kb2, qb, B,
+                                            workspace=ws2, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2), (t, "out")
+        assert torch.equal(l1, l2), (t, "lse")
+        assert torch.equal(a1, a2), (t, "active_blocks")
+    assert completed > 0
+    assert torch.equal(kc, kc2) and torch.equal(vc, vc2) and torch.equal(kb, kb2)
+    flush(f"  {name}: {steps} steps, {completed} chunks completed, bit-exact")
