@@ -10,18 +10,17 @@
 //   the rows that have j's chunk active (bias b = log_prior) and the rows of
 //   j's own chunk at or after j (bias 0).
 //
-// bwd_headt_kernel: Q and dO copied per (token, KV head) as contiguous blocks
-// of their transposes (units of two dims x four heads).
 // bwd_dkdv_kernel: one workgroup of 4 waves per (64-key block, slice of 4096
 // rows, sequence, KV head); wave w owns keys 16w .. 16w+15 of the block and
 // holds their K and V rows as MFMA operands for the whole kernel.  It scans
 // its slice's mask words 1024 rows at a time, compacts the rows that see the
 // block (ballots and a block-wide prefix, in row order), and streams those
-// rows through a ring of LDS stages filled by direct global->LDS loads (q_i
-// and dO_i XOR-swizzled, their transposes in the unit order of
-// bwd_headt_kernel, so that the operand reads below are free of bank
-// conflicts; the row's LSE, D and bias beside them), several rows ahead of
-// the one computed:
+// rows' q_i and dO_i through a ring of LDS stages filled by direct
+// global->LDS loads (16-byte pieces XOR-swizzled per head, so that the
+// operand reads below are free of bank conflicts; the row's LSE, D and bias
+// beside them), several rows ahead of the one computed.  The transposed
+// operands of the dV and dK products come from the same staged rows by
+// gfx950's transposing LDS reads, so each row crosses the fabric once:
 //   S  = Q_i K_w^T and dP = dO_i V_w^T   (16 heads x 16 keys, 16x16x32 MFMA;
 //                                         the accumulators of S are exactly
 //                                         the operand layout P needs below)
@@ -68,40 +67,6 @@ __global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ x, int64_
 constexpr int kDkdvSlice = 4096;  // rows per workgroup of bwd_dkdv_kernel
 constexpr int kDkdvTiles = 1;     // 16-key tiles per wave of bwd_dkdv_kernel (2: slower)
 
-// The transposed copy of one (token, KV head): 16-byte units of two adjacent
-// dims x four heads, unit (quad, pair) at (quad D/2 + pair) 16 bytes,
-//   xt[(h T + t) G D + 8 (quad D/2 + pair) + 4 parity + jj]
-//     = x[t, h G + 4 quad + jj, 2 pair + parity],
-// so that the 16 lanes of an MFMA operand read (16 consecutive dims, one
-// head quad, 8 bytes each) cover one contiguous 128 bytes of LDS.
-template <int D, int G>
-__global__ __launch_bounds__(256) void bwd_headt_kernel(Geom g, const uint16_t* __restrict__ x,
-                                                        uint16_t* __restrict__ xt) {
-  constexpr int ROW = D + 8;
-  constexpr int NU = G * D / 8;  // 16-byte units
-  __shared__ __align__(16) uint16_t tile[G * ROW];
-  const int64_t tok = blockIdx.x;
-  const int h = blockIdx.y, tid = threadIdx.x;
-  for (int u = tid; u < NU; u += 256) {
-    const int j = u / (D / 8), d0 = (u % (D / 8)) * 8;
-    *reinterpret_cast<u32x4*>(&tile[j * ROW + d0]) =
-        ldg16(x + (tok * g.Hq + h * G + j) * (int64_t)D + d0);
-  }
-  __syncthreads();
-  uint16_t* dst = xt + ((int64_t)h * g.T + tok) * (D * G);
-  for (int u = tid; u < NU; u += 256) {
-    const int quad = u / (D / 2), pair = u % (D / 2);
-    u32x4 o;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int par = w >> 1, jj = 2 * (w & 1);
-      const int d = 2 * pair + par, j = 4 * quad + jj;
-      o[w] = (uint32_t)tile[j * ROW + d] | ((uint32_t)tile[(j + 1) * ROW + d] << 16);
-    }
-    *reinterpret_cast<u32x4*>(dst + 8 * u) = o;
-  }
-}
-
 template <int D, int HT, int KT>
 struct DkdvCfg {
   static constexpr int NW = 4 / KT;                    // waves: KT 16-key tiles each
@@ -109,12 +74,23 @@ struct DkdvCfg {
   static constexpr int G = 16 * HT;
   static constexpr int NS = HT == 1 ? 4 : 3;           // ring stages, one row each
   static constexpr int ABYTES = G * D * 2;             // one array of one row
-  static constexpr int SBYTES = 4 * ABYTES;            // Q, dO, Q^T, dO^T
+  static constexpr int SBYTES = 2 * ABYTES;            // Q, dO
   static constexpr int AU = ABYTES / 16;               // 16-byte units per array
-  static constexpr int NUT = 4 * AU / NTH;             // unit loads per thread per stage
+  static constexpr int NUT = 2 * AU / NTH;             // unit loads per thread per stage
   static constexpr int PER = NUT + 2;                  // loads per wave per stage
-  static_assert(4 * AU % NTH == 0, "units per stage");
+  static_assert(2 * AU % NTH == 0, "units per stage");
 };
+
+// Slot of 16-byte piece pc of head j's row in the staged Q and dO: pc ^ f(j),
+// with f giving the heads that share the 64 banks (one 256-byte row at
+// D = 128, two 128-byte rows at D = 64) distinct even offsets.  Then eight
+// heads' 16-byte reads of one piece (the S and dP operands) and four heads'
+// 8-byte transposing reads of two adjacent pieces (the dV and dK operands)
+// each touch every bank at most once.
+template <int D>
+__device__ __forceinline__ int dkdv_swz(int j) {
+  return D == 128 ? (2 * j) & 15 : j & 6;
+}
 
 template <int D, int HT, int KT>
 __global__ __launch_bounds__(256 / KT) void bwd_dkdv_kernel(Geom g, BwdParams p, float* dk,
@@ -179,8 +155,6 @@ __global__ __launch_bounds__(256 / KT) void bwd_dkdv_kernel(Geom g, BwdParams p,
   const float sl2 = p.scale * kLog2e;
   const uint16_t* qg = (const uint16_t*)p.q;
   const uint16_t* dg = (const uint16_t*)p.dout;
-  const uint16_t* qtg = (const uint16_t*)p.qt;
-  const uint16_t* dtg = (const uint16_t*)p.dot;
 
   // one row into ring slot `slot`: thread tid loads units tid + 256 e
   auto issue = [&](int row, int slot) {
@@ -190,15 +164,9 @@ __global__ __launch_bounds__(256 / KT) void bwd_dkdv_kernel(Geom g, BwdParams p,
     for (int e = 0; e < C::NUT; ++e) {
       const int U = tid + NTH * e;
       const int arr = U / C::AU, u = U % C::AU;
-      const uint16_t* src;
-      if (arr < 2) {
-        // row-major: head j, 16-byte piece (u % UPH) ^ (j % UPH)
-        const int j = u / UPH, pc = (u % UPH) ^ (j % UPH);
-        src = (arr == 0 ? qg : dg) + (tok * g.Hq + h * G + j) * (int64_t)D + 8 * pc;
-      } else {
-        // transposed: the units in their order (see bwd_headt_kernel)
-        src = (arr == 2 ? qtg : dtg) + ((int64_t)h * T + tok) * (D * G) + 8 * u;
-      }
+      // row-major: slot u % UPH of head j holds the piece dkdv_swz places there
+      const int j = u / UPH, pc = (u % UPH) ^ dkdv_swz<D>(j);
+      const uint16_t* src = (arr == 0 ? qg : dg) + (tok * g.Hq + h * G + j) * (int64_t)D + 8 * pc;
       lds_dma16(src, __builtin_amdgcn_readfirstlane(base + (uint32_t)(16 * (NTH * e + 64 * wv))));
     }
     if (lane < 2 * G) {
@@ -215,8 +183,6 @@ __global__ __launch_bounds__(256 / KT) void bwd_dkdv_kernel(Geom g, BwdParams p,
     const uint8_t* st = Ring + slot * C::SBYTES;
     lds_u8* Qs = (lds_u8*)(st);
     lds_u8* Ds = (lds_u8*)(st + C::ABYTES);
-    lds_u8* Qt = (lds_u8*)(st + 2 * C::ABYTES);
-    lds_u8* Dt = (lds_u8*)(st + 3 * C::ABYTES);
     const bool own = row < cend;  // the block's own chunk: keys after the row are unseen
     const float bz = own ? 0.f : Bz[slot][wv][0] * kLog2e;
 #pragma unroll
@@ -231,7 +197,7 @@ __global__ __launch_bounds__(256 / KT) void bwd_dkdv_kernel(Geom g, BwdParams p,
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         // one read of the row's Q and dO fragments serves the wave's KT key tiles
-        const int off = 16 * (j * UPH + ((4 * ks + gq) ^ (j % UPH)));
+        const int off = 16 * (j * UPH + ((4 * ks + gq) ^ dkdv_swz<D>(j)));
         const bf16x8 qf = as_bf16x8(lds_read16(Qs + off)), df = as_bf16x8(lds_read16(Ds + off));
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
@@ -256,19 +222,21 @@ __global__ __launch_bounds__(256 / KT) void bwd_dkdv_kernel(Geom g, BwdParams p,
         pb[kt] = u32x2{cvt_pk_bf16(pv[0], pv[1]), cvt_pk_bf16(pv[2], pv[3])};
         sb[kt] = u32x2{cvt_pk_bf16(ds[0], ds[1]), cvt_pk_bf16(ds[2], ds[3])};
       }
-      const int quad = 4 * ht + gq;
+      // transposing reads: lane (gq, r) points at head 16 ht + 4 gq + r / 4,
+      // dims 16 dt + 4 (r % 4) .. +3, and receives dim 16 dt + r of heads
+      // 16 ht + 4 gq .. +3 (the A operand of X^T)
+      const int jt = 16 * ht + 4 * gq + (r >> 2);
+      const int tbase = 16 * jt * UPH + 8 * (r & 1);
+      const int tsw = dkdv_swz<D>(jt), tpc = (r & 3) >> 1;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        // A = X^T tile: dims 16 dt + r, heads 16 ht + 4 gq .. +3 (one read for
-        // the KT key tiles)
-        const int off = 16 * (quad * (D / 2) + 8 * dt + (r >> 1)) + 8 * (r & 1);
-        typedef const __attribute__((address_space(3))) u32x2 lds_u32x2;
-        const u32x2 ta = *reinterpret_cast<lds_u32x2*>(Dt + off);
-        const u32x2 tq = *reinterpret_cast<lds_u32x2*>(Qt + off);
+        const int off = tbase + 16 * ((2 * dt + tpc) ^ tsw);
+        const s16x4 ta = lds_read_tr8(Ds + off);
+        const s16x4 tq = lds_read_tr8(Qs + off);
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
-          adv[kt][dt] = mfma16x16x16(as_s16x4(ta), as_s16x4(pb[kt]), adv[kt][dt]);
-          adk[kt][dt] = mfma16x16x16(as_s16x4(tq), as_s16x4(sb[kt]), adk[kt][dt]);
+          adv[kt][dt] = mfma16x16x16(ta, as_s16x4(pb[kt]), adv[kt][dt]);
+          adk[kt][dt] = mfma16x16x16(tq, as_s16x4(sb[kt]), adk[kt][dt]);
         }
       }
     }
@@ -362,20 +330,6 @@ hipError_t launch_bwd_delta(const Geom& g, const void* out, const void* dout, fl
   else
     hipLaunchKernelGGL(bwd_delta_kernel<128>, grid, dim3(256), 0, st, g, (const uint16_t*)out,
                        (const uint16_t*)dout, delta);
-  return hipGetLastError();
-}
-
-hipError_t launch_bwd_headt(const Geom& g, const void* x, void* xt, hipStream_t st) {
-  if (g.T == 0) return hipSuccess;
-  dim3 grid((unsigned)g.T, g.Hkv);
-#define DASH_HT(DD, GG) \
-  hipLaunchKernelGGL((bwd_headt_kernel<DD, GG>), grid, dim3(256), 0, st, g, (const uint16_t*)x, (uint16_t*)xt)
-  if (g.G == 16) {
-    if (g.D == 64) DASH_HT(64, 16); else DASH_HT(128, 16);
-  } else {
-    if (g.D == 64) DASH_HT(64, 32); else DASH_HT(128, 32);
-  }
-#undef DASH_HT
   return hipGetLastError();
 }
 

@@ -199,7 +199,7 @@ RouteDecodeWs route_decode_ws(const Geom& g) {
 }
 // Backward of phase 2: K^T, D = <dO, O>, and fp32 dQ / dK / dV.
 struct BackwardWs {
-  size_t meta, kt, delta, dq, dk, dv, qt, dot, total;
+  size_t meta, kt, delta, dq, dk, dv, total;
 };
 BackwardWs backward_ws(const Geom& g) {
   BackwardWs w{};
@@ -216,10 +216,6 @@ BackwardWs backward_ws(const Geom& g) {
   o += align_up((size_t)g.T * g.Hkv * g.D * 4);
   w.dv = o;
   o += align_up((size_t)g.T * g.Hkv * g.D * 4);
-  w.qt = o;
-  o += align_up((size_t)g.T * g.Hq * g.D * 2);
-  w.dot = o;
-  o += align_up((size_t)g.T * g.Hq * g.D * 2);
   w.total = o;
   return w;
 }
@@ -852,10 +848,6 @@ dash_status dash_attn_sparse_backward(const dash_shape* shape, const void* q, co
   DASH_HIP(dash::launch_bwd_delta(g, out, dout, reinterpret_cast<float*>(at(workspace, w.delta)), s));
   DASH_HIP(dash::launch_zero(dbias, (int64_t)g.Hkv * g.T * g.C_slots, s));
   DASH_HIP(dash::launch_bwd_dq(g, p, s));
-  DASH_HIP(dash::launch_bwd_headt(g, q, at(workspace, w.qt), s));
-  DASH_HIP(dash::launch_bwd_headt(g, dout, at(workspace, w.dot), s));
-  p.qt = at(workspace, w.qt);
-  p.dot = at(workspace, w.dot);
   DASH_HIP(dash::launch_bwd_dkdv(g, p, dkw, dvw, s));
   DASH_HIP(dash::launch_to_bf16(p.dq, dq, g.T * g.Hq * g.D, s));
   DASH_HIP(dash::launch_to_bf16(dkw, dk, g.T * g.Hkv * g.D, s));
@@ -938,10 +930,6 @@ dash_status dash_attn_prefill_backward(const dash_shape* shape, const void* q, c
   DASH_HIP(dash::launch_bwd_delta(g, out, dout, reinterpret_cast<float*>(at(workspace, w.a.delta)), s));
   DASH_HIP(dash::launch_zero(p.dbias, (int64_t)g.Hkv * g.T * g.C_slots, s));
   DASH_HIP(dash::launch_bwd_dq(g, p, s));
-  DASH_HIP(dash::launch_bwd_headt(g, q, at(workspace, w.a.qt), s));
-  DASH_HIP(dash::launch_bwd_headt(g, dout, at(workspace, w.a.dot), s));
-  p.qt = at(workspace, w.a.qt);
-  p.dot = at(workspace, w.a.dot);
   DASH_HIP(dash::launch_bwd_dkdv(g, p, dkw, dvw, s));
   // phases 1 and 0
   dash::RouteBwdParams rb;

@@ -257,6 +257,17 @@ __device__ __forceinline__ u32x4 lds_read16(lds_u8* p) {
   return *reinterpret_cast<lds_u32x4*>(p);
 }
 
+// Transposing LDS read of 16-bit elements, 8 bytes a lane (gfx950): within
+// each group of 16 lanes, lane i receives as its element j element i % 4 of
+// the 8 bytes that lane 4 j + i / 4 of the group points at.  With lane a
+// pointing at 4 consecutive columns 4 (a % 4) .. +3 of row a / 4 of a
+// row-major tile, lane i thus receives column i of rows 0..3: the operand
+// layout of a 16x16x16 MFMA for the tile's transpose.
+__device__ __forceinline__ s16x4 lds_read_tr8(lds_u8* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+}
+
 // s_waitcnt for at most N outstanding vector-memory operations (N < 64) and
 // no outstanding LDS operation
 template <int N>

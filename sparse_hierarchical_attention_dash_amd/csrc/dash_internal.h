@@ -138,8 +138,6 @@ struct BwdParams {
   const void* kt = nullptr;             // K^T workspace [Hkv, D, Tp] (the V^T layout)
   int64_t Tp = 0;
   const void* dout = nullptr;           // [T, Hq, D]
-  const void* qt = nullptr;             // Q and dO with the group's heads innermost:
-  const void* dot = nullptr;            //   [Hkv, T, D, G] (launch_bwd_headt)
   const float* lse = nullptr;           // [Hq, T] natural log, from the forward
   const float* delta = nullptr;         // [Hq, T] <dO, O>
   const uint64_t* mask = nullptr;       // [Hkv, T, W]
@@ -151,7 +149,6 @@ struct BwdParams {
 hipError_t launch_bwd_dq(const Geom& g, const BwdParams& p, hipStream_t st);
 hipError_t launch_bwd_delta(const Geom& g, const void* out, const void* dout, float* delta,
                             hipStream_t st);
-hipError_t launch_bwd_headt(const Geom& g, const void* x, void* xt, hipStream_t st);
 hipError_t launch_bwd_dkdv(const Geom& g, const BwdParams& p, float* dk, float* dv,
                            hipStream_t st);
 hipError_t launch_to_bf16(const float* src, void* dst, int64_t n, hipStream_t st);
