@@ -548,6 +548,160 @@ __device__ __forceinline__ void visit_ring(lds_u8* ks_, lds_u8* vt_,
   }
 }
 
+// The ordered list of the union of a workgroup's positions' active chunks
+// (Blist), for each listed chunk the positions that have it active (Act, bit
+// t: the workgroup's position t), and with 64-key chunks the visiting order
+// (the list permuted in place); returns the list's length.  mbase: the mask
+// row of the workgroup's first position (W words a row), npos positions,
+// cdiag the positions' own chunk (not routable); HT tiles per position.
+// Every thread of the workgroup calls it.
+template <int NWV, int TW, typename ActT>
+__device__ __forceinline__ int ring_build_list(int W, int HT, bool b128,
+                                               const unsigned long long* __restrict__ mbase,
+                                               int npos, int cdiag, unsigned long long* Umask,
+                                               int* Wpref, uint16_t* Blist, ActT* Act,
+                                               uint16_t* Ord) {
+  constexpr int NTH = 64 * NWV;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (tid < 32) Umask[tid] = 0ull;
+  __syncthreads();
+  for (int idx = tid; idx < npos * W; idx += NTH) {
+    const int w = idx % W;
+    const unsigned long long v = mbase[idx] & routable_bits(w, cdiag);
+    if (v) atomicOr(&Umask[w], v);
+  }
+  __syncthreads();
+  if (tid < 64) {
+    int cnt = (tid < W) ? __popcll(Umask[tid]) : 0;
+    int inc = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o);
+      if (lane >= o) inc += y;
+    }
+    if (tid < 33) Wpref[tid] = inc - cnt;
+  }
+  __syncthreads();
+  if (tid < W) {
+    unsigned long long v = Umask[tid];
+    int o = Wpref[tid];
+    while (v) {
+      Blist[o++] = (uint16_t)(tid * 64 + __ffsll(v) - 1);
+      v &= v - 1;
+    }
+  }
+  __syncthreads();
+  const int nlist = Wpref[W];
+  for (int j = tid; j < nlist; j += NTH) {
+    const int c = Blist[j];
+    uint32_t bits = 0;
+    for (int t = 0; t < npos; ++t)
+      bits |= (uint32_t)((mbase[t * W + (c >> 6)] >> (c & 63)) & 1ull) << t;
+    Act[j] = (ActT)bits;
+  }
+  __syncthreads();
+
+  // visiting order (64-key chunks).  The loop below takes two listed
+  // chunks per barrier, so the wait at a barrier is for the busiest wave over
+  // both; they are paired so that their active tiles fall on different
+  // waves.  Wave w pairs the entries of list blocks w, w + NWV, ... (64
+  // entries each) greedily: the first unpaired entry i of the block takes
+  // the first unpaired entry after it that keeps the pair's load lowest.
+  // With two tiles a wave: every wave at one visit, else at two, else any
+  // (v packs per wave, 4 bits each, the tile visits of an entry; a sum of two
+  // never carries between the fields).  With one tile a wave: the busiest
+  // SIMD's visits, then whether some wave visits twice (16 waves x 1 tile:
+  // 64K attention 15.1 -> 14.9 ms against the wave rule alone).
+  if (!b128 && nlist > 2) {
+    for (int b = wv; b * 64 < nlist; b += NWV) {
+      const int e = b * 64 + lane;
+      uint32_t v = 0;
+      if (e < nlist) {
+        const uint32_t act = Act[e];
+        if constexpr (TW == 1) {
+          // one tile a wave: a bit per wave
+#pragma unroll
+          for (int w = 0; w < NWV; ++w) v |= ((act >> (w / HT)) & 1u) << w;
+        } else {
+#pragma unroll
+          for (int w = 0; w < NWV; ++w) {
+            uint32_t c = 0;
+#pragma unroll
+            for (int u = 0; u < TW; ++u) c += (act >> ((TW * w + u) / HT)) & 1u;
+            v |= c << (4 * w);
+          }
+        }
+      }
+      uint64_t taken = ~__ballot(e < nlist);
+      // one tile a wave: the visits per SIMD too (4 bits each), taking wave w
+      // to run on SIMD w % 4 (waves are placed on the four SIMDs in turn)
+      uint32_t sl = 0;
+      if constexpr (TW == 1) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sl |= (uint32_t)__popc(v & (0x1111u << q)) << (4 * q);
+      }
+      int out = b * 64;
+      while (~taken) {
+        const int i = __ffsll((long long)~taken) - 1;
+        taken |= 1ull << i;
+        const uint32_t vi = (uint32_t)__builtin_amdgcn_readlane((int)v, i);
+        const uint32_t t = vi + v;
+        int j = -1;
+        if constexpr (TW == 1) {
+          // the partner keeping the busiest SIMD lowest, then no wave twice
+          const uint32_t ts = (uint32_t)__builtin_amdgcn_readlane((int)sl, i) + sl;
+          const uint32_t mx = max(max(ts & 15u, (ts >> 4) & 15u), max((ts >> 8) & 15u, ts >> 12));
+          int k = ((taken >> lane) & 1ull) ? 64 : (int)(2 * mx + ((vi & v) ? 1u : 0u));
+          int km = k;
+#pragma unroll
+          for (int o = 1; o < 64; o <<= 1) km = min(km, __shfl_xor(km, o));
+          if (km < 64) j = __ffsll((long long)__ballot(k == km)) - 1;
+        } else {
+        // 1: no wave visits twice, 2: at most twice, 3: more; 4: taken
+        const bool ge2 = TW == 1 ? (vi & v) != 0u : ((t + 0x66666666u) & 0x88888888u) != 0u;
+        const bool ge3 = TW == 1 ? false : ((t + 0x55555555u) & 0x88888888u) != 0u;
+        const int k = ((taken >> lane) & 1ull) ? 4 : (ge3 ? 3 : (ge2 ? 2 : 1));
+        for (int cls = 1; cls <= 3 && j < 0; ++cls) {
+          const uint64_t bm = __ballot(k <= cls);
+          if (bm) j = __ffsll((long long)bm) - 1;
+        }
+        }
+        if (lane == 0) {
+          Ord[out] = (uint16_t)(b * 64 + i);
+          if (j >= 0) Ord[out + 1] = (uint16_t)(b * 64 + j);
+        }
+        out += j >= 0 ? 2 : 1;
+        if (j >= 0) taken |= 1ull << j;
+      }
+    }
+    __syncthreads();
+    constexpr int PER = (2048 + NTH - 1) / NTH;
+    uint16_t tb[PER];
+    ActT ta[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int j = tid + q * NTH;
+      if (j < nlist) {
+        const int o = Ord[j];
+        tb[q] = Blist[o];
+        ta[q] = Act[o];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int j = tid + q * NTH;
+      if (j < nlist) {
+        Blist[j] = tb[q];
+        Act[j] = ta[q];
+      }
+    }
+    __syncthreads();
+  }
+  return nlist;
+}
+
 // Prefill attention for G >= 16 (every 16-row tile is 16 query heads of one
 // position).  A workgroup of NWV waves owns NT = NWV * TW tiles, TW per wave,
 // so P = NT / (G / 16) positions (P divides B: the positions share one
@@ -639,145 +793,12 @@ __global__ __launch_bounds__(64 * NWV, 1) void prefill_attn_ring_kernel(
     }
   }
 
-  // ---- ordered list of the union of the positions' active chunks, and for
-  // each listed chunk the positions that have it active
-  if (tid < 32) Umask[tid] = 0ull;
-  __syncthreads();
+  // ---- ordered list of the union of the positions' active chunks, the
+  // positions that have each listed chunk active, and the visiting order
   const unsigned long long* mbase = mask + ((int64_t)h * T + si.start + p0) * W;
-  for (int idx = tid; idx < npos * W; idx += NTH) {
-    const int w = idx % W;
-    const unsigned long long v = mbase[idx] & routable_bits(w, cdiag);
-    if (v) atomicOr(&Umask[w], v);
-  }
-  __syncthreads();
-  if (tid < 64) {
-    int cnt = (tid < W) ? __popcll(Umask[tid]) : 0;
-    int inc = cnt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(inc, o);
-      if (lane >= o) inc += y;
-    }
-    if (tid < 33) Wpref[tid] = inc - cnt;
-  }
-  __syncthreads();
-  if (tid < W) {
-    unsigned long long v = Umask[tid];
-    int o = Wpref[tid];
-    while (v) {
-      Blist[o++] = (uint16_t)(tid * 64 + __ffsll(v) - 1);
-      v &= v - 1;
-    }
-  }
-  __syncthreads();
-  const int nlist = Wpref[W];
-  for (int j = tid; j < nlist; j += NTH) {
-    const int c = Blist[j];
-    uint32_t bits = 0;
-    for (int t = 0; t < npos; ++t)
-      bits |= (uint32_t)((mbase[t * W + (c >> 6)] >> (c & 63)) & 1ull) << t;
-    Act[j] = (ActT)bits;
-  }
-  __syncthreads();
+  const int nlist = ring_build_list<NWV, TW>(W, tg.HT, g.B == 128, mbase, npos, cdiag, Umask,
+                                             Wpref, Blist, Act, Ord);
   const int sbl = g.B == 128 ? 1 : 0;  // log2 of the 64-key blocks per chunk
-
-  // ---- visiting order (64-key chunks).  The loop below takes two listed
-  // chunks per barrier, so the wait at a barrier is for the busiest wave over
-  // both; they are paired so that their active tiles fall on different
-  // waves.  Wave w pairs the entries of list blocks w, w + NWV, ... (64
-  // entries each) greedily: the first unpaired entry i of the block takes
-  // the first unpaired entry after it that keeps the pair's load lowest.
-  // With two tiles a wave: every wave at one visit, else at two, else any
-  // (v packs per wave, 4 bits each, the tile visits of an entry; a sum of two
-  // never carries between the fields).  With one tile a wave: the busiest
-  // SIMD's visits, then whether some wave visits twice (16 waves x 1 tile:
-  // 64K attention 15.1 -> 14.9 ms against the wave rule alone).
-  if (sbl == 0 && nlist > 2) {
-    for (int b = wv; b * 64 < nlist; b += NWV) {
-      const int e = b * 64 + lane;
-      uint32_t v = 0;
-      if (e < nlist) {
-        const uint32_t act = Act[e];
-        if constexpr (TW == 1) {
-          // one tile a wave: a bit per wave
-#pragma unroll
-          for (int w = 0; w < NWV; ++w) v |= ((act >> (w / tg.HT)) & 1u) << w;
-        } else {
-#pragma unroll
-          for (int w = 0; w < NWV; ++w) {
-            uint32_t c = 0;
-#pragma unroll
-            for (int u = 0; u < TW; ++u) c += (act >> ((TW * w + u) / tg.HT)) & 1u;
-            v |= c << (4 * w);
-          }
-        }
-      }
-      uint64_t taken = ~__ballot(e < nlist);
-      // one tile a wave: the visits per SIMD too (4 bits each), taking wave w
-      // to run on SIMD w % 4 (waves are placed on the four SIMDs in turn)
-      uint32_t sl = 0;
-      if constexpr (TW == 1) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) sl |= (uint32_t)__popc(v & (0x1111u << q)) << (4 * q);
-      }
-      int out = b * 64;
-      while (~taken) {
-        const int i = __ffsll((long long)~taken) - 1;
-        taken |= 1ull << i;
-        const uint32_t vi = (uint32_t)__builtin_amdgcn_readlane((int)v, i);
-        const uint32_t t = vi + v;
-        int j = -1;
-        if constexpr (TW == 1) {
-          // the partner keeping the busiest SIMD lowest, then no wave twice
-          const uint32_t ts = (uint32_t)__builtin_amdgcn_readlane((int)sl, i) + sl;
-          const uint32_t mx = max(max(ts & 15u, (ts >> 4) & 15u), max((ts >> 8) & 15u, ts >> 12));
-          int k = ((taken >> lane) & 1ull) ? 64 : (int)(2 * mx + ((vi & v) ? 1u : 0u));
-          int km = k;
-#pragma unroll
-          for (int o = 1; o < 64; o <<= 1) km = min(km, __shfl_xor(km, o));
-          if (km < 64) j = __ffsll((long long)__ballot(k == km)) - 1;
-        } else {
-        // 1: no wave visits twice, 2: at most twice, 3: more; 4: taken
-        const bool ge2 = TW == 1 ? (vi & v) != 0u : ((t + 0x66666666u) & 0x88888888u) != 0u;
-        const bool ge3 = TW == 1 ? false : ((t + 0x55555555u) & 0x88888888u) != 0u;
-        const int k = ((taken >> lane) & 1ull) ? 4 : (ge3 ? 3 : (ge2 ? 2 : 1));
-        for (int cls = 1; cls <= 3 && j < 0; ++cls) {
-          const uint64_t bm = __ballot(k <= cls);
-          if (bm) j = __ffsll((long long)bm) - 1;
-        }
-        }
-        if (lane == 0) {
-          Ord[out] = (uint16_t)(b * 64 + i);
-          if (j >= 0) Ord[out + 1] = (uint16_t)(b * 64 + j);
-        }
-        out += j >= 0 ? 2 : 1;
-        if (j >= 0) taken |= 1ull << j;
-      }
-    }
-    __syncthreads();
-    constexpr int PER = (2048 + NTH - 1) / NTH;
-    uint16_t tb[PER];
-    ActT ta[PER];
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int j = tid + q * NTH;
-      if (j < nlist) {
-        const int o = Ord[j];
-        tb[q] = Blist[o];
-        ta[q] = Act[o];
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int j = tid + q * NTH;
-      if (j < nlist) {
-        Blist[j] = tb[q];
-        Act[j] = ta[q];
-      }
-    }
-    __syncthreads();
-  }
   const int nrouted = nlist << sbl;
   const int ndiag = (pend - cdiag * g.B + 63) / 64;
   const int NS = nrouted + ndiag;
@@ -1008,37 +1029,135 @@ __global__ __launch_bounds__(64 * NWV, 1) void prefill_attn_ring_kernel(
 // Backward of phase 2 for the queries, G >= 16, bf16 (the derivative of the
 // prior-induced softmax attention: dS = P (dP - D), dQ = s dS K, and each
 // routed chunk's bias gradient, the sum of dS over its keys and the group's
-// heads).  The layout of work follows the forward ring kernel: 16 row tiles
-// per workgroup (two per wave) walk the union of their positions' active
-// blocks and the diagonal.  A block's K rows, V rows (both in the K layout)
-// and K^T rows (from the transposed-K workspace, in the V^T layout) are staged
-// in LDS, double-buffered, by plain vector loads.  Visit of an active tile:
-// S^T = K Q^T and dP^T = V dO^T (16 MFMAs each), P^T = exp2(s S^T + b - LSE)
-// from the forward's LSE, dS^T = P^T (dP^T - D) with D = <dO, O>, the tile's
-// bias gradient sum(dS^T) added to dbias, and dQ^T += K^T dS^T (16 MFMAs).
-// dQ (times s) is written in fp32 for the routing backward to add to.
-// Blocks are staged by direct global->LDS loads (the swizzle applied on the
-// source side), one block ahead, with a full vmcnt wait before each barrier.
-constexpr int kBqWaves = 8;
-constexpr int kBqThreads = 64 * kBqWaves;
-constexpr int kBqTiles = 2 * kBqWaves;
+// heads).  The work is laid out as in the forward ring kernel: 16 row tiles
+// per workgroup (one a wave for G = 16, a pair of one position for G = 32)
+// walk the union of their positions' active blocks (ring_build_list, paired
+// for 64-key chunks) and then the diagonal, through the same 4-slot LDS ring
+// and barrier schedule.  A staged block is the block's K rows and V rows,
+// 16-byte pieces XOR-swizzled by dq_swz; K^T, the operand of the dQ product,
+// comes from the K rows by gfx950's transposing LDS reads, so a block crosses
+// the fabric once, as 2 x 64 rows.  Visit of an active tile, 32 keys at a
+// time: S^T = K Q^T and dP^T = V dO^T (16x16x32), P^T = exp2(s S^T + b - LSE)
+// from the forward's LSE, dS^T = P^T (dP^T - D) with D = <dO, O>, dQ^T +=
+// K^T dS^T (16x16x32); a routed block's bias gradient, the tile's sum of dS,
+// is added atomically.  dQ (times s) is written in fp32 for the routing
+// backward to add to.
 
+// Slot of 16-byte piece pc of staged row `row`: pc ^ f(row), with f giving
+// the rows that share the 64 banks distinct even offsets, so that eight
+// consecutive rows' 16-byte reads of one piece (the S^T and dP^T operands)
+// and four consecutive rows' 8-byte transposing reads of two adjacent pieces
+// (the K^T operand) each touch every bank at most once.
 template <int D>
-__global__ __launch_bounds__(kBqThreads, 1) void bwd_dq_kernel(Geom g, BwdParams p, TileGeom tg) {
-  constexpr int NTH = kBqThreads;
-  using R = RingCfg<D>;
+__device__ __forceinline__ int dq_swz(int row) {
+  return D == 128 ? (2 * row) & 15 : row & 6;
+}
+
+// One visit of tiles U0 .. U0+NTL-1 of a wave to one staged block (K rows at
+// ks_, V rows at vs_), in two halves of 32 keys.  koff: the lane's S^T / dP^T
+// operand offsets (row r, piece 4 ks + gq); tb, tx: the transposing reads'
+// row offset and swizzle (below).  Adds each tile's partial sum of dS to
+// dsum.  MASKED: key j of the block is seen iff kbase + j - 4 gq <= the
+// tile's position (kbase = the block's first key + 4 gq).
+template <int D, bool MASKED, int U0, int NTL, int TWN>
+__device__ __forceinline__ void visit_dq(lds_u8* ks_, lds_u8* vs_, const int (&koff)[D / 32],
+                                         int tb, int tx, const bf16x8 (&qa)[TWN][D / 32],
+                                         const bf16x8 (&da)[TWN][D / 32],
+                                         const float (&lse2)[TWN], const float (&dlt)[TWN],
+                                         f32x4 (&o)[TWN][D / 16], float (&dsum)[TWN], float sl2,
+                                         const float (&bz)[TWN], int kbase,
+                                         const int (&rpos)[TWN]) {
+  constexpr int KROW = 2 * D;
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
-  constexpr int KB = R::KBYTES;           // K rows; V rows follow, then K^T rows
-  constexpr int SB = 2 * KB + R::VBYTES;  // bytes of one staged block
-  constexpr int NPC = SB / (16 * NTH);    // 16-byte pieces per thread
-  static_assert(NPC * 16 * NTH == SB, "a block splits into whole pieces");
-  __shared__ __attribute__((aligned(1024))) uint8_t stage[2][SB];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    // S^T and dP^T of keys 32 h2 .. +31 (key tiles t = 0, 1 of the half):
+    // lane (gq, r) holds keys 32 h2 + 16 t + 4 gq + j of head r
+    f32x4 sacc[NTL][2], pacc[NTL][2];
+#pragma unroll
+    for (int u = 0; u < NTL; ++u)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        sacc[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        pacc[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 fk[2], fv[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        fk[t] = lds_read16(ks_ + koff[ks] + (32 * h2 + 16 * t) * KROW);
+        fv[t] = lds_read16(vs_ + koff[ks] + (32 * h2 + 16 * t) * KROW);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int u = 0; u < NTL; ++u) {
+          sacc[u][t] = mfma16x16x32(as_bf16x8(fk[t]), qa[U0 + u][ks], sacc[u][t]);
+          pacc[u][t] = mfma16x16x32(as_bf16x8(fv[t]), da[U0 + u][ks], pacc[u][t]);
+        }
+    }
+    // dS^T, packed as the B operand of dQ^T += K^T dS^T: k-slot 8 gq + 4 t + j
+    // is key 32 h2 + 16 t + 4 gq + j
+    u32x4 pb[NTL];
+#pragma unroll
+    for (int u = 0; u < NTL; ++u) {
+      const float off = bz[U0 + u] - lse2[U0 + u];
+      float ds[2][4];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float pv = __builtin_amdgcn_exp2f(fmaf(sacc[u][t][j], sl2, off));
+          if constexpr (MASKED) pv = kbase + 32 * h2 + 16 * t + j <= rpos[U0 + u] ? pv : 0.f;
+          ds[t][j] = pv * (pacc[u][t][j] - dlt[U0 + u]);
+          dsum[U0 + u] += ds[t][j];
+        }
+      pb[u] = u32x4{cvt_pk_bf16(ds[0][0], ds[0][1]), cvt_pk_bf16(ds[0][2], ds[0][3]),
+                    cvt_pk_bf16(ds[1][0], ds[1][1]), cvt_pk_bf16(ds[1][2], ds[1][3])};
+    }
+    // K^T operand of dims 16 dt .. +15: two transposing reads, of key rows
+    // 32 h2 + 4 gq + r / 4 and the same + 16, give lane (gq, r) dim 16 dt + r
+    // of the keys of its k-slots
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      lds_u8* a = ks_ + tb + 32 * h2 * KROW + 32 * (dt ^ tx);
+      const s16x4 a0 = lds_read_tr8(a), a1 = lds_read_tr8(a + 16 * KROW);
+      const bf16x8 ka = __builtin_bit_cast(
+          bf16x8, u32x4{__builtin_bit_cast(u32x2, a0)[0], __builtin_bit_cast(u32x2, a0)[1],
+                        __builtin_bit_cast(u32x2, a1)[0], __builtin_bit_cast(u32x2, a1)[1]});
+#pragma unroll
+      for (int u = 0; u < NTL; ++u)
+        o[U0 + u][dt] = mfma16x16x32(ka, as_bf16x8(pb[u]), o[U0 + u][dt]);
+    }
+  }
+}
+
+template <int D, int NWV, int TW, bool PAIR>
+__global__ __launch_bounds__(64 * NWV, 1) void bwd_dq_ring_kernel(Geom g, BwdParams p,
+                                                                  TileGeom tg) {
+  constexpr int NTH = 64 * NWV;
+  constexpr int NT = NWV * TW;
+  constexpr int KROW = 2 * D;
+  constexpr int KBYTES = 64 * KROW;
+  constexpr int STAGE = 2 * KBYTES;       // K rows, then V rows
+  constexpr int NP = STAGE / (16 * NTH);  // 16-byte loads per thread per block
+  constexpr int LPS = NP + 1;             // + the tiles' bias words
+  constexpr int KS = D / 32;
+  constexpr int DT = D / 16;
+  static_assert(NP * 16 * NTH == STAGE, "a block splits into whole loads");
+  static_assert(KBYTES % (NP * 1024) == 0, "a wave's pieces lie all in K or all in V");
+  static_assert(NT <= 16, "one 16-bit activity word per listed chunk");
+  static_assert(!PAIR || TW == 2, "pairs of tiles");
+  static_assert(TW == 1 ? NWV <= 32 : NWV <= 8, "per-wave visit counts packed in 32 bits");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kRing][STAGE];
+  __shared__ float bias[kRing][NT];
   __shared__ unsigned long long Umask[32];
   __shared__ int Wpref[33];
   __shared__ uint16_t Blist[2048];
   __shared__ uint16_t Act[2048];
-  __shared__ float Bz[2][64];   // the staged block's bias per position (routed blocks)
+  __shared__ uint16_t Ord[2048];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1055,11 +1174,11 @@ __global__ __launch_bounds__(kBqThreads, 1) void bwd_dq_kernel(Geom g, BwdParams
   const int W = g.W;
   const unsigned long long* __restrict__ mask = (const unsigned long long*)p.mask;
 
-  int tpos[2], rpos[2], rhead[2];
-  bool rvalid[2];
+  int tpos[TW], rpos[TW], rhead[TW];
+  bool rvalid[TW];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int ti = 2 * wv + u;
+  for (int u = 0; u < TW; ++u) {
+    const int ti = TW * wv + u;
     tpos[u] = ti / tg.HT;
     rpos[u] = p0 + tpos[u];
     rhead[u] = (ti % tg.HT) * 16 + r;
@@ -1067,10 +1186,10 @@ __global__ __launch_bounds__(kBqThreads, 1) void bwd_dq_kernel(Geom g, BwdParams
   }
   // Q and dO operands (B of S^T = K Q^T and dP^T = V dO^T), the forward's LSE
   // and D = <dO, O> of the lane's head, in log2 units where they meet exp2
-  bf16x8 qa[2][KS], da[2][KS];
-  float lse2[2], dlt[2];
+  bf16x8 qa[TW][KS], da[TW][KS];
+  float lse2[TW], dlt[TW];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < TW; ++u) {
     const int64_t tok = si.start + min(rpos[u], pend - 1);
     const int64_t row = (tok * g.Hq + h * g.G + rhead[u]) * (int64_t)D;
 #pragma unroll
@@ -1088,207 +1207,187 @@ __global__ __launch_bounds__(kBqThreads, 1) void bwd_dq_kernel(Geom g, BwdParams
     dlt[u] = p.delta[hr];
   }
 
-  // ---- the union of the positions' active chunks and their bitmap (as in
-  // the forward kernel)
-  if (tid < 32) Umask[tid] = 0ull;
-  __syncthreads();
   const unsigned long long* mbase = mask + ((int64_t)h * T + si.start + p0) * W;
-  for (int idx = tid; idx < npos * W; idx += NTH) {
-    const int w = idx % W;
-    const unsigned long long v = mbase[idx] & routable_bits(w, cdiag);
-    if (v) atomicOr(&Umask[w], v);
-  }
-  __syncthreads();
-  if (tid < 64) {
-    int cnt = (tid < W) ? __popcll(Umask[tid]) : 0;
-    int inc = cnt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(inc, o);
-      if (lane >= o) inc += y;
-    }
-    if (tid < 33) Wpref[tid] = inc - cnt;
-  }
-  __syncthreads();
-  if (tid < W) {
-    unsigned long long v = Umask[tid];
-    int o = Wpref[tid];
-    while (v) {
-      Blist[o++] = (uint16_t)(tid * 64 + __ffsll(v) - 1);
-      v &= v - 1;
-    }
-  }
-  __syncthreads();
-  const int nlist = Wpref[W];
-  for (int j = tid; j < nlist; j += NTH) {
-    const int c = Blist[j];
-    uint32_t bits = 0;
-    for (int t = 0; t < npos; ++t)
-      bits |= (uint32_t)((mbase[t * W + (c >> 6)] >> (c & 63)) & 1ull) << t;
-    Act[j] = (uint16_t)bits;
-  }
-  __syncthreads();
+  const int nlist = ring_build_list<NWV, TW>(W, tg.HT, g.B == 128, mbase, npos, cdiag, Umask,
+                                             Wpref, Blist, Act, Ord);
   const int sbl = g.B == 128 ? 1 : 0;
   const int nrouted = nlist << sbl;
   const int ndiag = (pend - cdiag * g.B + 63) / 64;
   const int NS = nrouted + ndiag;
 
-  // ---- staging: segment i of this wave is the 1 KB at (8 i + wv) KB of
-  // the block; lane l fills its 16 bytes at l * 16, from the source piece that
-  // the swizzled layout puts there (K and V rows in the K layout, K^T rows in
-  // the V^T layout)
-  const int kmax = pend - 1;  // last key of the sequence this workgroup may see
-  const uint8_t* kb8 = (const uint8_t*)p.k + (si.start * (int64_t)g.Hkv + h) * D * 2;
-  const uint8_t* vb8 = (const uint8_t*)p.v + (si.start * (int64_t)g.Hkv + h) * D * 2;
-  const uint8_t* tb8 = (const uint8_t*)p.kt + (((int64_t)h * D) * p.Tp + pad_off(g, s)) * 2;
-  auto block_key0 = [&](int sx) -> int {
-    return sx < nrouted ? (int)Blist[sx >> sbl] * g.B + ((sx & sbl) << 6)
-                        : cdiag * g.B + ((sx - nrouted) << 6);
-  };
-  const uint32_t krs = (uint32_t)(g.Hkv * D * 2);  // bytes between consecutive keys
-  const uint32_t trs = (uint32_t)(p.Tp * 2);        // bytes between K^T rows
-  auto sload = [&](int sx, int buf) {
-    const int key0 = block_key0(sx);
-    const uint32_t base = lds_addr(&stage[buf][0]);
+  // ---- per-thread DMA sources: piece i of this thread is 16 bytes of K row
+  // or V row kr of the block (a wave's pieces all K or all V), from the source
+  // piece dq_swz places at its slot
+  const int64_t krs = (int64_t)g.Hkv * D * 2;  // bytes between consecutive keys
+  const bool isk = wv * NP * 1024 < KBYTES;
+  const uint8_t* rbase = (const uint8_t*)(isk ? p.k : p.v) + (si.start * (int64_t)g.Hkv + h) * D * 2;
+  int prow[NP];
+  const uint8_t* pbase[NP];
 #pragma unroll
-    for (int i = 0; i < NPC; ++i) {
-      const int seg = 8 * i + wv;  // wave-uniform: the segment lies in one region
-      const int o = seg * 1024 + lane * 16;
-      if (seg * 1024 < 2 * KB) {
-        const int ok = o % KB;
-        const int kr = ok / R::KROW;
-        const int pc = ((ok % R::KROW) / 16) ^ swz<R::KP>(kr);
-        const uint32_t key = (uint32_t)min(key0 + kr, kmax);
-        lds_dma16s(seg * 1024 < KB ? kb8 : vb8, key * krs + (uint32_t)(pc * 16),
-                   base + (uint32_t)(seg * 1024));
-      } else {
-        const int ot = o - 2 * KB;
-        const int d = ot / R::VROW;
-        const int pc = ((ot % R::VROW) / 16) ^ swz<8>(d);
-        lds_dma16s(tb8, (uint32_t)d * trs + (uint32_t)(key0 * 2 + pc * 16),
-                   base + (uint32_t)(seg * 1024));
-      }
+  for (int i = 0; i < NP; ++i) {
+    const int o = ((wv * NP + i) * 1024 + lane * 16) % KBYTES;
+    prow[i] = o / KROW;
+    pbase[i] = rbase + prow[i] * krs + (((o % KROW) / 16) ^ dq_swz<D>(prow[i])) * 16;
+  }
+  const int bpos = min(p0 + (TW * wv + min(lane, TW - 1)) / tg.HT, pend - 1);
+  const float* bsrc = p.log_prior + ((int64_t)h * T + si.start + bpos) * g.C_slots;
+  const int kmax = pend - 1;
+  auto issue_at = [&](int key0, int c, uint32_t slot, uint32_t bslot) {
+    if (key0 + 63 <= kmax) {
+#pragma unroll
+      for (int i = 0; i < NP; ++i)
+        lds_dma16(pbase[i] + (int64_t)key0 * krs, slot + (wv * NP + i) * 1024);
+    } else {
+      // rows past the sequence end (its last chunk): the last key again
+#pragma unroll
+      for (int i = 0; i < NP; ++i)
+        lds_dma16(pbase[i] + (int64_t)(min(key0 + prow[i], kmax) - prow[i]) * krs,
+                  slot + (wv * NP + i) * 1024);
     }
-    // a routed block's bias for each position, beside it (a load in the loop
-    // itself would make the compiler wait for the whole staging)
-    if (sx < nrouted && wv == 0 && lane < npos) {
-      const int c = Blist[sx >> sbl];
-      lds_dma4(p.log_prior + ((int64_t)h * T + si.start + p0 + lane) * g.C_slots + c,
-               __builtin_amdgcn_readfirstlane(lds_addr(&Bz[buf][0])));
-    }
+    if (lane < TW) lds_dma4(bsrc + c, bslot + wv * TW * 4);
+  };
+  auto block_key0 = [&](int sx, int cl) -> int {
+    return sx < nrouted ? cl * g.B + ((sx & sbl) << 6) : cdiag * g.B + ((sx - nrouted) << 6);
+  };
+  auto listed = [&](int sx) -> int {
+    return sx < nrouted ? __builtin_amdgcn_readfirstlane((int)Blist[sx >> sbl]) : 0;
+  };
+  auto issue = [&](int sx, uint32_t slot, uint32_t bslot) {
+    const int c = listed(sx);
+    issue_at(block_key0(sx, c), c, slot, bslot);
   };
 
-  f32x4 o[2][DT];
+  f32x4 o[TW][DT];
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int u = 0; u < TW; ++u)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float sl2 = p.scale * kLog2e;
-  int koff[KS], voff[2];
+  const int rsw = dq_swz<D>(r);  // rows 16 t + r share r's swizzle
+  int koff[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) koff[ks] = r * R::KROW + (((4 * ks + gq) ^ swz<R::KP>(r)) * 16);
-#pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2) voff[s2] = r * R::VROW + (((4 * s2 + gq) ^ swz<8>(r)) * 16);
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = r * KROW + ((4 * ks + gq) ^ rsw) * 16;
+  // transposing reads: lane (gq, r) points at row 4 gq + r / 4 (+ 32 h2, + 16),
+  // dims 16 dt + 4 (r % 4) .. +3, i.e. piece 2 dt + (r % 4) / 2 at its slot
+  // ((2 dt) ^ f) + (r % 4) / 2 (f even), byte 8 (r % 2)
+  const int trow = 4 * gq + (r >> 2);
+  const int tb = trow * KROW + 16 * ((r & 3) >> 1) + 8 * (r & 1);
+  const int tx = dq_swz<D>(trow) >> 1;
   float* dbias = p.dbias;
+  const uint32_t ring0 = lds_addr(&ring[0][0]), bias0 = lds_addr(&bias[0][0]);
 
-  // one tile's visit of the staged block kv; returns the tile's sum of dS
-  auto visit = [&](auto masked_tag, auto u_tag, lds_u8* kv, float bz, int kbase0) -> float {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    constexpr int U = decltype(u_tag)::value;
-    f32x4 sacc[4], pacc[4];
+  auto active_mask = [&](int j) -> uint32_t {
+    const uint32_t act = Act[j];
+    uint32_t am = 0;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      pacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 f[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) f[t] = lds_read16(kv + koff[ks] + 16 * t * R::KROW);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) sacc[t] = mfma16x16x32(as_bf16x8(f[t]), qa[U][ks], sacc[t]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) f[t] = lds_read16(kv + KB + koff[ks] + 16 * t * R::KROW);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) pacc[t] = mfma16x16x32(as_bf16x8(f[t]), da[U][ks], pacc[t]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    uint32_t pk[4][2];
-    float dsum = 0.f;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      float ds[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float pv = __builtin_amdgcn_exp2f(fmaf(sacc[t][j], sl2, bz - lse2[U]));
-        if constexpr (MASKED) pv = kbase0 + 16 * t + j <= rpos[U] ? pv : 0.f;
-        ds[j] = pv * (pacc[t][j] - dlt[U]);
-        dsum += ds[j];
-      }
-      pk[t][0] = cvt_pk_bf16(ds[0], ds[1]);
-      pk[t][1] = cvt_pk_bf16(ds[2], ds[3]);
-    }
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const u32x4 pb = {pk[2 * s2][0], pk[2 * s2][1], pk[2 * s2 + 1][0], pk[2 * s2 + 1][1]};
-#pragma unroll
-      for (int d0 = 0; d0 < DT; d0 += 4) {
-        u32x4 a[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          a[i] = lds_read16(kv + 2 * KB + voff[s2] + 16 * (d0 + i) * R::VROW);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          o[U][d0 + i] = mfma16x16x32(as_bf16x8(a[i]), as_bf16x8(pb), o[U][d0 + i]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    // the tile's sum of dS over its 16 heads and the block's keys
-    dsum = row16_sum(dsum);
-    dsum += xor16(dsum);
-    dsum += xor32(dsum);
-    return dsum;
+    for (int u = 0; u < TW; ++u)
+      am |= (rvalid[u] && ((act >> tpos[u]) & 1u)) ? (1u << u) : 0u;
+    return am;
   };
-  using F = std::false_type;
-  using Tr = std::true_type;
-  using U0 = std::integral_constant<int, 0>;
-  using U1 = std::integral_constant<int, 1>;
-
-  __builtin_amdgcn_s_waitcnt(0 | (7 << 4));  // operand and mask reads done
-  sload(0, 0);
-  for (int st = 0; st < NS; ++st) {
-    const int buf = st & 1;
-    // this block's loads landed, every wave is done with the other buffer
-    __builtin_amdgcn_s_waitcnt(0 | (7 << 4));
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (st + 1 < NS) sload(st + 1, buf ^ 1);
-    lds_u8* kv = (lds_u8*)&stage[buf][0];
-    if (st < nrouted) {
-      const int c = Blist[st >> sbl];
-      const uint32_t act = Act[st >> sbl];
+  auto routed_step = [&](int st, lds_u8* kv, uint32_t am) {
+    float bz[TW], ds[TW];
+    const float* bs = &bias[st & 3][TW * wv];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        if (!(rvalid[u] && ((act >> tpos[u]) & 1u))) continue;
-        const int64_t brow = ((int64_t)h * T + si.start + rpos[u]) * g.C_slots + c;
-        const float bz = Bz[buf][tpos[u]] * kLog2e;
-        const float d = u == 0 ? visit(F(), U0(), kv, bz, 0) : visit(F(), U1(), kv, bz, 0);
-        if (lane == 0) atomicAdd(&dbias[brow], d);
+    for (int u = 0; u < TW; ++u) {
+      bz[u] = bs[u] * kLog2e;
+      ds[u] = 0.f;
+    }
+    const int c = listed(st);
+    static_for<0, (PAIR ? TW / 2 : TW)>([&](auto k_) {
+      constexpr int U0 = PAIR ? 2 * decltype(k_)::value : decltype(k_)::value;
+      constexpr int NTL = PAIR ? 2 : 1;
+      if ((am >> U0) & 1u) {
+        visit_dq<D, false, U0, NTL, TW>(kv, kv + KBYTES, koff, tb, tx, qa, da, lse2, dlt, o, ds,
+                                        sl2, bz, 0, rpos);
+        // the tile's sum of dS over the block's keys and its 16 heads
+#pragma unroll
+        for (int u = U0; u < U0 + NTL; ++u) {
+          float d = row16_sum(ds[u]);
+          d += xor16(d);
+          d += xor32(d);
+          if (lane == 0)
+            atomicAdd(&dbias[((int64_t)h * T + si.start + rpos[u]) * g.C_slots + c], d);
+        }
       }
-    } else {
-      const int key0 = cdiag * g.B + ((st - nrouted) << 6);
-      if (rvalid[0]) visit(Tr(), U0(), kv, 0.f, key0 + 4 * gq);
-      if (rvalid[1]) visit(Tr(), U1(), kv, 0.f, key0 + 4 * gq);
+    });
+  };
+  auto diag_step = [&](int st, lds_u8* kv) {
+    float bz[TW], ds[TW];
+#pragma unroll
+    for (int u = 0; u < TW; ++u) {
+      bz[u] = 0.f;
+      ds[u] = 0.f;
+    }
+    const int key0 = cdiag * g.B + ((st - nrouted) << 6);
+    static_for<0, (PAIR ? TW / 2 : TW)>([&](auto k_) {
+      constexpr int U0 = PAIR ? 2 * decltype(k_)::value : decltype(k_)::value;
+      constexpr int NTL = PAIR ? 2 : 1;
+      if (rvalid[U0])
+        visit_dq<D, true, U0, NTL, TW>(kv, kv + KBYTES, koff, tb, tx, qa, da, lse2, dlt, o, ds,
+                                       sl2, bz, key0 + 4 * gq, rpos);
+    });
+  };
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4));  // operand and mask reads done first
+  if (sbl == 0) {
+    // 64-key chunks: two blocks per barrier, the next two loading meanwhile
+    // (the forward ring kernel's schedule)
+    issue(0, ring0, bias0);
+    if (NS > 1) issue(1, ring0 + STAGE, bias0 + 4 * NT);
+    auto pair_enter = [&](int st) {
+      if (st & 1) return;
+      wait_vm<0>();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+#pragma unroll 1
+      for (int b = st + 2; b < min(st + 4, NS); ++b)
+        issue(b, ring0 + (b & 3) * STAGE, bias0 + (b & 3) * 4 * NT);
+    };
+    for (int st = 0; st < nrouted; ++st) {
+      pair_enter(st);
+      routed_step(st, (lds_u8*)&ring[st & 3][0], active_mask(st));
+    }
+    for (int st = nrouted; st < NS; ++st) {
+      pair_enter(st);
+      diag_step(st, (lds_u8*)&ring[st & 3][0]);
+    }
+  } else {
+    // 128-key chunks: one block per barrier, three ahead; every step issues
+    // exactly one block's loads (past the list's end the last block again,
+    // into the free slot), so one fixed counted wait proves slot st & 3 done
+    issue(0, ring0, bias0);
+    issue(min(1, NS - 1), ring0 + STAGE, bias0 + 4 * NT);
+    issue(min(2, NS - 1), ring0 + 2 * STAGE, bias0 + 8 * NT);
+    auto enter = [&](int st) -> lds_u8* {
+      wait_vm<2 * LPS>();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      return (lds_u8*)&ring[st & 3][0];
+    };
+    auto leave = [&](int st, int cnext) {
+      const int sr = st + 3, sx = min(sr, NS - 1);
+      issue_at(block_key0(sx, cnext), cnext, ring0 + (sr & 3) * STAGE, bias0 + (sr & 3) * 4 * NT);
+    };
+    for (int st = 0; st < nrouted; ++st) {
+      lds_u8* kv = enter(st);
+      const int cnext = listed(min(st + 3, NS - 1));
+      const uint32_t am = active_mask(st >> sbl);
+      if (!am) leave(st, cnext);
+      routed_step(st, kv, am);
+      if (am) leave(st, cnext);
+    }
+    for (int st = nrouted; st < NS; ++st) {
+      lds_u8* kv = enter(st);
+      diag_step(st, kv);
+      leave(st, 0);
     }
   }
-  __builtin_amdgcn_s_waitcnt(0 | (7 << 4));  // no staging load outlives the kernel
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4));  // no ring load outlives the kernel
 
   // dQ = s dQ^T^T, fp32: lane (gq, r) holds dims 16 dt + 4 gq .. +3 of head r
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < TW; ++u) {
     if (!rvalid[u]) continue;
     const int64_t tok = si.start + rpos[u];
     float* drow = p.dq + (tok * g.Hq + h * g.G + rhead[u]) * (int64_t)D;
@@ -1513,12 +1612,17 @@ hipError_t launch_vt_transpose(const Geom& g, const void* src, void* dst, int64_
 
 hipError_t launch_bwd_dq(const Geom& g, const BwdParams& p, hipStream_t st) {
   if (g.T == 0) return hipSuccess;
-  const TileGeom rg = make_ring_tiles(g);
+  // the forward's tiling: 16 waves of one tile (G = 16) or 8 of a pair (G = 32)
+  const TileGeom rg = make_ring_tiles(g, 16, g.G == 32 ? 2 : 1);
   dim3 grid(rg.tiles_per_seq, g.num_seqs, g.Hkv);
-  if (g.D == 64)
-    hipLaunchKernelGGL(bwd_dq_kernel<64>, grid, dim3(kBqThreads), 0, st, g, p, rg);
-  else
-    hipLaunchKernelGGL(bwd_dq_kernel<128>, grid, dim3(kBqThreads), 0, st, g, p, rg);
+#define DASH_BQ(DD, NW, TW_, PR) \
+  hipLaunchKernelGGL((bwd_dq_ring_kernel<DD, NW, TW_, PR>), grid, dim3(64 * NW), 0, st, g, p, rg)
+  if (g.G == 32) {
+    if (g.D == 64) DASH_BQ(64, 8, 2, true); else DASH_BQ(128, 8, 2, true);
+  } else {
+    if (g.D == 64) DASH_BQ(64, 16, 1, false); else DASH_BQ(128, 16, 1, false);
+  }
+#undef DASH_BQ
   return hipGetLastError();
 }
 

@@ -197,17 +197,15 @@ RouteDecodeWs route_decode_ws(const Geom& g) {
   w.total = o;
   return w;
 }
-// Backward of phase 2: K^T, D = <dO, O>, and fp32 dQ / dK / dV.
+// Backward of phase 2: D = <dO, O>, and fp32 dQ / dK / dV.
 struct BackwardWs {
-  size_t meta, kt, delta, dq, dk, dv, total;
+  size_t meta, delta, dq, dk, dv, total;
 };
 BackwardWs backward_ws(const Geom& g) {
   BackwardWs w{};
   size_t o = 0;
   w.meta = o;
   o += meta_ws(g);
-  w.kt = o;
-  o += align_up((size_t)g.Hkv * g.D * dash::padded_tokens(g.T, g.num_seqs) * 2);
   w.delta = o;
   o += align_up((size_t)g.Hq * g.T * 4);
   w.dq = o;
@@ -832,8 +830,6 @@ dash_status dash_attn_sparse_backward(const dash_shape* shape, const void* q, co
   p.q = q;
   p.k = k;
   p.v = v;
-  p.kt = at(workspace, w.kt);
-  p.Tp = dash::padded_tokens(g.T, g.num_seqs);
   p.dout = dout;
   p.lse = lse;
   p.delta = reinterpret_cast<float*>(at(workspace, w.delta));
@@ -844,7 +840,6 @@ dash_status dash_attn_sparse_backward(const dash_shape* shape, const void* q, co
   p.dbias = dbias;
   float* dkw = reinterpret_cast<float*>(at(workspace, w.dk));
   float* dvw = reinterpret_cast<float*>(at(workspace, w.dv));
-  DASH_HIP(dash::launch_vt_transpose(g, k, at(workspace, w.kt), p.Tp, s));
   DASH_HIP(dash::launch_bwd_delta(g, out, dout, reinterpret_cast<float*>(at(workspace, w.delta)), s));
   DASH_HIP(dash::launch_zero(dbias, (int64_t)g.Hkv * g.T * g.C_slots, s));
   DASH_HIP(dash::launch_bwd_dq(g, p, s));
@@ -914,8 +909,6 @@ dash_status dash_attn_prefill_backward(const dash_shape* shape, const void* q, c
   p.q = q;
   p.k = k;
   p.v = v;
-  p.kt = at(workspace, w.a.kt);
-  p.Tp = dash::padded_tokens(g.T, g.num_seqs);
   p.dout = dout;
   p.lse = lse;
   p.delta = reinterpret_cast<float*>(at(workspace, w.a.delta));
@@ -926,7 +919,6 @@ dash_status dash_attn_prefill_backward(const dash_shape* shape, const void* q, c
   p.dbias = reinterpret_cast<float*>(at(workspace, w.db));
   float* dkw = reinterpret_cast<float*>(at(workspace, w.a.dk));
   float* dvw = reinterpret_cast<float*>(at(workspace, w.a.dv));
-  DASH_HIP(dash::launch_vt_transpose(g, k, at(workspace, w.a.kt), p.Tp, s));
   DASH_HIP(dash::launch_bwd_delta(g, out, dout, reinterpret_cast<float*>(at(workspace, w.a.delta)), s));
   DASH_HIP(dash::launch_zero(p.dbias, (int64_t)g.Hkv * g.T * g.C_slots, s));
   DASH_HIP(dash::launch_bwd_dq(g, p, s));

@@ -135,8 +135,6 @@ struct BwdParams {
   const void* q = nullptr;              // [T, Hq, D]
   const void* k = nullptr;              // [T, Hkv, D]
   const void* v = nullptr;
-  const void* kt = nullptr;             // K^T workspace [Hkv, D, Tp] (the V^T layout)
-  int64_t Tp = 0;
   const void* dout = nullptr;           // [T, Hq, D]
   const float* lse = nullptr;           // [Hq, T] natural log, from the forward
   const float* delta = nullptr;         // [Hq, T] <dO, O>
