@@ -222,7 +222,7 @@ BackwardWs backward_ws(const Geom& g) {
 // per-head terms of the routing backward.
 struct PrefillBwdWs {
   BackwardWs a;
-  size_t kbar, mask, logp, tau, db, sc, kbt, dkb, kdiag, dkdiag, total;
+  size_t kbar, mask, logp, tau, db, sc, kbt, dkb, kdiag, dkdiag, flags, total;
 };
 PrefillBwdWs prefill_bwd_ws(const Geom& g) {
   PrefillBwdWs w{};
@@ -248,6 +248,8 @@ PrefillBwdWs prefill_bwd_ws(const Geom& g) {
   o += align_up((size_t)g.T * g.Hkv * g.D * elt(g));
   w.dkdiag = o;
   o += align_up((size_t)g.T * g.Hkv * g.D * 4);
+  w.flags = o;  // the routing's row-group flags (the forward's routing kernels)
+  o += flag_bytes(g);
   w.total = o;
   return w;
 }
@@ -880,7 +882,7 @@ dash_status dash_attn_prefill_backward(const dash_shape* shape, const void* q, c
     DASH_HIP(dash::launch_varlen_meta(g.cu_seqlens, g.num_seqs, g.B, meta_chunks(meta),
                                       meta_pad(g, meta), s));
   }
-  // the forward's routing, recomputed
+  // the forward's routing, recomputed by the same kernels
   void* kbar = at(workspace, w.kbar);
   uint64_t* mask = reinterpret_cast<uint64_t*>(at(workspace, w.mask));
   float* logp = reinterpret_cast<float*>(at(workspace, w.logp));
@@ -903,7 +905,7 @@ dash_status dash_attn_prefill_backward(const dash_shape* shape, const void* q, c
   rp.log_prior = logp;
   rp.tau = tau;
   rp.rows = g.T;
-  DASH_HIP(dash::launch_route(g, rp, s));
+  DASH_HIP(run_route(g, rp, w.flags < w.total ? at(workspace, w.flags) : nullptr, s));
   // phase 2
   dash::BwdParams p;
   p.q = q;

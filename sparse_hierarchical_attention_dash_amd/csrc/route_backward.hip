@@ -170,10 +170,13 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
     }
   }
   __syncthreads();
-  // ---- dp on the active chunks (written over db)
+  // ---- dp on the active chunks (written over db).  A chunk the mask holds
+  // but whose recomputed w_bar is 0 (every head's logit within rounding of
+  // its threshold: the mask's kernel forms the logits in another order) has
+  // r = 0 for every head below, so it carries no gradient: dp = 0 there.
   float* drow = p.db + ((int64_t)h * T + row) * g.C_slots;
   for (int c = tid; c < n; c += NTH) {
-    const float dp = On[c] ? p.sigma * drow[c] / Wp[c] : 0.f;
+    const float dp = (On[c] && Wp[c] > 0.f) ? p.sigma * drow[c] / Wp[c] : 0.f;
     Wp[c] = dp;
     drow[c] = dp;
   }
