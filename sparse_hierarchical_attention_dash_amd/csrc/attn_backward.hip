@@ -81,16 +81,6 @@ struct DkdvCfg {
   static_assert(2 * AU % NTH == 0, "units per stage");
 };
 
-// Slot of 16-byte piece pc of head j's row in the staged Q and dO: pc ^ f(j),
-// with f giving the heads that share the 64 banks (one 256-byte row at
-// D = 128, two 128-byte rows at D = 64) distinct even offsets.  Then eight
-// heads' 16-byte reads of one piece (the S and dP operands) and four heads'
-// 8-byte transposing reads of two adjacent pieces (the dV and dK operands)
-// each touch every bank at most once.
-template <int D>
-__device__ __forceinline__ int dkdv_swz(int j) {
-  return D == 128 ? (2 * j) & 15 : j & 6;
-}
 
 template <int D, int HT, int KT>
 __global__ __launch_bounds__(256 / KT) void bwd_dkdv_kernel(Geom g, BwdParams p, float* dk,
@@ -164,8 +154,8 @@ __global__ __launch_bounds__(256 / KT) void bwd_dkdv_kernel(Geom g, BwdParams p,
     for (int e = 0; e < C::NUT; ++e) {
       const int U = tid + NTH * e;
       const int arr = U / C::AU, u = U % C::AU;
-      // row-major: slot u % UPH of head j holds the piece dkdv_swz places there
-      const int j = u / UPH, pc = (u % UPH) ^ dkdv_swz<D>(j);
+      // row-major: slot u % UPH of head j holds the piece head_row_swz places there
+      const int j = u / UPH, pc = (u % UPH) ^ head_row_swz<D>(j);
       const uint16_t* src = (arr == 0 ? qg : dg) + (tok * g.Hq + h * G + j) * (int64_t)D + 8 * pc;
       lds_dma16(src, __builtin_amdgcn_readfirstlane(base + (uint32_t)(16 * (NTH * e + 64 * wv))));
     }
@@ -197,7 +187,7 @@ __global__ __launch_bounds__(256 / KT) void bwd_dkdv_kernel(Geom g, BwdParams p,
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         // one read of the row's Q and dO fragments serves the wave's KT key tiles
-        const int off = 16 * (j * UPH + ((4 * ks + gq) ^ dkdv_swz<D>(j)));
+        const int off = 16 * (j * UPH + ((4 * ks + gq) ^ head_row_swz<D>(j)));
         const bf16x8 qf = as_bf16x8(lds_read16(Qs + off)), df = as_bf16x8(lds_read16(Ds + off));
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
@@ -227,7 +217,7 @@ __global__ __launch_bounds__(256 / KT) void bwd_dkdv_kernel(Geom g, BwdParams p,
       // 16 ht + 4 gq .. +3 (the A operand of X^T)
       const int jt = 16 * ht + 4 * gq + (r >> 2);
       const int tbase = 16 * jt * UPH + 8 * (r & 1);
-      const int tsw = dkdv_swz<D>(jt), tpc = (r & 3) >> 1;
+      const int tsw = head_row_swz<D>(jt), tpc = (r & 3) >> 1;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int off = tbase + 16 * ((2 * dt + tpc) ^ tsw);

@@ -1034,7 +1034,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void prefill_attn_ring_kernel(
 // walk the union of their positions' active blocks (ring_build_list, paired
 // for 64-key chunks) and then the diagonal, through the same 4-slot LDS ring
 // and barrier schedule.  A staged block is the block's K rows and V rows,
-// 16-byte pieces XOR-swizzled by dq_swz; K^T, the operand of the dQ product,
+// 16-byte pieces XOR-swizzled by head_row_swz; K^T, the operand of the dQ product,
 // comes from the K rows by gfx950's transposing LDS reads, so a block crosses
 // the fabric once, as 2 x 64 rows.  Visit of an active tile, 32 keys at a
 // time: S^T = K Q^T and dP^T = V dO^T (16x16x32), P^T = exp2(s S^T + b - LSE)
@@ -1042,16 +1042,6 @@ __global__ __launch_bounds__(64 * NWV, 1) void prefill_attn_ring_kernel(
 // K^T dS^T (16x16x32); a routed block's bias gradient, the tile's sum of dS,
 // is added atomically.  dQ (times s) is written in fp32 for the routing
 // backward to add to.
-
-// Slot of 16-byte piece pc of staged row `row`: pc ^ f(row), with f giving
-// the rows that share the 64 banks distinct even offsets, so that eight
-// consecutive rows' 16-byte reads of one piece (the S^T and dP^T operands)
-// and four consecutive rows' 8-byte transposing reads of two adjacent pieces
-// (the K^T operand) each touch every bank at most once.
-template <int D>
-__device__ __forceinline__ int dq_swz(int row) {
-  return D == 128 ? (2 * row) & 15 : row & 6;
-}
 
 // One visit of tiles U0 .. U0+NTL-1 of a wave to one staged block (K rows at
 // ks_, V rows at vs_), in two halves of 32 keys.  koff: the lane's S^T / dP^T
@@ -1217,7 +1207,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void bwd_dq_ring_kernel(Geom g, BwdPar
 
   // ---- per-thread DMA sources: piece i of this thread is 16 bytes of K row
   // or V row kr of the block (a wave's pieces all K or all V), from the source
-  // piece dq_swz places at its slot
+  // piece head_row_swz places at its slot
   const int64_t krs = (int64_t)g.Hkv * D * 2;  // bytes between consecutive keys
   const bool isk = wv * NP * 1024 < KBYTES;
   const uint8_t* rbase = (const uint8_t*)(isk ? p.k : p.v) + (si.start * (int64_t)g.Hkv + h) * D * 2;
@@ -1227,7 +1217,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void bwd_dq_ring_kernel(Geom g, BwdPar
   for (int i = 0; i < NP; ++i) {
     const int o = ((wv * NP + i) * 1024 + lane * 16) % KBYTES;
     prow[i] = o / KROW;
-    pbase[i] = rbase + prow[i] * krs + (((o % KROW) / 16) ^ dq_swz<D>(prow[i])) * 16;
+    pbase[i] = rbase + prow[i] * krs + (((o % KROW) / 16) ^ head_row_swz<D>(prow[i])) * 16;
   }
   const int bpos = min(p0 + (TW * wv + min(lane, TW - 1)) / tg.HT, pend - 1);
   const float* bsrc = p.log_prior + ((int64_t)h * T + si.start + bpos) * g.C_slots;
@@ -1263,7 +1253,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void bwd_dq_ring_kernel(Geom g, BwdPar
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float sl2 = p.scale * kLog2e;
-  const int rsw = dq_swz<D>(r);  // rows 16 t + r share r's swizzle
+  const int rsw = head_row_swz<D>(r);  // rows 16 t + r share r's swizzle
   int koff[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) koff[ks] = r * KROW + ((4 * ks + gq) ^ rsw) * 16;
@@ -1272,7 +1262,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void bwd_dq_ring_kernel(Geom g, BwdPar
   // ((2 dt) ^ f) + (r % 4) / 2 (f even), byte 8 (r % 2)
   const int trow = 4 * gq + (r >> 2);
   const int tb = trow * KROW + 16 * ((r & 3) >> 1) + 8 * (r & 1);
-  const int tx = dq_swz<D>(trow) >> 1;
+  const int tx = head_row_swz<D>(trow) >> 1;
   float* dbias = p.dbias;
   const uint32_t ring0 = lds_addr(&ring[0][0]), bias0 = lds_addr(&bias[0][0]);
 

@@ -268,6 +268,18 @@ __device__ __forceinline__ s16x4 lds_read_tr8(lds_u8* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
 }
 
+// Slot of 16-byte piece pc of row j of a staged tile of D-dim bf16 rows
+// (query heads of one token, or keys): pc ^ head_row_swz(j), which gives
+// the rows that share the 64 banks (one 256-byte row at D = 128, two
+// 128-byte rows at D = 64) distinct even offsets.  Then eight consecutive
+// rows' 16-byte reads of one piece (an MFMA operand with the dims as k) and
+// four consecutive rows' 8-byte transposing reads of two adjacent pieces (an
+// operand with the rows as k) each touch every bank at most once.
+template <int D>
+__device__ __forceinline__ int head_row_swz(int j) {
+  return D == 128 ? (2 * j) & 15 : j & 6;
+}
+
 // s_waitcnt for at most N outstanding vector-memory operations (N < 64) and
 // no outstanding LDS operation
 template <int N>

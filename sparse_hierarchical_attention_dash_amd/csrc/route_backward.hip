@@ -74,7 +74,9 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
   constexpr int USTR = CP + 16;
   __shared__ __align__(16) float U[16 * USTR];   // logits, then du, of one 16-head tile
   __shared__ float Wp[CP];         // sum over the group's heads of p, then dp
-  __shared__ uint8_t On[CP];       // the row's active chunks
+  __shared__ uint8_t On[CP];       // the entry's chunk is active
+  __shared__ uint16_t L[CP];       // the row's entries: chunk of entry k
+  __shared__ int Wpre[33];         // entries before each mask word
   __shared__ float Hp[16][2];      // per head: threshold (x units) or max u; softmax sum
   __shared__ float Dd[16];         // per head: du of the own-chunk entry
   const int row = row0 + (int)blockIdx.x, h = blockIdx.y;
@@ -93,35 +95,80 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
     if (p.kdiag && tid < D) p.dkdiag[((int64_t)row * g.Hkv + h) * D + tid] = 0.f;
     return;
   }
-  // the row's own-chunk estimate, when given, is entry n of every head's entmax
-  const int ns = p.kdiag ? n + 1 : n;
-  const uint16_t* kdrow = (const uint16_t*)p.kdiag + ((int64_t)row * g.Hkv + h) * D;
   const float alpha = p.alpha_per_seq ? p.alpha_per_seq[s] : p.alpha;
   const bool smax = !(alpha > 1.f);
   const float am1 = alpha - 1.f;
   const float ep = smax ? 1.f : 1.f / am1;            // p = d^ep
   const float er = smax ? 1.f : (2.f - alpha) / am1;  // r = d^er
   const int HT = G / 16;
-  const int n32 = (n + 31) & ~31;
 
-  // logits of head tile ht into U (16 heads x n chunks, MFMA)
+  // ---- the row's entries.  alpha > 1: only the chunks the mask holds (every
+  // head's support lies in the union the mask is, so p, r and du vanish on
+  // the others); softmax: every routable chunk (every p > 0).  With
+  // estimate_diagonal the own-chunk estimate is one more entry, last.
+  const unsigned long long* mrow = p.mask + ((int64_t)h * T + row) * g.W;
+  const int nw = (n + 63) >> 6;
+  if (tid < 64) {
+    const unsigned long long wd = tid < nw ? mrow[tid] & routable_bits(tid, n) : 0ull;
+    const int cnt = smax ? max(0, min(64, n - 64 * tid)) : __popcll(wd);
+    int inc = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o);
+      if (lane >= o) inc += y;
+    }
+    if (tid < 33) Wpre[tid] = inc - cnt;
+    if (tid < nw) {
+      int o = inc - cnt;
+      if (smax) {
+        for (int b = 0; b < cnt; ++b) {
+          L[o + b] = (uint16_t)(64 * tid + b);
+          On[o + b] = (uint8_t)((wd >> b) & 1ull);
+        }
+      } else {
+        unsigned long long v = wd;
+        while (v) {
+          L[o] = (uint16_t)(64 * tid + __ffsll((long long)v) - 1);
+          On[o++] = 1;
+          v &= v - 1;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const int na = Wpre[nw];                  // listed chunks
+  const int ns = p.kdiag ? na + 1 : na;     // entries
+  const int n32 = (na + 31) & ~31;
+  const uint16_t* kdrow = (const uint16_t*)p.kdiag + ((int64_t)row * g.Hkv + h) * D;
+
+  // logits of head tile ht for the entries into U (16 heads x ns, MFMA)
   auto logits = [&](int ht) {
     const uint16_t* qrow = (const uint16_t*)p.q + (((int64_t)row * g.Hq + h * G + 16 * ht + r) * D);
     bf16x8 qa[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qa[ks] = as_bf16x8(ldg16(qrow + 32 * ks + 8 * gq));
     const int nct = (ns + 15) >> 4;
-    for (int ct = wv; ct < nct; ct += 4) {
-      const int c = min(ct * 16 + r, ns - 1);
-      const uint16_t* krow =
-          c == n ? kdrow : (const uint16_t*)p.kbar + (((kb0 + c) * g.Hkv + h) * (int64_t)D);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // two entry tiles per round, their summary loads in flight together
+    for (int ct0 = wv; ct0 < nct; ct0 += 8) {
+      u32x4 kf[2][KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        acc = mfma16x16x32(qa[ks], as_bf16x8(ldg16(krow + 32 * ks + 8 * gq)), acc);
-      if (ct * 16 + r < ns) {
+      for (int e = 0; e < 2; ++e) {
+        const int k = min((ct0 + 4 * e) * 16 + r, ns - 1);
+        const uint16_t* krow =
+            k == na ? kdrow : (const uint16_t*)p.kbar + (((kb0 + L[k]) * g.Hkv + h) * (int64_t)D);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) U[(4 * gq + j) * USTR + ct * 16 + r] = acc[j] * p.gamma_scale;
+        for (int ks = 0; ks < KS; ++ks) kf[e][ks] = ldg16(krow + 32 * ks + 8 * gq);
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int ct = ct0 + 4 * e;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(qa[ks], as_bf16x8(kf[e][ks]), acc);
+        if (ct * 16 + r < ns) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) U[(4 * gq + j) * USTR + ct * 16 + r] = acc[j] * p.gamma_scale;
+        }
       }
     }
   };
@@ -151,22 +198,18 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
   };
 
   // ---- pass 1: w_bar (as G w_bar) over all head tiles
-  const unsigned long long* mrow = p.mask + ((int64_t)h * T + row) * g.W;
-  for (int c = tid; c < n; c += NTH) {
-    Wp[c] = 0.f;
-    On[c] = (uint8_t)((mrow[c >> 6] >> (c & 63)) & 1ull);
-  }
+  for (int k = tid; k < na; k += NTH) Wp[k] = 0.f;
   for (int ht = 0; ht < HT; ++ht) {
     __syncthreads();
     logits(ht);
     __syncthreads();
     head_params(ht);
     __syncthreads();
-    for (int c = tid; c < n; c += NTH) {
+    for (int k = tid; k < na; k += NTH) {
       float w = 0.f;
 #pragma unroll 4
-      for (int hh = 0; hh < 16; ++hh) w += prob(U[hh * USTR + c], hh);
-      Wp[c] += w;
+      for (int hh = 0; hh < 16; ++hh) w += prob(U[hh * USTR + k], hh);
+      Wp[k] += w;
     }
   }
   __syncthreads();
@@ -175,9 +218,10 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
   // its threshold: the mask's kernel forms the logits in another order) has
   // r = 0 for every head below, so it carries no gradient: dp = 0 there.
   float* drow = p.db + ((int64_t)h * T + row) * g.C_slots;
-  for (int c = tid; c < n; c += NTH) {
-    const float dp = (On[c] && Wp[c] > 0.f) ? p.sigma * drow[c] / Wp[c] : 0.f;
-    Wp[c] = dp;
+  for (int k = tid; k < na; k += NTH) {
+    const int c = L[k];
+    const float dp = (On[k] && Wp[k] > 0.f) ? p.sigma * drow[c] / Wp[k] : 0.f;
+    Wp[k] = dp;
     drow[c] = dp;
   }
   // ---- pass 2 per head tile: r, rho, du; dq += gamma s du K_bar
@@ -194,42 +238,63 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
       const int hh = wv * 4 + (lane >> 4);
       float* ur = U + hh * USTR;
       float num = 0.f, den = 0.f;
-      for (int c = r; c < n; c += 16) {
-        const float rr = On[c] ? rterm(ur[c], hh) : 0.f;
-        num = fmaf(rr, Wp[c], num);
+      for (int k = r; k < na; k += 16) {
+        const float rr = On[k] ? rterm(ur[k], hh) : 0.f;
+        num = fmaf(rr, Wp[k], num);
         den += rr;
       }
       // the own-chunk entry: in the entmax, no prior (its dp is 0)
-      const float rd = (p.kdiag && r == 0) ? rterm(ur[n], hh) : 0.f;
+      const float rd = (p.kdiag && r == 0) ? rterm(ur[na], hh) : 0.f;
       den += rd;
       num = row16_sum(num);
       den = row16_sum(den);
       const float rho = den > 0.f ? num / den : 0.f;
       if (p.kdiag && r == 0) Dd[hh] = -rd * rho;
       // every lane of the head has read its U entries above; du overwrites them
-      for (int c = r; c < n32; c += 16) {
+      for (int k = r; k < n32; k += 16) {
         float du = 0.f;
-        if (c < n && On[c]) du = rterm(ur[c], hh) * (Wp[c] - rho);
-        ur[c] = du;
+        if (k < na && On[k]) du = rterm(ur[k], hh) * (Wp[k] - rho);
+        ur[k] = du;
       }
       if (r == 0)
         sc[(int64_t)(h * G + 16 * ht + hh) * T + row] = make_float4(Hp[hh][0], Hp[hh][1], rho, 0.f);
     }
     __syncthreads();
-    // dq tile (16 heads x 16 dims) = du (16 x n32) K_bar (n32 x 16), K_bar^T rows
-    // as the B operand; wave wv: dim tiles wv, wv + 4
+    // dq tile (16 heads x 16 dims) = du (16 x n32) K_bar (n32 x 16) over the
+    // listed chunks, the B operand gathered from K_bar^T; wave wv: dim tiles
+    // wv, wv + 4
     constexpr int NT = D / 16;
     const uint16_t* kt = p.kbt + ((int64_t)(s * g.Hkv + h) * D) * p.cpad;
     for (int dt = wv; dt < NT; dt += 4) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const uint16_t* ktr = kt + (int64_t)(16 * dt + r) * p.cpad + 8 * gq;
+      const uint16_t* ktr = kt + (int64_t)(16 * dt + r) * p.cpad;
       const float* ua = U + r * USTR + 8 * gq;
-      for (int c0 = 0; c0 < n32; c0 += 32) {
-        const f32x4 a0 = *reinterpret_cast<const f32x4*>(ua + c0);
-        const f32x4 a1 = *reinterpret_cast<const f32x4*>(ua + c0 + 4);
-        const u32x4 av = {cvt_pk_bf16(a0[0], a0[1]), cvt_pk_bf16(a0[2], a0[3]),
-                          cvt_pk_bf16(a1[0], a1[1]), cvt_pk_bf16(a1[2], a1[3])};
-        acc = mfma16x16x32(as_bf16x8(av), as_bf16x8(ldg16(ktr + c0)), acc);
+      // four 32-entry steps per round, their gathered loads in flight together
+      for (int cb = 0; cb < n32; cb += 128) {
+        uint16_t kv[4][8];
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            // entries past the list carry du = 0: any listed chunk serves there
+            const int k = min(cb + 32 * st + 8 * gq + i, na - 1);
+            kv[st][i] = cb + 32 * st < n32 ? ktr[L[k]] : (uint16_t)0;
+          }
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const int c0 = cb + 32 * st;
+          if (c0 < n32) {
+            const f32x4 a0 = *reinterpret_cast<const f32x4*>(ua + c0);
+            const f32x4 a1 = *reinterpret_cast<const f32x4*>(ua + c0 + 4);
+            const u32x4 av = {cvt_pk_bf16(a0[0], a0[1]), cvt_pk_bf16(a0[2], a0[3]),
+                              cvt_pk_bf16(a1[0], a1[1]), cvt_pk_bf16(a1[2], a1[3])};
+            u32x4 bv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              bv[i] = (uint32_t)kv[st][2 * i] | ((uint32_t)kv[st][2 * i + 1] << 16);
+            acc = mfma16x16x32(as_bf16x8(av), as_bf16x8(bv), acc);
+          }
+        }
       }
       // lane (gq, r): heads 16 ht + 4 gq + j, dim 16 dt + r
       const float kd = p.kdiag ? bf16_to_f32(kdrow[16 * dt + r]) : 0.f;
@@ -250,25 +315,38 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
   if (p.kdiag && tid < D) p.dkdiag[((int64_t)row * g.Hkv + h) * D + tid] = p.gamma_scale * dkd;
 }
 
-// dk_bar of 64 chunks: rows that route to any of them, in slices over blockIdx.y
+// dk_bar of 64 chunks: rows that route to any of them, in slices over
+// blockIdx.y.  Wave w owns chunks c0 + 16 w .. +15 (their K_bar rows as the B
+// operand of the logits).  The slice's rows with any of the 64 chunks active
+// are compacted from the mask words, and each such row's Q (all G heads, in
+// 16-byte pieces swizzled by head_row_swz), its heads' stored (threshold,
+// softmax sum, rho) and its dp of the 64 chunks stream through a ring of LDS
+// stages by direct global->LDS loads, several rows ahead of the one computed
+// (no plain load in the loop: the compiler would wait for the whole ring).
+// Per row and head tile: u = Q K_bar^T (16x16x32), du from the stored terms,
+// dk_bar^T += du^T Q (16x16x16, Q's transpose by transposing LDS reads).
 template <int D, int HT>
 __global__ __launch_bounds__(256) void kbar_grad_kernel(Geom g, RouteBwdParams p) {
   constexpr int NTH = 256;
   constexpr int G = 16 * HT;
   constexpr int KS = D / 32;
   constexpr int NT = D / 16;
-  constexpr int QROW = D + 8;        // row-major copy, padded
-  constexpr int TROW = G + 4;        // transposed copy, padded (8-byte aligned reads)
-  constexpr int NPC = (G * D / 8 + NTH - 1) / NTH;
-  __shared__ __align__(16) uint16_t Qr[2][G * QROW];
-  __shared__ __align__(16) uint16_t Qt[2][D * TROW];
-  __shared__ float4 Sc[2][G];
+  constexpr int UPH = D / 8;               // 16-byte pieces per head row
+  constexpr int ABYTES = G * D * 2;        // one row's Q
+  constexpr int PPW = ABYTES / 16 / 4;     // pieces per wave per row
+  constexpr int NOP = (PPW + 63) / 64;     // 16-byte loads per wave per row
+  constexpr int PER = NOP + 2;             // + the heads' terms and the chunks' dp
+  constexpr int NSR = 4;                   // ring stages, one row each
+  __shared__ __align__(16) uint8_t Ring[NSR][ABYTES];
+  __shared__ __align__(16) float4 Sc[NSR][G];
+  __shared__ __align__(16) float Dp[NSR][64];
   __shared__ int Rows[NTH];
   __shared__ unsigned long long Words[NTH];
   __shared__ int Wcnt[NTH / 64];
   const int tile = blockIdx.x;
   const int h = blockIdx.z % g.Hkv, s = blockIdx.z / g.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, gq = lane >> 4;
   const SeqInfo si = seq_info(g.cu_seqlens, g.cu_chunks, s, g.max_seqlen, g.B);
   const int len = si.len;
@@ -299,41 +377,73 @@ __global__ __launch_bounds__(256) void kbar_grad_kernel(Geom g, RouteBwdParams p
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kb[ks] = as_bf16x8(ldg16(krow + 32 * ks + 8 * gq));
   }
+  // the operand loads complete here, so that the compiler's own waits for
+  // them do not land in the ring loop
+  wait_vm<0>();
   f32x4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 ra[NPC];
-  float4 rsc = make_float4(0.f, 0.f, 0.f, 0.f);
-  auto fetch = [&](int i) {
-    const int64_t tok = start + i;
+  // one row into ring slot `slot`: every wave issues PER loads
+  const int cpw = min(c0 + 16 * wv + lane, g.C_slots - 1);  // lane < 16: its dp word
+  auto issue = [&](int row, int slot) {
+    const int64_t tok = start + row;
+    const uint32_t base = lds_addr(&Ring[slot][0]);
 #pragma unroll
-    for (int e = 0; e < NPC; ++e) {
-      const int pc = tid + NTH * e;
-      if (pc < G * D / 8)
-        ra[e] = ldg16((const uint16_t*)p.q + (tok * g.Hq + h * G) * (int64_t)D + 8 * pc);
-    }
-    if (tid < G) rsc = p.sc[(int64_t)(h * G + tid) * T + tok];
-  };
-  auto put = [&](int b) {
-#pragma unroll
-    for (int e = 0; e < NPC; ++e) {
-      const int pc = tid + NTH * e;
-      if (pc < G * D / 8) {
-        const int hh = pc / (D / 8), d0 = (pc % (D / 8)) * 8;
-        const u32x4 a = ra[e];
-        *reinterpret_cast<u32x4*>(&Qr[b][hh * QROW + d0]) = a;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          Qt[b][(d0 + 2 * w) * TROW + hh] = (uint16_t)(a[w] & 0xFFFFu);
-          Qt[b][(d0 + 2 * w + 1) * TROW + hh] = (uint16_t)(a[w] >> 16);
-        }
+    for (int e = 0; e < NOP; ++e) {
+      const int pl = 64 * e + lane;  // piece of this wave
+      if (pl < PPW) {
+        const int u = wv * PPW + pl;
+        const int j = u / UPH, pc = (u % UPH) ^ head_row_swz<D>(j);
+        lds_dma16((const uint16_t*)p.q + (tok * g.Hq + h * G + j) * (int64_t)D + 8 * pc,
+                  __builtin_amdgcn_readfirstlane(base + (uint32_t)(16 * (wv * PPW + 64 * e))));
       }
     }
-    if (tid < G) Sc[b][tid] = rsc;
+    if (lane < G / 4)
+      lds_dma16(p.sc + (int64_t)(h * G + (G / 4) * wv + lane) * T + tok,
+                __builtin_amdgcn_readfirstlane(lds_addr(&Sc[slot][(G / 4) * wv])));
+    if (lane < 16)
+      lds_dma4(p.db + ((int64_t)h * T + tok) * g.C_slots + cpw,
+               __builtin_amdgcn_readfirstlane(lds_addr(&Dp[slot][16 * wv])));
+  };
+  // transposing reads: lane (gq, r) points at head 16 ht + 4 gq + r / 4,
+  // dims 16 nt + 4 (r % 4) .. +3 and receives dim 16 nt + r of heads
+  // 16 ht + 4 gq .. +3
+  auto compute = [&](int slot, unsigned long long wbits) {
+    lds_u8* qs = (lds_u8*)&Ring[slot][0];
+    // dp of this lane's chunk (0 where the chunk is not active)
+    const bool act = (wbits >> (16 * wv + r)) & 1ull;
+    const float dp = act ? Dp[slot][16 * wv + r] : 0.f;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const int j = 16 * ht + r;
+      f32x4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 qa = lds_read16(qs + 16 * (j * UPH + ((4 * ks + gq) ^ head_row_swz<D>(j))));
+        u = mfma16x16x32(as_bf16x8(qa), kb[ks], u);
+      }
+      // lane (gq, r): heads 16 ht + 4 gq + jj, chunk myc
+      float du[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float4 t = Sc[slot][16 * ht + 4 * gq + jj];
+        const float x = u[jj] * gs;
+        const float rr = smax ? exp2f((x - t.x) * kLog2e) / t.y : pow_pos(x * am1 - t.x, er);
+        du[jj] = act ? rr * (dp - t.z) : 0.f;
+      }
+      const u32x2 da = {cvt_pk_bf16(du[0], du[1]), cvt_pk_bf16(du[2], du[3])};
+      const int jt = 16 * ht + 4 * gq + (r >> 2);
+      const int tb = 16 * jt * UPH + 16 * ((r & 3) >> 1) + 8 * (r & 1);
+      const int tx = head_row_swz<D>(jt);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const s16x4 qb = lds_read_tr8(qs + tb + 16 * ((2 * nt) ^ tx));
+        acc[nt] = mfma16x16x16(as_s16x4(da), qb, acc[nt]);
+      }
+    }
   };
 
-  int parity = 0;
   for (int r0 = rlo; r0 < rhi; r0 += NTH) {
     // rows r0 .. r0+255 with any of the tile's chunks active, compacted in order
     const int i = r0 + tid;
@@ -355,45 +465,19 @@ __global__ __launch_bounds__(256) void kbar_grad_kernel(Geom g, RouteBwdParams p
       Words[at] = word;
     }
     __syncthreads();
+    for (int k = 0; k < NSR - 1 && k < total; ++k) issue(Rows[k], k);
     for (int k = 0; k < total; ++k) {
-      const int b = parity;
-      parity ^= 1;
-      if (k == 0) fetch(Rows[0]);
-      put(b);
+      // this wave's loads of row k have landed once at most the later rows'
+      // loads are outstanding; the barrier then covers every wave's
+      const int ahead = min(NSR - 2, total - 1 - k);
+      if (ahead >= 2) wait_vm<2 * PER>();
+      else if (ahead == 1) wait_vm<PER>();
+      else wait_vm<0>();
       __syncthreads();
-      const int row = Rows[k];
-      const unsigned long long wbits = Words[k];
-      if (k + 1 < total) fetch(Rows[k + 1]);  // in flight while this row computes
-      const int64_t tok = start + row;
-      // dp of this lane's chunk (0 where the chunk is not active)
-      const bool act = (wbits >> (16 * wv + r)) & 1ull;
-      const float dp = act ? p.db[((int64_t)h * T + tok) * g.C_slots + myc] : 0.f;
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) {
-        f32x4 u = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const u32x4 qa = *reinterpret_cast<const u32x4*>(&Qr[b][(16 * ht + r) * QROW + 32 * ks + 8 * gq]);
-          u = mfma16x16x32(as_bf16x8(qa), kb[ks], u);
-        }
-        // lane (gq, r): heads 16 ht + 4 gq + j, chunk myc
-        float du[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float4 t = Sc[b][16 * ht + 4 * gq + j];
-          const float x = u[j] * gs;
-          const float rr = smax ? exp2f((x - t.x) * kLog2e) / t.y : pow_pos(x * am1 - t.x, er);
-          du[j] = act ? rr * (dp - t.z) : 0.f;
-        }
-        const u32x2 da = {cvt_pk_bf16(du[0], du[1]), cvt_pk_bf16(du[2], du[3])};
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const u32x2 qb = *reinterpret_cast<const u32x2*>(&Qt[b][(16 * nt + r) * TROW + 16 * ht + 4 * gq]);
-          acc[nt] = mfma16x16x16(as_s16x4(da), as_s16x4(qb), acc[nt]);
-        }
-      }
+      if (k + NSR - 1 < total) issue(Rows[k + NSR - 1], (k + NSR - 1) % NSR);
+      compute(k % NSR, Words[k]);
     }
-    __syncthreads();  // Rows and Words are refilled
+    __syncthreads();  // the ring, Rows and Words are refilled
   }
   // lane (gq, r) holds dk_bar of chunks c0 + 16 wv + 4 gq + j, dims 16 nt + r
 #pragma unroll
