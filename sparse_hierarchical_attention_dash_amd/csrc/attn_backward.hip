@@ -143,37 +143,49 @@ __global__ __launch_bounds__(256 / KT) void bwd_dkdv_kernel(Geom g, BwdParams p,
       adv[kt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   const float sl2 = p.scale * kLog2e;
-  const uint16_t* qg = (const uint16_t*)p.q;
-  const uint16_t* dg = (const uint16_t*)p.dout;
-
-  // one row into ring slot `slot`: thread tid loads units tid + 256 e
-  auto issue = [&](int row, int slot) {
-    const int64_t tok = si.start + row;
-    const uint32_t base = lds_addr(Ring) + (uint32_t)(slot * C::SBYTES);
+  // per-thread staging: piece e of this thread is 16 bytes of head j's row of
+  // Q (or dO), at a fixed byte offset from the row's first head; a wave's
+  // pieces lie all in Q or all in dO
+  uint32_t poff[C::NUT];
+  int parr[C::NUT];
 #pragma unroll
-    for (int e = 0; e < C::NUT; ++e) {
-      const int U = tid + NTH * e;
-      const int arr = U / C::AU, u = U % C::AU;
-      // row-major: slot u % UPH of head j holds the piece head_row_swz places there
-      const int j = u / UPH, pc = (u % UPH) ^ head_row_swz<D>(j);
-      const uint16_t* src = (arr == 0 ? qg : dg) + (tok * g.Hq + h * G + j) * (int64_t)D + 8 * pc;
-      lds_dma16(src, __builtin_amdgcn_readfirstlane(base + (uint32_t)(16 * (NTH * e + 64 * wv))));
-    }
-    if (lane < 2 * G) {
-      const float* src = lane < G ? p.lse + (int64_t)(h * G + lane) * T + tok
-                                  : p.delta + (int64_t)(h * G + lane - G) * T + tok;
-      lds_dma4(src, __builtin_amdgcn_readfirstlane(lds_addr(&Sc[slot][wv][0])));
-    }
+  for (int e = 0; e < C::NUT; ++e) {
+    const int U = tid + NTH * e;
+    const int u = U % C::AU;
+    // slot u % UPH of head j holds the piece head_row_swz places there
+    const int j = u / UPH, pc = (u % UPH) ^ head_row_swz<D>(j);
+    poff[e] = (uint32_t)((j * D + 8 * pc) * 2);
+    parr[e] = __builtin_amdgcn_readfirstlane(U / C::AU);
+  }
+  // lanes < 2G: the LSE (lanes < G) or D of head lane % G, for token 0
+  const float* scsrc = lane < G ? p.lse + (int64_t)(h * G + lane) * T + si.start
+                                : p.delta + (int64_t)(h * G + (lane & (G - 1))) * T + si.start;
+  const float* bzsrc = p.log_prior + ((int64_t)h * T + si.start) * g.C_slots + c;
+  const int64_t qrs = (int64_t)g.Hq * D * 2;  // bytes between tokens of Q and dO
+
+  // one row (wave-uniform) into ring slot `slot`: thread tid loads units
+  // tid + 256 e
+  auto issue = [&](int row, int slot) {
+    const uint32_t base = lds_addr(Ring) + (uint32_t)(slot * C::SBYTES);
+    const int64_t rb = (si.start + row) * qrs + (int64_t)h * G * D * 2;
+#pragma unroll
+    for (int e = 0; e < C::NUT; ++e)
+      lds_dma16s((const uint8_t*)(parr[e] == 0 ? p.q : p.dout) + rb, poff[e],
+                 __builtin_amdgcn_readfirstlane(base + (uint32_t)(16 * (NTH * e + 64 * wv))));
+    if (lane < 2 * G)
+      lds_dma4(scsrc + row, __builtin_amdgcn_readfirstlane(lds_addr(&Sc[slot][wv][0])));
     if (lane == 0)  // the bias (any valid word for rows of the block's own chunk)
-      lds_dma4(p.log_prior + ((int64_t)h * T + tok) * g.C_slots + c,
+      lds_dma4(bzsrc + (int64_t)row * g.C_slots,
                __builtin_amdgcn_readfirstlane(lds_addr(&Bz[slot][wv][0])));
   };
 
+  // one staged row (wave-uniform).  A row of the block's own chunk sees key
+  // j iff j <= row (row <= the sequence's last key), with bias 0
   auto compute = [&](int slot, int row) {
+    const bool own = row < cend;
     const uint8_t* st = Ring + slot * C::SBYTES;
     lds_u8* Qs = (lds_u8*)(st);
     lds_u8* Ds = (lds_u8*)(st + C::ABYTES);
-    const bool own = row < cend;  // the block's own chunk: keys after the row are unseen
     const float bz = own ? 0.f : Bz[slot][wv][0] * kLog2e;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
@@ -205,7 +217,6 @@ __global__ __launch_bounds__(256 / KT) void bwd_dkdv_kernel(Geom g, BwdParams p,
           const int hh = 16 * ht + 4 * gq + jj;
           float e = __builtin_amdgcn_exp2f(fmaf(sacc[kt][jj], sl2, bz - Sc[slot][wv][hh] * kLog2e));
           if (own) e = mykey[kt] <= row ? e : 0.f;
-          e = mykey[kt] <= kmax ? e : 0.f;
           pv[jj] = e;
           ds[jj] = e * (pacc[kt][jj] - Sc[slot][wv][G + hh]);
         }
@@ -231,7 +242,6 @@ __global__ __launch_bounds__(256 / KT) void bwd_dkdv_kernel(Geom g, BwdParams p,
       }
     }
   };
-
   int seen = 0;  // rows this workgroup visited
   for (int r0 = rlo; r0 < rhi; r0 += NR) {
     // ---- rows r0 .. r0+1023 that see the block, compacted in order
@@ -267,7 +277,8 @@ __global__ __launch_bounds__(256 / KT) void bwd_dkdv_kernel(Geom g, BwdParams p,
     __syncthreads();
     seen += total;
 
-    for (int k = 0; k < NS - 1 && k < total; ++k) issue(Rows[k], k);
+    for (int k = 0; k < NS - 1 && k < total; ++k)
+      issue(__builtin_amdgcn_readfirstlane(Rows[k]), k);
     for (int k = 0; k < total; ++k) {
       // this wave's loads of row k have landed once at most the later
       // stages' loads are outstanding; the barrier then covers every wave's
@@ -276,8 +287,9 @@ __global__ __launch_bounds__(256 / KT) void bwd_dkdv_kernel(Geom g, BwdParams p,
       else if (ahead == 1) wait_vm<C::PER>();
       else wait_vm<0>();
       __syncthreads();
-      if (k + NS - 1 < total) issue(Rows[k + NS - 1], (k + NS - 1) % NS);
-      compute(k % NS, Rows[k]);
+      if (k + NS - 1 < total)
+        issue(__builtin_amdgcn_readfirstlane(Rows[k + NS - 1]), (k + NS - 1) % NS);
+      compute(k % NS, __builtin_amdgcn_readfirstlane(Rows[k]));
     }
     __syncthreads();  // the ring and Rows are refilled
   }
