@@ -65,28 +65,24 @@ __global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ x, int64_
 }
 
 constexpr int kDkdvSlice = 4096;  // rows per workgroup of bwd_dkdv_kernel
-constexpr int kDkdvTiles = 1;     // 16-key tiles per wave of bwd_dkdv_kernel (2: slower)
 
-template <int D, int HT, int KT>
+template <int D, int HT>
 struct DkdvCfg {
-  static constexpr int NW = 4 / KT;                    // waves: KT 16-key tiles each
+  static constexpr int NW = 4;                         // waves: one 16-key tile each
   static constexpr int NTH = 64 * NW;
   static constexpr int G = 16 * HT;
-  static constexpr int NS = HT == 1 ? 4 : 3;           // ring stages, one row each
+  static constexpr int NS = 4;                         // ring stages, one row each
   static constexpr int ABYTES = G * D * 2;             // one array of one row
   static constexpr int SBYTES = 2 * ABYTES;            // Q, dO
   static constexpr int AU = ABYTES / 16;               // 16-byte units per array
   static constexpr int NUT = 2 * AU / NTH;             // unit loads per thread per stage
-  static constexpr int PER = NUT + 2;                  // loads per wave per stage
   static_assert(2 * AU % NTH == 0, "units per stage");
 };
 
-
-template <int D, int HT, int KT>
-__global__ __launch_bounds__(256 / KT) void bwd_dkdv_kernel(Geom g, BwdParams p, float* dk,
-                                                            float* dv) {
-  using C = DkdvCfg<D, HT, KT>;
-  static_assert(C::NTH == 256 / KT, "launch bounds");
+template <int D, int HT>
+__global__ __launch_bounds__(256, HT == 1 ? 3 : 2) void bwd_dkdv_kernel(Geom g, BwdParams p, float* dk,
+                                                       float* dv) {
+  using C = DkdvCfg<D, HT>;
   constexpr int G = C::G;
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
@@ -117,31 +113,26 @@ __global__ __launch_bounds__(256 / KT) void bwd_dkdv_kernel(Geom g, BwdParams p,
   const int64_t T = g.T;
   const unsigned long long* __restrict__ mask = (const unsigned long long*)p.mask;
 
-  // this wave's KT tiles of 16 keys: K and V rows as the B operand of Q K^T
-  // and dO V^T
-  int mykey[KT];
-  bf16x8 kf[KT][KS], vf[KT][KS];
-#pragma unroll
-  for (int kt = 0; kt < KT; ++kt) {
-    mykey[kt] = key0 + 16 * (KT * wv + kt) + r;
-    const int64_t row = ((si.start + min(mykey[kt], kmax)) * g.Hkv + h) * (int64_t)D;
+  // this wave's 16 keys: K and V rows as the B operand of Q K^T and dO V^T
+  const int mykey = key0 + 16 * wv + r;
+  bf16x8 kf[KS], vf[KS];
+  {
+    const int64_t row = ((si.start + min(mykey, kmax)) * g.Hkv + h) * (int64_t)D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      kf[kt][ks] = as_bf16x8(ldg16((const uint16_t*)p.k + row + 32 * ks + 8 * gq));
-      vf[kt][ks] = as_bf16x8(ldg16((const uint16_t*)p.v + row + 32 * ks + 8 * gq));
+      kf[ks] = as_bf16x8(ldg16((const uint16_t*)p.k + row + 32 * ks + 8 * gq));
+      vf[ks] = as_bf16x8(ldg16((const uint16_t*)p.v + row + 32 * ks + 8 * gq));
     }
   }
   // the operand loads complete here, so that the compiler's own waits for them
   // do not land inside the ring loop, where they would also wait for the ring
   wait_vm<0>();
-  f32x4 adk[KT][DT], adv[KT][DT];
+  f32x4 adk[DT], adv[DT];
 #pragma unroll
-  for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      adk[kt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      adv[kt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+  for (int dt = 0; dt < DT; ++dt) {
+    adk[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    adv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   const float sl2 = p.scale * kLog2e;
   // per-thread staging: piece e of this thread is 16 bytes of head j's row of
   // Q (or dO), at a fixed byte offset from the row's first head; a wave's
@@ -179,69 +170,72 @@ __global__ __launch_bounds__(256 / KT) void bwd_dkdv_kernel(Geom g, BwdParams p,
                __builtin_amdgcn_readfirstlane(lds_addr(&Bz[slot][wv][0])));
   };
 
-  // one staged row (wave-uniform).  A row of the block's own chunk sees key
-  // j iff j <= row (row <= the sequence's last key), with bias 0
-  auto compute = [&](int slot, int row) {
+  // S and dP of one staged row and head tile, then P and dS packed as the B
+  // operand's half: lane (gq, r) holds heads 16 ht + 4 gq + jj, key mykey.  A
+  // row of the block's own chunk sees key j iff j <= row (row <= the
+  // sequence's last key), with bias 0.
+  auto row_terms = [&](int slot, int row, int ht, u32x2& pb, u32x2& sb) {
     const bool own = row < cend;
-    const uint8_t* st = Ring + slot * C::SBYTES;
-    lds_u8* Qs = (lds_u8*)(st);
-    lds_u8* Ds = (lds_u8*)(st + C::ABYTES);
+    lds_u8* Qs = (lds_u8*)(Ring + slot * C::SBYTES);
+    lds_u8* Ds = Qs + C::ABYTES;
     const float bz = own ? 0.f : Bz[slot][wv][0] * kLog2e;
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f}, pacc = {0.f, 0.f, 0.f, 0.f};
+    const int j = 16 * ht + r;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int off = 16 * (j * UPH + ((4 * ks + gq) ^ head_row_swz<D>(j)));
+      sacc = mfma16x16x32(as_bf16x8(lds_read16(Qs + off)), kf[ks], sacc);
+      pacc = mfma16x16x32(as_bf16x8(lds_read16(Ds + off)), vf[ks], pacc);
+    }
+    float pv[4], ds[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int hh = 16 * ht + 4 * gq + jj;
+      float e = __builtin_amdgcn_exp2f(fmaf(sacc[jj], sl2, bz - Sc[slot][wv][hh] * kLog2e));
+      if (own) e = mykey <= row ? e : 0.f;
+      pv[jj] = e;
+      ds[jj] = e * (pacc[jj] - Sc[slot][wv][G + hh]);
+    }
+    pb = u32x2{cvt_pk_bf16(pv[0], pv[1]), cvt_pk_bf16(pv[2], pv[3])};
+    sb = u32x2{cvt_pk_bf16(ds[0], ds[1]), cvt_pk_bf16(ds[2], ds[3])};
+  };
+  // two staged rows per step (the second absent past the list's end): the
+  // dV and dK products contract over (row, head), 32 at a time.  k-slot
+  // 8 gq + 4 x + jj is head 16 ht + 4 gq + jj of row x; the transposing reads
+  // (lane (gq, r) pointing at head 16 ht + 4 gq + r / 4, dims 16 dt + 4 (r % 4)
+  // .. +3) give lane (gq, r) dim 16 dt + r of those heads.
+  auto compute_pair = [&](int sa, int ra, int sbs, int rb) {
+    const bool two = rb >= 0;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-      f32x4 sacc[KT], pacc[KT];
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        pacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-      const int j = 16 * ht + r;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        // one read of the row's Q and dO fragments serves the wave's KT key tiles
-        const int off = 16 * (j * UPH + ((4 * ks + gq) ^ head_row_swz<D>(j)));
-        const bf16x8 qf = as_bf16x8(lds_read16(Qs + off)), df = as_bf16x8(lds_read16(Ds + off));
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-          sacc[kt] = mfma16x16x32(qf, kf[kt][ks], sacc[kt]);
-          pacc[kt] = mfma16x16x32(df, vf[kt][ks], pacc[kt]);
-        }
-      }
-      // lane (gq, r): heads 16 ht + 4 gq + j, key mykey[kt]
-      u32x2 pb[KT], sb[KT];
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        float pv[4], ds[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int hh = 16 * ht + 4 * gq + jj;
-          float e = __builtin_amdgcn_exp2f(fmaf(sacc[kt][jj], sl2, bz - Sc[slot][wv][hh] * kLog2e));
-          if (own) e = mykey[kt] <= row ? e : 0.f;
-          pv[jj] = e;
-          ds[jj] = e * (pacc[kt][jj] - Sc[slot][wv][G + hh]);
-        }
-        pb[kt] = u32x2{cvt_pk_bf16(pv[0], pv[1]), cvt_pk_bf16(pv[2], pv[3])};
-        sb[kt] = u32x2{cvt_pk_bf16(ds[0], ds[1]), cvt_pk_bf16(ds[2], ds[3])};
-      }
-      // transposing reads: lane (gq, r) points at head 16 ht + 4 gq + r / 4,
-      // dims 16 dt + 4 (r % 4) .. +3, and receives dim 16 dt + r of heads
-      // 16 ht + 4 gq .. +3 (the A operand of X^T)
+      u32x2 pa, da, pbb = {0u, 0u}, dbb = {0u, 0u};
+      row_terms(sa, ra, ht, pa, da);
+      if (two) row_terms(sbs, rb, ht, pbb, dbb);
+      const u32x4 pb4 = {pa[0], pa[1], pbb[0], pbb[1]};
+      const u32x4 sb4 = {da[0], da[1], dbb[0], dbb[1]};
+      lds_u8* Qa = (lds_u8*)(Ring + sa * C::SBYTES);
+      lds_u8* Qb = (lds_u8*)(Ring + sbs * C::SBYTES);
       const int jt = 16 * ht + 4 * gq + (r >> 2);
       const int tbase = 16 * jt * UPH + 8 * (r & 1);
       const int tsw = head_row_swz<D>(jt), tpc = (r & 3) >> 1;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int off = tbase + 16 * ((2 * dt + tpc) ^ tsw);
-        const s16x4 ta = lds_read_tr8(Ds + off);
-        const s16x4 tq = lds_read_tr8(Qs + off);
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-          adv[kt][dt] = mfma16x16x16(ta, as_s16x4(pb[kt]), adv[kt][dt]);
-          adk[kt][dt] = mfma16x16x16(tq, as_s16x4(sb[kt]), adk[kt][dt]);
+        const u32x2 ta0 = __builtin_bit_cast(u32x2, lds_read_tr8(Qa + C::ABYTES + off));
+        const u32x2 tq0 = __builtin_bit_cast(u32x2, lds_read_tr8(Qa + off));
+        u32x2 ta1 = {0u, 0u}, tq1 = {0u, 0u};
+        if (two) {
+          ta1 = __builtin_bit_cast(u32x2, lds_read_tr8(Qb + C::ABYTES + off));
+          tq1 = __builtin_bit_cast(u32x2, lds_read_tr8(Qb + off));
         }
+        const u32x4 ta = {ta0[0], ta0[1], ta1[0], ta1[1]};
+        const u32x4 tq = {tq0[0], tq0[1], tq1[0], tq1[1]};
+        adv[dt] = mfma16x16x32(as_bf16x8(ta), as_bf16x8(pb4), adv[dt]);
+        adk[dt] = mfma16x16x32(as_bf16x8(tq), as_bf16x8(sb4), adk[dt]);
       }
     }
   };
+
   int seen = 0;  // rows this workgroup visited
   for (int r0 = rlo; r0 < rhi; r0 += NR) {
     // ---- rows r0 .. r0+1023 that see the block, compacted in order
@@ -277,35 +271,32 @@ __global__ __launch_bounds__(256 / KT) void bwd_dkdv_kernel(Geom g, BwdParams p,
     __syncthreads();
     seen += total;
 
-    for (int k = 0; k < NS - 1 && k < total; ++k)
-      issue(__builtin_amdgcn_readfirstlane(Rows[k]), k);
-    for (int k = 0; k < total; ++k) {
-      // this wave's loads of row k have landed once at most the later
-      // stages' loads are outstanding; the barrier then covers every wave's
-      const int ahead = min(NS - 2, total - 1 - k);
-      if (ahead >= 2) wait_vm<2 * C::PER>();
-      else if (ahead == 1) wait_vm<C::PER>();
-      else wait_vm<0>();
+    // rows 2q and 2q + 1 in slots (2q) % 4 and (2q + 1) % 4: a step waits for
+    // its two rows (the only loads in flight), and at its barrier every wave
+    // has left the previous step's slots, which then take the next two rows
+    issue(__builtin_amdgcn_readfirstlane(Rows[0]), 0);
+    if (total > 1) issue(__builtin_amdgcn_readfirstlane(Rows[1]), 1);
+    for (int k = 0; k < total; k += 2) {
+      wait_vm<0>();
       __syncthreads();
-      if (k + NS - 1 < total)
-        issue(__builtin_amdgcn_readfirstlane(Rows[k + NS - 1]), (k + NS - 1) % NS);
-      compute(k % NS, __builtin_amdgcn_readfirstlane(Rows[k]));
+#pragma unroll 1
+      for (int n = k + 2; n < min(k + 4, total); ++n)
+        issue(__builtin_amdgcn_readfirstlane(Rows[n]), n & 3);
+      compute_pair(k & 3, __builtin_amdgcn_readfirstlane(Rows[k]), (k + 1) & 3,
+                   k + 1 < total ? __builtin_amdgcn_readfirstlane(Rows[k + 1]) : -1);
     }
     __syncthreads();  // the ring and Rows are refilled
   }
   // ---- add this slice's sums for the wave's keys: lane (gq, r) holds dims
   // 16 dt + 4 gq .. +3 of key mykey
+  if (seen > 0 && mykey <= kmax) {
+    const int64_t row = ((si.start + mykey) * g.Hkv + h) * (int64_t)D;
 #pragma unroll
-  for (int kt = 0; kt < KT; ++kt) {
-    if (seen > 0 && mykey[kt] <= kmax) {
-      const int64_t row = ((si.start + mykey[kt]) * g.Hkv + h) * (int64_t)D;
+    for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          atomicAdd(dk + row + 16 * dt + 4 * gq + j, adk[kt][dt][j] * p.scale);
-          atomicAdd(dv + row + 16 * dt + 4 * gq + j, adv[kt][dt][j]);
-        }
+      for (int j = 0; j < 4; ++j) {
+        atomicAdd(dk + row + 16 * dt + 4 * gq + j, adk[dt][j] * p.scale);
+        atomicAdd(dv + row + 16 * dt + 4 * gq + j, adv[dt][j]);
       }
     }
   }
@@ -345,8 +336,8 @@ hipError_t launch_bwd_dkdv(const Geom& g, const BwdParams& p, float* dk, float* 
   dim3 grid((g.max_seqlen + 63) / 64, (g.max_seqlen + kDkdvSlice - 1) / kDkdvSlice,
             g.num_seqs * g.Hkv);
 #define DASH_BK(DD, HH)                                                              \
-  hipLaunchKernelGGL((bwd_dkdv_kernel<DD, HH, kDkdvTiles>), grid,                      \
-                     dim3(DkdvCfg<DD, HH, kDkdvTiles>::NTH), 0, st, g, p, dk, dv)
+  hipLaunchKernelGGL((bwd_dkdv_kernel<DD, HH>), grid, dim3(DkdvCfg<DD, HH>::NTH), 0, st, g, p, \
+                     dk, dv)
   if (g.G == 16) {
     if (g.D == 64) DASH_BK(64, 1); else DASH_BK(128, 1);
   } else {
