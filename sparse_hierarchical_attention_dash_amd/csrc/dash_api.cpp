@@ -222,7 +222,7 @@ BackwardWs backward_ws(const Geom& g) {
 // per-head terms of the routing backward.
 struct PrefillBwdWs {
   BackwardWs a;
-  size_t kbar, mask, logp, tau, db, sc, kbt, dkb, kdiag, dkdiag, flags, total;
+  size_t kbar, mask, logp, tau, db, sc, kbt, dkb, kdiag, dkdiag, flags, rbf, total;
 };
 PrefillBwdWs prefill_bwd_ws(const Geom& g) {
   PrefillBwdWs w{};
@@ -250,6 +250,8 @@ PrefillBwdWs prefill_bwd_ws(const Geom& g) {
   o += align_up((size_t)g.T * g.Hkv * g.D * 4);
   w.flags = o;  // the routing's row-group flags (the forward's routing kernels)
   o += flag_bytes(g);
+  w.rbf = o;    // the routing backward's rows with more entries than its first pass holds
+  o += align_up((size_t)dash::route_flag_stride(g.T) * g.Hkv);
   w.total = o;
   return w;
 }
@@ -945,6 +947,7 @@ dash_status dash_attn_prefill_backward(const dash_shape* shape, const void* q, c
   rb.kbt = reinterpret_cast<const uint16_t*>(at(workspace, w.kbt));
   rb.dkb = reinterpret_cast<float*>(at(workspace, w.dkb));
   rb.cpad = dash::route_bwd_cpad(g);
+  rb.rflags = reinterpret_cast<uint8_t*>(at(workspace, w.rbf));
   rb.kdiag = kdiag;
   rb.dkdiag = reinterpret_cast<float*>(at(workspace, w.dkdiag));
   DASH_HIP(dash::launch_zero(dqbar, (int64_t)g.Hkv * g.D, s));

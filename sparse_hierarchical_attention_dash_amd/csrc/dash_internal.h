@@ -170,6 +170,7 @@ struct RouteBwdParams {
   float* dkdiag = nullptr;              // [T, Hkv, D] fp32, their gradient (written)
   float* dkb = nullptr;                 // [T/B rows, Hkv, D] fp32 dk_bar (zeroed first)
   int cpad = 0;                         // route_bwd_cpad(g)
+  uint8_t* rflags = nullptr;            // [Hkv, route_flag_stride(T)]: rows left to the wide pass
   float alpha = 1.5f;
   const float* alpha_per_seq = nullptr; // [num_seqs] or null (varlen)
   float gamma_scale = 1.f;              // gamma * s

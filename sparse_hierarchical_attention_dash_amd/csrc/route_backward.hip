@@ -67,8 +67,11 @@ __global__ __launch_bounds__(256) void kbar_t_kernel(Geom g, const uint16_t* __r
   kbt[idx] = v;
 }
 
+// wide = 0: the rows whose entries fit CP (every row's flag written: 1 for a
+// row left to the wide pass); wide = 1: only the rows flagged so.
 template <int D, int CP>
-__global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p, int row0) {
+__global__ __launch_bounds__(256, 7) void route_bwd_kernel(Geom g, RouteBwdParams p, int row0,
+                                                        int row1, int wide) {
   constexpr int NTH = 256;
   constexpr int KS = D / 32;
   constexpr int USTR = CP + 16;
@@ -80,6 +83,7 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
   __shared__ float Hp[16][2];      // per head: threshold (x units) or max u; softmax sum
   __shared__ float Dd[16];         // per head: du of the own-chunk entry
   const int row = row0 + (int)blockIdx.x, h = blockIdx.y;
+  if (row >= row1) return;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = lane & 15, gq = lane >> 4;
   const int64_t T = g.T;
@@ -90,7 +94,10 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
   const int n = pos / g.B;
   const int G = g.G;
   float4* sc = p.sc;
+  uint8_t* rflag = p.rflags + (int64_t)h * route_flag_stride(T) + row;
+  if (wide && *rflag == 0) return;
   if (n == 0) {
+    if (tid == 0) *rflag = 0;
     if (tid < G) sc[(int64_t)(h * G + tid) * T + row] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (p.kdiag && tid < D) p.dkdiag[((int64_t)row * g.Hkv + h) * D + tid] = 0.f;
     return;
@@ -121,13 +128,13 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
     if (tid < nw) {
       int o = inc - cnt;
       if (smax) {
-        for (int b = 0; b < cnt; ++b) {
+        for (int b = 0; b < cnt && o + b < CP; ++b) {
           L[o + b] = (uint16_t)(64 * tid + b);
           On[o + b] = (uint8_t)((wd >> b) & 1ull);
         }
       } else {
         unsigned long long v = wd;
-        while (v) {
+        while (v && o < CP) {  // (a longer list leaves the row to the wide pass)
           L[o] = (uint16_t)(64 * tid + __ffsll((long long)v) - 1);
           On[o++] = 1;
           v &= v - 1;
@@ -137,6 +144,11 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
   }
   __syncthreads();
   const int na = Wpre[nw];                  // listed chunks
+  if (!wide) {
+    // more entries than this pass holds: left to the wide pass
+    if (tid == 0) *rflag = na > CP ? 1 : 0;
+    if (na > CP) return;
+  }
   const int ns = p.kdiag ? na + 1 : na;     // entries
   const int n32 = (na + 31) & ~31;
   const uint16_t* kdrow = (const uint16_t*)p.kdiag + ((int64_t)row * g.Hkv + h) * D;
@@ -148,27 +160,17 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qa[ks] = as_bf16x8(ldg16(qrow + 32 * ks + 8 * gq));
     const int nct = (ns + 15) >> 4;
-    // two entry tiles per round, their summary loads in flight together
-    for (int ct0 = wv; ct0 < nct; ct0 += 8) {
-      u32x4 kf[2][KS];
+    for (int ct = wv; ct < nct; ct += 4) {
+      const int k = min(ct * 16 + r, ns - 1);
+      const uint16_t* krow =
+          k == na ? kdrow : (const uint16_t*)p.kbar + (((kb0 + L[k]) * g.Hkv + h) * (int64_t)D);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int k = min((ct0 + 4 * e) * 16 + r, ns - 1);
-        const uint16_t* krow =
-            k == na ? kdrow : (const uint16_t*)p.kbar + (((kb0 + L[k]) * g.Hkv + h) * (int64_t)D);
+      for (int ks = 0; ks < KS; ++ks)
+        acc = mfma16x16x32(qa[ks], as_bf16x8(ldg16(krow + 32 * ks + 8 * gq)), acc);
+      if (ct * 16 + r < ns) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kf[e][ks] = ldg16(krow + 32 * ks + 8 * gq);
-      }
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int ct = ct0 + 4 * e;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(qa[ks], as_bf16x8(kf[e][ks]), acc);
-        if (ct * 16 + r < ns) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) U[(4 * gq + j) * USTR + ct * 16 + r] = acc[j] * p.gamma_scale;
-        }
+        for (int j = 0; j < 4; ++j) U[(4 * gq + j) * USTR + ct * 16 + r] = acc[j] * p.gamma_scale;
       }
     }
   };
@@ -269,32 +271,20 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(Geom g, RouteBwdParams p
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       const uint16_t* ktr = kt + (int64_t)(16 * dt + r) * p.cpad;
       const float* ua = U + r * USTR + 8 * gq;
-      // four 32-entry steps per round, their gathered loads in flight together
-      for (int cb = 0; cb < n32; cb += 128) {
-        uint16_t kv[4][8];
+      for (int c0 = 0; c0 < n32; c0 += 32) {
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(ua + c0);
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(ua + c0 + 4);
+        const u32x4 av = {cvt_pk_bf16(a0[0], a0[1]), cvt_pk_bf16(a0[2], a0[3]),
+                          cvt_pk_bf16(a1[0], a1[1]), cvt_pk_bf16(a1[2], a1[3])};
+        // entries past the list carry du = 0: any listed chunk serves there
+        u32x4 bv;
 #pragma unroll
-        for (int st = 0; st < 4; ++st)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            // entries past the list carry du = 0: any listed chunk serves there
-            const int k = min(cb + 32 * st + 8 * gq + i, na - 1);
-            kv[st][i] = cb + 32 * st < n32 ? ktr[L[k]] : (uint16_t)0;
-          }
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const int c0 = cb + 32 * st;
-          if (c0 < n32) {
-            const f32x4 a0 = *reinterpret_cast<const f32x4*>(ua + c0);
-            const f32x4 a1 = *reinterpret_cast<const f32x4*>(ua + c0 + 4);
-            const u32x4 av = {cvt_pk_bf16(a0[0], a0[1]), cvt_pk_bf16(a0[2], a0[3]),
-                              cvt_pk_bf16(a1[0], a1[1]), cvt_pk_bf16(a1[2], a1[3])};
-            u32x4 bv;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              bv[i] = (uint32_t)kv[st][2 * i] | ((uint32_t)kv[st][2 * i + 1] << 16);
-            acc = mfma16x16x32(as_bf16x8(av), as_bf16x8(bv), acc);
-          }
+        for (int i = 0; i < 4; ++i) {
+          const int k0 = min(c0 + 8 * gq + 2 * i, na - 1);
+          const int k1 = min(c0 + 8 * gq + 2 * i + 1, na - 1);
+          bv[i] = (uint32_t)ktr[L[k0]] | ((uint32_t)ktr[L[k1]] << 16);
         }
+        acc = mfma16x16x32(as_bf16x8(av), as_bf16x8(bv), acc);
       }
       // lane (gq, r): heads 16 ht + 4 gq + j, dim 16 dt + r
       const float kd = p.kdiag ? bf16_to_f32(kdrow[16 * dt + r]) : 0.f;
@@ -673,6 +663,8 @@ __global__ __launch_bounds__(256) void diag_sum_bwd_kernel(Geom g, RouteBwdParam
   }
 }
 
+constexpr int kRbCap = 256;  // entries of route_bwd_kernel's first pass
+
 int route_bwd_cpad(const Geom& g) { return ((g.max_seqlen / g.B) + 31) & ~31; }
 
 hipError_t launch_route_bwd(const Geom& g, const RouteBwdParams& p, hipStream_t st) {
@@ -683,15 +675,17 @@ hipError_t launch_route_bwd(const Geom& g, const RouteBwdParams& p, hipStream_t 
     hipLaunchKernelGGL(kbar_t_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, g,
                        (const uint16_t*)p.kbar, const_cast<uint16_t*>(p.kbt), p.cpad);
   }
-  // rows by range of routable chunks (one sequence): a row at position i has
-  // floor(i/B) of them, so the rows below CP*B fit the CP-wide variant (less
-  // LDS, more workgroups per CU); the longest rows first
-  auto launch_rows = [&](int cp, int64_t lo, int64_t hi) {
+  // first pass: every row, the entries held for up to kRbCap chunks (the
+  // active chunks of nearly every row: small LDS, many workgroups per CU);
+  // the rows with more are flagged and take the wide pass, by range of
+  // routable chunks for one sequence (a row at position i has floor(i/B) of
+  // them, so the rows below CP*B fit the CP-wide variant), else all at once
+  auto launch_rows = [&](int cp, int64_t lo, int64_t hi, int wide) {
     if (hi <= lo) return;
     dim3 grid((unsigned)(hi - lo), g.Hkv);
-    const int r0 = (int)lo;
+    const int r0 = (int)lo, r1 = (int)hi;
 #define DASH_RB(DD, CPV) \
-  hipLaunchKernelGGL((route_bwd_kernel<DD, CPV>), grid, dim3(256), 0, st, g, p, r0)
+  hipLaunchKernelGGL((route_bwd_kernel<DD, CPV>), grid, dim3(256), 0, st, g, p, r0, r1, wide)
 #define DASH_RB_CP(DD)                   \
   do {                                   \
     if (cp == 256) DASH_RB(DD, 256);     \
@@ -703,15 +697,18 @@ hipError_t launch_route_bwd(const Geom& g, const RouteBwdParams& p, hipStream_t 
 #undef DASH_RB_CP
 #undef DASH_RB
   };
-  const int cpmax = g.C_slots <= 256 ? 256 : g.C_slots <= 512 ? 512 : g.C_slots <= 1024 ? 1024 : 2048;
-  if (!g.cu_seqlens && g.num_seqs == 1) {
-    for (int cp = cpmax; cp >= 256; cp /= 2) {
-      const int64_t hi = std::min<int64_t>(g.T, (int64_t)cp * g.B);
-      const int64_t lo = cp == 256 ? 0 : std::min<int64_t>(g.T, (int64_t)(cp / 2) * g.B);
-      launch_rows(cp, lo, hi);
+  launch_rows(kRbCap, 0, g.T, 0);
+  const int cpmax = g.C_slots <= 512 ? 512 : g.C_slots <= 1024 ? 1024 : 2048;
+  if (g.C_slots > kRbCap) {
+    if (!g.cu_seqlens && g.num_seqs == 1) {
+      for (int cp = cpmax; cp >= 512; cp /= 2) {
+        const int64_t hi = std::min<int64_t>(g.T, (int64_t)cp * g.B);
+        const int64_t lo = std::min<int64_t>(g.T, (int64_t)(cp / 2) * g.B);
+        launch_rows(cp, lo, hi, 1);
+      }
+    } else {
+      launch_rows(cpmax, 0, g.T, 1);
     }
-  } else {
-    launch_rows(cpmax, 0, g.T);
   }
   if (cs == 0) return hipGetLastError();
   // chunk pass: 64-chunk tiles x row slices, about 2048 workgroups in all
