@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void kbar_t_kernel(Geom g, const uint16_t* __r
 // wide = 0: the rows whose entries fit CP (every row's flag written: 1 for a
 // row left to the wide pass); wide = 1: only the rows flagged so.
 template <int D, int CP>
-__global__ __launch_bounds__(256, 7) void route_bwd_kernel(Geom g, RouteBwdParams p, int row0,
+__global__ __launch_bounds__(256, CP == 256 ? 7 : 1) void route_bwd_kernel(Geom g, RouteBwdParams p, int row0,
                                                         int row1, int wide) {
   constexpr int NTH = 256;
   constexpr int KS = D / 32;
