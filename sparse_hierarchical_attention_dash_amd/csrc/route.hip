@@ -714,6 +714,55 @@ __global__ __launch_bounds__(256) void route_logits_kernel(Geom g, RouteParams p
   }
 }
 
+// Threshold of one decode row held by a wave (xs[k]: entry li + 64 k), on a
+// short candidate list.  The entmax root of the 64 lane maxima is a lower
+// bound b on tau (a subset of the entries has no more mass at any threshold,
+// so its root is no larger); a few Newton steps from below reach it, less a
+// relative rounding margin.  Only entries above b can be in the support, and
+// on these inputs they are about as many as the support itself (tens of the
+// 2048); they are compacted into LDS and the threshold solved on them alone,
+// NKC values a lane instead of NK.  A longer list solves on the whole row.
+constexpr int kDecBoundIters = 6;
+template <int NK, int NKC, int ECLS>
+__device__ float solve_tau_compact(const float (&xs)[NK], float xmax, float ex, float* cand) {
+  const int li = threadIdx.x & 63;
+  float lm = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < NK; ++k) lm = fmaxf(lm, xs[k]);
+  float b = xmax - 1.f;  // the top entry alone has mass 1 here
+#pragma unroll
+  for (int it = 0; it < kDecBoundIters; ++it) {
+    float pw, pd;
+    pow_pair<ECLS>(fmaxf(lm - b, 0.f), ex, pw, pd);
+    const float f = head_sum<64>(pw), fd = head_sum<64>(pd);
+    const float step = (f - 1.f) / (ex * fd);
+    b = (step > 0.f && fd > 0.f) ? b + step : b;
+  }
+  b -= 1e-4f * fmaxf(1.f, fabsf(b));
+  int cnt = 0;
+  float xo = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    const bool c = xs[k] > b;
+    cnt += c ? 1 : 0;
+    xo = fmaxf(xo, c ? -INFINITY : xs[k]);
+  }
+  const int incl = head_scan<64>(cnt, li);
+  const int m = __shfl(incl, 63, 64);  // list length (last lane's inclusive count)
+  if (m > 64 * NKC) return solve_tau_row<NK, 64, ECLS>(xs, xmax, ex, true, -INFINITY);
+  int pos = incl - cnt;
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    if (xs[k] > b) cand[pos] = xs[k];
+    pos += xs[k] > b ? 1 : 0;
+  }
+  // the wave reads back what its own lanes wrote (LDS ops of a wave are in order)
+  float cv[NKC];
+#pragma unroll
+  for (int j = 0; j < NKC; ++j) cv[j] = li + 64 * j < m ? cand[li + 64 * j] : kFar;
+  return solve_tau_row<NKC, 64, ECLS>(cv, xmax, ex, true, head_max<64>(xo));
+}
+
 // Decode threshold solve: one wave per (query head, row, KV head) reads the
 // head's logits row from the scratch (CP / 64 values per lane) and writes its
 // threshold in x units (alpha > 1), or its maximum and softmax denominator
@@ -763,11 +812,13 @@ __global__ __launch_bounds__(64) void route_solve_kernel(Geom g, RouteParams p) 
     }
     return;
   }
+  __shared__ float cand[128];
+  constexpr int NKC = NK < 2 ? NK : 2;
   float tau;
-  if (ecls == 2) tau = solve_tau_row<NK, 64, 2>(xs, xmax, ex, true, -INFINITY);
-  else if (ecls == 1) tau = solve_tau_row<NK, 64, 1>(xs, xmax, ex, true, -INFINITY);
-  else if (ecls == 4) tau = solve_tau_row<NK, 64, 4>(xs, xmax, ex, true, -INFINITY);
-  else tau = solve_tau_row<NK, 64, 0>(xs, xmax, ex, true, -INFINITY);
+  if (ecls == 2) tau = solve_tau_compact<NK, NKC, 2>(xs, xmax, ex, cand);
+  else if (ecls == 1) tau = solve_tau_compact<NK, NKC, 1>(xs, xmax, ex, cand);
+  else if (ecls == 4) tau = solve_tau_compact<NK, NKC, 4>(xs, xmax, ex, cand);
+  else tau = solve_tau_compact<NK, NKC, 0>(xs, xmax, ex, cand);
   if (li == 0) {
     ts[0] = tau;
     ts[1] = 0.f;
