@@ -3,9 +3,18 @@
 Phase 2 alone (dash_attn_sparse_backward) is compared on the GPU's own
 routing (mask and log-prior) with the oracle's attention backward.  The GPU
 recomputes P from the forward's LSE and rounds P and dS to bf16 for its
-products, as the forward rounds P, so each gradient is held to 2e-2 of its
-largest magnitude (bf16: 2^-8 relative per rounding, accumulated over up to
-a few thousand keys with random signs).
+products, as the forward rounds P, and returns bf16 gradients.  Each
+gradient is held to two bounds (grad_err):
+- max |g - o| <= 2e-2 max |o| (bf16: 2^-8 relative per rounding, accumulated
+  over up to a few thousand keys with random signs);
+- the RMS of g - o <= 6e-3 of the RMS of o, so that an error spread over many
+  small entries shows even where the largest entries are right (measured on
+  these cases: at most 2.9e-3; the bf16 rounding of the returned gradient
+  alone is about 1e-3).  No elementwise bound relative to each entry: where
+  a row's softmax gradient cancels (one key holding nearly all of P, so dP
+  minus <dO, O> nearly vanishes) the rounding of the forward's bf16 O in
+  <dO, O> leaves an error of a few percent of the gradient's RMS on entries
+  far smaller than that.
 """
 
 import math
@@ -23,10 +32,20 @@ from gpu_helpers import flush, to_dev, unpack_bits
 pytestmark = pytest.mark.gpu
 
 REL = 2e-2
+RMS_REL = 6e-3
 
 
-def rel_err(g, o):
-    return float(np.max(np.abs(g - o)) / max(np.max(np.abs(o)), 1e-30))
+def grad_err(g, o):
+    """max |g - o| / max |o|, after asserting the RMS bound of the module
+    docstring."""
+    g = np.asarray(g, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    d = np.abs(g - o)
+    rms = float(np.sqrt(np.mean(o * o))) if o.size else 0.0
+    if rms > 0:
+        rr = float(np.sqrt(np.mean(d * d))) / rms
+        assert rr <= RMS_REL, ("rms", rr)
+    return float(np.max(d) / max(np.max(np.abs(o)), 1e-30)) if o.size else 0.0
 
 
 CASES = [
@@ -62,11 +81,11 @@ def test_attention_backward(case):
     ref = OB.attention_backward_rows(qx, kx, vx, bits, lpx, B, 1 / math.sqrt(D), Hq // Hkv, dox)
     errs = {}
     for nm, gt, rt in (("dq", dq, ref["dq"]), ("dk", dk, ref["dk"]), ("dv", dv, ref["dv"])):
-        errs[nm] = rel_err(gt.to(torch.float64).cpu().numpy(), rt)
+        errs[nm] = grad_err(gt.to(torch.float64).cpu().numpy(), rt)
         assert errs[nm] <= REL, (nm, errs[nm])
     gb = dbias.cpu().numpy().astype(np.float64)
     assert np.all(gb[~bits] == 0.0)
-    errs["dbias"] = rel_err(gb[bits], ref["dbias"][bits]) if bits.any() else 0.0
+    errs["dbias"] = grad_err(gb[bits], ref["dbias"][bits]) if bits.any() else 0.0
     assert errs["dbias"] <= REL, errs["dbias"]
     flush(f"  backward {name}: " + " ".join(f"{k_} {v_:.2e}" for k_, v_ in errs.items()))
 
@@ -141,7 +160,7 @@ def test_prefill_backward(case):
         assert max(kfrac) > 0.02, kfrac
     errs = {}
     for nm, gt in (("dq", dq), ("dk", dk), ("dv", dv), ("dqbar", dqb)):
-        errs[nm] = rel_err(gt.to(torch.float64).cpu().numpy(), ref[nm])
+        errs[nm] = grad_err(gt.to(torch.float64).cpu().numpy(), ref[nm])
         assert errs[nm] <= REL, (nm, errs[nm])
     flush(f"  prefill backward {name}: " + " ".join(f"{k_} {v_:.2e}" for k_, v_ in errs.items())
           + f" routing/attention dq {max(rfrac):.2f} dk {max(kfrac):.2f}")
@@ -188,7 +207,7 @@ def test_backward_full_size_64k():
     rng = np.random.default_rng(82)
     rows = sorted(set(rng.integers(B, L, 20).tolist()) | {B, 2 * B - 1, L // 2, L - 1})
     a = OB.attention_backward_rows(qx, kx, vx, bits, lpx, B, s, G, dox, rows=rows)
-    e = rel_err(dq2[rows].to(torch.float64).cpu().numpy(), a["dq"][rows])
+    e = grad_err(dq2[rows].to(torch.float64).cpu().numpy(), a["dq"][rows])
     assert e <= REL, ("phase-2 dq", e)
     _, _, th = O.route_sequence(qx, kbx, B, w.alpha, w.gamma, w.sigma, G, s, rows=rows,
                                 num_slots=S)
@@ -197,7 +216,7 @@ def test_backward_full_size_64k():
     assert len(clear) >= len(rows) // 2, (len(clear), len(rows))
     r = OB.routing_backward(qx, kbx, B, w.alpha, w.gamma, w.sigma, G, s, a["dbias"], rows=clear)
     full = a["dq"][clear] + r["dq"][clear]
-    e_full = rel_err(dq[clear].to(torch.float64).cpu().numpy(), full)
+    e_full = grad_err(dq[clear].to(torch.float64).cpu().numpy(), full)
     assert e_full <= REL, ("dq", e_full)
 
     # dk and dv on sampled keys (chunk 0, a planted-chunk neighbourhood, the tail)
@@ -207,7 +226,7 @@ def test_backward_full_size_64k():
                                       lse.cpu().numpy().astype(np.float64), outx, keys)
     errs = {}
     for nm, gt, rt in (("dk", dk2, cols["dk"]), ("dv", dv2, cols["dv"]), ("dv whole", dv, cols["dv"])):
-        errs[nm] = rel_err(gt[keys].to(torch.float64).cpu().numpy(), rt)
+        errs[nm] = grad_err(gt[keys].to(torch.float64).cpu().numpy(), rt)
         assert errs[nm] <= REL, (nm, errs[nm])
     flush(f"  full-size backward: phase-2 dq {e:.2e}, dq {e_full:.2e} on {len(clear)} rows, "
           + " ".join(f"{k_} {v_:.2e}" for k_, v_ in errs.items()) + f" on {len(keys)} keys")
@@ -245,7 +264,7 @@ def test_prefill_backward_degenerate_lengths(L):
     m = OB.summarize_backward(kx, d["qbar"], B, r["dkbar"])
     ref = {"dq": a["dq"] + r["dq"], "dk": a["dk"] + m["dk"], "dv": a["dv"]}
     for nm, gt in (("dq", dq), ("dk", dk), ("dv", dv)):
-        e = rel_err(gt.to(torch.float64).cpu().numpy(), ref[nm])
+        e = grad_err(gt.to(torch.float64).cpu().numpy(), ref[nm])
         assert e <= REL, (nm, e)
     gq = dqb.cpu().numpy().astype(np.float64)
     # (one routed chunk: entmax over one entry is constant, so dq_bar is 0 up to
@@ -313,7 +332,7 @@ def test_backward_varlen(case):
         lpx = np.where(bits, lp_all[:, sl], -np.inf)
         a = OB.attention_backward_rows(qx[sl], kx[sl], vx[sl], bits, lpx, B, s, G, dox[sl])
         for nm in ("dq", "dk", "dv"):
-            e = rel_err(g[nm + "2"][sl], a[nm])
+            e = grad_err(g[nm + "2"][sl], a[nm])
             assert e <= REL, ("phase 2", sq, nm, e)
         nc = Ls // B
         kbx = kbx_all[coff:coff + nc]
@@ -328,16 +347,16 @@ def test_backward_varlen(case):
         r = OB.routing_backward(qx[sl], kbx, B, al, gamma, sigma, G, s, a["dbias"])
         m = OB.summarize_backward(kx[sl], d["qbar"], B, r["dkbar"])
         ref_dq = a["dq"] + r["dq"]
-        e = rel_err(g["dq"][sl][rows_ok], ref_dq[rows_ok])
+        e = grad_err(g["dq"][sl][rows_ok], ref_dq[rows_ok])
         assert e <= REL, ("dq", sq, e)
-        e = rel_err(g["dv"][sl], a["dv"])
+        e = grad_err(g["dv"][sl], a["dv"])
         assert e <= REL, ("dv", sq, e)
         if rows_ok.all():
-            e = rel_err(g["dk"][sl], a["dk"] + m["dk"])
+            e = grad_err(g["dk"][sl], a["dk"] + m["dk"])
             assert e <= REL, ("dk", sq, e)
         ref_dqbar += m["dqbar"]
     if all_clear:
-        e = rel_err(dqb.cpu().numpy().astype(np.float64), ref_dqbar)
+        e = grad_err(dqb.cpu().numpy().astype(np.float64), ref_dqbar)
         assert e <= REL, ("dqbar", e)
     flush(f"  varlen backward {lens}: ok (all rows clear of thresholds: {all_clear})")
 
@@ -393,6 +412,6 @@ def test_prefill_backward_estimate_diagonal(case):
     assert np.max(np.abs(md["dk"])) > 0.02 * np.max(np.abs(a["dk"]))
     errs = {}
     for nm, gt in (("dq", dq), ("dk", dk), ("dv", dv), ("dqbar", dqb)):
-        errs[nm] = rel_err(gt.to(torch.float64).cpu().numpy(), ref[nm])
+        errs[nm] = grad_err(gt.to(torch.float64).cpu().numpy(), ref[nm])
         assert errs[nm] <= REL, (nm, errs[nm])
     flush(f"  prefill backward {name}: " + " ".join(f"{k_} {v_:.2e}" for k_, v_ in errs.items()))
