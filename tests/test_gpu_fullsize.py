@@ -77,6 +77,48 @@ def test_prefill_full_size(name, nrows):
           f"support {support:.3f}")
 
 
+def test_prefill_max_chunk_slots():
+    """The largest prefill the library takes: 131,072 tokens at B = 64 are 2048
+    chunk slots and 32 mask words a row (the routing's widest variant, the
+    attention's chunk lists at their full length), with planted chunks as in
+    the 64K workload and its gamma."""
+    flush("max chunk slots prefill (131072 tokens, B = 64)")
+    L, Hq, Hkv, D, B = 131072, 32, 2, 128, 64
+    gamma, alpha, sigma = 6.29, 1.5, 1.0
+    d = W.gen_prefill(L, Hq, Hkv, D, seed=9, B=B, needles=32)
+    q, qx = to_dev(d["q"], "bf16")
+    k, kx = to_dev(d["k"], "bf16")
+    v, vx = to_dev(d["v"], "bf16")
+    del d["q"]
+    qb = torch.from_numpy(d["qbar"]).cuda()
+    out, lse, ab = ops.attn_prefill(q, k, v, qb, B, alpha=alpha, gamma=gamma, sigma=sigma,
+                                    return_lse=True, return_active_blocks=True)
+    kb = ops.summarize(k, qb, B)
+    torch.cuda.synchronize()
+    del q, k, v
+    S = L // B
+    assert ab.shape[-1] == 32 and S == 2048
+    bits_all = unpack_bits(ab, S)
+    full_mask_properties(bits_all, L, B)
+    support = bits_all.sum() / (np.sum(np.arange(L) // B) * Hkv)
+    assert 0.05 < support < 0.6, support
+    rows = sample_rows(L, B, 96, seed=9)
+    ref = O.prefill(qx, kx, vx, d["qbar"], B, alpha, gamma, sigma, True, to_bf16=True,
+                    rows=rows, num_slots=S)
+    kbg = kb.to(torch.float64).cpu().numpy()
+    check_summaries(kbg, ref["kbar"], "bf16", kx, B)
+    om, margin, _ = oracle_mask_on(qx, kbg, B, alpha, gamma, sigma, Hq // Hkv,
+                                   1 / math.sqrt(D), rows, S)
+    flips = compare_masks(bits_all[:, rows], om, margin, "max slots")
+    o = out[rows].to(torch.float64).cpu().numpy()
+    err = float(np.max(np.abs(o - ref["out"])))
+    assert err <= TOL["bf16"], err
+    lerr = float(np.max(np.abs(lse.cpu().numpy()[:, rows] - ref["lse"])))
+    assert lerr <= LSE_TOL["bf16"], lerr
+    flush(f"  max slots: rows {len(rows)} max-abs {err:.2e} lse {lerr:.2e} flips {flips} "
+          f"support {support:.3f}")
+
+
 def test_decode_full_size():
     flush("full-size decode")
     d = W.make("decode_128k")
