@@ -92,10 +92,15 @@ def active_flops_at(pop, pos, B, D, G):
     return 4.0 * D * G * float(per.sum())
 
 
-def extra_config(name, stream, reps, cpu_rows, do_cpu):
+FULL_CPU_BUDGET_S = 45.0  # a configuration's oracle runs on every row if that fits
+
+
+def extra_config(name, stream, reps, cpu_rows, do_cpu, full_cpu=False):
     """One more configuration timed as a whole fused dash_attn_prefill
     (summaries, routing and attention), with its active FLOPs, its roofline
-    fraction and the oracle timed on a sample of its rows."""
+    fraction and the oracle timed on a sample of its rows (on every row with
+    full_cpu, when the sample's time extrapolates to FULL_CPU_BUDGET_S or
+    less)."""
     import torch
     import oracle as O
     from sparse_hierarchical_attention_dash_amd import ops
@@ -139,40 +144,51 @@ def extra_config(name, stream, reps, cpu_rows, do_cpu):
          "support_histogram": support_histogram(pop, w.B, pos)}
     if do_cpu:
         # oracle: a stratified sample of rows of every sequence (all of them
-        # when the sequence is short), summaries prorated per row
+        # when the sequence is short), summaries prorated per row; with
+        # full_cpu, every row when the sample says that takes at most
+        # FULL_CPU_BUDGET_S seconds
         qx = qh.to(torch.float64).numpy()
         kx = kh.to(torch.float64).numpy()
         vx = vh.to(torch.float64).numpy()
         rng = np.random.default_rng(0)
         s = 1.0 / math.sqrt(w.D)
         alphas = d.get("alphas", np.full(len(lens), w.alpha))
-        tot_rows, secs, fl = 0, 0.0, 0.0
-        per_seq = max(1, cpu_rows // len(lens))
-        full = T <= cpu_rows
-        for si, (a, b) in enumerate(zip(cu[:-1], cu[1:])):
-            Ls = int(b - a)
-            if full or Ls <= per_seq:
-                rows = list(range(Ls))
-            else:
-                edges = np.linspace(0, Ls, per_seq + 1).astype(int)
-                rows = sorted(int(rng.integers(x, max(x + 1, y)))
-                              for x, y in zip(edges[:-1], edges[1:]))
-            t0 = time.perf_counter()
-            kbar = O.summarize(kx[a:b], d["qbar"], w.B, to_bf16=bf)
-            t_sum = time.perf_counter() - t0
-            t0 = time.perf_counter()
-            m_, lp_, _ = O.route_sequence(qx[a:b], kbar, w.B, float(alphas[si]), w.gamma,
-                                          w.sigma, G, s, rows=rows)
-            O.attention_rows(qx[a:b], kx[a:b], vx[a:b], m_, lp_, w.B, s, G, rows)
-            secs += time.perf_counter() - t0 + t_sum * len(rows) / Ls
-            tot_rows += len(rows)
-            for i in rows:
-                for h in range(w.Hkv):
-                    fl += 4.0 * w.D * G * (w.B * int(m_[h, i].sum()) + (i % w.B) + 1)
+
+        def oracle_pass(all_rows):
+            tot_rows, secs, fl = 0, 0.0, 0.0
+            per_seq = max(1, cpu_rows // len(lens))
+            full = all_rows or T <= cpu_rows
+            for si, (a, b) in enumerate(zip(cu[:-1], cu[1:])):
+                Ls = int(b - a)
+                if full or Ls <= per_seq:
+                    rows = list(range(Ls))
+                else:
+                    edges = np.linspace(0, Ls, per_seq + 1).astype(int)
+                    rows = sorted(int(rng.integers(x, max(x + 1, y)))
+                                  for x, y in zip(edges[:-1], edges[1:]))
+                t0 = time.perf_counter()
+                kbar = O.summarize(kx[a:b], d["qbar"], w.B, to_bf16=bf)
+                t_sum = time.perf_counter() - t0
+                t0 = time.perf_counter()
+                m_, lp_, _ = O.route_sequence(qx[a:b], kbar, w.B, float(alphas[si]), w.gamma,
+                                              w.sigma, G, s, rows=rows)
+                O.attention_rows(qx[a:b], kx[a:b], vx[a:b], m_, lp_, w.B, s, G, rows)
+                secs += time.perf_counter() - t0 + t_sum * len(rows) / Ls
+                tot_rows += len(rows)
+                for i in rows:
+                    for h in range(w.Hkv):
+                        fl += 4.0 * w.D * G * (w.B * int(m_[h, i].sum()) + (i % w.B) + 1)
+            return tot_rows, secs, fl
+
+        tot_rows, secs, fl = oracle_pass(False)
+        est_full = secs * flops / max(fl, 1.0)
+        if full_cpu and tot_rows < T and est_full <= FULL_CPU_BUDGET_S:
+            tot_rows, secs, fl = oracle_pass(True)
         r["cpu"] = {"value": fl / secs / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
                     "cpu_model": cpu_model(), "kind": "oracle", "seconds": secs,
                     "extrapolated_full_seconds": secs * flops / max(fl, 1.0),
-                    "sample": ("every row" if tot_rows == T else
+                    "sample": ("every row (routing + attention in float64 NumPy, and the "
+                               "summaries)" if tot_rows == T else
                                f"{tot_rows} stratified rows of {T} (routing + attention in "
                                "float64 NumPy, summaries prorated per row); the full time is "
                                "extrapolated by active FLOPs")}
@@ -815,8 +831,11 @@ def main():
         res["configs"] = {}
         for name in [x for x in args.configs.split(",") if x]:
             log(f"  {name}")
+            # the small fixed-length configurations' oracle in full, the
+            # varlen pack's on a sample
             res["configs"][name] = extra_config(name, stream, 20, 256,
-                                                not args.no_cpu_baseline)
+                                                not args.no_cpu_baseline,
+                                                full_cpu=name in ("tiny_f32", "prefill_16k"))
     log("measured peaks ...")
     res["peaks_measured"] = measured_peaks(stream)
     if "roofline" in res:
