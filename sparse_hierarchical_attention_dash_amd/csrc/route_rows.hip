@@ -378,6 +378,20 @@ __device__ __forceinline__ void route_rows_body(const Geom& g, const RouteParams
   float wsum[RPW];
 #pragma unroll
   for (int j = 0; j < RPW; ++j) word[j] = 0ull;
+  // After the reduce-scatter below, lane group gq holds the sums of row rr:
+  // rows 0, 2, 1, 3 for lane groups 0 .. 3 (four rows a wave), rows 0, 1, 0, 1
+  // (two rows a wave: lane groups 0 and 1 store them)
+  const int rr = RPW == 4 ? 2 * (gq & 1) + (gq >> 1) : (gq & 1);
+  int nr = n[0];
+  int64_t tr = tok[0];
+  bool ovr_r = ovr[0];
+#pragma unroll
+  for (int j = 1; j < RPW; ++j) {
+    nr = rr == j ? n[j] : nr;
+    tr = rr == j ? tok[j] : tr;
+    ovr_r = rr == j ? ovr[j] : ovr_r;
+  }
+  const bool writer = RPW == 4 || (gq & 2) == 0;
   pass([&](int t, int j, int ht, const float (&a)[4]) {
     if (ht == 0) wsum[j] = 0.f;
 #pragma unroll
@@ -387,24 +401,45 @@ __device__ __forceinline__ void route_rows_body(const Geom& g, const RouteParams
       rr_pow<ECLS>(fmaxf(d, 0.f), ex, pw, pd);
       wsum[j] += pw;
     }
-    if (ht != HT - 1) return;
-    // sum over the four lane groups (the group's heads), in a fixed order;
-    // the chunk is active iff some head's weight is positive
-    float w = wsum[j] + xor16(wsum[j]);
-    w += xor32(w);
-    const int c = 16 * t + r;
-    const uint32_t act = (uint32_t)(__builtin_amdgcn_ballot_w64(w > 0.f && c < n[j]) & 0xffffull);
-    // the row's lane group (j % 4) writes its 16 chunks of the prior
-    if (p.log_prior && gq == (j & 3) && c < n[j] && !ovr[j]) {
-      const bool a = (act >> r) & 1u;
-      p.log_prior[((int64_t)h * rows + tok[j]) * g.C_slots + c] =
-          a ? (p.sigma == 0.f ? 0.f : p.sigma * logf(fmaxf(w * invG, 1e-38f))) : -INFINITY;
+    if (j != RPW - 1 || ht != HT - 1) return;
+    // every row's sum over the four lane groups (the group's heads), as a
+    // reduce-scatter: each lane group keeps half of its rows and adds the
+    // partner group's half (lane l ^ 16), then the same across l ^ 32.  The
+    // additions are those of a per-row sum in the fixed order (g0 + g1) +
+    // (g2 + g3) up to commutativity, so every row gets the same bits as from
+    // an all-reduce, with one ballot, one log and one store for all rows.
+    float w;
+    const bool od = (gq & 1) != 0;
+    if constexpr (RPW == 4) {
+      const float k0 = od ? wsum[2] : wsum[0], k1 = od ? wsum[3] : wsum[1];
+      const float s0 = od ? wsum[0] : wsum[2], s1 = od ? wsum[1] : wsum[3];
+      const float a0 = k0 + xor16(s0), a1 = k1 + xor16(s1);
+      const bool hi = (gq & 2) != 0;
+      w = (hi ? a1 : a0) + xor32(hi ? a0 : a1);
+    } else {
+      const float a0 = (od ? wsum[1] : wsum[0]) + xor16(od ? wsum[0] : wsum[1]);
+      w = a0 + xor32(a0);
     }
-    word[j] |= (uint64_t)act << (16 * (t & 3));
+    // the chunk is active iff some head's weight is positive
+    const int c = 16 * t + r;
+    const bool on = w > 0.f && c < nr;
+    const uint64_t bits = __builtin_amdgcn_ballot_w64(on);
+    if (p.log_prior && writer && c < nr && !ovr_r)
+      p.log_prior[((int64_t)h * rows + tr) * g.C_slots + c] =
+          on ? (p.sigma == 0.f ? 0.f : p.sigma * logf(fmaxf(w * invG, 1e-38f))) : -INFINITY;
+#pragma unroll
+    for (int jr = 0; jr < RPW; ++jr) {
+      // row jr's 16 chunks are the bits of the lane group holding it
+      const int gj = RPW == 4 ? ((jr & 1) << 1) | (jr >> 1) : jr;
+      word[jr] |= ((bits >> (16 * gj)) & 0xffffull) << (16 * (t & 3));
+    }
     if (((t & 3) == 3 || t == ntile - 1) && t < ntile) {
-      if (lane == 0 && pos[j] < si.len && !ovr[j])
-        p.mask[((int64_t)h * rows + tok[j]) * g.W + (t >> 2)] = word[j];
-      word[j] = 0ull;
+#pragma unroll
+      for (int jr = 0; jr < RPW; ++jr) {
+        if (lane == 0 && pos[jr] < si.len && !ovr[jr])
+          p.mask[((int64_t)h * rows + tok[jr]) * g.W + (t >> 2)] = word[jr];
+        word[jr] = 0ull;
+      }
     }
   });
   // words past the last tile's
