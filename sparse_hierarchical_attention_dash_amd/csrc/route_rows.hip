@@ -242,11 +242,16 @@ __device__ __forceinline__ void route_rows_body(const Geom& g, const RouteParams
       for (int jj = 0; jj < 4; ++jj) braw[j][ht][jj] = mx[j][ht][jj] / xsc;
   pass([&](int t, int j, int ht, const float (&a)[4]) {
     const bool ok = 16 * t + r < n[j];
+    // (the ballots of the bare compares, masked by the chunk range on the
+    // scalar side: a ballot of the combined condition costs two more vector
+    // instructions an element)
+    const uint64_t okm = __builtin_amdgcn_ballot_w64(ok);
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const bool c = ok && a[jj] > braw[j][ht][jj];
+      const bool gt = a[jj] > braw[j][ht][jj];
+      const bool c = ok && gt;
       const uint32_t grp =
-          (uint32_t)(__builtin_amdgcn_ballot_w64(c) >> (16 * gq)) & 0xffffu;
+          (uint32_t)((__builtin_amdgcn_ballot_w64(gt) & okm) >> (16 * gq)) & 0xffffu;
       // past the capacity: the row's pad word (the count records the overflow)
       const int slot = ::min(cnt[j][ht][jj] + (int)__popc(grp & below), kRrCap);
       if (c) Cand[wv][j * NH + 16 * ht + 4 * gq + jj][slot] = a[jj] * xsc;
