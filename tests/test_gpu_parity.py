@@ -277,6 +277,10 @@ DECODE_CASES = [
     ("g32", "bf16", 2, 1024, [1024, 777], 32, 1, 128, 64, 1.5, 20.0, 1.0),
     ("f32", "f32", 2, 512, [512, 300], 4, 2, 64, 64, 1.5, 20.0, 1.0),
     ("softmax", "bf16", 2, 512, [512, 200], 32, 2, 128, 64, 1.0, 3.0, 1.0),
+    # nearly flat logits: more candidates than the decode solve's short list
+    # holds, so it solves on the whole row
+    ("flat-a15", "bf16", 2, 16384, [16384, 12000], 32, 2, 128, 64, 1.5, 0.5, 1.0),
+    ("flat-a2", "bf16", 2, 16384, [16384, 9000], 16, 1, 128, 64, 2.0, 0.05, 1.0),
 ]
 
 
