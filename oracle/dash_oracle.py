@@ -34,9 +34,13 @@ Readings taken where the pages are silent (each one is listed in the design doc):
 * The prior is g = w_bar ** sigma on routed chunks, with g = 0 wherever
   w_bar = 0 (so the bias is sigma * log(w_bar), and -inf off the support,
   also when sigma = 0) ([NL] Fase 2, "Dynamische Maskering" and the sigma
-  sentence of "Diagonaal Afhandeling").  This exact form is not fixed by the
-  pages: parity of g beyond its sigma = 0 and "g = 0 where w = 0" properties
-  is unpinned.
+  sentence of "Diagonaal Afhandeling").  The pages fix g only through these
+  properties (its support, sigma as its strength, a uniform prior at
+  sigma = 0), so the power form is a reading.  This function's computation of
+  it is pinned in the tests: at sigma = 0.7 the attention equals a numerical
+  solution of the KL-regularised argmax the pages describe, with prior g; at
+  sigma = 1 with softmax routing the bias is the routing's log-probability;
+  at sigma = 0 the result is plain block-sparse attention on the support.
 * Under GQA the routing probabilities of the query heads sharing a KV head
   are averaged ([NL] Fase 1, "GQA-afhandeling"); query head q uses KV head
   floor(q / G).  A chunk is active iff some head gives it a non-zero
