@@ -92,6 +92,14 @@ def active_flops_at(pop, pos, B, D, G):
     return 4.0 * D * G * float(per.sum())
 
 
+def decode_kv_bytes(popd, seqlens, B, D):
+    """Algorithmic bytes of one bf16 decode step: every key and value row the
+    new query of each (KV head, sequence) reads, once: the B keys of each
+    active chunk (popd [Hkv, batch]) and its own chunk's keys up to itself."""
+    diag = ((np.asarray(seqlens, dtype=np.int64) - 1) % B) + 1
+    return float(np.sum(B * popd.astype(np.int64) + diag[None, :])) * D * 2 * 2
+
+
 FULL_CPU_BUDGET_S = 45.0  # a configuration's oracle runs on every row if that fits
 
 
@@ -600,8 +608,7 @@ def main():
         torch.cuda.synchronize()
         popd = popcounts(abd.cpu().numpy())                  # [Hkv, batch]
         sl = dd["seqlens"].astype(np.int64)
-        diag = ((sl - 1) % wd.B) + 1
-        kv_bytes = float(np.sum(wd.B * popd + diag[None, :])) * wd.D * 2 * 2
+        kv_bytes = decode_kv_bytes(popd, sl, wd.B, wd.D)
         gbs = kv_bytes / (t_dec * 1e-3) / 1e9
         routable = float(np.sum((sl - 1) // wd.B)) * wd.Hkv
         dec_traffic = None

@@ -7,7 +7,8 @@ key a row attends (its active chunks' keys and its own chunk's keys up to
 itself).  Here that count is checked against an explicit boolean matrix of
 attended (row, key) pairs built from the same mask, for a fixed-length
 sequence and a packed batch, and the popcount of the mask words against a
-per-bit count.
+per-bit count.  The decode step's algorithmic bytes likewise: every key and
+value row (D bf16 values each) the new query of a (KV head, sequence) reads.
 """
 
 import numpy as np
@@ -91,3 +92,22 @@ def test_packed_sequences_count_each_sequence_from_its_start():
     assert np.array_equal(pos[cu[1]:cu[2]], np.arange(lens[1]))
     pop = bench.popcounts(to_words(packed))
     assert bench.active_flops_at(pop, pos, B, D, G) == want
+
+
+def test_decode_kv_bytes_count_every_row_read_once():
+    rng = np.random.default_rng(5)
+    Hkv, B, D = 2, 16, 8
+    seqlens = np.array([1, 16, 17, 95, 160], dtype=np.int64)
+    C = -(-int(seqlens.max()) // B)
+    m = np.zeros((Hkv, len(seqlens), C), dtype=bool)
+    rows = 0
+    for b, L in enumerate(seqlens):
+        n = (int(L) - 1) // B
+        m[:, b, :n] = rng.random((Hkv, n)) < 0.4
+        for h in range(Hkv):
+            keys = set(range(n * B, int(L)))              # own chunk, up to the query
+            for c in np.nonzero(m[h, b])[0]:
+                keys |= set(range(c * B, (c + 1) * B))
+            rows += len(keys)
+    pop = bench.popcounts(to_words(m))
+    assert bench.decode_kv_bytes(pop, seqlens, B, D) == rows * D * 2 * 2   # K and V, bf16
